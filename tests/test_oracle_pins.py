@@ -1,0 +1,390 @@
+"""Pins for the oracle: checks against closed forms, dense solves, finite
+differences and textbook bounds -- never against the oracle itself.
+
+Each ``pin_*`` function raises AssertionError on a violation; the pytest
+wrappers at the bottom run them, and ``test_oracle_mutants.py`` re-runs them
+against deliberately broken oracle builds to show each plausible mistake is
+caught.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from dense_ref import (laplacian_eigval_2d, laplacian_eigvec_2d, pattern_rows,
+                       to_dense)
+
+
+def _relerr(a, b):
+    return float(np.linalg.norm(np.ravel(a) - np.ravel(b)) / max(np.linalg.norm(np.ravel(b)), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# P1 -- SpMV against the closed-form Dirichlet Laplacian spectra (1D and 2D)
+# --------------------------------------------------------------------------
+def pin_p1_spmv_eigvecs():
+    N = 16
+    rp, col, val = W.varcoef_diffusion((N,), np.ones(N))
+    h = np.pi / (N + 1)
+    p = np.arange(1, N + 1)
+    for j in (1, 5, 16):
+        v = np.sin(j * p * h)
+        lam = 2.0 - 2.0 * np.cos(j * h)
+        y = O.spmv(rp, col, val, v)
+        assert np.max(np.abs(y - lam * v)) <= 1e-14 * np.max(np.abs(v)) * 4, "1D eigenpair"
+    N = 32
+    rp, col, val = W.laplacian_2d(N)
+    for (j, k) in [(1, 1), (3, 7), (32, 1), (17, 29)]:
+        v = laplacian_eigvec_2d(N, j, k)
+        lam = laplacian_eigval_2d(N, j, k)
+        y = O.spmv(rp, col, val, v)
+        assert np.max(np.abs(y - lam * v)) <= 1e-14 * 8, f"2D eigenpair {(j, k)}"
+
+
+# --------------------------------------------------------------------------
+# P2 -- SpMV against a dense product on random tiny CSR matrices
+# --------------------------------------------------------------------------
+def pin_p2_spmv_dense():
+    rng = np.random.default_rng(11)
+    for seed, n in [(1, 7), (2, 33), (3, 64)]:
+        rp, col, val = W.random_csr(n, 0.2, seed, symmetric=False)
+        A = to_dense(rp, col, val)
+        x = rng.standard_normal(n)
+        y = O.spmv(rp, col, val, x)
+        ref = A @ x
+        scale = np.abs(A) @ np.abs(x)
+        assert np.all(np.abs(y - ref) <= 4e-16 * 8 * scale + 1e-300), "dense matvec"
+
+
+# --------------------------------------------------------------------------
+# P3 -- A.1 for the variable-coefficient stencil (also pins the generator)
+# --------------------------------------------------------------------------
+def pin_p3_ones():
+    N = 9
+    rng = np.random.default_rng(5)
+    kap = np.exp(rng.standard_normal(N ** 3))
+    rp, col, val = W.varcoef_diffusion((N, N, N), kap)
+    y = O.spmv(rp, col, val, np.ones(N ** 3))
+    idx = np.arange(N ** 3)
+    ix, iy, iz = idx % N, (idx // N) % N, idx // (N * N)
+    nb = ((ix == 0).astype(int) + (ix == N - 1) + (iy == 0) + (iy == N - 1)
+          + (iz == 0) + (iz == N - 1))
+    expect = kap * nb
+    rowsum_abs = O.spmv(rp, col, np.abs(val), np.ones(N ** 3))
+    assert np.all(np.abs(y - expect) <= 1e-15 * 8 * rowsum_abs), "A.1 boundary law"
+
+
+# --------------------------------------------------------------------------
+# P4 -- CG terminates in m steps when b spans m eigenvectors
+# --------------------------------------------------------------------------
+def pin_p4_cg_krylov_termination():
+    N = 32
+    rp, col, val = W.laplacian_2d(N)
+    pairs = [(1, 1), (2, 2), (3, 5), (7, 4), (11, 13)]
+    lams = [laplacian_eigval_2d(N, j, k) for j, k in pairs]
+    assert len(set(np.round(lams, 12))) == len(lams)
+    for m in range(1, 6):
+        b = sum((1.0 + 0.25 * i) * laplacian_eigvec_2d(N, *pairs[i]) for i in range(m))
+        for pre in ("none", "jacobi"):
+            # exact arithmetic terminates at step m; in fp64 the residual falls
+            # off a cliff there (to ~1e-9 here: rounding times the spectral
+            # spread), so the pin is the cliff rather than a 1e-10 test
+            r = O.solve(rp, col, val, b, "cg", pre, tol=1e-7, maxit=50, history=True)
+            assert r.status[0] == O.OK
+            assert r.iters[0] == m, f"CG took {r.iters[0]} steps for {m} eigenvectors ({pre})"
+            if m == 1:
+                v, lam = laplacian_eigvec_2d(N, *pairs[0]), lams[0]
+                assert _relerr(r.x[0], v / lam) <= 1e-14
+            if m > 1:
+                assert r.hist[0][m - 1] > 1e-2, "converged too early"
+
+
+# --------------------------------------------------------------------------
+# P5 -- at most n CG steps on tiny well-conditioned SPD systems, and config 1
+# converges well within its number of distinct eigenvalues
+# --------------------------------------------------------------------------
+def pin_p5_cg_step_bound():
+    rng = np.random.default_rng(3)
+    for seed, n in [(4, 8), (5, 16), (6, 32)]:
+        rp, col, val = W.random_csr(n, 0.3, seed, symmetric=True)
+        b = rng.standard_normal(n)
+        r = O.solve(rp, col, val, b, "cg", "none", tol=1e-10, maxit=10 * n)
+        assert r.status[0] == O.OK and r.iters[0] <= n, f"n={n}: {r.iters[0]} steps"
+    p = W.config(1)
+    N = 32
+    lams = {round(laplacian_eigval_2d(N, j, k), 10) for j in range(1, N + 1) for k in range(1, N + 1)}
+    r = O.solve(p.row_ptr, p.col, p.values, p.b, "cg", "none", tol=1e-10, maxit=5000)
+    assert r.status[0] == O.OK and r.iters[0] <= len(lams)
+
+
+# --------------------------------------------------------------------------
+# P6 -- forward solves against dense LU (numpy.linalg.solve)
+# --------------------------------------------------------------------------
+def _dense_cases():
+    p1 = W.config(1, size=16)
+    p2 = W.config(2, size=6)
+    p3 = W.config(3, size=12, batch=3)
+    p4 = W.config(4, size=16)
+    return [p1, p2, p3, p4]
+
+
+def pin_p6_dense_solve():
+    for p in _dense_cases():
+        r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, p.tol, 5000)
+        for s in range(p.batch):
+            A = to_dense(p.row_ptr, p.col, p.values[s])
+            xd = np.linalg.solve(A, p.b[s])
+            kap = np.linalg.cond(A)
+            assert r.status[s] == O.OK, p.name
+            assert _relerr(r.x[s], xd) <= kap * p.tol, f"{p.name} sys {s}: {_relerr(r.x[s], xd)}"
+
+
+# --------------------------------------------------------------------------
+# P7 -- Jacobi-PCG on a diagonal matrix converges in one step to b/d
+# --------------------------------------------------------------------------
+def pin_p7_jacobi_diagonal():
+    n = 40
+    rng = np.random.default_rng(8)
+    d = rng.uniform(0.5, 20.0, n)
+    rp = np.arange(n + 1, dtype=np.int32)
+    col = np.arange(n, dtype=np.int32)
+    b = rng.standard_normal(n)
+    r = O.solve(rp, col, d[None, :], b, "cg", "jacobi", tol=1e-12, maxit=5)
+    assert r.status[0] == O.OK and r.iters[0] == 1
+    assert _relerr(r.x[0], b / d) <= 4e-16
+
+
+# --------------------------------------------------------------------------
+# P8 -- BiCGStab on an SPD matrix returns CG's solution
+# --------------------------------------------------------------------------
+def pin_p8_bicgstab_vs_cg():
+    p = W.config(1)
+    rc = O.solve(p.row_ptr, p.col, p.values, p.b, "cg", "none", 1e-12, 5000)
+    rb = O.solve(p.row_ptr, p.col, p.values, p.b, "bicgstab", "none", 1e-12, 5000)
+    assert rc.status[0] == O.OK and rb.status[0] == O.OK
+    assert _relerr(rb.x[0], rc.x[0]) <= 1e-9
+
+
+# --------------------------------------------------------------------------
+# P9 -- transpose map: permutation, involution, dense transpose, <Ax,y>=<x,A^T y>
+# --------------------------------------------------------------------------
+def pin_p9_transpose():
+    for seed, n in [(21, 9), (22, 40)]:
+        rp, col, val = W.random_csr(n, 0.25, seed, symmetric=False)
+        rpt, ct, perm = O.transpose(n, rp, col)
+        assert np.array_equal(np.sort(perm), np.arange(col.shape[0]))
+        At = to_dense(rpt, ct, val[0][perm])
+        assert np.array_equal(At, to_dense(rp, col, val).T)
+        rptt, ctt, permt = O.transpose(n, rpt, ct)
+        assert np.array_equal(rptt, rp.astype(np.int64)) and np.array_equal(ctt, col)
+        assert np.array_equal(perm[permt], np.arange(col.shape[0]))
+        for i in range(n):  # sorted rows of A^T
+            seg = ct[rpt[i]:rpt[i + 1]]
+            assert np.all(np.diff(seg) > 0)
+    p = W.config(4, size=256)
+    rng = np.random.default_rng(9)
+    x, y = rng.standard_normal(p.n), rng.standard_normal(p.n)
+    rpt, ct, perm = O.transpose(p.n, p.row_ptr, p.col)
+    lhs = O.dot(O.spmv(p.row_ptr, p.col, p.values, x), y)
+    rhs = O.dot(x, O.spmv(rpt, ct, p.values[0][perm], y))
+    assert abs(lhs - rhs) <= 1e-13 * abs(lhs)
+    q = W.config(2, size=12)  # symmetric pattern and values
+    rpt, ct, perm = O.transpose(q.n, q.row_ptr, q.col)
+    assert np.array_equal(perm[perm], np.arange(q.nnz))
+    assert np.array_equal(q.values[0][perm], q.values[0])
+
+
+# --------------------------------------------------------------------------
+# P10 -- symmetric A: the adjoint solve with g = b gives lambda = x (bitwise)
+# --------------------------------------------------------------------------
+def pin_p10_symmetric_adjoint():
+    p = W.config(2, size=10)
+    r = O.solve(p.row_ptr, p.col, p.values, p.b, "cg", "jacobi", 1e-10, 1000)
+    a = O.adjoint(p.row_ptr, p.col, p.values, r.x, p.b, "cg", "jacobi", 1e-10, 1000)
+    assert np.array_equal(a.grad_b, r.x)
+    rb = O.solve(p.row_ptr, p.col, p.values, p.b, "bicgstab", "none", 1e-10, 1000)
+    ab = O.adjoint(p.row_ptr, p.col, p.values, rb.x, p.b, "bicgstab", "none", 1e-10, 1000)
+    assert np.array_equal(ab.grad_b, rb.x)
+
+
+# --------------------------------------------------------------------------
+# P11 -- closed-form gradient for A = diag(d), L = 0.5 ||x - x_t||^2
+# --------------------------------------------------------------------------
+def pin_p11_diag_gradient():
+    n = 30
+    rng = np.random.default_rng(12)
+    d = rng.uniform(1.0, 4.0, n)
+    b = rng.standard_normal(n)
+    xt = rng.uniform(-1, 1, n)
+    rp = np.arange(n + 1, dtype=np.int32)
+    col = np.arange(n, dtype=np.int32)
+    for method, pre in (("cg", "jacobi"), ("cg", "none"), ("bicgstab", "none")):
+        r = O.solve(rp, col, d[None, :], b, method, pre, 1e-13, 200)
+        a = O.adjoint(rp, col, d[None, :], r.x, r.x - xt, method, pre, 1e-13, 200)
+        x = b / d
+        assert _relerr(a.grad_values[0], -(x - xt) * b / d ** 2) <= 1e-12, method
+        assert _relerr(a.grad_b[0], (x - xt) / d) <= 1e-12, method
+
+
+# --------------------------------------------------------------------------
+# P12 -- central finite differences of L = 0.5||x - x_t||^2 (dense LU solves)
+# --------------------------------------------------------------------------
+def _fd_case(p, s=0):
+    A0 = to_dense(p.row_ptr, p.col, p.values[s])
+    rows = pattern_rows(p.row_ptr)
+    cols = np.asarray(p.col, dtype=np.int64)
+    b0, xt = p.b[s].astype(np.float64), p.x_t[s].astype(np.float64)
+
+    def L(A, b):
+        x = np.linalg.solve(A, b)
+        return 0.5 * float(np.dot(x - xt, x - xt))
+
+    gv = np.empty(p.nnz)
+    for k in range(p.nnz):
+        v = A0[rows[k], cols[k]]
+        eps = 1e-6 * max(1.0, abs(v))
+        Ap, Am = A0.copy(), A0.copy()
+        Ap[rows[k], cols[k]] += eps
+        Am[rows[k], cols[k]] -= eps
+        gv[k] = (L(Ap, b0) - L(Am, b0)) / (2 * eps)
+    gb = np.empty(p.n)
+    for i in range(p.n):
+        eps = 1e-6 * max(1.0, abs(b0[i]))
+        bp, bm = b0.copy(), b0.copy()
+        bp[i] += eps
+        bm[i] -= eps
+        gb[i] = (L(A0, bp) - L(A0, bm)) / (2 * eps)
+    return gv, gb
+
+
+def pin_p12_finite_differences():
+    cases = [W.config(1, size=4), W.config(2, size=2), W.config(4, size=4)]
+    rp, col, val = W.random_csr(12, 0.3, 31, symmetric=False)
+    rng = np.random.default_rng(31)
+    cases.append(W.Problem("random_nonsym_12", 12, rp, col, val, rng.standard_normal((1, 12)),
+                           rng.uniform(-1, 1, (1, 12)), method="bicgstab", precond="none",
+                           tol=1e-13, maxit=500))
+    for p in cases:
+        r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, 1e-13, 500)
+        a = O.adjoint(p.row_ptr, p.col, p.values, r.x, r.x - p.x_t, p.method, p.precond, 1e-13, 500)
+        gv, gb = _fd_case(p)
+        assert np.max(np.abs(a.grad_values[0] - gv)) <= 1e-6 * np.max(np.abs(gv)), p.name
+        assert np.max(np.abs(a.grad_b[0] - gb)) <= 1e-6 * np.max(np.abs(gb)), p.name
+
+
+# --------------------------------------------------------------------------
+# P13 -- grad_values equals the dense -lambda x^T restricted to the pattern
+# --------------------------------------------------------------------------
+def pin_p13_dense_outer():
+    p = W.config(4, size=8)
+    r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, 1e-12, 1000)
+    g = r.x[0] - p.x_t[0]
+    a = O.adjoint(p.row_ptr, p.col, p.values, r.x, g, p.method, p.precond, 1e-12, 1000)
+    A = to_dense(p.row_ptr, p.col, p.values[0])
+    lam = np.linalg.solve(A.T, g)
+    x = np.linalg.solve(A, p.b[0])
+    full = -np.outer(lam, x)
+    assert _relerr(a.grad_values[0], full[pattern_rows(p.row_ptr), p.col]) <= 1e-9
+    assert _relerr(a.grad_b[0], lam) <= 1e-9
+
+
+# --------------------------------------------------------------------------
+# P14 -- homogeneity: sum(gradA * A) + sum(gradb * b) = lambda.(b - A x)
+# (x(tA, tb) = x(A, b) for every t; derived here, not printed on the pages)
+# --------------------------------------------------------------------------
+def pin_p14_homogeneity():
+    for p in (W.config(2, size=20), W.config(4, size=64), W.config(3, size=16, batch=2)):
+        r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, p.tol, 5000)
+        a = O.adjoint(p.row_ptr, p.col, p.values, r.x, r.x - p.x_t, p.method, p.precond, p.tol, 5000)
+        for s in range(p.batch):
+            res = p.b[s] - O.spmv(p.row_ptr, p.col, p.values[s], r.x[s])
+            lhs = O.dot(a.grad_values[s], p.values[s]) + O.dot(a.grad_b[s], p.b[s])
+            scale = O.dot(np.abs(a.grad_values[s]), np.abs(p.values[s]))
+            assert abs(lhs - O.dot(a.grad_b[s], res)) <= 1e-13 * scale, p.name
+            assert abs(lhs) <= 10 * p.tol * scale, p.name
+
+
+# --------------------------------------------------------------------------
+# P15 -- a batch equals the loop of its single systems (bitwise)
+# --------------------------------------------------------------------------
+def pin_p15_batch_is_loop():
+    p = W.config(3, size=10, batch=4)
+    r = O.solve(p.row_ptr, p.col, p.values, p.b, "cg", "jacobi", 1e-10, 1000)
+    for s in range(p.batch):
+        rs = O.solve(p.row_ptr, p.col, p.values[s], p.b[s], "cg", "jacobi", 1e-10, 1000)
+        assert np.array_equal(rs.x[0], r.x[s]) and rs.iters[0] == r.iters[s]
+
+
+# --------------------------------------------------------------------------
+# pattern validation (invalid inputs are rejected, valid ones give diagpos)
+# --------------------------------------------------------------------------
+def pin_pattern_checks():
+    rp, col, _ = W.laplacian_2d(5)
+    st, dp = O.check_pattern(25, rp, col)
+    assert st == O.OK and np.all(col[dp] == np.arange(25))
+    bad = col.copy()
+    bad[1], bad[2] = bad[2], bad[1]                     # unsorted row
+    assert O.check_pattern(25, rp, bad)[0] == O.ERR_PATTERN
+    bad = col.copy()
+    bad[-1] = 25                                          # out of range
+    assert O.check_pattern(25, rp, bad)[0] == O.ERR_PATTERN
+    bad = col.copy()
+    bad[1] = bad[0]                                       # duplicate
+    assert O.check_pattern(25, rp, bad)[0] == O.ERR_PATTERN
+    rp2, col2 = np.array([0, 1, 2]), np.array([1, 0], dtype=np.int32)  # no diagonal
+    assert O.check_pattern(2, rp2, col2)[0] == O.ERR_PATTERN
+    rp3 = rp.copy()
+    rp3[3] = rp3[4] + 1                                   # decreasing row_ptr
+    assert O.check_pattern(25, rp3, col)[0] == O.ERR_PATTERN
+
+
+def pin_special_cases():
+    p = W.config(1, size=6)
+    r = O.solve(p.row_ptr, p.col, p.values, np.zeros(p.n), "cg", "jacobi", 1e-10, 100)
+    assert r.status[0] == O.OK and r.iters[0] == 0 and not np.any(r.x)
+    r = O.solve(p.row_ptr, p.col, p.values, np.zeros(p.n), "bicgstab", "none", 1e-10, 100)
+    assert r.status[0] == O.OK and r.iters[0] == 0 and not np.any(r.x)
+    r = O.solve(p.row_ptr, p.col, p.values, p.b, "cg", "none", 1e-10, 3)
+    assert r.status[0] == O.NOT_CONVERGED and r.iters[0] == 3
+    v = p.values.copy()
+    v[0, np.asarray(O.check_pattern(p.n, p.row_ptr, p.col)[1])[0]] = 0.0
+    r = O.solve(p.row_ptr, p.col, v, p.b, "cg", "jacobi", 1e-10, 100)
+    assert r.status[0] == O.ERR_ZERO_DIAG
+    # indefinite symmetric matrix: p.Ap <= 0 is reported as a breakdown
+    rp = np.array([0, 1, 2], dtype=np.int32)
+    col = np.array([0, 1], dtype=np.int32)
+    r = O.solve(rp, col, np.array([[1.0, -1.0]]), np.array([0.0, 1.0]), "cg", "none", 1e-10, 10)
+    assert r.status[0] == O.BREAKDOWN
+    # BiCGStab breakdown: rhat.v = 0 for A = [[0,1],[1,0]], b = e1
+    rp = np.array([0, 2, 4], dtype=np.int32)
+    col = np.array([0, 1, 0, 1], dtype=np.int32)
+    r = O.solve(rp, col, np.array([[0.0, 1.0, 1.0, 0.0]]), np.array([1.0, 0.0]), "bicgstab",
+                "none", 1e-10, 10)
+    assert r.status[0] == O.BREAKDOWN
+
+
+# --------------------------------------------------------------------------
+# P16 -- BiCGStab half step: b an eigenvector => s = 0 after one product,
+# x = v / lambda (closed form), one iteration, one SpMV
+# --------------------------------------------------------------------------
+def pin_p16_bicgstab_half_step():
+    N = 32
+    rp, col, val = W.laplacian_2d(N)
+    for (j, k) in [(1, 1), (5, 9)]:
+        v = laplacian_eigvec_2d(N, j, k)
+        lam = laplacian_eigval_2d(N, j, k)
+        r = O.solve(rp, col, val, v, "bicgstab", "none", tol=1e-10, maxit=20)
+        assert r.status[0] == O.OK and r.iters[0] == 1 and r.spmv[0] == 1
+        assert _relerr(r.x[0], v / lam) <= 1e-13
+
+
+ALL_PINS = [pin_p16_bicgstab_half_step,pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
+            pin_p5_cg_step_bound, pin_p6_dense_solve, pin_p7_jacobi_diagonal,
+            pin_p8_bicgstab_vs_cg, pin_p9_transpose, pin_p10_symmetric_adjoint,
+            pin_p11_diag_gradient, pin_p12_finite_differences, pin_p13_dense_outer,
+            pin_p14_homogeneity, pin_p15_batch_is_loop, pin_pattern_checks, pin_special_cases]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[f.__name__ for f in ALL_PINS])
+def test_pin(pin):
+    pin()

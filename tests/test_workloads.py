@@ -1,0 +1,64 @@
+"""The seeded generators reproduce the named workloads' shapes and structure."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+
+@pytest.mark.parametrize("k,n,nnz", [(1, 1024, 4992), (2, 1_000_000, 6_940_000),
+                                     (3, 4096, 20224), (4, 1_048_576, 5_238_784)])
+def test_sizes(k, n, nnz):
+    p = W.config(k)
+    assert p.n == n and p.nnz == nnz
+    assert p.row_ptr.dtype == np.int32 and p.col.dtype == np.int32
+    assert int(p.row_ptr[-1]) == nnz
+    if k == 3:
+        assert p.values.shape == (1024, nnz) and p.b.shape == (1024, n)
+
+
+def test_config5_counts_and_index_type():
+    # full 512^3 is built on the GPU machine; here check the count law and the
+    # int64 row_ptr on a scaled copy with the same recipe
+    assert int(W._grid_counts((512, 512, 512)).sum(dtype=np.int64)) == 937_951_232
+    p = W.config(5, size=12)
+    assert p.row_ptr.dtype == np.int64 and p.nnz == 7 * 12 ** 3 - 6 * 12 ** 2
+
+
+def test_valid_patterns_and_exact_symmetry():
+    for p in (W.config(1), W.config(2, size=16), W.config(3, size=16, batch=3), W.config(5, size=10)):
+        st, dp = O.check_pattern(p.n, p.row_ptr, p.col)
+        assert st == O.OK
+        rpt, ct, perm = O.transpose(p.n, p.row_ptr, p.col)
+        assert np.array_equal(rpt, p.row_ptr.astype(np.int64)) and np.array_equal(ct, p.col)
+        for s in range(p.batch):
+            assert np.array_equal(p.values[s][perm], p.values[s]), p.name
+            assert np.all(p.values[s][dp] > 0)
+
+
+def test_convdiff_rows():
+    p = W.config(4, size=8)
+    st, _ = O.check_pattern(p.n, p.row_ptr, p.col)
+    assert st == O.OK
+    i = 3 * 8 + 4  # interior row: south, west, centre, east, north
+    seg = slice(p.row_ptr[i], p.row_ptr[i + 1])
+    assert list(p.col[seg]) == [i - 8, i - 1, i, i + 1, i + 8]
+    assert list(p.values[0][seg]) == [-6.0, -11.0, 19.0, -1.0, -1.0]
+    seg0 = slice(p.row_ptr[0], p.row_ptr[1])  # corner keeps the full diagonal
+    assert list(p.values[0][seg0]) == [19.0, -1.0, -1.0]
+
+
+def test_seeded_and_fp32_rounding():
+    a, b = W.config(3, size=8, batch=2), W.config(3, size=8, batch=2)
+    assert np.array_equal(a.values, b.values) and np.array_equal(a.b, b.b)
+    f = W.config(3, size=8, batch=2, dtype=np.float32)
+    assert f.values.dtype == np.float32 and f.tol == 1e-5
+    assert np.array_equal(f.values, a.values.astype(np.float32))
+
+
+def test_powerlaw_graph_long_rows():
+    rp, col, val = W.powerlaw_graph_laplacian(20000, seed=7)
+    lens = np.diff(rp)
+    assert lens.max() > 1000 and np.median(lens) < 16
+    st, _ = O.check_pattern(20000, rp, col)
+    assert st == O.OK
