@@ -1,0 +1,327 @@
+"""Differentiable sparse linear solves on MI355X (gfx950).
+
+Thin Python binding over ``libsla.so`` (C ABI declared in ``include/sla.h``).
+Every step of the solve runs in the library's HIP kernels; this module only
+marshals torch tensors (device memory, the current stream) into the C calls,
+and fails loudly if the library has not been built.
+
+What is computed (torch-sla explainer pages on gist.science, "Technical
+summary"): x = A^-1 b for CSR A by Jacobi-preconditioned CG or BiCGStab
+(Methodology section 1), and the adjoint backward pass A^T lambda = dL/dx,
+dL/db = lambda, dL/dA_ij = -lambda_i x_j on the stored pattern
+(Methodology section 2, linear systems).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "load", "SlaError", "Pattern", "SparseSolve", "sparse_solve",
+    "sla_create", "sla_destroy", "sla_matvec", "sla_solve", "sla_solve_adjoint",
+    "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
+    "SLA_OK", "SLA_NOT_CONVERGED", "SLA_BREAKDOWN", "SLA_ERR_ARG", "SLA_ERR_PATTERN",
+    "SLA_ERR_ZERO_DIAG", "SLA_ERR_NO_MEMORY", "SLA_ERR_DEVICE", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsla.so")
+
+SLA_F32, SLA_F64 = 0, 1
+SLA_I32, SLA_I64 = 0, 1
+SLA_CG, SLA_BICGSTAB = 0, 1
+SLA_PRECOND_NONE, SLA_PRECOND_JACOBI = 0, 1
+SLA_OK, SLA_NOT_CONVERGED, SLA_BREAKDOWN = 0, 1, 2
+SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
+SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
+
+EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_solve", "sla_solve_adjoint",
+                    "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
+                    "sla_last_error")
+
+_METHODS = {"cg": SLA_CG, "bicgstab": SLA_BICGSTAB}
+_PRECONDS = {"none": SLA_PRECOND_NONE, "jacobi": SLA_PRECOND_JACOBI}
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("tol", ctypes.c_double), ("maxit", ctypes.c_int32), ("method", ctypes.c_int32),
+                ("precond", ctypes.c_int32), ("use_x0", ctypes.c_int32),
+                ("graph_chunk", ctypes.c_int32), ("profile", ctypes.c_int32)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("iters", ctypes.c_void_p), ("spmv", ctypes.c_void_p), ("relres", ctypes.c_void_p),
+                ("status", ctypes.c_void_p), ("kernel_ms", ctypes.c_double),
+                ("kernel_launches", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None):
+    """Load libsla.so (built by ``python -m differentiable_sparse_linear_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m differentiable_sparse_linear_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.sla_create.argtypes = [ctypes.POINTER(P), I64, I64, I64, I32, I32, P, P, I32, P]
+    lib.sla_create.restype = I32
+    lib.sla_destroy.argtypes = [P]
+    lib.sla_destroy.restype = I32
+    lib.sla_matvec.argtypes = [P, P, P, P, I32, P]
+    lib.sla_matvec.restype = I32
+    lib.sla_solve.argtypes = [P, P, P, P, ctypes.POINTER(_Opts), ctypes.POINTER(_Info), P]
+    lib.sla_solve.restype = I32
+    lib.sla_solve_adjoint.argtypes = [P, P, P, P, P, P, ctypes.POINTER(_Opts),
+                                      ctypes.POINTER(_Info), P]
+    lib.sla_solve_adjoint.restype = I32
+    lib.sla_export_pattern.argtypes = [P, P, P, P, P, P]
+    lib.sla_export_pattern.restype = I32
+    lib.sla_workspace_bytes.argtypes = [P]
+    lib.sla_workspace_bytes.restype = I64
+    lib.sla_status_string.argtypes = [I32]
+    lib.sla_status_string.restype = ctypes.c_char_p
+    lib.sla_last_error.argtypes = []
+    lib.sla_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.sla_status_string(status).decode()
+        if status == SLA_ERR_DEVICE:
+            msg += f" ({lib.sla_last_error().decode()})"
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def sla_status_string(status: int) -> str:
+    return load().sla_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, numel=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+# -------------------------------------------------------------- raw C calls
+
+def sla_create(n, nnz, batch, dtype, row_ptr: torch.Tensor, col: torch.Tensor,
+               build_transpose: bool, stream=None) -> int:
+    lib = load()
+    h = ctypes.c_void_p()
+    itype = SLA_I64 if row_ptr.dtype == torch.int64 else SLA_I32
+    dt = SLA_F64 if dtype == torch.float64 else SLA_F32
+    st = lib.sla_create(ctypes.byref(h), int(n), int(nnz), int(batch), dt, itype, _ptr(row_ptr),
+                        _ptr(col), 1 if build_transpose else 0, _stream(stream))
+    if st != SLA_OK:
+        raise SlaError(st, "sla_create")
+    return h.value
+
+
+def sla_destroy(h: int) -> None:
+    st = load().sla_destroy(ctypes.c_void_p(h))
+    if st != SLA_OK:
+        raise SlaError(st, "sla_destroy")
+
+
+def sla_matvec(h, values, x, y, transpose=False, stream=None) -> int:
+    return load().sla_matvec(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(y),
+                             1 if transpose else 0, _stream(stream))
+
+
+def _make_opts(tol, maxit, method, precond, use_x0, graph_chunk, profile):
+    return _Opts(float(tol), int(maxit), _METHODS[method], _PRECONDS[precond], int(use_x0),
+                 int(graph_chunk), int(profile))
+
+
+def _make_info(batch):
+    arrs = {"iters": np.zeros(batch, np.int32), "spmv": np.zeros(batch, np.int32),
+            "relres": np.zeros(batch, np.float64), "status": np.zeros(batch, np.int32)}
+    info = _Info(arrs["iters"].ctypes.data, arrs["spmv"].ctypes.data, arrs["relres"].ctypes.data,
+                 arrs["status"].ctypes.data, 0.0, 0)
+    return info, arrs
+
+
+def sla_solve(h, values, b, x, opts: _Opts, info: _Info, stream=None) -> int:
+    return load().sla_solve(ctypes.c_void_p(h), _ptr(values), _ptr(b), _ptr(x), ctypes.byref(opts),
+                            ctypes.byref(info), _stream(stream))
+
+
+def sla_solve_adjoint(h, values, x, grad_x, grad_values, grad_b, opts: _Opts, info: _Info,
+                      stream=None) -> int:
+    return load().sla_solve_adjoint(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(grad_x),
+                                    _ptr(grad_values), _ptr(grad_b), ctypes.byref(opts),
+                                    ctypes.byref(info), _stream(stream))
+
+
+def sla_export_pattern(h, diagpos=None, row_ptr_t=None, col_t=None, perm=None, stream=None) -> int:
+    return load().sla_export_pattern(ctypes.c_void_p(h), _ptr(diagpos), _ptr(row_ptr_t),
+                                     _ptr(col_t), _ptr(perm), _stream(stream))
+
+
+def sla_workspace_bytes(h) -> int:
+    return int(load().sla_workspace_bytes(ctypes.c_void_p(h)))
+
+
+# -------------------------------------------------------------- object API
+
+class Pattern:
+    """A CSR pattern on the device shared by ``batch`` value arrays.
+
+    row_ptr: int32/int64 [n+1], col: int32 [nnz] (device tensors, kept alive
+    by this object because the library borrows them).
+    """
+
+    def __init__(self, row_ptr: torch.Tensor, col: torch.Tensor, batch: int = 1,
+                 dtype: torch.dtype = torch.float64, build_transpose: bool = False, stream=None):
+        _check(row_ptr, "row_ptr")
+        _check(col, "col", torch.int32)
+        if row_ptr.dtype not in (torch.int32, torch.int64):
+            raise ValueError("row_ptr must be int32 or int64")
+        if dtype not in (torch.float32, torch.float64):
+            raise ValueError("dtype must be float32 or float64")
+        self.row_ptr, self.col = row_ptr, col
+        self.n = row_ptr.numel() - 1
+        self.nnz = col.numel()
+        self.batch = int(batch)
+        self.dtype = dtype
+        self.has_transpose = bool(build_transpose)
+        self.device = row_ptr.device
+        self.handle = sla_create(self.n, self.nnz, self.batch, dtype, row_ptr, col,
+                                 build_transpose, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            sla_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self) -> int:
+        return sla_workspace_bytes(self.handle)
+
+    def _vals(self, values):
+        _check(values, "values", self.dtype, self.batch * self.nnz)
+
+    def _vec(self, v, name):
+        _check(v, name, self.dtype, self.batch * self.n)
+
+    def matvec(self, values, x, transpose=False, out=None, stream=None):
+        self._vals(values)
+        self._vec(x, "x")
+        y = out if out is not None else torch.empty_like(x)
+        self._vec(y, "out")
+        st = sla_matvec(self.handle, values, x, y, transpose, stream)
+        if st != SLA_OK:
+            raise SlaError(st, "sla_matvec")
+        return y
+
+    def solve(self, values, b, tol=1e-10, maxit=1000, method="cg", precond="jacobi", x0=None,
+              graph_chunk=0, profile=False, check=True, out=None, stream=None):
+        """Returns (x, info); info holds per-system iters/spmv/relres/status."""
+        self._vals(values)
+        self._vec(b, "b")
+        if x0 is not None:
+            self._vec(x0, "x0")
+            x = x0.clone() if out is None else out.copy_(x0)
+        else:
+            x = out if out is not None else torch.empty_like(b)
+        self._vec(x, "x")
+        opts = _make_opts(tol, maxit, method, precond, x0 is not None, graph_chunk, profile)
+        info, arrs = _make_info(self.batch)
+        st = sla_solve(self.handle, values, b, x, opts, info, stream)
+        arrs["return"] = st
+        arrs["kernel_ms"] = info.kernel_ms
+        arrs["kernel_launches"] = info.kernel_launches
+        if check and st < 0:
+            raise SlaError(st, "sla_solve")
+        return x, arrs
+
+    def solve_adjoint(self, values, x, grad_x, tol=1e-10, maxit=1000, method="cg",
+                      precond="jacobi", graph_chunk=0, profile=False, check=True, out=None,
+                      stream=None):
+        """Returns (grad_values, grad_b, info)."""
+        self._vals(values)
+        self._vec(x, "x")
+        self._vec(grad_x, "grad_x")
+        gv = torch.empty_like(values) if out is None else out[0]
+        gb = torch.empty_like(grad_x) if out is None else out[1]
+        opts = _make_opts(tol, maxit, method, precond, 0, graph_chunk, profile)
+        info, arrs = _make_info(self.batch)
+        st = sla_solve_adjoint(self.handle, values, x, grad_x, gv, gb, opts, info, stream)
+        arrs["return"] = st
+        arrs["kernel_ms"] = info.kernel_ms
+        arrs["kernel_launches"] = info.kernel_launches
+        if check and st < 0:
+            raise SlaError(st, "sla_solve_adjoint")
+        return gv, gb, arrs
+
+    def export_pattern(self, stream=None):
+        """Derived structures: diagpos, and (row_ptr_t, col_t, perm) if built."""
+        idt = self.row_ptr.dtype
+        dp = torch.empty(self.n, dtype=idt, device=self.device)
+        rpt = ct = pm = None
+        if self.has_transpose:
+            rpt = torch.empty(self.n + 1, dtype=idt, device=self.device)
+            ct = torch.empty(self.nnz, dtype=torch.int32, device=self.device)
+            pm = torch.empty(self.nnz, dtype=torch.int32, device=self.device)
+        st = sla_export_pattern(self.handle, dp, rpt, ct, pm, stream)
+        if st != SLA_OK:
+            raise SlaError(st, "sla_export_pattern")
+        return dp, rpt, ct, pm
+
+
+class SparseSolve(torch.autograd.Function):
+    """x = A^-1 b with the adjoint backward; saves only x (O(n) per system)."""
+
+    @staticmethod
+    def forward(ctx, values, b, pattern: Pattern, opts: dict):
+        x, info = pattern.solve(values.contiguous(), b.contiguous(), **opts)
+        ctx.pattern = pattern
+        ctx.opts = opts
+        ctx.save_for_backward(values, x)
+        return x
+
+    @staticmethod
+    def backward(ctx, grad_x):
+        values, x = ctx.saved_tensors
+        gv, gb, _ = ctx.pattern.solve_adjoint(values.contiguous(), x, grad_x.contiguous(),
+                                              **{k: v for k, v in ctx.opts.items()
+                                                 if k not in ("x0",)})
+        return gv, gb, None, None
+
+
+def sparse_solve(pattern: Pattern, values: torch.Tensor, b: torch.Tensor, **opts) -> torch.Tensor:
+    """Differentiable x = A(values)^-1 b; gradients flow to values and b."""
+    return SparseSolve.apply(values, b, pattern, opts)

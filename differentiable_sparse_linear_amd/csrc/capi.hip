@@ -1,0 +1,642 @@
+// C ABI of the sparse solve: handle lifetime, workspace, and the drivers that
+// enqueue the iteration kernels.
+//
+// Launch control (torch-sla explainer, Problem statement: iterative solvers
+// pay kernel-launch overhead on small problems):
+//  * small systems (n <= 4096, short rows) solve with CG in one workgroup per
+//    system, a single launch for the whole batch;
+//  * larger systems run the grid kernels; K iterations are captured once in a
+//    HIP graph that reads its arguments from a device block, every kernel
+//    returns at entry once the device-side `done` flag is set, and the host
+//    keeps one replay in flight while it polls the flag of the previous one.
+// Nothing is allocated after sla_create (memory is O(n + nnz) whatever the
+// iteration count -- Methodology section 2, complexity bullet).
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <type_traits>
+#include <vector>
+
+#include "sla_internal.h"
+
+using namespace sla;
+
+namespace {
+
+thread_local hipError_t g_last_error = hipSuccess;
+
+constexpr int kNumVec = 11;  // r z q rh s t p0 p1 v0 v1 dinv
+constexpr int kDefaultChunk = 16;
+
+struct GraphEntry {
+    int key = -1;
+    int chunk = 0;
+    hipGraphExec_t exec = nullptr;
+};
+
+}  // namespace
+
+struct sla_ctx {
+    int device = 0;
+    int64_t n = 0, nnz = 0, batch = 0;
+    int dtype = SLA_F64, itype = SLA_I32;
+    const void *rp = nullptr;
+    const int32_t *col = nullptr;
+    void *diagpos = nullptr;
+    bool has_t = false;
+    void *rp_t = nullptr;
+    int32_t *col_t = nullptr;
+    int32_t *perm = nullptr;
+    void *val_t = nullptr;
+    int G = 8;
+    void *vec = nullptr;
+    SolveState *st = nullptr;
+    double *part = nullptr;
+    void *args_dev = nullptr;
+    void *args_host = nullptr;   // pinned
+    int32_t *flag = nullptr;
+    int32_t *poll = nullptr;     // pinned [2]
+    SolveState *st_host = nullptr;  // pinned [batch]
+    hipStream_t cap = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    std::vector<hipEvent_t> prof_ev;
+    GraphEntry graphs[8];
+    int64_t ws_bytes = 0;
+};
+
+namespace {
+
+inline size_t tsize(const sla_ctx *h) { return h->dtype == SLA_F64 ? 8 : 4; }
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        int cur = 0;
+        if (hipGetDevice(&cur) == hipSuccess && cur != dev) {
+            prev = cur;
+            (void)hipSetDevice(dev);
+        }
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+#define HIP_TRY(...)                          \
+    do {                                      \
+        hipError_t e_ = (__VA_ARGS__);        \
+        if (e_ != hipSuccess) {               \
+            g_last_error = e_;                \
+            return SLA_ERR_DEVICE;            \
+        }                                     \
+    } while (0)
+
+template <typename P>
+hipError_t dmalloc(sla_ctx *h, P **p, size_t bytes) {
+    hipError_t e = hipMalloc((void **)p, bytes > 0 ? bytes : 1);
+    if (e == hipSuccess) h->ws_bytes += (int64_t)(bytes > 0 ? bytes : 1);
+    return e;
+}
+
+void release(sla_ctx *h) {
+    if (!h) return;
+    for (auto &g : h->graphs)
+        if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    for (auto e : h->prof_ev) (void)hipEventDestroy(e);
+    for (auto e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    if (h->cap) (void)hipStreamDestroy(h->cap);
+    (void)hipFree(h->diagpos);
+    (void)hipFree(h->rp_t);
+    (void)hipFree(h->col_t);
+    (void)hipFree(h->perm);
+    (void)hipFree(h->val_t);
+    (void)hipFree(h->vec);
+    (void)hipFree(h->st);
+    (void)hipFree(h->part);
+    (void)hipFree(h->args_dev);
+    (void)hipFree(h->flag);
+    if (h->args_host) (void)hipHostFree(h->args_host);
+    if (h->poll) (void)hipHostFree(h->poll);
+    if (h->st_host) (void)hipHostFree(h->st_host);
+    delete h;
+}
+
+sla_solve_opts default_opts() {
+    sla_solve_opts o;
+    o.tol = 1e-10;
+    o.maxit = 1000;
+    o.method = SLA_CG;
+    o.precond = SLA_PRECOND_JACOBI;
+    o.use_x0 = 0;
+    o.graph_chunk = 0;
+    o.profile = 0;
+    return o;
+}
+
+sla_status check_opts(const sla_solve_opts &o) {
+    if (!(o.tol >= 0.0) || o.maxit < 0) return SLA_ERR_ARG;
+    if (o.method != SLA_CG && o.method != SLA_BICGSTAB) return SLA_ERR_ARG;
+    if (o.precond != SLA_PRECOND_NONE && o.precond != SLA_PRECOND_JACOBI) return SLA_ERR_ARG;
+    if (o.method == SLA_BICGSTAB && o.precond != SLA_PRECOND_NONE) return SLA_ERR_ARG;
+    return SLA_OK;
+}
+
+// The operator a solve iterates with: A itself or the mapped A^T.
+struct Operator {
+    const void *rp;
+    const int32_t *col;
+    int G;
+};
+
+// One system on the grid path: fill the argument block, run init, then
+// replay/launch iteration chunks until the device reports done.
+template <typename T, typename IT>
+sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T *b, T *x,
+                          SolveState *st, const sla_solve_opts &o, hipStream_t s,
+                          double *prof_ms, int64_t *prof_launches) {
+    const int64_t n = h->n;
+    const bool cg = o.method == SLA_CG;
+    const bool jac = cg && o.precond == SLA_PRECOND_JACOBI;
+    T *vec = reinterpret_cast<T *>(h->vec);
+    IterArgs<T, IT> a;
+    memset(&a, 0, sizeof(a));
+    a.val = val;
+    a.rp = reinterpret_cast<const IT *>(op.rp);
+    a.col = op.col;
+    a.x = x;
+    a.b = b;
+    a.r = vec + 0 * n;
+    a.z = vec + 1 * n;
+    a.q = vec + 2 * n;
+    a.rh = vec + 3 * n;
+    a.s = vec + 4 * n;
+    a.t = vec + 5 * n;
+    a.p[0] = vec + 6 * n;
+    a.p[1] = vec + 7 * n;
+    a.v[0] = vec + 8 * n;
+    a.v[1] = vec + 9 * n;
+    a.dinv = vec + 10 * n;
+    a.st = st;
+    a.part = h->part;
+    a.n = n;
+    a.tol = o.tol;
+    a.maxit = o.maxit;
+    a.use_x0 = o.use_x0;
+    // the previous call has completed (every call ends with a sync), so the
+    // pinned staging block is free to rewrite
+    memcpy(h->args_host, &a, sizeof(a));
+    const IterArgs<T, IT> *ad = reinterpret_cast<const IterArgs<T, IT> *>(h->args_dev);
+    HIP_TRY(hipMemcpyAsync(h->args_dev, h->args_host, sizeof(a), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState), s));
+    if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, vec + 10 * n,
+                                        n, st, s));
+    if (o.use_x0)
+        HIP_TRY(launch_spmv<T, IT>(op.G, a.rp, op.col, val, 0, x, a.q, n, 0, 1, s));
+    if (cg)
+        HIP_TRY(launch_cg_init<T, IT>(jac, ad, n, s));
+    else
+        HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
+
+    auto one_iter = [&](hipStream_t ss) -> hipError_t {
+        hipError_t e;
+        if (cg) {
+            if ((e = launch_cg_spmv<T, IT>(op.G, jac, ad, n, ss)) != hipSuccess) return e;
+            return launch_cg_update<T, IT>(jac, ad, n, ss);
+        }
+        if ((e = launch_bicg_pv<T, IT>(op.G, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_bicg_st<T, IT>(op.G, ad, n, ss)) != hipSuccess) return e;
+        return launch_bicg_update<T, IT>(ad, n, ss);
+    };
+
+    if (o.profile) {
+        // every iteration launched directly, each fused SpMV kernel bracketed
+        // by a pair of events on `s`
+        const int per = cg ? 1 : 2;
+        const size_t need = (size_t)2 * per * (size_t)o.maxit;
+        while (h->prof_ev.size() < need) {
+            hipEvent_t e;
+            HIP_TRY(hipEventCreate(&e));
+            h->prof_ev.push_back(e);
+        }
+        size_t ev = 0;
+        for (int k = 0; k < o.maxit; ++k) {
+            if (cg) {
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_cg_spmv<T, IT>(op.G, jac, ad, n, s));
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_cg_update<T, IT>(jac, ad, n, s));
+            } else {
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_bicg_pv<T, IT>(op.G, ad, n, s));
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_bicg_st<T, IT>(op.G, ad, n, s));
+                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
+            }
+            if ((k & 63) == 63 || k + 1 == o.maxit) {
+                HIP_TRY(hipMemcpyAsync(&h->poll[0], &st->done, sizeof(int32_t),
+                                       hipMemcpyDeviceToHost, s));
+                HIP_TRY(hipStreamSynchronize(s));
+                if (h->poll[0]) break;
+            }
+        }
+        SolveState hs;
+        HIP_TRY(hipMemcpyAsync(&hs, st, sizeof(hs), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        // the first `nfused` bracketed launches did work; later ones returned
+        // at entry
+        int64_t active = hs.nfused;
+        if ((size_t)(2 * active) > ev) active = (int64_t)(ev / 2);
+        double total = 0.0;
+        for (int64_t j = 0; j < active; ++j) {
+            float ms = 0.f;
+            HIP_TRY(hipEventElapsedTime(&ms, h->prof_ev[2 * j], h->prof_ev[2 * j + 1]));
+            total += ms;
+        }
+        *prof_ms += total;
+        *prof_launches += active;
+    } else {
+        int chunk = o.graph_chunk == 0 ? kDefaultChunk : (o.graph_chunk < 0 ? -o.graph_chunk : o.graph_chunk);
+        if (chunk > o.maxit && o.maxit > 0) chunk = o.maxit;
+        if (chunk < 1) chunk = 1;
+        hipGraphExec_t exec = nullptr;
+        if (o.graph_chunk >= 0) {
+            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.G != h->G || op.rp != h->rp ? 2 : 0);
+            GraphEntry *slot = nullptr;
+            for (auto &g : h->graphs)
+                if (g.key == key && g.chunk == chunk) slot = &g;
+            if (!slot) {
+                for (auto &g : h->graphs)
+                    if (g.key == -1 || g.key == key) {
+                        slot = &g;
+                        break;
+                    }
+                if (!slot) slot = &h->graphs[0];
+                if (slot->exec) {
+                    HIP_TRY(hipGraphExecDestroy(slot->exec));
+                    slot->exec = nullptr;
+                    slot->key = -1;
+                }
+                hipGraph_t graph = nullptr;
+                HIP_TRY(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
+                hipError_t ce = hipSuccess;
+                for (int k = 0; k < chunk && ce == hipSuccess; ++k) ce = one_iter(h->cap);
+                hipError_t ee = hipStreamEndCapture(h->cap, &graph);
+                HIP_TRY(ce);
+                HIP_TRY(ee);
+                hipError_t ie = hipGraphInstantiate(&slot->exec, graph, nullptr, nullptr, 0);
+                (void)hipGraphDestroy(graph);
+                HIP_TRY(ie);
+                slot->key = key;
+                slot->chunk = chunk;
+            }
+            exec = slot->exec;
+        }
+        const int64_t max_chunks = (o.maxit + chunk - 1) / chunk + 1;
+        for (int64_t c = 0; c <= max_chunks; ++c) {
+            if (c < max_chunks) {
+                if (exec) {
+                    HIP_TRY(hipGraphLaunch(exec, s));
+                } else {
+                    for (int k = 0; k < chunk; ++k) HIP_TRY(one_iter(s));
+                }
+                HIP_TRY(hipMemcpyAsync(&h->poll[c & 1], &st->done, sizeof(int32_t),
+                                       hipMemcpyDeviceToHost, s));
+                HIP_TRY(hipEventRecord(h->ev[c & 1], s));
+            }
+            if (c >= 1) {
+                HIP_TRY(hipEventSynchronize(h->ev[(c - 1) & 1]));
+                if (h->poll[(c - 1) & 1]) break;
+            }
+        }
+    }
+    if (o.use_x0) HIP_TRY(launch_zero_if<T>(st, x, n, s));
+    return SLA_OK;
+}
+
+template <typename T, typename IT>
+sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T *x,
+                     const sla_solve_opts &o, sla_solve_info *info, hipStream_t s) {
+    const int64_t n = h->n, nnz = h->nnz, B = h->batch;
+    const bool cg = o.method == SLA_CG;
+    double prof_ms = 0.0;
+    int64_t prof_launches = 0;
+    const bool block_path = cg && n <= kBlockSolveMaxN && op.G <= 16 && !o.profile;
+    if (block_path) {
+        BlockCgParams p;
+        p.val = val;
+        p.rp = op.rp;
+        p.col = op.col;
+        p.diagpos = h->diagpos;
+        p.x = x;
+        p.b = b;
+        p.st = h->st;
+        p.n = n;
+        p.nnz = nnz;
+        p.tol = o.tol;
+        p.maxit = o.maxit;
+        p.use_x0 = o.use_x0;
+        p.jac = o.precond == SLA_PRECOND_JACOBI;
+        for (int64_t s0 = 0; s0 < B; s0 += 65535) {
+            const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
+            BlockCgParams q = p;
+            q.val = reinterpret_cast<const T *>(val) + s0 * nnz;
+            q.b = reinterpret_cast<const T *>(b) + s0 * n;
+            q.x = reinterpret_cast<T *>(x) + s0 * n;
+            q.st = h->st + s0;
+            HIP_TRY(launch_block_cg<T, IT>(op.G, q, nb, s));
+        }
+    } else {
+        for (int64_t sys = 0; sys < B; ++sys) {
+            sla_status r = grid_solve_one<T, IT>(h, op, val + sys * nnz, b + sys * n, x + sys * n,
+                                                 h->st + sys, o, s, &prof_ms, &prof_launches);
+            if (r != SLA_OK) return r;
+        }
+    }
+    HIP_TRY(hipMemcpyAsync(h->st_host, h->st, sizeof(SolveState) * B, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    int worst_err = 0, worst_pos = 0;
+    for (int64_t sys = 0; sys < B; ++sys) {
+        const SolveState &ss = h->st_host[sys];
+        const int stc = ss.status;
+        if (stc < 0 && stc < worst_err) worst_err = stc;
+        if (stc > worst_pos) worst_pos = stc;
+        if (info) {
+            if (info->iters) info->iters[sys] = ss.iter;
+            if (info->spmv) info->spmv[sys] = ss.spmv;
+            if (info->status) info->status[sys] = stc;
+            if (info->relres) info->relres[sys] = ss.bb > 0.0 ? sqrt(ss.rr) / sqrt(ss.bb) : 0.0;
+        }
+    }
+    if (info) {
+        info->kernel_ms = prof_ms;
+        info->kernel_launches = prof_launches;
+    }
+    return (sla_status)(worst_err < 0 ? worst_err : worst_pos);
+}
+
+template <typename T, typename IT>
+sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gval, T *gb,
+                       const sla_solve_opts &o, sla_solve_info *info, hipStream_t s) {
+    const int64_t n = h->n, nnz = h->nnz, B = h->batch;
+    sla_solve_opts oo = o;
+    oo.use_x0 = 0;
+    sla_status st;
+    if (o.method == SLA_CG) {
+        Operator op{h->rp, h->col, h->G};
+        st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
+    } else {
+        // A^T with values gathered through the transpose map, one system at
+        // a time into the handle's buffer
+        Operator op{h->rp_t, h->col_t, h->G};
+        const int64_t B0 = h->batch;
+        st = SLA_OK;
+        std::vector<int32_t> it(B0), mv(B0), stc(B0);
+        std::vector<double> rr(B0);
+        double kms = 0.0;
+        int64_t kl = 0;
+        h->batch = 1;
+        for (int64_t sys = 0; sys < B0; ++sys) {
+            hipError_t e = launch_gather<T>(h->perm, val + sys * nnz, reinterpret_cast<T *>(h->val_t),
+                                            nnz, s);
+            if (e != hipSuccess) {
+                h->batch = B0;
+                g_last_error = e;
+                return SLA_ERR_DEVICE;
+            }
+            sla_solve_info one;
+            one.iters = &it[sys];
+            one.spmv = &mv[sys];
+            one.relres = &rr[sys];
+            one.status = &stc[sys];
+            sla_status r = solve_all<T, IT>(h, op, reinterpret_cast<const T *>(h->val_t), gx + sys * n,
+                                            gb + sys * n, oo, &one, s);
+            kms += one.kernel_ms;
+            kl += one.kernel_launches;
+            if (r < 0 && (st >= 0 || r < st)) st = r;
+            if (r > 0 && st >= 0 && r > st) st = r;
+            if (r == SLA_ERR_DEVICE) break;
+        }
+        h->batch = B0;
+        if (info) {
+            for (int64_t sys = 0; sys < B0; ++sys) {
+                if (info->iters) info->iters[sys] = it[sys];
+                if (info->spmv) info->spmv[sys] = mv[sys];
+                if (info->relres) info->relres[sys] = rr[sys];
+                if (info->status) info->status[sys] = stc[sys];
+            }
+            info->kernel_ms = kms;
+            info->kernel_launches = kl;
+        }
+    }
+    if (st == SLA_ERR_DEVICE) return st;
+    for (int64_t s0 = 0; s0 < B; s0 += 65535) {
+        const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
+        HIP_TRY(launch_grad<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp), h->col, gb + s0 * n,
+                                   x + s0 * n, gval + s0 * nnz, n, nnz, nb, s));
+    }
+    HIP_TRY(hipStreamSynchronize(s));
+    return st;
+}
+
+template <typename T, typename IT>
+sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
+    const int64_t n = h->n, nnz = h->nnz;
+    const IT *rp = reinterpret_cast<const IT *>(h->rp);
+    HIP_TRY(dmalloc(h, &h->diagpos, sizeof(IT) * n));
+    HIP_TRY(dmalloc(h, &h->flag, sizeof(int32_t)));
+    HIP_TRY(setup_validate<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->diagpos), h->flag, s));
+    int32_t bad = 0;
+    HIP_TRY(hipMemcpyAsync(&bad, h->flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (bad) return SLA_ERR_PATTERN;
+    if (build_t) {
+        HIP_TRY(dmalloc(h, &h->rp_t, sizeof(IT) * (n + 1)));
+        HIP_TRY(dmalloc(h, &h->col_t, sizeof(int32_t) * nnz));
+        HIP_TRY(dmalloc(h, &h->perm, sizeof(int32_t) * nnz));
+        HIP_TRY(dmalloc(h, &h->val_t, sizeof(T) * nnz));
+        HIP_TRY(setup_transpose<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->rp_t), h->col_t,
+                                    h->perm, s));
+        h->has_t = true;
+    }
+    HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
+    HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
+    HIP_TRY(dmalloc(h, &h->part, sizeof(double) * kMaxRed * kMaxGrid));
+    HIP_TRY(dmalloc(h, &h->args_dev, sizeof(IterArgs<T, IT>)));
+    HIP_TRY(hipHostMalloc(&h->args_host, sizeof(IterArgs<T, IT>), hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void **)&h->poll, 2 * sizeof(int32_t), hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void **)&h->st_host, sizeof(SolveState) * h->batch, hipHostMallocDefault));
+    HIP_TRY(hipMemsetAsync(h->st, 0, sizeof(SolveState) * h->batch, s));
+    HIP_TRY(hipMemsetAsync(h->part, 0, sizeof(double) * kMaxRed * kMaxGrid, s));
+    HIP_TRY(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&h->ev[0], hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&h->ev[1], hipEventDisableTiming));
+    HIP_TRY(hipStreamSynchronize(s));
+    return SLA_OK;
+}
+
+template <typename F>
+sla_status dispatch(const sla_ctx *h, F &&f) {
+    if (h->dtype == SLA_F64) {
+        if (h->itype == SLA_I64) return f((double *)nullptr, (int64_t *)nullptr);
+        return f((double *)nullptr, (int32_t *)nullptr);
+    }
+    if (h->itype == SLA_I64) return f((float *)nullptr, (int64_t *)nullptr);
+    return f((float *)nullptr, (int32_t *)nullptr);
+}
+
+}  // namespace
+
+extern "C" {
+
+sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch, int32_t dtype,
+                      int32_t row_ptr_type, const void *d_row_ptr, const int32_t *d_col,
+                      int32_t build_transpose, void *stream) {
+    if (!out) return SLA_ERR_ARG;
+    *out = nullptr;
+    if (n < 1 || n >= ((int64_t)1 << 31) || nnz < n || batch < 1) return SLA_ERR_ARG;
+    if (dtype != SLA_F32 && dtype != SLA_F64) return SLA_ERR_ARG;
+    if (row_ptr_type != SLA_I32 && row_ptr_type != SLA_I64) return SLA_ERR_ARG;
+    if (row_ptr_type == SLA_I32 && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
+    if (build_transpose && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
+    if (!d_row_ptr || !d_col) return SLA_ERR_ARG;
+    sla_ctx *h = new (std::nothrow) sla_ctx();
+    if (!h) return SLA_ERR_NO_MEMORY;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return SLA_ERR_DEVICE;
+    }
+    h->n = n;
+    h->nnz = nnz;
+    h->batch = batch;
+    h->dtype = dtype;
+    h->itype = row_ptr_type;
+    h->rp = d_row_ptr;
+    h->col = d_col;
+    h->G = lanes_for(n, nnz);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    sla_status st = dispatch(h, [&](auto t, auto it) {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        return create_typed<T, IT>(h, build_transpose, s);
+    });
+    if (st != SLA_OK) {
+        if (st == SLA_ERR_DEVICE && g_last_error == hipErrorOutOfMemory) st = SLA_ERR_NO_MEMORY;
+        (void)hipStreamSynchronize(s);
+        release(h);
+        return st;
+    }
+    *out = h;
+    return SLA_OK;
+}
+
+sla_status sla_destroy(sla_handle h) {
+    if (!h) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    release(h);
+    return SLA_OK;
+}
+
+sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void *d_y,
+                      int32_t transpose, void *stream) {
+    if (!h || !d_values || !d_x || !d_y || d_x == d_y) return SLA_ERR_ARG;
+    if (transpose && !h->has_t) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        for (int64_t s0 = 0; s0 < h->batch; s0 += 65535) {
+            const int nb = (int)((h->batch - s0) < 65535 ? (h->batch - s0) : 65535);
+            const T *v = reinterpret_cast<const T *>(d_values) + s0 * h->nnz;
+            const T *x = reinterpret_cast<const T *>(d_x) + s0 * h->n;
+            T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
+            if (transpose)
+                HIP_TRY((launch_spmv_perm<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
+                                                 h->perm, v, h->nnz, x, y, h->n, h->n, nb, s)));
+            else
+                HIP_TRY((launch_spmv<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp), h->col, v,
+                                            h->nnz, x, y, h->n, h->n, nb, s)));
+        }
+        return SLA_OK;
+    });
+}
+
+sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *d_x,
+                     const sla_solve_opts *opts, sla_solve_info *info, void *stream) {
+    if (!h || !d_values || !d_b || !d_x || d_b == d_x) return SLA_ERR_ARG;
+    const sla_solve_opts o = opts ? *opts : default_opts();
+    if (check_opts(o) != SLA_OK) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        Operator op{h->rp, h->col, h->G};
+        return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
+                                reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
+                                info, s);
+    });
+}
+
+sla_status sla_solve_adjoint(sla_handle h, const void *d_values, const void *d_x,
+                             const void *d_grad_x, void *d_grad_values, void *d_grad_b,
+                             const sla_solve_opts *opts, sla_solve_info *info, void *stream) {
+    if (!h || !d_values || !d_x || !d_grad_x || !d_grad_values || !d_grad_b) return SLA_ERR_ARG;
+    if (d_grad_b == d_grad_x || d_grad_b == d_x || d_grad_b == d_values) return SLA_ERR_ARG;
+    const sla_solve_opts o = opts ? *opts : default_opts();
+    if (check_opts(o) != SLA_OK) return SLA_ERR_ARG;
+    if (o.method == SLA_BICGSTAB && !h->has_t) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        return adjoint_all<T, IT>(h, reinterpret_cast<const T *>(d_values),
+                                  reinterpret_cast<const T *>(d_x),
+                                  reinterpret_cast<const T *>(d_grad_x),
+                                  reinterpret_cast<T *>(d_grad_values), reinterpret_cast<T *>(d_grad_b),
+                                  o, info, s);
+    });
+}
+
+sla_status sla_export_pattern(sla_handle h, void *d_diagpos, void *d_row_ptr_t, void *d_col_t,
+                              void *d_perm, void *stream) {
+    if (!h) return SLA_ERR_ARG;
+    if ((d_row_ptr_t || d_col_t || d_perm) && !h->has_t) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t isz = h->itype == SLA_I64 ? 8 : 4;
+    if (d_diagpos)
+        HIP_TRY(hipMemcpyAsync(d_diagpos, h->diagpos, isz * h->n, hipMemcpyDeviceToDevice, s));
+    if (d_row_ptr_t)
+        HIP_TRY(hipMemcpyAsync(d_row_ptr_t, h->rp_t, isz * (h->n + 1), hipMemcpyDeviceToDevice, s));
+    if (d_col_t)
+        HIP_TRY(hipMemcpyAsync(d_col_t, h->col_t, 4 * h->nnz, hipMemcpyDeviceToDevice, s));
+    if (d_perm) HIP_TRY(hipMemcpyAsync(d_perm, h->perm, 4 * h->nnz, hipMemcpyDeviceToDevice, s));
+    return SLA_OK;
+}
+
+int64_t sla_workspace_bytes(sla_handle h) { return h ? h->ws_bytes : -1; }
+
+const char *sla_status_string(int32_t status) {
+    switch (status) {
+        case SLA_OK: return "ok";
+        case SLA_NOT_CONVERGED: return "not converged (maxit reached)";
+        case SLA_BREAKDOWN: return "breakdown (a Krylov denominator vanished)";
+        case SLA_ERR_ARG: return "invalid argument";
+        case SLA_ERR_PATTERN: return "invalid CSR pattern";
+        case SLA_ERR_ZERO_DIAG: return "zero diagonal entry with Jacobi preconditioning";
+        case SLA_ERR_NO_MEMORY: return "device out of memory";
+        case SLA_ERR_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *sla_last_error(void) { return hipGetErrorString(g_last_error); }
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// Sparse matrix-vector products and the single-pass kernels around them.
+//
+// SpMV (torch-sla explainer, Methodology section 1: .matvec of the unified
+// API; the shared-pattern SparseTensor holds a batch of value arrays):
+//   y[s][i] = sum over stored k of row i: values[s][k] * x[s][col[k]].
+// A row is handled by a group of G lanes (G = smallest power of two >= the
+// mean row length): lane l reads entries rp[i]+l, rp[i]+l+G, ..., so one
+// wavefront instruction reads 64/G consecutive rows' entries as one coalesced
+// run, and the G partial sums are combined with cross-lane shuffles.
+// Gradient on the pattern (Methodology section 2, linear systems):
+//   grad[s][k] = -lambda[s][row(k)] * x[s][col(k)].
+#include "sla_internal.h"
+
+namespace sla {
+
+template <int G, typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
+                                                      const int32_t *__restrict__ col,
+                                                      const T *__restrict__ val, int64_t val_stride,
+                                                      const T *__restrict__ x, T *__restrict__ y,
+                                                      int64_t n, int64_t vec_stride) {
+    const int sys = blockIdx.y;
+    val += (int64_t)sys * val_stride;
+    x += (int64_t)sys * vec_stride;
+    y += (int64_t)sys * vec_stride;
+    constexpr int RPP = kBlock / G;
+    const int lane = threadIdx.x & (G - 1);
+    const int grp = threadIdx.x / G;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t base = t * kTileRows;
+        for (int pass = 0; pass < G; ++pass) {
+            const int64_t i = base + pass * RPP + grp;
+            if (i < n) {
+                const IT e = rp[i + 1];
+                T acc = T(0);
+                for (IT k = rp[i] + lane; k < e; k += G) acc += val[k] * x[col[k]];
+                acc = group_sum<G>(acc);
+                if (lane == 0) y[i] = acc;
+            }
+        }
+    }
+}
+
+// y = A^T x through the transpose map: rp/col describe A^T and the value of
+// A^T entry kt is val[perm[kt]].
+template <int G, typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
+    const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ perm,
+    const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
+    int64_t n, int64_t vec_stride) {
+    const int sys = blockIdx.y;
+    val += (int64_t)sys * val_stride;
+    x += (int64_t)sys * vec_stride;
+    y += (int64_t)sys * vec_stride;
+    constexpr int RPP = kBlock / G;
+    const int lane = threadIdx.x & (G - 1);
+    const int grp = threadIdx.x / G;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t base = t * kTileRows;
+        for (int pass = 0; pass < G; ++pass) {
+            const int64_t i = base + pass * RPP + grp;
+            if (i < n) {
+                const IT e = rp[i + 1];
+                T acc = T(0);
+                for (IT k = rp[i] + lane; k < e; k += G) acc += val[perm[k]] * x[col[k]];
+                acc = group_sum<G>(acc);
+                if (lane == 0) y[i] = acc;
+            }
+        }
+    }
+}
+
+template <int G, typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
+                                                      const int32_t *__restrict__ col,
+                                                      const T *__restrict__ lam,
+                                                      const T *__restrict__ x, T *__restrict__ grad,
+                                                      int64_t n, int64_t nnz) {
+    const int sys = blockIdx.y;
+    lam += (int64_t)sys * n;
+    x += (int64_t)sys * n;
+    grad += (int64_t)sys * nnz;
+    constexpr int RPP = kBlock / G;
+    const int lane = threadIdx.x & (G - 1);
+    const int grp = threadIdx.x / G;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t base = t * kTileRows;
+        for (int pass = 0; pass < G; ++pass) {
+            const int64_t i = base + pass * RPP + grp;
+            if (i < n) {
+                const T li = lam[i];
+                const IT e = rp[i + 1];
+                for (IT k = rp[i] + lane; k < e; k += G) grad[k] = -(li * x[col[k]]);
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restrict__ perm,
+                                                        const T *__restrict__ val,
+                                                        T *__restrict__ out, int64_t nnz) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride)
+        out[k] = val[perm[k]];
+}
+
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void dinv_kernel(const IT *__restrict__ diagpos,
+                                                      const T *__restrict__ val,
+                                                      T *__restrict__ dinv, int64_t n,
+                                                      SolveState *st) {
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    int bad = 0;
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i < n) {
+            const T d = val[diagpos[i]];
+            bad |= (d == T(0));
+            dinv[i] = T(1) / d;
+        }
+    }
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(&st->zero_diag, 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T *x, int64_t n) {
+    if (!st->zero_x) return;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) x[i] = T(0);
+}
+
+// ------------------------------------------------------------------ launchers
+
+#define SLA_DISPATCH_G(G, ...)                      \
+    switch (G) {                                    \
+        case 2: { constexpr int kG = 2; __VA_ARGS__; } break;   \
+        case 4: { constexpr int kG = 4; __VA_ARGS__; } break;   \
+        case 8: { constexpr int kG = 8; __VA_ARGS__; } break;   \
+        case 16: { constexpr int kG = 16; __VA_ARGS__; } break; \
+        case 32: { constexpr int kG = 32; __VA_ARGS__; } break; \
+        default: { constexpr int kG = 64; __VA_ARGS__; } break; \
+    }
+
+template <typename T, typename IT>
+hipError_t launch_spmv(int G, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
+                       const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
+                       hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    SLA_DISPATCH_G(G, spmv_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(rp, col, val, val_stride, x,
+                                                                     y, n, vec_stride));
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_spmv_perm(int G, const IT *rp, const int32_t *col, const int32_t *perm,
+                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
+                            int64_t vec_stride, int batch, hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    SLA_DISPATCH_G(G, spmv_perm_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(
+                          rp, col, perm, val, val_stride, x, y, n, vec_stride));
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_grad(int G, const IT *rp, const int32_t *col, const T *lam, const T *x,
+                       T *grad, int64_t n, int64_t nnz, int batch, hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    SLA_DISPATCH_G(G, grad_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n,
+                                                                     nnz));
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s) {
+    int64_t blocks = (nnz + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    gather_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(perm, val, out, nnz);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
+                       hipStream_t s) {
+    dinv_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(diagpos, val, dinv, n, st);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    zero_if_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(st, x, n);
+    return hipGetLastError();
+}
+
+#define SLA_INST(T, IT)                                                                         \
+    template hipError_t launch_spmv<T, IT>(int, const IT *, const int32_t *, const T *, int64_t, \
+                                           const T *, T *, int64_t, int64_t, int, hipStream_t);  \
+    template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const int32_t *,               \
+                                                const int32_t *, const T *, int64_t, const T *,  \
+                                                T *, int64_t, int64_t, int, hipStream_t);        \
+    template hipError_t launch_grad<T, IT>(int, const IT *, const int32_t *, const T *,         \
+                                           const T *, T *, int64_t, int64_t, int, hipStream_t);  \
+    template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
+                                           hipStream_t);
+
+SLA_INST(float, int32_t)
+SLA_INST(float, int64_t)
+SLA_INST(double, int32_t)
+SLA_INST(double, int64_t)
+template hipError_t launch_gather<float>(const int32_t *, const float *, float *, int64_t,
+                                         hipStream_t);
+template hipError_t launch_gather<double>(const int32_t *, const double *, double *, int64_t,
+                                          hipStream_t);
+template hipError_t launch_zero_if<float>(const SolveState *, float *, int64_t, hipStream_t);
+template hipError_t launch_zero_if<double>(const SolveState *, double *, int64_t, hipStream_t);
+
+}  // namespace sla

@@ -1,0 +1,158 @@
+// Pattern set-up, once per sla_create.
+//
+// Validation: row_ptr[0] = 0, non-decreasing, row_ptr[n] = nnz; columns in
+// range, strictly ascending per row; the diagonal stored (its position is
+// kept in diagpos for the Jacobi preconditioner -- the native backend's only
+// preconditioner per the torch-sla explainer's Significance section).
+//
+// Transpose map (needed by the adjoint solve with A^T, Methodology section 2,
+// linear systems): a stable LSD radix sort of (col[k], k) by column gives
+// perm[kt] = k in column-major order with rows ascending inside each column,
+// so row kt of A^T is sorted; col_t[kt] = row(perm[kt]); row_ptr_t[c] is the
+// first kt whose key is >= c, found from the sorted keys without atomics.
+#include <hipcub/hipcub.hpp>
+
+#include "sla_internal.h"
+
+namespace sla {
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restrict__ rp, int64_t n,
+                                                              int64_t nnz, int32_t *flag) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const IT a = rp[i], b = rp[i + 1];
+        if (b < a) bad = 1;
+        if (i == 0 && a != 0) bad = 1;
+        if (i == n - 1 && (int64_t)b != nnz) bad = 1;
+    }
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void check_cols_kernel(const IT *__restrict__ rp,
+                                                            const int32_t *__restrict__ col,
+                                                            int64_t n, IT *__restrict__ diagpos,
+                                                            int32_t *flag) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const IT e = rp[i + 1];
+        int64_t prev = -1;
+        IT dpos = -1;
+        for (IT k = rp[i]; k < e; ++k) {
+            const int64_t c = col[k];
+            if (c < 0 || c >= n || c <= prev) bad = 1;
+            if (c == i) dpos = k;
+            prev = c;
+        }
+        if (dpos < 0) bad = 1;
+        diagpos[i] = dpos;
+    }
+    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+}
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void row_index_kernel(const IT *__restrict__ rp, int64_t n,
+                                                           int32_t *__restrict__ rowidx) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        for (IT k = rp[i]; k < rp[i + 1]; ++k) rowidx[k] = (int32_t)i;
+}
+
+__global__ __launch_bounds__(kBlock) void iota_kernel(int32_t *a, int64_t m) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride)
+        a[k] = (int32_t)k;
+}
+
+__global__ __launch_bounds__(kBlock) void col_t_kernel(const int32_t *__restrict__ perm,
+                                                       const int32_t *__restrict__ rowidx,
+                                                       int32_t *__restrict__ col_t, int64_t m) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride)
+        col_t[k] = rowidx[perm[k]];
+}
+
+// rp_t[c] = first position whose sorted key is >= c, for c in [0, n]
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void rowptr_t_kernel(const int32_t *__restrict__ keys,
+                                                          int64_t m, int64_t n, IT *__restrict__ rp_t) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k <= m; k += stride) {
+        const int64_t lo = (k == 0) ? -1 : (int64_t)keys[k - 1];
+        const int64_t hi = (k == m) ? n : (int64_t)keys[k];
+        for (int64_t c = lo + 1; c <= hi; ++c) rp_t[c] = (IT)k;
+    }
+}
+
+static unsigned blocks_for(int64_t m) {
+    int64_t b = (m + kBlock - 1) / kBlock;
+    if (b > 65536) b = 65536;
+    if (b < 1) b = 1;
+    return (unsigned)b;
+}
+
+template <typename IT>
+hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
+                          int32_t *flag, hipStream_t s) {
+    int32_t h = 0;
+    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
+    if (e != hipSuccess) return e;
+    check_rowptr_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, nnz, flag);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(&h, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    if (h) return hipSuccess;  // flag stays set: row_ptr invalid, columns not read
+    check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
+    return hipGetLastError();
+}
+
+template <typename IT>
+hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
+                           int32_t *col_t, int32_t *perm, hipStream_t s) {
+    int32_t *keys_out = nullptr, *vals_in = nullptr, *rowidx = nullptr;
+    void *temp = nullptr;
+    size_t temp_bytes = 0;
+    int end_bit = 1;
+    while (end_bit < 32 && ((int64_t)1 << end_bit) < n) ++end_bit;
+    const int m = (int)nnz;
+    hipError_t e = hipSuccess;
+    do {
+        if ((e = hipMalloc(&keys_out, sizeof(int32_t) * nnz)) != hipSuccess) break;
+        if ((e = hipMalloc(&vals_in, sizeof(int32_t) * nnz)) != hipSuccess) break;
+        if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) break;
+        iota_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(vals_in, nnz);
+        row_index_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        e = hipcub::DeviceRadixSort::SortPairs(nullptr, temp_bytes, col, keys_out, vals_in, perm,
+                                               m, 0, end_bit, s);
+        if (e != hipSuccess) break;
+        if ((e = hipMalloc(&temp, temp_bytes > 0 ? temp_bytes : 1)) != hipSuccess) break;
+        e = hipcub::DeviceRadixSort::SortPairs(temp, temp_bytes, col, keys_out, vals_in, perm, m,
+                                               0, end_bit, s);
+        if (e != hipSuccess) break;
+        col_t_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(perm, rowidx, col_t, nnz);
+        rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kBlock, 0, s>>>(keys_out, nnz, n, rp_t);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        e = hipStreamSynchronize(s);
+    } while (0);
+    (void)hipFree(keys_out);
+    (void)hipFree(vals_in);
+    (void)hipFree(rowidx);
+    (void)hipFree(temp);
+    return e;
+}
+
+template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
+                                            int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
+                                            int64_t *, int32_t *, hipStream_t);
+template hipError_t setup_transpose<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
+                                             int32_t *, int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_transpose<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
+                                             int64_t *, int32_t *, int32_t *, hipStream_t);
+
+}  // namespace sla

@@ -1,0 +1,246 @@
+// Internal declarations of the gfx950 sparse-solve library.
+//
+// Layout in HBM: values [batch][nnz] (caller's, CSR order), vectors
+// [batch][n]; every grid kernel walks rows in tiles of kTileRows and maps
+// tiles to XCDs in contiguous ranges so that one XCD's L2 sees one slab of
+// the matrix and the neighbouring vector entries it gathers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sla.h"
+
+namespace sla {
+
+constexpr int kBlock = 256;        // threads per block of the grid kernels
+constexpr int kWaves = kBlock / 64;
+constexpr int kTileRows = 256;     // rows per tile (one row per thread in
+                                   // element-wise kernels)
+constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, 32 CUs each
+constexpr int kMaxBlocksPerXcd = 256;  // 8 resident blocks per CU
+constexpr int kMaxGrid = kNumXcd * kMaxBlocksPerXcd;
+constexpr int kMaxRed = 4;         // reduction values per kernel
+constexpr int kBlockSolveThreads = 1024;
+constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread
+
+// Per-system solver state, device resident.  Written only by the last block
+// of a kernel (ticket order) and read by later kernels.
+struct SolveState {
+    double rho;      // CG: r.z ; BiCGStab: rhat.r of the current iteration
+    double alpha, beta, omega;
+    double bb;       // ||rhs||^2
+    double rr;       // ||r||^2 after the last update
+    double ss;       // BiCGStab ||s||^2
+    double aux;      // last denominator (p.q or rhat.v)
+    int32_t iter;    // completed iterations
+    int32_t done;    // 1 once converged / stopped
+    int32_t status;  // sla_status of the system
+    int32_t half;    // BiCGStab: half-step exit pending
+    int32_t spmv;    // products with the operator
+    int32_t zero_diag;
+    int32_t zero_x;  // rhs == 0 with a user initial guess: x must become 0
+    uint32_t ticket; // arrivals of the running kernel's blocks
+    int32_t nfused;  // launches of the fused SpMV kernels that did work
+    int32_t pad;
+};
+
+// Device-resident arguments of the iteration kernels.  Kernels take a pointer
+// to this block, so a captured HIP graph stays valid across calls while the
+// host rewrites the pointers before each solve.
+template <typename T, typename IT>
+struct IterArgs {
+    const T *val;
+    const IT *rp;
+    const int32_t *col;
+    T *x;
+    const T *b;
+    const T *dinv;
+    T *r, *z, *q, *rh, *s, *t;
+    T *p[2];
+    T *v[2];
+    SolveState *st;
+    double *part;   // [kMaxRed][kMaxGrid]
+    int64_t n;
+    double tol;
+    int32_t maxit;
+    int32_t use_x0;
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int G, typename A>
+__device__ __forceinline__ A group_sum(A v) {
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, G);
+    return v;
+}
+
+// Contiguous tile range of this block's XCD, strided over the XCD's blocks.
+// Requires gridDim.x to be a multiple of kNumXcd.
+struct TileRange {
+    int64_t first, end, stride;
+};
+
+__device__ __forceinline__ TileRange xcd_tiles(int64_t ntiles) {
+    const int b = blockIdx.x;
+    const int xcd = b % kNumXcd;
+    const int local = b / kNumXcd;
+    const int per = gridDim.x / kNumXcd;
+    const int64_t chunk = (ntiles + kNumXcd - 1) / kNumXcd;
+    const int64_t lo = (int64_t)xcd * chunk;
+    int64_t hi = lo + chunk;
+    if (hi > ntiles) hi = ntiles;
+    TileRange tr;
+    tr.first = lo + local;
+    tr.end = hi;
+    tr.stride = per;
+    return tr;
+}
+
+// Reduce NR per-thread values over the grid.  Every block stores its block
+// sums in part[r][blockIdx.x]; the last block to arrive (ticket order) adds
+// the partials in block-index order, so the totals are bitwise reproducible.
+// Returns true in every thread of the last block, with tot[] filled.
+template <int NR>
+__device__ __forceinline__ bool grid_reduce(double (&v)[NR], double *part, uint32_t *ticket,
+                                            double (&tot)[NR]) {
+    __shared__ double red[NR][kWaves];
+    __shared__ int last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        double w = wave_sum(v[r]);
+        if (lane == 0) red[r][wave] = w;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            double s = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) s += red[r][w];
+            __hip_atomic_store(&part[r * kMaxGrid + blockIdx.x], s, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        last = (t == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (!last) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every block's partials
+    const int nb = gridDim.x;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        double s = 0.0;
+        for (int j = threadIdx.x; j < nb; j += kBlock)
+            s += __hip_atomic_load(&part[r * kMaxGrid + j], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        s = wave_sum(s);
+        __syncthreads();
+        if (lane == 0) red[r][wave] = s;
+        __syncthreads();
+        double acc = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) acc += red[r][w];
+        tot[r] = acc;
+    }
+    if (threadIdx.x == 0) *ticket = 0u;
+    return true;
+}
+
+// Grid size for a tile count: a multiple of kNumXcd, at most kMaxGrid.
+inline int grid_for_tiles(int64_t ntiles) {
+    int64_t per = (ntiles + kNumXcd - 1) / kNumXcd;
+    if (per > kMaxBlocksPerXcd) per = kMaxBlocksPerXcd;
+    if (per < 1) per = 1;
+    return (int)(per * kNumXcd);
+}
+
+__host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
+
+// Lanes per row from the mean row length: the smallest power of two >= mean,
+// in [2, 64].
+inline int lanes_for(int64_t n, int64_t nnz) {
+    const double mean = n > 0 ? (double)nnz / (double)n : 1.0;
+    int g = 2;
+    while (g < 64 && g < mean) g <<= 1;
+    return g;
+}
+
+// ---------------------------------------------------------------- launchers
+// (defined in the .hip files; all return hipError_t of the launch)
+
+template <typename T, typename IT>
+hipError_t launch_spmv(int G, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
+                       const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
+                       hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_spmv_perm(int G, const IT *rp, const int32_t *col, const int32_t *perm,
+                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
+                            int64_t vec_stride, int batch, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_grad(int G, const IT *rp, const int32_t *col, const T *lam, const T *x,
+                       T *grad, int64_t n, int64_t nnz, int batch, hipStream_t s);
+template <typename T>
+hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
+                       hipStream_t s);
+
+// CG (grid path, one system)
+template <typename T, typename IT>
+hipError_t launch_cg_init(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_cg_spmv(int G, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_cg_update(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+
+// BiCGStab (grid path, one system)
+template <typename T, typename IT>
+hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_bicg_pv(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_bicg_st(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+
+// shared by both grid solvers: x = 0 when the state asks for it
+template <typename T>
+hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s);
+
+// CG, one workgroup per system (n <= kBlockSolveMaxN)
+struct BlockCgParams {
+    const void *val;
+    const void *rp;
+    const int32_t *col;
+    const void *diagpos;
+    void *x;
+    const void *b;
+    SolveState *st;
+    int64_t n, nnz;
+    double tol;
+    int32_t maxit;
+    int32_t use_x0;
+    int32_t jac;
+};
+template <typename T, typename IT>
+hipError_t launch_block_cg(int G, const BlockCgParams &p, int batch, hipStream_t s);
+
+// pattern setup
+template <typename IT>
+hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
+                          int32_t *flag, hipStream_t s);
+template <typename IT>
+hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
+                           int32_t *col_t, int32_t *perm, hipStream_t s);
+
+}  // namespace sla

@@ -1,0 +1,175 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) differentiable sparse linear solve.
+ *
+ * The operation (torch-sla explainer pages, gist.science, "Technical summary"):
+ *   forward   x = A^-1 b for a CSR matrix A, by Jacobi-preconditioned CG (SPD A)
+ *             or BiCGStab (nonsymmetric A) -- Methodology section 1 names the
+ *             iterative solvers, the Significance section the Jacobi
+ *             preconditioner of the native backend;
+ *   backward  one adjoint solve A^T lambda = dL/dx, then dL/db = lambda and
+ *             dL/dA_ij = -lambda_i x_j on the stored pattern only --
+ *             Methodology section 2, linear systems; memory stays O(n + nnz)
+ *             whatever the iteration count (same section, complexity bullet);
+ *   batching  one pattern shared by a batch of value arrays (Methodology
+ *             section 1, "SparseTensor: single matrix / shared pattern").
+ *
+ * Conventions shared by every call
+ *   - All d_* pointers are device pointers on the current HIP device.  Arrays
+ *     are dense and contiguous, system-major: values [batch][nnz] in CSR order,
+ *     vectors [batch][n].  The float type (SLA_F32 / SLA_F64) is fixed at
+ *     sla_create and applies to every value and vector argument.
+ *   - row_ptr is int32 or int64 (fixed at create); col is always int32.  The
+ *     pattern must have row_ptr[0] = 0, non-decreasing row_ptr,
+ *     row_ptr[n] = nnz, columns in [0, n) strictly ascending in each row, and
+ *     every diagonal entry stored.
+ *   - The pattern arrays are BORROWED: the caller keeps d_row_ptr and d_col
+ *     alive and unchanged until sla_destroy.  The handle owns everything it
+ *     derives (diagonal index, transpose map, solver workspace); nothing is
+ *     allocated after sla_create and nothing grows with the iteration count.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it.  sla_solve and sla_solve_adjoint return after the solve has
+ *     finished (they poll a device-resident convergence flag and read the
+ *     per-system results); sla_matvec returns without synchronizing.
+ *   - One handle serves one stream at a time; calls on a handle must not
+ *     overlap.  Different handles are independent.
+ *   - Errors are returned, never thrown or aborted across the ABI.  Argument
+ *     and pattern errors are detected before any solver kernel is launched.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sla_ctx *sla_handle;
+
+enum { SLA_F32 = 0, SLA_F64 = 1 };                 /* value / vector type   */
+enum { SLA_I32 = 0, SLA_I64 = 1 };                 /* row_ptr index type    */
+enum { SLA_CG = 0, SLA_BICGSTAB = 1 };             /* Krylov method         */
+enum { SLA_PRECOND_NONE = 0, SLA_PRECOND_JACOBI = 1 };
+
+typedef enum {
+    SLA_OK = 0,
+    SLA_NOT_CONVERGED = 1,  /* maxit reached: x holds the maxit-th iterate  */
+    SLA_BREAKDOWN = 2,      /* CG: p.Ap <= 0; BiCGStab: rhat.r, rhat.v, t.t
+                               or t.s vanished; x holds the last iterate    */
+    SLA_ERR_ARG = -1,       /* bad argument (NULL, size, type, option)      */
+    SLA_ERR_PATTERN = -2,   /* invalid CSR pattern (see conventions)        */
+    SLA_ERR_ZERO_DIAG = -3, /* Jacobi requested and some A_ii == 0          */
+    SLA_ERR_NO_MEMORY = -4, /* device allocation failed at sla_create       */
+    SLA_ERR_DEVICE = -5     /* a HIP runtime call failed                    */
+} sla_status;
+
+/* Solver options.  Pass NULL for the defaults in brackets. */
+typedef struct {
+    double tol;          /* stop when ||r_k||_2 <= tol * ||rhs||_2 [1e-10]     */
+    int32_t maxit;       /* iteration cap (>= 0) [1000]                        */
+    int32_t method;      /* SLA_CG or SLA_BICGSTAB [SLA_CG]                    */
+    int32_t precond;     /* SLA_PRECOND_JACOBI or _NONE [JACOBI]; BiCGStab
+                            supports NONE only                                  */
+    int32_t use_x0;      /* 1: d_x holds the initial guess; 0: start at 0 [0]  */
+    int32_t graph_chunk; /* iterations per captured HIP graph replay for large
+                            systems: 0 = default, < 0 = launch kernels directly */
+    int32_t profile;     /* 1: no graph; time every launch of the fused SpMV
+                            kernel with HIP events on `stream` (slower)       */
+} sla_solve_opts;
+
+/*
+ * Per-call results.  The array members are HOST arrays of `batch` entries
+ * (each may be NULL); the scalar members are filled in always.
+ */
+typedef struct {
+    int32_t *iters;   /* iterations done per system (BiCGStab: started
+                         iterations, a half-step exit counts as one)           */
+    int32_t *spmv;    /* products with A (or A^T) per system                   */
+    double *relres;   /* recurrence residual ||r||/||rhs|| per system          */
+    int32_t *status;  /* sla_status per system                                  */
+    double kernel_ms;        /* profile mode: summed duration of the fused
+                                SpMV kernel launches (ms), else 0              */
+    int64_t kernel_launches; /* profile mode: number of those launches         */
+} sla_solve_info;
+
+/*
+ * sla_create -- validate a CSR pattern and build its derived structures.
+ *   n, nnz      matrix order and stored entries (n >= 1, nnz >= n; n < 2^31;
+ *               nnz < 2^31 with SLA_I32 row_ptr)
+ *   batch       number of value arrays / systems served by one call (>= 1)
+ *   dtype       SLA_F32 or SLA_F64;  row_ptr_type  SLA_I32 or SLA_I64
+ *   d_row_ptr   [n+1] device array of row_ptr_type (borrowed)
+ *   d_col       [nnz] device int32 column indices (borrowed)
+ *   build_transpose  1: build the map of A^T (needed by sla_matvec with
+ *               transpose = 1 and by the BiCGStab adjoint); requires
+ *               nnz < 2^31
+ * Checks the pattern on the device (synchronizes `stream`).  Returns
+ * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
+ */
+sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch,
+                      int32_t dtype, int32_t row_ptr_type, const void *d_row_ptr,
+                      const int32_t *d_col, int32_t build_transpose,
+                      void *stream);
+
+/* Release everything the handle owns (synchronizes the device). */
+sla_status sla_destroy(sla_handle h);
+
+/*
+ * sla_matvec -- y[s] = A_s x[s] (transpose = 0) or A_s^T x[s] (transpose = 1)
+ * for every system s of the batch.  d_values [batch][nnz], d_x and d_y
+ * [batch][n]; d_y must not alias d_x.  Asynchronous on `stream`.
+ */
+sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x,
+                      void *d_y, int32_t transpose, void *stream);
+
+/*
+ * sla_solve -- forward solve A_s x[s] = b[s] for every system.
+ *   d_values [batch][nnz]; d_b [batch][n]; d_x [batch][n] output (input
+ *   initial guess when opts->use_x0).  Per-system stopping: a converged system
+ *   is frozen while the others continue.  Returns the most severe per-system
+ *   status (errors < 0 first, then BREAKDOWN, then NOT_CONVERGED).
+ */
+sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b,
+                     void *d_x, const sla_solve_opts *opts,
+                     sla_solve_info *info, void *stream);
+
+/*
+ * sla_solve_adjoint -- backward pass of x = A^-1 b for dL/dx = d_grad_x.
+ *   Solves A_s^T lambda = grad_x[s] from lambda = 0 with the same method
+ *   (CG uses A itself, which it presumes symmetric; BiCGStab uses the
+ *   transpose map, so the handle needs build_transpose = 1), tol relative to
+ *   ||grad_x[s]||.  Writes d_grad_b [batch][n] = lambda and
+ *   d_grad_values [batch][nnz] = -lambda[row(k)] * x[col(k)] for every stored
+ *   entry k (one gradient per stored entry, no symmetrisation).
+ *   d_x is the forward solution.  d_grad_b must not alias any input.
+ */
+sla_status sla_solve_adjoint(sla_handle h, const void *d_values,
+                             const void *d_x, const void *d_grad_x,
+                             void *d_grad_values, void *d_grad_b,
+                             const sla_solve_opts *opts, sla_solve_info *info,
+                             void *stream);
+
+/*
+ * sla_export_pattern -- copy the derived pattern structures into caller
+ * device buffers (any pointer may be NULL): d_diagpos [n] (row_ptr type),
+ * and, if the transpose was built, d_row_ptr_t [n+1] (row_ptr type),
+ * d_col_t [nnz] int32 (row of each A^T entry) and d_perm [nnz] int32 (A's
+ * position of each A^T entry).  Asynchronous on `stream`.
+ */
+sla_status sla_export_pattern(sla_handle h, void *d_diagpos, void *d_row_ptr_t,
+                              void *d_col_t, void *d_perm, void *stream);
+
+/* Device bytes owned by the handle (constant after sla_create). */
+int64_t sla_workspace_bytes(sla_handle h);
+
+/* Static description of a status code. */
+const char *sla_status_string(int32_t status);
+
+/* Text of the last HIP runtime error seen by this thread (after SLA_ERR_DEVICE). */
+const char *sla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

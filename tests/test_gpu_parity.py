@@ -1,0 +1,376 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on the same
+seeded inputs.
+
+Bars (fp64 / fp32): SpMV componentwise |dy_i| <= tol * sum_j |A_ij||x_j| with
+tol 1e-12 / 1e-5; converged solves and gradients relative L2 <= 1e-7 / 1e-3
+when both sides reach ||r||/||b|| <= tol.  Integer set-up outputs (diagonal
+index, transpose map) are compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_helpers import (FP_TOL, banner, gpu_forward_adjoint, oracle_forward_adjoint, relerr,
+                         spmv_bound, tdtype, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ set-up
+
+@pytest.mark.parametrize("case", ["convdiff_64", "random_nonsym_300", "powerlaw_5000", "poisson_i64"])
+def test_pattern_setup_bit_exact(hip, case):
+    banner(f"setup {case}")
+    if case == "convdiff_64":
+        p = W.config(4, size=64)
+        rp, col = p.row_ptr, p.col
+    elif case == "random_nonsym_300":
+        rp, col, _ = W.random_csr(300, 0.05, 3)
+    elif case == "powerlaw_5000":
+        rp, col, _ = W.powerlaw_graph_laplacian(5000, 4)
+    else:
+        p = W.config(5, size=9)
+        rp, col = p.row_ptr, p.col
+    n = rp.shape[0] - 1
+    st, dp = O.check_pattern(n, rp, col)
+    assert st == O.OK
+    rpt, ct, perm = O.transpose(n, rp, col)
+    drp = torch.from_numpy(rp).cuda()
+    dcol = torch.from_numpy(col).cuda()
+    pat = hip.Pattern(drp, dcol, batch=1, dtype=torch.float64, build_transpose=True)
+    g_dp, g_rpt, g_ct, g_perm = pat.export_pattern()
+    torch.cuda.synchronize()
+    assert np.array_equal(g_dp.cpu().numpy().astype(np.int64), dp)
+    assert np.array_equal(g_rpt.cpu().numpy().astype(np.int64), rpt)
+    assert np.array_equal(g_ct.cpu().numpy(), ct)
+    assert np.array_equal(g_perm.cpu().numpy().astype(np.int64), perm)
+
+
+def test_invalid_patterns_rejected(hip):
+    banner("invalid patterns")
+    rp, col, _ = W.laplacian_2d(6)
+    n = 36
+    cases = []
+    bad = col.copy(); bad[1], bad[2] = bad[2], bad[1]; cases.append((rp, bad))
+    bad = col.copy(); bad[-1] = n; cases.append((rp, bad))
+    bad = col.copy(); bad[1] = bad[0]; cases.append((rp, bad))
+    rp2 = rp.copy(); rp2[5] = rp2[6] + 1; cases.append((rp2, col))
+    rp3 = rp.copy(); rp3[0] = 1; cases.append((rp3, col))
+    cases.append((np.array([0, 1, 2], dtype=np.int32), np.array([1, 0], dtype=np.int32)))
+    for r, c in cases:
+        assert O.check_pattern(r.shape[0] - 1, r, c)[0] == O.ERR_PATTERN
+        with pytest.raises(hip.SlaError) as ei:
+            hip.Pattern(torch.from_numpy(r).cuda(), torch.from_numpy(c).cuda())
+        assert ei.value.status == hip.SLA_ERR_PATTERN
+
+
+# ------------------------------------------------------------------ SpMV
+
+def _spmv_case(hip, p, transpose=False):
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p), build_transpose=transpose)
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)
+    y = pat.matvec(d["val"], torch.from_numpy(x).cuda(), transpose=transpose).cpu().numpy()
+    tol = FP_TOL[p.values.dtype]["spmv"]
+    if transpose:
+        rpt, ct, perm = O.transpose(p.n, p.row_ptr, p.col)
+    for s in range(p.batch):
+        if transpose:
+            vt = p.values[s].astype(np.float64)[perm]
+            ref = O.spmv(rpt, ct, vt, x[s].astype(np.float64))
+            bound = tol * O.spmv(rpt, ct, np.abs(vt), np.abs(x[s].astype(np.float64))) + 1e-300
+        else:
+            ref = O.spmv(p.row_ptr, p.col, p.values[s].astype(np.float64), x[s].astype(np.float64))
+            bound = spmv_bound(p, x[s], s, tol)
+        err = np.abs(y[s].astype(np.float64) - ref)
+        assert np.all(err <= bound), f"{p.name} sys {s}: worst {np.max(err / bound)}"
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_spmv_full_configs(hip, k):
+    banner(f"spmv config {k}")
+    _spmv_case(hip, W.config(k), transpose=(k == 4))
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_spmv_batched_shared_pattern(hip, dtype):
+    banner(f"spmv batched {np.dtype(dtype).name}")
+    _spmv_case(hip, W.config(3, dtype=dtype))
+
+
+@pytest.mark.parametrize("size", [1, 3, 7, 17])
+def test_spmv_ragged_and_tiny(hip, size):
+    banner(f"spmv ragged {size}")
+    _spmv_case(hip, W.config(2, size=size), transpose=True)
+
+
+def test_spmv_long_rows_powerlaw(hip):
+    banner("spmv powerlaw")
+    rp, col, val = W.powerlaw_graph_laplacian(60000, 9)
+    p = W.Problem("powerlaw", 60000, rp, col, val, np.zeros((1, 60000)), np.zeros((1, 60000)))
+    _spmv_case(hip, p, transpose=True)
+
+
+def test_spmv_int64_row_ptr(hip):
+    banner("spmv int64")
+    p = W.config(5, size=40)
+    _spmv_case(hip, p)
+
+
+# ------------------------------------------------------------------ solves
+
+def _check_solve(p, g, r, a, systems=None):
+    systems = list(range(p.batch)) if systems is None else list(systems)
+    tol = FP_TOL[p.values.dtype]["sol"]
+    for j, s in enumerate(systems):
+        assert g["info"]["status"][s] == 0 and r.status[j] == 0, (p.name, s)
+        assert g["ainfo"]["status"][s] == 0 and a.status[j] == 0, (p.name, s)
+        ex = relerr(g["x"][s], r.x[j])
+        egv = relerr(g["gv"][s], a.grad_values[j])
+        egb = relerr(g["gb"][s], a.grad_b[j])
+        assert ex <= tol and egv <= tol and egb <= tol, (p.name, s, ex, egv, egb)
+        # iteration counts agree up to reduction-order effects
+        assert abs(int(g["info"]["iters"][s]) - int(r.iters[j])) <= max(3, r.iters[j] // 50)
+
+
+@pytest.mark.parametrize("case", ["cfg1", "cfg1_grid", "cfg2_20", "cfg2_31_ragged", "cfg3_small64",
+                                  "cfg3_small32", "cfg4_48", "cfg4_33_ragged"])
+def test_solve_and_adjoint_small(hip, case):
+    banner(f"solve {case}")
+    kw = {}
+    if case == "cfg1":
+        p = W.config(1)
+    elif case == "cfg1_grid":
+        p = W.config(1)
+        kw["profile"] = True   # forces the grid kernels on a small system
+    elif case == "cfg2_20":
+        p = W.config(2, size=20)
+    elif case == "cfg2_31_ragged":
+        p = W.config(2, size=31)
+    elif case == "cfg3_small64":
+        p = W.config(3, size=20, batch=16)
+    elif case == "cfg3_small32":
+        p = W.config(3, size=20, batch=16, dtype=np.float32)
+    elif case == "cfg4_48":
+        p = W.config(4, size=48)
+    else:
+        p = W.config(4, size=33)
+    g = gpu_forward_adjoint(hip, p, **kw)
+    r, a = oracle_forward_adjoint(p)
+    _check_solve(p, g, r, a)
+
+
+def test_solve_config2_full(hip):
+    banner("solve config 2 full")
+    p = W.config(2)
+    g = gpu_forward_adjoint(hip, p)
+    r, a = oracle_forward_adjoint(p)
+    _check_solve(p, g, r, a)
+    tr = O.true_relres(p.row_ptr, p.col, p.values, g["x"], p.b)
+    assert tr[0] <= 10 * p.tol
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_solve_config3_full_batch(hip, dtype):
+    banner(f"solve config 3 full {np.dtype(dtype).name}")
+    p = W.config(3, dtype=dtype)
+    g = gpu_forward_adjoint(hip, p)
+    sample = list(range(0, p.batch, 32)) + [p.batch - 1]
+    r, a = oracle_forward_adjoint(p, systems=sample)
+    gs = dict(g)
+    _check_solve(p, gs, r, a, systems=sample)
+    # every system: converged, and the oracle's true residual confirms it
+    assert np.all(g["info"]["status"] == 0) and np.all(g["ainfo"]["status"] == 0)
+    tr = O.true_relres(p.row_ptr, p.col, p.values.astype(np.float64), g["x"].astype(np.float64),
+                       p.b.astype(np.float64))
+    limit = 10 * p.tol if dtype == np.float64 else 1e-3
+    assert np.all(tr <= limit), float(tr.max())
+
+
+def test_solve_config4_full(hip):
+    banner("solve config 4 full")
+    p = W.config(4)
+    g = gpu_forward_adjoint(hip, p)
+    r, a = oracle_forward_adjoint(p)
+    _check_solve(p, g, r, a)
+    assert g["info"]["iters"][0] < p.maxit
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_fixed_iteration_count_matches_oracle_iterates(hip):
+    banner("fixed iterations")
+    for p, path in ((W.config(2, size=24), {}), (W.config(1), {}), (W.config(1), {"profile": True}),
+                    (W.config(4, size=40), {})):
+        for k in (1, 2, 7):
+            g = gpu_forward_adjoint(hip, p, maxit=k, **path)
+            r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, p.tol, k)
+            assert g["info"]["status"][0] == hip.SLA_NOT_CONVERGED and r.status[0] == O.NOT_CONVERGED
+            assert g["info"]["iters"][0] == k == r.iters[0]
+            assert relerr(g["x"][0], r.x[0]) <= 1e-12, (p.name, k, path)
+            assert abs(g["info"]["relres"][0] - r.relres[0]) <= 1e-10 * r.relres[0]
+
+
+def test_zero_rhs_and_zero_maxit(hip):
+    banner("zero rhs / maxit 0")
+    for p in (W.config(1), W.config(2, size=12), W.config(4, size=16)):
+        d = to_dev(p)
+        pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+        for kw in ({}, {"profile": True}):
+            x, info = pat.solve(d["val"], torch.zeros_like(d["b"]), method=p.method,
+                                precond=p.precond, **kw)
+            assert info["status"][0] == 0 and info["iters"][0] == 0
+            assert not torch.any(x)
+            x0 = torch.ones_like(d["b"])
+            x, info = pat.solve(d["val"], torch.zeros_like(d["b"]), method=p.method,
+                                precond=p.precond, x0=x0, **kw)
+            assert info["status"][0] == 0 and not torch.any(x)
+            x, info = pat.solve(d["val"], d["b"], maxit=0, method=p.method, precond=p.precond,
+                                check=False, **kw)
+            assert info["return"] == hip.SLA_NOT_CONVERGED and info["iters"][0] == 0
+            assert not torch.any(x)
+
+
+def test_initial_guess(hip):
+    banner("initial guess")
+    for p, kw in ((W.config(2, size=16), {}), (W.config(1), {}), (W.config(4, size=24), {})):
+        d = to_dev(p)
+        pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+        x, info = pat.solve(d["val"], d["b"], tol=1e-12, maxit=5000, method=p.method,
+                            precond=p.precond)
+        x2, info2 = pat.solve(d["val"], d["b"], tol=1e-10, maxit=5000, method=p.method,
+                              precond=p.precond, x0=x)
+        assert info2["status"][0] == 0 and info2["iters"][0] == 0
+        rng = np.random.default_rng(3)
+        x0 = torch.from_numpy(rng.standard_normal((1, p.n))).cuda()
+        x3, info3 = pat.solve(d["val"], d["b"], tol=1e-11, maxit=5000, method=p.method,
+                              precond=p.precond, x0=x0)
+        assert info3["status"][0] == 0
+        assert relerr(x3.cpu().numpy(), x.cpu().numpy()) <= 1e-7
+
+
+def test_zero_diagonal_and_breakdown(hip):
+    banner("zero diag / breakdown")
+    p = W.config(1, size=8)
+    st, dp = O.check_pattern(p.n, p.row_ptr, p.col)
+    v = p.values.copy()
+    v[0, dp[5]] = 0.0
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=torch.float64)
+    for kw in ({}, {"profile": True}):
+        with pytest.raises(hip.SlaError) as ei:
+            pat.solve(torch.from_numpy(v).cuda(), d["b"], precond="jacobi", **kw)
+        assert ei.value.status == hip.SLA_ERR_ZERO_DIAG
+    # indefinite symmetric diagonal: p.Ap <= 0
+    rp = torch.tensor([0, 1, 2], dtype=torch.int32).cuda()
+    col = torch.tensor([0, 1], dtype=torch.int32).cuda()
+    pat2 = hip.Pattern(rp, col, dtype=torch.float64, build_transpose=True)
+    vals = torch.tensor([[1.0, -1.0]], dtype=torch.float64).cuda()
+    bb = torch.tensor([[0.0, 1.0]], dtype=torch.float64).cuda()
+    for kw in ({}, {"profile": True}):
+        x, info = pat2.solve(vals, bb, precond="none", check=False, **kw)
+        assert info["return"] == hip.SLA_BREAKDOWN
+    # BiCGStab: rhat.v = 0 for A = [[0,1],[1,0]], b = e1
+    rp = torch.tensor([0, 2, 4], dtype=torch.int32).cuda()
+    col = torch.tensor([0, 1, 0, 1], dtype=torch.int32).cuda()
+    pat3 = hip.Pattern(rp, col, dtype=torch.float64, build_transpose=True)
+    vals = torch.tensor([[0.0, 1.0, 1.0, 0.0]], dtype=torch.float64).cuda()
+    bb = torch.tensor([[1.0, 0.0]], dtype=torch.float64).cuda()
+    x, info = pat3.solve(vals, bb, method="bicgstab", precond="none", check=False)
+    assert info["return"] == hip.SLA_BREAKDOWN
+
+
+def test_bicgstab_half_step(hip):
+    banner("bicgstab half step")
+    N = 32
+    rp, col, val = W.laplacian_2d(N)
+    pp = np.arange(1, N + 1)
+    h = np.pi / (N + 1)
+    v = np.outer(np.sin(9 * pp * h), np.sin(5 * pp * h)).reshape(-1)
+    lam = 4 - 2 * np.cos(5 * h) - 2 * np.cos(9 * h)
+    pat = hip.Pattern(torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda(),
+                      build_transpose=True)
+    x, info = pat.solve(torch.from_numpy(val).cuda(), torch.from_numpy(v[None, :]).cuda(),
+                        method="bicgstab", precond="none")
+    assert info["iters"][0] == 1 and info["spmv"][0] == 1
+    assert relerr(x.cpu().numpy()[0], v / lam) <= 1e-13
+
+
+def test_single_unknown(hip):
+    banner("n = 1")
+    rp = torch.tensor([0, 1], dtype=torch.int32).cuda()
+    col = torch.tensor([0], dtype=torch.int32).cuda()
+    pat = hip.Pattern(rp, col, dtype=torch.float64, build_transpose=True)
+    vals = torch.tensor([[4.0]], dtype=torch.float64).cuda()
+    b = torch.tensor([[2.0]], dtype=torch.float64).cuda()
+    for m, pre in (("cg", "jacobi"), ("cg", "none"), ("bicgstab", "none")):
+        x, info = pat.solve(vals, b, method=m, precond=pre)
+        assert abs(x.item() - 0.5) <= 1e-15
+        gv, gb, _ = pat.solve_adjoint(vals, x, x - 1.0, method=m, precond=pre)
+        assert abs(gb.item() - (-0.5 / 4.0)) <= 1e-15
+        assert abs(gv.item() - (0.5 / 4.0) * 0.5) <= 1e-15
+
+
+def test_batch_mixed_convergence_is_loop_of_singles(hip):
+    banner("batch = loop")
+    p = W.config(3, size=24, batch=6)
+    p.b[2] = 0.0
+    g = gpu_forward_adjoint(hip, p)
+    for s in range(p.batch):
+        q = W.Problem("one", p.n, p.row_ptr, p.col, p.values[s:s + 1], p.b[s:s + 1],
+                      p.x_t[s:s + 1], method="cg", precond="jacobi", tol=p.tol, maxit=p.maxit)
+        gs = gpu_forward_adjoint(hip, q)
+        assert np.array_equal(gs["x"][0], g["x"][s])
+        assert gs["info"]["iters"][0] == g["info"]["iters"][s]
+    assert g["info"]["iters"][2] == 0 and not np.any(g["x"][2])
+
+
+def test_determinism_and_launch_modes_agree(hip):
+    banner("determinism")
+    for p in (W.config(2, size=28), W.config(4, size=40)):
+        d = to_dev(p)
+        pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+        outs = []
+        for kw in ({}, {}, {"graph_chunk": -8}, {"graph_chunk": 3}, {"profile": True}):
+            x, info = pat.solve(d["val"], d["b"], method=p.method, precond=p.precond, **kw)
+            gv, gb, _ = pat.solve_adjoint(d["val"], x, x - d["xt"], method=p.method,
+                                          precond=p.precond, **kw)
+            outs.append((x.cpu().numpy(), gv.cpu().numpy(), gb.cpu().numpy(), info["iters"][0]))
+        for o in outs[1:]:
+            assert all(np.array_equal(a, b) for a, b in zip(o[:3], outs[0][:3]))
+            assert o[3] == outs[0][3]
+
+
+def test_workspace_independent_of_iterations(hip):
+    banner("memory vs maxit")
+    p = W.config(2, size=24)
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p))
+    ws0 = pat.workspace_bytes()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for maxit in (10, 1000):
+        x, info = pat.solve(d["val"], d["b"], maxit=maxit, check=False)
+        pat.solve_adjoint(d["val"], x, x - d["xt"], maxit=maxit, check=False)
+        torch.cuda.synchronize()
+        assert pat.workspace_bytes() == ws0
+    assert torch.cuda.mem_get_info()[0] >= free0 - (64 << 20)
+    assert ws0 < 40 * 8 * p.n + 4 * (1 << 20)
+
+
+def test_autograd_function(hip):
+    banner("autograd")
+    p = W.config(4, size=20)
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=torch.float64, build_transpose=True)
+    vals = d["val"].clone().requires_grad_(True)
+    b = d["b"].clone().requires_grad_(True)
+    x = hip.sparse_solve(pat, vals, b, method="bicgstab", precond="none", tol=1e-12, maxit=2000)
+    loss = 0.5 * ((x - d["xt"]) ** 2).sum()
+    loss.backward()
+    r, a = oracle_forward_adjoint(p, tol=1e-12, maxit=2000)
+    assert relerr(vals.grad.cpu().numpy(), a.grad_values) <= 1e-7
+    assert relerr(b.grad.cpu().numpy(), a.grad_b) <= 1e-7
