@@ -28,16 +28,17 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=(), tmpdir: str = None) -> str:
+    """Compile every csrc/*.hip and link ``out``; ``defines`` are extra -D flags."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
-    tmpdir = os.path.join(PKG, "_build")
+    tmpdir = tmpdir or os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
     procs = []
     for src in sources():
         obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], "-c", "-I", INCLUDE, "-I", CSRC,
-               src, "-o", obj]
+        cmd = [hipcc, *[f for f in FLAGS if f != "-shared"], *[f"-D{d}" for d in defines], "-c",
+               "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd)))
@@ -45,13 +46,13 @@ def build(verbose: bool = False) -> str:
     failed = [src for src, p in procs if p.wait() != 0]
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + f".tmp{os.getpid()}"
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

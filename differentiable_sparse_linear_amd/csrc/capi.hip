@@ -212,16 +212,18 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
 
     if (o.profile) {
         // every iteration launched directly, each fused SpMV kernel bracketed
-        // by a pair of events on `s`
+        // by a pair of events on `s`; the stop (including maxit) is detected
+        // by the first kernel of the next iteration, so maxit + 1 are enqueued
         const int per = cg ? 1 : 2;
-        const size_t need = (size_t)2 * per * (size_t)o.maxit;
+        const int launches = o.maxit + 1;
+        const size_t need = (size_t)2 * per * (size_t)launches;
         while (h->prof_ev.size() < need) {
             hipEvent_t e;
             HIP_TRY(hipEventCreate(&e));
             h->prof_ev.push_back(e);
         }
         size_t ev = 0;
-        for (int k = 0; k < o.maxit; ++k) {
+        for (int k = 0; k < launches; ++k) {
             if (cg) {
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
                 HIP_TRY(launch_cg_spmv<T, IT>(op.G, jac, ad, n, s));
@@ -236,7 +238,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
-            if ((k & 63) == 63 || k + 1 == o.maxit) {
+            if ((k & 63) == 63 || k + 1 == launches) {
                 HIP_TRY(hipMemcpyAsync(&h->poll[0], &st->done, sizeof(int32_t),
                                        hipMemcpyDeviceToHost, s));
                 HIP_TRY(hipStreamSynchronize(s));

@@ -3,19 +3,19 @@
 // Vorst, SIAM J. Sci. Stat. Comput. 13, 1992), unpreconditioned, grid path.
 //
 // Iteration k, three kernels:
-//   bicg_pv:     p = r + beta (p - omega v) evaluated while gathering,
-//                v = A p, stored p and v, partial rhat.v
-//                -> last block: alpha = rho / rhat.v (0: breakdown)
-//   bicg_st:     s = r - alpha v evaluated while gathering, t = A s, stored
-//                s and t, partials t.s, t.t, s.s
-//                -> last block: half-step test ||s|| <= tol ||b||, else
-//                   omega = t.s / t.t (t.t = 0 or t.s = 0: breakdown)
-//   bicg_update: half step: x += alpha p; else x += alpha p + omega s,
-//                r = s - omega t, partials rhat.r and r.r
-//                -> last block: stop test, maxit, next rho and beta
-// p and v are double-buffered by iteration parity (the SpMV kernels read the
-// old vectors at neighbouring rows while they write the new ones).
-#include "sla_internal.h"
+//   bicg_pv:     stop tests; rho = rhat.r, beta; p = r + beta (p - omega v)
+//                evaluated while gathering, v = A p; partial rhat.v
+//   bicg_st:     alpha = rho / rhat.v; s = r - alpha v evaluated while
+//                gathering, t = A s; partials t.s, t.t, s.s
+//   bicg_update: half step (||s|| <= tol ||b||): x += alpha p; else
+//                omega = t.s / t.t, x += alpha p + omega s, r = s - omega t;
+//                partials rhat.r and r.r
+// Each kernel stores per-block partial sums; every block of the next kernel
+// adds them in the same order, so the scalars are identical everywhere and no
+// kernel needs a grid-wide fence.  p and v are double-buffered by iteration
+// parity (the SpMV kernels read the old vectors at neighbouring rows while
+// they write the new ones).
+#include "spmv_tile.h"
 
 namespace sla {
 
@@ -30,9 +30,9 @@ __device__ __forceinline__ T pdir(bool first, T beta, T omega, T r, T p, T v) {
     return first ? r : fmaB(beta, fmaB(-omega, v, p), r);
 }
 
+// r = rhat = b - A x0 (or b with x = 0); partials r.r (= rhat.r) and b.b.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
-    SolveState *st = A->st;
     const int64_t n = A->n;
     const T *b = A->b;
     T *x = A->x;
@@ -57,37 +57,60 @@ __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT>
             bb += (double)bi * (double)bi;
         }
     }
-    double v[2] = {rr, bb}, tot[2];
-    if (grid_reduce<2>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        st->rho = tot[0];  // rhat = r
-        st->rr = tot[0];
-        st->bb = tot[1];
-        st->iter = 0;
-        st->alpha = 1.0;
-        st->omega = 1.0;
-        st->beta = 0.0;
-        st->half = 0;
-        if (tot[1] == 0.0) {
-            st->done = 1;
-            st->status = SLA_OK;
-            st->zero_x = x0 ? 1 : 0;
-        } else if (sqrt(tot[0]) <= A->tol * sqrt(tot[1])) {
-            st->done = 1;
-            st->status = SLA_OK;
-        } else if (A->maxit <= 0) {
-            st->done = 1;
-            st->status = SLA_NOT_CONVERGED;
-        }
-    }
+    double v[3] = {rr, rr, bb};
+    const int slot[3] = {kBiRHR, kBiRR, kBiBB};
+    store_partials<3>(v, A->part, slot);
 }
 
-template <int G, typename T, typename IT>
+// Iteration k (0-based, k = iter_a): a pending half-step exit stops here;
+// stop tests on r_k; rho_k = rhat.r_k
+// (0: breakdown); beta = (rho_k/rho_{k-1})(alpha_{k-1}/omega_{k-1});
+// p = r + beta (p - omega v) evaluated while gathering (p = r at k = 0);
+// v = A p; partial rhat.v.
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (st->done) return;
-    const int it = st->iter;
+    if (load_done(st)) return;
+    const int it = st->iter_a;
+    double tot[3];
+    {
+        const int slot[3] = {kBiRHR, kBiRR, kBiBB};
+        load_totals<3>(A->part, gridDim.x, slot, tot);
+    }
+    if (st->half_exit) {
+        finish(st, SLA_OK, it, st->half_ss);
+        return;
+    }
+    const double rho = tot[0], rr = tot[1];
+    const double bb = it == 0 ? tot[2] : st->bb;
+    if (it == 0 && bb == 0.0) {
+        if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+        finish(st, SLA_OK, 0, 0.0);
+        return;
+    }
+    if (sqrt(rr) <= A->tol * sqrt(bb)) {
+        finish(st, SLA_OK, it, rr);
+        return;
+    }
+    if (it >= A->maxit) {
+        finish(st, SLA_NOT_CONVERGED, it, rr);
+        return;
+    }
+    if (rho == 0.0) {
+        finish(st, SLA_BREAKDOWN, it, rr);
+        return;
+    }
     const bool first = (it == 0);
-    const T beta = (T)st->beta, omega = (T)st->omega;
+    const int pv = (it + 1) & 1;  // parity slot of iteration k-1
+    const T beta = first ? T(0) : (T)((rho / st->rho[pv]) * (st->alpha[pv] / st->omega[pv]));
+    const T omega = first ? T(0) : (T)st->omega[pv];
+    if (block0()) {
+        st->rho[it & 1] = rho;
+        st->iter_b = it;
+        st->spmv += (first && A->use_x0) ? 2 : 1;  // counts the A x0 product
+        st->nfused += 1;
+        if (first) st->bb = bb;
+    }
     const T *__restrict__ r = A->r;
     const T *__restrict__ rh = A->rh;
     const T *__restrict__ pold = A->p[it & 1];
@@ -98,55 +121,46 @@ __global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *
     const int32_t *__restrict__ col = A->col;
     const T *__restrict__ val = A->val;
     const int64_t n = A->n;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
+    __shared__ TileLds<T, IT> sm;
     double rv = 0.0;
+    auto pk = [&](int64_t c) { return first ? r[c] : pdir(false, beta, omega, r[c], pold[c], vold[c]); };
     const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const IT e = rp[i + 1];
-                T acc = T(0);
-                if (first) {
-                    for (IT k = rp[i] + lane; k < e; k += G) acc += val[k] * r[col[k]];
-                } else {
-                    for (IT k = rp[i] + lane; k < e; k += G) {
-                        const int32_t c = col[k];
-                        acc += val[k] * pdir(false, beta, omega, r[c], pold[c], vold[c]);
-                    }
-                }
-                acc = group_sum<G>(acc);
-                if (lane == 0) {
-                    pnew[i] = first ? r[i] : pdir(false, beta, omega, r[i], pold[i], vold[i]);
-                    vnew[i] = acc;
-                    rv += (double)rh[i] * (double)acc;
-                }
-            }
-        }
-    }
-    double v[1] = {rv}, tot[1];
-    if (grid_reduce<1>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        st->aux = tot[0];
-        st->spmv += 1;
-        st->nfused += 1;
-        if (tot[0] == 0.0) {
-            st->done = 1;
-            st->status = SLA_BREAKDOWN;
-        } else {
-            st->alpha = st->rho / tot[0];
-        }
-    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
+        spmv_tile<T, IT>(
+            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return pk(c); },
+            [&](int64_t i, T acc) {
+                pnew[i] = pk(i);
+                vnew[i] = acc;
+                rv += (double)rh[i] * (double)acc;
+            });
+    double v[1] = {rv};
+    const int slot[1] = {kBiRV};
+    store_partials<1>(v, A->part, slot);
 }
 
-template <int G, typename T, typename IT>
+// Iteration k (k = iter_b): alpha = rho_k / rhat.v (0: breakdown);
+// s = r - alpha v evaluated while gathering, t = A s; partials t.s, t.t, s.s.
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (st->done) return;
-    const int it = st->iter;
-    const T alpha = (T)st->alpha;
+    if (load_done(st)) return;
+    const int it = st->iter_b;
+    double tot[1];
+    {
+        const int slot[1] = {kBiRV};
+        load_totals<1>(A->part, gridDim.x, slot, tot);
+    }
+    if (tot[0] == 0.0) {
+        finish(st, SLA_BREAKDOWN, it, 0.0);
+        return;
+    }
+    const double alpha_d = st->rho[it & 1] / tot[0];
+    const T alpha = (T)alpha_d;
+    if (block0()) {
+        st->alpha[it & 1] = alpha_d;
+        st->iter_c = it;
+        st->nfused += 1;
+    }
     const T *__restrict__ r = A->r;
     const T *__restrict__ v = A->v[(it + 1) & 1];
     T *__restrict__ s = A->s;
@@ -155,59 +169,49 @@ __global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *
     const int32_t *__restrict__ col = A->col;
     const T *__restrict__ val = A->val;
     const int64_t n = A->n;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
+    __shared__ TileLds<T, IT> sm;
     double ts = 0.0, tt = 0.0, ss = 0.0;
+    auto sk = [&](int64_t c) { return fmaB(-alpha, v[c], r[c]); };
     const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const IT e = rp[i + 1];
-                T acc = T(0);
-                for (IT k = rp[i] + lane; k < e; k += G) {
-                    const int32_t c = col[k];
-                    acc += val[k] * fmaB(-alpha, v[c], r[c]);
-                }
-                acc = group_sum<G>(acc);
-                if (lane == 0) {
-                    const T si = fmaB(-alpha, v[i], r[i]);
-                    s[i] = si;
-                    tv[i] = acc;
-                    ts += (double)acc * (double)si;
-                    tt += (double)acc * (double)acc;
-                    ss += (double)si * (double)si;
-                }
-            }
-        }
-    }
-    double red[3] = {ts, tt, ss}, tot[3];
-    if (grid_reduce<3>(red, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        st->ss = tot[2];
-        st->nfused += 1;
-        if (sqrt(tot[2]) <= A->tol * sqrt(st->bb)) {
-            st->half = 1;  // bicg_update applies x += alpha p and stops
-        } else {
-            st->spmv += 1;
-            if (tot[1] == 0.0 || tot[0] == 0.0) {
-                st->done = 1;
-                st->status = SLA_BREAKDOWN;
-            } else {
-                st->omega = tot[0] / tot[1];
-            }
-        }
-    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
+        spmv_tile<T, IT>(
+            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return sk(c); },
+            [&](int64_t i, T acc) {
+                const T si = sk(i);
+                s[i] = si;
+                tv[i] = acc;
+                ts += (double)acc * (double)si;
+                tt += (double)acc * (double)acc;
+                ss += (double)si * (double)si;
+            });
+    double red[3] = {ts, tt, ss};
+    const int slot[3] = {kBiTS, kBiTT, kBiSS};
+    store_partials<3>(red, A->part, slot);
 }
 
+// Iteration k (k = iter_c): half-step exit when ||s|| <= tol ||b||
+// (x += alpha p); else omega = t.s / t.t (t.t = 0 or t.s = 0: breakdown),
+// x += alpha p + omega s, r = s - omega t; partials rhat.r and r.r.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_update_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (st->done) return;
-    const int it = st->iter;
-    const bool half = st->half != 0;
-    const T alpha = (T)st->alpha, omega = (T)st->omega;
+    if (load_done(st)) return;
+    const int it = st->iter_c;
+    double tot[3];
+    {
+        const int slot[3] = {kBiTS, kBiTT, kBiSS};
+        load_totals<3>(A->part, gridDim.x, slot, tot);
+    }
+    const double bb = st->bb;
+    const bool half = sqrt(tot[2]) <= A->tol * sqrt(bb);
+    if (!half && (tot[1] == 0.0 || tot[0] == 0.0)) {
+        if (block0()) st->spmv += 1;
+        finish(st, SLA_BREAKDOWN, it, 0.0);
+        return;
+    }
+    const T alpha = (T)st->alpha[it & 1];
+    const double omega_d = half ? 0.0 : tot[0] / tot[1];
+    const T omega = (T)omega_d;
     const T *__restrict__ p = A->p[(it + 1) & 1];
     const T *__restrict__ s = A->s;
     const T *__restrict__ tv = A->t;
@@ -232,44 +236,27 @@ __global__ __launch_bounds__(kBlock) void bicg_update_kernel(const IterArgs<T, I
             }
         }
     }
-    double v[2] = {rhr, rr}, tot[2];
-    if (grid_reduce<2>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        const int k = it + 1;
-        st->iter = k;
-        if (half) {
-            st->rr = st->ss;
-            st->done = 1;
-            st->status = SLA_OK;
-        } else {
-            st->rr = tot[1];
-            if (sqrt(tot[1]) <= A->tol * sqrt(st->bb)) {
-                st->done = 1;
-                st->status = SLA_OK;
-            } else if (k >= A->maxit) {
-                st->done = 1;
-                st->status = SLA_NOT_CONVERGED;
-            } else if (tot[0] == 0.0) {
-                st->done = 1;
-                st->status = SLA_BREAKDOWN;
-            } else {
-                st->beta = (tot[0] / st->rho) * (st->alpha / st->omega);
-                st->rho = tot[0];
-            }
+    if (half) {
+        // stop in the next kernel: a block still to start must not see
+        // `done` before it has applied its x update
+        if (block0()) {
+            st->half_ss = tot[2];
+            st->half_exit = 1;
+            st->iter_a = it + 1;
         }
+        return;
     }
+    if (block0()) {
+        st->omega[it & 1] = omega_d;
+        st->iter_a = it + 1;
+        st->spmv += 1;
+    }
+    double v[2] = {rhr, rr};
+    const int slot[2] = {kBiRHR, kBiRR};
+    store_partials<2>(v, A->part, slot);
 }
 
 // ------------------------------------------------------------------ launchers
-
-#define SLA_DISPATCH_G(G, ...)                      \
-    switch (G) {                                    \
-        case 2: { constexpr int kG = 2; __VA_ARGS__; } break;   \
-        case 4: { constexpr int kG = 4; __VA_ARGS__; } break;   \
-        case 8: { constexpr int kG = 8; __VA_ARGS__; } break;   \
-        case 16: { constexpr int kG = 16; __VA_ARGS__; } break; \
-        case 32: { constexpr int kG = 32; __VA_ARGS__; } break; \
-        default: { constexpr int kG = 64; __VA_ARGS__; } break; \
-    }
 
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
@@ -278,16 +265,14 @@ hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) 
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
-    SLA_DISPATCH_G(G, bicg_pv_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(a));
+hipError_t launch_bicg_pv(int, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+    bicg_pv_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
-    SLA_DISPATCH_G(G, bicg_st_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(a));
+hipError_t launch_bicg_st(int, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+    bicg_st_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

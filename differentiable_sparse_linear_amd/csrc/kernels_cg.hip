@@ -4,22 +4,26 @@
 // steps as in Saad, Iterative Methods for Sparse Linear Systems, Alg. 9.1).
 //
 // Grid path, two kernels per iteration over one system:
-//   cg_spmv:   p_k = z_k + beta p_{k-1} (p_0 = z_0) evaluated while gathering,
-//              q = A p_k, stored p_k and q, partial p.q
-//              -> last block: alpha = rho / p.q (p.q <= 0: breakdown)
-//   cg_update: x += alpha p, r -= alpha q, z = M^-1 r, partials r.z and r.r
-//              -> last block: stop test ||r|| <= tol ||b||, beta, rho
-// p is double-buffered by iteration parity because cg_spmv reads the old p
-// at neighbouring rows while it writes the new one.  Scalars stay on the
-// device; every kernel returns at entry once the system is done, so the host
-// can enqueue many iterations (HIP graph replays) and poll rarely.
+//   cg_spmv:   stop test on r_k; beta = rho_k / rho_{k-1};
+//              p_k = z_k + beta p_{k-1} (p_0 = z_0) evaluated while gathering,
+//              q = A p_k, stored p_k and q; partial p.q
+//   cg_update: alpha = rho_k / p.q (p.q <= 0: breakdown); x += alpha p,
+//              r -= alpha q, z = M^-1 r; partials r.z and r.r
+// Each kernel stores per-block partial sums with plain stores; every block
+// of the next kernel adds them in block order, so all blocks derive the same
+// scalars and no grid-wide fence is needed (a release at agent scope costs an
+// L2 write-back per block on a multi-XCD part).  p is double-buffered by
+// iteration parity because cg_spmv reads the old p at neighbouring rows while
+// it writes the new one.  Every kernel returns at entry once the device-side
+// `done` flag is set, so the host can enqueue many iterations (HIP graph
+// replays) and poll rarely.
 //
 // Block path: one 1024-thread workgroup runs the whole solve of one small
 // system (n <= 4096): vectors live in registers, the search direction in LDS
 // for the gathers, reductions in LDS; no grid-wide synchronisation and no
 // per-iteration launches (the pages note that launch overhead hurts iterative
 // solvers on small problems: Problem statement, backend fragmentation).
-#include "sla_internal.h"
+#include "spmv_tile.h"
 
 namespace sla {
 
@@ -28,9 +32,9 @@ __device__ __forceinline__ T fmaT(T a, T b, T c) {
     return fma(a, b, c);
 }
 
+// r = b - A x0 (or b with x = 0), z = M^-1 r; partials r.z, r.r, b.b.
 template <typename T, typename IT, bool JAC>
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
-    SolveState *st = A->st;
     const int64_t n = A->n;
     const T *b = A->b;
     T *x = A->x;
@@ -61,37 +65,53 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
             bb += (double)bi * (double)bi;
         }
     }
-    double v[3] = {rz, rr, bb}, tot[3];
-    if (grid_reduce<3>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        st->rho = tot[0];
-        st->rr = tot[1];
-        st->bb = tot[2];
-        st->iter = 0;
-        st->beta = 0.0;
-        if (st->zero_diag) {
-            st->done = 1;
-            st->status = SLA_ERR_ZERO_DIAG;
-        } else if (tot[2] == 0.0) {
-            st->done = 1;
-            st->status = SLA_OK;
-            st->zero_x = x0 ? 1 : 0;
-        } else if (sqrt(tot[1]) <= A->tol * sqrt(tot[2])) {
-            st->done = 1;
-            st->status = SLA_OK;
-        } else if (A->maxit <= 0) {
-            st->done = 1;
-            st->status = SLA_NOT_CONVERGED;
-        }
-    }
+    double v[3] = {rz, rr, bb};
+    const int slot[3] = {kCgRZ, kCgRR, kCgBB};
+    store_partials<3>(v, A->part, slot);
 }
 
-template <int G, typename T, typename IT, bool JAC>
+// Iteration k (k = iter_a): stop test on r_k, beta_k = rho_k / rho_{k-1},
+// p_k = z_k + beta_k p_{k-1} evaluated while gathering, q = A p_k,
+// partial p_k.q.
+template <typename T, typename IT, bool JAC>
 __global__ __launch_bounds__(kBlock) void cg_spmv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (st->done) return;
-    const int it = st->iter;
-    const T beta = (T)st->beta;
+    if (load_done(st)) return;
+    const int it = st->iter_a;
+    double tot[3];
+    {
+        const int slot[3] = {kCgRZ, kCgRR, kCgBB};
+        load_totals<3>(A->part, gridDim.x, slot, tot);
+    }
+    const double rho = tot[0], rr = tot[1];
+    const double bb = it == 0 ? tot[2] : st->bb;
+    // stop tests on the residual left by the previous update (or the start)
+    if (it == 0 && st->zero_diag) {
+        finish(st, SLA_ERR_ZERO_DIAG, 0, rr);
+        return;
+    }
+    if (it == 0 && bb == 0.0) {
+        if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+        finish(st, SLA_OK, 0, 0.0);
+        return;
+    }
+    if (sqrt(rr) <= A->tol * sqrt(bb)) {
+        finish(st, SLA_OK, it, rr);
+        return;
+    }
+    if (it >= A->maxit) {
+        finish(st, SLA_NOT_CONVERGED, it, rr);
+        return;
+    }
     const bool first = (it == 0);
+    const T beta = first ? T(0) : (T)(rho / st->rho[(it + 1) & 1]);
+    if (block0()) {
+        st->rho[it & 1] = rho;
+        st->iter_b = it;
+        st->spmv += (first && A->use_x0) ? 2 : 1;  // counts the A x0 product
+        st->nfused += 1;
+        if (first) st->bb = bb;
+    }
     const T *__restrict__ zz = JAC ? A->z : A->r;
     const T *__restrict__ pold = A->p[it & 1];
     T *__restrict__ pnew = A->p[(it + 1) & 1];
@@ -100,56 +120,42 @@ __global__ __launch_bounds__(kBlock) void cg_spmv_kernel(const IterArgs<T, IT> *
     const T *__restrict__ val = A->val;
     T *__restrict__ q = A->q;
     const int64_t n = A->n;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
+    __shared__ TileLds<T, IT> sm;
     double pq = 0.0;
+    auto pdir = [&](int64_t c) { return first ? zz[c] : fmaT(beta, pold[c], zz[c]); };
     const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const IT e = rp[i + 1];
-                T acc = T(0);
-                if (first) {
-                    for (IT k = rp[i] + lane; k < e; k += G) acc += val[k] * zz[col[k]];
-                } else {
-                    for (IT k = rp[i] + lane; k < e; k += G) {
-                        const int32_t c = col[k];
-                        acc += val[k] * fmaT(beta, pold[c], zz[c]);
-                    }
-                }
-                acc = group_sum<G>(acc);
-                if (lane == 0) {
-                    const T pi = first ? zz[i] : fmaT(beta, pold[i], zz[i]);
-                    pnew[i] = pi;
-                    q[i] = acc;
-                    pq += (double)pi * (double)acc;
-                }
-            }
-        }
-    }
-    double v[1] = {pq}, tot[1];
-    if (grid_reduce<1>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        st->aux = tot[0];
-        st->spmv += 1;
-        st->nfused += 1;
-        if (!(tot[0] > 0.0)) {
-            st->done = 1;
-            st->status = SLA_BREAKDOWN;
-        } else {
-            st->alpha = st->rho / tot[0];
-        }
-    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
+        spmv_tile<T, IT>(
+            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return pdir(c); },
+            [&](int64_t i, T acc) {
+                const T pi = pdir(i);
+                pnew[i] = pi;
+                q[i] = acc;
+                pq += (double)pi * (double)acc;
+            });
+    double v[1] = {pq};
+    const int slot[1] = {kCgPQ};
+    store_partials<1>(v, A->part, slot);
 }
 
+// Iteration k (k = iter_b): alpha = rho_k / p.q (p.q <= 0: breakdown);
+// x += alpha p, r -= alpha q, z = M^-1 r; partials r.z and r.r.
 template <typename T, typename IT, bool JAC>
 __global__ __launch_bounds__(kBlock) void cg_update_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (st->done) return;
-    const int it = st->iter;
-    const T alpha = (T)st->alpha;
+    if (load_done(st)) return;
+    const int it = st->iter_b;
+    double tot[1];
+    {
+        const int slot[1] = {kCgPQ};
+        load_totals<1>(A->part, gridDim.x, slot, tot);
+    }
+    if (!(tot[0] > 0.0)) {
+        finish(st, SLA_BREAKDOWN, it, 0.0);
+        return;
+    }
+    const T alpha = (T)(st->rho[it & 1] / tot[0]);
+    if (block0()) st->iter_a = it + 1;
     const T *__restrict__ p = A->p[(it + 1) & 1];
     const T *__restrict__ q = A->q;
     const T *__restrict__ dinv = A->dinv;
@@ -174,22 +180,9 @@ __global__ __launch_bounds__(kBlock) void cg_update_kernel(const IterArgs<T, IT>
             rr += (double)ri * (double)ri;
         }
     }
-    double v[2] = {rz, rr}, tot[2];
-    if (grid_reduce<2>(v, A->part, &st->ticket, tot) && threadIdx.x == 0) {
-        const int k = it + 1;
-        st->iter = k;
-        st->rr = tot[1];
-        if (sqrt(tot[1]) <= A->tol * sqrt(st->bb)) {
-            st->done = 1;
-            st->status = SLA_OK;
-        } else if (k >= A->maxit) {
-            st->done = 1;
-            st->status = SLA_NOT_CONVERGED;
-        } else {
-            st->beta = tot[0] / st->rho;
-            st->rho = tot[0];
-        }
-    }
+    double v[2] = {rz, rr};
+    const int slot[2] = {kCgRZ, kCgRR};
+    store_partials<2>(v, A->part, slot);
 }
 
 // ------------------------------------------------------------ block path
@@ -398,13 +391,12 @@ hipError_t launch_cg_init(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStre
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_spmv(int G, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+hipError_t launch_cg_spmv(int, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
     const int grid = grid_for_tiles(tiles_of(n));
-    if (jac) {
-        SLA_DISPATCH_G(G, cg_spmv_kernel<kG, T, IT, true><<<grid, kBlock, 0, s>>>(a));
-    } else {
-        SLA_DISPATCH_G(G, cg_spmv_kernel<kG, T, IT, false><<<grid, kBlock, 0, s>>>(a));
-    }
+    if (jac)
+        cg_spmv_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(a);
+    else
+        cg_spmv_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -3,99 +3,107 @@
 // SpMV (torch-sla explainer, Methodology section 1: .matvec of the unified
 // API; the shared-pattern SparseTensor holds a batch of value arrays):
 //   y[s][i] = sum over stored k of row i: values[s][k] * x[s][col[k]].
-// A row is handled by a group of G lanes (G = smallest power of two >= the
-// mean row length): lane l reads entries rp[i]+l, rp[i]+l+G, ..., so one
-// wavefront instruction reads 64/G consecutive rows' entries as one coalesced
-// run, and the G partial sums are combined with cross-lane shuffles.
+// Rows are processed in tiles (spmv_tile.h): a tile's entries are read as one
+// coalesced run with several independent loads in flight per thread, the
+// products are staged in LDS and each row is summed in entry order.
 // Gradient on the pattern (Methodology section 2, linear systems):
 //   grad[s][k] = -lambda[s][row(k)] * x[s][col(k)].
-#include "sla_internal.h"
+#include "spmv_tile.h"
 
 namespace sla {
 
-template <int G, typename T, typename IT>
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
                                                       const int32_t *__restrict__ col,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride) {
+    __shared__ TileLds<T, IT> sm;
     const int sys = blockIdx.y;
     val += (int64_t)sys * val_stride;
     x += (int64_t)sys * vec_stride;
     y += (int64_t)sys * vec_stride;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
     const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const IT e = rp[i + 1];
-                T acc = T(0);
-                for (IT k = rp[i] + lane; k < e; k += G) acc += val[k] * x[col[k]];
-                acc = group_sum<G>(acc);
-                if (lane == 0) y[i] = acc;
-            }
-        }
-    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
+        spmv_tile<T, IT>(
+            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return x[c]; },
+            [&](int64_t i, T s) { y[i] = s; });
 }
 
 // y = A^T x through the transpose map: rp/col describe A^T and the value of
 // A^T entry kt is val[perm[kt]].
-template <int G, typename T, typename IT>
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ perm,
     const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
     int64_t n, int64_t vec_stride) {
+    __shared__ TileLds<T, IT> sm;
     const int sys = blockIdx.y;
     val += (int64_t)sys * val_stride;
     x += (int64_t)sys * vec_stride;
     y += (int64_t)sys * vec_stride;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
     const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const IT e = rp[i + 1];
-                T acc = T(0);
-                for (IT k = rp[i] + lane; k < e; k += G) acc += val[perm[k]] * x[col[k]];
-                acc = group_sum<G>(acc);
-                if (lane == 0) y[i] = acc;
-            }
-        }
-    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
+        spmv_tile<T, IT>(
+            t, n, rp, col, sm, [&](IT k) { return val[perm[k]]; },
+            [&](int32_t c) { return x[c]; }, [&](int64_t i, T s) { y[i] = s; });
 }
 
-template <int G, typename T, typename IT>
+// grad[k] = -lambda[row(k)] * x[col[k]].  Short tiles: each thread marks the
+// tile-local row of its row's entries in LDS, then the entries are written as
+// one coalesced run.  Tiles with long rows: one wavefront per row.
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                                                       const int32_t *__restrict__ col,
                                                       const T *__restrict__ lam,
                                                       const T *__restrict__ x, T *__restrict__ grad,
                                                       int64_t n, int64_t nnz) {
+    __shared__ IT srp[kTileRows + 1];
+    __shared__ T slam[kTileRows];
+    __shared__ uint16_t rid[kCap];
     const int sys = blockIdx.y;
     lam += (int64_t)sys * n;
     x += (int64_t)sys * n;
     grad += (int64_t)sys * nnz;
-    constexpr int RPP = kBlock / G;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
+    const int tid = threadIdx.x;
     const TileRange tr = xcd_tiles(tiles_of(n));
     for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t base = t * kTileRows;
-        for (int pass = 0; pass < G; ++pass) {
-            const int64_t i = base + pass * RPP + grp;
-            if (i < n) {
-                const T li = lam[i];
-                const IT e = rp[i + 1];
-                for (IT k = rp[i] + lane; k < e; k += G) grad[k] = -(li * x[col[k]]);
+        const int64_t row0 = t * kTileRows;
+        const int64_t left = n - row0;
+        const int rows = left < kTileRows ? (int)left : kTileRows;
+        if (tid < rows) {
+            srp[tid] = rp[row0 + tid];
+            slam[tid] = lam[row0 + tid];
+        }
+        if (tid == 0) srp[rows] = rp[row0 + rows];
+        __syncthreads();
+        const IT base = srp[0];
+        const int64_t cnt = (int64_t)(srp[rows] - base);
+        if (cnt <= kCap) {
+            if (tid < rows)
+                for (int e = (int)(srp[tid] - base); e < (int)(srp[tid + 1] - base); ++e)
+                    rid[e] = (uint16_t)tid;
+            __syncthreads();
+            int32_t c[kEpt];
+#pragma unroll
+            for (int j = 0; j < kEpt; ++j) {
+                const int e = tid + j * kBlock;
+                if (e < cnt) c[j] = col[base + e];
+            }
+#pragma unroll
+            for (int j = 0; j < kEpt; ++j) {
+                const int e = tid + j * kBlock;
+                if (e < cnt) grad[base + e] = -(slam[rid[e]] * x[c[j]]);
+            }
+        } else {
+            const int lane = tid & 63, wave = tid >> 6;
+            for (int r = wave; r < rows; r += kWaves) {
+                const T li = slam[r];
+                const IT hi = srp[r + 1];
+                for (IT k = srp[r] + lane; k < hi; k += 64) grad[k] = -(li * x[col[k]]);
             }
         }
+        __syncthreads();
     }
 }
 
@@ -135,42 +143,30 @@ __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T
 
 // ------------------------------------------------------------------ launchers
 
-#define SLA_DISPATCH_G(G, ...)                      \
-    switch (G) {                                    \
-        case 2: { constexpr int kG = 2; __VA_ARGS__; } break;   \
-        case 4: { constexpr int kG = 4; __VA_ARGS__; } break;   \
-        case 8: { constexpr int kG = 8; __VA_ARGS__; } break;   \
-        case 16: { constexpr int kG = 16; __VA_ARGS__; } break; \
-        case 32: { constexpr int kG = 32; __VA_ARGS__; } break; \
-        default: { constexpr int kG = 64; __VA_ARGS__; } break; \
-    }
-
 template <typename T, typename IT>
-hipError_t launch_spmv(int G, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
+hipError_t launch_spmv(int, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
                        const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
                        hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_G(G, spmv_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(rp, col, val, val_stride, x,
-                                                                     y, n, vec_stride));
+    spmv_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, val, val_stride, x, y, n, vec_stride);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int G, const IT *rp, const int32_t *col, const int32_t *perm,
+hipError_t launch_spmv_perm(int, const IT *rp, const int32_t *col, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
                             int64_t vec_stride, int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_G(G, spmv_perm_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(
-                          rp, col, perm, val, val_stride, x, y, n, vec_stride));
+    spmv_perm_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, perm, val, val_stride, x, y, n,
+                                                    vec_stride);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_grad(int G, const IT *rp, const int32_t *col, const T *lam, const T *x,
-                       T *grad, int64_t n, int64_t nnz, int batch, hipStream_t s) {
+hipError_t launch_grad(int, const IT *rp, const int32_t *col, const T *lam, const T *x, T *grad,
+                       int64_t n, int64_t nnz, int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_G(G, grad_kernel<kG, T, IT><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n,
-                                                                     nnz));
+    grad_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
     return hipGetLastError();
 }
 

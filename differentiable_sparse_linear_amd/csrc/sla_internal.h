@@ -13,36 +13,56 @@
 
 namespace sla {
 
-constexpr int kBlock = 256;        // threads per block of the grid kernels
+#ifndef SLA_BLOCK
+#define SLA_BLOCK 256
+#endif
+#ifndef SLA_BLOCKS_PER_XCD
+#define SLA_BLOCKS_PER_XCD 128
+#endif
+constexpr int kBlock = SLA_BLOCK;  // threads per block of the grid kernels
 constexpr int kWaves = kBlock / 64;
-constexpr int kTileRows = 256;     // rows per tile (one row per thread in
+constexpr int kTileRows = kBlock;  // rows per tile (one row per thread in
                                    // element-wise kernels)
 constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, 32 CUs each
-constexpr int kMaxBlocksPerXcd = 256;  // 8 resident blocks per CU
+// Grid kernels are persistent-style (a bounded grid strides over tiles):
+// the number of blocks is also the number of partial sums that every block
+// of the next kernel adds up, so it is kept moderate.
+constexpr int kMaxBlocksPerXcd = SLA_BLOCKS_PER_XCD;
 constexpr int kMaxGrid = kNumXcd * kMaxBlocksPerXcd;
-constexpr int kMaxRed = 4;         // reduction values per kernel
+constexpr int kMaxRed = 8;         // partial-sum slots
 constexpr int kBlockSolveThreads = 1024;
 constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread
 
-// Per-system solver state, device resident.  Written only by the last block
-// of a kernel (ticket order) and read by later kernels.
+// Per-system solver state, device resident.  A field is written by block 0
+// of one kernel and read by later kernels; fields that a kernel both reads
+// and writes live in two slots selected by iteration parity, and the
+// iteration counter is kept once per kernel role (iter_a read by the first
+// kernel of an iteration, iter_b by the second, iter_c by the third).
 struct SolveState {
-    double rho;      // CG: r.z ; BiCGStab: rhat.r of the current iteration
-    double alpha, beta, omega;
-    double bb;       // ||rhs||^2
-    double rr;       // ||r||^2 after the last update
-    double ss;       // BiCGStab ||s||^2
-    double aux;      // last denominator (p.q or rhat.v)
-    int32_t iter;    // completed iterations
-    int32_t done;    // 1 once converged / stopped
-    int32_t status;  // sla_status of the system
-    int32_t half;    // BiCGStab: half-step exit pending
-    int32_t spmv;    // products with the operator
+    double rho[2];    // CG: r.z ; BiCGStab: rhat.r, by iteration parity
+    double alpha[2];  // BiCGStab alpha by parity
+    double omega[2];  // BiCGStab omega by parity
+    double bb;        // ||rhs||^2
+    double rr;        // ||r||^2 at the stop
+    double half_ss;   // BiCGStab ||s||^2 of a half-step exit
+    int32_t iter_a, iter_b, iter_c;
+    int32_t iter;     // completed iterations at the stop
+    int32_t done;     // 1 once converged / stopped (relaxed atomic access)
+    int32_t status;   // sla_status of the system
+    int32_t spmv;     // products with the operator
+    int32_t nfused;   // launches of the fused SpMV kernels that did work
     int32_t zero_diag;
-    int32_t zero_x;  // rhs == 0 with a user initial guess: x must become 0
-    uint32_t ticket; // arrivals of the running kernel's blocks
-    int32_t nfused;  // launches of the fused SpMV kernels that did work
+    int32_t zero_x;   // rhs == 0 with a user initial guess: x must become 0
+    int32_t half_exit;  // BiCGStab: x took its half step, stop next kernel
     int32_t pad;
+};
+
+// Slots of the per-block partial sums ([kMaxRed][kMaxGrid] doubles).  A
+// kernel reads only slots that the previous kernel wrote and writes only
+// slots that it does not read.
+enum : int {
+    kCgPQ = 0, kCgRZ = 1, kCgRR = 2, kCgBB = 3,
+    kBiRV = 0, kBiTS = 1, kBiTT = 2, kBiSS = 3, kBiRHR = 4, kBiRR = 5, kBiBB = 6,
 };
 
 // Device-resident arguments of the iteration kernels.  Kernels take a pointer
@@ -104,19 +124,16 @@ __device__ __forceinline__ TileRange xcd_tiles(int64_t ntiles) {
     return tr;
 }
 
-// Reduce NR per-thread values over the grid.  Every block stores its block
-// sums in part[r][blockIdx.x]; the last block to arrive (ticket order) adds
-// the partials in block-index order, so the totals are bitwise reproducible.
-// Returns true in every thread of the last block, with tot[] filled.
+// Block sums of NR per-thread values, stored by thread 0 in
+// part[slot[r]][blockIdx.x] with plain stores: the kernel boundary publishes
+// them to the next kernel.
 template <int NR>
-__device__ __forceinline__ bool grid_reduce(double (&v)[NR], double *part, uint32_t *ticket,
-                                            double (&tot)[NR]) {
+__device__ __forceinline__ void store_partials(double (&v)[NR], double *part, const int (&slot)[NR]) {
     __shared__ double red[NR][kWaves];
-    __shared__ int last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-        double w = wave_sum(v[r]);
+        const double w = wave_sum(v[r]);
         if (lane == 0) red[r][wave] = w;
     }
     __syncthreads();
@@ -126,34 +143,51 @@ __device__ __forceinline__ bool grid_reduce(double (&v)[NR], double *part, uint3
             double s = 0.0;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) s += red[r][w];
-            __hip_atomic_store(&part[r * kMaxGrid + blockIdx.x], s, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            part[slot[r] * kMaxGrid + blockIdx.x] = s;
         }
-        const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-        last = (t == gridDim.x - 1);
     }
-    __syncthreads();
-    if (!last) return false;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every block's partials
-    const int nb = gridDim.x;
+}
+
+// Totals of the partial sums a previous kernel of nb blocks stored; every
+// block adds them in the same fixed order, so all blocks (and all runs) get
+// bitwise the same totals.
+template <int NR>
+__device__ __forceinline__ void load_totals(const double *part, int nb, const int (&slot)[NR],
+                                            double (&tot)[NR]) {
+    __shared__ double red[NR][kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         double s = 0.0;
-        for (int j = threadIdx.x; j < nb; j += kBlock)
-            s += __hip_atomic_load(&part[r * kMaxGrid + j], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int j = threadIdx.x; j < nb; j += kBlock) s += part[slot[r] * kMaxGrid + j];
         s = wave_sum(s);
-        __syncthreads();
         if (lane == 0) red[r][wave] = s;
-        __syncthreads();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
         double acc = 0.0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) acc += red[r][w];
         tot[r] = acc;
     }
-    if (threadIdx.x == 0) *ticket = 0u;
-    return true;
+    __syncthreads();
+}
+
+__device__ __forceinline__ int load_done(const SolveState *st) {
+    return __hip_atomic_load(&st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool block0() { return blockIdx.x == 0 && threadIdx.x == 0; }
+
+// Block 0 records the end of the solve.
+__device__ __forceinline__ void finish(SolveState *st, int status, int iter, double rr) {
+    if (block0()) {
+        st->status = status;
+        st->iter = iter;
+        st->rr = rr;
+        __hip_atomic_store(&st->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // Grid size for a tile count: a multiple of kNumXcd, at most kMaxGrid.

@@ -208,7 +208,8 @@ def test_fixed_iteration_count_matches_oracle_iterates(hip):
         for k in (1, 2, 7):
             g = gpu_forward_adjoint(hip, p, maxit=k, **path)
             r = O.solve(p.row_ptr, p.col, p.values, p.b, p.method, p.precond, p.tol, k)
-            assert g["info"]["status"][0] == hip.SLA_NOT_CONVERGED and r.status[0] == O.NOT_CONVERGED
+            assert g["info"]["status"][0] == hip.SLA_NOT_CONVERGED, (p.name, k, path, g["info"])
+            assert r.status[0] == O.NOT_CONVERGED
             assert g["info"]["iters"][0] == k == r.iters[0]
             assert relerr(g["x"][0], r.x[0]) <= 1e-12, (p.name, k, path)
             assert abs(g["info"]["relres"][0] - r.relres[0]) <= 1e-10 * r.relres[0]
