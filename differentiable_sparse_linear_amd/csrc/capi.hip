@@ -49,7 +49,9 @@ struct sla_ctx {
     int32_t *col_t = nullptr;
     int32_t *perm = nullptr;
     void *val_t = nullptr;
-    int G = 8;
+    int G = 8;       // lanes per row of the one-workgroup solver
+    int slots = 8;   // gather slots per row (A), from its longest row
+    int slots_t = 8; // the same for A^T
     void *vec = nullptr;
     SolveState *st = nullptr;
     double *part = nullptr;
@@ -148,6 +150,7 @@ struct Operator {
     const void *rp;
     const int32_t *col;
     int G;
+    int slots;
 };
 
 // One system on the grid path: fill the argument block, run init, then
@@ -192,21 +195,23 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState), s));
     if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, vec + 10 * n,
                                         n, st, s));
+    // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
+    // reads it always, so it is zeroed when there is no initial guess
     if (o.use_x0)
-        HIP_TRY(launch_spmv<T, IT>(op.G, a.rp, op.col, val, 0, x, a.q, n, 0, 1, s));
+        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.col, val, 0, x, cg ? a.t : a.q, n, 0, 1, s));
+    else if (cg)
+        HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n, s));
     if (cg)
-        HIP_TRY(launch_cg_init<T, IT>(jac, ad, n, s));
+        HIP_TRY(launch_cg_init<T, IT>(op.slots, jac, ad, n, s));
     else
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
 
-    auto one_iter = [&](hipStream_t ss) -> hipError_t {
+    // iteration k; CG launches carry the iteration's parity
+    auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) {
-            if ((e = launch_cg_spmv<T, IT>(op.G, jac, ad, n, ss)) != hipSuccess) return e;
-            return launch_cg_update<T, IT>(jac, ad, n, ss);
-        }
-        if ((e = launch_bicg_pv<T, IT>(op.G, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_bicg_st<T, IT>(op.G, ad, n, ss)) != hipSuccess) return e;
+        if (cg) return launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, ss);
+        if ((e = launch_bicg_pv<T, IT>(op.slots, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_bicg_st<T, IT>(op.slots, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_update<T, IT>(ad, n, ss);
     };
 
@@ -226,15 +231,14 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         for (int k = 0; k < launches; ++k) {
             if (cg) {
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_cg_spmv<T, IT>(op.G, jac, ad, n, s));
+                HIP_TRY(launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, s));
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_cg_update<T, IT>(jac, ad, n, s));
             } else {
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_bicg_pv<T, IT>(op.G, ad, n, s));
+                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, ad, n, s));
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_bicg_st<T, IT>(op.G, ad, n, s));
+                HIP_TRY(launch_bicg_st<T, IT>(op.slots, ad, n, s));
                 HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
@@ -261,9 +265,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         *prof_ms += total;
         *prof_launches += active;
     } else {
+        // the stop is detected by the first kernel of iteration maxit, so
+        // maxit + 1 iterations may be launched; CG chunks have even length so
+        // that every chunk starts at an even iteration
         int chunk = o.graph_chunk == 0 ? kDefaultChunk : (o.graph_chunk < 0 ? -o.graph_chunk : o.graph_chunk);
-        if (chunk > o.maxit && o.maxit > 0) chunk = o.maxit;
+        if (chunk > o.maxit + 1) chunk = o.maxit + 1;
         if (chunk < 1) chunk = 1;
+        if (cg && (chunk & 1)) ++chunk;
         hipGraphExec_t exec = nullptr;
         if (o.graph_chunk >= 0) {
             const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.G != h->G || op.rp != h->rp ? 2 : 0);
@@ -285,7 +293,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
                 hipGraph_t graph = nullptr;
                 HIP_TRY(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
                 hipError_t ce = hipSuccess;
-                for (int k = 0; k < chunk && ce == hipSuccess; ++k) ce = one_iter(h->cap);
+                for (int k = 0; k < chunk && ce == hipSuccess; ++k) ce = one_iter(h->cap, k);
                 hipError_t ee = hipStreamEndCapture(h->cap, &graph);
                 HIP_TRY(ce);
                 HIP_TRY(ee);
@@ -297,13 +305,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
             }
             exec = slot->exec;
         }
-        const int64_t max_chunks = (o.maxit + chunk - 1) / chunk + 1;
+        const int64_t max_chunks = (o.maxit + 1 + chunk - 1) / chunk + 1;
         for (int64_t c = 0; c <= max_chunks; ++c) {
             if (c < max_chunks) {
                 if (exec) {
                     HIP_TRY(hipGraphLaunch(exec, s));
                 } else {
-                    for (int k = 0; k < chunk; ++k) HIP_TRY(one_iter(s));
+                    for (int k = 0; k < chunk; ++k) HIP_TRY(one_iter(s, k));
                 }
                 HIP_TRY(hipMemcpyAsync(&h->poll[c & 1], &st->done, sizeof(int32_t),
                                        hipMemcpyDeviceToHost, s));
@@ -388,12 +396,12 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     oo.use_x0 = 0;
     sla_status st;
     if (o.method == SLA_CG) {
-        Operator op{h->rp, h->col, h->G};
+        Operator op{h->rp, h->col, h->G, h->slots};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
         // A^T with values gathered through the transpose map, one system at
         // a time into the handle's buffer
-        Operator op{h->rp_t, h->col_t, h->G};
+        Operator op{h->rp_t, h->col_t, h->G, h->slots_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
         std::vector<int32_t> it(B0), mv(B0), stc(B0);
@@ -455,6 +463,10 @@ sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
     HIP_TRY(hipMemcpyAsync(&bad, h->flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
     if (bad) return SLA_ERR_PATTERN;
+    int32_t maxlen = 0;
+    HIP_TRY(setup_max_row<IT>(rp, n, h->flag, &maxlen, s));
+    h->slots = slots_for(maxlen);
+    h->slots_t = h->slots;
     if (build_t) {
         HIP_TRY(dmalloc(h, &h->rp_t, sizeof(IT) * (n + 1)));
         HIP_TRY(dmalloc(h, &h->col_t, sizeof(int32_t) * nnz));
@@ -463,6 +475,8 @@ sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
         HIP_TRY(setup_transpose<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->rp_t), h->col_t,
                                     h->perm, s));
         h->has_t = true;
+        HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
+        h->slots_t = slots_for(maxlen);
     }
     HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
     HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
@@ -558,10 +572,10 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             const T *x = reinterpret_cast<const T *>(d_x) + s0 * h->n;
             T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
             if (transpose)
-                HIP_TRY((launch_spmv_perm<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
+                HIP_TRY((launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
                                                  h->perm, v, h->nnz, x, y, h->n, h->n, nb, s)));
             else
-                HIP_TRY((launch_spmv<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp), h->col, v,
+                HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->col, v,
                                             h->nnz, x, y, h->n, h->n, nb, s)));
         }
         return SLA_OK;
@@ -578,7 +592,7 @@ sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *
     return dispatch(h, [&](auto t, auto it) -> sla_status {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        Operator op{h->rp, h->col, h->G};
+        Operator op{h->rp, h->col, h->G, h->slots};
         return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
                                 reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
                                 info, s);

@@ -34,11 +34,11 @@ __device__ __forceinline__ T pdir(bool first, T beta, T omega, T r, T p, T v) {
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
     const int64_t n = A->n;
-    const T *b = A->b;
-    T *x = A->x;
-    T *r = A->r;
-    T *rh = A->rh;
-    const T *ax0 = A->q;
+    const gptr<const T> b = glb(A->b);
+    const gptr<const T> ax0 = glb((const T *)A->q);
+    const gptr<T> x = glb(A->x);
+    const gptr<T> r = glb(A->r);
+    const gptr<T> rh = glb(A->rh);
     const bool x0 = A->use_x0 != 0;
     double rr = 0.0, bb = 0.0;
     const TileRange tr = xcd_tiles(tiles_of(n));
@@ -62,131 +62,158 @@ __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT>
     store_partials<3>(v, A->part, slot);
 }
 
+template <typename T>
+struct PvOwn {
+    T r, p, v, rh;
+};
+
 // Iteration k (0-based, k = iter_a): a pending half-step exit stops here;
-// stop tests on r_k; rho_k = rhat.r_k
-// (0: breakdown); beta = (rho_k/rho_{k-1})(alpha_{k-1}/omega_{k-1});
+// stop tests on r_k; rho_k = rhat.r_k (0: breakdown);
+// beta = (rho_k/rho_{k-1})(alpha_{k-1}/omega_{k-1});
 // p = r + beta (p - omega v) evaluated while gathering (p = r at k = 0);
 // v = A p; partial rhat.v.
-template <typename T, typename IT>
+template <typename T, typename IT, int SLOTS>
 __global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
     const int it = st->iter_a;
-    double tot[3];
-    {
-        const int slot[3] = {kBiRHR, kBiRR, kBiBB};
-        load_totals<3>(A->part, gridDim.x, slot, tot);
-    }
-    if (st->half_exit) {
-        finish(st, SLA_OK, it, st->half_ss);
-        return;
-    }
-    const double rho = tot[0], rr = tot[1];
-    const double bb = it == 0 ? tot[2] : st->bb;
-    if (it == 0 && bb == 0.0) {
-        if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
-        finish(st, SLA_OK, 0, 0.0);
-        return;
-    }
-    if (sqrt(rr) <= A->tol * sqrt(bb)) {
-        finish(st, SLA_OK, it, rr);
-        return;
-    }
-    if (it >= A->maxit) {
-        finish(st, SLA_NOT_CONVERGED, it, rr);
-        return;
-    }
-    if (rho == 0.0) {
-        finish(st, SLA_BREAKDOWN, it, rr);
-        return;
-    }
     const bool first = (it == 0);
-    const int pv = (it + 1) & 1;  // parity slot of iteration k-1
-    const T beta = first ? T(0) : (T)((rho / st->rho[pv]) * (st->alpha[pv] / st->omega[pv]));
-    const T omega = first ? T(0) : (T)st->omega[pv];
-    if (block0()) {
-        st->rho[it & 1] = rho;
-        st->iter_b = it;
-        st->spmv += (first && A->use_x0) ? 2 : 1;  // counts the A x0 product
-        st->nfused += 1;
-        if (first) st->bb = bb;
-    }
-    const T *__restrict__ r = A->r;
-    const T *__restrict__ rh = A->rh;
-    const T *__restrict__ pold = A->p[it & 1];
-    const T *__restrict__ vold = A->v[it & 1];
-    T *__restrict__ pnew = A->p[(it + 1) & 1];
-    T *__restrict__ vnew = A->v[(it + 1) & 1];
-    const IT *__restrict__ rp = A->rp;
-    const int32_t *__restrict__ col = A->col;
-    const T *__restrict__ val = A->val;
     const int64_t n = A->n;
-    __shared__ TileLds<T, IT> sm;
-    double rv = 0.0;
-    auto pk = [&](int64_t c) { return first ? r[c] : pdir(false, beta, omega, r[c], pold[c], vold[c]); };
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
-        spmv_tile<T, IT>(
-            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return pk(c); },
-            [&](int64_t i, T acc) {
-                pnew[i] = pk(i);
-                vnew[i] = acc;
-                rv += (double)rh[i] * (double)acc;
-            });
-    double v[1] = {rv};
+    const gptr<const T> val = glb(A->val);
+    const gptr<const T> r = glb((const T *)A->r);
+    const gptr<const T> rh = glb((const T *)A->rh);
+    const gptr<const T> pold = glb((const T *)A->p[it & 1]);
+    const gptr<const T> vold = glb((const T *)A->v[it & 1]);
+    const gptr<T> pnew = glb(A->p[(it + 1) & 1]);
+    const gptr<T> vnew = glb(A->v[(it + 1) & 1]);
+    __shared__ SpmvLds<T, IT> sm;
+    __shared__ double red[3][kWaves];
+    auto pre = [&]() {
+        const int slot[3] = {kBiRHR, kBiRR, kBiBB};
+        partial_loads<3>(A->part, slot, red);
+    };
+    T beta = T(0), omega = T(0);
+    auto post = [&]() -> bool {
+        if (st->half_exit) {
+            finish(st, SLA_OK, it, st->half_ss);
+            return false;
+        }
+        double tot[3];
+        totals<3>(red, tot);
+        const double rho = tot[0], rr = tot[1];
+        const double bb = it == 0 ? tot[2] : st->bb;
+        if (it == 0 && bb == 0.0) {
+            if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+            finish(st, SLA_OK, 0, 0.0);
+            return false;
+        }
+        if (sqrt(rr) <= A->tol * sqrt(bb)) {
+            finish(st, SLA_OK, it, rr);
+            return false;
+        }
+        if (it >= A->maxit) {
+            finish(st, SLA_NOT_CONVERGED, it, rr);
+            return false;
+        }
+        if (rho == 0.0) {
+            finish(st, SLA_BREAKDOWN, it, rr);
+            return false;
+        }
+        const int pv = (it + 1) & 1;  // parity slot of iteration k-1
+        beta = first ? T(0) : (T)((rho / st->rho[pv]) * (st->alpha[pv] / st->omega[pv]));
+        omega = first ? T(0) : (T)st->omega[pv];
+        if (block0()) {
+            st->rho[it & 1] = rho;
+            st->iter_b = it;
+            st->spmv += (first && A->use_x0) ? 2 : 1;  // counts the A x0 product
+            st->nfused += 1;
+            if (first) st->bb = bb;
+        }
+        return true;
+    };
+    // p_k at one index; the first iteration has beta = omega = 0 and reads r
+    // in place of the (not yet written) previous p and v, which gives r
+    // exactly
+    const gptr<const T> pp = first ? r : pold;
+    const gptr<const T> vp = first ? r : vold;
+    auto pk = [&](const G3<T> &g) -> T { return pdir(false, beta, omega, g.a, g.b, g.c); };
+    double rv_acc = 0.0;
+    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, 4>(
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
+        [&](int32_t c) { return G3<T>{r[c], pp[c], vp[c]}; }, pk,
+        [&](int64_t i) { return PvOwn<T>{r[i], pp[i], vp[i], rh[i]}; },
+        [&](int64_t i, T acc, const PvOwn<T> &o) {
+            pnew[i] = pk(G3<T>{o.r, o.p, o.v});
+            vnew[i] = acc;
+            rv_acc += (double)o.rh * (double)acc;
+        },
+        pre, post);
+    if (!go) return;
+    double v[1] = {rv_acc};
     const int slot[1] = {kBiRV};
     store_partials<1>(v, A->part, slot);
 }
 
+template <typename T>
+struct StOwn {
+    T r, v;
+};
+
 // Iteration k (k = iter_b): alpha = rho_k / rhat.v (0: breakdown);
 // s = r - alpha v evaluated while gathering, t = A s; partials t.s, t.t, s.s.
-template <typename T, typename IT>
+template <typename T, typename IT, int SLOTS>
 __global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
     const int it = st->iter_b;
-    double tot[1];
-    {
-        const int slot[1] = {kBiRV};
-        load_totals<1>(A->part, gridDim.x, slot, tot);
-    }
-    if (tot[0] == 0.0) {
-        finish(st, SLA_BREAKDOWN, it, 0.0);
-        return;
-    }
-    const double alpha_d = st->rho[it & 1] / tot[0];
-    const T alpha = (T)alpha_d;
-    if (block0()) {
-        st->alpha[it & 1] = alpha_d;
-        st->iter_c = it;
-        st->nfused += 1;
-    }
-    const T *__restrict__ r = A->r;
-    const T *__restrict__ v = A->v[(it + 1) & 1];
-    T *__restrict__ s = A->s;
-    T *__restrict__ tv = A->t;
-    const IT *__restrict__ rp = A->rp;
-    const int32_t *__restrict__ col = A->col;
-    const T *__restrict__ val = A->val;
     const int64_t n = A->n;
-    __shared__ TileLds<T, IT> sm;
+    const gptr<const T> val = glb(A->val);
+    const gptr<const T> r = glb((const T *)A->r);
+    const gptr<const T> v = glb((const T *)A->v[(it + 1) & 1]);
+    const gptr<T> s = glb(A->s);
+    const gptr<T> tv = glb(A->t);
+    __shared__ SpmvLds<T, IT> sm;
+    __shared__ double red[1][kWaves];
+    auto pre = [&]() {
+        const int slot[1] = {kBiRV};
+        partial_loads<1>(A->part, slot, red);
+    };
+    T alpha = T(0);
+    auto post = [&]() -> bool {
+        double tot[1];
+        totals<1>(red, tot);
+        if (tot[0] == 0.0) {
+            finish(st, SLA_BREAKDOWN, it, 0.0);
+            return false;
+        }
+        const double alpha_d = st->rho[it & 1] / tot[0];
+        alpha = (T)alpha_d;
+        if (block0()) {
+            st->alpha[it & 1] = alpha_d;
+            st->iter_c = it;
+            st->nfused += 1;
+        }
+        return true;
+    };
+    auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0;
-    auto sk = [&](int64_t c) { return fmaB(-alpha, v[c], r[c]); };
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
-        spmv_tile<T, IT>(
-            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return sk(c); },
-            [&](int64_t i, T acc) {
-                const T si = sk(i);
-                s[i] = si;
-                tv[i] = acc;
-                ts += (double)acc * (double)si;
-                tt += (double)acc * (double)acc;
-                ss += (double)si * (double)si;
-            });
-    double red[3] = {ts, tt, ss};
+    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
+        [&](int32_t c) { return G2<T>{r[c], v[c]}; }, sk,
+        [&](int64_t i) { return StOwn<T>{r[i], v[i]}; },
+        [&](int64_t i, T acc, const StOwn<T> &o) {
+            const T si = sk(G2<T>{o.r, o.v});
+            s[i] = si;
+            tv[i] = acc;
+            ts += (double)acc * (double)si;
+            tt += (double)acc * (double)acc;
+            ss += (double)si * (double)si;
+        },
+        pre, post);
+    if (!go) return;
+    double red3[3] = {ts, tt, ss};
     const int slot[3] = {kBiTS, kBiTT, kBiSS};
-    store_partials<3>(red, A->part, slot);
+    store_partials<3>(red3, A->part, slot);
 }
 
 // Iteration k (k = iter_c): half-step exit when ||s|| <= tol ||b||
@@ -212,12 +239,12 @@ __global__ __launch_bounds__(kBlock) void bicg_update_kernel(const IterArgs<T, I
     const T alpha = (T)st->alpha[it & 1];
     const double omega_d = half ? 0.0 : tot[0] / tot[1];
     const T omega = (T)omega_d;
-    const T *__restrict__ p = A->p[(it + 1) & 1];
-    const T *__restrict__ s = A->s;
-    const T *__restrict__ tv = A->t;
-    const T *__restrict__ rh = A->rh;
-    T *__restrict__ x = A->x;
-    T *__restrict__ r = A->r;
+    const gptr<const T> p = glb((const T *)A->p[(it + 1) & 1]);
+    const gptr<const T> s = glb((const T *)A->s);
+    const gptr<const T> tv = glb((const T *)A->t);
+    const gptr<const T> rh = glb((const T *)A->rh);
+    const gptr<T> x = glb(A->x);
+    const gptr<T> r = glb(A->r);
     const int64_t n = A->n;
     double rhr = 0.0, rr = 0.0;
     const TileRange tr = xcd_tiles(tiles_of(n));
@@ -265,14 +292,14 @@ hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) 
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    bicg_pv_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a);
+hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+    SLA_DISPATCH_SLOTS(slots, bicg_pv_kernel<T, IT, kS><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a));
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    bicg_st_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a);
+hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+    SLA_DISPATCH_SLOTS(slots, bicg_st_kernel<T, IT, kS><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a));
     return hipGetLastError();
 }
 

@@ -1,22 +1,30 @@
 // Conjugate gradients with an optional Jacobi preconditioner M = diag(A)
 // (torch-sla explainer, Methodology section 1 and the Significance section:
-// the native backend is an iterative solver with a Jacobi preconditioner;
-// steps as in Saad, Iterative Methods for Sparse Linear Systems, Alg. 9.1).
+// the native backend is an iterative solver with a Jacobi preconditioner).
 //
-// Grid path, two kernels per iteration over one system:
-//   cg_spmv:   stop test on r_k; beta = rho_k / rho_{k-1};
-//              p_k = z_k + beta p_{k-1} (p_0 = z_0) evaluated while gathering,
-//              q = A p_k, stored p_k and q; partial p.q
-//   cg_update: alpha = rho_k / p.q (p.q <= 0: breakdown); x += alpha p,
-//              r -= alpha q, z = M^-1 r; partials r.z and r.r
-// Each kernel stores per-block partial sums with plain stores; every block
-// of the next kernel adds them in block order, so all blocks derive the same
-// scalars and no grid-wide fence is needed (a release at agent scope costs an
-// L2 write-back per block on a multi-XCD part).  p is double-buffered by
-// iteration parity because cg_spmv reads the old p at neighbouring rows while
-// it writes the new one.  Every kernel returns at entry once the device-side
-// `done` flag is set, so the host can enqueue many iterations (HIP graph
-// replays) and poll rarely.
+// Grid path: the Chronopoulos-Gear arrangement of preconditioned CG, which
+// produces the same iterates as the textbook recurrence (Saad, Iterative
+// Methods for Sparse Linear Systems, Alg. 9.1) in exact arithmetic but needs
+// one global reduction per iteration instead of two:
+//   r_0 = b - A x_0, u_0 = M^-1 r_0, w_0 = A u_0
+//   iteration i: gamma_i = r_i.u_i, delta_i = w_i.u_i
+//     beta_i  = gamma_i / gamma_{i-1}                       (beta_0 = 0)
+//     alpha_i = gamma_i / (delta_i - beta_i gamma_i / alpha_{i-1})
+//             = gamma_i / (p_i . A p_i)                     (<= 0: breakdown)
+//     p_i = u_i + beta_i p_{i-1},  s_i = w_i + beta_i s_{i-1}  (= A p_i)
+//     x_{i+1} = x_i + alpha_i p_i,  r_{i+1} = r_i - alpha_i s_i
+//     u_{i+1} = M^-1 r_{i+1},  w_{i+1} = A u_{i+1}
+// One kernel does a whole iteration: the vector updates of its rows, and the
+// product w_{i+1} = A u_{i+1} with u_{i+1} evaluated at each gathered column
+// from r_i, w_i, s_{i-1} and M^-1.  It stores per-block partial sums of
+// gamma_{i+1}, delta_{i+1} and ||r_{i+1}||^2 with plain stores; every block
+// of the next launch adds them in block order (identical scalars everywhere,
+// no grid-wide fence).  r, w, s and the partial-sum slots alternate between
+// two buffers by iteration parity, which each launch receives as an argument
+// (neighbouring rows still read the old vectors while a block writes the new
+// ones).  Every launch returns at entry once the device-side `done` flag is
+// set, so the host enqueues many iterations (HIP graph replays) and polls
+// rarely.
 //
 // Block path: one 1024-thread workgroup runs the whole solve of one small
 // system (n <= 4096): vectors live in registers, the search direction in LDS
@@ -32,157 +40,182 @@ __device__ __forceinline__ T fmaT(T a, T b, T c) {
     return fma(a, b, c);
 }
 
-// r = b - A x0 (or b with x = 0), z = M^-1 r; partials r.z, r.r, b.b.
-template <typename T, typename IT, bool JAC>
+// Vectors of the grid CG in the workspace: r by parity = {r, z}, w = {q, rh},
+// s = {s, t}, p = p[0]; t doubles as A x0 before the first iteration.
+// (Selected with conditionals: a pointer array indexed by a runtime parity
+// would live in scratch memory.)
+template <typename T, typename IT>
+__device__ __forceinline__ T *cg_r(const IterArgs<T, IT> *A, int ph) { return ph ? A->z : A->r; }
+template <typename T, typename IT>
+__device__ __forceinline__ T *cg_w(const IterArgs<T, IT> *A, int ph) { return ph ? A->rh : A->q; }
+template <typename T, typename IT>
+__device__ __forceinline__ T *cg_s(const IterArgs<T, IT> *A, int ph) { return ph ? A->t : A->s; }
+
+template <typename T>
+struct CgOwn {
+    T r, w, s, d, p, x;
+};
+
+// r_0 = b - A x_0, u_0 = M^-1 r_0, w_0 = A u_0 (A x_0 is in t; the host
+// zeroes t when there is no initial guess); partials gamma_0, delta_0,
+// ||r_0||^2 and ||b||^2 (parity-0 slots).
+template <typename T, typename IT, bool JAC, int SLOTS>
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
     const int64_t n = A->n;
-    const T *b = A->b;
-    T *x = A->x;
-    T *r = A->r;
-    T *z = A->z;
-    const T *dinv = A->dinv;
-    const T *ax0 = A->q;  // A x0 when use_x0
+    const gptr<const T> b = glb(A->b);
+    const gptr<const T> ax0 = glb((const T *)cg_s(A, 1));
+    const gptr<const T> dinv = glb(A->dinv);
+    const gptr<const T> val = glb(A->val);
+    const gptr<T> x = glb(A->x);
+    const gptr<T> r0 = glb(cg_r(A, 0));
+    const gptr<T> w0 = glb(cg_w(A, 0));
     const bool x0 = A->use_x0 != 0;
-    double rz = 0.0, rr = 0.0, bb = 0.0;
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t i = t * kTileRows + threadIdx.x;
-        if (i < n) {
-            const T bi = b[i];
-            T ri = bi;
-            if (x0)
-                ri = bi - ax0[i];
-            else
-                x[i] = T(0);
-            r[i] = ri;
-            T zi = ri;
-            if (JAC) {
-                zi = dinv[i] * ri;
-                z[i] = zi;
-            }
-            rz += (double)ri * (double)zi;
+    __shared__ SpmvLds<T, IT> sm;
+    double ga = 0.0, de = 0.0, rr = 0.0, bb = 0.0;
+    auto load = [&](int64_t c) { return G3<T>{b[c], ax0[c], JAC ? dinv[c] : T(1)}; };
+    auto u0 = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
+    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
+        load, u0, load,
+        [&](int64_t i, T acc, const G3<T> &o) {
+            const T ri = o.a - o.b;
+            const T ui = u0(o);
+            r0[i] = ri;
+            w0[i] = acc;
+            if (!x0) x[i] = T(0);
+            ga += (double)ri * (double)ui;
+            de += (double)acc * (double)ui;
             rr += (double)ri * (double)ri;
-            bb += (double)bi * (double)bi;
-        }
-    }
-    double v[3] = {rz, rr, bb};
-    const int slot[3] = {kCgRZ, kCgRR, kCgBB};
-    store_partials<3>(v, A->part, slot);
+            bb += (double)o.a * (double)o.a;
+        },
+        NoPre(), NoPost());
+    double v[4] = {ga, de, rr, bb};
+    const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
+    store_partials<4>(v, A->part, slot);
 }
 
-// Iteration k (k = iter_a): stop test on r_k, beta_k = rho_k / rho_{k-1},
-// p_k = z_k + beta_k p_{k-1} evaluated while gathering, q = A p_k,
-// partial p_k.q.
-template <typename T, typename IT, bool JAC>
-__global__ __launch_bounds__(kBlock) void cg_spmv_kernel(const IterArgs<T, IT> *__restrict__ A) {
+// Iteration i (i = st->iter_p[ph], ph = i & 1): stop tests on r_i, the
+// scalars, the row updates and w_{i+1} = A u_{i+1}.
+#ifndef SLA_CG_ROUND
+#define SLA_CG_ROUND 4
+#endif
+template <typename T, typename IT, bool JAC, int SLOTS>
+__global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A,
+                                                         int ph) {
     SolveState *st = A->st;
     if (load_done(st)) return;
-    const int it = st->iter_a;
-    double tot[3];
-    {
-        const int slot[3] = {kCgRZ, kCgRR, kCgBB};
-        load_totals<3>(A->part, gridDim.x, slot, tot);
-    }
-    const double rho = tot[0], rr = tot[1];
-    const double bb = it == 0 ? tot[2] : st->bb;
-    // stop tests on the residual left by the previous update (or the start)
-    if (it == 0 && st->zero_diag) {
-        finish(st, SLA_ERR_ZERO_DIAG, 0, rr);
-        return;
-    }
-    if (it == 0 && bb == 0.0) {
-        if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
-        finish(st, SLA_OK, 0, 0.0);
-        return;
-    }
-    if (sqrt(rr) <= A->tol * sqrt(bb)) {
-        finish(st, SLA_OK, it, rr);
-        return;
-    }
-    if (it >= A->maxit) {
-        finish(st, SLA_NOT_CONVERGED, it, rr);
-        return;
-    }
+    const int it = st->iter_p[ph];
     const bool first = (it == 0);
-    const T beta = first ? T(0) : (T)(rho / st->rho[(it + 1) & 1]);
-    if (block0()) {
-        st->rho[it & 1] = rho;
-        st->iter_b = it;
-        st->spmv += (first && A->use_x0) ? 2 : 1;  // counts the A x0 product
-        st->nfused += 1;
-        if (first) st->bb = bb;
-    }
-    const T *__restrict__ zz = JAC ? A->z : A->r;
-    const T *__restrict__ pold = A->p[it & 1];
-    T *__restrict__ pnew = A->p[(it + 1) & 1];
-    const IT *__restrict__ rp = A->rp;
-    const int32_t *__restrict__ col = A->col;
-    const T *__restrict__ val = A->val;
-    T *__restrict__ q = A->q;
     const int64_t n = A->n;
-    __shared__ TileLds<T, IT> sm;
-    double pq = 0.0;
-    auto pdir = [&](int64_t c) { return first ? zz[c] : fmaT(beta, pold[c], zz[c]); };
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
-        spmv_tile<T, IT>(
-            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return pdir(c); },
-            [&](int64_t i, T acc) {
-                const T pi = pdir(i);
-                pnew[i] = pi;
-                q[i] = acc;
-                pq += (double)pi * (double)acc;
-            });
-    double v[1] = {pq};
-    const int slot[1] = {kCgPQ};
-    store_partials<1>(v, A->part, slot);
-}
+    const gptr<const T> val = glb(A->val);
+    const gptr<const T> dinv = glb(A->dinv);
+    const gptr<const T> rc = glb((const T *)cg_r(A, ph));
+    const gptr<const T> wc = glb((const T *)cg_w(A, ph));
+    const gptr<const T> sp = glb((const T *)cg_s(A, ph ^ 1));
+    const gptr<T> rn = glb(cg_r(A, ph ^ 1));
+    const gptr<T> wn = glb(cg_w(A, ph ^ 1));
+    const gptr<T> sc = glb(cg_s(A, ph));
+    const gptr<T> p = glb(A->p[0]);
+    const gptr<T> x = glb(A->x);
+    __shared__ SpmvLds<T, IT> sm;
+    __shared__ double red[4][kWaves];
 
-// Iteration k (k = iter_b): alpha = rho_k / p.q (p.q <= 0: breakdown);
-// x += alpha p, r -= alpha q, z = M^-1 r; partials r.z and r.r.
-template <typename T, typename IT, bool JAC>
-__global__ __launch_bounds__(kBlock) void cg_update_kernel(const IterArgs<T, IT> *__restrict__ A) {
-    SolveState *st = A->st;
-    if (load_done(st)) return;
-    const int it = st->iter_b;
-    double tot[1];
-    {
-        const int slot[1] = {kCgPQ};
-        load_totals<1>(A->part, gridDim.x, slot, tot);
-    }
-    if (!(tot[0] > 0.0)) {
-        finish(st, SLA_BREAKDOWN, it, 0.0);
-        return;
-    }
-    const T alpha = (T)(st->rho[it & 1] / tot[0]);
-    if (block0()) st->iter_a = it + 1;
-    const T *__restrict__ p = A->p[(it + 1) & 1];
-    const T *__restrict__ q = A->q;
-    const T *__restrict__ dinv = A->dinv;
-    T *__restrict__ x = A->x;
-    T *__restrict__ r = A->r;
-    T *__restrict__ z = A->z;
-    const int64_t n = A->n;
-    double rz = 0.0, rr = 0.0;
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t i = t * kTileRows + threadIdx.x;
-        if (i < n) {
-            x[i] = fmaT(alpha, p[i], x[i]);
-            const T ri = fmaT(-alpha, q[i], r[i]);
-            r[i] = ri;
-            T zi = ri;
-            if (JAC) {
-                zi = dinv[i] * ri;
-                z[i] = zi;
-            }
-            rz += (double)ri * (double)zi;
-            rr += (double)ri * (double)ri;
+    // previous launch's partial sums, loaded with the first row pointers
+    auto pre = [&]() {
+        if (it == 0) {
+            const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
+            partial_loads<4>(A->part, slot, red);
+        } else {
+            const int slot[3] = {ph ? kCgGA1 : kCgGA, ph ? kCgDE1 : kCgDE, ph ? kCgRR1 : kCgRR};
+            partial_loads<3>(A->part, slot, red);
         }
-    }
-    double v[2] = {rz, rr};
-    const int slot[2] = {kCgRZ, kCgRR};
-    store_partials<2>(v, A->part, slot);
+    };
+    T beta = T(0), alpha = T(0);
+    auto post = [&]() -> bool {
+        double tot[4];
+        if (it == 0) {
+            totals<4>(red, tot);
+        } else {
+            double t3[3];
+            totals<3>(red, t3);
+            tot[0] = t3[0];
+            tot[1] = t3[1];
+            tot[2] = t3[2];
+            tot[3] = st->bb;
+        }
+        const double gamma = tot[0], delta = tot[1], rr = tot[2], bb = tot[3];
+        if (it == 0 && st->zero_diag) {
+            finish(st, SLA_ERR_ZERO_DIAG, 0, rr);
+            return false;
+        }
+        if (it == 0 && bb == 0.0) {
+            if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+            finish(st, SLA_OK, 0, 0.0);
+            return false;
+        }
+        if (sqrt(rr) <= A->tol * sqrt(bb)) {
+            finish(st, SLA_OK, it, rr);
+            return false;
+        }
+        if (it >= A->maxit) {
+            finish(st, SLA_NOT_CONVERGED, it, rr);
+            return false;
+        }
+        const double beta_d = first ? 0.0 : gamma / st->rho[ph ^ 1];
+        const double den = first ? delta : delta - beta_d * gamma / st->alpha[ph ^ 1];
+        if (!(den > 0.0)) {
+            finish(st, SLA_BREAKDOWN, it, rr);
+            return false;
+        }
+        const double alpha_d = gamma / den;
+        if (block0()) {
+            st->rho[ph] = gamma;
+            st->alpha[ph] = alpha_d;
+            st->iter_p[ph ^ 1] = it + 1;
+            st->nfused += 1;
+            st->spmv += first ? (A->use_x0 ? 3 : 2) : 1;  // init (and A x0) products
+            if (first) st->bb = bb;
+        }
+        beta = (T)beta_d;
+        alpha = (T)alpha_d;
+        return true;
+    };
+    // s_i and u_{i+1} from the four vectors at one index (the gathers and the
+    // row updates use the same expressions, so they see the same values).
+    // The first iteration has beta = 0 and reads w and r in place of the
+    // (not yet written) previous s and p: fma(0, finite, w) == w exactly.
+    const gptr<const T> sprev = first ? wc : sp;
+    const gptr<const T> pprev = first ? rc : (gptr<const T>)p;
+    auto s_of = [&](T w, T sv) -> T { return fmaT(beta, sv, w); };
+    auto u_of = [&](const G4<T> &g) -> T {
+        const T rv = fmaT(-alpha, s_of(g.b, g.c), g.a);
+        return JAC ? g.d * rv : rv;
+    };
+    double g = 0.0, d = 0.0, q = 0.0;
+    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, SLA_CG_ROUND>(
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
+        [&](int32_t c) { return G4<T>{rc[c], wc[c], sprev[c], JAC ? dinv[c] : T(1)}; }, u_of,
+        [&](int64_t i) { return CgOwn<T>{rc[i], wc[i], sprev[i], JAC ? dinv[i] : T(1), pprev[i], x[i]}; },
+        [&](int64_t i, T acc, const CgOwn<T> &o) {
+            const T ui = JAC ? o.d * o.r : o.r;
+            const T pi = fmaT(beta, o.p, ui);
+            const T si = s_of(o.w, o.s);
+            const T rni = fmaT(-alpha, si, o.r);
+            const T uni = JAC ? o.d * rni : rni;
+            x[i] = fmaT(alpha, pi, o.x);
+            p[i] = pi;
+            sc[i] = si;
+            rn[i] = rni;
+            wn[i] = acc;
+            g += (double)rni * (double)uni;
+            d += (double)acc * (double)uni;
+            q += (double)rni * (double)rni;
+        },
+        pre, post);
+    if (!go) return;
+    double v[3] = {g, d, q};
+    const int slot[3] = {ph ? kCgGA : kCgGA1, ph ? kCgDE : kCgDE1, ph ? kCgRR : kCgRR1};
+    store_partials<3>(v, A->part, slot);
 }
 
 // ------------------------------------------------------------ block path
@@ -381,32 +414,25 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     }
 
 template <typename T, typename IT>
-hipError_t launch_cg_init(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+hipError_t launch_cg_init(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
     const int grid = grid_for_tiles(tiles_of(n));
-    if (jac)
-        cg_init_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(a);
-    else
-        cg_init_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(a);
+    if (jac) {
+        SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, true, kS><<<grid, kBlock, 0, s>>>(a));
+    } else {
+        SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, false, kS><<<grid, kBlock, 0, s>>>(a));
+    }
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_spmv(int, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
+                          hipStream_t s) {
     const int grid = grid_for_tiles(tiles_of(n));
-    if (jac)
-        cg_spmv_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(a);
-    else
-        cg_spmv_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-template <typename T, typename IT>
-hipError_t launch_cg_update(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
-    if (jac)
-        cg_update_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(a);
-    else
-        cg_update_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(a);
+    if (jac) {
+        SLA_DISPATCH_SLOTS(slots, cg_iter_kernel<T, IT, true, kS><<<grid, kBlock, 0, s>>>(a, ph));
+    } else {
+        SLA_DISPATCH_SLOTS(slots, cg_iter_kernel<T, IT, false, kS><<<grid, kBlock, 0, s>>>(a, ph));
+    }
     return hipGetLastError();
 }
 
@@ -429,12 +455,10 @@ hipError_t launch_block_cg(int G, const BlockCgParams &p, int batch, hipStream_t
 }
 
 #define SLA_INST(T, IT)                                                                         \
-    template hipError_t launch_cg_init<T, IT>(bool, const IterArgs<T, IT> *, int64_t,           \
+    template hipError_t launch_cg_init<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t,      \
                                               hipStream_t);                                     \
-    template hipError_t launch_cg_spmv<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t,      \
+    template hipError_t launch_cg_iter<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t, int, \
                                               hipStream_t);                                     \
-    template hipError_t launch_cg_update<T, IT>(bool, const IterArgs<T, IT> *, int64_t,         \
-                                                hipStream_t);                                   \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
 
 SLA_INST(float, int32_t)

@@ -12,41 +12,40 @@
 
 namespace sla {
 
-template <typename T, typename IT>
+template <typename T, typename IT, int SLOTS>
 __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
                                                       const int32_t *__restrict__ col,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride) {
-    __shared__ TileLds<T, IT> sm;
+    __shared__ SpmvLds<T, IT> sm;
     const int sys = blockIdx.y;
-    val += (int64_t)sys * val_stride;
-    x += (int64_t)sys * vec_stride;
-    y += (int64_t)sys * vec_stride;
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
-        spmv_tile<T, IT>(
-            t, n, rp, col, sm, [&](IT k) { return val[k]; }, [&](int32_t c) { return x[c]; },
-            [&](int64_t i, T s) { y[i] = s; });
+    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
+    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
+    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+        xcd_tiles(tiles_of(n)), n, glb(rp), glb(col), sm, [&](IT k) { return v[k]; },
+        [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
+        [&](int64_t i, T s, int) { ys[i] = s; }, NoPre(), NoPost());
 }
 
 // y = A^T x through the transpose map: rp/col describe A^T and the value of
 // A^T entry kt is val[perm[kt]].
-template <typename T, typename IT>
+template <typename T, typename IT, int SLOTS>
 __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ perm,
     const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
     int64_t n, int64_t vec_stride) {
-    __shared__ TileLds<T, IT> sm;
+    __shared__ SpmvLds<T, IT> sm;
     const int sys = blockIdx.y;
-    val += (int64_t)sys * val_stride;
-    x += (int64_t)sys * vec_stride;
-    y += (int64_t)sys * vec_stride;
-    const TileRange tr = xcd_tiles(tiles_of(n));
-    for (int64_t t = tr.first; t < tr.end; t += tr.stride)
-        spmv_tile<T, IT>(
-            t, n, rp, col, sm, [&](IT k) { return val[perm[k]]; },
-            [&](int32_t c) { return x[c]; }, [&](int64_t i, T s) { y[i] = s; });
+    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
+    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
+    const gptr<const int32_t> pm = glb(perm);
+    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+        xcd_tiles(tiles_of(n)), n, glb(rp), glb(col), sm, [&](IT k) { return v[pm[k]]; },
+        [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
+        [&](int64_t i, T s, int) { ys[i] = s; }, NoPre(), NoPost());
 }
 
 // grad[k] = -lambda[row(k)] * x[col[k]].  Short tiles: each thread marks the
@@ -144,21 +143,22 @@ __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T
 // ------------------------------------------------------------------ launchers
 
 template <typename T, typename IT>
-hipError_t launch_spmv(int, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
-                       const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
-                       hipStream_t s) {
+hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const T *val,
+                       int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
+                       int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    spmv_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, val, val_stride, x, y, n, vec_stride);
+    SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS><<<grid, kBlock, 0, s>>>(
+                                  rp, col, val, val_stride, x, y, n, vec_stride));
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int, const IT *rp, const int32_t *col, const int32_t *perm,
+hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
                             int64_t vec_stride, int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    spmv_perm_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, perm, val, val_stride, x, y, n,
-                                                    vec_stride);
+    SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS><<<grid, kBlock, 0, s>>>(
+                                  rp, col, perm, val, val_stride, x, y, n, vec_stride));
     return hipGetLastError();
 }
 

@@ -87,6 +87,19 @@ __global__ __launch_bounds__(kBlock) void rowptr_t_kernel(const int32_t *__restr
     }
 }
 
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ rp, int64_t n,
+                                                         int32_t *out) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int64_t m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const int64_t len = (int64_t)(rp[i + 1] - rp[i]);
+        m = len > m ? len : m;
+    }
+    const int32_t mi = m > 0x7fffffff ? 0x7fffffff : (int32_t)m;
+    atomicMax(out, mi);
+}
+
 static unsigned blocks_for(int64_t m) {
     int64_t b = (m + kBlock - 1) / kBlock;
     if (b > 65536) b = 65536;
@@ -108,6 +121,18 @@ hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t n
     if (h) return hipSuccess;  // flag stays set: row_ptr invalid, columns not read
     check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
     return hipGetLastError();
+}
+
+// Longest row of a valid pattern (synchronizes the stream).
+template <typename IT>
+hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s) {
+    hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
+    if (e != hipSuccess) return e;
+    max_row_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(out, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return e;
+    return hipStreamSynchronize(s);
 }
 
 template <typename IT>
@@ -150,6 +175,10 @@ template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, in
                                             int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
                                             int64_t *, int32_t *, hipStream_t);
+template hipError_t setup_max_row<int32_t>(const int32_t *, int64_t, int32_t *, int32_t *,
+                                           hipStream_t);
+template hipError_t setup_max_row<int64_t>(const int64_t *, int64_t, int32_t *, int32_t *,
+                                           hipStream_t);
 template hipError_t setup_transpose<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
                                              int32_t *, int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_transpose<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,

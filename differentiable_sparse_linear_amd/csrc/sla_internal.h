@@ -39,13 +39,14 @@ constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread
 // iteration counter is kept once per kernel role (iter_a read by the first
 // kernel of an iteration, iter_b by the second, iter_c by the third).
 struct SolveState {
-    double rho[2];    // CG: r.z ; BiCGStab: rhat.r, by iteration parity
-    double alpha[2];  // BiCGStab alpha by parity
+    double rho[2];    // CG: gamma = r.u ; BiCGStab: rhat.r, by iteration parity
+    double alpha[2];  // alpha by iteration parity
     double omega[2];  // BiCGStab omega by parity
     double bb;        // ||rhs||^2
     double rr;        // ||r||^2 at the stop
     double half_ss;   // BiCGStab ||s||^2 of a half-step exit
-    int32_t iter_a, iter_b, iter_c;
+    int32_t iter_a, iter_b, iter_c;  // BiCGStab kernels
+    int32_t iter_p[2];  // CG: iteration of the launch with parity 0 / 1
     int32_t iter;     // completed iterations at the stop
     int32_t done;     // 1 once converged / stopped (relaxed atomic access)
     int32_t status;   // sla_status of the system
@@ -61,7 +62,7 @@ struct SolveState {
 // kernel reads only slots that the previous kernel wrote and writes only
 // slots that it does not read.
 enum : int {
-    kCgPQ = 0, kCgRZ = 1, kCgRR = 2, kCgBB = 3,
+    kCgGA = 0, kCgGA1 = 1, kCgDE = 2, kCgDE1 = 3, kCgRR = 4, kCgRR1 = 5, kCgBB = 6,
     kBiRV = 0, kBiTS = 1, kBiTT = 2, kBiSS = 3, kBiRHR = 4, kBiRR = 5, kBiBB = 6,
 };
 
@@ -200,6 +201,10 @@ inline int grid_for_tiles(int64_t ntiles) {
 
 __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileRows - 1) / kTileRows; }
 
+// Gather slots per row for the row-per-lane SpMV from the longest row:
+// 4, 6 or 8 (longer rows finish with a loop).
+inline int slots_for(int64_t max_len) { return max_len <= 4 ? 4 : (max_len <= 6 ? 6 : 8); }
+
 // Lanes per row from the mean row length: the smallest power of two >= mean,
 // in [2, 64].
 inline int lanes_for(int64_t n, int64_t nnz) {
@@ -212,12 +217,13 @@ inline int lanes_for(int64_t n, int64_t nnz) {
 // ---------------------------------------------------------------- launchers
 // (defined in the .hip files; all return hipError_t of the launch)
 
+// The `slots` argument of the SpMV-shaped launchers is slots_for(longest row).
 template <typename T, typename IT>
-hipError_t launch_spmv(int G, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
+hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
                        const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
                        hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int G, const IT *rp, const int32_t *col, const int32_t *perm,
+hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
                             int64_t vec_stride, int batch, hipStream_t s);
 template <typename T, typename IT>
@@ -229,21 +235,21 @@ template <typename T, typename IT>
 hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
                        hipStream_t s);
 
-// CG (grid path, one system)
+// CG (grid path, one system): init, then one launch per iteration with the
+// iteration's parity
 template <typename T, typename IT>
-hipError_t launch_cg_init(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_cg_init(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_cg_spmv(int G, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
-template <typename T, typename IT>
-hipError_t launch_cg_update(bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
+                          hipStream_t s);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int G, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
@@ -273,6 +279,8 @@ hipError_t launch_block_cg(int G, const BlockCgParams &p, int batch, hipStream_t
 template <typename IT>
 hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
                           int32_t *flag, hipStream_t s);
+template <typename IT>
+hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s);
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
                            int32_t *col_t, int32_t *perm, hipStream_t s);
