@@ -51,6 +51,7 @@ struct sla_ctx {
     void *val_t = nullptr;
     int G = 8;       // lanes per row of the one-workgroup solver
     int slots = 8;   // gather slots per row (A), from its longest row
+    int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
     void *vec = nullptr;
     SolveState *st = nullptr;
@@ -334,7 +335,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
     const bool cg = o.method == SLA_CG;
     double prof_ms = 0.0;
     int64_t prof_launches = 0;
-    const bool block_path = cg && n <= kBlockSolveMaxN && op.G <= 16 && !o.profile;
+    const bool block_path = cg && n <= kBlockSolveMaxN && !o.profile;
     if (block_path) {
         BlockCgParams p;
         p.val = val;
@@ -357,7 +358,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
             q.b = reinterpret_cast<const T *>(b) + s0 * n;
             q.x = reinterpret_cast<T *>(x) + s0 * n;
             q.st = h->st + s0;
-            HIP_TRY(launch_block_cg<T, IT>(op.G, q, nb, s));
+            HIP_TRY(launch_block_cg<T, IT>(h->max_len, q, nb, s));
         }
     } else {
         for (int64_t sys = 0; sys < B; ++sys) {
@@ -466,6 +467,7 @@ sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
     int32_t maxlen = 0;
     HIP_TRY(setup_max_row<IT>(rp, n, h->flag, &maxlen, s));
     h->slots = slots_for(maxlen);
+    h->max_len = maxlen;
     h->slots_t = h->slots;
     if (build_t) {
         HIP_TRY(dmalloc(h, &h->rp_t, sizeof(IT) * (n + 1)));

@@ -221,9 +221,11 @@ __global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *
 // ------------------------------------------------------------ block path
 
 constexpr int kBW = kBlockSolveThreads / 64;  // waves per workgroup
-constexpr int kMaxRpt = kBlockSolveMaxN / kBlockSolveThreads;
 
 // Sum over the workgroup; every thread receives the same, order-fixed total.
+// Wavefront sums go to LDS; after the barrier lane l of every wavefront reads
+// wavefront l's sum and a 16-lane butterfly adds them (the same tree in every
+// wavefront, so every thread gets bitwise the same total).
 template <int NR>
 __device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -234,104 +236,161 @@ __device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW])
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        double s = 0.0;
+    for (int r = 0; r < NR; ++r) v[r] = group_sum<kBW>(slots[r][lane & (kBW - 1)]);
+}
+
+// One row's matrix entries, SLOTS slots (slots past the row repeat its last
+// entry; they are left out of the sum).  The block path has n <= 4096, so an
+// offset inside one system fits 32 bits and a column 16 bits.
+template <typename T, int SLOTS>
+__device__ __forceinline__ void block_row_load(gptr<const T> val, gptr<const int32_t> col, int lo,
+                                               int len, T (&v)[SLOTS], int32_t (&c)[SLOTS]) {
+    const int lastk = len > 0 ? len - 1 : 0;
 #pragma unroll
-        for (int w = 0; w < kBW; ++w) s += slots[r][w];
-        v[r] = s;
+    for (int k = 0; k < SLOTS; ++k) {
+        const int idx = lo + (k < lastk ? k : lastk);
+        v[k] = val[idx];
+        c[k] = col[idx];
     }
 }
 
-// Row ownership: the SpMV sweeps rows in passes of RPP = 1024/G rows, one row
-// per G-lane group; pass `ps` covers rows ps*RPP + group.  The lane
-// (ps % G) of that group keeps the row's vector entries in register slot
-// ps / G, so the product lands in registers without an LDS round trip.
-template <typename T, typename IT, int G>
+// The row's product with the LDS-resident vector, in entry order; colf(k)
+// gives slot k's column.
+template <typename T, int SLOTS, typename CF>
+__device__ __forceinline__ T block_row_dot(const T (&v)[SLOTS], CF colf, gptr<const T> val,
+                                           gptr<const int32_t> col, const T *ps, int lo, int len) {
+    T acc = T(0);
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k) {
+        const T term = v[k] * ps[colf(k)];
+        acc = k < len ? acc + term : acc;
+    }
+    for (int k = SLOTS; k < len; ++k) acc += val[lo + k] * ps[col[lo + k]];
+    return acc;
+}
+
+// Row ownership: thread t owns rows t, t + 1024, ... (RPT rows, interleaved
+// so the vector loads of a wavefront are consecutive).  The vectors p, x, r
+// and M^-1 live in LDS (p is gathered by every row's product anyway); only
+// the product q stays in registers.  With RESIDENT (every row fits the
+// slots) the thread's matrix entries are loaded once -- values with the
+// padding slots zeroed, columns packed two per register -- and kept in
+// registers for the whole solve, so the matrix is read from memory once per
+// solve instead of once per iteration.  Otherwise the entries are re-read
+// every iteration (the row offsets go through an empty asm so the compiler
+// cannot hoist the address arithmetic out of the iteration loop).  Products:
+// SLOTS slots per row, p gathered from LDS (neighbouring rows gather
+// neighbouring LDS words), entry-order sums; rows longer than SLOTS finish
+// with a loop.
+template <typename T, typename IT, int RPT, int SLOTS, bool RESIDENT>
 __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgParams P) {
     extern __shared__ unsigned char lds_raw[];
-    T *ps = reinterpret_cast<T *>(lds_raw);  // search direction (or x0), [n]
-    __shared__ double slots[4][3][kBW];
-    constexpr int RPP = kBlockSolveThreads / G;
-    const int sys = blockIdx.x;
     const int64_t n = P.n, nnz = P.nnz;
-    const T *__restrict__ val = reinterpret_cast<const T *>(P.val) + (int64_t)sys * nnz;
-    const T *__restrict__ b = reinterpret_cast<const T *>(P.b) + (int64_t)sys * n;
-    T *__restrict__ x = reinterpret_cast<T *>(P.x) + (int64_t)sys * n;
-    const IT *__restrict__ rp = reinterpret_cast<const IT *>(P.rp);
-    const IT *__restrict__ dpos = reinterpret_cast<const IT *>(P.diagpos);
-    const int32_t *__restrict__ col = P.col;
+    T *ps = reinterpret_cast<T *>(lds_raw);  // direction p (or x0 at the start)
+    T *xs = ps + n;                          // iterate x
+    T *rs = xs + n;                          // residual r
+    T *ds = rs + n;                          // M^-1 (1 without preconditioner)
+    __shared__ double slots[4][3][kBW];
+    const int sys = blockIdx.x;
+    const int tid = threadIdx.x;
+    const gptr<const T> val = glb(reinterpret_cast<const T *>(P.val) + (int64_t)sys * nnz);
+    const gptr<const T> b = glb(reinterpret_cast<const T *>(P.b) + (int64_t)sys * n);
+    const gptr<T> x = glb(reinterpret_cast<T *>(P.x) + (int64_t)sys * n);
+    const gptr<const IT> rp = glb(reinterpret_cast<const IT *>(P.rp));
+    const gptr<const IT> dpos = glb(reinterpret_cast<const IT *>(P.diagpos));
+    const gptr<const int32_t> col = glb(P.col);
     SolveState *st = P.st + sys;
-    const int lane = threadIdx.x & (G - 1);
-    const int grp = threadIdx.x / G;
-    const int npass = (int)((n + RPP - 1) / RPP);
+    auto row_of = [&](int j) -> int { return tid + j * kBlockSolveThreads; };
+    constexpr int MR = RESIDENT ? RPT : 1;
+    constexpr int PC = (SLOTS + 1) / 2;
+    constexpr int SR = RESIDENT ? 1 : RPT;
 
-    T xr[kMaxRpt], rr[kMaxRpt], pr[kMaxRpt], qr[kMaxRpt], dr[kMaxRpt];
+    int lo[SR], len[SR];  // row offsets (streaming mode only)
+    T qr[RPT];
+    T mv[MR][SLOTS];
+    uint32_t mc[MR][PC];  // two 16-bit columns per register
     int bad = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxRpt; ++j) {
-        const int64_t i = (int64_t)(j * G + lane) * RPP + grp;
-        xr[j] = rr[j] = pr[j] = qr[j] = T(0);
-        dr[j] = T(1);
-        if (j * G + lane < npass && i < n) {
-            if (P.use_x0) xr[j] = x[i];
+    for (int j = 0; j < RPT; ++j) {
+        const int i = row_of(j);
+        int l = 0, ln = 0;
+        qr[j] = T(0);
+        if (i < n) {
+            l = (int)rp[i];
+            ln = (int)(rp[i + 1] - rp[i]);
+            const T x0 = P.use_x0 ? x[i] : T(0);
+            xs[i] = x0;
+            ps[i] = x0;
+            T d = T(1);
             if (P.jac) {
-                const T d = val[dpos[i]];
-                bad |= (d == T(0));
-                dr[j] = T(1) / d;
+                const T a = val[dpos[i]];
+                bad |= (a == T(0));
+                d = T(1) / a;
             }
+            ds[i] = d;
+        }
+        if (RESIDENT) {
+            T v[SLOTS];
+            int32_t c[SLOTS];
+            block_row_load<T, SLOTS>(val, col, l, ln, v, c);
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) mv[RESIDENT ? j : 0][k] = k < ln ? v[k] : T(0);
+#pragma unroll
+            for (int k = 0; k < PC; ++k)
+                mc[RESIDENT ? j : 0][k] = (uint32_t)c[2 * k] |
+                                          (2 * k + 1 < SLOTS ? (uint32_t)c[2 * k + 1] << 16 : 0u);
+        } else {
+            lo[RESIDENT ? 0 : j] = l;
+            len[RESIDENT ? 0 : j] = ln;
         }
     }
 
-    // q = A v for v staged in ps; results go to the owning lane's register.
-    auto spmv = [&](T(&out)[kMaxRpt]) {
+    // out[j] = (A p)_i for the owned rows (p in LDS)
+    auto spmv = [&](T(&out)[RPT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kMaxRpt; ++j) {
+        for (int j = 0; j < RPT; ++j) {
+            if (RESIDENT) {
+                const uint32_t *pc = mc[RESIDENT ? j : 0];
+                const T *v = mv[RESIDENT ? j : 0];
+                T acc = T(0);
 #pragma unroll
-            for (int l = 0; l < G; ++l) {
-                const int pss = j * G + l;
-                if (pss < npass) {
-                    const int64_t i = (int64_t)pss * RPP + grp;
-                    T acc = T(0);
-                    if (i < n) {
-                        const IT e = rp[i + 1];
-                        for (IT k = rp[i] + lane; k < e; k += G) acc += val[k] * ps[col[k]];
-                    }
-                    acc = group_sum<G>(acc);
-                    if (lane == l) out[j] = acc;
-                }
+                for (int k = 0; k < SLOTS; ++k)
+                    acc += v[k] * ps[(pc[k >> 1] >> (16 * (k & 1))) & 0xffffu];
+                out[j] = acc;
+            } else {
+                int l = lo[RESIDENT ? 0 : j];
+                asm volatile("" : "+v"(l));
+                const int ln = len[RESIDENT ? 0 : j];
+                T v[SLOTS];
+                int32_t c[SLOTS];
+                block_row_load<T, SLOTS>(val, col, l, ln, v, c);
+                out[j] = block_row_dot<T, SLOTS>(v, [&](int k) { return c[k]; }, val, col, ps, l, ln);
             }
         }
     };
-    auto stage = [&](const T(&v)[kMaxRpt]) {
-#pragma unroll
-        for (int j = 0; j < kMaxRpt; ++j) {
-            const int64_t i = (int64_t)(j * G + lane) * RPP + grp;
-            if (j * G + lane < npass && i < n) ps[i] = v[j];
-        }
-    };
 
-    if (P.use_x0) {
-        stage(xr);
-        __syncthreads();
-        spmv(qr);
-        __syncthreads();
-    }
+    __syncthreads();
+    if (P.use_x0) spmv(qr);  // A x0 (ps holds x0)
     double r0[3] = {0.0, 0.0, 0.0};  // r.z, r.r, b.b
 #pragma unroll
-    for (int j = 0; j < kMaxRpt; ++j) {
-        const int64_t i = (int64_t)(j * G + lane) * RPP + grp;
-        if (j * G + lane < npass && i < n) {
+    for (int j = 0; j < RPT; ++j) {
+        const int i = row_of(j);
+        if (i < n) {
             const T bi = b[i];
             const T ri = P.use_x0 ? bi - qr[j] : bi;
-            rr[j] = ri;
-            const T zi = P.jac ? dr[j] * ri : ri;
-            pr[j] = zi;
+            rs[i] = ri;
+            const T zi = ds[i] * ri;
             r0[0] += (double)ri * (double)zi;
             r0[1] += (double)ri * (double)ri;
             r0[2] += (double)bi * (double)bi;
         }
     }
-    block_sum<3>(r0, slots[0]);
+    block_sum<3>(r0, slots[0]);  // its barrier also ends every read of x0 in ps
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+        const int i = row_of(j);
+        if (i < n) ps[i] = ds[i] * rs[i];  // p_0 = z_0
+    }
     const int any_bad = __syncthreads_or(bad);
     double rho = r0[0], rnorm2 = r0[1];
     const double bb = r0[2];
@@ -348,13 +407,14 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     } else {
         int slot = 1;
         while (it < P.maxit) {
-            stage(pr);
-            __syncthreads();
             spmv(qr);
             double pq[1] = {0.0};
 #pragma unroll
-            for (int j = 0; j < kMaxRpt; ++j) pq[0] += (double)pr[j] * (double)qr[j];
-            block_sum<1>(pq, slots[slot]);
+            for (int j = 0; j < RPT; ++j) {
+                const int i = row_of(j);
+                if (i < n) pq[0] += (double)ps[i] * (double)qr[j];
+            }
+            block_sum<1>(pq, slots[slot]);  // every gather of p is done
             slot = (slot + 1) & 3;
             if (!(pq[0] > 0.0)) {
                 status = SLA_BREAKDOWN;
@@ -362,14 +422,17 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
             }
             const T alpha = (T)(rho / pq[0]);
             double red[2] = {0.0, 0.0};
-            T zr[kMaxRpt];
 #pragma unroll
-            for (int j = 0; j < kMaxRpt; ++j) {
-                xr[j] = fmaT(alpha, pr[j], xr[j]);
-                rr[j] = fmaT(-alpha, qr[j], rr[j]);
-                zr[j] = P.jac ? dr[j] * rr[j] : rr[j];
-                red[0] += (double)rr[j] * (double)zr[j];
-                red[1] += (double)rr[j] * (double)rr[j];
+            for (int j = 0; j < RPT; ++j) {
+                const int i = row_of(j);
+                if (i < n) {
+                    xs[i] = fmaT(alpha, ps[i], xs[i]);
+                    const T ri = fmaT(-alpha, qr[j], rs[i]);
+                    rs[i] = ri;
+                    const T zi = ds[i] * ri;
+                    red[0] += (double)ri * (double)zi;
+                    red[1] += (double)ri * (double)ri;
+                }
             }
             block_sum<2>(red, slots[slot]);
             slot = (slot + 1) & 3;
@@ -382,14 +445,17 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
             const T beta = (T)(red[0] / rho);
             rho = red[0];
 #pragma unroll
-            for (int j = 0; j < kMaxRpt; ++j) pr[j] = fmaT(beta, pr[j], zr[j]);
-            __syncthreads();  // every gather of the old direction is done
+            for (int j = 0; j < RPT; ++j) {
+                const int i = row_of(j);
+                if (i < n) ps[i] = fmaT(beta, ps[i], ds[i] * rs[i]);
+            }
+            __syncthreads();  // the new p is complete before the next product
         }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxRpt; ++j) {
-        const int64_t i = (int64_t)(j * G + lane) * RPP + grp;
-        if (j * G + lane < npass && i < n) x[i] = zero_x ? T(0) : xr[j];
+    for (int j = 0; j < RPT; ++j) {
+        const int i = row_of(j);
+        if (i < n) x[i] = zero_x ? T(0) : xs[i];
     }
     if (threadIdx.x == 0) {
         st->iter = it;
@@ -436,21 +502,45 @@ hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t
     return hipGetLastError();
 }
 
+// The matrix stays in registers when every row fits the slots and a
+// thread's entries fit in 56 VGPRs.
+template <typename T, int RPT, int SLOTS>
+constexpr bool block_resident() {
+    return RPT * (SLOTS * ((int)sizeof(T) / 4) + (SLOTS + 1) / 2) <= 56;
+}
+
+// Slots per row for the block solver: the longest row rounded up to 4, 5, 6
+// or 8 (5 is the five-point stencil's exact width); longer rows stream.
 template <typename T, typename IT>
-hipError_t launch_block_cg(int G, const BlockCgParams &p, int batch, hipStream_t s) {
-    const size_t lds = (size_t)p.n * sizeof(T);
-    switch (G) {
-        case 2:
-        case 4:
-            block_cg_kernel<T, IT, 4><<<batch, kBlockSolveThreads, lds, s>>>(p);
-            break;
-        case 8:
-            block_cg_kernel<T, IT, 8><<<batch, kBlockSolveThreads, lds, s>>>(p);
-            break;
-        default:
-            block_cg_kernel<T, IT, 16><<<batch, kBlockSolveThreads, lds, s>>>(p);
-            break;
+hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipStream_t s) {
+    const size_t lds = 4 * (size_t)p.n * sizeof(T);  // p, x, r, M^-1
+    const int rpt = (int)((p.n + kBlockSolveThreads - 1) / kBlockSolveThreads);
+    const bool fits = max_len <= 8;
+#define SLA_BLOCK_LAUNCH(R, S)                                                                     \
+    if (fits && block_resident<T, R, S>())                                                         \
+        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>()>                                    \
+            <<<batch, kBlockSolveThreads, lds, s>>>(p);                                            \
+    else                                                                                           \
+        block_cg_kernel<T, IT, R, S, false><<<batch, kBlockSolveThreads, lds, s>>>(p)
+#define SLA_BLOCK_ROWS(R)                     \
+    if (max_len <= 4) {                       \
+        SLA_BLOCK_LAUNCH(R, 4);               \
+    } else if (max_len == 5) {                \
+        SLA_BLOCK_LAUNCH(R, 5);               \
+    } else if (max_len == 6) {                \
+        SLA_BLOCK_LAUNCH(R, 6);               \
+    } else {                                  \
+        SLA_BLOCK_LAUNCH(R, 8);               \
     }
+    if (rpt <= 1) {
+        SLA_BLOCK_ROWS(1)
+    } else if (rpt <= 2) {
+        SLA_BLOCK_ROWS(2)
+    } else {
+        SLA_BLOCK_ROWS(4)
+    }
+#undef SLA_BLOCK_ROWS
+#undef SLA_BLOCK_LAUNCH
     return hipGetLastError();
 }
 

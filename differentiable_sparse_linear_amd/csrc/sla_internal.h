@@ -31,7 +31,7 @@ constexpr int kMaxBlocksPerXcd = SLA_BLOCKS_PER_XCD;
 constexpr int kMaxGrid = kNumXcd * kMaxBlocksPerXcd;
 constexpr int kMaxRed = 8;         // partial-sum slots
 constexpr int kBlockSolveThreads = 1024;
-constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread
+constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread; p, x, r, M^-1 in LDS
 
 // Per-system solver state, device resident.  A field is written by block 0
 // of one kernel and read by later kernels; fields that a kernel both reads
@@ -273,7 +273,7 @@ struct BlockCgParams {
     int32_t jac;
 };
 template <typename T, typename IT>
-hipError_t launch_block_cg(int G, const BlockCgParams &p, int batch, hipStream_t s);
+hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipStream_t s);
 
 // pattern setup
 template <typename IT>
