@@ -10,16 +10,37 @@ Prints one JSON line.  ``value`` = PCG iterations per second (forward and
 adjoint iterations summed over the timed steps, divided by the wall time
 between the synchronised start and end).
 
-``roofline`` describes the dominant kernel (the fused SpMV + direction update
-of CG, ``cg_spmv_kernel``), timed live with HIP events on the stream it runs
-on; its algorithmic bytes per launch are
-    nnz*(8 + 4) + (n + 1)*4   matrix values, columns, row pointers
-  + 2*n*8                     gathered z and previous p (each read once)
-  + 2*n*8                     stored p and q.
+``roofline`` describes the dominant kernel, timed live with HIP events around
+every launch on the stream it runs on (a separate, untimed step in the
+library's profile mode).  For CG that is ``cg_iter_kernel`` (one launch = one
+whole PCG iteration); its algorithmic bytes per launch are
+    nnz*(sv + 4) + (n + 1)*sr        matrix values, columns, row pointers
+  + 6*n*sv                           r, w, s_prev, M^-1, p_prev, x read once
+  + 5*n*sv                           x, p, s, r_next, w_next written
+(sv, sr: value and row-pointer widths; 5 + 5 vectors without a
+preconditioner).  For BiCGStab the two SpMV kernels are timed; their mean
+algorithmic bytes are nnz*(sv + 4) + (n + 1)*sr + 5*n*sv.
+``traffic`` is the HBM bytes per launch measured with rocprofv3 counters
+(FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
+1 GiB copy) and stored under profiles/ with a hash of the kernel's sources;
+it is null when no such record matches the sources being run.
 ``cpu_baseline`` times the oracle (plain fp64 C) on the host on one forward +
 adjoint solve of the same arrays.
+
+Counter and trace summaries (written under profiles/):
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- \
+        python3 bench.py --kernel-only 2
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- \
+        python3 bench.py --kernel-only 2
+    python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write
+    rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- \
+        python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
+    python3 bench.py --summarize-trace OUT/trace
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +53,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+CSRC = os.path.join(ROOT, "differentiable_sparse_linear_amd", "csrc")
+CALIB_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
 
 
 def parse():
@@ -44,35 +67,206 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-chunk", type=int, default=0)
     ap.add_argument("--kernel-only", type=int, default=0,
-                    help="instead of the benchmark, launch the dominant kernel's solve this "
-                         "many times (for counter collection)")
+                    help="run this many steps and a 1 GiB calibration copy, nothing timed "
+                         "(for counter collection)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --kernel-only")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run")
     return ap.parse_args()
 
 
-def spmv_kernel_bytes(n, nnz, sv=8, sr=4):
-    return nnz * (sv + 4) + (n + 1) * sr + 2 * n * sv + 2 * n * sv
+def dominant_kernel(method, precond, n, nnz, sv, sr):
+    """(kernel name(s), algorithmic bytes per launch, source files)."""
+    mat = nnz * (sv + 4) + (n + 1) * sr
+    if method == "cg":
+        vecs = 11 if precond == "jacobi" else 10
+        return ("cg_iter_kernel", mat + vecs * n * sv,
+                ["kernels_cg.hip", "spmv_tile.h", "sla_internal.h"])
+    return ("bicg_pv_kernel+bicg_st_kernel", mat + 5 * n * sv,
+            ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
 
 
-def pcg_iteration_bytes(n, nnz, sv=8, sr=4):
-    # fused SpMV kernel + update kernel (reads x, p, q, r, dinv; writes x, r, z)
-    return spmv_kernel_bytes(n, nnz, sv, sr) + 5 * n * sv + 3 * n * sv
+def sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
+
+def traffic_path(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.txt")
+
+
+def read_traffic(kernel, workload, sha):
+    """HBM bytes per launch from a counter summary made from these sources, else None."""
+    path = traffic_path(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("source_sha256") != sha:
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def load_problem(args):
+    import workloads as W
+    return W.config(args.workload, size=args.size)
+
+
+# ------------------------------------------------------------------ summaries
+
+def _rows(d, pattern):
+    files = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not files:
+        raise SystemExit(f"no {pattern} under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _counter_pass(d, short_names):
+    """(mean KiB of the active dominant-kernel dispatches, their count, all
+    dispatches, KiB of the calibration copy)."""
+    rows = _rows(d, "*counter_collection.csv")
+    vals, copies = [], []
+    for r in rows:
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if any(f"sla::{s}<" in name for s in short_names):
+            vals.append(v)
+        elif "copy" in name.lower() and "sla::" not in name:
+            copies.append(v)
+    if not vals or not copies:
+        raise SystemExit(f"{d}: dominant kernel or calibration copy not found")
+    # launches enqueued after the stop return at entry and read a few bytes
+    top = max(vals)
+    active = [v for v in vals if v >= 0.01 * top]
+    return sum(active) / len(active), len(active), len(vals), max(copies)
+
+
+def summarize_counters(args):
+    p = load_problem(args)
+    kernel, kbytes, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
+                                           p.row_ptr.itemsize)
+    names = kernel.split("+")
+    f_kib, f_n, f_all, f_copy = _counter_pass(args.summarize_counters[0], names)
+    w_kib, w_n, w_all, w_copy = _counter_pass(args.summarize_counters[1], names)
+    f_fac = CALIB_BYTES / (f_copy * 1024.0)
+    w_fac = CALIB_BYTES / (w_copy * 1024.0)
+    fetch = f_kib * 1024.0 * f_fac
+    write = w_kib * 1024.0 * w_fac
+    out = [
+        f"# HBM traffic of {kernel}, workload {p.name}",
+        "",
+        "Commands (repository root; OUT is any output folder):",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- "
+        f"python3 bench.py --kernel-only 2 --workload {args.workload}",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- "
+        f"python3 bench.py --kernel-only 2 --workload {args.workload}",
+        f"  python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write --workload "
+        f"{args.workload}",
+        "",
+        "Calibration: a torch copy of 1 GiB (reads 1 GiB, writes 1 GiB) in the same run;",
+        "factor = 1 GiB / counter reading of that copy.",
+        "",
+        f"kernel: {kernel}",
+        f"workload: {p.name}",
+        f"n: {p.n}",
+        f"nnz: {p.nnz}",
+        f"source_sha256: {sources_sha(srcs)}",
+        f"dispatches_active_fetch_pass: {f_n} of {f_all}",
+        f"dispatches_active_write_pass: {w_n} of {w_all}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"copy_fetch_kib: {f_copy:.1f}",
+        f"copy_write_kib: {w_copy:.1f}",
+        f"fetch_factor: {f_fac:.4f}",
+        f"write_factor: {w_fac:.4f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"hbm_bytes_per_launch: {fetch + write:.0f}",
+        f"algorithmic_bytes_per_launch: {kbytes}",
+        f"traffic_over_algorithmic: {(fetch + write) / kbytes:.3f}",
+    ]
+    print("\n".join(out))
+
+
+def summarize_trace(args):
+    p = load_problem(args)
+    kernel, kbytes, _ = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
+                                        p.row_ptr.itemsize)
+    names = kernel.split("+")
+    stats = _rows(args.summarize_trace, "*kernel_stats.csv")
+    trace = _rows(args.summarize_trace, "*kernel_trace.csv")
+    stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [
+        f"# Kernel time, bench.py on workload {p.name}",
+        "",
+        "Commands (repository root; OUT is any output folder):",
+        "  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- "
+        f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload {args.workload}",
+        f"  python3 bench.py --summarize-trace OUT/trace --workload {args.workload}",
+        "",
+        "rocprofv3 --stats (all dispatches):",
+        f"{'calls':>8} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel",
+    ]
+    for r in stats[:12]:
+        name = r["Name"]
+        short = name.split("(")[0].replace("void ", "")
+        out.append(f"{int(r['Calls']):8d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['TotalDurationNs']) / 1e6:10.2f} {float(r['Percentage']):6.2f}  "
+                   f"{short}")
+    durs = []
+    for r in trace:
+        if any(f"sla::{s}<" in r["Kernel_Name"] for s in names):
+            durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if durs:
+        top = max(durs)
+        # launches enqueued after the stop return at entry (a few microseconds)
+        active = [d for d in durs if d >= 0.25 * top]
+        avg = sum(active) / len(active)
+        out += [
+            "",
+            f"kernel: {kernel}",
+            f"dispatches: {len(durs)}",
+            f"dispatches_active: {len(active)} (the others returned at entry after the stop)",
+            f"avg_us_all: {sum(durs) / len(durs):.2f}",
+            f"avg_us_active: {avg:.2f}",
+            f"algorithmic_bytes_per_launch: {kbytes}",
+            f"achieved_GBps_active: {kbytes / (avg * 1e-6) / 1e9:.1f}",
+        ]
+    print("\n".join(out))
+
+
+# ------------------------------------------------------------------ benchmark
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        return summarize_counters(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
               "sharding is a design note, not part of this build", file=sys.stderr)
         sys.exit(2)
     import torch
-    import workloads as W
     import differentiable_sparse_linear_amd as sla
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     sla.load()
-    p = W.config(args.workload, size=args.size)
+    p = load_problem(args)
     dev = "cuda:0"
     tdt = torch.float64 if p.values.dtype == np.float64 else torch.float32
     rp = torch.from_numpy(p.row_ptr).to(dev)
@@ -98,7 +292,11 @@ def main():
         for _ in range(args.kernel_only):
             step()
         torch.cuda.synchronize()
-        print(json.dumps({"kernel_only": args.kernel_only}))
+        src = torch.empty(CALIB_BYTES // 8, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": args.kernel_only, "calibration_copy_bytes": CALIB_BYTES}))
         return
 
     for _ in range(args.warmup):
@@ -127,10 +325,11 @@ def main():
     k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
     k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
     k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
-    kbytes = spmv_kernel_bytes(p.n, p.nnz, sv=p.values.itemsize, sr=p.row_ptr.itemsize) * p.batch
+    kernel, kbytes, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
+                                           p.row_ptr.itemsize)
     achieved = kbytes / k_avg_s / 1e9
+    traffic = read_traffic(kernel, p.name, sources_sha(srcs))
 
-    iter_bytes = pcg_iteration_bytes(p.n, p.nnz, sv=p.values.itemsize, sr=p.row_ptr.itemsize)
     result = {
         "metric": "CG iters/sec + achieved HBM GB/s (% peak), fwd+adjoint solve, 1e6-DOF 3D Poisson",
         "value": iters / wall,
@@ -150,11 +349,9 @@ def main():
                    "forward_iters": int(fi["iters"].sum()), "adjoint_iters": int(ai["iters"].sum())},
         "solves_per_s": 2 * args.steps / wall,
         "event_ms_per_step": ev_ms / args.steps,
-        "model_iteration_bytes": iter_bytes,
-        "model_iteration_GBps": iter_bytes * iters / wall / 1e9,
-        "roofline": {"bound": "hbm", "kernel": "cg_spmv_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": kbytes,
+                     "traffic": traffic, "bytes_per_launch": kbytes,
                      "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n},
     }
     if not args.no_cpu_baseline:
