@@ -217,9 +217,10 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     };
 
     if (o.profile) {
-        // every iteration launched directly, each fused SpMV kernel bracketed
-        // by a pair of events on `s`; the stop (including maxit) is detected
-        // by the first kernel of the next iteration, so maxit + 1 are enqueued
+        // every iteration launched directly; each fused SpMV kernel carries a
+        // pair of events that the runtime records at its start and end; the
+        // stop (including maxit) is detected by the first kernel of the next
+        // iteration, so maxit + 1 are enqueued
         const int per = cg ? 1 : 2;
         const int launches = o.maxit + 1;
         const size_t need = (size_t)2 * per * (size_t)launches;
@@ -231,16 +232,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, s));
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, s, &h->prof_ev[ev]));
+                ev += 2;
             } else {
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, ad, n, s));
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
-                HIP_TRY(launch_bicg_st<T, IT>(op.slots, ad, n, s));
-                HIP_TRY(hipEventRecord(h->prof_ev[ev++], s));
+                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, ad, n, s, &h->prof_ev[ev]));
+                ev += 2;
+                HIP_TRY(launch_bicg_st<T, IT>(op.slots, ad, n, s, &h->prof_ev[ev]));
+                ev += 2;
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
             if ((k & 63) == 63 || k + 1 == launches) {

@@ -292,14 +292,20 @@ hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) 
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    SLA_DISPATCH_SLOTS(slots, bicg_pv_kernel<T, IT, kS><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a));
+hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
+                          const hipEvent_t *ev) {
+    SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(bicg_pv_kernel<T, IT, kS>,
+                                                 dim3(grid_for_tiles(tiles_of(n))), dim3(kBlock),
+                                                 0, s, ev, a));
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    SLA_DISPATCH_SLOTS(slots, bicg_st_kernel<T, IT, kS><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a));
+hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
+                          const hipEvent_t *ev) {
+    SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS>,
+                                                 dim3(grid_for_tiles(tiles_of(n))), dim3(kBlock),
+                                                 0, s, ev, a));
     return hipGetLastError();
 }
 
@@ -312,9 +318,9 @@ hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s
 #define SLA_INST(T, IT)                                                                        \
     template hipError_t launch_bicg_init<T, IT>(const IterArgs<T, IT> *, int64_t, hipStream_t); \
     template hipError_t launch_bicg_pv<T, IT>(int, const IterArgs<T, IT> *, int64_t,           \
-                                              hipStream_t);                                    \
+                                              hipStream_t, const hipEvent_t *);                \
     template hipError_t launch_bicg_st<T, IT>(int, const IterArgs<T, IT> *, int64_t,           \
-                                              hipStream_t);                                    \
+                                              hipStream_t, const hipEvent_t *);                \
     template hipError_t launch_bicg_update<T, IT>(const IterArgs<T, IT> *, int64_t, hipStream_t);
 
 SLA_INST(float, int32_t)

@@ -492,12 +492,14 @@ hipError_t launch_cg_init(int slots, bool jac, const IterArgs<T, IT> *a, int64_t
 
 template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
-                          hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
+                          hipStream_t s, const hipEvent_t *ev) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)));
     if (jac) {
-        SLA_DISPATCH_SLOTS(slots, cg_iter_kernel<T, IT, true, kS><<<grid, kBlock, 0, s>>>(a, ph));
+        SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(cg_iter_kernel<T, IT, true, kS>, grid,
+                                                     dim3(kBlock), 0, s, ev, a, ph));
     } else {
-        SLA_DISPATCH_SLOTS(slots, cg_iter_kernel<T, IT, false, kS><<<grid, kBlock, 0, s>>>(a, ph));
+        SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(cg_iter_kernel<T, IT, false, kS>, grid,
+                                                     dim3(kBlock), 0, s, ev, a, ph));
     }
     return hipGetLastError();
 }
@@ -548,7 +550,7 @@ hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipSt
     template hipError_t launch_cg_init<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t,      \
                                               hipStream_t);                                     \
     template hipError_t launch_cg_iter<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t, int, \
-                                              hipStream_t);                                     \
+                                              hipStream_t, const hipEvent_t *);                 \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
 
 SLA_INST(float, int32_t)

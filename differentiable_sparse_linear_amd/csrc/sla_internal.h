@@ -6,6 +6,7 @@
 // the matrix and the neighbouring vector entries it gathers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -217,6 +218,19 @@ inline int lanes_for(int64_t n, int64_t nnz) {
 // ---------------------------------------------------------------- launchers
 // (defined in the .hip files; all return hipError_t of the launch)
 
+// Launch `k`; with `ev` (two events) the runtime records ev[0] when the
+// kernel starts and ev[1] when it ends (hipExtLaunchKernel), so the pair
+// times the kernel alone.  The iteration launchers take `ev` for the
+// library's profile mode.
+template <typename... KArgs, typename... Args>
+inline void launch_maybe_timed(void (*k)(KArgs...), dim3 grid, dim3 block, uint32_t lds,
+                               hipStream_t s, const hipEvent_t *ev, Args... args) {
+    if (ev)
+        hipExtLaunchKernelGGL(k, grid, block, lds, s, ev[0], ev[1], 0, args...);
+    else
+        hipLaunchKernelGGL(k, grid, block, lds, s, args...);
+}
+
 // The `slots` argument of the SpMV-shaped launchers is slots_for(longest row).
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
@@ -241,15 +255,17 @@ template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
-                          hipStream_t s);
+                          hipStream_t s, const hipEvent_t *ev = nullptr);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
+                          const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
+                          const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
 hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
