@@ -186,6 +186,24 @@ def spmv(row_ptr, col, values, x) -> np.ndarray:
     return Y[0] if one else Y
 
 
+def spmv_rows(row_ptr, col, values, x, rows) -> np.ndarray:
+    """(A x)_i for the listed rows only, in fp64, each row summed in stored
+    entry order -- the product's definition written out row by row, for
+    sampled checks of systems too large to recompute whole.  ``values`` and
+    ``x`` are 1-D (one system)."""
+    rp = np.asarray(row_ptr)
+    out = np.empty(len(rows))
+    for j, i in enumerate(rows):
+        lo, hi = int(rp[i]), int(rp[i + 1])
+        vs = np.asarray(values[lo:hi], dtype=np.float64)
+        xs = np.asarray(x, dtype=np.float64)[np.asarray(col[lo:hi], dtype=np.int64)]
+        acc = 0.0
+        for k in range(hi - lo):
+            acc += float(vs[k]) * float(xs[k])
+        out[j] = acc
+    return out
+
+
 def dot(a, b) -> float:
     a, b = _f(a), _f(b)
     return float(_load().orc_dot(a.shape[0], _p(a), _p(b)))

@@ -56,6 +56,21 @@ def pin_p2_spmv_dense():
         assert np.all(np.abs(y - ref) <= 4e-16 * 8 * scale + 1e-300), "dense matvec"
 
 
+def pin_p2b_sampled_rows_dense():
+    """The row-by-row product used for sampled checks of huge systems agrees
+    with a dense product on the rows it is asked for (any order, repeats)."""
+    rng = np.random.default_rng(12)
+    for seed, n in [(4, 9), (5, 50)]:
+        rp, col, val = W.random_csr(n, 0.3, seed, symmetric=False)
+        A = to_dense(rp, col, val)
+        x = rng.standard_normal(n)
+        rows = [n - 1, 0, n // 2, n // 2, 1]
+        y = O.spmv_rows(rp, col, val[0], x, rows)
+        ref = (A @ x)[rows]
+        scale = (np.abs(A) @ np.abs(x))[rows]
+        assert np.all(np.abs(y - ref) <= 4e-16 * 8 * scale + 1e-300), "sampled rows"
+
+
 # --------------------------------------------------------------------------
 # P3 -- A.1 for the variable-coefficient stencil (also pins the generator)
 # --------------------------------------------------------------------------
@@ -378,11 +393,12 @@ def pin_p16_bicgstab_half_step():
         assert _relerr(r.x[0], v / lam) <= 1e-13
 
 
-ALL_PINS = [pin_p16_bicgstab_half_step,pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
+ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
             pin_p5_cg_step_bound, pin_p6_dense_solve, pin_p7_jacobi_diagonal,
             pin_p8_bicgstab_vs_cg, pin_p9_transpose, pin_p10_symmetric_adjoint,
             pin_p11_diag_gradient, pin_p12_finite_differences, pin_p13_dense_outer,
-            pin_p14_homogeneity, pin_p15_batch_is_loop, pin_pattern_checks, pin_special_cases]
+            pin_p14_homogeneity, pin_p15_batch_is_loop, pin_p16_bicgstab_half_step,
+            pin_pattern_checks, pin_special_cases]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=[f.__name__ for f in ALL_PINS])

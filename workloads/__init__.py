@@ -30,6 +30,8 @@ of the pages' 4e8-unknown scale).  Readings used where the pages are silent:
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional, Sequence
 
 import numpy as np
@@ -152,9 +154,12 @@ def _assemble(dims, slot_fn, batch: int, index_dtype, value_dtype=np.float64,
         offs.append(strides[ax])
     offs = np.asarray(offs, dtype=np.int64)
     planes_per_chunk = max(1, chunk_rows // plane)
-    lo = 0
-    while lo < n:
-        hi = min(n, lo + planes_per_chunk * plane)
+    step = planes_per_chunk * plane
+
+    def fill(lo):
+        # chunks write disjoint slices, so they run on a thread pool (numpy
+        # releases the GIL); the result does not depend on the order
+        hi = min(n, lo + step)
         vals, mask = slot_fn(lo, hi)
         rows = np.arange(lo, hi, dtype=np.int64)
         cols = rows[:, None] + offs[None, :]
@@ -162,7 +167,14 @@ def _assemble(dims, slot_fn, batch: int, index_dtype, value_dtype=np.float64,
         col[s:e] = cols[mask].astype(np.int32)
         for bi in range(batch):
             values[bi, s:e] = vals[bi][mask]
-        lo = hi
+
+    starts = list(range(0, n, step))
+    if len(starts) > 1:
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, starts))
+    else:
+        for lo in starts:
+            fill(lo)
     return row_ptr, col, values
 
 
