@@ -322,6 +322,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
             }
         }
     }
+    if (cg) HIP_TRY(launch_cg_lag<T>(st, a.p[0], x, n, s));
     if (o.use_x0) HIP_TRY(launch_zero_if<T>(st, x, n, s));
     return SLA_OK;
 }

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *
     const gptr<const T> vold = glb((const T *)A->v[it & 1]);
     const gptr<T> pnew = glb(A->p[(it + 1) & 1]);
     const gptr<T> vnew = glb(A->v[(it + 1) & 1]);
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     __shared__ double red[3][kWaves];
     auto pre = [&]() {
         const int slot[3] = {kBiRHR, kBiRR, kBiBB};
@@ -138,11 +138,11 @@ __global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *
     const gptr<const T> vp = first ? r : vold;
     auto pk = [&](const G3<T> &g) -> T { return pdir(false, beta, omega, g.a, g.b, g.c); };
     double rv_acc = 0.0;
-    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, 4>(
+    const bool go = spmv_rows<T, IT, SLOTS, 4>(
         xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
         [&](int32_t c) { return G3<T>{r[c], pp[c], vp[c]}; }, pk,
         [&](int64_t i) { return PvOwn<T>{r[i], pp[i], vp[i], rh[i]}; },
-        [&](int64_t i, T acc, const PvOwn<T> &o) {
+        [&](int64_t i, T acc, const PvOwn<T> &o, T) {
             pnew[i] = pk(G3<T>{o.r, o.p, o.v});
             vnew[i] = acc;
             rv_acc += (double)o.rh * (double)acc;
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *
     const gptr<const T> v = glb((const T *)A->v[(it + 1) & 1]);
     const gptr<T> s = glb(A->s);
     const gptr<T> tv = glb(A->t);
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     __shared__ double red[1][kWaves];
     auto pre = [&]() {
         const int slot[1] = {kBiRV};
@@ -197,11 +197,11 @@ __global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *
     };
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0;
-    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+    const bool go = spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
         [&](int32_t c) { return G2<T>{r[c], v[c]}; }, sk,
         [&](int64_t i) { return StOwn<T>{r[i], v[i]}; },
-        [&](int64_t i, T acc, const StOwn<T> &o) {
+        [&](int64_t i, T acc, const StOwn<T> &o, T) {
             const T si = sk(G2<T>{o.r, o.v});
             s[i] = si;
             tv[i] = acc;

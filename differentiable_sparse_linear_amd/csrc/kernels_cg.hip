@@ -14,17 +14,28 @@
 //     p_i = u_i + beta_i p_{i-1},  s_i = w_i + beta_i s_{i-1}  (= A p_i)
 //     x_{i+1} = x_i + alpha_i p_i,  r_{i+1} = r_i - alpha_i s_i
 //     u_{i+1} = M^-1 r_{i+1},  w_{i+1} = A u_{i+1}
+// With M = diag(A) the kernels keep the scaled vectors u = M^-1 r,
+// w^ = M^-1 w and s^ = M^-1 s instead of r, w and s: then
+//   s^_i = w^_i + beta_i s^_{i-1},  u_{i+1} = u_i - alpha_i s^_i,
+//   w^_{i+1} = (A u_{i+1}) / a_ii,  r = a_ii u,
+// so the product's gathers need u, w^ and s^ only (no M^-1 vector) and a_ii
+// comes from the row's own diagonal entry.  Without a preconditioner a_ii is
+// taken as 1 and the same code runs on r, w and s.
 // One kernel does a whole iteration: the vector updates of its rows, and the
 // product w_{i+1} = A u_{i+1} with u_{i+1} evaluated at each gathered column
-// from r_i, w_i, s_{i-1} and M^-1.  It stores per-block partial sums of
+// from u_i, w^_i and s^_{i-1}.  It stores per-block partial sums of
 // gamma_{i+1}, delta_{i+1} and ||r_{i+1}||^2 with plain stores; every block
 // of the next launch adds them in block order (identical scalars everywhere,
-// no grid-wide fence).  r, w, s and the partial-sum slots alternate between
-// two buffers by iteration parity, which each launch receives as an argument
+// no grid-wide fence).  u, w^, s^ and the partial-sum slots alternate between
+// two buffers by iteration parity, a template argument of the kernel
 // (neighbouring rows still read the old vectors while a block writes the new
-// ones).  Every launch returns at entry once the device-side `done` flag is
-// set, so the host enqueues many iterations (HIP graph replays) and polls
-// rarely.
+// ones).  x is brought up to date every second iteration: the odd launch i
+// adds alpha_{i-1} p_{i-1} + alpha_i p_i (p_{i-1} is read anyway); a stop at
+// an odd iteration leaves x one step behind and flags it, and one launch
+// after the solve adds the pending alpha_{i-1} p_{i-1} (in the stopping launch
+// itself, blocks that start after block 0 has set `done` would skip it).
+// Every launch returns at entry once the device-side `done` flag is set, so
+// the host enqueues many iterations (HIP graph replays) and polls rarely.
 //
 // Block path: one 1024-thread workgroup runs the whole solve of one small
 // system (n <= 4096): vectors live in registers, the search direction in LDS
@@ -40,12 +51,12 @@ __device__ __forceinline__ T fmaT(T a, T b, T c) {
     return fma(a, b, c);
 }
 
-// Vectors of the grid CG in the workspace: r by parity = {r, z}, w = {q, rh},
-// s = {s, t}, p = p[0]; t doubles as A x0 before the first iteration.
+// Vectors of the grid CG in the workspace: u by parity = {r, z}, w^ = {q, rh},
+// s^ = {s, t}, p = p[0]; t doubles as A x0 before the first iteration.
 // (Selected with conditionals: a pointer array indexed by a runtime parity
 // would live in scratch memory.)
 template <typename T, typename IT>
-__device__ __forceinline__ T *cg_r(const IterArgs<T, IT> *A, int ph) { return ph ? A->z : A->r; }
+__device__ __forceinline__ T *cg_u(const IterArgs<T, IT> *A, int ph) { return ph ? A->z : A->r; }
 template <typename T, typename IT>
 __device__ __forceinline__ T *cg_w(const IterArgs<T, IT> *A, int ph) { return ph ? A->rh : A->q; }
 template <typename T, typename IT>
@@ -53,12 +64,13 @@ __device__ __forceinline__ T *cg_s(const IterArgs<T, IT> *A, int ph) { return ph
 
 template <typename T>
 struct CgOwn {
-    T r, w, s, d, p, x;
+    T u, w, s, p, x;
 };
 
-// r_0 = b - A x_0, u_0 = M^-1 r_0, w_0 = A u_0 (A x_0 is in t; the host
-// zeroes t when there is no initial guess); partials gamma_0, delta_0,
-// ||r_0||^2 and ||b||^2 (parity-0 slots).
+// r_0 = b - A x_0 (A x_0 is in t; the host zeroes t when there is no initial
+// guess), u_0 = M^-1 r_0, w_0 = A u_0; stores u_0 and w^_0 = M^-1 w_0 in the
+// parity-0 buffers and zeroes x without an initial guess; partials gamma_0,
+// delta_0, ||r_0||^2 and ||b||^2 (parity-0 slots).
 template <typename T, typename IT, bool JAC, int SLOTS>
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
     const int64_t n = A->n;
@@ -67,21 +79,21 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
     const gptr<const T> dinv = glb(A->dinv);
     const gptr<const T> val = glb(A->val);
     const gptr<T> x = glb(A->x);
-    const gptr<T> r0 = glb(cg_r(A, 0));
+    const gptr<T> u0 = glb(cg_u(A, 0));
     const gptr<T> w0 = glb(cg_w(A, 0));
     const bool x0 = A->use_x0 != 0;
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     double ga = 0.0, de = 0.0, rr = 0.0, bb = 0.0;
     auto load = [&](int64_t c) { return G3<T>{b[c], ax0[c], JAC ? dinv[c] : T(1)}; };
-    auto u0 = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
-    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+    auto u_of = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
+    spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
-        load, u0, load,
-        [&](int64_t i, T acc, const G3<T> &o) {
+        load, u_of, load,
+        [&](int64_t i, T acc, const G3<T> &o, T) {
             const T ri = o.a - o.b;
-            const T ui = u0(o);
-            r0[i] = ri;
-            w0[i] = acc;
+            const T ui = u_of(o);
+            u0[i] = ui;
+            w0[i] = JAC ? acc * o.c : acc;
             if (!x0) x[i] = T(0);
             ga += (double)ri * (double)ui;
             de += (double)acc * (double)ui;
@@ -94,46 +106,53 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
     store_partials<4>(v, A->part, slot);
 }
 
-// Iteration i (i = st->iter_p[ph], ph = i & 1): stop tests on r_i, the
+// Iteration i (i = st->iter_p[PH], PH = i & 1): stop tests on r_i, the
 // scalars, the row updates and w_{i+1} = A u_{i+1}.
 #ifndef SLA_CG_ROUND
 #define SLA_CG_ROUND 4
 #endif
-template <typename T, typename IT, bool JAC, int SLOTS>
-__global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A,
-                                                         int ph) {
+#ifndef SLA_CG_WAVES
+#define SLA_CG_WAVES 5
+#endif
+template <typename T, typename IT, bool JAC, int SLOTS, int PH>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_CG_WAVES)))
+void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
-    const int it = st->iter_p[ph];
-    const bool first = (it == 0);
+    const int it = st->iter_p[PH];
+    const bool first = PH == 0 && it == 0;
     const int64_t n = A->n;
     const gptr<const T> val = glb(A->val);
-    const gptr<const T> dinv = glb(A->dinv);
-    const gptr<const T> rc = glb((const T *)cg_r(A, ph));
-    const gptr<const T> wc = glb((const T *)cg_w(A, ph));
-    const gptr<const T> sp = glb((const T *)cg_s(A, ph ^ 1));
-    const gptr<T> rn = glb(cg_r(A, ph ^ 1));
-    const gptr<T> wn = glb(cg_w(A, ph ^ 1));
-    const gptr<T> sc = glb(cg_s(A, ph));
+    const gptr<const T> uc = glb((const T *)cg_u(A, PH));
+    const gptr<const T> wc = glb((const T *)cg_w(A, PH));
+    const gptr<const T> sp = glb((const T *)cg_s(A, PH ^ 1));
+    const gptr<T> un = glb(cg_u(A, PH ^ 1));
+    const gptr<T> wn = glb(cg_w(A, PH ^ 1));
+    const gptr<T> sc = glb(cg_s(A, PH));
     const gptr<T> p = glb(A->p[0]);
     const gptr<T> x = glb(A->x);
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     __shared__ double red[4][kWaves];
 
     // previous launch's partial sums, loaded with the first row pointers
     auto pre = [&]() {
-        if (it == 0) {
+        if (first) {
             const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
             partial_loads<4>(A->part, slot, red);
         } else {
-            const int slot[3] = {ph ? kCgGA1 : kCgGA, ph ? kCgDE1 : kCgDE, ph ? kCgRR1 : kCgRR};
+            const int slot[3] = {PH ? kCgGA1 : kCgGA, PH ? kCgDE1 : kCgDE, PH ? kCgRR1 : kCgRR};
             partial_loads<3>(A->part, slot, red);
         }
     };
-    T beta = T(0), alpha = T(0);
+    T beta = T(0), alpha = T(0), alpha_prev = T(0);
+    // a stop at an odd iteration leaves x = x_{i-1}
+    auto stop = [&](int status, double rr) {
+        if (PH == 1 && block0()) st->lag = 1;
+        finish(st, status, it, rr);
+    };
     auto post = [&]() -> bool {
         double tot[4];
-        if (it == 0) {
+        if (first) {
             totals<4>(red, tot);
         } else {
             double t3[3];
@@ -144,34 +163,35 @@ __global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *
             tot[3] = st->bb;
         }
         const double gamma = tot[0], delta = tot[1], rr = tot[2], bb = tot[3];
-        if (it == 0 && st->zero_diag) {
+        if (PH == 1) alpha_prev = (T)st->alpha[0];
+        if (first && st->zero_diag) {
             finish(st, SLA_ERR_ZERO_DIAG, 0, rr);
             return false;
         }
-        if (it == 0 && bb == 0.0) {
+        if (first && bb == 0.0) {
             if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
             finish(st, SLA_OK, 0, 0.0);
             return false;
         }
         if (sqrt(rr) <= A->tol * sqrt(bb)) {
-            finish(st, SLA_OK, it, rr);
+            stop(SLA_OK, rr);
             return false;
         }
         if (it >= A->maxit) {
-            finish(st, SLA_NOT_CONVERGED, it, rr);
+            stop(SLA_NOT_CONVERGED, rr);
             return false;
         }
-        const double beta_d = first ? 0.0 : gamma / st->rho[ph ^ 1];
-        const double den = first ? delta : delta - beta_d * gamma / st->alpha[ph ^ 1];
+        const double beta_d = first ? 0.0 : gamma / st->rho[PH ^ 1];
+        const double den = first ? delta : delta - beta_d * gamma / st->alpha[PH ^ 1];
         if (!(den > 0.0)) {
-            finish(st, SLA_BREAKDOWN, it, rr);
+            stop(SLA_BREAKDOWN, rr);
             return false;
         }
         const double alpha_d = gamma / den;
         if (block0()) {
-            st->rho[ph] = gamma;
-            st->alpha[ph] = alpha_d;
-            st->iter_p[ph ^ 1] = it + 1;
+            st->rho[PH] = gamma;
+            st->alpha[PH] = alpha_d;
+            st->iter_p[PH ^ 1] = it + 1;
             st->nfused += 1;
             st->spmv += first ? (A->use_x0 ? 3 : 2) : 1;  // init (and A x0) products
             if (first) st->bb = bb;
@@ -180,33 +200,29 @@ __global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *
         alpha = (T)alpha_d;
         return true;
     };
-    // s_i and u_{i+1} from the four vectors at one index (the gathers and the
-    // row updates use the same expressions, so they see the same values).
-    // The first iteration has beta = 0 and reads w and r in place of the
-    // (not yet written) previous s and p: fma(0, finite, w) == w exactly.
+    // s^_i and u_{i+1} from the three vectors at one index (the gathers and
+    // the row updates use the same expressions, so they see the same values).
+    // The first iteration has beta = 0 and reads w^ and u in place of the
+    // (not yet written) previous s^ and p: fma(0, finite, w) == w exactly.
     const gptr<const T> sprev = first ? wc : sp;
-    const gptr<const T> pprev = first ? rc : (gptr<const T>)p;
+    const gptr<const T> pprev = first ? uc : (gptr<const T>)p;
     auto s_of = [&](T w, T sv) -> T { return fmaT(beta, sv, w); };
-    auto u_of = [&](const G4<T> &g) -> T {
-        const T rv = fmaT(-alpha, s_of(g.b, g.c), g.a);
-        return JAC ? g.d * rv : rv;
-    };
+    auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
-    const bool go = SLA_SPMV_LOOP<T, IT, SLOTS, SLA_CG_ROUND>(
+    const bool go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
         xcd_tiles(tiles_of(n)), n, glb(A->rp), glb(A->col), sm, [&](IT k) { return val[k]; },
-        [&](int32_t c) { return G4<T>{rc[c], wc[c], sprev[c], JAC ? dinv[c] : T(1)}; }, u_of,
-        [&](int64_t i) { return CgOwn<T>{rc[i], wc[i], sprev[i], JAC ? dinv[i] : T(1), pprev[i], x[i]}; },
-        [&](int64_t i, T acc, const CgOwn<T> &o) {
-            const T ui = JAC ? o.d * o.r : o.r;
-            const T pi = fmaT(beta, o.p, ui);
+        [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; }, u_of,
+        [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
+        [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
+            const T pi = fmaT(beta, o.p, o.u);
             const T si = s_of(o.w, o.s);
-            const T rni = fmaT(-alpha, si, o.r);
-            const T uni = JAC ? o.d * rni : rni;
-            x[i] = fmaT(alpha, pi, o.x);
+            const T uni = fmaT(-alpha, si, o.u);
+            if (PH) x[i] = fmaT(alpha, pi, fmaT(alpha_prev, o.p, o.x));
             p[i] = pi;
             sc[i] = si;
-            rn[i] = rni;
-            wn[i] = acc;
+            un[i] = uni;
+            wn[i] = JAC ? acc / aii : acc;
+            const T rni = JAC ? aii * uni : uni;
             g += (double)rni * (double)uni;
             d += (double)acc * (double)uni;
             q += (double)rni * (double)rni;
@@ -214,8 +230,20 @@ __global__ __launch_bounds__(kBlock) void cg_iter_kernel(const IterArgs<T, IT> *
         pre, post);
     if (!go) return;
     double v[3] = {g, d, q};
-    const int slot[3] = {ph ? kCgGA : kCgGA1, ph ? kCgDE : kCgDE1, ph ? kCgRR : kCgRR1};
+    const int slot[3] = {PH ? kCgGA : kCgGA1, PH ? kCgDE : kCgDE1, PH ? kCgRR : kCgRR1};
     store_partials<3>(v, A->part, slot);
+}
+
+// x_i = x_{i-1} + alpha_{i-1} p_{i-1} after a stop at an odd iteration i
+// (alpha_{i-1} is the parity-0 alpha, p holds p_{i-1}).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void cg_lag_kernel(const SolveState *st, const T *__restrict__ p,
+                                                        T *__restrict__ x, int64_t n) {
+    if (!st->lag) return;
+    const T a = (T)st->alpha[0];
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        x[i] = fmaT(a, p[i], x[i]);
 }
 
 // ------------------------------------------------------------ block path
@@ -494,13 +522,23 @@ template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
                           hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
+#define SLA_CG_ITER(J, P) \
+    SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(cg_iter_kernel<T, IT, J, kS, P>, grid, \
+                                                 dim3(kBlock), 0, s, ev, a))
     if (jac) {
-        SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(cg_iter_kernel<T, IT, true, kS>, grid,
-                                                     dim3(kBlock), 0, s, ev, a, ph));
+        if (ph) {
+            SLA_CG_ITER(true, 1);
+        } else {
+            SLA_CG_ITER(true, 0);
+        }
     } else {
-        SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(cg_iter_kernel<T, IT, false, kS>, grid,
-                                                     dim3(kBlock), 0, s, ev, a, ph));
+        if (ph) {
+            SLA_CG_ITER(false, 1);
+        } else {
+            SLA_CG_ITER(false, 0);
+        }
     }
+#undef SLA_CG_ITER
     return hipGetLastError();
 }
 
@@ -545,6 +583,19 @@ hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipSt
 #undef SLA_BLOCK_LAUNCH
     return hipGetLastError();
 }
+
+template <typename T>
+hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, hipStream_t s) {
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    cg_lag_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(st, p, x, n);
+    return hipGetLastError();
+}
+template hipError_t launch_cg_lag<float>(const SolveState *, const float *, float *, int64_t,
+                                         hipStream_t);
+template hipError_t launch_cg_lag<double>(const SolveState *, const double *, double *, int64_t,
+                                          hipStream_t);
 
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, bool, const IterArgs<T, IT> *, int64_t,      \

@@ -18,15 +18,15 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride) {
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
     const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
-    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+    spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(rp), glb(col), sm, [&](IT k) { return v[k]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
-        [&](int64_t i, T s, int) { ys[i] = s; }, NoPre(), NoPost());
+        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
 
 // y = A^T x through the transpose map: rp/col describe A^T and the value of
@@ -36,16 +36,16 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ perm,
     const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
     int64_t n, int64_t vec_stride) {
-    __shared__ SpmvLds<T, IT> sm;
+    __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
     const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     const gptr<const int32_t> pm = glb(perm);
-    SLA_SPMV_LOOP<T, IT, SLOTS, SLOTS>(
+    spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(rp), glb(col), sm, [&](IT k) { return v[pm[k]]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
-        [&](int64_t i, T s, int) { ys[i] = s; }, NoPre(), NoPost());
+        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
 
 // grad[k] = -lambda[row(k)] * x[col[k]].  Short tiles: each thread marks the

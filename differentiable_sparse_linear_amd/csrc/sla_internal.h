@@ -56,7 +56,8 @@ struct SolveState {
     int32_t zero_diag;
     int32_t zero_x;   // rhs == 0 with a user initial guess: x must become 0
     int32_t half_exit;  // BiCGStab: x took its half step, stop next kernel
-    int32_t pad;
+    int32_t lag;      // CG: stopped at an odd iteration i with x = x_{i-1};
+                      // the finishing launch adds alpha[0] p
 };
 
 // Slots of the per-block partial sums ([kMaxRed][kMaxGrid] doubles).  A
@@ -272,6 +273,9 @@ hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s
 // shared by both grid solvers: x = 0 when the state asks for it
 template <typename T>
 hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s);
+// After a grid CG solve: x += alpha[0] p when the stop left x one step behind.
+template <typename T>
+hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, hipStream_t s);
 
 // CG, one workgroup per system (n <= kBlockSolveMaxN)
 struct BlockCgParams {

@@ -2,14 +2,17 @@
 //
 // A tile is kTileRows consecutive rows.  Their entries form one contiguous run
 // [rp[row0], rp[row0 + rows]) of the value and column arrays, so the block
-// reads that run as consecutive elements: entry e by thread e mod kBlock,
-// kEpt entries per thread.  The loads are unconditional (indices past the
-// run are clamped to its last entry) so the compiler issues all of them
-// before the first use instead of one branch and one wait per entry.  Each
-// value is multiplied by the gathered vector entry and staged in LDS; after a
-// barrier each thread adds the products of one row in entry order.  A tile
-// with more than kBlock * kEpt entries (long rows) is processed one
-// wavefront per row instead, lanes striding over the row's entries.
+// reads that run as consecutive elements (entry e by thread e mod kBlock,
+// kEpt entries per thread) into LDS.  The loads are unconditional (indices
+// past the run are clamped to its last entry) so the compiler issues all of
+// them before the first use.  After a barrier thread t walks row t from LDS
+// and gathers its k-th neighbour for k = 0..SLOTS-1 in lock step with the
+// other lanes (slots past the row repeat its last entry and are left out of
+// the sum).  For banded and stencil matrices neighbouring rows have
+// neighbouring columns, so each gather instruction touches a few consecutive
+// cache lines.  Each row's sum is formed in entry order; rows longer than
+// SLOTS finish with a plain loop; a tile with more than kCap entries (long
+// rows) is processed one wavefront per row, lanes striding over the row.
 //
 // Pipelining: the next tile's row pointers are loaded while this tile is
 // processed and parked in a second LDS buffer; a row's own vector entries
@@ -34,12 +37,6 @@ template <typename T>
 __device__ __forceinline__ gptr<T> glb(T *p) {
     return (gptr<T>)p;
 }
-
-template <typename T, typename IT>
-struct TileLds {
-    IT rp[2][kTileRows + 1];
-    T prod[kCap];
-};
 
 __device__ __forceinline__ float wave_sum_t(float v) {
 #pragma unroll
@@ -111,115 +108,6 @@ struct PlainGather {
     __device__ V operator()(V v) const { return v; }
 };
 
-// vf(k): value of stored entry k; gf(c): the loads gathered at column c;
-// cf(g): the vector entry those loads make (the gathers of ROUND entries are
-// all issued before the first cf); of(i): this thread's own-row inputs,
-// loaded early (i is clamped into the tile, so the load is always in bounds);
-// rf(i, s, own): consumes row i's product s.  pre(): start-up loads issued
-// with the first row pointers (no barrier inside); post(): runs after the
-// first barrier, every thread, and returns false to end the kernel (the same
-// in every thread).
-template <typename T, typename IT, int ROUND, typename VF, typename GF, typename CF, typename OF,
-          typename RF, typename PRE, typename POST>
-__device__ __forceinline__ bool spmv_tiles(const TileRange &tr, int64_t n, gptr<const IT> rp,
-                                           gptr<const int32_t> col, TileLds<T, IT> &sm, VF vf,
-                                           GF gf, CF cf, OF of, RF rf, PRE pre, POST post) {
-    static_assert(kEpt % ROUND == 0, "ROUND must divide kEpt");
-    const int tid = threadIdx.x;
-    auto rows_of = [&](int64_t tt) -> int {
-        const int64_t left = n - tt * kTileRows;
-        return left < kTileRows ? (int)left : kTileRows;
-    };
-    int64_t t = tr.first;
-    int cur = 0;
-    if (t < tr.end) {
-        const int rows = rows_of(t);
-        if (tid < rows) sm.rp[0][tid] = rp[t * kTileRows + tid];
-        if (tid == 0) sm.rp[0][rows] = rp[t * kTileRows + rows];
-    }
-    pre();
-    __syncthreads();
-    if (!post()) return false;
-    for (; t < tr.end; t += tr.stride) {
-        const int64_t row0 = t * kTileRows;
-        const int rows = rows_of(t);
-        const IT *cr = sm.rp[cur];
-        const int64_t tn = t + tr.stride;
-        const bool has_next = tn < tr.end;
-        const int rows_n = has_next ? rows_of(tn) : 0;
-        IT nrp = 0, nend = 0;
-        if (has_next) {
-            nrp = rp[tn * kTileRows + (tid < rows_n ? tid : rows_n - 1)];
-            nend = rp[tn * kTileRows + rows_n];
-        }
-        const int me = tid < rows ? tid : rows - 1;
-        const auto own = of(row0 + me);
-        const IT base = cr[0];
-        const int64_t cnt = (int64_t)(cr[rows] - base);
-        // a tile always has entries (every row stores its diagonal); an empty
-        // one would take the per-row path, which reads nothing
-        const bool staged = cnt > 0 && cnt <= kCap;
-        if (staged) {
-            const int last = (int)cnt - 1;
-            T v[kEpt];
-            int32_t c[kEpt];
-#pragma unroll
-            for (int j = 0; j < kEpt; ++j) {
-                const int e = tid + j * kBlock;
-                const IT k = base + (e < last ? e : last);
-                v[j] = vf(k);
-                c[j] = col[k];
-            }
-#pragma unroll
-            for (int h = 0; h < kEpt; h += ROUND) {
-                decltype(gf(0)) g[ROUND];
-#pragma unroll
-                for (int j = 0; j < ROUND; ++j) g[j] = gf(c[h + j]);
-#pragma unroll
-                for (int j = 0; j < ROUND; ++j) sm.prod[tid + (h + j) * kBlock] = v[h + j] * cf(g[j]);
-            }
-        }
-        if (has_next) {
-            if (tid < rows_n) sm.rp[cur ^ 1][tid] = nrp;
-            if (tid == 0) sm.rp[cur ^ 1][rows_n] = nend;
-        }
-        __syncthreads();
-        if (staged) {
-            if (tid < rows) {
-                const int lo = (int)(cr[tid] - base), hi = (int)(cr[tid + 1] - base);
-                T s = T(0);
-                for (int e = lo; e < hi; ++e) s += sm.prod[e];
-                rf(row0 + tid, s, own);
-            }
-        } else {
-            const int lane = tid & 63, wave = tid >> 6;
-            for (int r = wave; r < rows; r += kWaves) {
-                const IT hi = cr[r + 1];
-                T s = T(0);
-                for (IT k = cr[r] + lane; k < hi; k += 64) s += vf(k) * cf(gf(col[k]));
-                s = wave_sum_t(s);
-                if (lane == 0) sm.prod[r] = s;
-            }
-            __syncthreads();
-            if (tid < rows) rf(row0 + tid, sm.prod[tid], own);
-        }
-        __syncthreads();
-        cur ^= 1;
-    }
-    return true;
-}
-
-// Row-per-lane variant.  The tile's values and columns are read as one
-// coalesced run into LDS; then thread t walks row t from LDS and gathers its
-// k-th neighbour for k = 0..kRowSlots-1 in lock step with the other lanes
-// (slots past the row repeat its last entry and are left out of the sum).  For banded
-// and stencil matrices neighbouring rows have neighbouring columns, so each
-// gather instruction touches a few consecutive cache lines instead of one
-// region per stencil offset.  The row's sum is formed in entry order, as in
-// spmv_tiles.  SLOTS (>= the usual row length) gathers are issued per row,
-// ROUND at a time; rows longer than SLOTS finish with a plain loop; tiles
-// with more than kCap entries go one wavefront per row.
-
 // Largest divisor of slots that does not exceed round (rounds must tile the
 // slots exactly).
 constexpr int round_for(int slots, int round) {
@@ -235,6 +123,15 @@ struct RowLds {
     int32_t col[kCap];
 };
 
+// vf(k): value of stored entry k; gf(c): the loads gathered at column c;
+// cf(g): the vector entry those loads make (the gathers of ROUND slots are
+// all issued before the first cf); of(i): this thread's own-row inputs,
+// loaded early (i is clamped into the tile, so the load is always in bounds);
+// rf(i, s, own, d): consumes row i's product s; d is the row's diagonal entry
+// (the stored entry whose column is i; every validated pattern has one).
+// pre(): start-up loads issued with the first row pointers (no barrier
+// inside); post(): runs after the first barrier, every thread, and returns
+// false to end the kernel (the same in every thread).
 template <typename T, typename IT, int SLOTS, int ROUND, typename VF, typename GF, typename CF,
           typename OF, typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
@@ -300,6 +197,10 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 const int lo = (int)(cr[tid] - base);
                 const int len = (int)(cr[tid + 1] - cr[tid]);
                 const int lastk = len > 0 ? len - 1 : 0;
+                // columns are ascending and the diagonal is stored, so its
+                // position is the number of the row's columns below the row
+                const int32_t me32 = (int32_t)(row0 + tid);
+                int below = 0;
                 T s = T(0);
 #pragma unroll
                 for (int h = 0; h < SLOTS; h += R) {
@@ -308,8 +209,10 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
 #pragma unroll
                     for (int k = 0; k < R; ++k) {
                         const int idx = lo + (h + k < lastk ? h + k : lastk);
+                        const int32_t c = sm.col[idx];
                         w[k] = sm.val[idx];
-                        g[k] = gf(sm.col[idx]);
+                        below += (h + k < len && c < me32) ? 1 : 0;
+                        g[k] = gf(c);
                     }
 #pragma unroll
                     for (int k = 0; k < R; ++k) {
@@ -317,47 +220,38 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                         s = h + k < len ? s + term : s;
                     }
                 }
-                for (int k = SLOTS; k < len; ++k) s += sm.val[lo + k] * cf(gf(sm.col[lo + k]));
-                rf(row0 + tid, s, own);
+                for (int k = SLOTS; k < len; ++k) {
+                    const int32_t c = sm.col[lo + k];
+                    below += c < me32 ? 1 : 0;
+                    s += sm.val[lo + k] * cf(gf(c));
+                }
+                rf(row0 + tid, s, own, sm.val[lo + (below < lastk ? below : lastk)]);
             }
         } else {
             const int lane = tid & 63, wave = tid >> 6;
-            T *ps = sm.val;
+            T *ps = sm.val;              // row sums
+            T *pd = sm.val + kTileRows;  // diagonal entries
             for (int r = wave; r < rows; r += kWaves) {
                 const IT hi = cr[r + 1];
+                const int64_t row = row0 + r;
                 T s = T(0);
-                for (IT k = cr[r] + lane; k < hi; k += 64) s += vf(k) * cf(gf(col[k]));
+                for (IT k = cr[r] + lane; k < hi; k += 64) {
+                    const int32_t c = col[k];
+                    const T v = vf(k);
+                    s += v * cf(gf(c));
+                    if (c == row) pd[r] = v;  // one lane: the diagonal is stored once
+                }
                 s = wave_sum_t(s);
                 if (lane == 0) ps[r] = s;
             }
             __syncthreads();
-            if (tid < rows) rf(row0 + tid, ps[tid], own);
+            if (tid < rows) rf(row0 + tid, ps[tid], own, pd[tid]);
         }
         __syncthreads();
         cur ^= 1;
     }
     return true;
 }
-
-// The loop the SpMV-shaped kernels use: SLA_SPMV_LOOP<T, IT, SLOTS, ROUND>.
-#ifndef SLA_ROW_GATHER
-#define SLA_ROW_GATHER 1
-#endif
-#if SLA_ROW_GATHER
-template <typename T, typename IT>
-using SpmvLds = RowLds<T, IT>;
-#define SLA_SPMV_LOOP spmv_rows
-#else
-template <typename T, typename IT>
-using SpmvLds = TileLds<T, IT>;
-template <typename T, typename IT, int SLOTS, int ROUND, typename... A>
-__device__ __forceinline__ bool spmv_tiles_sr(const TileRange &tr, int64_t n, gptr<const IT> rp,
-                                              gptr<const int32_t> col, TileLds<T, IT> &sm,
-                                              A... a) {
-    return spmv_tiles<T, IT, round_for(kEpt, ROUND)>(tr, n, rp, col, sm, a...);
-}
-#define SLA_SPMV_LOOP spmv_tiles_sr
-#endif
 
 #define SLA_DISPATCH_SLOTS(slots, ...)                          \
     switch (slots) {                                            \

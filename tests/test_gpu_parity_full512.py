@@ -8,12 +8,19 @@ The oracle cannot redo 500-iteration solves of this size inside a test, so:
     bound 1e-12 * sum_j |A_ij||x_j|;
   * forward and adjoint solves cut to K iterations: every element of x and of
     lambda against the oracle's K-iteration iterates (relative L2 1e-10);
-  * the configured solve (tol 1e-10, maxit 500): the residual the solver
-    reports equals the oracle's recomputation of ||b - A x|| / ||b||, and the
-    status agrees with it;
+  * the configured solve (tol 1e-10, maxit 500, not reached): forward and
+    adjoint 500th iterates against the oracle's, stored by
+    tests/golden/make_config5_reference.py (iteration counts, statuses and
+    residuals; norms of x and lambda and their values at sampled rows, the
+    gradient at sampled entries; relative 1e-7, the benchmark spec's bar for
+    solves compared at the same iterate); the residual the solver reports
+    equals the oracle's recomputation of ||b - A x|| / ||b||;
   * the gradient on the pattern at sampled entries equals -lambda_i x_j
     exactly (one rounding on both sides), and grad_b equals lambda.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -96,21 +103,37 @@ def test_config5_cut_forward_and_adjoint_match_oracle_iterates(big, hip):
     assert relerr(got, a.grad_values[0][ent]) <= 1e-10
 
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "config5_maxit500.json")
+
+
 @pytest.mark.timeout(900)
-def test_config5_configured_solve_reports_true_residual(big, hip):
+def test_config5_configured_solve_matches_oracle_at_maxit(big, hip):
     p, d, pat = big
-    banner(f"config 5: configured solve (tol {p.tol}, maxit {p.maxit})")
-    x, info = pat.solve(d["val"], d["b"], tol=p.tol, maxit=p.maxit, method="cg",
-                        precond="jacobi")
+    ref = json.load(open(GOLDEN))
+    assert (ref["n"], ref["nnz"], ref["maxit"]) == (p.n, p.nnz, p.maxit)
+    banner(f"config 5: configured solve (tol {p.tol}, maxit {p.maxit}) + adjoint")
+    opts = dict(tol=p.tol, maxit=p.maxit, method="cg", precond="jacobi")
+    x, info = pat.solve(d["val"], d["b"], **opts)
+    gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **opts)
     torch.cuda.synchronize()
     it, st, rel = int(info["iters"][0]), int(info["status"][0]), float(info["relres"][0])
-    banner(f"config 5: {it} iterations, status {st}, relres {rel:.3e}")
-    assert st in (hip.SLA_OK, hip.SLA_NOT_CONVERGED)
-    assert (st == hip.SLA_OK) == (rel <= p.tol)
-    assert it == p.maxit or st == hip.SLA_OK
-    tr = float(O.true_relres(p.row_ptr, p.col, p.values, x.cpu().numpy(), p.b)[0])
-    # the recurrence residual tracks the true one; they drift apart by
-    # rounding only (relative 1e-6 of the residual here, far above 1e-10)
-    assert abs(tr - rel) <= 1e-6 * tr + 1e-14, (tr, rel)
-    # CG with Jacobi reduces the residual by orders of magnitude in 500 steps
-    assert tr < 1e-2
+    banner(f"config 5: {it} iterations, status {st}, relres {rel:.6e} "
+           f"(oracle {ref['forward']['relres']:.6e})")
+    for got, want in ((info, ref["forward"]), (ainfo, ref["adjoint"])):
+        assert int(got["iters"][0]) == want["iters"] == p.maxit
+        assert int(got["status"][0]) == want["status"] == hip.SLA_NOT_CONVERGED
+        assert abs(float(got["relres"][0]) - want["relres"]) <= 1e-7 * want["relres"]
+    rows = np.asarray(ref["rows"], dtype=np.int64)
+    xh = x.cpu().numpy()[0]
+    lam = gb.cpu().numpy()[0]
+    assert relerr(xh[rows], ref["x"]) <= 1e-7
+    assert relerr(lam[rows], ref["lambda"]) <= 1e-7
+    assert abs(np.linalg.norm(xh) - ref["forward"]["norm"]) <= 1e-7 * ref["forward"]["norm"]
+    assert abs(np.linalg.norm(lam) - ref["adjoint"]["norm"]) <= 1e-7 * ref["adjoint"]["norm"]
+    ents = torch.from_numpy(np.asarray(ref["entries"], dtype=np.int64)).cuda()
+    assert relerr(gv[0, ents].cpu().numpy(), ref["grad_values"]) <= 1e-7
+    # the reported (recurrence) residual against the oracle's true residual
+    # of the GPU's x; they drift apart by rounding only
+    tr = float(O.true_relres(p.row_ptr, p.col, p.values, xh[None, :], p.b)[0])
+    assert abs(tr - rel) <= 1e-6 * tr, (tr, rel)
