@@ -10,16 +10,19 @@ Prints one JSON line.  ``value`` = PCG iterations per second (forward and
 adjoint iterations summed over the timed steps, divided by the wall time
 between the synchronised start and end).
 
-``roofline`` describes the dominant kernel, timed live with HIP events around
-every launch on the stream it runs on (a separate, untimed step in the
-library's profile mode).  For CG that is ``cg_iter_kernel`` (one launch = one
-whole PCG iteration); its algorithmic bytes per launch are
-    nnz*(sv + 4) + (n + 1)*sr        matrix values, columns, row pointers
-  + 6*n*sv                           r, w, s_prev, M^-1, p_prev, x read once
-  + 5*n*sv                           x, p, s, r_next, w_next written
-(sv, sr: value and row-pointer widths; 5 + 5 vectors without a
-preconditioner).  For BiCGStab the two SpMV kernels are timed; their mean
-algorithmic bytes are nnz*(sv + 4) + (n + 1)*sr + 5*n*sv.
+``roofline`` describes the dominant kernel, timed live with HIP events that
+the runtime records at the start and end of every launch (hipExtLaunchKernel,
+on the stream the kernel runs on) in a separate, untimed step in the
+library's profile mode.  For CG that is ``cg_iter_kernel``: one launch is one
+whole PCG iteration, and ``achieved`` prices it at the method's algorithmic
+bytes per PCG iteration (SpMV plus the textbook recurrence's 11 vector passes)
+    nnz*(sv + 4) + (n + 1)*sr + 2*n*sv + 11*n*sv
+(sv, sr: value and row-pointer widths; 9 passes without a preconditioner).
+``kernel_bytes_per_launch`` is what the fused kernel itself must move: the
+matrix once plus, on average over the two iteration parities, 9 vectors
+(even launches read u, w, s, p and write p, s, u, w; odd launches also read
+and write x).  For BiCGStab the two SpMV kernels are timed and priced at the
+SpMV's algorithmic bytes nnz*(sv + 4) + (n + 1)*sr + 2*n*sv.
 ``traffic`` is the HBM bytes per launch measured with rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
 1 GiB copy) and stored under profiles/ with a hash of the kernel's sources;
@@ -77,13 +80,14 @@ def parse():
 
 
 def dominant_kernel(method, precond, n, nnz, sv, sr):
-    """(kernel name(s), algorithmic bytes per launch, source files)."""
+    """(kernel name(s), algorithmic bytes per launch, the kernel's own bytes
+    per launch, source files)."""
     mat = nnz * (sv + 4) + (n + 1) * sr
     if method == "cg":
-        vecs = 11 if precond == "jacobi" else 10
-        return ("cg_iter_kernel", mat + vecs * n * sv,
+        passes = 11 if precond == "jacobi" else 9
+        return ("cg_iter_kernel", mat + (2 + passes) * n * sv, mat + 9 * n * sv,
                 ["kernels_cg.hip", "spmv_tile.h", "sla_internal.h"])
-    return ("bicg_pv_kernel+bicg_st_kernel", mat + 5 * n * sv,
+    return ("bicg_pv_kernel+bicg_st_kernel", mat + 2 * n * sv, mat + 5 * n * sv,
             ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
 
 
@@ -155,8 +159,8 @@ def _counter_pass(d, short_names):
 
 def summarize_counters(args):
     p = load_problem(args)
-    kernel, kbytes, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
-                                           p.row_ptr.itemsize)
+    kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
+                                                p.values.itemsize, p.row_ptr.itemsize)
     names = kernel.split("+")
     f_kib, f_n, f_all, f_copy = _counter_pass(args.summarize_counters[0], names)
     w_kib, w_n, w_all, w_copy = _counter_pass(args.summarize_counters[1], names)
@@ -195,15 +199,16 @@ def summarize_counters(args):
         f"write_bytes_per_launch: {write:.0f}",
         f"hbm_bytes_per_launch: {fetch + write:.0f}",
         f"algorithmic_bytes_per_launch: {kbytes}",
-        f"traffic_over_algorithmic: {(fetch + write) / kbytes:.3f}",
+        f"kernel_bytes_per_launch: {own}",
+        f"traffic_over_kernel_bytes: {(fetch + write) / own:.3f}",
     ]
     print("\n".join(out))
 
 
 def summarize_trace(args):
     p = load_problem(args)
-    kernel, kbytes, _ = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
-                                        p.row_ptr.itemsize)
+    kernel, kbytes, own, _ = dominant_kernel(p.method, p.precond, p.n, p.nnz,
+                                             p.values.itemsize, p.row_ptr.itemsize)
     names = kernel.split("+")
     stats = _rows(args.summarize_trace, "*kernel_stats.csv")
     trace = _rows(args.summarize_trace, "*kernel_trace.csv")
@@ -243,6 +248,8 @@ def summarize_trace(args):
             f"avg_us_active: {avg:.2f}",
             f"algorithmic_bytes_per_launch: {kbytes}",
             f"achieved_GBps_active: {kbytes / (avg * 1e-6) / 1e9:.1f}",
+            f"kernel_bytes_per_launch: {own}",
+            f"kernel_GBps_active: {own / (avg * 1e-6) / 1e9:.1f}",
         ]
     print("\n".join(out))
 
@@ -325,8 +332,8 @@ def main():
     k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
     k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
     k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
-    kernel, kbytes, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz, p.values.itemsize,
-                                           p.row_ptr.itemsize)
+    kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
+                                                p.values.itemsize, p.row_ptr.itemsize)
     achieved = kbytes / k_avg_s / 1e9
     traffic = read_traffic(kernel, p.name, sources_sha(srcs))
 
@@ -352,6 +359,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_launch": kbytes,
+                     "kernel_bytes_per_launch": own,
+                     "kernel_GBps": own / k_avg_s / 1e9,
                      "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n},
     }
     if not args.no_cpu_baseline:

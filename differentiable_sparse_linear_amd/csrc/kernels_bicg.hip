@@ -72,8 +72,12 @@ struct PvOwn {
 // beta = (rho_k/rho_{k-1})(alpha_{k-1}/omega_{k-1});
 // p = r + beta (p - omega v) evaluated while gathering (p = r at k = 0);
 // v = A p; partial rhat.v.
+#ifndef SLA_BICG_WAVES
+#define SLA_BICG_WAVES 5
+#endif
 template <typename T, typename IT, int SLOTS>
-__global__ __launch_bounds__(kBlock) void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_BICG_WAVES)))
+void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
     const int it = st->iter_a;
@@ -162,7 +166,8 @@ struct StOwn {
 // Iteration k (k = iter_b): alpha = rho_k / rhat.v (0: breakdown);
 // s = r - alpha v evaluated while gathering, t = A s; partials t.s, t.t, s.s.
 template <typename T, typename IT, int SLOTS>
-__global__ __launch_bounds__(kBlock) void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_BICG_WAVES)))
+void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
     const int it = st->iter_b;
