@@ -19,9 +19,10 @@ bytes per PCG iteration (SpMV plus the textbook recurrence's 11 vector passes)
     nnz*(sv + 4) + (n + 1)*sr + 2*n*sv + 11*n*sv
 (sv, sr: value and row-pointer widths; 9 passes without a preconditioner).
 ``kernel_bytes_per_launch`` is what the fused kernel itself must move: the
-matrix once plus, on average over the two iteration parities, 9 vectors
-(even launches read u, w, s, p and write p, s, u, w; odd launches also read
-and write x).  For BiCGStab the two SpMV kernels are timed and priced at the
+matrix once (columns at 2 bytes when the handle keeps its compact
+tile-relative copy, else 4) plus, on average over the two iteration
+parities, 9 vectors (even launches read u, w, s, p and write p, s, u, w; odd
+launches also read and write x).  For BiCGStab the two SpMV kernels are timed and priced at the
 SpMV's algorithmic bytes nnz*(sv + 4) + (n + 1)*sr + 2*n*sv.
 ``traffic`` is the HBM bytes per launch measured with rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
@@ -76,19 +77,38 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs of --kernel-only")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
+                    help="column width the summarised run's products read")
     return ap.parse_args()
 
 
-def dominant_kernel(method, precond, n, nnz, sv, sr):
+def dominant_kernel(method, precond, n, nnz, sv, sr, sc=4):
     """(kernel name(s), algorithmic bytes per launch, the kernel's own bytes
-    per launch, source files)."""
+    per launch with column width sc, source files)."""
     mat = nnz * (sv + 4) + (n + 1) * sr
+    own = nnz * (sv + sc) + (n + 1) * sr
     if method == "cg":
         passes = 11 if precond == "jacobi" else 9
-        return ("cg_iter_kernel", mat + (2 + passes) * n * sv, mat + 9 * n * sv,
+        return ("cg_iter_kernel", mat + (2 + passes) * n * sv, own + 9 * n * sv,
                 ["kernels_cg.hip", "spmv_tile.h", "sla_internal.h"])
-    return ("bicg_pv_kernel+bicg_st_kernel", mat + 2 * n * sv, mat + 5 * n * sv,
+    return ("bicg_pv_kernel+bicg_st_kernel", mat + 2 * n * sv, own + 5 * n * sv,
             ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
+
+
+def column_bytes(p):
+    """2 when a handle on this pattern keeps the compact column copy, else 4
+    (decided by the library: a compact handle holds 2 bytes per entry more
+    than a wide one, per stored pattern)."""
+    import torch
+    import differentiable_sparse_linear_amd as sla
+    rp = torch.from_numpy(p.row_ptr).cuda()
+    col = torch.from_numpy(p.col).cuda()
+    a = sla.Pattern(rp, col, compact_columns=True)
+    b = sla.Pattern(rp, col, compact_columns=False)
+    extra = a.workspace_bytes() - b.workspace_bytes()
+    a.close()
+    b.close()
+    return 2 if extra == 2 * p.nnz else 4
 
 
 def sources_sha(files):
@@ -160,7 +180,8 @@ def _counter_pass(d, short_names):
 def summarize_counters(args):
     p = load_problem(args)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
-                                                p.values.itemsize, p.row_ptr.itemsize)
+                                                p.values.itemsize, p.row_ptr.itemsize,
+                                                args.column_bytes)
     names = kernel.split("+")
     f_kib, f_n, f_all, f_copy = _counter_pass(args.summarize_counters[0], names)
     w_kib, w_n, w_all, w_copy = _counter_pass(args.summarize_counters[1], names)
@@ -208,7 +229,8 @@ def summarize_counters(args):
 def summarize_trace(args):
     p = load_problem(args)
     kernel, kbytes, own, _ = dominant_kernel(p.method, p.precond, p.n, p.nnz,
-                                             p.values.itemsize, p.row_ptr.itemsize)
+                                             p.values.itemsize, p.row_ptr.itemsize,
+                                             args.column_bytes)
     names = kernel.split("+")
     stats = _rows(args.summarize_trace, "*kernel_stats.csv")
     trace = _rows(args.summarize_trace, "*kernel_trace.csv")
@@ -332,8 +354,9 @@ def main():
     k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
     k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
     k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
+    sc = column_bytes(p)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
-                                                p.values.itemsize, p.row_ptr.itemsize)
+                                                p.values.itemsize, p.row_ptr.itemsize, sc)
     achieved = kbytes / k_avg_s / 1e9
     traffic = read_traffic(kernel, p.name, sources_sha(srcs))
 
@@ -359,7 +382,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "bytes_per_launch": kbytes,
-                     "kernel_bytes_per_launch": own,
+                     "kernel_bytes_per_launch": own, "column_bytes": sc,
                      "kernel_GBps": own / k_avg_s / 1e9,
                      "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n},
     }

@@ -35,6 +35,7 @@ SLA_F32, SLA_F64 = 0, 1
 SLA_I32, SLA_I64 = 0, 1
 SLA_CG, SLA_BICGSTAB = 0, 1
 SLA_PRECOND_NONE, SLA_PRECOND_JACOBI = 0, 1
+SLA_CREATE_TRANSPOSE, SLA_CREATE_WIDE_COLUMNS = 1, 2
 SLA_OK, SLA_NOT_CONVERGED, SLA_BREAKDOWN = 0, 1, 2
 SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
 SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
@@ -133,13 +134,13 @@ def _check(t: torch.Tensor, name: str, dtype=None, numel=None):
 # -------------------------------------------------------------- raw C calls
 
 def sla_create(n, nnz, batch, dtype, row_ptr: torch.Tensor, col: torch.Tensor,
-               build_transpose: bool, stream=None) -> int:
+               flags: int, stream=None) -> int:
     lib = load()
     h = ctypes.c_void_p()
     itype = SLA_I64 if row_ptr.dtype == torch.int64 else SLA_I32
     dt = SLA_F64 if dtype == torch.float64 else SLA_F32
     st = lib.sla_create(ctypes.byref(h), int(n), int(nnz), int(batch), dt, itype, _ptr(row_ptr),
-                        _ptr(col), 1 if build_transpose else 0, _stream(stream))
+                        _ptr(col), int(flags), _stream(stream))
     if st != SLA_OK:
         raise SlaError(st, "sla_create")
     return h.value
@@ -196,11 +197,15 @@ class Pattern:
     """A CSR pattern on the device shared by ``batch`` value arrays.
 
     row_ptr: int32/int64 [n+1], col: int32 [nnz] (device tensors, kept alive
-    by this object because the library borrows them).
+    by this object because the library borrows them).  ``build_transpose``
+    builds the map of A^T (transposed products, BiCGStab adjoint);
+    ``compact_columns`` lets the handle read a 2-byte tile-relative copy of
+    the columns where every entry fits (identical results, fewer bytes).
     """
 
     def __init__(self, row_ptr: torch.Tensor, col: torch.Tensor, batch: int = 1,
-                 dtype: torch.dtype = torch.float64, build_transpose: bool = False, stream=None):
+                 dtype: torch.dtype = torch.float64, build_transpose: bool = False,
+                 compact_columns: bool = True, stream=None):
         _check(row_ptr, "row_ptr")
         _check(col, "col", torch.int32)
         if row_ptr.dtype not in (torch.int32, torch.int64):
@@ -214,8 +219,9 @@ class Pattern:
         self.dtype = dtype
         self.has_transpose = bool(build_transpose)
         self.device = row_ptr.device
-        self.handle = sla_create(self.n, self.nnz, self.batch, dtype, row_ptr, col,
-                                 build_transpose, stream)
+        flags = (SLA_CREATE_TRANSPOSE if build_transpose else 0) | \
+            (0 if compact_columns else SLA_CREATE_WIDE_COLUMNS)
+        self.handle = sla_create(self.n, self.nnz, self.batch, dtype, row_ptr, col, flags, stream)
 
     def close(self):
         if getattr(self, "handle", None):

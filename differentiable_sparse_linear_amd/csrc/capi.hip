@@ -43,13 +43,14 @@ struct sla_ctx {
     int dtype = SLA_F64, itype = SLA_I32;
     const void *rp = nullptr;
     const int32_t *col = nullptr;
+    int16_t *col16 = nullptr;    // compact columns of A, or null
     void *diagpos = nullptr;
     bool has_t = false;
     void *rp_t = nullptr;
     int32_t *col_t = nullptr;
+    int16_t *col16_t = nullptr;  // compact columns of A^T, or null
     int32_t *perm = nullptr;
     void *val_t = nullptr;
-    int G = 8;       // lanes per row of the one-workgroup solver
     int slots = 8;   // gather slots per row (A), from its longest row
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
@@ -111,8 +112,10 @@ void release(sla_ctx *h) {
         if (e) (void)hipEventDestroy(e);
     if (h->cap) (void)hipStreamDestroy(h->cap);
     (void)hipFree(h->diagpos);
+    (void)hipFree(h->col16);
     (void)hipFree(h->rp_t);
     (void)hipFree(h->col_t);
+    (void)hipFree(h->col16_t);
     (void)hipFree(h->perm);
     (void)hipFree(h->val_t);
     (void)hipFree(h->vec);
@@ -150,7 +153,7 @@ sla_status check_opts(const sla_solve_opts &o) {
 struct Operator {
     const void *rp;
     const int32_t *col;
-    int G;
+    const int16_t *col16;
     int slots;
 };
 
@@ -163,12 +166,14 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     const int64_t n = h->n;
     const bool cg = o.method == SLA_CG;
     const bool jac = cg && o.precond == SLA_PRECOND_JACOBI;
+    const bool c16 = op.col16 != nullptr;
     T *vec = reinterpret_cast<T *>(h->vec);
     IterArgs<T, IT> a;
     memset(&a, 0, sizeof(a));
     a.val = val;
     a.rp = reinterpret_cast<const IT *>(op.rp);
     a.col = op.col;
+    a.col16 = op.col16;
     a.x = x;
     a.b = b;
     a.r = vec + 0 * n;
@@ -199,20 +204,21 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
     // reads it always, so it is zeroed when there is no initial guess
     if (o.use_x0)
-        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.col, val, 0, x, cg ? a.t : a.q, n, 0, 1, s));
+        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.col, op.col16, val, 0, x, cg ? a.t : a.q, n,
+                                   0, 1, s));
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n, s));
     if (cg)
-        HIP_TRY(launch_cg_init<T, IT>(op.slots, jac, ad, n, s));
+        HIP_TRY(launch_cg_init<T, IT>(op.slots, c16, jac, ad, n, s));
     else
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) return launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, ss);
-        if ((e = launch_bicg_pv<T, IT>(op.slots, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_bicg_st<T, IT>(op.slots, ad, n, ss)) != hipSuccess) return e;
+        if (cg) return launch_cg_iter<T, IT>(op.slots, c16, jac, ad, n, k & 1, ss);
+        if ((e = launch_bicg_pv<T, IT>(op.slots, c16, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_bicg_st<T, IT>(op.slots, c16, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_update<T, IT>(ad, n, ss);
     };
 
@@ -232,12 +238,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(op.slots, jac, ad, n, k & 1, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_cg_iter<T, IT>(op.slots, c16, jac, ad, n, k & 1, s,
+                                              &h->prof_ev[ev]));
                 ev += 2;
             } else {
-                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, c16, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_st<T, IT>(op.slots, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_st<T, IT>(op.slots, c16, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
@@ -273,7 +280,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         if (cg && (chunk & 1)) ++chunk;
         hipGraphExec_t exec = nullptr;
         if (o.graph_chunk >= 0) {
-            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.G != h->G || op.rp != h->rp ? 2 : 0);
+            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0);
             GraphEntry *slot = nullptr;
             for (auto &g : h->graphs)
                 if (g.key == key && g.chunk == chunk) slot = &g;
@@ -396,12 +403,12 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     oo.use_x0 = 0;
     sla_status st;
     if (o.method == SLA_CG) {
-        Operator op{h->rp, h->col, h->G, h->slots};
+        Operator op{h->rp, h->col, h->col16, h->slots};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
         // A^T with values gathered through the transpose map, one system at
         // a time into the handle's buffer
-        Operator op{h->rp_t, h->col_t, h->G, h->slots_t};
+        Operator op{h->rp_t, h->col_t, h->col16_t, h->slots_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
         std::vector<int32_t> it(B0), mv(B0), stc(B0);
@@ -445,15 +452,28 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     if (st == SLA_ERR_DEVICE) return st;
     for (int64_t s0 = 0; s0 < B; s0 += 65535) {
         const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
-        HIP_TRY(launch_grad<T, IT>(h->G, reinterpret_cast<const IT *>(h->rp), h->col, gb + s0 * n,
+        HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, gb + s0 * n,
                                    x + s0 * n, gval + s0 * nnz, n, nnz, nb, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
     return st;
 }
 
+// Compact columns for the pattern (rp, col) when every entry fits.
+template <typename IT>
+hipError_t build_col16(sla_ctx *h, const IT *rp, const int32_t *col, int16_t **out,
+                       hipStream_t s) {
+    int32_t fits = 0;
+    hipError_t e = setup_col16<IT>(rp, col, h->n, nullptr, h->flag, &fits, s);
+    if (e != hipSuccess || !fits) return e;
+    if ((e = dmalloc(h, out, sizeof(int16_t) * h->nnz)) != hipSuccess) return e;
+    return setup_col16<IT>(rp, col, h->n, *out, h->flag, &fits, s);
+}
+
 template <typename T, typename IT>
-sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
+sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
+    const bool build_t = (flags & SLA_CREATE_TRANSPOSE) != 0;
+    const bool compact = (flags & SLA_CREATE_WIDE_COLUMNS) == 0;
     const int64_t n = h->n, nnz = h->nnz;
     const IT *rp = reinterpret_cast<const IT *>(h->rp);
     HIP_TRY(dmalloc(h, &h->diagpos, sizeof(IT) * n));
@@ -478,7 +498,11 @@ sla_status create_typed(sla_ctx *h, int32_t build_t, hipStream_t s) {
         h->has_t = true;
         HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
         h->slots_t = slots_for(maxlen);
+        if (compact)
+            HIP_TRY(build_col16<IT>(h, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
+                                    &h->col16_t, s));
     }
+    if (compact) HIP_TRY(build_col16<IT>(h, rp, h->col, &h->col16, s));
     HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
     HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
     HIP_TRY(dmalloc(h, &h->part, sizeof(double) * kMaxRed * kMaxGrid));
@@ -511,14 +535,15 @@ extern "C" {
 
 sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch, int32_t dtype,
                       int32_t row_ptr_type, const void *d_row_ptr, const int32_t *d_col,
-                      int32_t build_transpose, void *stream) {
+                      int32_t flags, void *stream) {
     if (!out) return SLA_ERR_ARG;
     *out = nullptr;
     if (n < 1 || n >= ((int64_t)1 << 31) || nnz < n || batch < 1) return SLA_ERR_ARG;
     if (dtype != SLA_F32 && dtype != SLA_F64) return SLA_ERR_ARG;
     if (row_ptr_type != SLA_I32 && row_ptr_type != SLA_I64) return SLA_ERR_ARG;
     if (row_ptr_type == SLA_I32 && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
-    if (build_transpose && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
+    if (flags & ~(SLA_CREATE_TRANSPOSE | SLA_CREATE_WIDE_COLUMNS)) return SLA_ERR_ARG;
+    if ((flags & SLA_CREATE_TRANSPOSE) && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
     if (!d_row_ptr || !d_col) return SLA_ERR_ARG;
     sla_ctx *h = new (std::nothrow) sla_ctx();
     if (!h) return SLA_ERR_NO_MEMORY;
@@ -533,12 +558,11 @@ sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch, in
     h->itype = row_ptr_type;
     h->rp = d_row_ptr;
     h->col = d_col;
-    h->G = lanes_for(n, nnz);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     sla_status st = dispatch(h, [&](auto t, auto it) {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        return create_typed<T, IT>(h, build_transpose, s);
+        return create_typed<T, IT>(h, flags, s);
     });
     if (st != SLA_OK) {
         if (st == SLA_ERR_DEVICE && g_last_error == hipErrorOutOfMemory) st = SLA_ERR_NO_MEMORY;
@@ -573,11 +597,12 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             const T *x = reinterpret_cast<const T *>(d_x) + s0 * h->n;
             T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
             if (transpose)
-                HIP_TRY((launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
-                                                 h->perm, v, h->nnz, x, y, h->n, h->n, nb, s)));
+                HIP_TRY((launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t),
+                                                 h->col_t, h->col16_t, h->perm, v, h->nnz, x, y,
+                                                 h->n, h->n, nb, s)));
             else
-                HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->col, v,
-                                            h->nnz, x, y, h->n, h->n, nb, s)));
+                HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->col,
+                                            h->col16, v, h->nnz, x, y, h->n, h->n, nb, s)));
         }
         return SLA_OK;
     });
@@ -593,7 +618,7 @@ sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *
     return dispatch(h, [&](auto t, auto it) -> sla_status {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        Operator op{h->rp, h->col, h->G, h->slots};
+        Operator op{h->rp, h->col, h->col16, h->slots};
         return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
                                 reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
                                 info, s);

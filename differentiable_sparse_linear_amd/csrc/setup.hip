@@ -100,6 +100,26 @@ __global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ 
     atomicMax(out, mi);
 }
 
+// One thread per row: the offsets of the row's columns from its tile's first
+// row; any offset outside int16 sets *bad.  `out` may be null (check only).
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void col16_kernel(const IT *__restrict__ rp,
+                                                       const int32_t *__restrict__ col, int64_t n,
+                                                       int16_t *__restrict__ out, int32_t *bad) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int b = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        const int64_t row0 = i / kTileRows * kTileRows;
+        for (IT k = rp[i]; k < rp[i + 1]; ++k) {
+            const int64_t d = (int64_t)col[k] - row0;
+            const bool ok = d >= -32768 && d <= 32767;
+            b |= !ok;
+            if (out && ok) out[k] = (int16_t)d;
+        }
+    }
+    if (__any(b) && (threadIdx.x & 63) == 0) atomicOr(bad, 1);
+}
+
 static unsigned blocks_for(int64_t m) {
     int64_t b = (m + kBlock - 1) / kBlock;
     if (b > 65536) b = 65536;
@@ -133,6 +153,21 @@ hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out
     if ((e = hipMemcpyAsync(out, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
     return hipStreamSynchronize(s);
+}
+
+template <typename IT>
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int16_t *out,
+                       int32_t *scratch, int32_t *fits, hipStream_t s) {
+    hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
+    if (e != hipSuccess) return e;
+    col16_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, out, scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int32_t bad = 1;
+    if ((e = hipMemcpyAsync(&bad, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    *fits = bad ? 0 : 1;
+    return hipSuccess;
 }
 
 template <typename IT>
@@ -175,6 +210,10 @@ template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, in
                                             int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
                                             int64_t *, int32_t *, hipStream_t);
+template hipError_t setup_col16<int32_t>(const int32_t *, const int32_t *, int64_t, int16_t *,
+                                         int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_col16<int64_t>(const int64_t *, const int32_t *, int64_t, int16_t *,
+                                         int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_max_row<int32_t>(const int32_t *, int64_t, int32_t *, int32_t *,
                                            hipStream_t);
 template hipError_t setup_max_row<int64_t>(const int64_t *, int64_t, int32_t *, int32_t *,

@@ -76,6 +76,7 @@ struct IterArgs {
     const T *val;
     const IT *rp;
     const int32_t *col;
+    const int16_t *col16;  // compact columns (tile-relative), or null
     T *x;
     const T *b;
     const T *dinv;
@@ -207,15 +208,6 @@ __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileRows -
 // 4, 6 or 8 (longer rows finish with a loop).
 inline int slots_for(int64_t max_len) { return max_len <= 4 ? 4 : (max_len <= 6 ? 6 : 8); }
 
-// Lanes per row from the mean row length: the smallest power of two >= mean,
-// in [2, 64].
-inline int lanes_for(int64_t n, int64_t nnz) {
-    const double mean = n > 0 ? (double)nnz / (double)n : 1.0;
-    int g = 2;
-    while (g < 64 && g < mean) g <<= 1;
-    return g;
-}
-
 // ---------------------------------------------------------------- launchers
 // (defined in the .hip files; all return hipError_t of the launch)
 
@@ -232,17 +224,19 @@ inline void launch_maybe_timed(void (*k)(KArgs...), dim3 grid, dim3 block, uint3
         hipLaunchKernelGGL(k, grid, block, lds, s, args...);
 }
 
-// The `slots` argument of the SpMV-shaped launchers is slots_for(longest row).
+// The `slots` argument of the SpMV-shaped launchers is slots_for(longest row);
+// `col16` (or `c16` for the kernels that read the argument block) selects the
+// compact tile-relative columns when the handle has them.
 template <typename T, typename IT>
-hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const T *val, int64_t val_stride,
-                       const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
-                       hipStream_t s);
+hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
+                       const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
+                       int64_t vec_stride, int batch, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int32_t *perm,
-                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                            int64_t vec_stride, int batch, hipStream_t s);
+hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
+                            const int32_t *perm, const T *val, int64_t val_stride, const T *x,
+                            T *y, int64_t n, int64_t vec_stride, int batch, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_grad(int G, const IT *rp, const int32_t *col, const T *lam, const T *x,
+hipError_t launch_grad(const IT *rp, const int32_t *col, const T *lam, const T *x,
                        T *grad, int64_t n, int64_t nnz, int batch, hipStream_t s);
 template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
@@ -253,20 +247,21 @@ hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, Solv
 // CG (grid path, one system): init, then one launch per iteration with the
 // iteration's parity
 template <typename T, typename IT>
-hipError_t launch_cg_init(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_cg_init(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+                          hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, bool jac, const IterArgs<T, IT> *a, int64_t n, int ph,
-                          hipStream_t s, const hipEvent_t *ev = nullptr);
+hipError_t launch_cg_iter(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+                          int ph, hipStream_t s, const hipEvent_t *ev = nullptr);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
-                          const hipEvent_t *ev = nullptr);
+hipError_t launch_bicg_pv(int slots, bool c16, const IterArgs<T, IT> *a, int64_t n,
+                          hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, const IterArgs<T, IT> *a, int64_t n, hipStream_t s,
-                          const hipEvent_t *ev = nullptr);
+hipError_t launch_bicg_st(int slots, bool c16, const IterArgs<T, IT> *a, int64_t n,
+                          hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
 hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
@@ -301,6 +296,12 @@ hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t n
                           int32_t *flag, hipStream_t s);
 template <typename IT>
 hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s);
+// Compact columns: out[k] = col[k] - (first row of row(k)'s tile) as int16.
+// With out == nullptr only checks; *fits = 1 when every entry fits
+// (synchronizes `s`).
+template <typename IT>
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int16_t *out,
+                       int32_t *scratch, int32_t *fits, hipStream_t s);
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
                            int32_t *col_t, int32_t *perm, hipStream_t s);

@@ -116,6 +116,27 @@ constexpr int round_for(int slots, int round) {
     return r;
 }
 
+// Where the kernels read column indices.  C16 = false: the caller's int32
+// array.  C16 = true: a compact copy built at set-up when every entry fits,
+// the int16 offset of the column from the first row of the entry's tile
+// (col = tile row0 + offset), which halves the index bytes of stencil-like
+// patterns.
+template <bool C16>
+struct ColSrc {
+    gptr<const int32_t> c32;
+    gptr<const int16_t> c16;
+    __device__ __forceinline__ int32_t operator()(int64_t k, int64_t row0) const {
+        if constexpr (C16)
+            return (int32_t)row0 + (int32_t)c16[k];
+        else
+            return c32[k];
+    }
+};
+template <bool C16>
+__device__ __forceinline__ ColSrc<C16> col_src(const int32_t *c32, const int16_t *c16) {
+    return ColSrc<C16>{glb(c32), glb(c16)};
+}
+
 template <typename T, typename IT>
 struct RowLds {
     IT rp[2][kTileRows + 1];
@@ -123,6 +144,7 @@ struct RowLds {
     int32_t col[kCap];
 };
 
+// col(k, row0): column of stored entry k of the tile starting at row0;
 // vf(k): value of stored entry k; gf(c): the loads gathered at column c;
 // cf(g): the vector entry those loads make (the gathers of ROUND slots are
 // all issued before the first cf); of(i): this thread's own-row inputs,
@@ -132,11 +154,11 @@ struct RowLds {
 // pre(): start-up loads issued with the first row pointers (no barrier
 // inside); post(): runs after the first barrier, every thread, and returns
 // false to end the kernel (the same in every thread).
-template <typename T, typename IT, int SLOTS, int ROUND, typename VF, typename GF, typename CF,
-          typename OF, typename RF, typename PRE, typename POST>
+template <typename T, typename IT, int SLOTS, int ROUND, typename CS, typename VF, typename GF,
+          typename CF, typename OF, typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
-                                          gptr<const int32_t> col, RowLds<T, IT> &sm, VF vf, GF gf,
-                                          CF cf, OF of, RF rf, PRE pre, POST post) {
+                                          CS col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf, OF of,
+                                          RF rf, PRE pre, POST post) {
     constexpr int R = round_for(SLOTS, ROUND);
     const int tid = threadIdx.x;
     auto rows_of = [&](int64_t tt) -> int {
@@ -179,7 +201,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 const int e = tid + j * kBlock;
                 const IT k = base + (e < last ? e : last);
                 v[j] = vf(k);
-                c[j] = col[k];
+                c[j] = col(k, row0);
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
@@ -236,7 +258,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 const int64_t row = row0 + r;
                 T s = T(0);
                 for (IT k = cr[r] + lane; k < hi; k += 64) {
-                    const int32_t c = col[k];
+                    const int32_t c = col(k, row0);
                     const T v = vf(k);
                     s += v * cf(gf(c));
                     if (c == row) pd[r] = v;  // one lane: the diagonal is stored once
@@ -252,6 +274,15 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
     }
     return true;
 }
+
+#define SLA_DISPATCH_C16(c16, ...)                  \
+    if (c16) {                                      \
+        constexpr bool kC = true;                   \
+        __VA_ARGS__;                                \
+    } else {                                        \
+        constexpr bool kC = false;                  \
+        __VA_ARGS__;                                \
+    }
 
 #define SLA_DISPATCH_SLOTS(slots, ...)                          \
     switch (slots) {                                            \

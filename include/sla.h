@@ -50,6 +50,7 @@ enum { SLA_F32 = 0, SLA_F64 = 1 };                 /* value / vector type   */
 enum { SLA_I32 = 0, SLA_I64 = 1 };                 /* row_ptr index type    */
 enum { SLA_CG = 0, SLA_BICGSTAB = 1 };             /* Krylov method         */
 enum { SLA_PRECOND_NONE = 0, SLA_PRECOND_JACOBI = 1 };
+enum { SLA_CREATE_TRANSPOSE = 1, SLA_CREATE_WIDE_COLUMNS = 2 };  /* sla_create flags */
 
 typedef enum {
     SLA_OK = 0,
@@ -100,16 +101,21 @@ typedef struct {
  *   dtype       SLA_F32 or SLA_F64;  row_ptr_type  SLA_I32 or SLA_I64
  *   d_row_ptr   [n+1] device array of row_ptr_type (borrowed)
  *   d_col       [nnz] device int32 column indices (borrowed)
- *   build_transpose  1: build the map of A^T (needed by sla_matvec with
- *               transpose = 1 and by the BiCGStab adjoint); requires
- *               nnz < 2^31
+ *   flags       SLA_CREATE_TRANSPOSE: build the map of A^T (needed by
+ *               sla_matvec with transpose = 1 and by the BiCGStab adjoint);
+ *               requires nnz < 2^31.
+ *               SLA_CREATE_WIDE_COLUMNS: read the caller's int32 columns in
+ *               every product.  Without it the handle also keeps a compact
+ *               copy (each column as an int16 offset from the first row of
+ *               its 256-row tile, 2 bytes per entry) when every entry fits,
+ *               and the products read that instead; results are identical.
+ *               Other bits: SLA_ERR_ARG.
  * Checks the pattern on the device (synchronizes `stream`).  Returns
  * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
  */
 sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch,
                       int32_t dtype, int32_t row_ptr_type, const void *d_row_ptr,
-                      const int32_t *d_col, int32_t build_transpose,
-                      void *stream);
+                      const int32_t *d_col, int32_t flags, void *stream);
 
 /* Release everything the handle owns (synchronizes the device). */
 sla_status sla_destroy(sla_handle h);

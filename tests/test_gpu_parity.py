@@ -345,6 +345,41 @@ def test_determinism_and_launch_modes_agree(hip):
             assert o[3] == outs[0][3]
 
 
+def test_compact_columns_change_nothing(hip):
+    """The 2-byte tile-relative column copy is a storage choice: products,
+    solves and adjoints are bitwise the same with the caller's int32 columns,
+    and it is kept only where every offset fits."""
+    banner("compact columns")
+    cases = [W.config(2, size=28), W.config(4, size=40), W.config(3, size=20, batch=4)]
+    for p in cases:
+        d = to_dev(p)
+        outs, ws = [], []
+        for compact in (True, False):
+            pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p),
+                              build_transpose=True, compact_columns=compact)
+            ws.append(pat.workspace_bytes())
+            xr = torch.from_numpy(np.random.default_rng(5).standard_normal((p.batch, p.n))
+                                  .astype(p.values.dtype)).cuda()
+            y = pat.matvec(d["val"], xr)
+            yt = pat.matvec(d["val"], xr, transpose=True)
+            kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit)
+            x, info = pat.solve(d["val"], d["b"], **kw)
+            gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
+            outs.append([t.cpu().numpy() for t in (y, yt, x, gv, gb)] +
+                        [info["iters"], ainfo["iters"]])
+            pat.close()
+        for a, b in zip(outs[0], outs[1]):
+            assert np.array_equal(a, b), p.name
+        # A and A^T compact: 2 bytes per stored entry each
+        assert ws[0] - ws[1] == 2 * 2 * p.nnz, (p.name, ws)
+    # offsets beyond int16: no compact copy
+    rp, col, val = W.powerlaw_graph_laplacian(60000, 9)
+    drp, dcol = torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda()
+    a = hip.Pattern(drp, dcol, compact_columns=True).workspace_bytes()
+    b = hip.Pattern(drp, dcol, compact_columns=False).workspace_bytes()
+    assert a == b
+
+
 def test_workspace_independent_of_iterations(hip):
     banner("memory vs maxit")
     p = W.config(2, size=24)
