@@ -17,7 +17,10 @@ arrays.  What it follows, from the torch-sla explainer pages (gist.science,
 * backward: one adjoint solve A^T lambda = dL/dx, dL/db = lambda and
   dL/dA_ij = -lambda_i x_j on the stored pattern only (Methodology section 2,
   linear systems).  dL/db = lambda is not printed on the pages; it follows from
-  the same implicit-function argument (b enters A x = b with coefficient +1).
+  the same implicit-function argument (b enters A x = b with coefficient +1);
+* the differentiable product y = A x (``.matvec`` of the autograd-aware API,
+  Methodology section 1) and its backward pass: grad_x = A^T dL/dy and
+  dL/dA_ij = (dL/dy)_i x_j on the stored pattern.
 
 Inputs of any float dtype are promoted to fp64 (an fp32 problem is solved in
 fp64 arithmetic on its fp32-rounded values); int32 row_ptr is widened to int64.
@@ -120,6 +123,8 @@ def _configure(lib):
     lib.orc_grad_on_pattern.restype = None
     lib.orc_adjoint.argtypes = [I64, I64, P, P, P, P, P, I, I, D, I64, P, P, P, P, P]
     lib.orc_adjoint.restype = I
+    lib.orc_matvec_vjp.argtypes = [I64, P, P, P, P, P, P, P]
+    lib.orc_matvec_vjp.restype = None
     return lib
 
 
@@ -281,6 +286,27 @@ def grad_on_pattern(row_ptr, col, lam, x) -> np.ndarray:
     for s in range(L.shape[0]):
         lib.orc_grad_on_pattern(n, _p(rp), _p(c), _p(L[s]), _p(X[s]), _p(G[s]))
     return G
+
+
+def matvec_vjp(row_ptr, col, values, x, grad_y):
+    """Backward pass of y = A x for upstream gradient grad_y = dL/dy:
+    (grad_x = A^T grad_y, grad_values[k] = grad_y[row(k)] x[col(k)]), each
+    [B, n] / [B, nnz] (1-D in, 1-D out)."""
+    lib = _load()
+    rp, c = _rp(row_ptr), _c(col)
+    n = rp.shape[0] - 1
+    one = np.ndim(x) == 1 and np.ndim(grad_y) == 1 and np.ndim(values) == 1
+    V = _batch2(values, c.shape[0])
+    X = _batch2(x, n)
+    G = _batch2(grad_y, n)
+    B = max(V.shape[0], X.shape[0], G.shape[0])
+    gx = np.empty((B, n))
+    gv = np.empty((B, c.shape[0]))
+    for s in range(B):
+        lib.orc_matvec_vjp(n, _p(rp), _p(c), _p(V[s if V.shape[0] > 1 else 0]),
+                           _p(X[s if X.shape[0] > 1 else 0]), _p(G[s if G.shape[0] > 1 else 0]),
+                           _p(gx[s]), _p(gv[s]))
+    return (gx[0], gv[0]) if one else (gx, gv)
 
 
 def adjoint(row_ptr, col, values, x, grad_x, method: str = "cg",

@@ -393,6 +393,35 @@ void orc_grad_on_pattern(int64_t n, const int64_t *row_ptr, const int32_t *col,
 }
 
 /*
+ * Vector-Jacobian product of the differentiable product y = A x (the
+ * autograd-aware .matvec of the unified API, Methodology section 1): for an
+ * upstream gradient gy = dL/dy,
+ *   grad_x[j]   = sum over stored entries (i, j) of A_ij gy[i]   (A^T gy),
+ *                 accumulated in increasing row i;
+ *   grad_val[k] = gy[row(k)] * x[col(k)]                          (dL/dA_ij).
+ * Either output may be NULL.
+ */
+void orc_matvec_vjp(int64_t n, const int64_t *row_ptr, const int32_t *col,
+                    const double *val, const double *x, const double *gy,
+                    double *grad_x, double *grad_val)
+{
+    int64_t i;
+    if (grad_x) {
+        for (i = 0; i < n; ++i)
+            grad_x[i] = 0.0;
+        for (i = 0; i < n; ++i)
+            for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+                grad_x[col[k]] += val[k] * gy[i];
+    }
+    if (grad_val) {
+#pragma omp parallel for schedule(static)
+        for (i = 0; i < n; ++i)
+            for (int64_t k = row_ptr[i]; k < row_ptr[i + 1]; ++k)
+                grad_val[k] = gy[i] * x[col[k]];
+    }
+}
+
+/*
  * Adjoint of x = A^-1 b for a loss gradient g = dL/dx:
  *   solve A^T lambda = g (x0 = 0, same method/tol/maxit, tol relative to ||g||),
  *   grad_b = lambda, grad_val[k] = -lambda[row(k)] x[col(k)].

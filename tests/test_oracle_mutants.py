@@ -27,6 +27,10 @@ MUTANTS = {
     "bicg_x_drops_omega_s": ("x[i] += alpha * p[i] + omega * s[i];", "x[i] += alpha * p[i];"),
     "bicg_half_step_skips_x": ("                x[i] += alpha * p[i];\n            rnorm = snorm;",
                                "                x[i] += 0.0 * p[i];\n            rnorm = snorm;"),
+    "vjp_grad_x_not_transposed": ("grad_x[col[k]] += val[k] * gy[i];",
+                                  "grad_x[i] += val[k] * gy[col[k]];"),
+    "vjp_grad_val_transposed": ("grad_val[k] = gy[i] * x[col[k]];",
+                                "grad_val[k] = x[i] * gy[col[k]];"),
     "transpose_unstable": ("int64_t dst = next[col[k]]++;", "int64_t dst = next[col[k]]; next[col[k]] += 1; dst = row_ptr_t[col[k] + 1] - 1 - (dst - row_ptr_t[col[k]]);"),
 }
 

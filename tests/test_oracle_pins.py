@@ -393,11 +393,56 @@ def pin_p16_bicgstab_half_step():
         assert _relerr(r.x[0], v / lam) <= 1e-13
 
 
+# --------------------------------------------------------------------------
+# P17 -- backward pass of the product y = A x: dense transpose product and
+# the dense outer product g x^T restricted to the pattern
+# --------------------------------------------------------------------------
+def pin_p17_matvec_vjp_dense():
+    rng = np.random.default_rng(21)
+    for seed, n in [(6, 9), (7, 40)]:
+        rp, col, val = W.random_csr(n, 0.25, seed, symmetric=False)
+        A = to_dense(rp, col, val)
+        x = rng.standard_normal(n)
+        g = rng.standard_normal(n)
+        gx, gv = O.matvec_vjp(rp, col, val[0], x, g)
+        scale = np.abs(A).T @ np.abs(g)
+        assert np.all(np.abs(gx - A.T @ g) <= 4e-16 * 8 * scale + 1e-300), "A^T g"
+        rows = np.repeat(np.arange(n), np.diff(rp))
+        assert np.array_equal(gv, g[rows] * x[col]), "g x^T on the pattern"
+
+
+# --------------------------------------------------------------------------
+# P18 -- the same backward pass by central differences of L = g . (A x)
+# --------------------------------------------------------------------------
+def pin_p18_matvec_vjp_finite_differences():
+    rng = np.random.default_rng(22)
+    rp, col, val = W.random_csr(12, 0.3, 8, symmetric=False)
+    v = val[0].copy()
+    x = rng.standard_normal(12)
+    g = rng.standard_normal(12)
+    loss = lambda vv, xx: float(g @ O.spmv(rp, col, vv, xx))
+    gx, gv = O.matvec_vjp(rp, col, v, x, g)
+    eps = 1e-6
+    for k in range(len(v)):
+        vp, vm = v.copy(), v.copy()
+        vp[k] += eps
+        vm[k] -= eps
+        fd = (loss(vp, x) - loss(vm, x)) / (2 * eps)
+        assert abs(fd - gv[k]) <= 1e-6 * max(1.0, abs(gv[k])), ("values", k)
+    for j in range(12):
+        xp, xm = x.copy(), x.copy()
+        xp[j] += eps
+        xm[j] -= eps
+        fd = (loss(v, xp) - loss(v, xm)) / (2 * eps)
+        assert abs(fd - gx[j]) <= 1e-6 * max(1.0, abs(gx[j])), ("x", j)
+
+
 ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
             pin_p5_cg_step_bound, pin_p6_dense_solve, pin_p7_jacobi_diagonal,
             pin_p8_bicgstab_vs_cg, pin_p9_transpose, pin_p10_symmetric_adjoint,
             pin_p11_diag_gradient, pin_p12_finite_differences, pin_p13_dense_outer,
             pin_p14_homogeneity, pin_p15_batch_is_loop, pin_p16_bicgstab_half_step,
+            pin_p17_matvec_vjp_dense, pin_p18_matvec_vjp_finite_differences,
             pin_pattern_checks, pin_special_cases]
 
 
