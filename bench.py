@@ -77,6 +77,10 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs of --kernel-only")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--op", default="solve", choices=("solve", "matvec", "matvec_vjp"),
+                    help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
+                         "the differentiable product and its backward pass on the same "
+                         "system, timed per call")
     ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
                     help="column width the summarised run's products read")
     return ap.parse_args()
@@ -235,13 +239,14 @@ def summarize_trace(args):
     stats = _rows(args.summarize_trace, "*kernel_stats.csv")
     trace = _rows(args.summarize_trace, "*kernel_trace.csv")
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    op = "" if args.op == "solve" else f" --op {args.op}"
     out = [
-        f"# Kernel time, bench.py on workload {p.name}",
+        f"# Kernel time, bench.py{op} on workload {p.name}",
         "",
         "Commands (repository root; OUT is any output folder):",
         "  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- "
-        f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload {args.workload}",
-        f"  python3 bench.py --summarize-trace OUT/trace --workload {args.workload}",
+        f"python3 bench.py{op} --steps 3 --warmup 1 --no-cpu-baseline --workload {args.workload}",
+        f"  python3 bench.py --summarize-trace OUT/trace{op} --workload {args.workload}",
         "",
         "rocprofv3 --stats (all dispatches):",
         f"{'calls':>8} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel",
@@ -253,6 +258,8 @@ def summarize_trace(args):
                    f"{float(r['TotalDurationNs']) / 1e6:10.2f} {float(r['Percentage']):6.2f}  "
                    f"{short}")
     durs = []
+    if args.op != "solve":
+        names = []  # the per-kernel block below describes the solve's iteration kernel
     for r in trace:
         if any(f"sla::{s}<" in r["Kernel_Name"] for s in names):
             durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -278,6 +285,64 @@ def summarize_trace(args):
 
 # ------------------------------------------------------------------ benchmark
 
+def bench_product(args, p):
+    """The differentiable product y = A x (matvec) or its backward pass
+    (matvec_vjp: grad_x = A^T g and grad_values = g_i x_j) on the workload's
+    matrix, `steps` calls timed with events on the stream they run on."""
+    import torch
+    import differentiable_sparse_linear_amd as sla
+    dev = "cuda:0"
+    tdt = torch.float64 if p.values.dtype == np.float64 else torch.float32
+    rp = torch.from_numpy(p.row_ptr).to(dev)
+    col = torch.from_numpy(p.col).to(dev)
+    val = torch.from_numpy(p.values).to(dev)
+    pat = sla.Pattern(rp, col, batch=p.batch, dtype=tdt, build_transpose=True)
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).to(dev)
+    g = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).to(dev)
+    y = torch.empty_like(x)
+    sv, sr = p.values.itemsize, p.row_ptr.itemsize
+    if args.op == "matvec":
+        call = lambda: pat.matvec(val, x, out=y)
+        # values + columns + row pointers, x once, y written
+        model = p.nnz * (sv + 4) + (p.n + 1) * sr + 2 * p.n * sv
+        kernel = "spmv_kernel"
+    else:
+        call = lambda: pat.matvec_adjoint(val, x, g)
+        # values + columns + row pointers once, g, x read, grad_x and
+        # grad_values written
+        model = p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv
+        kernel = "spmv_perm_kernel+grad_kernel"
+    model *= p.batch
+    steps = max(args.steps, 1) * 10
+    for _ in range(max(args.warmup, 1)):
+        call()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = ev0.elapsed_time(ev1) / steps * 1e-3
+    achieved = model / per / 1e9
+    print(json.dumps({
+        "metric": f"differentiable {args.op} calls/sec", "value": steps / wall,
+        "unit": "calls/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 1),
+        "ms_per_step": wall * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64" if p.values.dtype == np.float64 else "f32",
+        "data": "synthetic", "config": {"workload": p.name, "n": p.n, "nnz": p.nnz,
+                                        "batch": p.batch},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": model, "avg_launch_us": per * 1e6},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -296,6 +361,8 @@ def main():
         sys.exit(1)
     sla.load()
     p = load_problem(args)
+    if args.op != "solve":
+        return bench_product(args, p)
     dev = "cuda:0"
     tdt = torch.float64 if p.values.dtype == np.float64 else torch.float32
     rp = torch.from_numpy(p.row_ptr).to(dev)

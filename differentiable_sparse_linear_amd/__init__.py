@@ -21,8 +21,10 @@ import numpy as np
 import torch
 
 __all__ = [
-    "load", "SlaError", "Pattern", "SparseSolve", "sparse_solve",
-    "sla_create", "sla_destroy", "sla_matvec", "sla_solve", "sla_solve_adjoint",
+    "load", "SlaError", "Pattern", "PatternList", "SparseSolve", "sparse_solve",
+    "SparseMatvec", "sparse_matvec",
+    "sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
+    "sla_solve_adjoint",
     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
     "SLA_OK", "SLA_NOT_CONVERGED", "SLA_BREAKDOWN", "SLA_ERR_ARG", "SLA_ERR_PATTERN",
     "SLA_ERR_ZERO_DIAG", "SLA_ERR_NO_MEMORY", "SLA_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -40,7 +42,8 @@ SLA_OK, SLA_NOT_CONVERGED, SLA_BREAKDOWN = 0, 1, 2
 SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
 SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
 
-EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_solve", "sla_solve_adjoint",
+EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
+                    "sla_solve_adjoint",
                     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
                     "sla_last_error")
 
@@ -85,6 +88,8 @@ def load(path: Optional[str] = None):
     lib.sla_solve_adjoint.argtypes = [P, P, P, P, P, P, ctypes.POINTER(_Opts),
                                       ctypes.POINTER(_Info), P]
     lib.sla_solve_adjoint.restype = I32
+    lib.sla_matvec_adjoint.argtypes = [P, P, P, P, P, P, P]
+    lib.sla_matvec_adjoint.restype = I32
     lib.sla_export_pattern.argtypes = [P, P, P, P, P, P]
     lib.sla_export_pattern.restype = I32
     lib.sla_workspace_bytes.argtypes = [P]
@@ -155,6 +160,11 @@ def sla_destroy(h: int) -> None:
 def sla_matvec(h, values, x, y, transpose=False, stream=None) -> int:
     return load().sla_matvec(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(y),
                              1 if transpose else 0, _stream(stream))
+
+
+def sla_matvec_adjoint(h, values, x, grad_y, grad_x, grad_values, stream=None) -> int:
+    return load().sla_matvec_adjoint(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(grad_y),
+                                     _ptr(grad_x), _ptr(grad_values), _stream(stream))
 
 
 def _make_opts(tol, maxit, method, precond, use_x0, graph_chunk, profile):
@@ -253,6 +263,22 @@ class Pattern:
             raise SlaError(st, "sla_matvec")
         return y
 
+    def matvec_adjoint(self, values, x, grad_y, need_grad_x=True, need_grad_values=True,
+                       stream=None):
+        """Backward pass of y = A x: (grad_values, grad_x), either None when
+        not asked for.  grad_x = A^T grad_y needs the transpose map."""
+        self._vals(values)
+        self._vec(grad_y, "grad_y")
+        if need_grad_values:
+            self._vec(x, "x")
+        gx = torch.empty_like(grad_y) if need_grad_x else None
+        gv = torch.empty_like(values) if need_grad_values else None
+        st = sla_matvec_adjoint(self.handle, values, x if need_grad_values else None, grad_y,
+                                gx, gv, stream)
+        if st != SLA_OK:
+            raise SlaError(st, "sla_matvec_adjoint")
+        return gv, gx
+
     def solve(self, values, b, tol=1e-10, maxit=1000, method="cg", precond="jacobi", x0=None,
               graph_chunk=0, profile=False, check=True, out=None, stream=None):
         """Returns (x, info); info holds per-system iters/spmv/relres/status."""
@@ -331,3 +357,63 @@ class SparseSolve(torch.autograd.Function):
 def sparse_solve(pattern: Pattern, values: torch.Tensor, b: torch.Tensor, **opts) -> torch.Tensor:
     """Differentiable x = A(values)^-1 b; gradients flow to values and b."""
     return SparseSolve.apply(values, b, pattern, opts)
+
+
+class SparseMatvec(torch.autograd.Function):
+    """y = A(values) x with the product's backward pass (grad_x = A^T g needs
+    a pattern built with the transpose map)."""
+
+    @staticmethod
+    def forward(ctx, values, x, pattern: Pattern):
+        values, x = values.contiguous(), x.contiguous()
+        ctx.pattern = pattern
+        ctx.save_for_backward(values, x)
+        return pattern.matvec(values, x)
+
+    @staticmethod
+    def backward(ctx, grad_y):
+        values, x = ctx.saved_tensors
+        gv, gx = ctx.pattern.matvec_adjoint(values, x, grad_y.contiguous(),
+                                            need_grad_x=ctx.needs_input_grad[1],
+                                            need_grad_values=ctx.needs_input_grad[0])
+        return gv, gx, None
+
+
+def sparse_matvec(pattern: Pattern, values: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
+    """Differentiable y = A(values) x; gradients flow to values and x."""
+    return SparseMatvec.apply(values, x, pattern)
+
+
+class PatternList:
+    """Systems with distinct patterns (one handle per pattern), the ragged
+    counterpart of the shared-pattern batch.  Each call runs pattern by
+    pattern on the same stream; every product and solve runs in the
+    library's kernels."""
+
+    def __init__(self, patterns, dtype: torch.dtype = torch.float64,
+                 build_transpose: bool = False, compact_columns: bool = True, stream=None):
+        self.items = [Pattern(rp, col, 1, dtype, build_transpose, compact_columns, stream)
+                      for rp, col in patterns]
+
+    def __len__(self):
+        return len(self.items)
+
+    def __getitem__(self, i) -> Pattern:
+        return self.items[i]
+
+    def close(self):
+        for p in self.items:
+            p.close()
+
+    def matvec(self, values, xs, transpose=False, stream=None):
+        return [p.matvec(v, x, transpose=transpose, stream=stream)
+                for p, v, x in zip(self.items, values, xs)]
+
+    def solve(self, values, bs, **opts):
+        """Returns a list of (x, info)."""
+        return [p.solve(v, b, **opts) for p, v, b in zip(self.items, values, bs)]
+
+    def solve_adjoint(self, values, xs, grads, **opts):
+        """Returns a list of (grad_values, grad_b, info)."""
+        return [p.solve_adjoint(v, x, g, **opts)
+                for p, v, x, g in zip(self.items, values, xs, grads)]

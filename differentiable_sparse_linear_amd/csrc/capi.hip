@@ -453,7 +453,7 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     for (int64_t s0 = 0; s0 < B; s0 += 65535) {
         const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
         HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, gb + s0 * n,
-                                   x + s0 * n, gval + s0 * nnz, n, nnz, nb, s));
+                                   x + s0 * n, gval + s0 * nnz, n, nnz, nb, true, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
     return st;
@@ -603,6 +603,36 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             else
                 HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->col,
                                             h->col16, v, h->nnz, x, y, h->n, h->n, nb, s)));
+        }
+        return SLA_OK;
+    });
+}
+
+sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_x,
+                              const void *d_grad_y, void *d_grad_x, void *d_grad_values,
+                              void *stream) {
+    if (!h || !d_values || !d_grad_y || (!d_grad_x && !d_grad_values)) return SLA_ERR_ARG;
+    if (d_grad_x && (!h->has_t || d_grad_x == d_grad_y)) return SLA_ERR_ARG;
+    if (d_grad_values && !d_x) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        for (int64_t s0 = 0; s0 < h->batch; s0 += 65535) {
+            const int nb = (int)((h->batch - s0) < 65535 ? (h->batch - s0) : 65535);
+            const T *v = reinterpret_cast<const T *>(d_values) + s0 * h->nnz;
+            const T *gy = reinterpret_cast<const T *>(d_grad_y) + s0 * h->n;
+            if (d_grad_x)
+                HIP_TRY((launch_spmv_perm<T, IT>(
+                    h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->col_t, h->col16_t,
+                    h->perm, v, h->nnz, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, h->n,
+                    h->n, nb, s)));
+            if (d_grad_values)
+                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, gy,
+                                            reinterpret_cast<const T *>(d_x) + s0 * h->n,
+                                            reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz,
+                                            h->n, h->nnz, nb, false, s)));
         }
         return SLA_OK;
     });

@@ -49,10 +49,11 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
         [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
 
-// grad[k] = -lambda[row(k)] * x[col[k]].  Short tiles: each thread marks the
+// grad[k] = -lambda[row(k)] * x[col[k]] (NEG; the solve's gradient on the
+// pattern) or g[row(k)] * x[col[k]] (the product's).  Short tiles: each thread marks the
 // tile-local row of its row's entries in LDS, then the entries are written as
 // one coalesced run.  Tiles with long rows: one wavefront per row.
-template <typename T, typename IT>
+template <typename T, typename IT, bool NEG>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                                                       const int32_t *__restrict__ col,
                                                       const T *__restrict__ lam,
@@ -93,14 +94,20 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
-                if (e < cnt) grad[base + e] = -(slam[rid[e]] * x[c[j]]);
+                if (e < cnt) {
+                    const T g = slam[rid[e]] * x[c[j]];
+                    grad[base + e] = NEG ? -g : g;
+                }
             }
         } else {
             const int lane = tid & 63, wave = tid >> 6;
             for (int r = wave; r < rows; r += kWaves) {
                 const T li = slam[r];
                 const IT hi = srp[r + 1];
-                for (IT k = srp[r] + lane; k < hi; k += 64) grad[k] = -(li * x[col[k]]);
+                for (IT k = srp[r] + lane; k < hi; k += 64) {
+                    const T g = li * x[col[k]];
+                    grad[k] = NEG ? -g : g;
+                }
             }
         }
         __syncthreads();
@@ -170,9 +177,12 @@ hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const i
 
 template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const int32_t *col, const T *lam, const T *x, T *grad,
-                       int64_t n, int64_t nnz, int batch, hipStream_t s) {
+                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    grad_kernel<T, IT><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
+    if (neg)
+        grad_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
+    else
+        grad_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
     return hipGetLastError();
 }
 
@@ -209,8 +219,9 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
                                                 const int16_t *, const int32_t *, const T *,     \
                                                 int64_t, const T *, T *, int64_t, int64_t, int,  \
                                                 hipStream_t);                                    \
-    template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const T *,         \
-                                           const T *, T *, int64_t, int64_t, int, hipStream_t);  \
+    template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const T *,             \
+                                           const T *, T *, int64_t, int64_t, int, bool,          \
+                                           hipStream_t);  \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
                                            hipStream_t);
 

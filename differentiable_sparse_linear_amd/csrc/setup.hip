@@ -96,8 +96,13 @@ __global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ 
         const int64_t len = (int64_t)(rp[i + 1] - rp[i]);
         m = len > m ? len : m;
     }
-    const int32_t mi = m > 0x7fffffff ? 0x7fffffff : (int32_t)m;
-    atomicMax(out, mi);
+    int32_t mi = m > 0x7fffffff ? 0x7fffffff : (int32_t)m;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const int32_t o = __shfl_xor(mi, off, 64);
+        mi = o > mi ? o : mi;
+    }
+    if ((threadIdx.x & 63) == 0) atomicMax(out, mi);  // one atomic per wavefront
 }
 
 // One thread per row: the offsets of the row's columns from its tile's first

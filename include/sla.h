@@ -129,6 +129,23 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x,
                       void *d_y, int32_t transpose, void *stream);
 
 /*
+ * sla_matvec_adjoint -- backward pass of the differentiable product
+ * y[s] = A_s x[s] (the autograd-aware .matvec of the unified API, torch-sla
+ * explainer, Methodology section 1) for an upstream gradient
+ * d_grad_y[s] = dL/dy:
+ *   d_grad_x [batch][n]        = A_s^T grad_y[s]  (needs SLA_CREATE_TRANSPOSE;
+ *                                 must not alias d_grad_y)
+ *   d_grad_values [batch][nnz] = grad_y[s][row(k)] * x[s][col(k)] for every
+ *                                 stored entry k (needs d_x)
+ * Either output may be NULL (not both).  d_values, d_x, d_grad_y are inputs
+ * of the layouts above.  SLA_ERR_ARG for a missing input, a missing transpose
+ * map or aliasing.  Asynchronous on `stream`.
+ */
+sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_x,
+                              const void *d_grad_y, void *d_grad_x,
+                              void *d_grad_values, void *stream);
+
+/*
  * sla_solve -- forward solve A_s x[s] = b[s] for every system.
  *   d_values [batch][nnz]; d_b [batch][n]; d_x [batch][n] output (input
  *   initial guess when opts->use_x0).  Per-system stopping: a converged system

@@ -51,6 +51,7 @@ def test_status_strings_and_null_handle(libpath):
     h = ctypes.c_void_p()
     assert lib.sla_create(ctypes.byref(h), 0, 4, 1, 1, 0, None, None, 0, None) == sla.SLA_ERR_ARG
     assert lib.sla_solve(None, None, None, None, None, None, None) == sla.SLA_ERR_ARG
+    assert lib.sla_matvec_adjoint(None, None, None, None, None, None, None) == sla.SLA_ERR_ARG
 
 
 def test_product_path_has_no_oracle_or_fallback():

@@ -120,6 +120,109 @@ def test_spmv_int64_row_ptr(hip):
     _spmv_case(hip, p)
 
 
+# ------------------------------------------------------------------ product backward
+
+def _vjp_case(hip, p):
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p), build_transpose=True)
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)
+    g = rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)
+    gv, gx = pat.matvec_adjoint(d["val"], torch.from_numpy(x).cuda(), torch.from_numpy(g).cuda())
+    gv, gx = gv.cpu().numpy(), gx.cpu().numpy()
+    tol = FP_TOL[p.values.dtype]["spmv"]
+    rpt, ct, perm = O.transpose(p.n, p.row_ptr, p.col)
+    for s in range(p.batch):
+        v = p.values[s].astype(np.float64)
+        ogx, ogv = O.matvec_vjp(p.row_ptr, p.col, v, x[s].astype(np.float64),
+                                g[s].astype(np.float64))
+        bound = tol * O.spmv(rpt, ct, np.abs(v[perm]), np.abs(g[s].astype(np.float64))) + 1e-300
+        err = np.abs(gx[s].astype(np.float64) - ogx)
+        assert np.all(err <= bound), f"{p.name} sys {s}: grad_x worst {np.max(err / bound)}"
+        # one product per entry: the GPU's rounding of g_i x_j is the exact
+        # product rounded to the working precision, as is the oracle's
+        assert np.array_equal(gv[s], ogv.astype(p.values.dtype)), f"{p.name} sys {s}: grad_values"
+
+
+@pytest.mark.parametrize("case", ["convdiff_40", "random_nonsym_300", "batched_fp64",
+                                  "batched_fp32", "powerlaw", "cfg2_full"])
+def test_matvec_adjoint_matches_oracle(hip, case):
+    banner(f"matvec adjoint {case}")
+    if case == "convdiff_40":
+        p = W.config(4, size=40)
+    elif case == "random_nonsym_300":
+        rp, col, val = W.random_csr(300, 0.05, 3)
+        p = W.Problem("random300", 300, rp, col, val, np.zeros((1, 300)), np.zeros((1, 300)))
+    elif case == "batched_fp64":
+        p = W.config(3, size=20, batch=5)
+    elif case == "batched_fp32":
+        p = W.config(3, size=20, batch=5, dtype=np.float32)
+    elif case == "powerlaw":
+        rp, col, val = W.powerlaw_graph_laplacian(60000, 9)
+        p = W.Problem("powerlaw", 60000, rp, col, val, np.zeros((1, 60000)), np.zeros((1, 60000)))
+    else:
+        p = W.config(2)
+    _vjp_case(hip, p)
+
+
+def test_matvec_adjoint_arguments(hip):
+    banner("matvec adjoint arguments")
+    p = W.config(4, size=16)
+    d = to_dev(p)
+    x = torch.randn(p.n, dtype=torch.float64, device="cuda")
+    pat = hip.Pattern(d["rp"], d["col"])  # no transpose map
+    with pytest.raises(hip.SlaError) as ei:
+        pat.matvec_adjoint(d["val"], x, x)
+    assert ei.value.status == hip.SLA_ERR_ARG
+    gv, gx = pat.matvec_adjoint(d["val"], x, x, need_grad_x=False)  # values only: no map needed
+    assert gx is None and gv.shape == d["val"].shape
+    with pytest.raises(hip.SlaError):
+        pat.matvec_adjoint(d["val"], x, x, need_grad_x=False, need_grad_values=False)
+
+
+def test_sparse_matvec_autograd(hip):
+    banner("autograd matvec")
+    rp, col, val = W.random_csr(50, 0.2, 9, symmetric=False)
+    rows = torch.from_numpy(np.repeat(np.arange(50), np.diff(rp)))
+    cols = torch.from_numpy(col.astype(np.int64))
+    pat = hip.Pattern(torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda(),
+                      build_transpose=True)
+    v = torch.from_numpy(val[0].copy()).cuda().requires_grad_(True)
+    x = torch.randn(50, dtype=torch.float64, device="cuda", requires_grad=True)
+    w = torch.randn(50, dtype=torch.float64, device="cuda")
+    loss = (hip.sparse_matvec(pat, v, x) * w).sum()
+    loss.backward()
+    # the same loss through a dense CPU matrix
+    vc = v.detach().cpu().requires_grad_(True)
+    xc = x.detach().cpu().requires_grad_(True)
+    A = torch.zeros(50, 50, dtype=torch.float64).index_put((rows, cols), vc)
+    lc = ((A @ xc) * w.cpu()).sum()
+    lc.backward()
+    assert torch.allclose(v.grad.cpu(), vc.grad, rtol=1e-14, atol=1e-14)
+    assert torch.allclose(x.grad.cpu(), xc.grad, rtol=1e-12, atol=1e-13)
+    assert abs(loss.item() - lc.item()) <= 1e-12 * abs(lc.item())
+
+
+def test_pattern_list_is_a_loop_of_patterns(hip):
+    banner("pattern list")
+    probs = [W.config(1), W.config(4, size=24), W.config(2, size=9)]
+    devs = [to_dev(p) for p in probs]
+    plist = hip.PatternList([(d["rp"], d["col"]) for d in devs], build_transpose=True)
+    assert len(plist) == 3
+    xs = [torch.randn(p.n, dtype=torch.float64, device="cuda") for p in probs]
+    ys = plist.matvec([d["val"] for d in devs], xs)
+    outs = plist.solve([d["val"] for d in devs], [d["b"] for d in devs], tol=1e-10, maxit=4000,
+                       method="bicgstab", precond="none")
+    for p, d, x, y, (xsol, info) in zip(probs, devs, xs, ys, outs):
+        single = hip.Pattern(d["rp"], d["col"], build_transpose=True)
+        assert torch.equal(y, single.matvec(d["val"], x))
+        xs1, info1 = single.solve(d["val"], d["b"], tol=1e-10, maxit=4000, method="bicgstab",
+                                  precond="none")
+        assert torch.equal(xsol, xs1) and info["iters"][0] == info1["iters"][0]
+        r = O.solve(p.row_ptr, p.col, p.values, p.b, "bicgstab", "none", 1e-10, 4000)
+        assert relerr(xsol.cpu().numpy()[0], r.x[0]) <= 1e-7
+
+
 # ------------------------------------------------------------------ solves
 
 def _check_solve(p, g, r, a, systems=None):
