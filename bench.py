@@ -77,10 +77,13 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs of --kernel-only")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
-    ap.add_argument("--op", default="solve", choices=("solve", "matvec", "matvec_vjp"),
+    ap.add_argument("--op", default="solve",
+                    choices=("solve", "matvec", "matvec_vjp", "inverse"),
                     help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
                          "the differentiable product and its backward pass on the same "
-                         "system, timed per call")
+                         "system, timed per call; inverse: kappa recovery through the "
+                         "differentiable solve (64 x 64 grid, 8 forcings, 40 x steps Adam "
+                         "steps)")
     ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
                     help="column width the summarised run's products read")
     return ap.parse_args()
@@ -285,6 +288,28 @@ def summarize_trace(args):
 
 # ------------------------------------------------------------------ benchmark
 
+def bench_inverse(args):
+    """Recover kappa = exp(theta) on a 64 x 64 grid from 8 observed solutions
+    by Adam through the differentiable solve (forward and adjoint of 8
+    systems per step, one workgroup per system)."""
+    from differentiable_sparse_linear_amd import inverse as inv
+    steps = 40 * max(args.steps, 1)
+    inv.recover(N=64, B=8, steps=2)  # warm-up: library load, first launches
+    out = inv.recover(N=64, B=8, steps=steps)
+    print(json.dumps({
+        "metric": "inverse-coefficient recovery, Adam steps/sec through the differentiable solve",
+        "value": steps / out["wall_s"], "unit": "Adam steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": 2, "ms_per_step": out["wall_s"] * 1e3 / steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (smooth log-kappa, 8 N(0,1) forcing fields, seed 11)",
+        "config": {"workload": "inverse_kappa_64x64_b8", "grid": 64, "forcings": 8,
+                   "lr": 0.05, "beta": 1e-6},
+        "kappa_rel_err_start": out["kappa_rel_err_start"],
+        "kappa_rel_err": out["kappa_rel_err"], "loss_first": out["loss"][0],
+        "loss_last": out["loss"][-1], "wall_s": out["wall_s"], "roofline": None,
+    }), flush=True)
+
+
 def bench_product(args, p):
     """The differentiable product y = A x (matvec) or its backward pass
     (matvec_vjp: grad_x = A^T g and grad_values = g_i x_j) on the workload's
@@ -360,6 +385,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     sla.load()
+    if args.op == "inverse":
+        return bench_inverse(args)
     p = load_problem(args)
     if args.op != "solve":
         return bench_product(args, p)

@@ -1,0 +1,90 @@
+"""CPU reference of the inverse-coefficient experiment (test infrastructure).
+
+Independent of differentiable_sparse_linear_amd.inverse: the matrix comes
+from the seeded workload generator (workloads.varcoef_diffusion, the same
+harmonic-face stencil), the solves and adjoints from the oracle, the chain
+rule values -> kappa is derived here by hand, and Adam is written from
+Kingma & Ba (2015), Algorithm 1.
+
+Chain rule.  A face between cells a and b has coefficient
+f = 2 k_a k_b / (k_a + k_b); it enters A_ab = A_ba = -f and A_aa, A_bb with +f,
+so dL/df = G_aa + G_bb - G_ab - G_ba (G = dL/dvalues on the pattern), and
+df/dk_a = 2 k_b^2 / (k_a + k_b)^2.  A wall face of cell a is f = k_a and
+enters A_aa only.
+"""
+import numpy as np
+
+import oracle as O
+import workloads as W
+
+
+def interior_faces(N):
+    i = np.arange(N * N)
+    ix, iy = i % N, i // N
+    h = i[ix < N - 1]
+    v = i[iy < N - 1]
+    return np.concatenate([h, v]), np.concatenate([h + 1, v + N])
+
+
+def grad_kappa(N, rp, col, kap, G):
+    n = N * N
+    rows = np.repeat(np.arange(n), np.diff(rp))
+    pos = {(int(r), int(c)): k for k, (r, c) in enumerate(zip(rows, col))}
+    dk = np.zeros(n)
+    a, b = interior_faces(N)
+    for x, y in zip(a, b):
+        ka, kb = kap[x], kap[y]
+        dldf = G[pos[(x, x)]] + G[pos[(y, y)]] - G[pos[(x, y)]] - G[pos[(y, x)]]
+        dk[x] += dldf * 2.0 * kb * kb / (ka + kb) ** 2
+        dk[y] += dldf * 2.0 * ka * ka / (ka + kb) ** 2
+    i = np.arange(n)
+    ix, iy = i % N, i // N
+    walls = (ix == 0).astype(int) + (ix == N - 1) + (iy == 0) + (iy == N - 1)
+    for c in np.nonzero(walls)[0]:
+        dk[c] += walls[c] * G[pos[(c, c)]]
+    return dk
+
+
+class Reference:
+    def __init__(self, N, forcing, theta_true, beta, tol=1e-10, maxit=10000):
+        self.N, self.F, self.beta, self.tol, self.maxit = N, forcing, beta, tol, maxit
+        self.B = forcing.shape[0]
+        rp, col, vt = W.varcoef_diffusion((N, N), np.exp(theta_true))
+        self.rp, self.col = rp, col
+        self.u_obs = O.solve(rp, col, np.repeat(vt, self.B, axis=0), forcing, "cg", "jacobi",
+                             1e-12, maxit).x
+        self.scale = 0.5 * np.sum(self.u_obs ** 2)
+        self.a, self.b = interior_faces(N)
+
+    def loss_grad(self, theta):
+        kap = np.exp(theta)
+        _, _, vals = W.varcoef_diffusion((self.N, self.N), kap)
+        V = np.repeat(vals, self.B, axis=0)
+        r = O.solve(self.rp, self.col, V, self.F, "cg", "jacobi", self.tol, self.maxit)
+        gx = (r.x - self.u_obs) / self.scale
+        adj = O.adjoint(self.rp, self.col, V, r.x, gx, "cg", "jacobi", self.tol, self.maxit)
+        g = grad_kappa(self.N, self.rp, self.col, kap, adj.grad_values.sum(axis=0)) * kap
+        d = theta[self.a] - theta[self.b]
+        np.add.at(g, self.a, self.beta * d)
+        np.add.at(g, self.b, -self.beta * d)
+        loss = 0.5 * np.sum((r.x - self.u_obs) ** 2) / self.scale + \
+            0.5 * self.beta * np.sum(d * d)
+        return loss, g
+
+
+def adam(ref, steps, lr, b1=0.9, b2=0.999, eps=1e-8):
+    """Kingma & Ba, Algorithm 1, from theta = 0; returns (thetas, losses)."""
+    th = np.zeros(ref.N * ref.N)
+    m = np.zeros_like(th)
+    v = np.zeros_like(th)
+    thetas, losses = [], []
+    for t in range(1, steps + 1):
+        loss, g = ref.loss_grad(th)
+        m = b1 * m + (1 - b1) * g
+        v = b2 * v + (1 - b2) * g * g
+        mh = m / (1 - b1 ** t)
+        vh = v / (1 - b2 ** t)
+        th = th - lr * mh / (np.sqrt(vh) + eps)
+        thetas.append(th.copy())
+        losses.append(loss)
+    return thetas, losses

@@ -62,3 +62,17 @@ def test_powerlaw_graph_long_rows():
     assert lens.max() > 1000 and np.median(lens) < 16
     st, _ = O.check_pattern(20000, rp, col)
     assert st == O.OK
+
+
+def test_inverse_experiment_assembly_matches_generator():
+    """The inverse experiment's tensor assembly builds the same matrix as the
+    workload generator's harmonic-face stencil (host check, torch on CPU)."""
+    import torch
+    from differentiable_sparse_linear_amd import inverse as inv
+    for N in (1, 2, 7):
+        rp, col, mask = inv.stencil_pattern(N)
+        theta = np.random.default_rng(N).standard_normal(N * N)
+        r2, c2, v2 = W.varcoef_diffusion((N, N), np.exp(theta))
+        assert np.array_equal(rp, r2) and np.array_equal(col, c2)
+        v = inv.assemble_values(torch.from_numpy(theta), N, torch.from_numpy(mask)).numpy()
+        assert np.allclose(v, v2[0], rtol=1e-15, atol=0)
