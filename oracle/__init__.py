@@ -20,7 +20,10 @@ arrays.  What it follows, from the torch-sla explainer pages (gist.science,
   the same implicit-function argument (b enters A x = b with coefficient +1);
 * the differentiable product y = A x (``.matvec`` of the autograd-aware API,
   Methodology section 1) and its backward pass: grad_x = A^T dL/dy and
-  dL/dA_ij = (dL/dy)_i x_j on the stored pattern.
+  dL/dA_ij = (dL/dy)_i x_j on the stored pattern;
+* ``oracle.nonlinear``: Newton's method and the nonlinear adjoint for the
+  semilinear model F(u) = A u + c u^3 - f (Methodology section 2, nonlinear
+  systems).
 
 Inputs of any float dtype are promoted to fp64 (an fp32 problem is solved in
 fp64 arithmetic on its fp32-rounded values); int32 row_ptr is widened to int64.

@@ -437,12 +437,76 @@ def pin_p18_matvec_vjp_finite_differences():
         assert abs(fd - gx[j]) <= 1e-6 * max(1.0, abs(gx[j])), ("x", j)
 
 
+# --------------------------------------------------------------------------
+# P19 -- nonlinear adjoint, c = 0: Newton is one linear solve and the
+# gradients are the linear adjoint's
+# --------------------------------------------------------------------------
+def pin_p19_nonlinear_reduces_to_linear():
+    from oracle import nonlinear as NL
+    p = W.config(2, size=6)
+    v = p.values[0]
+    f = p.b[0]
+    c = np.zeros(p.n)
+    u, it, norms = NL.newton(p.row_ptr, p.col, v, c, f, tol=1e-10)
+    assert it == 1 and norms[-1] <= 1e-10 * norms[0]
+    g = u - p.x_t[0]
+    gv, gc, gf = NL.adjoint(p.row_ptr, p.col, v, c, u, g)
+    a = O.adjoint(p.row_ptr, p.col, v, u, g, "cg", "jacobi", 1e-12, 10000)
+    assert _relerr(gv, a.grad_values[0]) <= 1e-9 and _relerr(gf, a.grad_b[0]) <= 1e-9
+
+
+# --------------------------------------------------------------------------
+# P20 -- nonlinear adjoint against central differences of a dense Newton
+# (numpy.linalg.solve; a one-entry perturbation of A breaks symmetry)
+# --------------------------------------------------------------------------
+def _dense_newton(A, c, f):
+    u = np.zeros(len(f))
+    for _ in range(60):
+        F = A @ u + c * u ** 3 - f
+        if np.linalg.norm(F) <= 1e-15 * np.linalg.norm(f):
+            break
+        u = u - np.linalg.solve(A + np.diag(3.0 * c * u * u), F)
+    return u
+
+
+def pin_p20_nonlinear_adjoint_finite_differences():
+    from oracle import nonlinear as NL
+    rng = np.random.default_rng(31)
+    rp, col, val = W.varcoef_diffusion((4, 4), np.exp(0.5 * rng.standard_normal(16)))
+    v = val[0]
+    c = rng.uniform(0.5, 2.0, 16)
+    f = 3.0 * rng.standard_normal(16)
+    ut = rng.standard_normal(16)
+    u, it, _ = NL.newton(rp, col, v, c, f, tol=1e-14, lin_tol=1e-15)
+    A = to_dense(rp, col, v)
+    assert _relerr(u, _dense_newton(A, c, f)) <= 1e-12
+    assert it >= 3  # the cubic term matters
+    gv, gc, gf = NL.adjoint(rp, col, v, c, u, u - ut, lin_tol=1e-15)
+    loss = lambda A_, c_, f_: 0.5 * np.sum((_dense_newton(A_, c_, f_) - ut) ** 2)
+    eps = 1e-6
+    rows = np.repeat(np.arange(16), np.diff(rp))
+    for k in range(len(v)):
+        Ap, Am = A.copy(), A.copy()
+        Ap[rows[k], col[k]] += eps
+        Am[rows[k], col[k]] -= eps
+        fd = (loss(Ap, c, f) - loss(Am, c, f)) / (2 * eps)
+        assert abs(fd - gv[k]) <= 1e-6 * max(1.0, abs(gv[k])), ("v", k)
+    for i in range(16):
+        e = np.zeros(16)
+        e[i] = eps
+        fd = (loss(A, c + e, f) - loss(A, c - e, f)) / (2 * eps)
+        assert abs(fd - gc[i]) <= 1e-6 * max(1.0, abs(gc[i])), ("c", i)
+        fd = (loss(A, c, f + e) - loss(A, c, f - e)) / (2 * eps)
+        assert abs(fd - gf[i]) <= 1e-6 * max(1.0, abs(gf[i])), ("f", i)
+
+
 ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
             pin_p5_cg_step_bound, pin_p6_dense_solve, pin_p7_jacobi_diagonal,
             pin_p8_bicgstab_vs_cg, pin_p9_transpose, pin_p10_symmetric_adjoint,
             pin_p11_diag_gradient, pin_p12_finite_differences, pin_p13_dense_outer,
             pin_p14_homogeneity, pin_p15_batch_is_loop, pin_p16_bicgstab_half_step,
             pin_p17_matvec_vjp_dense, pin_p18_matvec_vjp_finite_differences,
+            pin_p19_nonlinear_reduces_to_linear, pin_p20_nonlinear_adjoint_finite_differences,
             pin_pattern_checks, pin_special_cases]
 
 
