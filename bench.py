@@ -78,12 +78,13 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--op", default="solve",
-                    choices=("solve", "matvec", "matvec_vjp", "inverse"),
+                    choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear"),
                     help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
                          "the differentiable product and its backward pass on the same "
                          "system, timed per call; inverse: kappa recovery through the "
                          "differentiable solve (64 x 64 grid, 8 forcings, 40 x steps Adam "
-                         "steps)")
+                         "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
+                         "on the workload's matrix")
     ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
                     help="column width the summarised run's products read")
     return ap.parse_args()
@@ -288,6 +289,49 @@ def summarize_trace(args):
 
 # ------------------------------------------------------------------ benchmark
 
+def bench_nonlinear(args, p):
+    """Differentiable Newton solve of A u + c u^3 = f (A the workload's
+    matrix, c = 10, f its right-hand side) and the backward pass of
+    L = 1/2 |u - x_t|^2 (one adjoint solve plus one vector-Jacobian product);
+    `steps` forward + backward passes timed."""
+    import torch
+    import differentiable_sparse_linear_amd as sla
+    from differentiable_sparse_linear_amd.nonlinear import Semilinear
+    dev = "cuda:0"
+    pat = sla.Pattern(torch.from_numpy(p.row_ptr).to(dev), torch.from_numpy(p.col).to(dev))
+    model = Semilinear(pat)
+    v = torch.from_numpy(p.values[0]).to(dev).requires_grad_(True)
+    c = torch.full((p.n,), 10.0, dtype=torch.float64, device=dev, requires_grad=True)
+    f = torch.from_numpy(p.b[0]).to(dev).requires_grad_(True)
+    xt = torch.from_numpy(p.x_t[0]).to(dev)
+    kw = dict(tol=1e-10, lin_tol=1e-10, lin_maxit=p.maxit, method=p.method, precond=p.precond)
+
+    def step():
+        u = model.solve(v, c, f, **kw)
+        loss = 0.5 * torch.sum((u - xt) ** 2)
+        loss.backward()
+        return u.grad_fn.newton_iters, u.grad_fn.norms
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        its, norms = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(json.dumps({
+        "metric": "differentiable Newton solves/sec (forward + nonlinear adjoint)",
+        "value": args.steps / wall, "unit": "solves/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": max(args.warmup, 1), "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic (the workload's matrix and b, c = 10)",
+        "config": {"workload": p.name + "_cubic", "n": p.n, "nnz": p.nnz,
+                   "solver": f"newton+{p.method}+{p.precond}", "newton_tol": 1e-10},
+        "newton_iters": its, "residual_norms": norms, "roofline": None,
+    }), flush=True)
+
+
 def bench_inverse(args):
     """Recover kappa = exp(theta) on a 64 x 64 grid from 8 observed solutions
     by Adam through the differentiable solve (forward and adjoint of 8
@@ -388,6 +432,8 @@ def main():
     if args.op == "inverse":
         return bench_inverse(args)
     p = load_problem(args)
+    if args.op == "nonlinear":
+        return bench_nonlinear(args, p)
     if args.op != "solve":
         return bench_product(args, p)
     dev = "cuda:0"
