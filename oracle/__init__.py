@@ -23,7 +23,10 @@ arrays.  What it follows, from the torch-sla explainer pages (gist.science,
   dL/dA_ij = (dL/dy)_i x_j on the stored pattern;
 * ``oracle.nonlinear``: Newton's method and the nonlinear adjoint for the
   semilinear model F(u) = A u + c u^3 - f (Methodology section 2, nonlinear
-  systems).
+  systems);
+* ``oracle.eigen``: dense eigenpairs of small symmetric systems and the
+  eigenvalue gradient v_i v_j on the pattern (Methodology section 2,
+  eigenvalue problems).
 
 Inputs of any float dtype are promoted to fp64 (an fp32 problem is solved in
 fp64 arithmetic on its fp32-rounded values); int32 row_ptr is widened to int64.

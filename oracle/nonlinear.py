@@ -26,7 +26,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import check_pattern, grad_on_pattern, solve, spmv, dot
+from . import adjoint as linear_adjoint
+from . import check_pattern, dot, grad_on_pattern, solve, spmv
 
 
 def residual(row_ptr, col, v, c, f, u):
@@ -43,8 +44,10 @@ def jacobian_values(row_ptr, col, v, c, u):
     return jv
 
 
-def newton(row_ptr, col, v, c, f, tol=1e-10, maxit=50, lin_tol=1e-12, lin_maxit=10000):
-    """Returns (u, newton iterations, residual norms ||F(u_k)||)."""
+def newton(row_ptr, col, v, c, f, tol=1e-10, maxit=50, lin_tol=1e-12, lin_maxit=10000,
+           method="cg", precond="jacobi"):
+    """Returns (u, newton iterations, residual norms ||F(u_k)||).  The
+    Jacobian solves use `method` (CG for symmetric, BiCGStab otherwise)."""
     n = np.asarray(row_ptr).shape[0] - 1
     u = np.zeros(n)
     F = residual(row_ptr, col, v, c, f, u)
@@ -52,7 +55,7 @@ def newton(row_ptr, col, v, c, f, tol=1e-10, maxit=50, lin_tol=1e-12, lin_maxit=
     it = 0
     while norms[-1] > tol * norms[0] and it < maxit:
         J = jacobian_values(row_ptr, col, v, c, u)
-        r = solve(row_ptr, col, J, F, "cg", "jacobi", lin_tol, lin_maxit)
+        r = solve(row_ptr, col, J, F, method, precond, lin_tol, lin_maxit)
         u = u - r.x[0]
         F = residual(row_ptr, col, v, c, f, u)
         norms.append(np.sqrt(dot(F, F)))
@@ -60,10 +63,17 @@ def newton(row_ptr, col, v, c, f, tol=1e-10, maxit=50, lin_tol=1e-12, lin_maxit=
     return u, it, norms
 
 
-def adjoint(row_ptr, col, v, c, u, grad_u, lin_tol=1e-12, lin_maxit=10000):
-    """(dL/dv [nnz], dL/dc [n], dL/df [n]) for dL/du = grad_u at the solution u."""
+def adjoint(row_ptr, col, v, c, u, grad_u, lin_tol=1e-12, lin_maxit=10000, method="cg",
+            precond="jacobi"):
+    """(dL/dv [nnz], dL/dc [n], dL/df [n]) for dL/du = grad_u at the solution
+    u.  lambda solves J^T lambda = grad_u: with CG J itself (symmetric), with
+    BiCGStab the oracle's transposed system."""
     J = jacobian_values(row_ptr, col, v, c, u)
-    lam = solve(row_ptr, col, J, grad_u, "cg", "jacobi", lin_tol, lin_maxit).x[0]
+    if method == "cg":
+        lam = solve(row_ptr, col, J, grad_u, method, precond, lin_tol, lin_maxit).x[0]
+    else:
+        lam = linear_adjoint(row_ptr, col, J, u, grad_u, method, precond, lin_tol,
+                             lin_maxit).grad_b[0]
     grad_v = grad_on_pattern(row_ptr, col, lam, u)[0]  # -lambda_i u_j
     grad_c = -lam * u ** 3
     return grad_v, grad_c, lam

@@ -500,6 +500,87 @@ def pin_p20_nonlinear_adjoint_finite_differences():
         assert abs(fd - gf[i]) <= 1e-6 * max(1.0, abs(gf[i])), ("f", i)
 
 
+def pin_p21_nonlinear_adjoint_nonsymmetric():
+    """The same central-difference check with a nonsymmetric A (upwind
+    convection-diffusion) and BiCGStab: the adjoint must use J^T."""
+    from oracle import nonlinear as NL
+    rng = np.random.default_rng(32)
+    p = W.config(4, size=4)
+    rp, col, v = p.row_ptr, p.col, p.values[0] / 19.0
+    c = rng.uniform(0.5, 2.0, 16)
+    f = 2.0 * rng.standard_normal(16)
+    ut = rng.standard_normal(16)
+    kw = dict(method="bicgstab", precond="none")
+    u, it, _ = NL.newton(rp, col, v, c, f, tol=1e-14, lin_tol=1e-15, **kw)
+    A = to_dense(rp, col, v)
+    assert _relerr(u, _dense_newton(A, c, f)) <= 1e-12 and it >= 3
+    gv, gc, gf = NL.adjoint(rp, col, v, c, u, u - ut, lin_tol=1e-15, **kw)
+    loss = lambda A_, c_, f_: 0.5 * np.sum((_dense_newton(A_, c_, f_) - ut) ** 2)
+    eps = 1e-6
+    rows = np.repeat(np.arange(16), np.diff(rp))
+    for k in range(len(v)):
+        Ap, Am = A.copy(), A.copy()
+        Ap[rows[k], col[k]] += eps
+        Am[rows[k], col[k]] -= eps
+        fd = (loss(Ap, c, f) - loss(Am, c, f)) / (2 * eps)
+        assert abs(fd - gv[k]) <= 1e-6 * max(1.0, abs(gv[k])), ("v", k)
+    for i in range(16):
+        e = np.zeros(16)
+        e[i] = eps
+        fd = (loss(A, c + e, f) - loss(A, c - e, f)) / (2 * eps)
+        assert abs(fd - gc[i]) <= 1e-6 * max(1.0, abs(gc[i])), ("c", i)
+        fd = (loss(A, c, f + e) - loss(A, c, f - e)) / (2 * eps)
+        assert abs(fd - gf[i]) <= 1e-6 * max(1.0, abs(gf[i])), ("f", i)
+
+
+# --------------------------------------------------------------------------
+# P22 -- eigenvalues: closed-form spectrum of the Dirichlet Laplacian
+# --------------------------------------------------------------------------
+def pin_p22_eigsh_laplacian_spectrum():
+    from oracle import eigen as E
+    N = 10
+    rp, col, val = W.laplacian_2d(N)
+    lam = np.sort([laplacian_eigval_2d(N, j, k) for j in range(1, N + 1)
+                   for k in range(1, N + 1)])
+    w, V = E.eigsh(rp, col, val[0], k=4)
+    assert np.allclose(w, lam[:4], rtol=1e-13, atol=0)
+    w, V = E.eigsh(rp, col, val[0], k=3, largest=True)
+    assert np.allclose(w, lam[::-1][:3], rtol=1e-13, atol=0)
+    # the lowest mode is the product of half sine waves
+    v = laplacian_eigvec_2d(N, 1, 1)
+    v = v / np.linalg.norm(v)
+    assert abs(abs(float(v @ E.eigsh(rp, col, val[0], k=1)[1][0])) - 1.0) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# P23 -- eigenvalue gradient against central differences (perturbing one
+# stored entry; eigenvalues of the perturbed matrix by numpy.linalg.eigvals)
+# --------------------------------------------------------------------------
+def pin_p23_eig_grad_finite_differences():
+    from oracle import eigen as E
+    rng = np.random.default_rng(33)
+    rp, col, val = W.varcoef_diffusion((4, 4), np.exp(0.5 * rng.standard_normal(16)))
+    v = val[0]
+    A = E.dense(rp, col, v)
+    rows = np.repeat(np.arange(16), np.diff(rp))
+    for largest in (False, True):
+        w, V = E.eigsh(rp, col, v, k=2, largest=largest)
+        g = np.array([1.0, -0.5])
+        gr = E.eig_grad(rp, col, V, g)
+        eps = 1e-7
+        for k in range(len(v)):
+            fd = 0.0
+            for q in range(2):
+                vals = []
+                for sgn in (1, -1):
+                    Ap = A.copy()
+                    Ap[rows[k], col[k]] += sgn * eps
+                    ev = np.linalg.eigvals(Ap).real
+                    vals.append(ev[np.argmin(np.abs(ev - w[q]))])
+                fd += g[q] * (vals[0] - vals[1]) / (2 * eps)
+            assert abs(fd - gr[k]) <= 1e-6 * max(1.0, abs(gr[k])), (largest, k)
+
+
 ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, pin_p3_ones, pin_p4_cg_krylov_termination,
             pin_p5_cg_step_bound, pin_p6_dense_solve, pin_p7_jacobi_diagonal,
             pin_p8_bicgstab_vs_cg, pin_p9_transpose, pin_p10_symmetric_adjoint,
@@ -507,6 +588,8 @@ ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, 
             pin_p14_homogeneity, pin_p15_batch_is_loop, pin_p16_bicgstab_half_step,
             pin_p17_matvec_vjp_dense, pin_p18_matvec_vjp_finite_differences,
             pin_p19_nonlinear_reduces_to_linear, pin_p20_nonlinear_adjoint_finite_differences,
+            pin_p21_nonlinear_adjoint_nonsymmetric, pin_p22_eigsh_laplacian_spectrum,
+            pin_p23_eig_grad_finite_differences,
             pin_pattern_checks, pin_special_cases]
 
 
