@@ -78,13 +78,14 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--op", default="solve",
-                    choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear"),
+                    choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"),
                     help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
                          "the differentiable product and its backward pass on the same "
                          "system, timed per call; inverse: kappa recovery through the "
                          "differentiable solve (64 x 64 grid, 8 forcings, 40 x steps Adam "
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
-                         "on the workload's matrix")
+                         "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
+                         "and the eigenvalue gradient")
     ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
                     help="column width the summarised run's products read")
     return ap.parse_args()
@@ -332,6 +333,42 @@ def bench_nonlinear(args, p):
     }), flush=True)
 
 
+def bench_eigsh(args, p):
+    """Largest eigenpair of the workload's matrix (Lanczos, 60-vector basis,
+    tol 1e-8) and the gradient of the eigenvalue on the pattern; `steps`
+    forward + backward passes timed."""
+    import torch
+    import differentiable_sparse_linear_amd as sla
+    dev = "cuda:0"
+    pat = sla.Pattern(torch.from_numpy(p.row_ptr).to(dev), torch.from_numpy(p.col).to(dev))
+    v = torch.from_numpy(p.values[0]).to(dev).requires_grad_(True)
+    opts = dict(k=1, largest=True, tol=1e-8, ncv=60, max_restarts=40)
+
+    def step():
+        v.grad = None
+        ev, X = sla.sparse_eigsh(pat, v, **opts)
+        ev.sum().backward()
+        return ev
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _, _, info = pat.eigsh(v.detach(), **opts)
+    print(json.dumps({
+        "metric": "largest eigenpair + eigenvalue gradient per second", "value": args.steps / wall,
+        "unit": "eigsh/s", "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, 1),
+        "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic (the workload's matrix)",
+        "config": {"workload": p.name, "n": p.n, "nnz": p.nnz, "k": 1, "ncv": 60, "tol": 1e-8},
+        "eigenvalue": float(ev.detach()[0, 0]), "restarts": int(info["restarts"][0]), "roofline": None,
+    }), flush=True)
+
+
 def bench_inverse(args):
     """Recover kappa = exp(theta) on a 64 x 64 grid from 8 observed solutions
     by Adam through the differentiable solve (forward and adjoint of 8
@@ -434,6 +471,8 @@ def main():
     p = load_problem(args)
     if args.op == "nonlinear":
         return bench_nonlinear(args, p)
+    if args.op == "eigsh":
+        return bench_eigsh(args, p)
     if args.op != "solve":
         return bench_product(args, p)
     dev = "cuda:0"

@@ -22,9 +22,9 @@ import torch
 
 __all__ = [
     "load", "SlaError", "Pattern", "PatternList", "SparseSolve", "sparse_solve",
-    "SparseMatvec", "sparse_matvec",
+    "SparseMatvec", "sparse_matvec", "SparseEigsh", "sparse_eigsh",
     "sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
-    "sla_solve_adjoint",
+    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint",
     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
     "SLA_OK", "SLA_NOT_CONVERGED", "SLA_BREAKDOWN", "SLA_ERR_ARG", "SLA_ERR_PATTERN",
     "SLA_ERR_ZERO_DIAG", "SLA_ERR_NO_MEMORY", "SLA_ERR_DEVICE", "EXPORTED_SYMBOLS",
@@ -43,12 +43,17 @@ SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
 SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
 
 EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
-                    "sla_solve_adjoint",
+                    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint",
                     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
                     "sla_last_error")
 
 _METHODS = {"cg": SLA_CG, "bicgstab": SLA_BICGSTAB}
 _PRECONDS = {"none": SLA_PRECOND_NONE, "jacobi": SLA_PRECOND_JACOBI}
+
+
+class _EigOpts(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("largest", ctypes.c_int32), ("ncv", ctypes.c_int32),
+                ("max_restarts", ctypes.c_int32), ("tol", ctypes.c_double)]
 
 
 class _Opts(ctypes.Structure):
@@ -90,6 +95,10 @@ def load(path: Optional[str] = None):
     lib.sla_solve_adjoint.restype = I32
     lib.sla_matvec_adjoint.argtypes = [P, P, P, P, P, P, P]
     lib.sla_matvec_adjoint.restype = I32
+    lib.sla_eigsh.argtypes = [P, P, P, P, ctypes.POINTER(_EigOpts), P, P]
+    lib.sla_eigsh.restype = I32
+    lib.sla_eigsh_adjoint.argtypes = [P, P, P, I32, P, P]
+    lib.sla_eigsh_adjoint.restype = I32
     lib.sla_export_pattern.argtypes = [P, P, P, P, P, P]
     lib.sla_export_pattern.restype = I32
     lib.sla_workspace_bytes.argtypes = [P]
@@ -165,6 +174,18 @@ def sla_matvec(h, values, x, y, transpose=False, stream=None) -> int:
 def sla_matvec_adjoint(h, values, x, grad_y, grad_x, grad_values, stream=None) -> int:
     return load().sla_matvec_adjoint(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(grad_y),
                                      _ptr(grad_x), _ptr(grad_values), _stream(stream))
+
+
+def sla_eigsh(h, values, evals: np.ndarray, evecs, opts: "_EigOpts", restarts: np.ndarray,
+              stream=None) -> int:
+    return load().sla_eigsh(ctypes.c_void_p(h), _ptr(values), evals.ctypes.data_as(ctypes.c_void_p),
+                            _ptr(evecs), ctypes.byref(opts),
+                            restarts.ctypes.data_as(ctypes.c_void_p), _stream(stream))
+
+
+def sla_eigsh_adjoint(h, evecs, grad_evals, k, grad_values, stream=None) -> int:
+    return load().sla_eigsh_adjoint(ctypes.c_void_p(h), _ptr(evecs), _ptr(grad_evals), int(k),
+                                    _ptr(grad_values), _stream(stream))
 
 
 def _make_opts(tol, maxit, method, precond, use_x0, graph_chunk, profile):
@@ -278,6 +299,33 @@ class Pattern:
         if st != SLA_OK:
             raise SlaError(st, "sla_matvec_adjoint")
         return gv, gx
+
+    def eigsh(self, values, k=1, largest=False, tol=1e-10, ncv=0, max_restarts=50, check=True,
+              stream=None):
+        """Extreme eigenpairs of each (symmetric) system: (evals [batch, k]
+        on the values' device, evecs [batch, k, n], info with the restarts
+        and the return status)."""
+        self._vals(values)
+        evals = np.zeros((self.batch, k), dtype=np.float64)
+        restarts = np.zeros(self.batch, dtype=np.int32)
+        evecs = torch.empty((self.batch, k, self.n), dtype=self.dtype, device=self.device)
+        opts = _EigOpts(int(k), 1 if largest else 0, int(ncv), int(max_restarts), float(tol))
+        st = sla_eigsh(self.handle, values, evals, evecs, opts, restarts, stream)
+        if check and st < 0:
+            raise SlaError(st, "sla_eigsh")
+        ev = torch.from_numpy(evals).to(device=self.device, dtype=self.dtype)
+        return ev, evecs, {"restarts": restarts, "return": st}
+
+    def eigsh_adjoint(self, evecs, grad_evals, stream=None):
+        """grad_values[s, k'] = sum_q grad_evals[s, q] v_q[row(k')] v_q[col(k')]."""
+        k = evecs.shape[-2]
+        _check(evecs, "evecs", self.dtype, self.batch * k * self.n)
+        _check(grad_evals, "grad_evals", self.dtype, self.batch * k)
+        gv = torch.empty(self.batch * self.nnz, dtype=self.dtype, device=self.device)
+        st = sla_eigsh_adjoint(self.handle, evecs, grad_evals, k, gv, stream)
+        if st != SLA_OK:
+            raise SlaError(st, "sla_eigsh_adjoint")
+        return gv
 
     def solve(self, values, b, tol=1e-10, maxit=1000, method="cg", precond="jacobi", x0=None,
               graph_chunk=0, profile=False, check=True, out=None, stream=None):
@@ -417,3 +465,28 @@ class PatternList:
         """Returns a list of (grad_values, grad_b, info)."""
         return [p.solve_adjoint(v, x, g, **opts)
                 for p, v, x, g in zip(self.items, values, xs, grads)]
+
+
+class SparseEigsh(torch.autograd.Function):
+    """Extreme eigenvalues of A(values) with the Hellmann-Feynman backward
+    (dlambda/dA_ij = v_i v_j on the pattern, simple eigenvalues); the
+    eigenvectors are returned but carry no gradient."""
+
+    @staticmethod
+    def forward(ctx, values, pattern: Pattern, opts: dict):
+        evals, evecs, info = pattern.eigsh(values.contiguous(), **opts)
+        ctx.pattern = pattern
+        ctx.save_for_backward(evecs)
+        ctx.mark_non_differentiable(evecs)
+        return evals, evecs
+
+    @staticmethod
+    def backward(ctx, grad_evals, grad_evecs):
+        (evecs,) = ctx.saved_tensors
+        gv = ctx.pattern.eigsh_adjoint(evecs, grad_evals.contiguous())
+        return gv, None, None
+
+
+def sparse_eigsh(pattern: Pattern, values: torch.Tensor, **opts):
+    """(evals, evecs) of A(values); evals are differentiable in values."""
+    return SparseEigsh.apply(values, pattern, opts)

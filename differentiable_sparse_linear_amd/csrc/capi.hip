@@ -14,6 +14,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <type_traits>
 #include <vector>
@@ -529,6 +530,171 @@ sla_status dispatch(const sla_ctx *h, F &&f) {
     return f((float *)nullptr, (int32_t *)nullptr);
 }
 
+
+// ------------------------------------------------------------- eigensolver
+
+// Eigen-decomposition of a small dense symmetric matrix by cyclic Jacobi
+// rotations (Golub & Van Loan, Matrix Computations, the symmetric Jacobi
+// method): each rotation zeroes one off-diagonal pair; sweeps repeat until
+// the off-diagonal part is negligible.  a [m][m] row-major is overwritten;
+// column q of Q is the eigenvector of evals[q].
+void jacobi_eig(std::vector<double> &a, int m, std::vector<double> &evals,
+                std::vector<double> &Q) {
+    Q.assign((size_t)m * m, 0.0);
+    for (int i = 0; i < m; ++i) Q[(size_t)i * m + i] = 1.0;
+    double total = 0.0;
+    for (double x : a) total += x * x;
+    for (int sweep = 0; sweep < 100; ++sweep) {
+        double off = 0.0;
+        for (int p = 0; p < m; ++p)
+            for (int q = p + 1; q < m; ++q) off += 2.0 * a[(size_t)p * m + q] * a[(size_t)p * m + q];
+        if (off <= 1e-32 * total || off == 0.0) break;
+        for (int p = 0; p < m; ++p)
+            for (int q = p + 1; q < m; ++q) {
+                const double apq = a[(size_t)p * m + q];
+                if (apq == 0.0) continue;
+                const double app = a[(size_t)p * m + p], aqq = a[(size_t)q * m + q];
+                const double theta = (aqq - app) / (2.0 * apq);
+                const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+                const double c = 1.0 / sqrt(t * t + 1.0), sn = t * c;
+                for (int r = 0; r < m; ++r) {  // columns p, q
+                    const double arp = a[(size_t)r * m + p], arq = a[(size_t)r * m + q];
+                    a[(size_t)r * m + p] = c * arp - sn * arq;
+                    a[(size_t)r * m + q] = sn * arp + c * arq;
+                }
+                for (int r = 0; r < m; ++r) {  // rows p, q
+                    const double apr = a[(size_t)p * m + r], aqr = a[(size_t)q * m + r];
+                    a[(size_t)p * m + r] = c * apr - sn * aqr;
+                    a[(size_t)q * m + r] = sn * apr + c * aqr;
+                }
+                for (int r = 0; r < m; ++r) {
+                    const double qrp = Q[(size_t)r * m + p], qrq = Q[(size_t)r * m + q];
+                    Q[(size_t)r * m + p] = c * qrp - sn * qrq;
+                    Q[(size_t)r * m + q] = sn * qrp + c * qrq;
+                }
+            }
+    }
+    evals.resize(m);
+    for (int i = 0; i < m; ++i) evals[i] = a[(size_t)i * m + i];
+}
+
+// A fixed pseudo-random start vector in [-1, 1) (the SplitMix64 output
+// function of the index), so every run starts from the same vector.
+inline double start_entry(uint64_t i) {
+    uint64_t z = i + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (double)(z >> 11) * (2.0 / 9007199254740992.0) - 1.0;
+}
+
+struct EigWork {
+    void *V = nullptr;       // [m + 1][n] basis
+    double *sc = nullptr;    // alpha [m], beta [m], coef [m + 1], S [m * k], norm [1]
+    double *part = nullptr;  // partial sums
+    ~EigWork() {
+        (void)hipFree(V);
+        (void)hipFree(sc);
+        (void)hipFree(part);
+    }
+};
+
+// Lanczos with full reorthogonalisation (two Gram-Schmidt passes) and
+// explicit restarts from the sum of the wanted Ritz vectors, for one system.
+template <typename T, typename IT>
+sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, double *evals,
+                     T *X, int32_t *restarts, EigWork &wk, hipStream_t s) {
+    const int64_t n = h->n;
+    const int k = o.k;
+    T *V = reinterpret_cast<T *>(wk.V);
+    double *alpha = wk.sc, *beta = alpha + m, *coef = beta + m, *S = coef + m + 1,
+           *nrm = S + (size_t)m * k;
+    const IT *rp = reinterpret_cast<const IT *>(h->rp);
+    // start vector
+    {
+        std::vector<T> v0((size_t)n);
+        for (int64_t i = 0; i < n; ++i) v0[(size_t)i] = (T)start_entry((uint64_t)i);
+        HIP_TRY(hipMemcpyAsync(V, v0.data(), sizeof(T) * n, hipMemcpyHostToDevice, s));
+        HIP_TRY(launch_eig_dots<T>(V, 1, V, n, wk.part, nrm, true, s));
+        HIP_TRY(launch_eig_scale<T>(V, V, nrm, 1e-200, n, s));
+        HIP_TRY(hipStreamSynchronize(s));  // v0 is a host buffer
+    }
+    std::vector<double> ha((size_t)m), hb((size_t)m), th, Q, Tm, Sh((size_t)m * k);
+    sla_status status = SLA_NOT_CONVERGED;
+    int r = 0;
+    for (;; ++r) {
+        for (int j = 0; j < m; ++j) {
+            T *vj = V + (size_t)j * n;
+            T *w = V + (size_t)(j + 1) * n;
+            HIP_TRY(launch_spmv<T, IT>(h->slots, rp, h->col, h->col16, val, 0, vj, w, n, 0, 1, s));
+            if (j > 0) HIP_TRY(launch_eig_update<T>(w, vj - n, 1, beta + j - 1, n, s));
+            HIP_TRY(launch_eig_dots<T>(vj, 1, w, n, wk.part, alpha + j, false, s));
+            HIP_TRY(launch_eig_update<T>(w, vj, 1, alpha + j, n, s));
+            for (int pass = 0; pass < 2; ++pass) {
+                HIP_TRY(launch_eig_dots<T>(V, j + 1, w, n, wk.part, coef, false, s));
+                HIP_TRY(launch_eig_update<T>(w, V, j + 1, coef, n, s));
+            }
+            HIP_TRY(launch_eig_dots<T>(w, 1, w, n, wk.part, beta + j, true, s));
+            HIP_TRY(launch_eig_scale<T>(w, w, beta + j, 1e-200, n, s));
+        }
+        HIP_TRY(hipMemcpyAsync(ha.data(), alpha, sizeof(double) * m, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipMemcpyAsync(hb.data(), beta, sizeof(double) * m, hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        // the basis stops at an invariant subspace (beta negligible)
+        double scale = 0.0;
+        for (int j = 0; j < m; ++j) scale = fmax(scale, fabs(ha[j]) + fabs(hb[j]));
+        int me = m;
+        for (int j = 0; j < m; ++j)
+            if (!(hb[j] > 1e-12 * scale)) {
+                me = j + 1;
+                break;
+            }
+        Tm.assign((size_t)me * me, 0.0);
+        for (int j = 0; j < me; ++j) {
+            Tm[(size_t)j * me + j] = ha[j];
+            if (j + 1 < me) Tm[(size_t)j * me + j + 1] = Tm[(size_t)(j + 1) * me + j] = hb[j];
+        }
+        jacobi_eig(Tm, me, th, Q);
+        std::vector<int> idx(me);
+        for (int j = 0; j < me; ++j) idx[j] = j;
+        std::sort(idx.begin(), idx.end(), [&](int a, int b) {
+            return o.largest ? th[a] > th[b] : th[a] < th[b];
+        });
+        const int kk = k < me ? k : me;
+        double tmax = 0.0;
+        for (int q = 0; q < kk; ++q) tmax = fmax(tmax, fabs(th[idx[q]]));
+        bool ok = kk == k;
+        const double bl = me < m ? 0.0 : hb[me - 1];
+        for (int q = 0; q < kk; ++q) {
+            evals[q] = th[idx[q]];
+            const double res = bl * fabs(Q[(size_t)(me - 1) * me + idx[q]]);
+            ok = ok && res <= o.tol * (tmax > 0.0 ? tmax : 1.0);
+        }
+        for (int q = kk; q < k; ++q) evals[q] = NAN;
+        std::fill(Sh.begin(), Sh.end(), 0.0);
+        for (int j = 0; j < me; ++j)
+            for (int q = 0; q < kk; ++q) Sh[(size_t)j * k + q] = Q[(size_t)j * me + idx[q]];
+        HIP_TRY(hipMemcpyAsync(S, Sh.data(), sizeof(double) * me * k, hipMemcpyHostToDevice, s));
+        HIP_TRY(launch_eig_combine<T>(X, V, me, k, S, n, s));
+        HIP_TRY(hipStreamSynchronize(s));  // Sh is reused
+        if (ok) {
+            status = SLA_OK;
+            break;
+        }
+        if (r >= o.max_restarts) break;
+        // restart from the sum of the wanted Ritz vectors
+        std::vector<double> ones((size_t)k, -1.0);
+        HIP_TRY(hipMemcpyAsync(coef, ones.data(), sizeof(double) * k, hipMemcpyHostToDevice, s));
+        HIP_TRY(hipMemsetAsync(V, 0, sizeof(T) * n, s));
+        HIP_TRY(launch_eig_update<T>(V, X, k, coef, n, s));  // V_0 = sum_q X_q
+        HIP_TRY(launch_eig_dots<T>(V, 1, V, n, wk.part, nrm, true, s));
+        HIP_TRY(launch_eig_scale<T>(V, V, nrm, 1e-200, n, s));
+        HIP_TRY(hipStreamSynchronize(s));  // `ones` is a host buffer
+    }
+    if (restarts) *restarts = r;
+    return status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -673,6 +839,57 @@ sla_status sla_solve_adjoint(sla_handle h, const void *d_values, const void *d_x
                                   reinterpret_cast<const T *>(d_grad_x),
                                   reinterpret_cast<T *>(d_grad_values), reinterpret_cast<T *>(d_grad_b),
                                   o, info, s);
+    });
+}
+
+sla_status sla_eigsh(sla_handle h, const void *d_values, double *h_evals, void *d_evecs,
+                     const sla_eig_opts *opts, int32_t *h_restarts, void *stream) {
+    if (!h || !d_values || !h_evals || !d_evecs || !opts) return SLA_ERR_ARG;
+    const sla_eig_opts o = *opts;
+    if (o.k < 1 || o.k > 8 || o.k > h->n || o.ncv < 0 || o.ncv > 512 || o.max_restarts < 0 ||
+        !(o.tol > 0.0))
+        return SLA_ERR_ARG;
+    int m = o.ncv ? o.ncv : (4 * o.k > 40 ? 4 * o.k : 40);
+    if (m > h->n) m = (int)h->n;
+    if (m < o.k) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        EigWork wk;
+        const int64_t nb = 256;
+        HIP_TRY(hipMalloc(&wk.V, sizeof(T) * (size_t)(m + 1) * h->n));
+        HIP_TRY(hipMalloc(&wk.sc, sizeof(double) * (size_t)(3 * m + 2 + m * o.k)));
+        HIP_TRY(hipMalloc(&wk.part, sizeof(double) * (size_t)nb * (m + 1)));
+        sla_status worst = SLA_OK;
+        for (int64_t sys = 0; sys < h->batch; ++sys) {
+            sla_status st = eigsh_one<T, IT>(
+                h, reinterpret_cast<const T *>(d_values) + sys * h->nnz, o, m,
+                h_evals + sys * o.k, reinterpret_cast<T *>(d_evecs) + sys * o.k * h->n,
+                h_restarts ? h_restarts + sys : nullptr, wk, s);
+            if (st < 0) return st;
+            if (st > worst) worst = st;
+        }
+        return worst;
+    });
+}
+
+sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_grad_evals,
+                             int32_t k, void *d_grad_values, void *stream) {
+    if (!h || !d_evecs || !d_grad_evals || !d_grad_values || k < 1 || k > 8) return SLA_ERR_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return dispatch(h, [&](auto t, auto it) -> sla_status {
+        using T = std::remove_pointer_t<decltype(t)>;
+        using IT = std::remove_pointer_t<decltype(it)>;
+        for (int64_t sys = 0; sys < h->batch; ++sys)
+            HIP_TRY((launch_eig_outer<T, IT>(
+                reinterpret_cast<const IT *>(h->rp), h->col,
+                reinterpret_cast<const T *>(d_evecs) + sys * k * h->n, k,
+                reinterpret_cast<const T *>(d_grad_evals) + sys * k,
+                reinterpret_cast<T *>(d_grad_values) + sys * h->nnz, h->n, s)));
+        return SLA_OK;
     });
 }
 

@@ -290,6 +290,22 @@ struct BlockCgParams {
 template <typename T, typename IT>
 hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipStream_t s);
 
+// Lanczos vector kernels and the eigenvalue gradient (kernels_eig.hip)
+template <typename T>
+hipError_t launch_eig_dots(const T *V, int m, const T *w, int64_t n, double *part, double *out,
+                           bool root, hipStream_t s);
+template <typename T>
+hipError_t launch_eig_update(T *w, const T *V, int m, const double *c, int64_t n, hipStream_t s);
+template <typename T>
+hipError_t launch_eig_scale(const T *w, T *out, const double *beta, double tiny, int64_t n,
+                            hipStream_t s);
+template <typename T>
+hipError_t launch_eig_combine(T *X, const T *V, int m, int k, const double *S, int64_t n,
+                              hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_eig_outer(const IT *rp, const int32_t *col, const T *X, int k, const T *g,
+                            T *grad, int64_t n, hipStream_t s);
+
 // pattern setup
 template <typename IT>
 hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,

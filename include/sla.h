@@ -173,6 +173,49 @@ sla_status sla_solve_adjoint(sla_handle h, const void *d_values,
                              void *stream);
 
 /*
+ * Options of sla_eigsh.
+ *   k             eigenpairs wanted, 1..8
+ *   largest       0: the k smallest (algebraic) eigenvalues, 1: the k largest
+ *   ncv           Lanczos basis per cycle, k..512 (0: max(4k, 40)), at most n
+ *   max_restarts  explicit restarts after the first cycle (>= 0)
+ *   tol           a Ritz pair (theta, x) is accepted when
+ *                 ||A x - theta x|| <= tol * max |theta| over the wanted ones
+ */
+typedef struct {
+    int32_t k;
+    int32_t largest;
+    int32_t ncv;
+    int32_t max_restarts;
+    double tol;
+} sla_eig_opts;
+
+/*
+ * sla_eigsh -- extreme eigenpairs of each system's symmetric A_s (the
+ * .eigsh of the unified API, torch-sla explainer, Methodology section 1), by
+ * Lanczos with full reorthogonalisation and explicit restarts.  Writes
+ * h_evals [batch][k] (host, ascending for the smallest, descending for the
+ * largest) and d_evecs [batch][k][n] (device, unit 2-norm, sign arbitrary);
+ * h_restarts [batch] (host, may be NULL) gets the restarts used.  The
+ * symmetry of A is the caller's promise.  Allocates its basis
+ * ((ncv + 1) * n values) for the call and synchronizes `stream`.  Returns
+ * SLA_NOT_CONVERGED when some system did not meet tol.
+ */
+sla_status sla_eigsh(sla_handle h, const void *d_values, double *h_evals, void *d_evecs,
+                     const sla_eig_opts *opts, int32_t *h_restarts, void *stream);
+
+/*
+ * sla_eigsh_adjoint -- gradient of sum_q g[s][q] lambda_q(A_s) with respect
+ * to the stored values, by the Hellmann-Feynman theorem for simple
+ * eigenvalues (torch-sla explainer, Methodology section 2, eigenvalue
+ * problems: dlambda/dA_ij = v_i v_j on the pattern):
+ *   d_grad_values[s][k'] = sum_q g[s][q] v_q[row(k')] v_q[col(k')].
+ * d_evecs [batch][k][n] as written by sla_eigsh, d_grad_evals [batch][k]
+ * (device, value dtype).  Asynchronous on `stream`.
+ */
+sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_grad_evals,
+                             int32_t k, void *d_grad_values, void *stream);
+
+/*
  * sla_export_pattern -- copy the derived pattern structures into caller
  * device buffers (any pointer may be NULL): d_diagpos [n] (row_ptr type),
  * and, if the transpose was built, d_row_ptr_t [n+1] (row_ptr type),
