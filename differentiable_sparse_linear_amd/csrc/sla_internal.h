@@ -112,6 +112,8 @@ struct TileRange {
     int64_t first, end, stride;
 };
 
+constexpr int64_t kRoundsFrom = 16;  // tiles per block from which tiles go in rounds
+
 __device__ __forceinline__ TileRange xcd_tiles(int64_t ntiles) {
     const int b = blockIdx.x;
     const int xcd = b % kNumXcd;
@@ -122,9 +124,20 @@ __device__ __forceinline__ TileRange xcd_tiles(int64_t ntiles) {
     int64_t hi = lo + chunk;
     if (hi > ntiles) hi = ntiles;
     TileRange tr;
-    tr.first = lo + local;
-    tr.end = hi;
-    tr.stride = per;
+    if (ntiles >= kRoundsFrom * (int64_t)gridDim.x) {
+        // large systems: rounds of gridDim.x consecutive tiles, XCD x taking
+        // the x-th run of `per` in each round, so the whole chip works on one
+        // window of rows at a time and neighbours one grid plane away (3D
+        // stencils) are still in the Infinity Cache when gathered
+        tr.first = (int64_t)xcd * per + local;
+        tr.end = ntiles;
+        tr.stride = gridDim.x;
+    } else {
+        // one contiguous slab per XCD: its L2 holds the slab's neighbours
+        tr.first = lo + local;
+        tr.end = hi;
+        tr.stride = per;
+    }
     return tr;
 }
 
