@@ -443,7 +443,9 @@ def bench_product(args, p):
         "vs_baseline": None, "dtype": "f64" if p.values.dtype == np.float64 else "f32",
         "data": "synthetic", "config": {"workload": p.name, "n": p.n, "nnz": p.nnz,
                                         "batch": p.batch},
-        "roofline": roofline,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "bytes_per_launch": model, "avg_launch_us": per * 1e6},
     }), flush=True)
 
 

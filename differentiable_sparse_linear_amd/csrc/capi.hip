@@ -453,7 +453,8 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     if (st == SLA_ERR_DEVICE) return st;
     for (int64_t s0 = 0; s0 < B; s0 += 65535) {
         const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
-        HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, gb + s0 * n,
+        HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, h->col16,
+                                   gb + s0 * n,
                                    x + s0 * n, gval + s0 * nnz, n, nnz, nb, true, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
@@ -795,7 +796,8 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
                     h->perm, v, h->nnz, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, h->n,
                     h->n, nb, s)));
             if (d_grad_values)
-                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, gy,
+                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col,
+                                            h->col16, gy,
                                             reinterpret_cast<const T *>(d_x) + s0 * h->n,
                                             reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz,
                                             h->n, h->nnz, nb, false, s)));

@@ -53,9 +53,10 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
 // pattern) or g[row(k)] * x[col[k]] (the product's).  Short tiles: each thread marks the
 // tile-local row of its row's entries in LDS, then the entries are written as
 // one coalesced run.  Tiles with long rows: one wavefront per row.
-template <typename T, typename IT, bool NEG>
+template <typename T, typename IT, bool NEG, bool C16>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
-                                                      const int32_t *__restrict__ col,
+                                                      const int32_t *__restrict__ col32,
+                                                      const int16_t *__restrict__ col16,
                                                       const T *__restrict__ lam,
                                                       const T *__restrict__ x, T *__restrict__ grad,
                                                       int64_t n, int64_t nnz) {
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
     __shared__ T slam[kTileRows];
     __shared__ uint16_t rid[kCap];
     const int sys = blockIdx.y;
+    const ColSrc<C16> col = col_src<C16>(col32, col16);
     lam += (int64_t)sys * n;
     x += (int64_t)sys * n;
     grad += (int64_t)sys * nnz;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
-                if (e < cnt) c[j] = col[base + e];
+                if (e < cnt) c[j] = col(base + e, row0);
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                 const T li = slam[r];
                 const IT hi = srp[r + 1];
                 for (IT k = srp[r] + lane; k < hi; k += 64) {
-                    const T g = li * x[col[k]];
+                    const T g = li * x[col(k, row0)];
                     grad[k] = NEG ? -g : g;
                 }
             }
@@ -176,13 +178,16 @@ hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const i
 }
 
 template <typename T, typename IT>
-hipError_t launch_grad(const IT *rp, const int32_t *col, const T *lam, const T *x, T *grad,
-                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s) {
+hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, const T *lam,
+                       const T *x, T *grad, int64_t n, int64_t nnz, int batch, bool neg,
+                       hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    if (neg)
-        grad_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
-    else
-        grad_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(rp, col, lam, x, grad, n, nnz);
+    SLA_DISPATCH_C16(col16 != nullptr, if (neg) {
+        grad_kernel<T, IT, true, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n, nnz);
+    } else {
+        grad_kernel<T, IT, false, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n,
+                                                             nnz);
+    });
     return hipGetLastError();
 }
 
@@ -219,9 +224,9 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
                                                 const int16_t *, const int32_t *, const T *,     \
                                                 int64_t, const T *, T *, int64_t, int64_t, int,  \
                                                 hipStream_t);                                    \
-    template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const T *,             \
-                                           const T *, T *, int64_t, int64_t, int, bool,          \
-                                           hipStream_t);  \
+    template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const int16_t *,       \
+                                           const T *, const T *, T *, int64_t, int64_t, int,     \
+                                           bool, hipStream_t);  \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
                                            hipStream_t);
 

@@ -62,3 +62,15 @@ def test_product_path_has_no_oracle_or_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text, f
+
+
+def test_bench_modes_parse_and_refuse_more_gpus():
+    """bench.py: every --op parses, and --gpus above 1 exits with a message
+    before touching a GPU (host check)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for op in ("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--op", op,
+                            "--gpus", "2"], capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2 and "one GPU" in r.stderr, (op, r.stderr)
