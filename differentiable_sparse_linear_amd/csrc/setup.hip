@@ -102,7 +102,13 @@ __global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ 
         const int32_t o = __shfl_xor(mi, off, 64);
         mi = o > mi ? o : mi;
     }
-    if ((threadIdx.x & 63) == 0) atomicMax(out, mi);  // one atomic per wavefront
+    __shared__ int32_t wm[kWaves];
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mi;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < kWaves; ++w) mi = wm[w] > mi ? wm[w] : mi;
+        atomicMax(out, mi > wm[0] ? mi : wm[0]);  // one atomic per block
+    }
 }
 
 // One thread per row: the offsets of the row's columns from its tile's first
@@ -153,7 +159,10 @@ template <typename IT>
 hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s) {
     hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
-    max_row_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, scratch);
+    // a few hundred blocks striding over the rows: the atomics on one word
+    // serialise, so their number is kept small
+    const unsigned nb = blocks_for(n) < 512 ? blocks_for(n) : 512;
+    max_row_kernel<IT><<<nb, kBlock, 0, s>>>(rp, n, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(out, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
