@@ -240,7 +240,8 @@ def _check_solve(p, g, r, a, systems=None):
 
 
 @pytest.mark.parametrize("case", ["cfg1", "cfg1_grid", "cfg2_20", "cfg2_31_ragged", "cfg3_small64",
-                                  "cfg3_small32", "cfg4_48", "cfg4_33_ragged"])
+                                  "cfg3_small32", "cfg4_48", "cfg4_33_ragged", "cfg2_24_fp32",
+                                  "cfg4_40_fp32"])
 def test_solve_and_adjoint_small(hip, case):
     banner(f"solve {case}")
     kw = {}
@@ -251,6 +252,13 @@ def test_solve_and_adjoint_small(hip, case):
         kw["profile"] = True   # forces the grid kernels on a small system
     elif case == "cfg2_20":
         p = W.config(2, size=20)
+    elif case == "cfg2_24_fp32":
+        # fp32 on the grid kernels (n = 13 824): tol 1e-5, fp64 dot products
+        p = W.config(2, size=24).astype(np.float32)
+        p.tol = 1e-5
+    elif case == "cfg4_40_fp32":
+        p = W.config(4, size=40).astype(np.float32)
+        p.tol = 1e-5
     elif case == "cfg2_31_ragged":
         p = W.config(2, size=31)
     elif case == "cfg3_small64":
