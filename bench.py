@@ -19,8 +19,9 @@ bytes per PCG iteration (SpMV plus the textbook recurrence's 11 vector passes)
     nnz*(sv + 4) + (n + 1)*sr + 2*n*sv + 11*n*sv
 (sv, sr: value and row-pointer widths; 9 passes without a preconditioner).
 ``kernel_bytes_per_launch`` is what the fused kernel itself must move: the
-matrix once (columns at 2 bytes when the handle keeps its compact
-tile-relative copy, else 4) plus, on average over the two iteration
+matrix once (column indices as the handle reads them: 4 bytes per entry,
+2 with its compact tile-relative copy, or 2 bytes per row with its
+diagonal masks) plus, on average over the two iteration
 parities, 9 vectors (even launches read u, w, s, p and write p, s, u, w; odd
 launches also read and write x).  For BiCGStab the two SpMV kernels are timed and priced at the
 SpMV's algorithmic bytes nnz*(sv + 4) + (n + 1)*sr + 2*n*sv.
@@ -86,16 +87,18 @@ def parse():
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
                          "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
                          "and the eigenvalue gradient")
-    ap.add_argument("--column-bytes", type=int, default=2, choices=(2, 4),
-                    help="column width the summarised run's products read")
+    ap.add_argument("--column-form", default="diagonal", choices=("wide", "tile16", "diagonal"),
+                    help="column form the summarised run's products read")
     return ap.parse_args()
 
 
-def dominant_kernel(method, precond, n, nnz, sv, sr, sc=4):
+def dominant_kernel(method, precond, n, nnz, sv, sr, ib=None):
     """(kernel name(s), algorithmic bytes per launch, the kernel's own bytes
-    per launch with column width sc, source files)."""
+    per launch with `ib` column-index bytes (default 4 per entry), source
+    files)."""
+    ib = 4 * nnz if ib is None else ib
     mat = nnz * (sv + 4) + (n + 1) * sr
-    own = nnz * (sv + sc) + (n + 1) * sr
+    own = nnz * sv + ib + (n + 1) * sr
     if method == "cg":
         passes = 11 if precond == "jacobi" else 9
         return ("cg_iter_kernel", mat + (2 + passes) * n * sv, own + 9 * n * sv,
@@ -104,20 +107,20 @@ def dominant_kernel(method, precond, n, nnz, sv, sr, sc=4):
             ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
 
 
-def column_bytes(p):
-    """2 when a handle on this pattern keeps the compact column copy, else 4
-    (decided by the library: a compact handle holds 2 bytes per entry more
-    than a wide one, per stored pattern)."""
+def form_bytes(form, p):
+    return {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[form]
+
+
+def index_bytes(p):
+    """(column form, bytes of column indices one product reads) for a handle
+    on this pattern, as the library chose it: int32 per entry, int16 per
+    entry, or one 16-bit diagonal mask per row."""
     import torch
     import differentiable_sparse_linear_amd as sla
-    rp = torch.from_numpy(p.row_ptr).cuda()
-    col = torch.from_numpy(p.col).cuda()
-    a = sla.Pattern(rp, col, compact_columns=True)
-    b = sla.Pattern(rp, col, compact_columns=False)
-    extra = a.workspace_bytes() - b.workspace_bytes()
-    a.close()
-    b.close()
-    return 2 if extra == 2 * p.nnz else 4
+    pat = sla.Pattern(torch.from_numpy(p.row_ptr).cuda(), torch.from_numpy(p.col).cuda())
+    mode = pat.column_mode()
+    pat.close()
+    return mode, {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[mode]
 
 
 def sources_sha(files):
@@ -190,7 +193,7 @@ def summarize_counters(args):
     p = load_problem(args)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
                                                 p.values.itemsize, p.row_ptr.itemsize,
-                                                args.column_bytes)
+                                                form_bytes(args.column_form, p))
     names = kernel.split("+")
     f_kib, f_n, f_all, f_copy = _counter_pass(args.summarize_counters[0], names)
     w_kib, w_n, w_all, w_copy = _counter_pass(args.summarize_counters[1], names)
@@ -239,7 +242,7 @@ def summarize_trace(args):
     p = load_problem(args)
     kernel, kbytes, own, _ = dominant_kernel(p.method, p.precond, p.n, p.nnz,
                                              p.values.itemsize, p.row_ptr.itemsize,
-                                             args.column_bytes)
+                                             form_bytes(args.column_form, p))
     names = kernel.split("+")
     stats = _rows(args.summarize_trace, "*kernel_stats.csv")
     trace = _rows(args.summarize_trace, "*kernel_trace.csv")
@@ -538,15 +541,15 @@ def main():
         k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
         k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
         k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
-        sc = column_bytes(p)
+        form, ib = index_bytes(p)
         kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
-                                                    p.values.itemsize, p.row_ptr.itemsize, sc)
+                                                    p.values.itemsize, p.row_ptr.itemsize, ib)
         achieved = kbytes / k_avg_s / 1e9
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": read_traffic(kernel, p.name, sources_sha(srcs)),
                     "bytes_per_launch": kbytes, "kernel_bytes_per_launch": own,
-                    "column_bytes": sc, "kernel_GBps": own / k_avg_s / 1e9,
+                    "column_form": form, "kernel_GBps": own / k_avg_s / 1e9,
                     "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n}
 
     result = {

@@ -43,7 +43,7 @@ SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
 SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
 
 EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
-                    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint",
+                    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint", "sla_column_mode",
                     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
                     "sla_last_error")
 
@@ -99,6 +99,8 @@ def load(path: Optional[str] = None):
     lib.sla_eigsh.restype = I32
     lib.sla_eigsh_adjoint.argtypes = [P, P, P, I32, P, P]
     lib.sla_eigsh_adjoint.restype = I32
+    lib.sla_column_mode.argtypes = [P, I32]
+    lib.sla_column_mode.restype = I32
     lib.sla_export_pattern.argtypes = [P, P, P, P, P, P]
     lib.sla_export_pattern.restype = I32
     lib.sla_workspace_bytes.argtypes = [P]
@@ -267,6 +269,14 @@ class Pattern:
 
     def workspace_bytes(self) -> int:
         return sla_workspace_bytes(self.handle)
+
+    def column_mode(self, transpose: bool = False) -> str:
+        """How the products read the columns: "wide" (int32), "tile16"
+        (2 bytes per entry) or "diagonal" (a 16-bit mask per row)."""
+        m = load().sla_column_mode(ctypes.c_void_p(self.handle), 1 if transpose else 0)
+        if m < 0:
+            raise SlaError(SLA_ERR_ARG, "sla_column_mode")
+        return ("wide", "tile16", "diagonal")[m]
 
     def _vals(self, values):
         _check(values, "values", self.dtype, self.batch * self.nnz)

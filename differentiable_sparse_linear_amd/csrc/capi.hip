@@ -44,6 +44,10 @@ struct sla_ctx {
     int dtype = SLA_F64, itype = SLA_I32;
     const void *rp = nullptr;
     const int32_t *col = nullptr;
+    ColArgs ca, ca_t;            // where the products read the columns of A, A^T
+    int32_t *dlt = nullptr;      // [2][kMaxDiags] diagonal offsets of A, A^T
+    uint16_t *msk = nullptr;     // per-row diagonal masks of A, or null
+    uint16_t *msk_t = nullptr;   // the same for A^T
     int16_t *col16 = nullptr;    // compact columns of A, or null
     void *diagpos = nullptr;
     bool has_t = false;
@@ -114,6 +118,9 @@ void release(sla_ctx *h) {
     if (h->cap) (void)hipStreamDestroy(h->cap);
     (void)hipFree(h->diagpos);
     (void)hipFree(h->col16);
+    (void)hipFree(h->dlt);
+    (void)hipFree(h->msk);
+    (void)hipFree(h->msk_t);
     (void)hipFree(h->rp_t);
     (void)hipFree(h->col_t);
     (void)hipFree(h->col16_t);
@@ -153,8 +160,7 @@ sla_status check_opts(const sla_solve_opts &o) {
 // The operator a solve iterates with: A itself or the mapped A^T.
 struct Operator {
     const void *rp;
-    const int32_t *col;
-    const int16_t *col16;
+    ColArgs cols;
     int slots;
 };
 
@@ -167,14 +173,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     const int64_t n = h->n;
     const bool cg = o.method == SLA_CG;
     const bool jac = cg && o.precond == SLA_PRECOND_JACOBI;
-    const bool c16 = op.col16 != nullptr;
+    const int cm = op.cols.mode;
     T *vec = reinterpret_cast<T *>(h->vec);
     IterArgs<T, IT> a;
     memset(&a, 0, sizeof(a));
     a.val = val;
     a.rp = reinterpret_cast<const IT *>(op.rp);
-    a.col = op.col;
-    a.col16 = op.col16;
+    a.cols = op.cols;
     a.x = x;
     a.b = b;
     a.r = vec + 0 * n;
@@ -205,21 +210,21 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
     // reads it always, so it is zeroed when there is no initial guess
     if (o.use_x0)
-        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.col, op.col16, val, 0, x, cg ? a.t : a.q, n,
-                                   0, 1, s));
+        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, 0, x, cg ? a.t : a.q, n, 0, 1,
+                                   s));
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n, s));
     if (cg)
-        HIP_TRY(launch_cg_init<T, IT>(op.slots, c16, jac, ad, n, s));
+        HIP_TRY(launch_cg_init<T, IT>(op.slots, cm, jac, ad, n, s));
     else
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) return launch_cg_iter<T, IT>(op.slots, c16, jac, ad, n, k & 1, ss);
-        if ((e = launch_bicg_pv<T, IT>(op.slots, c16, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_bicg_st<T, IT>(op.slots, c16, ad, n, ss)) != hipSuccess) return e;
+        if (cg) return launch_cg_iter<T, IT>(op.slots, cm, jac, ad, n, k & 1, ss);
+        if ((e = launch_bicg_pv<T, IT>(op.slots, cm, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_bicg_st<T, IT>(op.slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_update<T, IT>(ad, n, ss);
     };
 
@@ -239,13 +244,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(op.slots, c16, jac, ad, n, k & 1, s,
+                HIP_TRY(launch_cg_iter<T, IT>(op.slots, cm, jac, ad, n, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else {
-                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, c16, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_st<T, IT>(op.slots, c16, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_st<T, IT>(op.slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
@@ -347,7 +352,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
         BlockCgParams p;
         p.val = val;
         p.rp = op.rp;
-        p.col = op.col;
+        p.col = op.cols.col;
         p.diagpos = h->diagpos;
         p.x = x;
         p.b = b;
@@ -404,12 +409,12 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     oo.use_x0 = 0;
     sla_status st;
     if (o.method == SLA_CG) {
-        Operator op{h->rp, h->col, h->col16, h->slots};
+        Operator op{h->rp, h->ca, h->slots};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
         // A^T with values gathered through the transpose map, one system at
         // a time into the handle's buffer
-        Operator op{h->rp_t, h->col_t, h->col16_t, h->slots_t};
+        Operator op{h->rp_t, h->ca_t, h->slots_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
         std::vector<int32_t> it(B0), mv(B0), stc(B0);
@@ -472,6 +477,29 @@ hipError_t build_col16(sla_ctx *h, const IT *rp, const int32_t *col, int16_t **o
     return setup_col16<IT>(rp, col, h->n, *out, h->flag, &fits, s);
 }
 
+// Diagonal masks for the pattern (rp, col) when its entries lie on at most
+// kMaxDiags diagonals and no row holds more than 8 of them; fills `ca`.
+template <typename IT>
+hipError_t build_diag(sla_ctx *h, const IT *rp, const int32_t *col, int32_t max_len,
+                      int32_t *dlt_dev, uint16_t **msk, ColArgs &ca, hipStream_t s) {
+    if (max_len > 8) return hipSuccess;
+    int32_t dlt[kMaxDiags], nd = 0;
+    hipError_t e = setup_diag<IT>(rp, col, h->n, dlt_dev, h->flag, dlt, &nd, s);
+    if (e != hipSuccess || nd == 0) return e;
+    if ((e = hipMemcpyAsync(dlt_dev, dlt, sizeof(dlt), hipMemcpyHostToDevice, s)) != hipSuccess)
+        return e;
+    if ((e = dmalloc(h, msk, sizeof(uint16_t) * h->n)) != hipSuccess) return e;
+    if ((e = setup_diag_masks<IT>(rp, col, h->n, dlt_dev, nd, *msk, s)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;  // dlt is a host buffer
+    int nneg = 0;
+    while (nneg < nd && dlt[nneg] < 0) ++nneg;
+    ca.msk = *msk;
+    ca.dlt = dlt_dev;
+    ca.nneg = nneg;
+    ca.mode = kColDiag;
+    return hipSuccess;
+}
+
 template <typename T, typename IT>
 sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     const bool build_t = (flags & SLA_CREATE_TRANSPOSE) != 0;
@@ -500,11 +528,30 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
         h->has_t = true;
         HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
         h->slots_t = slots_for(maxlen);
-        if (compact)
-            HIP_TRY(build_col16<IT>(h, reinterpret_cast<const IT *>(h->rp_t), h->col_t,
-                                    &h->col16_t, s));
+        h->ca_t.col = h->col_t;
+        if (compact) {
+            const IT *rpt = reinterpret_cast<const IT *>(h->rp_t);
+            HIP_TRY(build_col16<IT>(h, rpt, h->col_t, &h->col16_t, s));
+            h->ca_t.col16 = h->col16_t;
+            if (h->col16_t) h->ca_t.mode = kColTile16;
+            HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));
+            HIP_TRY(build_diag<IT>(h, rpt, h->col_t, maxlen, h->dlt + kMaxDiags, &h->msk_t,
+                                   h->ca_t, s));
+        }
     }
-    if (compact) HIP_TRY(build_col16<IT>(h, rp, h->col, &h->col16, s));
+    h->ca.col = h->col;
+    if (compact) {
+        HIP_TRY(build_col16<IT>(h, rp, h->col, &h->col16, s));
+        h->ca.col16 = h->col16;
+        if (h->col16) h->ca.mode = kColTile16;
+        if (!h->dlt) HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));
+        HIP_TRY(build_diag<IT>(h, rp, h->col, h->max_len, h->dlt, &h->msk, h->ca, s));
+        if (h->ca.mode != kColDiag && h->ca_t.mode != kColDiag) {  // the table went unused
+            HIP_TRY(hipFree(h->dlt));
+            h->dlt = nullptr;
+            h->ws_bytes -= (int64_t)sizeof(int32_t) * 2 * kMaxDiags;
+        }
+    }
     HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
     HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
     HIP_TRY(dmalloc(h, &h->part, sizeof(double) * kMaxRed * kMaxGrid));
@@ -627,7 +674,7 @@ sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, dou
         for (int j = 0; j < m; ++j) {
             T *vj = V + (size_t)j * n;
             T *w = V + (size_t)(j + 1) * n;
-            HIP_TRY(launch_spmv<T, IT>(h->slots, rp, h->col, h->col16, val, 0, vj, w, n, 0, 1, s));
+            HIP_TRY(launch_spmv<T, IT>(h->slots, rp, h->ca, val, 0, vj, w, n, 0, 1, s));
             if (j > 0) HIP_TRY(launch_eig_update<T>(w, vj - n, 1, beta + j - 1, n, s));
             HIP_TRY(launch_eig_dots<T>(vj, 1, w, n, wk.part, alpha + j, false, s));
             HIP_TRY(launch_eig_update<T>(w, vj, 1, alpha + j, n, s));
@@ -765,11 +812,11 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
             if (transpose)
                 HIP_TRY((launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t),
-                                                 h->col_t, h->col16_t, h->perm, v, h->nnz, x, y,
+                                                 h->ca_t, h->perm, v, h->nnz, x, y,
                                                  h->n, h->n, nb, s)));
             else
-                HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->col,
-                                            h->col16, v, h->nnz, x, y, h->n, h->n, nb, s)));
+                HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->ca,
+                                            v, h->nnz, x, y, h->n, h->n, nb, s)));
         }
         return SLA_OK;
     });
@@ -792,7 +839,7 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
             const T *gy = reinterpret_cast<const T *>(d_grad_y) + s0 * h->n;
             if (d_grad_x)
                 HIP_TRY((launch_spmv_perm<T, IT>(
-                    h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->col_t, h->col16_t,
+                    h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->ca_t,
                     h->perm, v, h->nnz, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, h->n,
                     h->n, nb, s)));
             if (d_grad_values)
@@ -816,7 +863,7 @@ sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *
     return dispatch(h, [&](auto t, auto it) -> sla_status {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        Operator op{h->rp, h->col, h->col16, h->slots};
+        Operator op{h->rp, h->ca, h->slots};
         return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
                                 reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
                                 info, s);
@@ -893,6 +940,11 @@ sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_gr
                 reinterpret_cast<T *>(d_grad_values) + sys * h->nnz, h->n, s)));
         return SLA_OK;
     });
+}
+
+int32_t sla_column_mode(sla_handle h, int32_t transpose) {
+    if (!h || (transpose && !h->has_t)) return -1;
+    return transpose ? h->ca_t.mode : h->ca.mode;
 }
 
 sla_status sla_export_pattern(sla_handle h, void *d_diagpos, void *d_row_ptr_t, void *d_col_t,

@@ -71,7 +71,7 @@ struct CgOwn {
 // guess), u_0 = M^-1 r_0, w_0 = A u_0; stores u_0 and w^_0 = M^-1 w_0 in the
 // parity-0 buffers and zeroes x without an initial guess; partials gamma_0,
 // delta_0, ||r_0||^2 and ||b||^2 (parity-0 slots).
-template <typename T, typename IT, bool JAC, int SLOTS, bool C16>
+template <typename T, typename IT, bool JAC, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
     const int64_t n = A->n;
     const gptr<const T> b = glb(A->b);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
     auto load = [&](int64_t c) { return G3<T>{b[c], ax0[c], JAC ? dinv[c] : T(1)}; };
     auto u_of = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
     spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<C16>(A->col, A->col16), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
         load, u_of, load,
         [&](int64_t i, T acc, const G3<T> &o, T) {
             const T ri = o.a - o.b;
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 #ifndef SLA_CG_WAVES
 #define SLA_CG_WAVES 5
 #endif
-template <typename T, typename IT, bool JAC, int SLOTS, int PH, bool C16>
+template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
@@ -210,7 +210,7 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<C16>(A->col, A->col16), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
         [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; }, u_of,
         [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
         [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
@@ -508,25 +508,25 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     }
 
 template <typename T, typename IT>
-hipError_t launch_cg_init(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s) {
     const int grid = grid_for_tiles(tiles_of(n));
     if (jac) {
-        SLA_DISPATCH_C16(c16, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, true, kS, kC>
+        SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, true, kS, kC>
                                                  <<<grid, kBlock, 0, s>>>(a)));
     } else {
-        SLA_DISPATCH_C16(c16, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, false, kS, kC>
+        SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, false, kS, kC>
                                                  <<<grid, kBlock, 0, s>>>(a)));
     }
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           int ph, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
 #define SLA_CG_ITER(J, P)                                                                      \
-    SLA_DISPATCH_C16(c16, SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(                        \
+    SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(                        \
                                                         cg_iter_kernel<T, IT, J, kS, P, kC>,   \
                                                         grid, dim3(kBlock), 0, s, ev, a)))
     if (jac) {
@@ -602,9 +602,9 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
                                           hipStream_t);
 
 #define SLA_INST(T, IT)                                                                         \
-    template hipError_t launch_cg_init<T, IT>(int, bool, bool, const IterArgs<T, IT> *,       \
+    template hipError_t launch_cg_init<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
                                               int64_t, hipStream_t);                            \
-    template hipError_t launch_cg_iter<T, IT>(int, bool, bool, const IterArgs<T, IT> *,       \
+    template hipError_t launch_cg_iter<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
                                               int64_t, int, hipStream_t, const hipEvent_t *);   \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
 

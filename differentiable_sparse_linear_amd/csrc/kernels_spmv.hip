@@ -12,10 +12,8 @@
 
 namespace sla {
 
-template <typename T, typename IT, int SLOTS, bool C16>
-__global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
-                                                      const int32_t *__restrict__ col,
-                                                      const int16_t *__restrict__ col16,
+template <typename T, typename IT, int SLOTS, int CM>
+__global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride) {
@@ -25,18 +23,18 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
     const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(rp), col_src<C16>(col, col16), sm, [&](IT k) { return v[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(rp), col_src<CM>(ca), sm, [&](IT k) { return v[k]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
         [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
 
 // y = A^T x through the transpose map: rp/col describe A^T and the value of
 // A^T entry kt is val[perm[kt]].
-template <typename T, typename IT, int SLOTS, bool C16>
+template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
-    const IT *__restrict__ rp, const int32_t *__restrict__ col, const int16_t *__restrict__ col16,
-    const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
-    const T *__restrict__ x, T *__restrict__ y, int64_t n, int64_t vec_stride) {
+    const IT *__restrict__ rp, ColArgs ca, const int32_t *__restrict__ perm,
+    const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
+    int64_t n, int64_t vec_stride) {
     __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
@@ -44,7 +42,7 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     const gptr<const int32_t> pm = glb(perm);
     spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(rp), col_src<C16>(col, col16), sm, [&](IT k) { return v[pm[k]]; },
+        xcd_tiles(tiles_of(n)), n, glb(rp), col_src<CM>(ca), sm, [&](IT k) { return v[pm[k]]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
         [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
@@ -53,7 +51,7 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
 // pattern) or g[row(k)] * x[col[k]] (the product's).  Short tiles: each thread marks the
 // tile-local row of its row's entries in LDS, then the entries are written as
 // one coalesced run.  Tiles with long rows: one wavefront per row.
-template <typename T, typename IT, bool NEG, bool C16>
+template <typename T, typename IT, bool NEG, int CM>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                                                       const int32_t *__restrict__ col32,
                                                       const int16_t *__restrict__ col16,
@@ -64,7 +62,10 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
     __shared__ T slam[kTileRows];
     __shared__ uint16_t rid[kCap];
     const int sys = blockIdx.y;
-    const ColSrc<C16> col = col_src<C16>(col32, col16);
+    ColArgs ca;
+    ca.col = col32;
+    ca.col16 = col16;
+    const ColSrc<CM> col = col_src<CM>(ca);
     lam += (int64_t)sys * n;
     x += (int64_t)sys * n;
     grad += (int64_t)sys * nnz;
@@ -153,27 +154,25 @@ __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T
 // ------------------------------------------------------------------ launchers
 
 template <typename T, typename IT>
-hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
-                       const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                       int64_t vec_stride, int batch, hipStream_t s) {
+hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
+                       int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
+                       int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_C16(col16 != nullptr,
-                     SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC><<<grid, kBlock, 0, s>>>(
-                                                   rp, col, col16, val, val_stride, x, y, n,
-                                                   vec_stride)));
+    SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC>
+                                                <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride,
+                                                                         x, y, n, vec_stride)));
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
-                            const int32_t *perm, const T *val, int64_t val_stride, const T *x,
-                            T *y, int64_t n, int64_t vec_stride, int batch, hipStream_t s) {
+hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
+                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
+                            int64_t vec_stride, int batch, hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_C16(col16 != nullptr,
-                     SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
-                                        <<<grid, kBlock, 0, s>>>(rp, col, col16, perm, val,
-                                                                 val_stride, x, y, n,
-                                                                 vec_stride)));
+    SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
+                                                <<<grid, kBlock, 0, s>>>(rp, ca, perm, val,
+                                                                         val_stride, x, y, n,
+                                                                         vec_stride)));
     return hipGetLastError();
 }
 
@@ -182,7 +181,7 @@ hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, c
                        const T *x, T *grad, int64_t n, int64_t nnz, int batch, bool neg,
                        hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_C16(col16 != nullptr, if (neg) {
+    SLA_DISPATCH_TILE16(col16 != nullptr, if (neg) {
         grad_kernel<T, IT, true, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n, nnz);
     } else {
         grad_kernel<T, IT, false, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n,
@@ -217,13 +216,11 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
 }
 
 #define SLA_INST(T, IT)                                                                         \
-    template hipError_t launch_spmv<T, IT>(int, const IT *, const int32_t *, const int16_t *,   \
-                                           const T *, int64_t, const T *, T *, int64_t, int64_t, \
-                                           int, hipStream_t);                                    \
-    template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const int32_t *,               \
-                                                const int16_t *, const int32_t *, const T *,     \
-                                                int64_t, const T *, T *, int64_t, int64_t, int,  \
-                                                hipStream_t);                                    \
+    template hipError_t launch_spmv<T, IT>(int, const IT *, const ColArgs &, const T *, int64_t, \
+                                           const T *, T *, int64_t, int64_t, int, hipStream_t);  \
+    template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
+                                                const int32_t *, const T *, int64_t, const T *,  \
+                                                T *, int64_t, int64_t, int, hipStream_t);        \
     template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const int16_t *,       \
                                            const T *, const T *, T *, int64_t, int64_t, int,     \
                                            bool, hipStream_t);  \

@@ -131,6 +131,61 @@ __global__ __launch_bounds__(kBlock) void col16_kernel(const IT *__restrict__ rp
     if (__any(b) && (threadIdx.x & 63) == 0) atomicOr(bad, 1);
 }
 
+// Distinct diagonals: each block gathers the offsets (col - row) of its
+// rows into a small set in LDS, then merges it into the global set `table`
+// [kMaxDiags] (kEmpty = free slot).  Insertion walks the slots in order and
+// claims the first free one with compare-and-swap, so no value is stored
+// twice; a value finding every slot taken by others sets *over.
+constexpr int32_t kEmpty = INT32_MIN;
+
+__device__ __forceinline__ bool set_insert(int32_t *tab, int32_t v) {
+    for (int q = 0; q < kMaxDiags; ++q) {
+        const int32_t old = atomicCAS(&tab[q], kEmpty, v);
+        if (old == kEmpty || old == v) return true;
+    }
+    return false;
+}
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void diag_collect_kernel(const IT *__restrict__ rp,
+                                                              const int32_t *__restrict__ col,
+                                                              int64_t n, int32_t *table,
+                                                              int32_t *over) {
+    __shared__ int32_t loc[kMaxDiags];
+    __shared__ int32_t bad;
+    if (threadIdx.x < kMaxDiags) loc[threadIdx.x] = kEmpty;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        for (IT k = rp[i]; k < rp[i + 1]; ++k)
+            if (!set_insert(loc, (int32_t)((int64_t)col[k] - i))) bad = 1;
+    __syncthreads();
+    if (threadIdx.x < kMaxDiags && loc[threadIdx.x] != kEmpty)
+        if (!set_insert(table, loc[threadIdx.x])) atomicOr(over, 1);
+    if (threadIdx.x == 0 && bad) atomicOr(over, 1);
+}
+
+// msk[i] = bit q set for every stored entry of row i on diagonal dlt[q].
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void diag_mask_kernel(const IT *__restrict__ rp,
+                                                           const int32_t *__restrict__ col,
+                                                           int64_t n,
+                                                           const int32_t *__restrict__ dlt,
+                                                           int32_t ndiag,
+                                                           uint16_t *__restrict__ msk) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        uint32_t m = 0;
+        for (IT k = rp[i]; k < rp[i + 1]; ++k) {
+            const int64_t d = (int64_t)col[k] - i;
+            for (int q = 0; q < ndiag; ++q)
+                if (dlt[q] == d) m |= 1u << q;
+        }
+        msk[i] = (uint16_t)m;
+    }
+}
+
 static unsigned blocks_for(int64_t m) {
     int64_t b = (m + kBlock - 1) / kBlock;
     if (b > 65536) b = 65536;
@@ -167,6 +222,47 @@ hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out
     if ((e = hipMemcpyAsync(out, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
     return hipStreamSynchronize(s);
+}
+
+template <typename IT>
+hipError_t setup_diag(const IT *rp, const int32_t *col, int64_t n, int32_t *dev_table,
+                      int32_t *scratch, int32_t *dlt, int32_t *ndiag, hipStream_t s) {
+    *ndiag = 0;
+    int32_t init[kMaxDiags];
+    for (int q = 0; q < kMaxDiags; ++q) init[q] = kEmpty;
+    hipError_t e = hipMemcpyAsync(dev_table, init, sizeof(init), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return e;
+    if ((e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s)) != hipSuccess) return e;
+    const unsigned nb = blocks_for(n) < 1024 ? blocks_for(n) : 1024;
+    diag_collect_kernel<IT><<<nb, kBlock, 0, s>>>(rp, col, n, dev_table, scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int32_t tab[kMaxDiags], over = 1;
+    if ((e = hipMemcpyAsync(tab, dev_table, sizeof(tab), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return e;
+    if ((e = hipMemcpyAsync(&over, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) !=
+        hipSuccess)
+        return e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;  // init, tab: host buffers
+    if (over) return hipSuccess;
+    int m = 0;
+    for (int q = 0; q < kMaxDiags; ++q)
+        if (tab[q] != kEmpty) dlt[m++] = tab[q];
+    for (int a = 1; a < m; ++a)  // ascending
+        for (int b = a; b > 0 && dlt[b - 1] > dlt[b]; --b) {
+            const int32_t t = dlt[b];
+            dlt[b] = dlt[b - 1];
+            dlt[b - 1] = t;
+        }
+    for (int q = m; q < kMaxDiags; ++q) dlt[q] = 0;
+    *ndiag = m;
+    return hipSuccess;
+}
+
+template <typename IT>
+hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const int32_t *dlt_dev,
+                            int32_t ndiag, uint16_t *msk, hipStream_t s) {
+    diag_mask_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, dlt_dev, ndiag, msk);
+    return hipGetLastError();
 }
 
 template <typename IT>
@@ -224,6 +320,14 @@ template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, in
                                             int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
                                             int64_t *, int32_t *, hipStream_t);
+template hipError_t setup_diag<int32_t>(const int32_t *, const int32_t *, int64_t, int32_t *,
+                                        int32_t *, int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_diag<int64_t>(const int64_t *, const int32_t *, int64_t, int32_t *,
+                                        int32_t *, int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_diag_masks<int32_t>(const int32_t *, const int32_t *, int64_t,
+                                              const int32_t *, int32_t, uint16_t *, hipStream_t);
+template hipError_t setup_diag_masks<int64_t>(const int64_t *, const int32_t *, int64_t,
+                                              const int32_t *, int32_t, uint16_t *, hipStream_t);
 template hipError_t setup_col16<int32_t>(const int32_t *, const int32_t *, int64_t, int16_t *,
                                          int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_col16<int64_t>(const int64_t *, const int32_t *, int64_t, int16_t *,

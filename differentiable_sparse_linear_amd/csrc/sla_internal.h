@@ -71,12 +71,26 @@ enum : int {
 // Device-resident arguments of the iteration kernels.  Kernels take a pointer
 // to this block, so a captured HIP graph stays valid across calls while the
 // host rewrites the pointers before each solve.
+// Column modes of a pattern (how the SpMV-shaped kernels find the columns):
+// the caller's int32 array, an int16 tile-relative copy, or per-row masks
+// over at most kMaxDiags diagonals.
+constexpr int kColWide = 0, kColTile16 = 1, kColDiag = 2;
+constexpr int kMaxDiags = 16;
+
+struct ColArgs {
+    const int32_t *col = nullptr;    // int32 columns (always present)
+    const int16_t *col16 = nullptr;  // tile-relative int16 columns, or null
+    const uint16_t *msk = nullptr;   // per-row diagonal masks, or null
+    const int32_t *dlt = nullptr;    // [kMaxDiags] diagonal offsets, ascending (device)
+    int32_t nneg = 0;                // diagonals below the main one
+    int32_t mode = kColWide;
+};
+
 template <typename T, typename IT>
 struct IterArgs {
     const T *val;
     const IT *rp;
-    const int32_t *col;
-    const int16_t *col16;  // compact columns (tile-relative), or null
+    ColArgs cols;
     T *x;
     const T *b;
     const T *dinv;
@@ -241,13 +255,13 @@ inline void launch_maybe_timed(void (*k)(KArgs...), dim3 grid, dim3 block, uint3
 // `col16` (or `c16` for the kernels that read the argument block) selects the
 // compact tile-relative columns when the handle has them.
 template <typename T, typename IT>
-hipError_t launch_spmv(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
-                       const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                       int64_t vec_stride, int batch, hipStream_t s);
+hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
+                       int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
+                       int batch, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_spmv_perm(int slots, const IT *rp, const int32_t *col, const int16_t *col16,
-                            const int32_t *perm, const T *val, int64_t val_stride, const T *x,
-                            T *y, int64_t n, int64_t vec_stride, int batch, hipStream_t s);
+hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
+                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
+                            int64_t vec_stride, int batch, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, const T *lam,
                        const T *x, T *grad, int64_t n, int64_t nnz, int batch, bool neg,
@@ -261,20 +275,20 @@ hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, Solv
 // CG (grid path, one system): init, then one launch per iteration with the
 // iteration's parity
 template <typename T, typename IT>
-hipError_t launch_cg_init(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, bool c16, bool jac, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           int ph, hipStream_t s, const hipEvent_t *ev = nullptr);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int slots, bool c16, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_pv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, bool c16, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
 hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
@@ -326,6 +340,16 @@ hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t n
                           int32_t *flag, hipStream_t s);
 template <typename IT>
 hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s);
+// Diagonal masks: the distinct column offsets (col - row) of the pattern
+// when there are at most kMaxDiags of them (*ndiag = their number, else 0;
+// dlt ascending, host array), then msk[i] = the set of diagonals row i
+// stores (synchronizes `s`).
+template <typename IT>
+hipError_t setup_diag(const IT *rp, const int32_t *col, int64_t n, int32_t *dev_table,
+                      int32_t *scratch, int32_t *dlt, int32_t *ndiag, hipStream_t s);
+template <typename IT>
+hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const int32_t *dlt_dev,
+                            int32_t ndiag, uint16_t *msk, hipStream_t s);
 // Compact columns: out[k] = col[k] - (first row of row(k)'s tile) as int16.
 // With out == nullptr only checks; *fits = 1 when every entry fits
 // (synchronizes `s`).

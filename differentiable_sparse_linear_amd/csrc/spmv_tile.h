@@ -116,25 +116,40 @@ constexpr int round_for(int slots, int round) {
     return r;
 }
 
-// Where the kernels read column indices.  C16 = false: the caller's int32
-// array.  C16 = true: a compact copy built at set-up when every entry fits,
-// the int16 offset of the column from the first row of the entry's tile
-// (col = tile row0 + offset), which halves the index bytes of stencil-like
-// patterns.
-template <bool C16>
+// Where the kernels read column indices (CM, the column mode):
+//   kColWide   the caller's int32 array;
+//   kColTile16 a compact copy built at set-up when every entry fits, the
+//              int16 offset of the column from the first row of the entry's
+//              tile (col = tile row0 + offset): 2 bytes per entry;
+//   kColDiag   for patterns whose entries lie on at most 16 diagonals (grid
+//              stencils) and whose rows hold at most 8 entries: one 16-bit
+//              mask per row says which diagonals the row stores; the column
+//              of diagonal q is row + dlt[q] (dlt ascending, so the row's
+//              columns ascend with q): 2 bytes per row, no per-entry index.
+template <int CM>
 struct ColSrc {
     gptr<const int32_t> c32;
     gptr<const int16_t> c16;
+    gptr<const uint16_t> msk;
+    gptr<const int32_t> dlt;
+    int32_t nneg;  // diagonals below the main one (dlt[q] < 0 for q < nneg)
+    // column of stored entry k in the tile starting at row0 (per-entry modes)
     __device__ __forceinline__ int32_t operator()(int64_t k, int64_t row0) const {
-        if constexpr (C16)
+        if constexpr (CM == kColTile16)
             return (int32_t)row0 + (int32_t)c16[k];
         else
             return c32[k];
     }
 };
-template <bool C16>
-__device__ __forceinline__ ColSrc<C16> col_src(const int32_t *c32, const int16_t *c16) {
-    return ColSrc<C16>{glb(c32), glb(c16)};
+template <int CM>
+__device__ __forceinline__ ColSrc<CM> col_src(const ColArgs &a) {
+    return ColSrc<CM>{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg};
+}
+
+// Index of the s-th set bit of m (s < popcount(m)).
+__device__ __forceinline__ int nth_bit(uint32_t m, int s) {
+    for (int i = 0; i < s; ++i) m &= m - 1;
+    return __builtin_ctz(m);
 }
 
 template <typename T, typename IT>
@@ -142,9 +157,10 @@ struct RowLds {
     IT rp[2][kTileRows + 1];
     T val[kCap];
     int32_t col[kCap];
+    int32_t dtab[kMaxDiags];  // diagonal offsets (kColDiag)
 };
 
-// col(k, row0): column of stored entry k of the tile starting at row0;
+// col: the column source (per-entry columns, or per-row diagonal masks);
 // vf(k): value of stored entry k; gf(c): the loads gathered at column c;
 // cf(g): the vector entry those loads make (the gathers of ROUND slots are
 // all issued before the first cf); of(i): this thread's own-row inputs,
@@ -154,12 +170,13 @@ struct RowLds {
 // pre(): start-up loads issued with the first row pointers (no barrier
 // inside); post(): runs after the first barrier, every thread, and returns
 // false to end the kernel (the same in every thread).
-template <typename T, typename IT, int SLOTS, int ROUND, typename CS, typename VF, typename GF,
+template <typename T, typename IT, int SLOTS, int ROUND, int CM, typename VF, typename GF,
           typename CF, typename OF, typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
-                                          CS col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf, OF of,
-                                          RF rf, PRE pre, POST post) {
+                                          ColSrc<CM> col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf,
+                                          OF of, RF rf, PRE pre, POST post) {
     constexpr int R = round_for(SLOTS, ROUND);
+    constexpr bool kDiag = CM == kColDiag;
     const int tid = threadIdx.x;
     auto rows_of = [&](int64_t tt) -> int {
         const int64_t left = n - tt * kTileRows;
@@ -172,6 +189,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         if (tid < rows) sm.rp[0][tid] = rp[t * kTileRows + tid];
         if (tid == 0) sm.rp[0][rows] = rp[t * kTileRows + rows];
     }
+    if (kDiag && tid < kMaxDiags) sm.dtab[tid] = col.dlt[tid];
     pre();
     __syncthreads();
     if (!post()) return false;
@@ -189,6 +207,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         }
         const int me = tid < rows ? tid : rows - 1;
         const auto own = of(row0 + me);
+        const uint32_t mk = kDiag ? (uint32_t)col.msk[row0 + me] : 0u;
         const IT base = cr[0];
         const int64_t cnt = (int64_t)(cr[rows] - base);
         const bool staged = cnt > 0 && cnt <= kCap;
@@ -201,12 +220,12 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 const int e = tid + j * kBlock;
                 const IT k = base + (e < last ? e : last);
                 v[j] = vf(k);
-                c[j] = col(k, row0);
+                if (!kDiag) c[j] = col(k, row0);
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 sm.val[tid + j * kBlock] = v[j];
-                sm.col[tid + j * kBlock] = c[j];
+                if (!kDiag) sm.col[tid + j * kBlock] = c[j];
             }
         }
         if (has_next) {
@@ -222,7 +241,8 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 // columns are ascending and the diagonal is stored, so its
                 // position is the number of the row's columns below the row
                 const int32_t me32 = (int32_t)(row0 + tid);
-                int below = 0;
+                int below = kDiag ? __builtin_popcount(mk & ((1u << col.nneg) - 1u)) : 0;
+                uint32_t mm = mk;  // diagonals still to visit (kColDiag)
                 T s = T(0);
 #pragma unroll
                 for (int h = 0; h < SLOTS; h += R) {
@@ -231,9 +251,17 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
 #pragma unroll
                     for (int k = 0; k < R; ++k) {
                         const int idx = lo + (h + k < lastk ? h + k : lastk);
-                        const int32_t c = sm.col[idx];
+                        int32_t c;
+                        if (kDiag) {
+                            // slot h + k is the row's (h + k)-th diagonal; past
+                            // the row the last one repeats, like the entries
+                            c = me32 + sm.dtab[__builtin_ctz(mm | 0x8000u)];
+                            mm = h + k < lastk ? (mm & (mm - 1u)) : mm;
+                        } else {
+                            c = sm.col[idx];
+                            below += (h + k < len && c < me32) ? 1 : 0;
+                        }
                         w[k] = sm.val[idx];
-                        below += (h + k < len && c < me32) ? 1 : 0;
                         g[k] = gf(c);
                     }
 #pragma unroll
@@ -243,8 +271,8 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                     }
                 }
                 for (int k = SLOTS; k < len; ++k) {
-                    const int32_t c = sm.col[lo + k];
-                    below += c < me32 ? 1 : 0;
+                    const int32_t c = kDiag ? me32 + sm.dtab[nth_bit(mk, k)] : sm.col[lo + k];
+                    if (!kDiag) below += c < me32 ? 1 : 0;
                     s += sm.val[lo + k] * cf(gf(c));
                 }
                 rf(row0 + tid, s, own, sm.val[lo + (below < lastk ? below : lastk)]);
@@ -257,8 +285,10 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 const IT hi = cr[r + 1];
                 const int64_t row = row0 + r;
                 T s = T(0);
+                const uint32_t mr = kDiag ? (uint32_t)col.msk[row] : 0u;
                 for (IT k = cr[r] + lane; k < hi; k += 64) {
-                    const int32_t c = col(k, row0);
+                    const int32_t c = kDiag ? (int32_t)row + sm.dtab[nth_bit(mr, (int)(k - cr[r]))]
+                                            : col(k, row0);
                     const T v = vf(k);
                     s += v * cf(gf(c));
                     if (c == row) pd[r] = v;  // one lane: the diagonal is stored once
@@ -275,12 +305,24 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
     return true;
 }
 
-#define SLA_DISPATCH_C16(c16, ...)                  \
-    if (c16) {                                      \
-        constexpr bool kC = true;                   \
+#define SLA_DISPATCH_CM(cm, ...)                    \
+    if ((cm) == kColDiag) {                         \
+        constexpr int kC = kColDiag;                \
+        __VA_ARGS__;                                \
+    } else if ((cm) == kColTile16) {                \
+        constexpr int kC = kColTile16;              \
         __VA_ARGS__;                                \
     } else {                                        \
-        constexpr bool kC = false;                  \
+        constexpr int kC = kColWide;                \
+        __VA_ARGS__;                                \
+    }
+
+#define SLA_DISPATCH_TILE16(c16, ...)               \
+    if (c16) {                                      \
+        constexpr int kC = kColTile16;              \
+        __VA_ARGS__;                                \
+    } else {                                        \
+        constexpr int kC = kColWide;                \
         __VA_ARGS__;                                \
     }
 

@@ -108,7 +108,10 @@ typedef struct {
  *               every product.  Without it the handle also keeps a compact
  *               copy (each column as an int16 offset from the first row of
  *               its 256-row tile, 2 bytes per entry) when every entry fits,
- *               and the products read that instead; results are identical.
+ *               and, for patterns on at most 16 diagonals with rows of at
+ *               most 8 entries, one 16-bit diagonal mask per row; the
+ *               products read the most compact form (sla_column_mode);
+ *               results are identical.
  *               Other bits: SLA_ERR_ARG.
  * Checks the pattern on the device (synchronizes `stream`).  Returns
  * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
@@ -214,6 +217,15 @@ sla_status sla_eigsh(sla_handle h, const void *d_values, double *h_evals, void *
  */
 sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_grad_evals,
                              int32_t k, void *d_grad_values, void *stream);
+
+/*
+ * sla_column_mode -- how the products read the columns of A (transpose = 0)
+ * or of A^T (transpose = 1): 0 the caller's int32 array, 1 the compact
+ * int16 tile-relative copy, 2 per-row masks over at most 16 diagonals (a
+ * pattern whose entries lie on at most 16 diagonals, rows of at most 8
+ * entries: 2 bytes per row).  -1 for a NULL handle or a missing transpose.
+ */
+int32_t sla_column_mode(sla_handle h, int32_t transpose);
 
 /*
  * sla_export_pattern -- copy the derived pattern structures into caller
