@@ -87,18 +87,18 @@ def parse():
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
                          "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
                          "and the eigenvalue gradient")
-    ap.add_argument("--column-form", default="diagonal", choices=("wide", "tile16", "diagonal"),
-                    help="column form the summarised run's products read")
+    ap.add_argument("--column-form", default="diagonal-major",
+                    choices=("wide", "tile16", "diagonal", "diagonal-major"),
+                    help="storage form the summarised run's iterations read")
     return ap.parse_args()
 
 
-def dominant_kernel(method, precond, n, nnz, sv, sr, ib=None):
+def dominant_kernel(method, precond, n, nnz, sv, sr, own_mat=None):
     """(kernel name(s), algorithmic bytes per launch, the kernel's own bytes
-    per launch with `ib` column-index bytes (default 4 per entry), source
-    files)."""
-    ib = 4 * nnz if ib is None else ib
+    per launch with `own_mat` bytes of matrix (default: CSR values, int32
+    columns and row pointers), source files)."""
     mat = nnz * (sv + 4) + (n + 1) * sr
-    own = nnz * sv + ib + (n + 1) * sr
+    own = mat if own_mat is None else own_mat
     if method == "cg":
         passes = 11 if precond == "jacobi" else 9
         return ("cg_iter_kernel", mat + (2 + passes) * n * sv, own + 9 * n * sv,
@@ -107,20 +107,32 @@ def dominant_kernel(method, precond, n, nnz, sv, sr, ib=None):
             ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
 
 
+def num_diagonals(p):
+    """Distinct column offsets col - row of the pattern."""
+    rows = np.repeat(np.arange(p.n, dtype=np.int64), np.diff(p.row_ptr))
+    return int(np.unique(p.col.astype(np.int64) - rows).size)
+
+
 def form_bytes(form, p):
-    return {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[form]
+    """Bytes of the matrix one iteration product reads in `form`: CSR values
+    plus int32 / int16 columns or one 16-bit diagonal mask per row plus the
+    row pointers, or the diagonal-major values (padding included, no index)."""
+    sv, sr = p.values.itemsize, p.row_ptr.itemsize
+    if form == "diagonal-major":
+        return num_diagonals(p) * p.n * sv
+    idx = {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[form]
+    return p.nnz * sv + idx + (p.n + 1) * sr
 
 
-def index_bytes(p):
-    """(column form, bytes of column indices one product reads) for a handle
-    on this pattern, as the library chose it: int32 per entry, int16 per
-    entry, or one 16-bit diagonal mask per row."""
+def iteration_form(p):
+    """(form, matrix bytes per product) of the solver iterations on a handle
+    for this pattern, as the library chose it."""
     import torch
     import differentiable_sparse_linear_amd as sla
     pat = sla.Pattern(torch.from_numpy(p.row_ptr).cuda(), torch.from_numpy(p.col).cuda())
-    mode = pat.column_mode()
+    form = pat.iteration_form()
     pat.close()
-    return mode, {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[mode]
+    return form, form_bytes(form, p)
 
 
 def sources_sha(files):
@@ -541,15 +553,15 @@ def main():
         k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
         k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
         k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
-        form, ib = index_bytes(p)
+        form, fb = iteration_form(p)
         kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
-                                                    p.values.itemsize, p.row_ptr.itemsize, ib)
+                                                    p.values.itemsize, p.row_ptr.itemsize, fb)
         achieved = kbytes / k_avg_s / 1e9
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": read_traffic(kernel, p.name, sources_sha(srcs)),
                     "bytes_per_launch": kbytes, "kernel_bytes_per_launch": own,
-                    "column_form": form, "kernel_GBps": own / k_avg_s / 1e9,
+                    "iteration_form": form, "kernel_GBps": own / k_avg_s / 1e9,
                     "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n}
 
     result = {

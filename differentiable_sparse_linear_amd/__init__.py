@@ -37,14 +37,14 @@ SLA_F32, SLA_F64 = 0, 1
 SLA_I32, SLA_I64 = 0, 1
 SLA_CG, SLA_BICGSTAB = 0, 1
 SLA_PRECOND_NONE, SLA_PRECOND_JACOBI = 0, 1
-SLA_CREATE_TRANSPOSE, SLA_CREATE_WIDE_COLUMNS = 1, 2
+SLA_CREATE_TRANSPOSE, SLA_CREATE_WIDE_COLUMNS, SLA_CREATE_CSR_VALUES = 1, 2, 4
 SLA_OK, SLA_NOT_CONVERGED, SLA_BREAKDOWN = 0, 1, 2
 SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
 SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
 
 EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
                     "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint", "sla_column_mode",
-                    "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
+                    "sla_iteration_form", "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
                     "sla_last_error")
 
 _METHODS = {"cg": SLA_CG, "bicgstab": SLA_BICGSTAB}
@@ -101,6 +101,8 @@ def load(path: Optional[str] = None):
     lib.sla_eigsh_adjoint.restype = I32
     lib.sla_column_mode.argtypes = [P, I32]
     lib.sla_column_mode.restype = I32
+    lib.sla_iteration_form.argtypes = [P, I32]
+    lib.sla_iteration_form.restype = I32
     lib.sla_export_pattern.argtypes = [P, P, P, P, P, P]
     lib.sla_export_pattern.restype = I32
     lib.sla_workspace_bytes.argtypes = [P]
@@ -233,12 +235,16 @@ class Pattern:
     by this object because the library borrows them).  ``build_transpose``
     builds the map of A^T (transposed products, BiCGStab adjoint);
     ``compact_columns`` lets the handle read a 2-byte tile-relative copy of
-    the columns where every entry fits (identical results, fewer bytes).
+    the columns where every entry fits, or one 16-bit diagonal mask per row
+    for stencil patterns (identical results, fewer bytes);
+    ``diagonal_major`` (with compact columns) lets the solver iterations of
+    3-, 5- and 7-diagonal patterns read a diagonal-major copy of the values
+    made at the start of each solve (no row pointers or columns read).
     """
 
     def __init__(self, row_ptr: torch.Tensor, col: torch.Tensor, batch: int = 1,
                  dtype: torch.dtype = torch.float64, build_transpose: bool = False,
-                 compact_columns: bool = True, stream=None):
+                 compact_columns: bool = True, stream=None, diagonal_major: bool = True):
         _check(row_ptr, "row_ptr")
         _check(col, "col", torch.int32)
         if row_ptr.dtype not in (torch.int32, torch.int64):
@@ -253,7 +259,8 @@ class Pattern:
         self.has_transpose = bool(build_transpose)
         self.device = row_ptr.device
         flags = (SLA_CREATE_TRANSPOSE if build_transpose else 0) | \
-            (0 if compact_columns else SLA_CREATE_WIDE_COLUMNS)
+            (0 if compact_columns else SLA_CREATE_WIDE_COLUMNS) | \
+            (0 if diagonal_major else SLA_CREATE_CSR_VALUES)
         self.handle = sla_create(self.n, self.nnz, self.batch, dtype, row_ptr, col, flags, stream)
 
     def close(self):
@@ -277,6 +284,14 @@ class Pattern:
         if m < 0:
             raise SlaError(SLA_ERR_ARG, "sla_column_mode")
         return ("wide", "tile16", "diagonal")[m]
+
+    def iteration_form(self, transpose: bool = False) -> str:
+        """What the solver iterations read: a column mode, or
+        "diagonal-major" (values repacked per solve, no index)."""
+        m = load().sla_iteration_form(ctypes.c_void_p(self.handle), 1 if transpose else 0)
+        if m < 0:
+            raise SlaError(SLA_ERR_ARG, "sla_iteration_form")
+        return ("wide", "tile16", "diagonal", "diagonal-major")[m]
 
     def _vals(self, values):
         _check(values, "values", self.dtype, self.batch * self.nnz)

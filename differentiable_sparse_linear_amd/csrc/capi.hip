@@ -45,6 +45,8 @@ struct sla_ctx {
     const void *rp = nullptr;
     const int32_t *col = nullptr;
     ColArgs ca, ca_t;            // where the products read the columns of A, A^T
+    ColArgs ia, ia_t;            // the form the solver iterations read for A, A^T
+    void *dia = nullptr;         // diagonal-major values of one system, or null
     int32_t *dlt = nullptr;      // [2][kMaxDiags] diagonal offsets of A, A^T
     uint16_t *msk = nullptr;     // per-row diagonal masks of A, or null
     uint16_t *msk_t = nullptr;   // the same for A^T
@@ -59,6 +61,7 @@ struct sla_ctx {
     int slots = 8;   // gather slots per row (A), from its longest row
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
+    int it_slots = 8, it_slots_t = 8;  // slots (or diagonals) of the iteration form
     void *vec = nullptr;
     SolveState *st = nullptr;
     double *part = nullptr;
@@ -126,6 +129,7 @@ void release(sla_ctx *h) {
     (void)hipFree(h->col16_t);
     (void)hipFree(h->perm);
     (void)hipFree(h->val_t);
+    (void)hipFree(h->dia);
     (void)hipFree(h->vec);
     (void)hipFree(h->st);
     (void)hipFree(h->part);
@@ -157,11 +161,16 @@ sla_status check_opts(const sla_solve_opts &o) {
     return SLA_OK;
 }
 
-// The operator a solve iterates with: A itself or the mapped A^T.
+// The operator a solve iterates with: A itself or the mapped A^T.  Products
+// with the caller's CSR values read `cols`; the iteration kernels read `it`,
+// which is either the same or the diagonal-major form (values repacked into
+// the handle's buffer at the start of each system's solve).
 struct Operator {
     const void *rp;
     ColArgs cols;
     int slots;
+    ColArgs it;
+    int it_slots;
 };
 
 // One system on the grid path: fill the argument block, run init, then
@@ -173,13 +182,15 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     const int64_t n = h->n;
     const bool cg = o.method == SLA_CG;
     const bool jac = cg && o.precond == SLA_PRECOND_JACOBI;
-    const int cm = op.cols.mode;
+    const int cm = op.it.mode;
+    const int slots = op.it_slots;
+    const bool dmaj = cm == kColDiaMajor;
     T *vec = reinterpret_cast<T *>(h->vec);
     IterArgs<T, IT> a;
     memset(&a, 0, sizeof(a));
-    a.val = val;
+    a.val = dmaj ? reinterpret_cast<const T *>(h->dia) : val;
     a.rp = reinterpret_cast<const IT *>(op.rp);
-    a.cols = op.cols;
+    a.cols = op.it;
     a.x = x;
     a.b = b;
     a.r = vec + 0 * n;
@@ -205,6 +216,9 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     const IterArgs<T, IT> *ad = reinterpret_cast<const IterArgs<T, IT> *>(h->args_dev);
     HIP_TRY(hipMemcpyAsync(h->args_dev, h->args_host, sizeof(a), hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState), s));
+    if (dmaj)
+        HIP_TRY(launch_dia_pack<T, IT>(a.rp, op.cols.msk, op.it.nd, val,
+                                       reinterpret_cast<T *>(h->dia), n, s));
     if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, vec + 10 * n,
                                         n, st, s));
     // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
@@ -215,16 +229,16 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n, s));
     if (cg)
-        HIP_TRY(launch_cg_init<T, IT>(op.slots, cm, jac, ad, n, s));
+        HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, s));
     else
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) return launch_cg_iter<T, IT>(op.slots, cm, jac, ad, n, k & 1, ss);
-        if ((e = launch_bicg_pv<T, IT>(op.slots, cm, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_bicg_st<T, IT>(op.slots, cm, ad, n, ss)) != hipSuccess) return e;
+        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, ad, n, k & 1, ss);
+        if ((e = launch_bicg_pv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_bicg_st<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_update<T, IT>(ad, n, ss);
     };
 
@@ -244,13 +258,13 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(op.slots, cm, jac, ad, n, k & 1, s,
+                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, ad, n, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else {
-                HIP_TRY(launch_bicg_pv<T, IT>(op.slots, cm, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_pv<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_st<T, IT>(op.slots, cm, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_st<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
                 HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
@@ -409,12 +423,12 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     oo.use_x0 = 0;
     sla_status st;
     if (o.method == SLA_CG) {
-        Operator op{h->rp, h->ca, h->slots};
+        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
         // A^T with values gathered through the transpose map, one system at
         // a time into the handle's buffer
-        Operator op{h->rp_t, h->ca_t, h->slots_t};
+        Operator op{h->rp_t, h->ca_t, h->slots_t, h->ia_t, h->it_slots_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
         std::vector<int32_t> it(B0), mv(B0), stc(B0);
@@ -496,6 +510,8 @@ hipError_t build_diag(sla_ctx *h, const IT *rp, const int32_t *col, int32_t max_
     ca.msk = *msk;
     ca.dlt = dlt_dev;
     ca.nneg = nneg;
+    ca.nd = nd;
+    for (int q = 0; q < nd && q < kMaxDiaMajor; ++q) ca.off[q] = dlt[q];
     ca.mode = kColDiag;
     return hipSuccess;
 }
@@ -504,6 +520,7 @@ template <typename T, typename IT>
 sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     const bool build_t = (flags & SLA_CREATE_TRANSPOSE) != 0;
     const bool compact = (flags & SLA_CREATE_WIDE_COLUMNS) == 0;
+    const bool dmajor = compact && (flags & SLA_CREATE_CSR_VALUES) == 0;
     const int64_t n = h->n, nnz = h->nnz;
     const IT *rp = reinterpret_cast<const IT *>(h->rp);
     HIP_TRY(dmalloc(h, &h->diagpos, sizeof(IT) * n));
@@ -551,6 +568,32 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
             h->dlt = nullptr;
             h->ws_bytes -= (int64_t)sizeof(int32_t) * 2 * kMaxDiags;
         }
+    }
+    // The iterations read diagonal-major values for patterns on 3, 5 or 7
+    // diagonals with the main one in the middle (nearest-neighbour stencils
+    // in 1, 2 and 3 dimensions) whose padding -- the slots of boundary rows
+    // that lack a diagonal -- stays within a quarter of the stored entries;
+    // one system's copy is kept.
+    h->ia = h->ca;
+    h->it_slots = h->slots;
+    h->ia_t = h->ca_t;
+    h->it_slots_t = h->slots_t;
+    if (dmajor) {
+        auto fits = [&](const ColArgs &c) {
+            return c.mode == kColDiag && (c.nd == 3 || c.nd == 5 || c.nd == 7) &&
+                   c.nneg == c.nd / 2 && (int64_t)c.nd * n <= nnz + nnz / 4;
+        };
+        int nd = 0;
+        if (fits(h->ca)) {
+            h->ia.mode = kColDiaMajor;
+            h->it_slots = nd = h->ca.nd;
+        }
+        if (h->has_t && fits(h->ca_t)) {
+            h->ia_t.mode = kColDiaMajor;
+            h->it_slots_t = h->ca_t.nd;
+            nd = std::max(nd, (int)h->ca_t.nd);
+        }
+        if (nd) HIP_TRY(dmalloc(h, &h->dia, sizeof(T) * (size_t)nd * n));
     }
     HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
     HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
@@ -756,7 +799,8 @@ sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch, in
     if (dtype != SLA_F32 && dtype != SLA_F64) return SLA_ERR_ARG;
     if (row_ptr_type != SLA_I32 && row_ptr_type != SLA_I64) return SLA_ERR_ARG;
     if (row_ptr_type == SLA_I32 && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
-    if (flags & ~(SLA_CREATE_TRANSPOSE | SLA_CREATE_WIDE_COLUMNS)) return SLA_ERR_ARG;
+    if (flags & ~(SLA_CREATE_TRANSPOSE | SLA_CREATE_WIDE_COLUMNS | SLA_CREATE_CSR_VALUES))
+        return SLA_ERR_ARG;
     if ((flags & SLA_CREATE_TRANSPOSE) && nnz >= ((int64_t)1 << 31)) return SLA_ERR_ARG;
     if (!d_row_ptr || !d_col) return SLA_ERR_ARG;
     sla_ctx *h = new (std::nothrow) sla_ctx();
@@ -863,7 +907,7 @@ sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *
     return dispatch(h, [&](auto t, auto it) -> sla_status {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        Operator op{h->rp, h->ca, h->slots};
+        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots};
         return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
                                 reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
                                 info, s);
@@ -945,6 +989,11 @@ sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_gr
 int32_t sla_column_mode(sla_handle h, int32_t transpose) {
     if (!h || (transpose && !h->has_t)) return -1;
     return transpose ? h->ca_t.mode : h->ca.mode;
+}
+
+int32_t sla_iteration_form(sla_handle h, int32_t transpose) {
+    if (!h || (transpose && !h->has_t)) return -1;
+    return transpose ? h->ia_t.mode : h->ia.mode;
 }
 
 sla_status sla_export_pattern(sla_handle h, void *d_diagpos, void *d_row_ptr_t, void *d_col_t,

@@ -76,7 +76,7 @@ struct PvOwn {
 #define SLA_BICG_WAVES 5
 #endif
 template <typename T, typename IT, int SLOTS, int CM>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_BICG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
@@ -143,7 +143,7 @@ void bicg_pv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto pk = [&](const G3<T> &g) -> T { return pdir(false, beta, omega, g.a, g.b, g.c); };
     double rv_acc = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, 4>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         [&](int32_t c) { return G3<T>{r[c], pp[c], vp[c]}; }, pk,
         [&](int64_t i) { return PvOwn<T>{r[i], pp[i], vp[i], rh[i]}; },
         [&](int64_t i, T acc, const PvOwn<T> &o, T) {
@@ -166,7 +166,7 @@ struct StOwn {
 // Iteration k (k = iter_b): alpha = rho_k / rhat.v (0: breakdown);
 // s = r - alpha v evaluated while gathering, t = A s; partials t.s, t.t, s.s.
 template <typename T, typename IT, int SLOTS, int CM>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_BICG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
@@ -203,7 +203,7 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         [&](int32_t c) { return G2<T>{r[c], v[c]}; }, sk,
         [&](int64_t i) { return StOwn<T>{r[i], v[i]}; },
         [&](int64_t i, T acc, const StOwn<T> &o, T) {
@@ -300,9 +300,9 @@ template <typename T, typename IT>
 hipError_t launch_bicg_pv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
-    SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(
+    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(
                                                         bicg_pv_kernel<T, IT, kS, kC>, grid,
-                                                        dim3(kBlock), 0, s, ev, a)));
+                                                        dim3(kBlock), 0, s, ev, a));
     return hipGetLastError();
 }
 
@@ -310,9 +310,9 @@ template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
-    SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(
+    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(
                                                         bicg_st_kernel<T, IT, kS, kC>, grid,
-                                                        dim3(kBlock), 0, s, ev, a)));
+                                                        dim3(kBlock), 0, s, ev, a));
     return hipGetLastError();
 }
 

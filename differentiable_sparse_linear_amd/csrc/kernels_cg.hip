@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
     auto load = [&](int64_t c) { return G3<T>{b[c], ax0[c], JAC ? dinv[c] : T(1)}; };
     auto u_of = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
     spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         load, u_of, load,
         [&](int64_t i, T acc, const G3<T> &o, T) {
             const T ri = o.a - o.b;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 #define SLA_CG_WAVES 5
 #endif
 template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(SLA_CG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
     if (load_done(st)) return;
@@ -210,7 +210,7 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](IT k) { return val[k]; },
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; }, u_of,
         [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
         [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
@@ -497,26 +497,16 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 
 // ------------------------------------------------------------------ launchers
 
-#define SLA_DISPATCH_G(G, ...)                      \
-    switch (G) {                                    \
-        case 2: { constexpr int kG = 2; __VA_ARGS__; } break;   \
-        case 4: { constexpr int kG = 4; __VA_ARGS__; } break;   \
-        case 8: { constexpr int kG = 8; __VA_ARGS__; } break;   \
-        case 16: { constexpr int kG = 16; __VA_ARGS__; } break; \
-        case 32: { constexpr int kG = 32; __VA_ARGS__; } break; \
-        default: { constexpr int kG = 64; __VA_ARGS__; } break; \
-    }
-
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s) {
     const int grid = grid_for_tiles(tiles_of(n));
     if (jac) {
-        SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, true, kS, kC>
-                                                 <<<grid, kBlock, 0, s>>>(a)));
+        SLA_DISPATCH_FORM(cm, slots, cg_init_kernel<T, IT, true, kS, kC>
+                                                 <<<grid, kBlock, 0, s>>>(a));
     } else {
-        SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, cg_init_kernel<T, IT, false, kS, kC>
-                                                 <<<grid, kBlock, 0, s>>>(a)));
+        SLA_DISPATCH_FORM(cm, slots, cg_init_kernel<T, IT, false, kS, kC>
+                                                 <<<grid, kBlock, 0, s>>>(a));
     }
     return hipGetLastError();
 }
@@ -526,9 +516,9 @@ hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
                           int ph, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
 #define SLA_CG_ITER(J, P)                                                                      \
-    SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, launch_maybe_timed(                        \
+    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(                        \
                                                         cg_iter_kernel<T, IT, J, kS, P, kC>,   \
-                                                        grid, dim3(kBlock), 0, s, ev, a)))
+                                                        grid, dim3(kBlock), 0, s, ev, a))
     if (jac) {
         if (ph) {
             SLA_CG_ITER(true, 1);

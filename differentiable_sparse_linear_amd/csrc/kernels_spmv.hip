@@ -126,6 +126,26 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restric
         out[k] = val[perm[k]];
 }
 
+// out[q * n + i] = row i's entry on diagonal q, 0 where bit q of msk[i] is
+// clear.  The row's entries are stored in ascending column order, which is
+// ascending q, so the k-th set bit takes the k-th entry.
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void dia_pack_kernel(const IT *__restrict__ rp,
+                                                          const uint16_t *__restrict__ msk, int nd,
+                                                          const T *__restrict__ val,
+                                                          T *__restrict__ out, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+        uint32_t m = msk[i];
+        IT k = rp[i];
+        for (int q = 0; q < nd; ++q, m >>= 1) {
+            T v = T(0);
+            if (m & 1u) v = val[k++];
+            out[(int64_t)q * n + i] = v;
+        }
+    }
+}
+
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void dinv_kernel(const IT *__restrict__ diagpos,
                                                       const T *__restrict__ val,
@@ -200,6 +220,16 @@ hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz,
 }
 
 template <typename T, typename IT>
+hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val, T *out,
+                           int64_t n, hipStream_t s) {
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    dia_pack_kernel<T, IT><<<(unsigned)blocks, kBlock, 0, s>>>(rp, msk, nd, val, out, n);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
 hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
                        hipStream_t s) {
     dinv_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(diagpos, val, dinv, n, st);
@@ -225,7 +255,9 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
                                            const T *, const T *, T *, int64_t, int64_t, int,     \
                                            bool, hipStream_t);  \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
-                                           hipStream_t);
+                                           hipStream_t);                                         \
+    template hipError_t launch_dia_pack<T, IT>(const IT *, const uint16_t *, int, const T *,    \
+                                               T *, int64_t, hipStream_t);
 
 SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)

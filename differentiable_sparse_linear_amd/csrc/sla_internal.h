@@ -73,9 +73,14 @@ enum : int {
 // host rewrites the pointers before each solve.
 // Column modes of a pattern (how the SpMV-shaped kernels find the columns):
 // the caller's int32 array, an int16 tile-relative copy, or per-row masks
-// over at most kMaxDiags diagonals.
-constexpr int kColWide = 0, kColTile16 = 1, kColDiag = 2;
+// over at most kMaxDiags diagonals.  The solver iterations have one more
+// form, kColDiaMajor: the values of the system repacked diagonal-major
+// ([nd][n], zero where a row lacks a diagonal) for patterns on 3, 5 or 7
+// diagonals (1D, 2D and 3D nearest-neighbour stencils), so that a row's
+// entries need neither row pointers nor columns.
+constexpr int kColWide = 0, kColTile16 = 1, kColDiag = 2, kColDiaMajor = 3;
 constexpr int kMaxDiags = 16;
+constexpr int kMaxDiaMajor = 8;  // diagonals a diagonal-major operator may have
 
 struct ColArgs {
     const int32_t *col = nullptr;    // int32 columns (always present)
@@ -84,6 +89,8 @@ struct ColArgs {
     const int32_t *dlt = nullptr;    // [kMaxDiags] diagonal offsets, ascending (device)
     int32_t nneg = 0;                // diagonals below the main one
     int32_t mode = kColWide;
+    int32_t nd = 0;                  // number of diagonals (kColDiag, kColDiaMajor)
+    int32_t off[kMaxDiaMajor] = {};  // their offsets when nd <= kMaxDiaMajor
 };
 
 template <typename T, typename IT>
@@ -268,6 +275,11 @@ hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, c
                        hipStream_t s);
 template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
+// Diagonal-major copy of one system's CSR values: out[q * n + i] = the entry
+// of row i on diagonal q (bit q of msk[i]), 0 where the row lacks it.
+template <typename T, typename IT>
+hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val, T *out,
+                           int64_t n, hipStream_t s);
 template <typename T, typename IT>
 hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
                        hipStream_t s);

@@ -126,6 +126,9 @@ constexpr int round_for(int slots, int round) {
 //              mask per row says which diagonals the row stores; the column
 //              of diagonal q is row + dlt[q] (dlt ascending, so the row's
 //              columns ascend with q): 2 bytes per row, no per-entry index.
+//   kColDiaMajor  (solver iterations) the values are a diagonal-major copy,
+//              vf(q * n + i) is row i's entry on diagonal q (0 where the row
+//              lacks it) and its column is i + off[q]: no index at all.
 template <int CM>
 struct ColSrc {
     gptr<const int32_t> c32;
@@ -133,6 +136,7 @@ struct ColSrc {
     gptr<const uint16_t> msk;
     gptr<const int32_t> dlt;
     int32_t nneg;  // diagonals below the main one (dlt[q] < 0 for q < nneg)
+    int32_t off[kMaxDiaMajor];  // kColDiaMajor: the diagonals' offsets, ascending
     // column of stored entry k in the tile starting at row0 (per-entry modes)
     __device__ __forceinline__ int32_t operator()(int64_t k, int64_t row0) const {
         if constexpr (CM == kColTile16)
@@ -143,7 +147,12 @@ struct ColSrc {
 };
 template <int CM>
 __device__ __forceinline__ ColSrc<CM> col_src(const ColArgs &a) {
-    return ColSrc<CM>{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg};
+    ColSrc<CM> c{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg, {}};
+    if constexpr (CM == kColDiaMajor) {
+#pragma unroll
+        for (int q = 0; q < kMaxDiaMajor; ++q) c.off[q] = a.off[q];
+    }
+    return c;
 }
 
 // Index of the s-th set bit of m (s < popcount(m)).
@@ -160,6 +169,63 @@ struct RowLds {
     int32_t dtab[kMaxDiags];  // diagonal offsets (kColDiag)
 };
 
+// Rows of a diagonal-major operator with ND diagonals, the main one in the
+// middle (slot ND / 2; the spmv_rows contract below, without the LDS): thread
+// t of a tile takes row row0 + t and reads its ND values as ND coalesced
+// loads, vf(q * n + i); the column of slot q is i + off[q], clamped into
+// [0, n) for the zero padding slots of boundary rows (0 * finite adds
+// nothing, so the sum over q -- ascending columns, the order of the CSR
+// forms -- equals the sum over the stored entries).  The main diagonal's
+// gathers use the row index itself, so they coincide with the row's own
+// loads.  All loads of a tile are issued before its first use, and the first
+// tile's before the start-up barrier, so that their latency overlaps the
+// kernel's start-up loads.
+template <typename T, int ND, typename VF, typename GF, typename CF, typename OF, typename RF,
+          typename PRE, typename POST>
+__device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
+                                         const ColSrc<kColDiaMajor> &col, VF vf, GF gf, CF cf,
+                                         OF of, RF rf, PRE pre, POST post) {
+    static_assert(ND >= 1 && ND <= kMaxDiaMajor && (ND & 1), "diagonal count");
+    using G = decltype(gf(0));
+    using O = decltype(of(0));
+    constexpr int d0 = ND / 2;  // the main diagonal's slot
+    const int tid = threadIdx.x;
+    T v[ND];
+    G g[ND];
+    O own;
+    auto load = [&](int64_t t) {
+        const int64_t row0 = t * kTileRows;
+        const int64_t left = n - row0;
+        const int64_t i = row0 + (tid < left ? tid : left - 1);
+        own = of(i);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) {
+            v[q] = vf((int64_t)q * n + i);
+            int64_t c = i + col.off[q];
+            c = c < 0 ? 0 : (c >= n ? n - 1 : c);
+            g[q] = gf(q == d0 ? (int32_t)i : (int32_t)c);
+        }
+    };
+    auto use = [&](int64_t t) {
+        const int64_t i = t * kTileRows + tid;
+        T s = T(0);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) s += v[q] * cf(g[q]);
+        if (i < n) rf(i, s, own, v[d0]);
+    };
+    int64_t t = tr.first;
+    if (t < tr.end) load(t);
+    pre();
+    __syncthreads();
+    if (!post()) return false;
+    if (t < tr.end) use(t);
+    for (t += tr.stride; t < tr.end; t += tr.stride) {
+        load(t);
+        use(t);
+    }
+    return true;
+}
+
 // col: the column source (per-entry columns, or per-row diagonal masks);
 // vf(k): value of stored entry k; gf(c): the loads gathered at column c;
 // cf(g): the vector entry those loads make (the gathers of ROUND slots are
@@ -175,6 +241,9 @@ template <typename T, typename IT, int SLOTS, int ROUND, int CM, typename VF, ty
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
                                           ColSrc<CM> col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf,
                                           OF of, RF rf, PRE pre, POST post) {
+    if constexpr (CM == kColDiaMajor) {
+        return dia_rows<T, SLOTS>(tr, n, col, vf, gf, cf, of, rf, pre, post);
+    } else {
     constexpr int R = round_for(SLOTS, ROUND);
     constexpr bool kDiag = CM == kColDiag;
     const int tid = threadIdx.x;
@@ -303,6 +372,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         cur ^= 1;
     }
     return true;
+    }
 }
 
 #define SLA_DISPATCH_CM(cm, ...)                    \
@@ -331,6 +401,20 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         case 4: { constexpr int kS = 4; __VA_ARGS__; } break;   \
         case 6: { constexpr int kS = 6; __VA_ARGS__; } break;   \
         default: { constexpr int kS = 8; __VA_ARGS__; } break;  \
+    }
+
+// Form of a solver-iteration kernel: kC the column mode, kS the gather slots
+// (CSR forms) or the diagonal count 3, 5 or 7 (kColDiaMajor).
+#define SLA_DISPATCH_FORM(cm, slots, ...)                           \
+    if ((cm) == kColDiaMajor) {                                     \
+        constexpr int kC = kColDiaMajor;                            \
+        switch (slots) {                                            \
+            case 3: { constexpr int kS = 3; __VA_ARGS__; } break;   \
+            case 5: { constexpr int kS = 5; __VA_ARGS__; } break;   \
+            default: { constexpr int kS = 7; __VA_ARGS__; } break;  \
+        }                                                           \
+    } else {                                                        \
+        SLA_DISPATCH_CM(cm, SLA_DISPATCH_SLOTS(slots, __VA_ARGS__)) \
     }
 
 }  // namespace sla

@@ -50,7 +50,8 @@ enum { SLA_F32 = 0, SLA_F64 = 1 };                 /* value / vector type   */
 enum { SLA_I32 = 0, SLA_I64 = 1 };                 /* row_ptr index type    */
 enum { SLA_CG = 0, SLA_BICGSTAB = 1 };             /* Krylov method         */
 enum { SLA_PRECOND_NONE = 0, SLA_PRECOND_JACOBI = 1 };
-enum { SLA_CREATE_TRANSPOSE = 1, SLA_CREATE_WIDE_COLUMNS = 2 };  /* sla_create flags */
+/* sla_create flags */
+enum { SLA_CREATE_TRANSPOSE = 1, SLA_CREATE_WIDE_COLUMNS = 2, SLA_CREATE_CSR_VALUES = 4 };
 
 typedef enum {
     SLA_OK = 0,
@@ -112,6 +113,17 @@ typedef struct {
  *               most 8 entries, one 16-bit diagonal mask per row; the
  *               products read the most compact form (sla_column_mode);
  *               results are identical.
+ *               SLA_CREATE_CSR_VALUES: the solver iterations read the
+ *               caller's CSR values.  Without it (and without
+ *               SLA_CREATE_WIDE_COLUMNS), when the pattern's entries lie on
+ *               3, 5 or 7 diagonals (nearest-neighbour stencils in 1, 2 and
+ *               3 dimensions) and nd * n <= 1.25 nnz, the handle keeps a
+ *               buffer of nd * n values (one system) and each grid-path
+ *               solve first copies the system's values into it
+ *               diagonal-major, zero where a row lacks a diagonal; the
+ *               iterations then read no row pointers or columns
+ *               (sla_iteration_form).  Results are identical as long as the
+ *               iterates stay finite.
  *               Other bits: SLA_ERR_ARG.
  * Checks the pattern on the device (synchronizes `stream`).  Returns
  * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
@@ -226,6 +238,14 @@ sla_status sla_eigsh_adjoint(sla_handle h, const void *d_evecs, const void *d_gr
  * entries: 2 bytes per row).  -1 for a NULL handle or a missing transpose.
  */
 int32_t sla_column_mode(sla_handle h, int32_t transpose);
+
+/*
+ * sla_iteration_form -- the form the solver iterations of the grid path read
+ * for A (transpose = 0) or for A^T (transpose = 1, BiCGStab adjoint): the
+ * sla_column_mode codes 0-2, or 3 for diagonal-major values (see
+ * SLA_CREATE_CSR_VALUES).  -1 for a NULL handle or a missing transpose.
+ */
+int32_t sla_iteration_form(sla_handle h, int32_t transpose);
 
 /*
  * sla_export_pattern -- copy the derived pattern structures into caller

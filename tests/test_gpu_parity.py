@@ -458,38 +458,55 @@ def test_determinism_and_launch_modes_agree(hip):
 
 def test_compact_columns_change_nothing(hip):
     """The compact column forms (2-byte tile-relative columns, per-row
-    diagonal masks) are storage choices: products, solves and adjoints are
-    bitwise the same as with the caller's int32 columns, and each form is
-    kept only where it fits."""
+    diagonal masks) and the diagonal-major values of the solver iterations
+    are storage choices: products, solves and adjoints are bitwise the same
+    as with the caller's int32 columns and CSR values, and each form is kept
+    only where it fits."""
     banner("compact columns")
     rp, col, val = W.random_csr(300, 0.05, 3)
     rnd = W.Problem("random300", 300, rp, col, val, np.ones((1, 300)), np.zeros((1, 300)),
                     method="bicgstab", precond="none", tol=1e-10, maxit=2000)
-    cases = [(W.config(2, size=28), "diagonal"), (W.config(4, size=40), "diagonal"),
-             (W.config(3, size=20, batch=4), "diagonal"), (W.config(5, size=33), "diagonal"),
-             (rnd, "tile16")]
-    for p, mode in cases:
+    # (problem, product form, iteration form with diagonal-major allowed)
+    cases = [(W.config(2, size=28), "diagonal", "diagonal-major"),
+             (W.config(4, size=40), "diagonal", "diagonal-major"),
+             (W.config(3, size=20, batch=4), "diagonal", "diagonal-major"),
+             (W.config(5, size=33), "diagonal", "diagonal-major"),
+             (W.config(1), "diagonal", "diagonal-major"),
+             (rnd, "tile16", "tile16")]
+    variants = [(True, True), (True, False), (False, True)]  # (compact, diagonal-major)
+    for p, mode, form in cases:
         d = to_dev(p)
         outs, ws = [], []
-        for compact in (True, False):
+        for compact, dmaj in variants:
             pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p),
-                              build_transpose=True, compact_columns=compact)
-            assert pat.column_mode() == (mode if compact else "wide"), p.name
-            assert pat.column_mode(transpose=True) == (mode if compact else "wide"), p.name
+                              build_transpose=True, compact_columns=compact,
+                              diagonal_major=dmaj)
+            want = mode if compact else "wide"
+            assert pat.column_mode() == want, p.name
+            assert pat.column_mode(transpose=True) == want, p.name
+            want_it = form if (compact and dmaj) else want
+            assert pat.iteration_form() == want_it, p.name
+            assert pat.iteration_form(transpose=True) == want_it, p.name
             ws.append(pat.workspace_bytes())
             xr = torch.from_numpy(np.random.default_rng(5).standard_normal((p.batch, p.n))
                                   .astype(p.values.dtype)).cuda()
             y = pat.matvec(d["val"], xr)
             yt = pat.matvec(d["val"], xr, transpose=True)
-            kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit)
-            x, info = pat.solve(d["val"], d["b"], **kw)
-            gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
-            outs.append([t.cpu().numpy() for t in (y, yt, x, gv, gb)] +
-                        [info["iters"], ainfo["iters"]])
+            res = [y, yt]
+            for prof in (False, True):  # profile mode: the grid path at every size
+                kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit,
+                          profile=prof)
+                x, info = pat.solve(d["val"], d["b"], **kw)
+                gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
+                res += [x, gv, gb, torch.from_numpy(np.asarray(info["iters"])),
+                        torch.from_numpy(np.asarray(ainfo["iters"]))]
+            outs.append([t.cpu().numpy() for t in res])
             pat.close()
-        for a, b in zip(outs[0], outs[1]):
-            assert np.array_equal(a, b), p.name
-        assert ws[0] > ws[1], (p.name, ws)
+        for o in outs[1:]:
+            for a, b in zip(outs[0], o):
+                assert np.array_equal(a, b), p.name
+        assert ws[1] > ws[2], (p.name, ws)
+        assert (ws[0] > ws[1]) == (form == "diagonal-major"), (p.name, ws)
     # offsets beyond int16 and more than 16 diagonals: no compact form
     rp, col, val = W.powerlaw_graph_laplacian(60000, 9)
     drp, dcol = torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda()
