@@ -19,12 +19,16 @@ bytes per PCG iteration (SpMV plus the textbook recurrence's 11 vector passes)
     nnz*(sv + 4) + (n + 1)*sr + 2*n*sv + 11*n*sv
 (sv, sr: value and row-pointer widths; 9 passes without a preconditioner).
 ``kernel_bytes_per_launch`` is what the fused kernel itself must move: the
-matrix once (column indices as the handle reads them: 4 bytes per entry,
-2 with its compact tile-relative copy, or 2 bytes per row with its
-diagonal masks) plus, on average over the two iteration
-parities, 9 vectors (even launches read u, w, s, p and write p, s, u, w; odd
-launches also read and write x).  For BiCGStab the two SpMV kernels are timed and priced at the
-SpMV's algorithmic bytes nnz*(sv + 4) + (n + 1)*sr + 2*n*sv.
+matrix once in the form the handle iterates on (CSR values with 4 bytes of
+column per entry, 2 with its compact tile-relative copy, or 2 bytes per row
+with its diagonal masks, plus row pointers; or the diagonal-major values,
+nd * n * sv, for 3/5/7-diagonal stencils) plus, on average over the two
+iteration parities, 9 vectors (even launches read u, w, s, p and write p, s,
+u, w; odd launches also read and write x).  For BiCGStab both kernels of an
+iteration are timed; each launch is priced at half of one textbook BiCGStab
+iteration, (2*(nnz*(sv + 4) + (n + 1)*sr) + 19*n*sv) / 2, and moves the
+matrix plus 7.5 vectors on average (bicg_xpv reads s, t, p, v, x, rhat and
+writes x, r, p, v; bicg_st reads r, v, rhat and writes s, t).
 ``traffic`` is the HBM bytes per launch measured with rocprofv3 counters
 (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
 1 GiB copy) and stored under profiles/ with a hash of the kernel's sources;
@@ -103,8 +107,10 @@ def dominant_kernel(method, precond, n, nnz, sv, sr, own_mat=None):
         passes = 11 if precond == "jacobi" else 9
         return ("cg_iter_kernel", mat + (2 + passes) * n * sv, own + 9 * n * sv,
                 ["kernels_cg.hip", "spmv_tile.h", "sla_internal.h"])
-    return ("bicg_pv_kernel+bicg_st_kernel", mat + 2 * n * sv, own + 5 * n * sv,
-            ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
+    # two launches per BiCGStab iteration: each is priced at half of one
+    # textbook iteration (2 products + 19 vector passes)
+    return ("bicg_xpv_kernel+bicg_st_kernel", (2 * mat + 19 * n * sv) // 2,
+            own + (15 * n * sv) // 2, ["kernels_bicg.hip", "spmv_tile.h", "sla_internal.h"])
 
 
 def num_diagonals(p):

@@ -237,16 +237,15 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
         if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, ad, n, k & 1, ss);
-        if ((e = launch_bicg_pv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_bicg_st<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
-        return launch_bicg_update<T, IT>(ad, n, ss);
+        if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
+        return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
     };
 
     if (o.profile) {
         // every iteration launched directly; each fused SpMV kernel carries a
         // pair of events that the runtime records at its start and end; the
-        // stop (including maxit) is detected by the first kernel of the next
-        // iteration, so maxit + 1 are enqueued
+        // stop at maxit is detected in iteration maxit (CG: its kernel;
+        // BiCGStab: its second kernel), so maxit + 1 iterations are enqueued
         const int per = cg ? 1 : 2;
         const int launches = o.maxit + 1;
         const size_t need = (size_t)2 * per * (size_t)launches;
@@ -262,11 +261,10 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else {
-                HIP_TRY(launch_bicg_pv<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
                 HIP_TRY(launch_bicg_st<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_update<T, IT>(ad, n, s));
             }
             if ((k & 63) == 63 || k + 1 == launches) {
                 HIP_TRY(hipMemcpyAsync(&h->poll[0], &st->done, sizeof(int32_t),

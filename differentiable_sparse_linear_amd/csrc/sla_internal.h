@@ -38,15 +38,14 @@ constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread; p, x, r, M^-1 in LD
 // of one kernel and read by later kernels; fields that a kernel both reads
 // and writes live in two slots selected by iteration parity, and the
 // iteration counter is kept once per kernel role (iter_a read by the first
-// kernel of an iteration, iter_b by the second, iter_c by the third).
+// kernel of an iteration, iter_b by the second).
 struct SolveState {
     double rho[2];    // CG: gamma = r.u ; BiCGStab: rhat.r, by iteration parity
     double alpha[2];  // alpha by iteration parity
-    double omega[2];  // BiCGStab omega by parity
     double bb;        // ||rhs||^2
     double rr;        // ||r||^2 at the stop
     double half_ss;   // BiCGStab ||s||^2 of a half-step exit
-    int32_t iter_a, iter_b, iter_c;  // BiCGStab kernels
+    int32_t iter_a, iter_b;  // BiCGStab kernels
     int32_t iter_p[2];  // CG: iteration of the launch with parity 0 / 1
     int32_t iter;     // completed iterations at the stop
     int32_t done;     // 1 once converged / stopped (relaxed atomic access)
@@ -65,7 +64,8 @@ struct SolveState {
 // slots that it does not read.
 enum : int {
     kCgGA = 0, kCgGA1 = 1, kCgDE = 2, kCgDE1 = 3, kCgRR = 4, kCgRR1 = 5, kCgBB = 6,
-    kBiRV = 0, kBiTS = 1, kBiTT = 2, kBiSS = 3, kBiRHR = 4, kBiRR = 5, kBiBB = 6,
+    kBiRV = 0, kBiTS = 1, kBiTT = 2, kBiSS = 3, kBiRS = 4, kBiRT = 5, kBiBB = 6, kBiRR = 7,
+    kBiRR0 = 1,  // ||r_0||^2 of the init kernel, read by the first bicg_xpv only
 };
 
 // Device-resident arguments of the iteration kernels.  Kernels take a pointer
@@ -297,13 +297,11 @@ hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_pv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
-                          hipStream_t s, const hipEvent_t *ev = nullptr);
+hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
+                           hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
-template <typename T, typename IT>
-hipError_t launch_bicg_update(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
 // shared by both grid solvers: x = 0 when the state asks for it
 template <typename T>
