@@ -252,8 +252,10 @@ constexpr int kBW = kBlockSolveThreads / 64;  // waves per workgroup
 
 // Sum over the workgroup; every thread receives the same, order-fixed total.
 // Wavefront sums go to LDS; after the barrier lane l of every wavefront reads
-// wavefront l's sum and a 16-lane butterfly adds them (the same tree in every
-// wavefront, so every thread gets bitwise the same total).
+// wavefront (l mod 16)'s sum and a 16-lane DPP row sum adds them (the same
+// steps in every row of every wavefront, so every thread gets bitwise the
+// same total).
+static_assert(kBW == 16, "the workgroup sum takes one wavefront sum per lane of a row");
 template <int NR>
 __device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -264,7 +266,7 @@ __device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW])
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = group_sum<kBW>(slots[r][lane & (kBW - 1)]);
+    for (int r = 0; r < NR; ++r) v[r] = row16_sum(slots[r][lane & (kBW - 1)]);
 }
 
 // One row's matrix entries, SLOTS slots (slots past the row repeat its last

@@ -114,17 +114,42 @@ struct IterArgs {
 
 // ---------------------------------------------------------------- helpers
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// v plus the value that the row-local DPP permutation CTRL brings to this
+// lane (both 32-bit halves moved in the VALU, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ double dpp_add(double v) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xf, 0xf, false);
+    return v + __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                                (unsigned)lo));
+}
+
+// Sum over each row of 16 lanes: pairs (quad_perm 1,0,3,2), quads (quad_perm
+// 2,3,0,1), half rows (row_half_mirror), rows (row_mirror).  Each step adds
+// two partial sums, in either order, so every lane of a row ends with the
+// same bits.
+__device__ __forceinline__ double row16_sum(double v) {
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x141>(v);
+    v = dpp_add<0x140>(v);
     return v;
 }
 
-template <int G, typename A>
-__device__ __forceinline__ A group_sum(A v) {
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, G);
-    return v;
+__device__ __forceinline__ double lane_value(double v, int lane) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(unsigned)u, lane);
+    const int hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                            (unsigned)lo));
+}
+
+// Sum over the wavefront, the same bits in every lane: row sums by DPP, then
+// the four row sums (read as uniform values) in a fixed order.
+__device__ __forceinline__ double wave_sum(double v) {
+    v = row16_sum(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // Contiguous tile range of this block's XCD, strided over the XCD's blocks.
