@@ -1,0 +1,113 @@
+"""Which storage form the solver iterations pick, at the edges of the
+diagonal-major form's eligibility (3, 5 or 7 diagonals, the main one in the
+middle, at most 25 % padding), and parity with the oracle in each case.
+
+Banded problems are built here from a list of diagonal offsets: row i stores
+column i + d for every offset d that lands in [0, n).  Symmetric cases take
+A_ij = A_ji = -(1 + sin(min(i, j) + |d|) / 2) off the diagonal and the
+diagonal sum of the row's off-diagonal magnitudes plus 1/2 (strictly
+diagonally dominant, hence SPD): CG with Jacobi.  Nonsymmetric cases scale the
+entries above the diagonal by 0.6 and below by 1.4 (still diagonally
+dominant): BiCGStab, whose adjoint iterates on the transposed pattern (the
+negated offsets).  n = 5000 keeps every solve on the grid kernels.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import FP_TOL, banner, gpu_forward_adjoint, oracle_forward_adjoint, relerr
+
+pytestmark = pytest.mark.gpu
+
+
+def banded(name, n, offsets, symmetric, seed):
+    offsets = sorted(offsets)
+    rows, cols = [], []
+    for d in offsets:
+        i = np.arange(max(0, -d), min(n, n - d))
+        rows.append(i)
+        cols.append(i + d)
+    rows = np.concatenate(rows)
+    cols = np.concatenate(cols)
+    order = np.lexsort((cols, rows))
+    rows, cols = rows[order], cols[order]
+    off = cols != rows
+    v = np.zeros(rows.size)
+    lo = np.minimum(rows, cols)
+    dist = np.abs(cols - rows)
+    v[off] = -(1.0 + 0.5 * np.sin(lo[off] + dist[off]))
+    if not symmetric:
+        v[off & (cols > rows)] *= 0.6
+        v[off & (cols < rows)] *= 1.4
+    diag = np.zeros(n)
+    np.add.at(diag, rows[off], np.abs(v[off]))
+    v[~off] = diag[rows[~off]] + 0.5
+    row_ptr = np.zeros(n + 1, dtype=np.int32)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    b = rng.standard_normal((1, n))
+    xt = rng.uniform(-1.0, 1.0, (1, n))
+    return W.Problem(name, n, row_ptr, cols.astype(np.int32), v[None, :], b, xt,
+                     method="cg" if symmetric else "bicgstab",
+                     precond="jacobi" if symmetric else "none", tol=1e-10, maxit=5000)
+
+
+# (name, offsets, symmetric, the form the iterations read for A)
+CASES = [
+    ("tridiagonal", (-1, 0, 1), True, "diagonal-major"),
+    ("tridiagonal_nonsym", (-1, 0, 1), False, "diagonal-major"),
+    ("five_band", (-70, -1, 0, 1, 70), True, "diagonal-major"),
+    ("five_band_nonsym", (-70, -1, 0, 1, 70), False, "diagonal-major"),
+    ("upper_band", (0, 1, 2), False, "diagonal"),         # main diagonal not in the middle
+    ("four_band", (-2, -1, 0, 1), False, "diagonal"),     # 4 diagonals
+    ("wide_padding", (-4000, -1, 0, 1, 4000), True, "diagonal"),  # padding above 25 %
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_iteration_form_and_parity(hip, case):
+    name, offsets, symmetric, form = case
+    banner(f"forms: {name}")
+    p = banded(name, 5000, offsets, symmetric, seed=len(name))
+    g = gpu_forward_adjoint(hip, p)
+    pat = g["pattern"]
+    assert pat.column_mode() == "diagonal", name
+    assert pat.iteration_form() == form, name
+    if not symmetric:
+        # A^T stores the negated offsets: the same eligibility
+        assert pat.iteration_form(transpose=True) == form, name
+    r, a = oracle_forward_adjoint(p)
+    tol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert g["info"]["status"][0] == 0 and r.status[0] == 0, (name, g["info"])
+    assert g["ainfo"]["status"][0] == 0 and a.status[0] == 0, (name, g["ainfo"])
+    assert relerr(g["x"][0], r.x[0]) <= tol, name
+    assert relerr(g["gv"][0], a.grad_values[0]) <= tol, name
+    assert relerr(g["gb"][0], a.grad_b[0]) <= tol, name
+    assert abs(int(g["info"]["iters"][0]) - int(r.iters[0])) <= max(3, r.iters[0] // 50)
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=[c[0] for c in CASES[:4]])
+def test_diagonal_major_matches_csr_values_bitwise(hip, case):
+    """The same solve and adjoint with the iterations on the caller's CSR
+    values (SLA_CREATE_CSR_VALUES) give bitwise the same results."""
+    import torch
+    name, offsets, symmetric, form = case
+    banner(f"forms bitwise: {name}")
+    p = banded(name, 5000, offsets, symmetric, seed=len(name))
+    outs = []
+    for dmaj in (True, False):
+        rp = torch.from_numpy(p.row_ptr).cuda()
+        col = torch.from_numpy(p.col).cuda()
+        val = torch.from_numpy(p.values).cuda()
+        b = torch.from_numpy(p.b).cuda()
+        xt = torch.from_numpy(p.x_t).cuda()
+        pat = hip.Pattern(rp, col, build_transpose=not symmetric, diagonal_major=dmaj)
+        assert pat.iteration_form() == ("diagonal-major" if dmaj else "diagonal")
+        kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit)
+        x, info = pat.solve(val, b, **kw)
+        gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
+        outs.append([t.cpu().numpy() for t in (x, gv, gb)] + [info["iters"], ainfo["iters"]])
+        pat.close()
+    for u, v in zip(outs[0], outs[1]):
+        assert np.array_equal(np.asarray(u), np.asarray(v)), name
