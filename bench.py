@@ -439,7 +439,10 @@ def bench_product(args, p):
         # values + columns + row pointers once, g, x read, grad_x and
         # grad_values written
         model = p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv
-        kernel = "spmv_perm_kernel+grad_kernel"
+        # A^T x reads A's own rows through its diagonal masks when it has
+        # them, else the transpose map
+        kernel = ("spmv_t_diag_kernel" if pat.column_mode() == "diagonal"
+                  else "spmv_perm_kernel") + "+grad_kernel"
     model *= p.batch
     steps = max(args.steps, 1) * 10
     for _ in range(max(args.warmup, 1)):

@@ -470,8 +470,7 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     if (st == SLA_ERR_DEVICE) return st;
     for (int64_t s0 = 0; s0 < B; s0 += 65535) {
         const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
-        HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col, h->col16,
-                                   gb + s0 * n,
+        HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, gb + s0 * n,
                                    x + s0 * n, gval + s0 * nnz, n, nnz, nb, true, s));
     }
     HIP_TRY(hipStreamSynchronize(s));
@@ -786,6 +785,21 @@ sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, dou
 
 }  // namespace
 
+namespace {
+
+// y = A^T x for `batch` systems: through A's diagonal masks when it has them
+// (no transpose map read), else through the transpose map.
+template <typename T, typename IT>
+hipError_t transposed_product(sla_ctx *h, const T *v, const T *x, T *y, int batch, hipStream_t s) {
+    if (h->ca.mode == kColDiag)
+        return launch_spmv_t_diag<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v, h->nnz, x,
+                                         y, h->n, h->n, batch, s);
+    return launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->ca_t,
+                                   h->perm, v, h->nnz, x, y, h->n, h->n, batch, s);
+}
+
+}  // namespace
+
 extern "C" {
 
 sla_status sla_create(sla_handle *out, int64_t n, int64_t nnz, int64_t batch, int32_t dtype,
@@ -853,9 +867,7 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             const T *x = reinterpret_cast<const T *>(d_x) + s0 * h->n;
             T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
             if (transpose)
-                HIP_TRY((launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t),
-                                                 h->ca_t, h->perm, v, h->nnz, x, y,
-                                                 h->n, h->n, nb, s)));
+                HIP_TRY(transposed_product<T, IT>(h, v, x, y, nb, s));
             else
                 HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->ca,
                                             v, h->nnz, x, y, h->n, h->n, nb, s)));
@@ -880,13 +892,10 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
             const T *v = reinterpret_cast<const T *>(d_values) + s0 * h->nnz;
             const T *gy = reinterpret_cast<const T *>(d_grad_y) + s0 * h->n;
             if (d_grad_x)
-                HIP_TRY((launch_spmv_perm<T, IT>(
-                    h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->ca_t,
-                    h->perm, v, h->nnz, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, h->n,
-                    h->n, nb, s)));
+                HIP_TRY(transposed_product<T, IT>(
+                    h, v, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, nb, s));
             if (d_grad_values)
-                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->col,
-                                            h->col16, gy,
+                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, gy,
                                             reinterpret_cast<const T *>(d_x) + s0 * h->n,
                                             reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz,
                                             h->n, h->nnz, nb, false, s)));

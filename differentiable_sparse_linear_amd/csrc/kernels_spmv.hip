@@ -47,25 +47,77 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
         [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
 }
 
+// y = A^T x for a pattern with per-row diagonal masks, read from A's own
+// rows (no transpose map): row i of A^T holds A[j][i] for j = i - dlt[q],
+// stored when bit q of msk[j] is set, at position rp[j] + (set bits of
+// msk[j] below q).  q runs downwards, so the terms are added in ascending j,
+// the column order of A^T's row.  NDT >= the pattern's diagonal count; all
+// NDT slots are unrolled so every mask and row-pointer load of a row is in
+// flight before its values are gathered.
+template <typename T, typename IT, int NDT>
+__global__ __launch_bounds__(kBlock) void spmv_t_diag_kernel(const IT *__restrict__ rp, ColArgs ca,
+                                                             const T *__restrict__ val,
+                                                             int64_t val_stride,
+                                                             const T *__restrict__ x,
+                                                             T *__restrict__ y, int64_t n,
+                                                             int64_t vec_stride) {
+    const int sys = blockIdx.y;
+    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
+    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
+    const gptr<const uint16_t> msk = glb(ca.msk);
+    const gptr<const IT> rpg = glb(rp);
+    const int nd = ca.nd;
+    int32_t dl[NDT];
+#pragma unroll
+    for (int q = 0; q < NDT; ++q) dl[q] = q < nd ? ca.dlt[q] : 0;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        bool on[NDT];
+        int64_t jj[NDT];
+        IT k[NDT];
+#pragma unroll
+        for (int q = 0; q < NDT; ++q) {
+            const int64_t j = i - dl[q];
+            on[q] = q < nd && j >= 0 && j < n;
+            jj[q] = on[q] ? j : i;
+        }
+#pragma unroll
+        for (int q = 0; q < NDT; ++q) {
+            const uint32_t m = msk[jj[q]];
+            on[q] = on[q] && ((m >> q) & 1u);
+            k[q] = rpg[jj[q]] + (IT)__builtin_popcount(m & ((1u << q) - 1u));
+        }
+        T s = T(0);
+#pragma unroll
+        for (int q = NDT - 1; q >= 0; --q) {
+            if (on[q]) s += v[k[q]] * xs[jj[q]];
+        }
+        ys[i] = s;
+    }
+}
+
 // grad[k] = -lambda[row(k)] * x[col[k]] (NEG; the solve's gradient on the
 // pattern) or g[row(k)] * x[col[k]] (the product's).  Short tiles: each thread marks the
-// tile-local row of its row's entries in LDS, then the entries are written as
-// one coalesced run.  Tiles with long rows: one wavefront per row.
+// tile-local row of its row's entries in LDS (with diagonal masks also their
+// columns, from the mask's set bits), then the entries are written as one
+// coalesced run.  Tiles with long rows: one wavefront per row.
 template <typename T, typename IT, bool NEG, int CM>
-__global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
-                                                      const int32_t *__restrict__ col32,
-                                                      const int16_t *__restrict__ col16,
+__global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ lam,
                                                       const T *__restrict__ x, T *__restrict__ grad,
                                                       int64_t n, int64_t nnz) {
+    constexpr bool kDiag = CM == kColDiag;
     __shared__ IT srp[kTileRows + 1];
     __shared__ T slam[kTileRows];
     __shared__ uint16_t rid[kCap];
+    __shared__ int32_t scol[kDiag ? kCap : 1];
+    __shared__ int32_t dtab[kMaxDiags];
     const int sys = blockIdx.y;
-    ColArgs ca;
-    ca.col = col32;
-    ca.col16 = col16;
     const ColSrc<CM> col = col_src<CM>(ca);
+    if (kDiag && threadIdx.x < kMaxDiags) dtab[threadIdx.x] = ca.dlt[threadIdx.x];
     lam += (int64_t)sys * n;
     x += (int64_t)sys * n;
     grad += (int64_t)sys * nnz;
@@ -84,15 +136,22 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
         const IT base = srp[0];
         const int64_t cnt = (int64_t)(srp[rows] - base);
         if (cnt <= kCap) {
-            if (tid < rows)
-                for (int e = (int)(srp[tid] - base); e < (int)(srp[tid + 1] - base); ++e)
+            if (tid < rows) {
+                uint32_t m = kDiag ? (uint32_t)col.msk[row0 + tid] : 0u;
+                for (int e = (int)(srp[tid] - base); e < (int)(srp[tid + 1] - base); ++e) {
                     rid[e] = (uint16_t)tid;
+                    if (kDiag) {
+                        scol[e] = (int32_t)(row0 + tid) + dtab[__builtin_ctz(m | 0x8000u)];
+                        m &= m - 1u;
+                    }
+                }
+            }
             __syncthreads();
             int32_t c[kEpt];
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
-                if (e < cnt) c[j] = col(base + e, row0);
+                if (e < cnt) c[j] = kDiag ? scol[e] : col(base + e, row0);
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
@@ -106,9 +165,12 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
             const int lane = tid & 63, wave = tid >> 6;
             for (int r = wave; r < rows; r += kWaves) {
                 const T li = slam[r];
-                const IT hi = srp[r + 1];
-                for (IT k = srp[r] + lane; k < hi; k += 64) {
-                    const T g = li * x[col(k, row0)];
+                const IT lo = srp[r], hi = srp[r + 1];
+                const uint32_t mr = kDiag ? (uint32_t)col.msk[row0 + r] : 0u;
+                for (IT k = lo + lane; k < hi; k += 64) {
+                    const int32_t c = kDiag ? (int32_t)(row0 + r) + dtab[nth_bit(mr, (int)(k - lo))]
+                                            : col(k, row0);
+                    const T g = li * x[c];
                     grad[k] = NEG ? -g : g;
                 }
             }
@@ -197,15 +259,30 @@ hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const in
 }
 
 template <typename T, typename IT>
-hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, const T *lam,
-                       const T *x, T *grad, int64_t n, int64_t nnz, int batch, bool neg,
-                       hipStream_t s) {
+hipError_t launch_spmv_t_diag(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
+                              const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
+                              hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_TILE16(col16 != nullptr, if (neg) {
-        grad_kernel<T, IT, true, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n, nnz);
+    if (ca.nd <= 4)
+        spmv_t_diag_kernel<T, IT, 4><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x, y, n,
+                                                             vec_stride);
+    else if (ca.nd <= 8)
+        spmv_t_diag_kernel<T, IT, 8><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x, y, n,
+                                                             vec_stride);
+    else
+        spmv_t_diag_kernel<T, IT, kMaxDiags><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x,
+                                                                     y, n, vec_stride);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
+                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    SLA_DISPATCH_CM(ca.mode, if (neg) {
+        grad_kernel<T, IT, true, kC><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz);
     } else {
-        grad_kernel<T, IT, false, kC><<<grid, kBlock, 0, s>>>(rp, col, col16, lam, x, grad, n,
-                                                             nnz);
+        grad_kernel<T, IT, false, kC><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz);
     });
     return hipGetLastError();
 }
@@ -251,9 +328,11 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
     template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
                                                 const int32_t *, const T *, int64_t, const T *,  \
                                                 T *, int64_t, int64_t, int, hipStream_t);        \
-    template hipError_t launch_grad<T, IT>(const IT *, const int32_t *, const int16_t *,       \
-                                           const T *, const T *, T *, int64_t, int64_t, int,     \
-                                           bool, hipStream_t);  \
+    template hipError_t launch_spmv_t_diag<T, IT>(const IT *, const ColArgs &, const T *,       \
+                                                  int64_t, const T *, T *, int64_t, int64_t,     \
+                                                  int, hipStream_t);                             \
+    template hipError_t launch_grad<T, IT>(const IT *, const ColArgs &, const T *, const T *,   \
+                                           T *, int64_t, int64_t, int, bool, hipStream_t);      \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
                                            hipStream_t);                                         \
     template hipError_t launch_dia_pack<T, IT>(const IT *, const uint16_t *, int, const T *,    \

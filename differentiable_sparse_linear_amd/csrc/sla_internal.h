@@ -294,10 +294,15 @@ template <typename T, typename IT>
 hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
                             int64_t vec_stride, int batch, hipStream_t s);
+// y = A^T x from A's own rows through its diagonal masks (ca.mode == kColDiag)
 template <typename T, typename IT>
-hipError_t launch_grad(const IT *rp, const int32_t *col, const int16_t *col16, const T *lam,
-                       const T *x, T *grad, int64_t n, int64_t nnz, int batch, bool neg,
-                       hipStream_t s);
+hipError_t launch_spmv_t_diag(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
+                              const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
+                              hipStream_t s);
+// the gradient on the pattern; columns from ca as the products read them
+template <typename T, typename IT>
+hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
+                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s);
 template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
 // Diagonal-major copy of one system's CSR values: out[q * n + i] = the entry

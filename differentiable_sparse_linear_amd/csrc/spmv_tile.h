@@ -387,15 +387,6 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         __VA_ARGS__;                                \
     }
 
-#define SLA_DISPATCH_TILE16(c16, ...)               \
-    if (c16) {                                      \
-        constexpr int kC = kColTile16;              \
-        __VA_ARGS__;                                \
-    } else {                                        \
-        constexpr int kC = kColWide;                \
-        __VA_ARGS__;                                \
-    }
-
 #define SLA_DISPATCH_SLOTS(slots, ...)                          \
     switch (slots) {                                            \
         case 4: { constexpr int kS = 4; __VA_ARGS__; } break;   \
