@@ -185,6 +185,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     const int cm = op.it.mode;
     const int slots = op.it_slots;
     const bool dmaj = cm == kColDiaMajor;
+    const bool zw = cg && cg_zwalk(op.it, n);
     T *vec = reinterpret_cast<T *>(h->vec);
     IterArgs<T, IT> a;
     memset(&a, 0, sizeof(a));
@@ -236,7 +237,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, ad, n, k & 1, ss);
+        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, k & 1, ss);
         if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
     };
@@ -257,7 +258,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, ad, n, k & 1, s,
+                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else {

@@ -60,8 +60,8 @@ __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT>
                 x[i] = T(0);
             r[i] = ri;
             rh[i] = ri;
-            rr += (double)ri * (double)ri;
-            bb += (double)bi * (double)bi;
+            rr = fma((double)ri, (double)ri, rr);
+            bb = fma((double)bi, (double)bi, bb);
         }
     }
     double v[2] = {rr, bb};
@@ -186,8 +186,8 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
             }
             pnew[i] = pj(G4<T>{o.s, o.t, o.p, o.v});
             vnew[i] = acc;
-            rv_acc += (double)o.rh * (double)acc;
-            rr_acc += (double)ri * (double)ri;
+            rv_acc = fma((double)o.rh, (double)acc, rv_acc);
+            rr_acc = fma((double)ri, (double)ri, rr_acc);
         },
         pre, post);
     if (!go) return;
@@ -270,11 +270,11 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
             const T si = sk(G2<T>{o.r, o.v});
             s[i] = si;
             tv[i] = acc;
-            ts += (double)acc * (double)si;
-            tt += (double)acc * (double)acc;
-            ss += (double)si * (double)si;
-            rs += (double)o.rh * (double)si;
-            rt += (double)o.rh * (double)acc;
+            ts = fma((double)acc, (double)si, ts);
+            tt = fma((double)acc, (double)acc, tt);
+            ss = fma((double)si, (double)si, ss);
+            rs = fma((double)o.rh, (double)si, rs);
+            rt = fma((double)o.rh, (double)acc, rt);
         },
         pre, post);
     if (!go) return;

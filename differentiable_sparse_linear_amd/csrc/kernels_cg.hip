@@ -95,10 +95,10 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
             u0[i] = ui;
             w0[i] = JAC ? acc * o.c : acc;
             if (!x0) x[i] = T(0);
-            ga += (double)ri * (double)ui;
-            de += (double)acc * (double)ui;
-            rr += (double)ri * (double)ri;
-            bb += (double)o.a * (double)o.a;
+            ga = fma((double)ri, (double)ui, ga);
+            de = fma((double)acc, (double)ui, de);
+            rr = fma((double)ri, (double)ri, rr);
+            bb = fma((double)o.a, (double)o.a, bb);
         },
         NoPre(), NoPost());
     double v[4] = {ga, de, rr, bb};
@@ -114,9 +114,12 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 #ifndef SLA_CG_WAVES
 #define SLA_CG_WAVES 5
 #endif
-template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM>
+// ZW: the z-walk of dia_rows_zw (diagonal-major, seven diagonals, the host
+// has checked that the outermost offset is one round of tiles).
+template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, bool ZW = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
     SolveState *st = A->st;
     if (load_done(st)) return;
     const int it = st->iter_p[PH];
@@ -209,25 +212,38 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto s_of = [&](T w, T sv) -> T { return fmaT(beta, sv, w); };
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
-    const bool go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
-        [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; }, u_of,
-        [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
-        [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
-            const T pi = fmaT(beta, o.p, o.u);
-            const T si = s_of(o.w, o.s);
-            const T uni = fmaT(-alpha, si, o.u);
-            if (PH) x[i] = fmaT(alpha, pi, fmaT(alpha_prev, o.p, o.x));
-            p[i] = pi;
-            sc[i] = si;
-            un[i] = uni;
-            wn[i] = JAC ? acc / aii : acc;
-            const T rni = JAC ? aii * uni : uni;
-            g += (double)rni * (double)uni;
-            d += (double)acc * (double)uni;
-            q += (double)rni * (double)rni;
-        },
-        pre, post);
+    auto gath = [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; };
+    auto row = [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
+        const T pi = fmaT(beta, o.p, o.u);
+        const T si = s_of(o.w, o.s);
+        const T uni = fmaT(-alpha, si, o.u);
+        if (PH) x[i] = fmaT(alpha, pi, fmaT(alpha_prev, o.p, o.x));
+        p[i] = pi;
+        sc[i] = si;
+        un[i] = uni;
+        wn[i] = JAC ? acc / aii : acc;
+        const T rni = JAC ? aii * uni : uni;
+        g = fma((double)rni, (double)uni, g);
+        d = fma((double)acc, (double)uni, d);
+        q = fma((double)rni, (double)rni, q);
+    };
+    bool go;
+    if constexpr (ZW) {
+        __shared__ G3<T> zring[3][kTileRows];
+        go = dia_rows_zw<T>(
+            xcd_tiles(tiles_of(n)), n, col_src<CM>(A->cols), [&](auto k) { return val[k]; }, gath,
+            u_of,
+            [&](int64_t i, const G3<T> &o) {
+                return CgOwn<T>{o.a, o.b, o.c, pprev[i], PH ? x[i] : T(0)};
+            },
+            row, pre, post, zring);
+    } else {
+        go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
+            xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm,
+            [&](auto k) { return val[k]; }, gath, u_of,
+            [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
+            row, pre, post);
+    }
     if (!go) return;
     double v[3] = {g, d, q};
     const int slot[3] = {PH ? kCgGA : kCgGA1, PH ? kCgDE : kCgDE1, PH ? kCgRR : kCgRR1};
@@ -499,6 +515,16 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 
 // ------------------------------------------------------------------ launchers
 
+bool cg_zwalk(const ColArgs &it, int64_t n) {
+    if (it.mode != kColDiaMajor || it.nd != 7) return false;
+    const int64_t nt = tiles_of(n);
+    const int64_t grid = grid_for_tiles(nt);
+    // tiles in rounds of `grid` (xcd_tiles) and the outermost offset exactly
+    // one round of tiles, so that a block's next tile is the next plane
+    return it.off[2] == -1 && it.off[4] == 1 && it.off[0] == -it.off[6] &&
+           (int64_t)it.off[6] == grid * kTileRows && nt >= kRoundsFrom * grid;
+}
+
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s) {
@@ -514,12 +540,15 @@ hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
-                          int ph, hipStream_t s, const hipEvent_t *ev) {
+hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
+                          int64_t n, int ph, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)));
 #define SLA_CG_ITER(J, P)                                                                      \
-    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(                        \
-                                                        cg_iter_kernel<T, IT, J, kS, P, kC>,   \
+    if (zw)                                                                                    \
+        launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, true>, grid,           \
+                           dim3(kBlock), 0, s, ev, a);                                         \
+    else                                                                                       \
+        SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(cg_iter_kernel<T, IT, J, kS, P, kC>,   \
                                                         grid, dim3(kBlock), 0, s, ev, a))
     if (jac) {
         if (ph) {
@@ -596,7 +625,7 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
                                               int64_t, hipStream_t);                            \
-    template hipError_t launch_cg_iter<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
+    template hipError_t launch_cg_iter<T, IT>(int, int, bool, bool, const IterArgs<T, IT> *, \
                                               int64_t, int, hipStream_t, const hipEvent_t *);   \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
 

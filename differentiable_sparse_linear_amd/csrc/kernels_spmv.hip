@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void spmv_t_diag_kernel(const IT *__restric
         T s = T(0);
 #pragma unroll
         for (int q = NDT - 1; q >= 0; --q) {
-            if (on[q]) s += v[k[q]] * xs[jj[q]];
+            if (on[q]) s = fma(v[k[q]], xs[jj[q]], s);
         }
         ys[i] = s;
     }

@@ -319,9 +319,13 @@ hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, Solv
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s);
+// zw: the z-walk variant (diagonal-major, seven diagonals with off[2] = -1,
+// off[4] = 1, off[0] = -off[6] = -kTileRows * grid, tiles in rounds)
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
-                          int ph, hipStream_t s, const hipEvent_t *ev = nullptr);
+hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
+                          int64_t n, int ph, hipStream_t s, const hipEvent_t *ev = nullptr);
+// whether the z-walk applies to an operator form on n rows
+bool cg_zwalk(const ColArgs &it, int64_t n);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>

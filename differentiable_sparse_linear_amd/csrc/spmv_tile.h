@@ -10,9 +10,12 @@
 // other lanes (slots past the row repeat its last entry and are left out of
 // the sum).  For banded and stencil matrices neighbouring rows have
 // neighbouring columns, so each gather instruction touches a few consecutive
-// cache lines.  Each row's sum is formed in entry order; rows longer than
-// SLOTS finish with a plain loop; a tile with more than kCap entries (long
-// rows) is processed one wavefront per row, lanes striding over the row.
+// cache lines.  Each row's sum is formed in entry order, one explicit fused
+// multiply-add per entry (as are the kernels' dot-product partials), so every
+// storage form and code path rounds the same way whatever the compiler would
+// contract on its own; rows longer than SLOTS finish with a plain loop; a tile
+// with more than kCap entries (long rows) is processed one wavefront per row,
+// lanes striding over the row.
 //
 // Pipelining: the next tile's row pointers are loaded while this tile is
 // processed and parked in a second LDS buffer; a row's own vector entries
@@ -210,7 +213,7 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
         const int64_t i = t * kTileRows + tid;
         T s = T(0);
 #pragma unroll
-        for (int q = 0; q < ND; ++q) s += v[q] * cf(g[q]);
+        for (int q = 0; q < ND; ++q) s = fma(v[q], cf(g[q]), s);
         if (i < n) rf(i, s, own, v[d0]);
     };
     int64_t t = tr.first;
@@ -222,6 +225,73 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
     for (t += tr.stride; t < tr.end; t += tr.stride) {
         load(t);
         use(t);
+    }
+    return true;
+}
+
+// Rows of a seven-diagonal operator walked along its outermost offset
+// D = off[6] = -off[0] (a 3D stencil's plane), with off[2] = -1, off[4] = 1.
+// When the tiles go in rounds of gridDim.x and D = gridDim.x * kTileRows, a
+// block's next tile is the plane above its current one, lane for lane.  The
+// block then keeps, per lane, the gathered entries of its column in planes
+// z - 1, z and z + 1 in an LDS ring: the +D gathers of plane z are plane
+// z + 1's own entries, so every plane's entries are read from memory once per
+// launch; the -D, own and (inside the tile) +-1 gathers come from the ring,
+// the other gathers from memory.  ofz(i, g) builds a row's own inputs from
+// its gathered entries g.  The terms and their order are those of dia_rows,
+// so the sums are bitwise the same.
+template <typename T, typename VF, typename GF, typename CF, typename OF, typename RF,
+          typename PRE, typename POST, typename G>
+__device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
+                                            const ColSrc<kColDiaMajor> &col, VF vf, GF gf, CF cf,
+                                            OF ofz, RF rf, PRE pre, POST post,
+                                            G (*ring)[kTileRows]) {
+    constexpr int ND = 7, d0 = 3;
+    const int tid = threadIdx.x;
+    auto row_of = [&](int64_t t) -> int64_t {
+        const int64_t row0 = t * kTileRows;
+        const int64_t left = n - row0;
+        return row0 + (tid < left ? tid : left - 1);
+    };
+    auto clampc = [&](int64_t c) -> int32_t {
+        return (int32_t)(c < 0 ? 0 : (c >= n ? n - 1 : c));
+    };
+    int prev = 2, cur = 0, next = 1;
+    int64_t t = tr.first;
+    if (t < tr.end) {
+        ring[prev][tid] = G{};  // the first plane's -D neighbours are padding
+        ring[cur][tid] = gf((int32_t)row_of(t));
+    }
+    pre();
+    __syncthreads();
+    if (!post()) return false;
+    for (; t < tr.end; t += tr.stride) {
+        const int64_t i = row_of(t);
+        T v[ND];
+        G g[ND];
+#pragma unroll
+        for (int q = 0; q < ND; ++q) v[q] = vf((int64_t)q * n + i);
+        g[6] = gf(clampc(i + col.off[6]));
+        g[1] = gf(clampc(i + col.off[1]));
+        g[5] = gf(clampc(i + col.off[5]));
+        g[2] = tid > 0 ? ring[cur][tid - 1] : gf(clampc(i - 1));
+        g[4] = tid < kTileRows - 1 ? ring[cur][tid + 1] : gf(clampc(i + 1));
+        g[0] = ring[prev][tid];
+        g[3] = ring[cur][tid];
+        const auto own = ofz(i, g[3]);
+        ring[next][tid] = g[6];
+        T s = T(0);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) s = fma(v[q], cf(g[q]), s);
+        const int64_t r = t * kTileRows + tid;
+        if (r < n) rf(r, s, own, v[d0]);
+        // the next plane's ring slot is complete, and this plane's reads of
+        // the slot about to be overwritten are done
+        __syncthreads();
+        const int o = prev;
+        prev = cur;
+        cur = next;
+        next = o;
     }
     return true;
 }
@@ -335,14 +405,14 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                     }
 #pragma unroll
                     for (int k = 0; k < R; ++k) {
-                        const T term = w[k] * cf(g[k]);
-                        s = h + k < len ? s + term : s;
+                        const T sk = fma(w[k], cf(g[k]), s);
+                        s = h + k < len ? sk : s;
                     }
                 }
                 for (int k = SLOTS; k < len; ++k) {
                     const int32_t c = kDiag ? me32 + sm.dtab[nth_bit(mk, k)] : sm.col[lo + k];
                     if (!kDiag) below += c < me32 ? 1 : 0;
-                    s += sm.val[lo + k] * cf(gf(c));
+                    s = fma(sm.val[lo + k], cf(gf(c)), s);
                 }
                 rf(row0 + tid, s, own, sm.val[lo + (below < lastk ? below : lastk)]);
             }
@@ -359,7 +429,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                     const int32_t c = kDiag ? (int32_t)row + sm.dtab[nth_bit(mr, (int)(k - cr[r]))]
                                             : col(k, row0);
                     const T v = vf(k);
-                    s += v * cf(gf(c));
+                    s = fma(v, cf(gf(c)), s);
                     if (c == row) pd[r] = v;  // one lane: the diagonal is stored once
                 }
                 s = wave_sum_t(s);

@@ -111,3 +111,74 @@ def test_diagonal_major_matches_csr_values_bitwise(hip, case):
         pat.close()
     for u, v in zip(outs[0], outs[1]):
         assert np.array_equal(np.asarray(u), np.asarray(v)), name
+
+
+def zwalk_problem(Z=16, seed=21):
+    """Lognormal-kappa diffusion on a 512 x 512 x Z grid: seven diagonals
+    with offsets 0, +-1, +-512, +-262144, and 262144 rows = 1024 tiles of 256
+    rows per plane -- the case where the CG kernel walks each block's column
+    along z with the plane above and below in LDS (tiles go in rounds of 1024
+    once there are 16 rounds, Z >= 16)."""
+    rng = np.random.default_rng(seed)
+    dims = (512, 512, Z)
+    n = 512 * 512 * Z
+    kap = np.exp(rng.standard_normal(n))
+    rp, col, val = W.varcoef_diffusion(dims, kap)
+    b = rng.standard_normal(n)[None, :]
+    xt = rng.uniform(-1.0, 1.0, n)[None, :]
+    return W.Problem(f"diffusion_512x512x{Z}", n, rp, col, val, b, xt, method="cg",
+                     precond="jacobi", tol=1e-10, maxit=1000)
+
+
+def test_zwalk_conditions_hold():
+    """The pattern of zwalk_problem meets the z-walk's conditions (the rule
+    the library applies at launch, restated): 7 diagonals with off[2] = -1,
+    off[4] = 1 and off[6] = -off[0] = 1024 * 256, and at least 16 rounds of
+    1024 tiles."""
+    p = zwalk_problem()
+    rows = np.repeat(np.arange(p.n, dtype=np.int64), np.diff(p.row_ptr))
+    off = np.unique(p.col.astype(np.int64) - rows)
+    assert list(off) == [-262144, -512, -1, 0, 1, 512, 262144]
+    assert (p.n + 255) // 256 >= 16 * 1024
+
+
+def test_zwalk_matches_oracle_iterates(hip):
+    """Fixed iteration counts (even and odd stops) against the oracle's
+    iterates, forward and adjoint."""
+    banner("z-walk: fixed iterations")
+    p = zwalk_problem()
+    for k in (1, 6, 7):
+        g = gpu_forward_adjoint(hip, p, maxit=k)
+        assert g["pattern"].iteration_form() == "diagonal-major"
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert g["info"]["iters"][0] == k == r.iters[0]
+        assert relerr(g["x"][0], r.x[0]) <= 1e-12, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= 1e-12, k
+        assert relerr(g["gv"][0], a.grad_values[0]) <= 1e-12, k
+
+
+def test_zwalk_equals_csr_value_iterations_bitwise(hip):
+    """A converged forward + adjoint with the z-walk equals, bit for bit, the
+    same solve on the caller's CSR values (no diagonal-major form, no
+    z-walk)."""
+    import torch
+    banner("z-walk: bitwise")
+    p = zwalk_problem()
+    outs = []
+    for dmaj in (True, False):
+        rp = torch.from_numpy(p.row_ptr).cuda()
+        col = torch.from_numpy(p.col).cuda()
+        val = torch.from_numpy(p.values).cuda()
+        b = torch.from_numpy(p.b).cuda()
+        xt = torch.from_numpy(p.x_t).cuda()
+        pat = hip.Pattern(rp, col, diagonal_major=dmaj)
+        kw = dict(method="cg", precond="jacobi", tol=1e-10, maxit=1000)
+        x, info = pat.solve(val, b, **kw)
+        gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
+        assert info["status"][0] == 0 and ainfo["status"][0] == 0
+        outs.append([t.cpu().numpy() for t in (x, gv, gb)] + [info["iters"], ainfo["iters"]])
+        pat.close()
+        del rp, col, val, b, xt, x, gv, gb
+        torch.cuda.empty_cache()
+    for u, v in zip(outs[0], outs[1]):
+        assert np.array_equal(np.asarray(u), np.asarray(v))
