@@ -213,15 +213,25 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
     auto gath = [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; };
+    // The z-walk runs on grids far beyond the Infinity Cache: there the
+    // values, p, x and the vectors written here are touched once per
+    // iteration, so they stream with non-temporal hints and leave L2 to the
+    // plane's +-N neighbours.
+    auto put = [&](gptr<T> v, int64_t i, T a) {
+        if constexpr (ZW)
+            __builtin_nontemporal_store(a, &v[i]);
+        else
+            v[i] = a;
+    };
     auto row = [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
         const T pi = fmaT(beta, o.p, o.u);
         const T si = s_of(o.w, o.s);
         const T uni = fmaT(-alpha, si, o.u);
-        if (PH) x[i] = fmaT(alpha, pi, fmaT(alpha_prev, o.p, o.x));
-        p[i] = pi;
-        sc[i] = si;
-        un[i] = uni;
-        wn[i] = JAC ? acc / aii : acc;
+        if (PH) put(x, i, fmaT(alpha, pi, fmaT(alpha_prev, o.p, o.x)));
+        put(p, i, pi);
+        put(sc, i, si);
+        put(un, i, uni);
+        put(wn, i, JAC ? acc / aii : acc);
         const T rni = JAC ? aii * uni : uni;
         g = fma((double)rni, (double)uni, g);
         d = fma((double)acc, (double)uni, d);
@@ -231,10 +241,11 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     if constexpr (ZW) {
         __shared__ G3<T> zring[3][kTileRows];
         go = dia_rows_zw<T>(
-            xcd_tiles(tiles_of(n)), n, col_src<CM>(A->cols), [&](auto k) { return val[k]; }, gath,
-            u_of,
+            xcd_tiles(tiles_of(n)), n, col_src<CM>(A->cols),
+            [&](auto k) { return __builtin_nontemporal_load(&val[k]); }, gath, u_of,
             [&](int64_t i, const G3<T> &o) {
-                return CgOwn<T>{o.a, o.b, o.c, pprev[i], PH ? x[i] : T(0)};
+                return CgOwn<T>{o.a, o.b, o.c, __builtin_nontemporal_load(&pprev[i]),
+                                PH ? __builtin_nontemporal_load(&x[i]) : T(0)};
             },
             row, pre, post, zring);
     } else {
