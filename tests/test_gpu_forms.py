@@ -157,13 +157,18 @@ def test_zwalk_matches_oracle_iterates(hip):
         assert relerr(g["gv"][0], a.grad_values[0]) <= 1e-12, k
 
 
-def test_zwalk_equals_csr_value_iterations_bitwise(hip):
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_zwalk_equals_csr_value_iterations_bitwise(hip, dtype):
     """A converged forward + adjoint with the z-walk equals, bit for bit, the
     same solve on the caller's CSR values (no diagonal-major form, no
-    z-walk)."""
+    z-walk), in fp64 (tol 1e-10) and fp32 (tol 1e-5)."""
     import torch
-    banner("z-walk: bitwise")
+    banner(f"z-walk: bitwise {np.dtype(dtype).name}")
     p = zwalk_problem()
+    tol = 1e-10
+    if dtype == np.float32:
+        p = p.astype(np.float32)
+        tol = 1e-5
     outs = []
     for dmaj in (True, False):
         rp = torch.from_numpy(p.row_ptr).cuda()
@@ -171,8 +176,9 @@ def test_zwalk_equals_csr_value_iterations_bitwise(hip):
         val = torch.from_numpy(p.values).cuda()
         b = torch.from_numpy(p.b).cuda()
         xt = torch.from_numpy(p.x_t).cuda()
-        pat = hip.Pattern(rp, col, diagonal_major=dmaj)
-        kw = dict(method="cg", precond="jacobi", tol=1e-10, maxit=1000)
+        pat = hip.Pattern(rp, col, dtype=torch.from_numpy(p.values[:1, :1]).dtype,
+                          diagonal_major=dmaj)
+        kw = dict(method="cg", precond="jacobi", tol=tol, maxit=1000)
         x, info = pat.solve(val, b, **kw)
         gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
         assert info["status"][0] == 0 and ainfo["status"][0] == 0
