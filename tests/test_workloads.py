@@ -18,7 +18,7 @@ def test_sizes(k, n, nnz):
 
 
 def test_config5_counts_and_index_type():
-    # full 512^3 is built on the GPU machine; here check the count law and the
+    # the full 512^3 pattern is built by the GPU tests; here check the count law and the
     # int64 row_ptr on a scaled copy with the same recipe
     assert int(W._grid_counts((512, 512, 512)).sum(dtype=np.int64)) == 937_951_232
     p = W.config(5, size=12)
