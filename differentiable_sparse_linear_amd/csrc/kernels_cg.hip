@@ -339,7 +339,10 @@ __device__ __forceinline__ T block_row_dot(const T (&v)[SLOTS], CF colf, gptr<co
 // SLOTS slots per row, p gathered from LDS (neighbouring rows gather
 // neighbouring LDS words), entry-order sums; rows longer than SLOTS finish
 // with a loop.
-template <typename T, typename IT, int RPT, int SLOTS, bool RESIDENT>
+// FULL: n == RPT * kBlockSolveThreads, every owned row exists, so the row
+// loops carry no guard (a guard is a branch, and the compiler does not move
+// the next row's LDS accesses above it).
+template <typename T, typename IT, int RPT, int SLOTS, bool RESIDENT, bool FULL>
 __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgParams P) {
     extern __shared__ unsigned char lds_raw[];
     const int64_t n = P.n, nnz = P.nnz;
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     const gptr<const int32_t> col = glb(P.col);
     SolveState *st = P.st + sys;
     auto row_of = [&](int j) -> int { return tid + j * kBlockSolveThreads; };
+    auto owned = [&](int i) -> bool { return FULL || i < n; };
     constexpr int MR = RESIDENT ? RPT : 1;
     constexpr int PC = (SLOTS + 1) / 2;
     constexpr int SR = RESIDENT ? 1 : RPT;
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
         const int i = row_of(j);
         int l = 0, ln = 0;
         qr[j] = T(0);
-        if (i < n) {
+        if (owned(i)) {
             l = (int)rp[i];
             ln = (int)(rp[i + 1] - rp[i]);
             const T x0 = P.use_x0 ? x[i] : T(0);
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int i = row_of(j);
-        if (i < n) {
+        if (owned(i)) {
             const T bi = b[i];
             const T ri = P.use_x0 ? bi - qr[j] : bi;
             rs[i] = ri;
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int i = row_of(j);
-        if (i < n) ps[i] = ds[i] * rs[i];  // p_0 = z_0
+        if (owned(i)) ps[i] = ds[i] * rs[i];  // p_0 = z_0
     }
     const int any_bad = __syncthreads_or(bad);
     double rho = r0[0], rnorm2 = r0[1];
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
-                if (i < n) pq[0] += (double)ps[i] * (double)qr[j];
+                if (owned(i)) pq[0] += (double)ps[i] * (double)qr[j];
             }
             block_sum<1>(pq, slots[slot]);  // every gather of p is done
             slot = (slot + 1) & 3;
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
-                if (i < n) {
+                if (owned(i)) {
                     xs[i] = fmaT(alpha, ps[i], xs[i]);
                     const T ri = fmaT(-alpha, qr[j], rs[i]);
                     rs[i] = ri;
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
-                if (i < n) ps[i] = fmaT(beta, ps[i], ds[i] * rs[i]);
+                if (owned(i)) ps[i] = fmaT(beta, ps[i], ds[i] * rs[i]);
             }
             __syncthreads();  // the new p is complete before the next product
         }
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int i = row_of(j);
-        if (i < n) x[i] = zero_x ? T(0) : xs[i];
+        if (owned(i)) x[i] = zero_x ? T(0) : xs[i];
     }
     if (threadIdx.x == 0) {
         st->iter = it;
@@ -593,11 +597,14 @@ hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipSt
     const int rpt = (int)((p.n + kBlockSolveThreads - 1) / kBlockSolveThreads);
     const bool fits = max_len <= 8;
 #define SLA_BLOCK_LAUNCH(R, S)                                                                     \
-    if (fits && block_resident<T, R, S>())                                                         \
-        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>()>                                    \
+    if (fits && block_resident<T, R, S>() && p.n == R * kBlockSolveThreads)                       \
+        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>(), true>                              \
+            <<<batch, kBlockSolveThreads, lds, s>>>(p);                                            \
+    else if (fits && block_resident<T, R, S>())                                                    \
+        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>(), false>                             \
             <<<batch, kBlockSolveThreads, lds, s>>>(p);                                            \
     else                                                                                           \
-        block_cg_kernel<T, IT, R, S, false><<<batch, kBlockSolveThreads, lds, s>>>(p)
+        block_cg_kernel<T, IT, R, S, false, false><<<batch, kBlockSolveThreads, lds, s>>>(p)
 #define SLA_BLOCK_ROWS(R)                     \
     if (max_len <= 4) {                       \
         SLA_BLOCK_LAUNCH(R, 4);               \
