@@ -241,7 +241,7 @@ def _check_solve(p, g, r, a, systems=None):
 
 @pytest.mark.parametrize("case", ["cfg1", "cfg1_grid", "cfg2_20", "cfg2_31_ragged", "cfg3_small64",
                                   "cfg3_small32", "cfg4_48", "cfg4_33_ragged", "cfg2_24_fp32",
-                                  "cfg4_40_fp32"])
+                                  "cfg4_40_fp32", "cfg5_20_fp32", "cfg4_40_i64"])
 def test_solve_and_adjoint_small(hip, case):
     banner(f"solve {case}")
     kw = {}
@@ -259,6 +259,14 @@ def test_solve_and_adjoint_small(hip, case):
     elif case == "cfg4_40_fp32":
         p = W.config(4, size=40).astype(np.float32)
         p.tol = 1e-5
+    elif case == "cfg5_20_fp32":
+        # int64 row_ptr with fp32 values on the grid kernels (n = 8000)
+        p = W.config(5, size=20).astype(np.float32)
+        p.tol = 1e-5
+    elif case == "cfg4_40_i64":
+        # BiCGStab and its transpose map with an int64 row_ptr
+        p = W.config(4, size=40)
+        p.row_ptr = p.row_ptr.astype(np.int64)
     elif case == "cfg2_31_ragged":
         p = W.config(2, size=31)
     elif case == "cfg3_small64":
