@@ -356,7 +356,10 @@ def test_zero_rhs_and_zero_maxit(hip):
 
 def test_initial_guess(hip):
     banner("initial guess")
-    for p, kw in ((W.config(2, size=16), {}), (W.config(1), {}), (W.config(4, size=24), {})):
+    # (config 2 at 16^3 and config 1 run on the one-workgroup solver, config 2
+    # at 20^3 on the grid kernels with the diagonal-major values)
+    for p, kw in ((W.config(2, size=16), {}), (W.config(2, size=20), {}), (W.config(1), {}),
+                  (W.config(4, size=24), {})):
         d = to_dev(p)
         pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
         x, info = pat.solve(d["val"], d["b"], tol=1e-12, maxit=5000, method=p.method,
