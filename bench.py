@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
     ap.add_argument("--size", type=int, default=None, help="grid edge override (scaled copy)")
+    ap.add_argument("--fp32", action="store_true",
+                    help="fp32 values and vectors (dot products in fp64), tol 1e-5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph-chunk", type=int, default=0)
     ap.add_argument("--kernel-only", type=int, default=0,
@@ -174,7 +176,14 @@ def read_traffic(kernel, workload, sha):
 
 def load_problem(args):
     import workloads as W
-    return W.config(args.workload, size=args.size)
+    if not getattr(args, "fp32", False):
+        return W.config(args.workload, size=args.size)
+    if args.workload == 3:
+        return W.config(3, size=args.size, dtype=np.float32)
+    p = W.config(args.workload, size=args.size).astype(np.float32)
+    p.tol = 1e-5
+    p.name += "_fp32"
+    return p
 
 
 # ------------------------------------------------------------------ summaries
