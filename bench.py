@@ -210,7 +210,7 @@ def _counter_pass(d, short_names):
             copies.append(v)
     if not vals or not copies:
         raise SystemExit(f"{d}: dominant kernel or calibration copy not found")
-    # launches enqueued after the stop return at entry and read a few bytes
+    # launches enqueued after the stop end at their first barrier and read a few bytes
     top = max(vals)
     active = [v for v in vals if v >= 0.01 * top]
     return sum(active) / len(active), len(active), len(vals), max(copies)
@@ -300,14 +300,14 @@ def summarize_trace(args):
             durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     if durs:
         top = max(durs)
-        # launches enqueued after the stop return at entry (a few microseconds)
+        # launches enqueued after the stop end at their first barrier (a few microseconds)
         active = [d for d in durs if d >= 0.25 * top]
         avg = sum(active) / len(active)
         out += [
             "",
             f"kernel: {kernel}",
             f"dispatches: {len(durs)}",
-            f"dispatches_active: {len(active)} (the others returned at entry after the stop)",
+            f"dispatches_active: {len(active)} (the others ended at their first barrier after the stop)",
             f"avg_us_all: {sum(durs) / len(durs):.2f}",
             f"avg_us_active: {avg:.2f}",
             f"algorithmic_bytes_per_launch: {kbytes}",

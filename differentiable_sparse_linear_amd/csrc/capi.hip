@@ -7,8 +7,12 @@
 //    system, a single launch for the whole batch;
 //  * larger systems run the grid kernels; K iterations are captured once in a
 //    HIP graph that reads its arguments from a device block, every kernel
-//    returns at entry once the device-side `done` flag is set, and the host
-//    keeps one replay in flight while it polls the flag of the previous one.
+//    ends at its first barrier once the device-side `done` flag is set, and
+//    the host keeps one replay in flight while it polls the flag of the
+//    previous one;
+//  * CG on a batch of larger systems advances a group of them per launch
+//    (the y dimension of the grid), as many as fit kGroupRows rows of
+//    workspace, and polls the count of the group's stopped systems.
 // Nothing is allocated after sla_create (memory is O(n + nnz) whatever the
 // iteration count -- Methodology section 2, complexity bullet).
 #include <math.h>
@@ -29,6 +33,10 @@ thread_local hipError_t g_last_error = hipSuccess;
 
 constexpr int kNumVec = 11;  // r z q rh s t p0 p1 v0 v1 dinv
 constexpr int kDefaultChunk = 16;
+// Rows of the systems that one grid CG launch advances together: about
+// 2M rows keep a launch's traffic (~190 bytes per row and iteration) two
+// orders of magnitude above the launch overhead; the workspace grows with it.
+constexpr int64_t kGroupRows = (int64_t)1 << 21;
 
 struct GraphEntry {
     int key = -1;
@@ -46,7 +54,7 @@ struct sla_ctx {
     const int32_t *col = nullptr;
     ColArgs ca, ca_t;            // where the products read the columns of A, A^T
     ColArgs ia, ia_t;            // the form the solver iterations read for A, A^T
-    void *dia = nullptr;         // diagonal-major values of one system, or null
+    void *dia = nullptr;         // diagonal-major values [gbatch][nd][n], or null
     int32_t *dlt = nullptr;      // [2][kMaxDiags] diagonal offsets of A, A^T
     uint16_t *msk = nullptr;     // per-row diagonal masks of A, or null
     uint16_t *msk_t = nullptr;   // the same for A^T
@@ -62,11 +70,13 @@ struct sla_ctx {
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
     int it_slots = 8, it_slots_t = 8;  // slots (or diagonals) of the iteration form
-    void *vec = nullptr;
+    int64_t gbatch = 1;          // systems per grid CG launch
+    void *vec = nullptr;         // [kNumVec][gbatch][n]
     SolveState *st = nullptr;
-    double *part = nullptr;
-    void *args_dev = nullptr;
-    void *args_host = nullptr;   // pinned
+    double *part = nullptr;      // [gbatch][kPartStride]
+    int32_t *ndone = nullptr;    // stopped systems of the running launch group
+    void *args_dev = nullptr;    // [gbatch] IterArgs, one per system of a launch group
+    void *args_host = nullptr;   // pinned staging copy of args_dev
     int32_t *flag = nullptr;
     int32_t *poll = nullptr;     // pinned [2]
     SolveState *st_host = nullptr;  // pinned [batch]
@@ -133,6 +143,7 @@ void release(sla_ctx *h) {
     (void)hipFree(h->vec);
     (void)hipFree(h->st);
     (void)hipFree(h->part);
+    (void)hipFree(h->ndone);
     (void)hipFree(h->args_dev);
     (void)hipFree(h->flag);
     if (h->args_host) (void)hipHostFree(h->args_host);
@@ -173,20 +184,23 @@ struct Operator {
     int it_slots;
 };
 
-// One system on the grid path: fill the argument block, run init, then
-// replay/launch iteration chunks until the device reports done.
+// nsys consecutive systems on the grid path (nsys <= gbatch; 1 for
+// BiCGStab and in profile mode): fill the argument block, run init, then
+// replay/launch iteration chunks until the device reports every system done.
 template <typename T, typename IT>
-sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T *b, T *x,
-                          SolveState *st, const sla_solve_opts &o, hipStream_t s,
-                          double *prof_ms, int64_t *prof_launches) {
-    const int64_t n = h->n;
+sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const T *b, T *x,
+                            SolveState *st, int nsys, const sla_solve_opts &o, hipStream_t s,
+                            double *prof_ms, int64_t *prof_launches) {
+    const int64_t n = h->n, nnz = h->nnz, G = h->gbatch;
     const bool cg = o.method == SLA_CG;
     const bool jac = cg && o.precond == SLA_PRECOND_JACOBI;
     const int cm = op.it.mode;
     const int slots = op.it_slots;
     const bool dmaj = cm == kColDiaMajor;
     const bool zw = cg && cg_zwalk(op.it, n);
+    // vector v of system j of the group: vec + (v * G + j) * n
     T *vec = reinterpret_cast<T *>(h->vec);
+    auto vp = [&](int v) { return vec + (int64_t)v * G * n; };
     IterArgs<T, IT> a;
     memset(&a, 0, sizeof(a));
     a.val = dmaj ? reinterpret_cast<const T *>(h->dia) : val;
@@ -194,50 +208,78 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
     a.cols = op.it;
     a.x = x;
     a.b = b;
-    a.r = vec + 0 * n;
-    a.z = vec + 1 * n;
-    a.q = vec + 2 * n;
-    a.rh = vec + 3 * n;
-    a.s = vec + 4 * n;
-    a.t = vec + 5 * n;
-    a.p[0] = vec + 6 * n;
-    a.p[1] = vec + 7 * n;
-    a.v[0] = vec + 8 * n;
-    a.v[1] = vec + 9 * n;
-    a.dinv = vec + 10 * n;
+    a.r = vp(0);
+    a.z = vp(1);
+    a.q = vp(2);
+    a.rh = vp(3);
+    a.s = vp(4);
+    a.t = vp(5);
+    a.p[0] = vp(6);
+    a.p[1] = vp(7);
+    a.v[0] = vp(8);
+    a.v[1] = vp(9);
+    a.dinv = vp(10);
     a.st = st;
     a.part = h->part;
+    a.ndone = h->ndone;
     a.n = n;
     a.tol = o.tol;
     a.maxit = o.maxit;
     a.use_x0 = o.use_x0;
-    // the previous call has completed (every call ends with a sync), so the
-    // pinned staging block is free to rewrite
-    memcpy(h->args_host, &a, sizeof(a));
+    // one argument block per system of the group, each pointing at its own
+    // data: values vstride apart, vectors n apart, state and partial sums of
+    // its own.  The previous group's copy of the pinned staging blocks has
+    // completed (the host waited for a chunk launched after it), so they are
+    // free to rewrite.
+    const int64_t vstride = dmaj ? (int64_t)op.it.nd * n : nnz;
+    IterArgs<T, IT> *ah = reinterpret_cast<IterArgs<T, IT> *>(h->args_host);
+    for (int j = 0; j < nsys; ++j) {
+        IterArgs<T, IT> e = a;
+        const int64_t o = (int64_t)j * n;
+        e.val += j * vstride;
+        e.x += o;
+        e.b += o;
+        e.dinv += o;
+        e.r += o;
+        e.z += o;
+        e.q += o;
+        e.rh += o;
+        e.s += o;
+        e.t += o;
+        for (int k = 0; k < 2; ++k) {
+            e.p[k] += o;
+            e.v[k] += o;
+        }
+        e.st += j;
+        e.part += (int64_t)j * kPartStride;
+        ah[j] = e;
+    }
     const IterArgs<T, IT> *ad = reinterpret_cast<const IterArgs<T, IT> *>(h->args_dev);
-    HIP_TRY(hipMemcpyAsync(h->args_dev, h->args_host, sizeof(a), hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState), s));
+    HIP_TRY(hipMemcpyAsync(h->args_dev, h->args_host, sizeof(a) * nsys, hipMemcpyHostToDevice,
+                           s));
+    HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState) * nsys, s));
+    HIP_TRY(hipMemsetAsync(h->ndone, 0, sizeof(int32_t), s));
     if (dmaj)
-        HIP_TRY(launch_dia_pack<T, IT>(a.rp, op.cols.msk, op.it.nd, val,
-                                       reinterpret_cast<T *>(h->dia), n, s));
-    if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, vec + 10 * n,
-                                        n, st, s));
+        HIP_TRY(launch_dia_pack<T, IT>(a.rp, op.cols.msk, op.it.nd, val, nnz,
+                                       reinterpret_cast<T *>(h->dia), n, nsys, s));
+    if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, nnz, vp(10),
+                                        n, st, nsys, s));
     // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
     // reads it always, so it is zeroed when there is no initial guess
     if (o.use_x0)
-        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, 0, x, cg ? a.t : a.q, n, 0, 1,
-                                   s));
+        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, x, cg ? a.t : a.q, n, n,
+                                   nsys, s));
     else if (cg)
-        HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n, s));
+        HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n * nsys, s));
     if (cg)
-        HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, s));
+        HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, nsys, s));
     else
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
-        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, k & 1, ss);
+        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, nsys, k & 1, ss);
         if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
     };
@@ -258,7 +300,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
             if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, k & 1, s,
+                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, 1, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else {
@@ -268,10 +310,10 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
                 ev += 2;
             }
             if ((k & 63) == 63 || k + 1 == launches) {
-                HIP_TRY(hipMemcpyAsync(&h->poll[0], &st->done, sizeof(int32_t),
+                HIP_TRY(hipMemcpyAsync(&h->poll[0], h->ndone, sizeof(int32_t),
                                        hipMemcpyDeviceToHost, s));
                 HIP_TRY(hipStreamSynchronize(s));
-                if (h->poll[0]) break;
+                if (h->poll[0] >= nsys) break;
             }
         }
         SolveState hs;
@@ -299,7 +341,7 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
         if (cg && (chunk & 1)) ++chunk;
         hipGraphExec_t exec = nullptr;
         if (o.graph_chunk >= 0) {
-            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0);
+            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0) + 8 * nsys;
             GraphEntry *slot = nullptr;
             for (auto &g : h->graphs)
                 if (g.key == key && g.chunk == chunk) slot = &g;
@@ -338,18 +380,18 @@ sla_status grid_solve_one(sla_ctx *h, const Operator &op, const T *val, const T 
                 } else {
                     for (int k = 0; k < chunk; ++k) HIP_TRY(one_iter(s, k));
                 }
-                HIP_TRY(hipMemcpyAsync(&h->poll[c & 1], &st->done, sizeof(int32_t),
+                HIP_TRY(hipMemcpyAsync(&h->poll[c & 1], h->ndone, sizeof(int32_t),
                                        hipMemcpyDeviceToHost, s));
                 HIP_TRY(hipEventRecord(h->ev[c & 1], s));
             }
             if (c >= 1) {
                 HIP_TRY(hipEventSynchronize(h->ev[(c - 1) & 1]));
-                if (h->poll[(c - 1) & 1]) break;
+                if (h->poll[(c - 1) & 1] >= nsys) break;
             }
         }
     }
-    if (cg) HIP_TRY(launch_cg_lag<T>(st, a.p[0], x, n, s));
-    if (o.use_x0) HIP_TRY(launch_zero_if<T>(st, x, n, s));
+    if (cg) HIP_TRY(launch_cg_lag<T>(st, a.p[0], x, n, nsys, s));
+    if (o.use_x0) HIP_TRY(launch_zero_if<T>(st, x, n, nsys, s));
     return SLA_OK;
 }
 
@@ -386,9 +428,12 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
             HIP_TRY(launch_block_cg<T, IT>(h->max_len, q, nb, s));
         }
     } else {
-        for (int64_t sys = 0; sys < B; ++sys) {
-            sla_status r = grid_solve_one<T, IT>(h, op, val + sys * nnz, b + sys * n, x + sys * n,
-                                                 h->st + sys, o, s, &prof_ms, &prof_launches);
+        const int64_t G = cg && !o.profile ? std::min(h->gbatch, B) : 1;
+        for (int64_t s0 = 0; s0 < B; s0 += G) {
+            const int nsys = (int)std::min(G, B - s0);
+            sla_status r = grid_solve_group<T, IT>(h, op, val + s0 * nnz, b + s0 * n, x + s0 * n,
+                                                   h->st + s0, nsys, o, s, &prof_ms,
+                                                   &prof_launches);
             if (r != SLA_OK) return r;
         }
     }
@@ -571,17 +616,17 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     // diagonals with the main one in the middle (nearest-neighbour stencils
     // in 1, 2 and 3 dimensions) whose padding -- the slots of boundary rows
     // that lack a diagonal -- stays within a quarter of the stored entries;
-    // one system's copy is kept.
+    // one copy per system of a launch group is kept.
     h->ia = h->ca;
     h->it_slots = h->slots;
     h->ia_t = h->ca_t;
     h->it_slots_t = h->slots_t;
+    int nd = 0;
     if (dmajor) {
         auto fits = [&](const ColArgs &c) {
             return c.mode == kColDiag && (c.nd == 3 || c.nd == 5 || c.nd == 7) &&
                    c.nneg == c.nd / 2 && (int64_t)c.nd * n <= nnz + nnz / 4;
         };
-        int nd = 0;
         if (fits(h->ca)) {
             h->ia.mode = kColDiaMajor;
             h->it_slots = nd = h->ca.nd;
@@ -591,17 +636,23 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
             h->it_slots_t = h->ca_t.nd;
             nd = std::max(nd, (int)h->ca_t.nd);
         }
-        if (nd) HIP_TRY(dmalloc(h, &h->dia, sizeof(T) * (size_t)nd * n));
     }
-    HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n));
+    // CG on a batch of systems too large for the one-workgroup solver
+    // advances up to gbatch of them per grid launch
+    if (h->batch > 1 && n > kBlockSolveMaxN)
+        h->gbatch = std::max<int64_t>(1, std::min<int64_t>({h->batch, 65535, kGroupRows / n}));
+    if (nd) HIP_TRY(dmalloc(h, &h->dia, sizeof(T) * (size_t)nd * n * h->gbatch));
+    HIP_TRY(dmalloc(h, &h->vec, sizeof(T) * (size_t)kNumVec * n * h->gbatch));
     HIP_TRY(dmalloc(h, &h->st, sizeof(SolveState) * h->batch));
-    HIP_TRY(dmalloc(h, &h->part, sizeof(double) * kMaxRed * kMaxGrid));
-    HIP_TRY(dmalloc(h, &h->args_dev, sizeof(IterArgs<T, IT>)));
-    HIP_TRY(hipHostMalloc(&h->args_host, sizeof(IterArgs<T, IT>), hipHostMallocDefault));
+    HIP_TRY(dmalloc(h, &h->part, sizeof(double) * kPartStride * h->gbatch));
+    HIP_TRY(dmalloc(h, &h->ndone, sizeof(int32_t)));
+    HIP_TRY(dmalloc(h, &h->args_dev, sizeof(IterArgs<T, IT>) * h->gbatch));
+    HIP_TRY(hipHostMalloc(&h->args_host, sizeof(IterArgs<T, IT>) * h->gbatch,
+                          hipHostMallocDefault));
     HIP_TRY(hipHostMalloc((void **)&h->poll, 2 * sizeof(int32_t), hipHostMallocDefault));
     HIP_TRY(hipHostMalloc((void **)&h->st_host, sizeof(SolveState) * h->batch, hipHostMallocDefault));
     HIP_TRY(hipMemsetAsync(h->st, 0, sizeof(SolveState) * h->batch, s));
-    HIP_TRY(hipMemsetAsync(h->part, 0, sizeof(double) * kMaxRed * kMaxGrid, s));
+    HIP_TRY(hipMemsetAsync(h->part, 0, sizeof(double) * kPartStride * h->gbatch, s));
     HIP_TRY(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
     HIP_TRY(hipEventCreateWithFlags(&h->ev[0], hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&h->ev[1], hipEventDisableTiming));

@@ -27,7 +27,8 @@
 // scalars are identical everywhere and no kernel needs a grid-wide fence.
 // p and v are double-buffered by iteration parity (the product kernels read
 // the old vectors at neighbouring rows while they write the new ones); r is
-// written only by bicg_xpv at j >= 1, whose gathers read s and t.
+// written only by bicg_xpv at j >= 1, whose gathers read s and t.  These
+// launches advance one system (a batch is solved one system after another).
 #include "spmv_tile.h"
 
 namespace sla {
@@ -82,7 +83,8 @@ template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (load_done(st)) return;
+    __shared__ int seen[kWaves];
+    const bool stopped = saw_stop(st, seen);
     const int it = st->iter_a;
     const bool first = (it == 0);
     const int64_t n = A->n;
@@ -101,6 +103,7 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     __shared__ RowLds<T, IT> sm;
     __shared__ double red[5][kWaves];
     auto pre = [&]() {
+        if (stopped) return;
         if (first) {
             const int slot[2] = {kBiRR0, kBiBB};
             partial_loads<2>(A->part, slot, red);
@@ -111,13 +114,14 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     };
     T alpha = T(0), omega = T(0), beta = T(0);
     auto post = [&]() -> bool {
+        if (any_saw_stop(seen)) return false;
         if (first) {
             double tot[2];
             totals<2>(red, tot);
             const double rr = tot[0], bb = tot[1];
             if (bb == 0.0) {
                 if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
-                finish(st, SLA_OK, 0, 0.0);
+                finish(st, A->ndone, SLA_OK, 0, 0.0);
                 return false;
             }
             if (block0()) {
@@ -151,7 +155,7 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
         }
         if (tt == 0.0 || ts == 0.0) {
             if (block0()) st->spmv += 1;  // the t product of iteration j - 1
-            finish(st, SLA_BREAKDOWN, it - 1, 0.0);
+            finish(st, A->ndone, SLA_BREAKDOWN, it - 1, 0.0);
             return false;
         }
         const double omega_d = ts / tt;
@@ -173,7 +177,7 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     };
     double rv_acc = 0.0, rr_acc = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, 4>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
+        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         [&](int32_t c) { return G4<T>{sv[c], tv[c], pold[c], vold[c]}; }, pj,
         [&](int64_t i) {
             return XpvOwn<T>{sv[i], tv[i], pold[i], vold[i], first ? T(0) : x[i], rh[i]};
@@ -209,7 +213,8 @@ template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     SolveState *st = A->st;
-    if (load_done(st)) return;
+    __shared__ int seen[kWaves];
+    const bool stopped = saw_stop(st, seen);
     const int it = st->iter_b;
     const int64_t n = A->n;
     const gptr<const T> val = glb(A->val);
@@ -221,34 +226,36 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     __shared__ RowLds<T, IT> sm;
     __shared__ double red[2][kWaves];
     auto pre = [&]() {
+        if (stopped) return;
         const int slot[2] = {kBiRV, kBiRR};
         partial_loads<2>(A->part, slot, red);
     };
     T alpha = T(0);
     auto post = [&]() -> bool {
+        if (any_saw_stop(seen)) return false;
         if (st->half_exit) {
-            finish(st, SLA_OK, it, st->half_ss);
+            finish(st, A->ndone, SLA_OK, it, st->half_ss);
             return false;
         }
         double tot[2];
         totals<2>(red, tot);
         const double rv = tot[0], rr = tot[1];
         if (sqrt(rr) <= A->tol * sqrt(st->bb)) {
-            finish(st, SLA_OK, it, rr);
+            finish(st, A->ndone, SLA_OK, it, rr);
             return false;
         }
         if (it >= A->maxit) {
-            finish(st, SLA_NOT_CONVERGED, it, rr);
+            finish(st, A->ndone, SLA_NOT_CONVERGED, it, rr);
             return false;
         }
         const double rho = st->rho[it & 1];
         if (rho == 0.0) {
-            finish(st, SLA_BREAKDOWN, it, rr);
+            finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
             return false;
         }
         if (block0()) st->spmv += 1;  // v_j = A p_j
         if (rv == 0.0) {
-            finish(st, SLA_BREAKDOWN, it, rr);
+            finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
             return false;
         }
         const double alpha_d = rho / rv;
@@ -263,7 +270,7 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0, rs = 0.0, rt = 0.0;
     const bool go = spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
+        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
         [&](int32_t c) { return G2<T>{r[c], v[c]}; }, sk,
         [&](int64_t i) { return StOwn<T>{r[i], v[i], rh[i]}; },
         [&](int64_t i, T acc, const StOwn<T> &o, T) {

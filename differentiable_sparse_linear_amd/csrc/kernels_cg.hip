@@ -34,8 +34,15 @@
 // an odd iteration leaves x one step behind and flags it, and one launch
 // after the solve adds the pending alpha_{i-1} p_{i-1} (in the stopping launch
 // itself, blocks that start after block 0 has set `done` would skip it).
-// Every launch returns at entry once the device-side `done` flag is set, so
-// the host enqueues many iterations (HIP graph replays) and polls rarely.
+// Once the device-side `done` flag is set every launch ends at its first
+// barrier without loading anything (each wavefront reads the flag at entry;
+// the block acts on what its wavefronts saw together, so they cannot split),
+// so the host enqueues many iterations (HIP graph replays) and polls rarely.
+// A launch may advance several systems of a batch (blockIdx.y is the
+// system, whose own argument block points at its vectors, state and partial
+// sums, so the kernel body is that of one system); a system that
+// has stopped ends at the first barrier while the others go on, and the host waits
+// for the count of stopped systems.
 //
 // Block path: one 1024-thread workgroup runs the whole solve of one small
 // system (n <= 4096): vectors live in registers, the search direction in LDS
@@ -73,6 +80,7 @@ struct CgOwn {
 // delta_0, ||r_0||^2 and ||b||^2 (parity-0 slots).
 template <typename T, typename IT, bool JAC, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;
     const int64_t n = A->n;
     const gptr<const T> b = glb(A->b);
     const gptr<const T> ax0 = glb((const T *)cg_s(A, 1));
@@ -120,11 +128,14 @@ template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, bool ZW 
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
+    A += blockIdx.y;
     SolveState *st = A->st;
-    if (load_done(st)) return;
+    __shared__ int seen[kWaves];
+    const bool stopped = saw_stop(st, seen);
     const int it = st->iter_p[PH];
     const bool first = PH == 0 && it == 0;
     const int64_t n = A->n;
+    double *part = A->part;
     const gptr<const T> val = glb(A->val);
     const gptr<const T> uc = glb((const T *)cg_u(A, PH));
     const gptr<const T> wc = glb((const T *)cg_w(A, PH));
@@ -139,21 +150,23 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
 
     // previous launch's partial sums, loaded with the first row pointers
     auto pre = [&]() {
+        if (stopped) return;
         if (first) {
             const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
-            partial_loads<4>(A->part, slot, red);
+            partial_loads<4>(part, slot, red);
         } else {
             const int slot[3] = {PH ? kCgGA1 : kCgGA, PH ? kCgDE1 : kCgDE, PH ? kCgRR1 : kCgRR};
-            partial_loads<3>(A->part, slot, red);
+            partial_loads<3>(part, slot, red);
         }
     };
     T beta = T(0), alpha = T(0), alpha_prev = T(0);
     // a stop at an odd iteration leaves x = x_{i-1}
     auto stop = [&](int status, double rr) {
         if (PH == 1 && block0()) st->lag = 1;
-        finish(st, status, it, rr);
+        finish(st, A->ndone, status, it, rr);
     };
     auto post = [&]() -> bool {
+        if (any_saw_stop(seen)) return false;
         double tot[4];
         if (first) {
             totals<4>(red, tot);
@@ -168,12 +181,12 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
         const double gamma = tot[0], delta = tot[1], rr = tot[2], bb = tot[3];
         if (PH == 1) alpha_prev = (T)st->alpha[0];
         if (first && st->zero_diag) {
-            finish(st, SLA_ERR_ZERO_DIAG, 0, rr);
+            finish(st, A->ndone, SLA_ERR_ZERO_DIAG, 0, rr);
             return false;
         }
         if (first && bb == 0.0) {
             if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
-            finish(st, SLA_OK, 0, 0.0);
+            finish(st, A->ndone, SLA_OK, 0, 0.0);
             return false;
         }
         if (sqrt(rr) <= A->tol * sqrt(bb)) {
@@ -241,7 +254,7 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     if constexpr (ZW) {
         __shared__ G3<T> zring[3][kTileRows];
         go = dia_rows_zw<T>(
-            xcd_tiles(tiles_of(n)), n, col_src<CM>(A->cols),
+            walk_tiles(tiles_of(n), stopped), n, col_src<CM>(A->cols),
             [&](auto k) { return __builtin_nontemporal_load(&val[k]); }, gath, u_of,
             [&](int64_t i, const G3<T> &o) {
                 return CgOwn<T>{o.a, o.b, o.c, __builtin_nontemporal_load(&pprev[i]),
@@ -250,7 +263,7 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
             row, pre, post, zring);
     } else {
         go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
-            xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm,
+            walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
             [&](auto k) { return val[k]; }, gath, u_of,
             [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
             row, pre, post);
@@ -258,14 +271,17 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     if (!go) return;
     double v[3] = {g, d, q};
     const int slot[3] = {PH ? kCgGA : kCgGA1, PH ? kCgDE : kCgDE1, PH ? kCgRR : kCgRR1};
-    store_partials<3>(v, A->part, slot);
+    store_partials<3>(v, part, slot);
 }
 
 // x_i = x_{i-1} + alpha_{i-1} p_{i-1} after a stop at an odd iteration i
-// (alpha_{i-1} is the parity-0 alpha, p holds p_{i-1}).
+// (alpha_{i-1} is the parity-0 alpha, p holds p_{i-1}); system blockIdx.y.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void cg_lag_kernel(const SolveState *st, const T *__restrict__ p,
                                                         T *__restrict__ x, int64_t n) {
+    st += blockIdx.y;
+    p += (int64_t)blockIdx.y * n;
+    x += (int64_t)blockIdx.y * n;
     if (!st->lag) return;
     const T a = (T)st->alpha[0];
     const int64_t stride = (int64_t)gridDim.x * kBlock;
@@ -542,8 +558,8 @@ bool cg_zwalk(const ColArgs &it, int64_t n) {
 
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
-                          hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
+                          int nsys, hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
     if (jac) {
         SLA_DISPATCH_FORM(cm, slots, cg_init_kernel<T, IT, true, kS, kC>
                                                  <<<grid, kBlock, 0, s>>>(a));
@@ -556,8 +572,8 @@ hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
 
 template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
-                          int64_t n, int ph, hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)));
+                          int64_t n, int nsys, int ph, hipStream_t s, const hipEvent_t *ev) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
 #define SLA_CG_ITER(J, P)                                                                      \
     if (zw)                                                                                    \
         launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, true>, grid,           \
@@ -628,23 +644,25 @@ hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipSt
 }
 
 template <typename T>
-hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, hipStream_t s) {
+hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, int nsys,
+                         hipStream_t s) {
     int64_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
-    cg_lag_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(st, p, x, n);
+    cg_lag_kernel<T><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(st, p, x, n);
     return hipGetLastError();
 }
-template hipError_t launch_cg_lag<float>(const SolveState *, const float *, float *, int64_t,
+template hipError_t launch_cg_lag<float>(const SolveState *, const float *, float *, int64_t, int,
                                          hipStream_t);
 template hipError_t launch_cg_lag<double>(const SolveState *, const double *, double *, int64_t,
-                                          hipStream_t);
+                                          int, hipStream_t);
 
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
-                                              int64_t, hipStream_t);                            \
+                                              int64_t, int, hipStream_t);                       \
     template hipError_t launch_cg_iter<T, IT>(int, int, bool, bool, const IterArgs<T, IT> *, \
-                                              int64_t, int, hipStream_t, const hipEvent_t *);   \
+                                              int64_t, int, int, hipStream_t,                   \
+                                              const hipEvent_t *);                              \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
 
 SLA_INST(float, int32_t)

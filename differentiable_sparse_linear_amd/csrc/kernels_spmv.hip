@@ -190,12 +190,16 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restric
 
 // out[q * n + i] = row i's entry on diagonal q, 0 where bit q of msk[i] is
 // clear.  The row's entries are stored in ascending column order, which is
-// ascending q, so the k-th set bit takes the k-th entry.
+// ascending q, so the k-th set bit takes the k-th entry.  System blockIdx.y
+// reads val + y * val_stride and writes out + y * nd * n.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void dia_pack_kernel(const IT *__restrict__ rp,
                                                           const uint16_t *__restrict__ msk, int nd,
                                                           const T *__restrict__ val,
+                                                          int64_t val_stride,
                                                           T *__restrict__ out, int64_t n) {
+    val += (int64_t)blockIdx.y * val_stride;
+    out += (int64_t)blockIdx.y * nd * n;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
         uint32_t m = msk[i];
@@ -208,11 +212,15 @@ __global__ __launch_bounds__(kBlock) void dia_pack_kernel(const IT *__restrict__
     }
 }
 
+// System blockIdx.y: values val + y * val_stride, dinv + y * n, state st + y.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void dinv_kernel(const IT *__restrict__ diagpos,
                                                       const T *__restrict__ val,
-                                                      T *__restrict__ dinv, int64_t n,
-                                                      SolveState *st) {
+                                                      int64_t val_stride, T *__restrict__ dinv,
+                                                      int64_t n, SolveState *st) {
+    val += (int64_t)blockIdx.y * val_stride;
+    dinv += (int64_t)blockIdx.y * n;
+    st += blockIdx.y;
     const TileRange tr = xcd_tiles(tiles_of(n));
     int bad = 0;
     for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
@@ -226,8 +234,11 @@ __global__ __launch_bounds__(kBlock) void dinv_kernel(const IT *__restrict__ dia
     if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(&st->zero_diag, 1);
 }
 
+// x + y * n = 0 for system y = blockIdx.y when its state asks for it.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T *x, int64_t n) {
+    st += blockIdx.y;
+    x += (int64_t)blockIdx.y * n;
     if (!st->zero_x) return;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) x[i] = T(0);
@@ -297,28 +308,30 @@ hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz,
 }
 
 template <typename T, typename IT>
-hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val, T *out,
-                           int64_t n, hipStream_t s) {
+hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val,
+                           int64_t val_stride, T *out, int64_t n, int nsys, hipStream_t s) {
     int64_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    dia_pack_kernel<T, IT><<<(unsigned)blocks, kBlock, 0, s>>>(rp, msk, nd, val, out, n);
+    dia_pack_kernel<T, IT><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(rp, msk, nd, val,
+                                                                           val_stride, out, n);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
-                       hipStream_t s) {
-    dinv_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(diagpos, val, dinv, n, st);
+hipError_t launch_dinv(const IT *diagpos, const T *val, int64_t val_stride, T *dinv, int64_t n,
+                       SolveState *st, int nsys, hipStream_t s) {
+    dinv_kernel<T, IT><<<dim3(grid_for_tiles(tiles_of(n)), nsys), kBlock, 0, s>>>(
+        diagpos, val, val_stride, dinv, n, st);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) {
+hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipStream_t s) {
     int64_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    zero_if_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(st, x, n);
+    zero_if_kernel<T><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(st, x, n);
     return hipGetLastError();
 }
 
@@ -333,10 +346,10 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s) 
                                                   int, hipStream_t);                             \
     template hipError_t launch_grad<T, IT>(const IT *, const ColArgs &, const T *, const T *,   \
                                            T *, int64_t, int64_t, int, bool, hipStream_t);      \
-    template hipError_t launch_dinv<T, IT>(const IT *, const T *, T *, int64_t, SolveState *,   \
-                                           hipStream_t);                                         \
+    template hipError_t launch_dinv<T, IT>(const IT *, const T *, int64_t, T *, int64_t,        \
+                                           SolveState *, int, hipStream_t);                      \
     template hipError_t launch_dia_pack<T, IT>(const IT *, const uint16_t *, int, const T *,    \
-                                               T *, int64_t, hipStream_t);
+                                               int64_t, T *, int64_t, int, hipStream_t);
 
 SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)
@@ -346,7 +359,8 @@ template hipError_t launch_gather<float>(const int32_t *, const float *, float *
                                          hipStream_t);
 template hipError_t launch_gather<double>(const int32_t *, const double *, double *, int64_t,
                                           hipStream_t);
-template hipError_t launch_zero_if<float>(const SolveState *, float *, int64_t, hipStream_t);
-template hipError_t launch_zero_if<double>(const SolveState *, double *, int64_t, hipStream_t);
+template hipError_t launch_zero_if<float>(const SolveState *, float *, int64_t, int, hipStream_t);
+template hipError_t launch_zero_if<double>(const SolveState *, double *, int64_t, int,
+                                           hipStream_t);
 
 }  // namespace sla

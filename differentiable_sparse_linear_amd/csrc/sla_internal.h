@@ -31,6 +31,7 @@ constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, 32 CUs each
 constexpr int kMaxBlocksPerXcd = SLA_BLOCKS_PER_XCD;
 constexpr int kMaxGrid = kNumXcd * kMaxBlocksPerXcd;
 constexpr int kMaxRed = 8;         // partial-sum slots
+constexpr int kPartStride = kMaxRed * kMaxGrid;  // partial-sum doubles per system
 constexpr int kBlockSolveThreads = 1024;
 constexpr int kBlockSolveMaxN = 4096;  // 4 rows per thread; p, x, r, M^-1 in LDS
 
@@ -93,6 +94,9 @@ struct ColArgs {
     int32_t off[kMaxDiaMajor] = {};  // their offsets when nd <= kMaxDiaMajor
 };
 
+// Arguments of the grid iteration kernels for one system.  A launch that
+// advances nsys systems of a batch at once reads an array of nsys of them,
+// each already pointing at its system's data; workgroup (x, y) uses entry y.
 template <typename T, typename IT>
 struct IterArgs {
     const T *val;
@@ -106,6 +110,7 @@ struct IterArgs {
     T *v[2];
     SolveState *st;
     double *part;   // [kMaxRed][kMaxGrid]
+    int32_t *ndone; // stopped systems of the launch (shared; the host waits for all)
     int64_t n;
     double tol;
     int32_t maxit;
@@ -241,15 +246,42 @@ __device__ __forceinline__ int load_done(const SolveState *st) {
     return __hip_atomic_load(&st->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Entry test of the iteration kernels.  Block 0 of the same launch may set
+// `done` while this block's wavefronts are still starting, so wavefronts can
+// read it differently; one that left at once would leave its share of the
+// block's partial sums unwritten and the others would go on with a wrong
+// total.  So each wavefront reads the flag once, records what it saw in
+// seen[wave] and, if it saw the stop, skips its loads; the block acts on the
+// records after its first barrier (any_saw_stop), every thread alike.
+__device__ __forceinline__ bool saw_stop(const SolveState *st, int *seen) {
+    const int d = __builtin_amdgcn_readfirstlane(load_done(st));
+    if ((threadIdx.x & 63) == 0) seen[threadIdx.x >> 6] = d;
+    return d != 0;
+}
+__device__ __forceinline__ bool any_saw_stop(const int *seen) {
+    int a = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) a |= seen[w];
+    return a != 0;
+}
+// The tiles a block walks, none for a wavefront that saw the stop.
+__device__ __forceinline__ TileRange walk_tiles(int64_t ntiles, bool stopped) {
+    TileRange tr = xcd_tiles(ntiles);
+    if (stopped) tr.end = tr.first;
+    return tr;
+}
+
 __device__ __forceinline__ bool block0() { return blockIdx.x == 0 && threadIdx.x == 0; }
 
-// Block 0 records the end of the solve.
-__device__ __forceinline__ void finish(SolveState *st, int status, int iter, double rr) {
+// Block 0 of the system records the end of its solve and counts it in *ndone.
+__device__ __forceinline__ void finish(SolveState *st, int32_t *ndone, int status, int iter,
+                                       double rr) {
     if (block0()) {
         st->status = status;
         st->iter = iter;
         st->rr = rr;
         __hip_atomic_store(&st->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(ndone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -305,25 +337,28 @@ hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x
                        int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s);
 template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
-// Diagonal-major copy of one system's CSR values: out[q * n + i] = the entry
-// of row i on diagonal q (bit q of msk[i]), 0 where the row lacks it.
+// Diagonal-major copy of the CSR values of nsys systems (val_stride apart):
+// out[s][q * n + i] = the entry of row i on diagonal q (bit q of msk[i]), 0
+// where the row lacks it.
 template <typename T, typename IT>
-hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val, T *out,
-                           int64_t n, hipStream_t s);
+hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val,
+                           int64_t val_stride, T *out, int64_t n, int nsys, hipStream_t s);
+// per system of nsys: dinv[s][i] = 1 / val[s][diagpos[i]] (values val_stride apart)
 template <typename T, typename IT>
-hipError_t launch_dinv(const IT *diagpos, const T *val, T *dinv, int64_t n, SolveState *st,
-                       hipStream_t s);
+hipError_t launch_dinv(const IT *diagpos, const T *val, int64_t val_stride, T *dinv, int64_t n,
+                       SolveState *st, int nsys, hipStream_t s);
 
-// CG (grid path, one system): init, then one launch per iteration with the
-// iteration's parity
+// CG (grid path, nsys systems per launch): init, then one launch per
+// iteration with the iteration's parity
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
-                          hipStream_t s);
+                          int nsys, hipStream_t s);
 // zw: the z-walk variant (diagonal-major, seven diagonals with off[2] = -1,
 // off[4] = 1, off[0] = -off[6] = -kTileRows * grid, tiles in rounds)
 template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
-                          int64_t n, int ph, hipStream_t s, const hipEvent_t *ev = nullptr);
+                          int64_t n, int nsys, int ph, hipStream_t s,
+                          const hipEvent_t *ev = nullptr);
 // whether the z-walk applies to an operator form on n rows
 bool cg_zwalk(const ColArgs &it, int64_t n);
 
@@ -337,12 +372,13 @@ template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
 
-// shared by both grid solvers: x = 0 when the state asks for it
+// shared by both grid solvers: x = 0 when the state asks for it (nsys systems)
 template <typename T>
-hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, hipStream_t s);
+hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipStream_t s);
 // After a grid CG solve: x += alpha[0] p when the stop left x one step behind.
 template <typename T>
-hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, hipStream_t s);
+hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, int nsys,
+                         hipStream_t s);
 
 // CG, one workgroup per system (n <= kBlockSolveMaxN)
 struct BlockCgParams {

@@ -118,13 +118,18 @@ typedef struct {
  *               SLA_CREATE_WIDE_COLUMNS), when the pattern's entries lie on
  *               3, 5 or 7 diagonals (nearest-neighbour stencils in 1, 2 and
  *               3 dimensions) and nd * n <= 1.25 nnz, the handle keeps a
- *               buffer of nd * n values (one system) and each grid-path
- *               solve first copies the system's values into it
+ *               buffer of nd * n values per system of a launch group (see
+ *               the workspace note below) and each grid-path solve first
+ *               copies the systems' values into it
  *               diagonal-major, zero where a row lacks a diagonal; the
  *               iterations then read no row pointers or columns
  *               (sla_iteration_form).  Results are identical as long as the
  *               iterates stay finite.
  *               Other bits: SLA_ERR_ARG.
+ * Workspace: CG on a batch of systems with n > 4096 advances a group of
+ * min(batch, 65535, 2^21 / n) systems (at least 1) per grid launch, so the
+ * solver vectors (11 per system) and the diagonal-major buffer are sized for
+ * that group; BiCGStab and single systems use the first system's share.
  * Checks the pattern on the device (synchronizes `stream`).  Returns
  * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
  */

@@ -452,8 +452,9 @@ def test_batch_mixed_convergence_is_loop_of_singles(hip):
 
 
 def test_grid_path_batch_is_loop_of_singles(hip):
-    """Batched systems on the grid kernels (n > 4096) run one after another
-    through the same graphs, diagonal-major buffer and transposed values: each
+    """Batched systems on the grid kernels (n > 4096): CG advances the batch
+    in one launch group, BiCGStab runs the systems one after another through
+    the same graphs, diagonal-major buffer and transposed values; each
     system's results equal a single-system solve bit for bit and match the
     oracle, and a zero right-hand side inside the batch stops at 0."""
     banner("grid batch = loop")
