@@ -93,6 +93,10 @@ def parse():
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
                          "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
                          "and the eigenvalue gradient")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --op matvec / matvec_vjp: the seeded power-law graph Laplacian "
+                         "(2^20 rows unless --size, seed 9; row lengths from 1 to 557 357) "
+                         "instead of a numbered workload")
     ap.add_argument("--column-form", default="diagonal-major",
                     choices=("wide", "tile16", "diagonal", "diagonal-major"),
                     help="storage form the summarised run's iterations read")
@@ -176,6 +180,11 @@ def read_traffic(kernel, workload, sha):
 
 def load_problem(args):
     import workloads as W
+    if getattr(args, "graph", False):
+        n = args.size or (1 << 20)
+        rp, col, val = W.powerlaw_graph_laplacian(n, 9)
+        return W.Problem(f"powerlaw_graph_{n}_seed9", n, rp, col, val, np.zeros((1, n)),
+                         np.zeros((1, n)))
     if not getattr(args, "fp32", False):
         return W.config(args.workload, size=args.size)
     if args.workload == 3:
@@ -438,20 +447,24 @@ def bench_product(args, p):
     g = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).to(dev)
     y = torch.empty_like(x)
     sv, sr = p.values.itemsize, p.row_ptr.itemsize
+    # a pattern with rows past the tile walker's slots (the graph) also runs
+    # the row plan's kernels
+    plan = "+plan_spmv_kernel+plan_finish_kernel" if args.graph else ""
     if args.op == "matvec":
         call = lambda: pat.matvec(val, x, out=y)
         # values + columns + row pointers, x once, y written
         model = p.nnz * (sv + 4) + (p.n + 1) * sr + 2 * p.n * sv
-        kernel = "spmv_kernel"
+        kernel = "spmv_kernel" + plan
     else:
         call = lambda: pat.matvec_adjoint(val, x, g)
         # values + columns + row pointers once, g, x read, grad_x and
         # grad_values written
         model = p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv
-        # A^T x reads A's own rows through its diagonal masks when it has
-        # them, else the transpose map
-        kernel = ("spmv_t_diag_kernel" if pat.column_mode() == "diagonal"
-                  else "spmv_perm_kernel") + "+grad_kernel"
+        # with diagonal masks one kernel makes both from A's own rows, else
+        # A^T x goes through the transpose map and the gradient is a second
+        # kernel
+        kernel = ("diag_vjp_kernel" if pat.column_mode() == "diagonal"
+                  else "spmv_perm_kernel+grad_kernel" + plan + ("+plan_grad_kernel" if plan else ""))
     model *= p.batch
     steps = max(args.steps, 1) * 10
     for _ in range(max(args.warmup, 1)):
@@ -499,6 +512,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     sla.load()
+    if args.graph and args.op not in ("matvec", "matvec_vjp"):
+        print("--graph is for --op matvec / matvec_vjp", file=sys.stderr)
+        sys.exit(2)
     if args.op == "inverse":
         return bench_inverse(args)
     p = load_problem(args)

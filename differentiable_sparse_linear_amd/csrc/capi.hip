@@ -70,6 +70,8 @@ struct sla_ctx {
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
     int it_slots = 8, it_slots_t = 8;  // slots (or diagonals) of the iteration form
+    RowPlan plan, plan_t;        // tiles past the LDS stage, of A and of A^T (or empty)
+    void *plan_mem[2][4] = {};   // their items, split rows, partial sums and tile flags
     int64_t gbatch = 1;          // systems per grid CG launch
     void *vec = nullptr;         // [kNumVec][gbatch][n]
     SolveState *st = nullptr;
@@ -140,6 +142,8 @@ void release(sla_ctx *h) {
     (void)hipFree(h->perm);
     (void)hipFree(h->val_t);
     (void)hipFree(h->dia);
+    for (auto &pm : h->plan_mem)
+        for (void *p : pm) (void)hipFree(p);
     (void)hipFree(h->vec);
     (void)hipFree(h->st);
     (void)hipFree(h->part);
@@ -182,6 +186,7 @@ struct Operator {
     int slots;
     ColArgs it;
     int it_slots;
+    const RowPlan *plan;  // the products' plan for tiles past the stage
 };
 
 // nsys consecutive systems on the grid path (nsys <= gbatch; 1 for
@@ -268,7 +273,7 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     // reads it always, so it is zeroed when there is no initial guess
     if (o.use_x0)
         HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, x, cg ? a.t : a.q, n, n,
-                                   nsys, s));
+                                   nsys, s, op.plan));
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n * nsys, s));
     if (cg)
@@ -467,12 +472,12 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     oo.use_x0 = 0;
     sla_status st;
     if (o.method == SLA_CG) {
-        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots};
+        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots, &h->plan};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
         // A^T with values gathered through the transpose map, one system at
         // a time into the handle's buffer
-        Operator op{h->rp_t, h->ca_t, h->slots_t, h->ia_t, h->it_slots_t};
+        Operator op{h->rp_t, h->ca_t, h->slots_t, h->ia_t, h->it_slots_t, &h->plan_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
         std::vector<int32_t> it(B0), mv(B0), stc(B0);
@@ -517,7 +522,7 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     for (int64_t s0 = 0; s0 < B; s0 += 65535) {
         const int nb = (int)((B - s0) < 65535 ? (B - s0) : 65535);
         HIP_TRY(launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, gb + s0 * n,
-                                   x + s0 * n, gval + s0 * nnz, n, nnz, nb, true, s));
+                                   x + s0 * n, gval + s0 * nnz, n, nnz, nb, true, s, &h->plan));
     }
     HIP_TRY(hipStreamSynchronize(s));
     return st;
@@ -559,6 +564,89 @@ hipError_t build_diag(sla_ctx *h, const IT *rp, const int32_t *col, int32_t max_
     return hipSuccess;
 }
 
+// The row plan of a pattern whose row pointers are rp_dev (see RowPlan):
+// the tiles whose entries exceed the tile walker's stage or that hold a row
+// longer than its slots (the products' gather slots per row).  Built on the
+// host from a copy of the row pointers when the longest row exceeds
+// kCap / kTileRows (below that no tile needs it; the walker's slots cover
+// at least 4 entries), kept only if some tile needs it.  which: 0 for A, 1
+// for A^T; partial sums for up to 65535 systems (one launch's batch).
+template <typename T, typename IT>
+hipError_t build_plan(sla_ctx *h, int which, const IT *rp_dev, const int32_t *col,
+                      int32_t max_len, int slots, RowPlan &pl, hipStream_t s) {
+    pl = RowPlan();
+    if ((int64_t)max_len * kTileRows <= kCap && max_len <= slots) return hipSuccess;
+    const int64_t n = h->n;
+    std::vector<IT> rp((size_t)n + 1);
+    hipError_t e = hipMemcpyAsync(rp.data(), rp_dev, sizeof(IT) * (n + 1), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess || (e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    std::vector<PlanItem> items;
+    std::vector<PlanFin> fin;
+    std::vector<uint8_t> tiles((size_t)tiles_of(n), 0);
+    int32_t nslots = 0;
+    for (int64_t t = 0; t < tiles_of(n); ++t) {
+        const int64_t a = t * kTileRows, b = std::min<int64_t>(a + kTileRows, n);
+        int64_t longest = 0;
+        for (int64_t r = a; r < b; ++r) longest = std::max<int64_t>(longest, rp[r + 1] - rp[r]);
+        if ((int64_t)(rp[b] - rp[a]) <= kCap && longest <= slots) continue;  // the walker's
+        tiles[(size_t)t] = 1;
+        for (int64_t r = a; r < b;) {
+            const int64_t len = (int64_t)(rp[r + 1] - rp[r]);
+            if (len > kShortRow) {  // a long row: chunks of kPlanCap entries
+                const int64_t nch = (len + kPlanCap - 1) / kPlanCap;
+                if (nch > 1) fin.push_back(PlanFin{(int32_t)r, nslots, (int32_t)nch, 0});
+                for (int64_t c = 0; c < nch; ++c) {
+                    const int64_t e0 = (int64_t)rp[r] + c * kPlanCap;
+                    items.push_back(PlanItem{(int32_t)r, (int32_t)(r + 1),
+                                             nch > 1 ? nslots + (int32_t)c : -1, 1, e0,
+                                             std::min<int64_t>(e0 + kPlanCap, (int64_t)rp[r + 1])});
+                }
+                if (nch > 1) nslots += (int32_t)nch;
+                ++r;
+                continue;
+            }
+            // a short block: consecutive short rows while the run fits kPlanCap
+            const int64_t r0 = r;
+            while (r < b && (int64_t)(rp[r + 1] - rp[r]) <= kShortRow &&
+                   (int64_t)(rp[r + 1] - rp[r0]) <= kPlanCap)
+                ++r;
+            items.push_back(PlanItem{(int32_t)r0, (int32_t)r, -1, 0, (int64_t)rp[r0],
+                                     (int64_t)rp[r]});
+        }
+    }
+    if (items.empty()) return hipSuccess;
+    void **mem = h->plan_mem[which];
+    if ((e = dmalloc(h, (uint8_t **)&mem[3], tiles.size())) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(mem[3], tiles.data(), tiles.size(), hipMemcpyHostToDevice, s)) !=
+        hipSuccess)
+        return e;
+    if ((e = dmalloc(h, (PlanItem **)&mem[0], sizeof(PlanItem) * items.size())) != hipSuccess)
+        return e;
+    if ((e = hipMemcpyAsync(mem[0], items.data(), sizeof(PlanItem) * items.size(),
+                            hipMemcpyHostToDevice, s)) != hipSuccess)
+        return e;
+    if (!fin.empty()) {
+        if ((e = dmalloc(h, (PlanFin **)&mem[1], sizeof(PlanFin) * fin.size())) != hipSuccess)
+            return e;
+        if ((e = hipMemcpyAsync(mem[1], fin.data(), sizeof(PlanFin) * fin.size(),
+                                hipMemcpyHostToDevice, s)) != hipSuccess)
+            return e;
+        const int64_t sys = std::min<int64_t>(h->batch, 65535);
+        if ((e = dmalloc(h, (T **)&mem[2], sizeof(T) * (size_t)nslots * sys)) != hipSuccess)
+            return e;
+    }
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;  // items and fin are host buffers
+    pl.tiles = reinterpret_cast<const uint8_t *>(mem[3]);
+    pl.items = reinterpret_cast<const PlanItem *>(mem[0]);
+    pl.nitems = (int32_t)items.size();
+    pl.fin = reinterpret_cast<const PlanFin *>(mem[1]);
+    pl.nfin = (int32_t)fin.size();
+    pl.nslots = nslots;
+    pl.col = col;
+    pl.part = mem[2];
+    return hipSuccess;
+}
+
 template <typename T, typename IT>
 sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     const bool build_t = (flags & SLA_CREATE_TRANSPOSE) != 0;
@@ -578,6 +666,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     h->slots = slots_for(maxlen);
     h->max_len = maxlen;
     h->slots_t = h->slots;
+    HIP_TRY((build_plan<T, IT>(h, 0, rp, h->col, maxlen, h->slots, h->plan, s)));
     if (build_t) {
         HIP_TRY(dmalloc(h, &h->rp_t, sizeof(IT) * (n + 1)));
         HIP_TRY(dmalloc(h, &h->col_t, sizeof(int32_t) * nnz));
@@ -589,6 +678,8 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
         HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
         h->slots_t = slots_for(maxlen);
         h->ca_t.col = h->col_t;
+        HIP_TRY((build_plan<T, IT>(h, 1, reinterpret_cast<const IT *>(h->rp_t), h->col_t, maxlen,
+                                   h->slots_t, h->plan_t, s)));
         if (compact) {
             const IT *rpt = reinterpret_cast<const IT *>(h->rp_t);
             HIP_TRY(build_col16<IT>(h, rpt, h->col_t, &h->col16_t, s));
@@ -766,7 +857,7 @@ sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, dou
         for (int j = 0; j < m; ++j) {
             T *vj = V + (size_t)j * n;
             T *w = V + (size_t)(j + 1) * n;
-            HIP_TRY(launch_spmv<T, IT>(h->slots, rp, h->ca, val, 0, vj, w, n, 0, 1, s));
+            HIP_TRY(launch_spmv<T, IT>(h->slots, rp, h->ca, val, 0, vj, w, n, 0, 1, s, &h->plan));
             if (j > 0) HIP_TRY(launch_eig_update<T>(w, vj - n, 1, beta + j - 1, n, s));
             HIP_TRY(launch_eig_dots<T>(vj, 1, w, n, wk.part, alpha + j, false, s));
             HIP_TRY(launch_eig_update<T>(w, vj, 1, alpha + j, n, s));
@@ -844,10 +935,10 @@ namespace {
 template <typename T, typename IT>
 hipError_t transposed_product(sla_ctx *h, const T *v, const T *x, T *y, int batch, hipStream_t s) {
     if (h->ca.mode == kColDiag)
-        return launch_spmv_t_diag<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v, h->nnz, x,
-                                         y, h->n, h->n, batch, s);
+        return launch_diag_vjp<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v, h->nnz, x,
+                                      nullptr, y, nullptr, h->n, h->nnz, batch, false, s);
     return launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->ca_t,
-                                   h->perm, v, h->nnz, x, y, h->n, h->n, batch, s);
+                                   h->perm, v, h->nnz, x, y, h->n, h->n, batch, s, &h->plan_t);
 }
 
 }  // namespace
@@ -922,7 +1013,7 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
                 HIP_TRY(transposed_product<T, IT>(h, v, x, y, nb, s));
             else
                 HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->ca,
-                                            v, h->nnz, x, y, h->n, h->n, nb, s)));
+                                            v, h->nnz, x, y, h->n, h->n, nb, s, &h->plan)));
         }
         return SLA_OK;
     });
@@ -943,6 +1034,16 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
             const int nb = (int)((h->batch - s0) < 65535 ? (h->batch - s0) : 65535);
             const T *v = reinterpret_cast<const T *>(d_values) + s0 * h->nnz;
             const T *gy = reinterpret_cast<const T *>(d_grad_y) + s0 * h->n;
+            if (h->ca.mode == kColDiag) {  // both outputs from one pass over A's rows
+                T *gx = d_grad_x ? reinterpret_cast<T *>(d_grad_x) + s0 * h->n : nullptr;
+                T *gv = d_grad_values ? reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz
+                                      : nullptr;
+                const T *x = d_x ? reinterpret_cast<const T *>(d_x) + s0 * h->n : nullptr;
+                HIP_TRY((launch_diag_vjp<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v,
+                                                h->nnz, gy, x, gx, gv, h->n, h->nnz, nb, false,
+                                                s)));
+                continue;
+            }
             if (d_grad_x)
                 HIP_TRY(transposed_product<T, IT>(
                     h, v, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, nb, s));
@@ -950,7 +1051,7 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
                 HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, gy,
                                             reinterpret_cast<const T *>(d_x) + s0 * h->n,
                                             reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz,
-                                            h->n, h->nnz, nb, false, s)));
+                                            h->n, h->nnz, nb, false, s, &h->plan)));
         }
         return SLA_OK;
     });
@@ -966,7 +1067,7 @@ sla_status sla_solve(sla_handle h, const void *d_values, const void *d_b, void *
     return dispatch(h, [&](auto t, auto it) -> sla_status {
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
-        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots};
+        Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots, &h->plan};
         return solve_all<T, IT>(h, op, reinterpret_cast<const T *>(d_values),
                                 reinterpret_cast<const T *>(d_b), reinterpret_cast<T *>(d_x), o,
                                 info, s);

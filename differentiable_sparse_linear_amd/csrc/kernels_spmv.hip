@@ -16,7 +16,8 @@ template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
-                                                      int64_t n, int64_t vec_stride) {
+                                                      int64_t n, int64_t vec_stride,
+                                                      const uint8_t *plan_tiles) {
     __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
     spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(rp), col_src<CM>(ca), sm, [&](IT k) { return v[k]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
-        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
+        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost(), plan_tiles);
 }
 
 // y = A^T x through the transpose map: rp/col describe A^T and the value of
@@ -34,7 +35,7 @@ template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     const IT *__restrict__ rp, ColArgs ca, const int32_t *__restrict__ perm,
     const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
-    int64_t n, int64_t vec_stride) {
+    int64_t n, int64_t vec_stride, const uint8_t *plan_tiles) {
     __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
@@ -44,80 +45,119 @@ __global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
     spmv_rows<T, IT, SLOTS, SLOTS>(
         xcd_tiles(tiles_of(n)), n, glb(rp), col_src<CM>(ca), sm, [&](IT k) { return v[pm[k]]; },
         [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
-        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost());
+        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost(), plan_tiles);
 }
 
-// y = A^T x for a pattern with per-row diagonal masks, read from A's own
-// rows (no transpose map): row i of A^T holds A[j][i] for j = i - dlt[q],
-// stored when bit q of msk[j] is set, at position rp[j] + (set bits of
-// msk[j] below q).  q runs downwards, so the terms are added in ascending j,
-// the column order of A^T's row.  NDT >= the pattern's diagonal count; all
-// NDT slots are unrolled so every mask and row-pointer load of a row is in
-// flight before its values are gathered.
-template <typename T, typename IT, int NDT>
-__global__ __launch_bounds__(kBlock) void spmv_t_diag_kernel(const IT *__restrict__ rp, ColArgs ca,
-                                                             const T *__restrict__ val,
-                                                             int64_t val_stride,
-                                                             const T *__restrict__ x,
-                                                             T *__restrict__ y, int64_t n,
-                                                             int64_t vec_stride) {
+// Backward pass of y = A x on a pattern with per-row diagonal masks, one row
+// i per thread, reading A's own rows (no transpose map):
+//  GX: gx[i] = (A^T g)_i.  Row i of A^T holds A[j][i] for j = i - dlt[q],
+//      stored when bit q of msk[j] is set, at position rp[j] + (set bits of
+//      msk[j] below q).  q runs downwards, so the terms are added in
+//      ascending j, the column order of A^T's row.  All NDT slots are
+//      unrolled so every mask and row-pointer load of a row is in flight
+//      before its values are gathered.
+//  GV: gv[k] = g_i x_j for row i's stored entries (NEG: -g_i x_j, the
+//      solve's gradient on the pattern with g = lambda).  Entry k = rp[i] +
+//      (set bits of msk[i] below q) has column i + dlt[q], so the x loads of
+//      one diagonal are consecutive across the wavefront.  The products go
+//      to LDS at the entry's place in the tile's run (at most 8 entries per
+//      row in this form, so a tile's run fits kCap) and leave as one
+//      coalesced run: a row's entries lie 8 bytes apart, and stores straight
+//      from the rows would scatter each store instruction over many lines.
+// NDT >= the pattern's diagonal count.  System blockIdx.y: values
+// val + y * val_stride, vectors + y * n, gv + y * nnz.
+template <typename T, typename IT, int NDT, bool GX, bool GV, bool NEG>
+__global__ __launch_bounds__(kBlock) void diag_vjp_kernel(const IT *__restrict__ rp, ColArgs ca,
+                                                          const T *__restrict__ val,
+                                                          int64_t val_stride,
+                                                          const T *__restrict__ g,
+                                                          const T *__restrict__ x,
+                                                          T *__restrict__ gx,
+                                                          T *__restrict__ gv, int64_t n,
+                                                          int64_t nnz) {
     const int sys = blockIdx.y;
-    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
-    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
-    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
+    const gptr<const T> v = glb(GX ? val + (int64_t)sys * val_stride : val);
+    const gptr<const T> gs = glb(g + (int64_t)sys * n);
+    const gptr<const T> xs = glb(GV ? x + (int64_t)sys * n : x);
+    const gptr<T> gxs = glb(GX ? gx + (int64_t)sys * n : gx);
+    const gptr<T> gvs = glb(GV ? gv + (int64_t)sys * nnz : gv);
     const gptr<const uint16_t> msk = glb(ca.msk);
     const gptr<const IT> rpg = glb(rp);
     const int nd = ca.nd;
     int32_t dl[NDT];
 #pragma unroll
     for (int q = 0; q < NDT; ++q) dl[q] = q < nd ? ca.dlt[q] : 0;
+    __shared__ T sg[GV ? kCap : 1];
     const TileRange tr = xcd_tiles(tiles_of(n));
     for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
-        const int64_t i = t * kTileRows + threadIdx.x;
+        const int64_t row0 = t * kTileRows;
+        const int64_t i = row0 + threadIdx.x;
+        if constexpr (GV) {
+            const int rows = n - row0 < kTileRows ? (int)(n - row0) : kTileRows;
+            const IT base = rpg[row0];
+            const int cnt = (int)(rpg[row0 + rows] - base);
+            if (i < n) {
+                const uint32_t m = msk[i];
+                const int at = (int)(rpg[i] - base);
+                const T gi = gs[i];
+#pragma unroll
+                for (int q = 0; q < NDT; ++q) {
+                    if (q < nd && ((m >> q) & 1u)) {
+                        const T pr = gi * xs[i + dl[q]];
+                        sg[at + __builtin_popcount(m & ((1u << q) - 1u))] = NEG ? -pr : pr;
+                    }
+                }
+            }
+            __syncthreads();
+            for (int e = threadIdx.x; e < cnt; e += kBlock) gvs[base + e] = sg[e];
+            __syncthreads();  // the next tile reuses sg
+        }
         if (i >= n) continue;
-        bool on[NDT];
-        int64_t jj[NDT];
-        IT k[NDT];
+        if constexpr (GX) {
+            bool on[NDT];
+            int64_t jj[NDT];
+            IT k[NDT];
 #pragma unroll
-        for (int q = 0; q < NDT; ++q) {
-            const int64_t j = i - dl[q];
-            on[q] = q < nd && j >= 0 && j < n;
-            jj[q] = on[q] ? j : i;
-        }
+            for (int q = 0; q < NDT; ++q) {
+                const int64_t j = i - dl[q];
+                on[q] = q < nd && j >= 0 && j < n;
+                jj[q] = on[q] ? j : i;
+            }
 #pragma unroll
-        for (int q = 0; q < NDT; ++q) {
-            const uint32_t m = msk[jj[q]];
-            on[q] = on[q] && ((m >> q) & 1u);
-            k[q] = rpg[jj[q]] + (IT)__builtin_popcount(m & ((1u << q) - 1u));
-        }
-        T s = T(0);
+            for (int q = 0; q < NDT; ++q) {
+                const uint32_t m = msk[jj[q]];
+                on[q] = on[q] && ((m >> q) & 1u);
+                k[q] = rpg[jj[q]] + (IT)__builtin_popcount(m & ((1u << q) - 1u));
+            }
+            T s = T(0);
 #pragma unroll
-        for (int q = NDT - 1; q >= 0; --q) {
-            if (on[q]) s = fma(v[k[q]], xs[jj[q]], s);
+            for (int q = NDT - 1; q >= 0; --q) {
+                if (on[q]) s = fma(v[k[q]], gs[jj[q]], s);
+            }
+            gxs[i] = s;
         }
-        ys[i] = s;
     }
 }
 
 // grad[k] = -lambda[row(k)] * x[col[k]] (NEG; the solve's gradient on the
-// pattern) or g[row(k)] * x[col[k]] (the product's).  Short tiles: each thread marks the
-// tile-local row of its row's entries in LDS (with diagonal masks also their
-// columns, from the mask's set bits), then the entries are written as one
-// coalesced run.  Tiles with long rows: one wavefront per row.
+// pattern) or g[row(k)] * x[col[k]] (the product's), for the per-entry column
+// forms (int32 or tile-relative int16; diagonal masks use diag_vjp_kernel).
+// Short tiles: each thread marks the tile-local row of its row's entries in
+// LDS, then the entries are written as one coalesced run.  Tiles that
+// plan_tiles flags are left to the row plan; other tiles past the stage take
+// one wavefront per row.
 template <typename T, typename IT, bool NEG, int CM>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ lam,
                                                       const T *__restrict__ x, T *__restrict__ grad,
-                                                      int64_t n, int64_t nnz) {
-    constexpr bool kDiag = CM == kColDiag;
+                                                      int64_t n, int64_t nnz,
+                                                      const uint8_t *plan_tiles) {
+    static_assert(CM == kColWide || CM == kColTile16, "per-entry column forms");
     __shared__ IT srp[kTileRows + 1];
     __shared__ T slam[kTileRows];
     __shared__ uint16_t rid[kCap];
-    __shared__ int32_t scol[kDiag ? kCap : 1];
-    __shared__ int32_t dtab[kMaxDiags];
     const int sys = blockIdx.y;
     const ColSrc<CM> col = col_src<CM>(ca);
-    if (kDiag && threadIdx.x < kMaxDiags) dtab[threadIdx.x] = ca.dlt[threadIdx.x];
     lam += (int64_t)sys * n;
     x += (int64_t)sys * n;
     grad += (int64_t)sys * nnz;
@@ -135,23 +175,18 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
         __syncthreads();
         const IT base = srp[0];
         const int64_t cnt = (int64_t)(srp[rows] - base);
-        if (cnt <= kCap) {
+        const bool planned = plan_tiles && plan_tiles[t];
+        if (!planned && cnt <= kCap) {
             if (tid < rows) {
-                uint32_t m = kDiag ? (uint32_t)col.msk[row0 + tid] : 0u;
-                for (int e = (int)(srp[tid] - base); e < (int)(srp[tid + 1] - base); ++e) {
+                for (int e = (int)(srp[tid] - base); e < (int)(srp[tid + 1] - base); ++e)
                     rid[e] = (uint16_t)tid;
-                    if (kDiag) {
-                        scol[e] = (int32_t)(row0 + tid) + dtab[__builtin_ctz(m | 0x8000u)];
-                        m &= m - 1u;
-                    }
-                }
             }
             __syncthreads();
             int32_t c[kEpt];
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
-                if (e < cnt) c[j] = kDiag ? scol[e] : col(base + e, row0);
+                if (e < cnt) c[j] = col(base + e, row0);
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
@@ -161,21 +196,158 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                     grad[base + e] = NEG ? -g : g;
                 }
             }
-        } else {
+        } else if (!planned) {
             const int lane = tid & 63, wave = tid >> 6;
             for (int r = wave; r < rows; r += kWaves) {
                 const T li = slam[r];
                 const IT lo = srp[r], hi = srp[r + 1];
-                const uint32_t mr = kDiag ? (uint32_t)col.msk[row0 + r] : 0u;
                 for (IT k = lo + lane; k < hi; k += 64) {
-                    const int32_t c = kDiag ? (int32_t)(row0 + r) + dtab[nth_bit(mr, (int)(k - lo))]
-                                            : col(k, row0);
-                    const T g = li * x[c];
+                    const T g = li * x[col(k, row0)];
                     grad[k] = NEG ? -g : g;
                 }
             }
         }
         __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------ row plans
+//
+// The tiles past the stage (PlanItem): workgroup b takes item b, system
+// blockIdx.y (values val_stride apart, vectors vec_stride apart, partials
+// nslots apart).  PERM: the operator is A^T through the transpose map, entry k's
+// value val[perm[k]].
+
+// Products of one item.  Short block: the run's products v x[col] go to
+// LDS in one coalesced pass, then thread t adds row r0 + t's products in
+// entry order.  Long-row chunk: thread t takes entries t, t + 256, ... of
+// the chunk (all loads first, then an fma chain), a fixed-order workgroup
+// sum, y[row] or the chunk's partial.
+template <typename T, typename IT, bool PERM>
+__global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
+    const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
+    const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
+    const T *__restrict__ x, T *__restrict__ y, int64_t vec_stride, T *__restrict__ part,
+    int32_t nslots) {
+    __shared__ T prod[kPlanCap];
+    __shared__ T wsum[kWaves];
+    const int sys = blockIdx.y;
+    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
+    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
+    const gptr<const int32_t> cg = glb(col);
+    const gptr<const int32_t> pm = glb(perm);
+    auto vf = [&](int64_t k) { return PERM ? v[pm[k]] : v[k]; };
+    const PlanItem it = items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const int64_t e0 = it.e0;
+    const int cnt = (int)(it.e1 - e0);
+    T pv[kPlanEpt], px[kPlanEpt];
+#pragma unroll
+    for (int j = 0; j < kPlanEpt; ++j) {
+        const int e = tid + j * kBlock;
+        pv[j] = T(0);
+        px[j] = T(0);
+        if (e < cnt) {
+            pv[j] = vf(e0 + e);
+            px[j] = xs[cg[e0 + e]];
+        }
+    }
+    if (it.kind == 0) {
+#pragma unroll
+        for (int j = 0; j < kPlanEpt; ++j) {
+            const int e = tid + j * kBlock;
+            if (e < cnt) prod[e] = pv[j] * px[j];
+        }
+        __syncthreads();
+        if (tid < it.r1 - it.r0) {
+            const int64_t r = it.r0 + tid;
+            const int lo = (int)(rp[r] - e0), hi = (int)(rp[r + 1] - e0);
+            T s = T(0);
+            for (int k = lo; k < hi; ++k) s += prod[k];
+            ys[r] = s;
+        }
+    } else {
+        T s = T(0);
+#pragma unroll
+        for (int j = 0; j < kPlanEpt; ++j) s = fma(pv[j], px[j], s);  // 0 * 0 past the chunk
+        s = wave_sum_t(s);
+        if ((tid & 63) == 0) wsum[tid >> 6] = s;
+        __syncthreads();
+        if (tid == 0) {
+            T tot = T(0);
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) tot += wsum[w];
+            if (it.slot < 0)
+                ys[it.r0] = tot;
+            else
+                part[(int64_t)sys * nslots + it.slot] = tot;
+        }
+    }
+}
+
+// A split row's value: its chunks' partials added in chunk order.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__restrict__ fin,
+                                                             int32_t nfin,
+                                                             const T *__restrict__ part,
+                                                             int32_t nslots, T *__restrict__ y,
+                                                             int64_t vec_stride) {
+    const int sys = blockIdx.y;
+    const int f = blockIdx.x * kBlock + threadIdx.x;
+    if (f >= nfin) return;
+    const PlanFin r = fin[f];
+    const T *p = part + (int64_t)sys * nslots + r.slot0;
+    T s = T(0);
+    for (int c = 0; c < r.nch; ++c) s += p[c];
+    y[(int64_t)sys * vec_stride + r.row] = s;
+}
+
+// The gradient on the pattern for one item: g[row(k)] x[col[k]] (NEG:
+// negated).  Short block: thread t marks row r0 + t's entries in LDS, then
+// the run is written coalesced; long-row chunk: one row, written coalesced.
+template <typename T, typename IT, bool NEG>
+__global__ __launch_bounds__(kBlock) void plan_grad_kernel(
+    const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
+    const T *__restrict__ g, const T *__restrict__ x, T *__restrict__ grad, int64_t n,
+    int64_t nnz) {
+    __shared__ uint16_t rid[kPlanCap];
+    __shared__ T sg[kTileRows];
+    const int sys = blockIdx.y;
+    const gptr<const T> gs = glb(g + (int64_t)sys * n);
+    const gptr<const T> xs = glb(x + (int64_t)sys * n);
+    const gptr<T> gr = glb(grad + (int64_t)sys * nnz);
+    const gptr<const int32_t> cg = glb(col);
+    const PlanItem it = items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const int64_t e0 = it.e0;
+    const int cnt = (int)(it.e1 - e0);
+    if (it.kind == 0) {
+        if (tid < it.r1 - it.r0) {
+            const int64_t r = it.r0 + tid;
+            sg[tid] = gs[r];
+            const int hi = (int)(rp[r + 1] - e0);
+            for (int e = (int)(rp[r] - e0); e < hi; ++e) rid[e] = (uint16_t)tid;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kPlanEpt; ++j) {
+            const int e = tid + j * kBlock;
+            if (e < cnt) {
+                const T p = sg[rid[e]] * xs[cg[e0 + e]];
+                gr[e0 + e] = NEG ? -p : p;
+            }
+        }
+    } else {
+        const T gi = gs[it.r0];
+#pragma unroll
+        for (int j = 0; j < kPlanEpt; ++j) {
+            const int e = tid + j * kBlock;
+            if (e < cnt) {
+                const T p = gi * xs[cg[e0 + e]];
+                gr[e0 + e] = NEG ? -p : p;
+            }
+        }
     }
 }
 
@@ -246,55 +418,123 @@ __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T
 
 // ------------------------------------------------------------------ launchers
 
+inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
+
+// The plan's rows of y = A x (PERM: A^T through the transpose map), after
+// the tile kernel has done the others.
+template <typename T, typename IT, bool PERM>
+void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, const T *val,
+                      int64_t val_stride, const T *x, T *y, int64_t vec_stride, int batch,
+                      hipStream_t s) {
+    T *part = reinterpret_cast<T *>(pl.part);
+    plan_spmv_kernel<T, IT, PERM><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
+        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots);
+    if (pl.nfin > 0)
+        plan_finish_kernel<T><<<dim3((pl.nfin + kBlock - 1) / kBlock, batch), kBlock, 0, s>>>(
+            pl.fin, pl.nfin, part, pl.nslots, y, vec_stride);
+}
+
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
-                       int batch, hipStream_t s) {
+                       int batch, hipStream_t s, const RowPlan *plan) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    const bool ps = planned(plan);
+    const uint8_t *pt = ps ? plan->tiles : nullptr;
     SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC>
                                                 <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride,
-                                                                         x, y, n, vec_stride)));
+                                                                         x, y, n, vec_stride,
+                                                                         pt)));
+    if (ps)
+        launch_plan_spmv<T, IT, false>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
+                                       batch, s);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
 hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                            int64_t vec_stride, int batch, hipStream_t s) {
+                            int64_t vec_stride, int batch, hipStream_t s, const RowPlan *plan) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    const bool ps = planned(plan);
+    const uint8_t *pt = ps ? plan->tiles : nullptr;
     SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
                                                 <<<grid, kBlock, 0, s>>>(rp, ca, perm, val,
                                                                          val_stride, x, y, n,
-                                                                         vec_stride)));
+                                                                         vec_stride, pt)));
+    if (ps)
+        launch_plan_spmv<T, IT, true>(*plan, rp, perm, val, val_stride, x, y, vec_stride, batch,
+                                      s);
     return hipGetLastError();
 }
 
-template <typename T, typename IT>
-hipError_t launch_spmv_t_diag(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
-                              const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
-                              hipStream_t s) {
+template <typename T, typename IT, bool GX, bool GV, bool NEG>
+void launch_diag_vjp_t(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
+                       const T *g, const T *x, T *gx, T *gv, int64_t n, int64_t nnz, int batch,
+                       hipStream_t s) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     if (ca.nd <= 4)
-        spmv_t_diag_kernel<T, IT, 4><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x, y, n,
-                                                             vec_stride);
+        diag_vjp_kernel<T, IT, 4, GX, GV, NEG>
+            <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, g, x, gx, gv, n, nnz);
     else if (ca.nd <= 8)
-        spmv_t_diag_kernel<T, IT, 8><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x, y, n,
-                                                             vec_stride);
+        diag_vjp_kernel<T, IT, 8, GX, GV, NEG>
+            <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, g, x, gx, gv, n, nnz);
     else
-        spmv_t_diag_kernel<T, IT, kMaxDiags><<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, x,
-                                                                     y, n, vec_stride);
+        diag_vjp_kernel<T, IT, kMaxDiags, GX, GV, NEG>
+            <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride, g, x, gx, gv, n, nnz);
+}
+
+template <typename T, typename IT>
+hipError_t launch_diag_vjp(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
+                           const T *g, const T *x, T *gx, T *gv, int64_t n, int64_t nnz,
+                           int batch, bool neg, hipStream_t s) {
+    if (gx && gv && !neg) {  // the product's backward: one pass
+        launch_diag_vjp_t<T, IT, true, true, false>(rp, ca, val, val_stride, g, x, gx, gv, n, nnz,
+                                                    batch, s);
+        return hipGetLastError();
+    }
+    if (gx)
+        launch_diag_vjp_t<T, IT, true, false, false>(rp, ca, val, val_stride, g, x, gx, gv, n,
+                                                     nnz, batch, s);
+    if (gv && neg)
+        launch_diag_vjp_t<T, IT, false, true, true>(rp, ca, val, val_stride, g, x, gx, gv, n, nnz,
+                                                    batch, s);
+    else if (gv)
+        launch_diag_vjp_t<T, IT, false, true, false>(rp, ca, val, val_stride, g, x, gx, gv, n,
+                                                     nnz, batch, s);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
-                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s) {
+                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s,
+                       const RowPlan *plan) {
+    if (ca.mode == kColDiag)
+        return launch_diag_vjp<T, IT>(rp, ca, nullptr, 0, lam, x, nullptr, grad, n, nnz, batch,
+                                      neg, s);
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    SLA_DISPATCH_CM(ca.mode, if (neg) {
-        grad_kernel<T, IT, true, kC><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz);
+    const bool ps = planned(plan);
+    const uint8_t *pt = ps ? plan->tiles : nullptr;
+#define SLA_GRAD(C)                                                                           \
+    if (neg)                                                                                  \
+        grad_kernel<T, IT, true, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt); \
+    else                                                                                      \
+        grad_kernel<T, IT, false, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt)
+    if (ca.mode == kColTile16) {
+        SLA_GRAD(kColTile16);
     } else {
-        grad_kernel<T, IT, false, kC><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz);
-    });
+        SLA_GRAD(kColWide);
+    }
+#undef SLA_GRAD
+    if (ps) {
+        const dim3 pg(plan->nitems, batch);
+        if (neg)
+            plan_grad_kernel<T, IT, true>
+                <<<pg, kBlock, 0, s>>>(plan->items, rp, plan->col, lam, x, grad, n, nnz);
+        else
+            plan_grad_kernel<T, IT, false>
+                <<<pg, kBlock, 0, s>>>(plan->items, rp, plan->col, lam, x, grad, n, nnz);
+    }
     return hipGetLastError();
 }
 
@@ -337,15 +577,18 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipSt
 
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_spmv<T, IT>(int, const IT *, const ColArgs &, const T *, int64_t, \
-                                           const T *, T *, int64_t, int64_t, int, hipStream_t);  \
+                                           const T *, T *, int64_t, int64_t, int, hipStream_t,   \
+                                           const RowPlan *);                                     \
     template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
                                                 const int32_t *, const T *, int64_t, const T *,  \
-                                                T *, int64_t, int64_t, int, hipStream_t);        \
-    template hipError_t launch_spmv_t_diag<T, IT>(const IT *, const ColArgs &, const T *,       \
-                                                  int64_t, const T *, T *, int64_t, int64_t,     \
-                                                  int, hipStream_t);                             \
+                                                T *, int64_t, int64_t, int, hipStream_t,         \
+                                                const RowPlan *);                                \
+    template hipError_t launch_diag_vjp<T, IT>(const IT *, const ColArgs &, const T *, int64_t,  \
+                                               const T *, const T *, T *, T *, int64_t, int64_t, \
+                                               int, bool, hipStream_t);                          \
     template hipError_t launch_grad<T, IT>(const IT *, const ColArgs &, const T *, const T *,   \
-                                           T *, int64_t, int64_t, int, bool, hipStream_t);      \
+                                           T *, int64_t, int64_t, int, bool, hipStream_t,       \
+                                           const RowPlan *);                                    \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, int64_t, T *, int64_t,        \
                                            SolveState *, int, hipStream_t);                      \
     template hipError_t launch_dia_pack<T, IT>(const IT *, const uint16_t *, int, const T *,    \

@@ -318,23 +318,70 @@ inline void launch_maybe_timed(void (*k)(KArgs...), dim3 grid, dim3 block, uint3
 // The `slots` argument of the SpMV-shaped launchers is slots_for(longest row);
 // `col16` (or `c16` for the kernels that read the argument block) selects the
 // compact tile-relative columns when the handle has them.
+// ------------------------------------------------------ rows past the stage
+//
+// A 256-row tile whose entries exceed kCap does not fit the tile walker's
+// LDS stage, and in a tile that fits, a row longer than the walker's slots
+// is summed by one thread with one gather after another.  For the
+// stand-alone products and the gradient such tiles are planned once at
+// set-up (the CSR-Adaptive idea of Greathouse and Daga, SC14: row blocks
+// sized to the LDS, long rows split over workgroups):
+//  - a short block: up to 256 consecutive rows of at most kShortRow entries
+//    each and at most kPlanCap entries in all; one workgroup loads the
+//    block's run coalesced, stages the products in LDS and sums each row in
+//    entry order;
+//  - a long row (more than kShortRow entries): chunks of kPlanCap entries,
+//    one workgroup each, a fixed-order workgroup sum; a row of several
+//    chunks leaves one partial per chunk and a last pass adds them in order.
+// The tile kernels skip the tiles flagged in `tiles` when a plan covers them.
+constexpr int kEpt = 8;              // staged entries per thread (tile walker)
+constexpr int kCap = kBlock * kEpt;  // staged entries per tile
+constexpr int kShortRow = 64;
+constexpr int kPlanEpt = 16;
+constexpr int kPlanCap = kBlock * kPlanEpt;  // entries per short block or chunk
+struct PlanItem {
+    int32_t r0, r1;  // rows [r0, r1) (a long row's chunk: r1 = r0 + 1)
+    int32_t slot;    // a chunk of a split row: its partial's slot; else -1
+    int32_t kind;    // 0 short block, 1 long-row chunk
+    int64_t e0, e1;  // entries [e0, e1)
+};
+struct PlanFin {
+    int32_t row, slot0, nch, pad;  // a split row: its partials [slot0, slot0 + nch)
+};
+struct RowPlan {
+    const uint8_t *tiles = nullptr;  // [tiles] 1 where the plan covers the tile
+    const PlanItem *items = nullptr;
+    int32_t nitems = 0;
+    const PlanFin *fin = nullptr;
+    int32_t nfin = 0;
+    int32_t nslots = 0;     // partials per system
+    const int32_t *col = nullptr;  // the pattern's int32 columns
+    void *part = nullptr;   // [systems of a launch][nslots] partial sums
+};
+
+// y = A x (plan: the tiles past the stage, or null)
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
-                       int batch, hipStream_t s);
+                       int batch, hipStream_t s, const RowPlan *plan = nullptr);
 template <typename T, typename IT>
 hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                            int64_t vec_stride, int batch, hipStream_t s);
-// y = A^T x from A's own rows through its diagonal masks (ca.mode == kColDiag)
+                            int64_t vec_stride, int batch, hipStream_t s,
+                            const RowPlan *plan = nullptr);
+// Backward of y = A x through A's diagonal masks (ca.mode == kColDiag), from
+// A's own rows: gx = A^T g (when gx is not null, values val_stride apart) and
+// gv[k] = g_i x_j on the pattern (when gv is not null; -g_i x_j with neg),
+// one pass when both are wanted; vectors n apart, gv nnz apart.
 template <typename T, typename IT>
-hipError_t launch_spmv_t_diag(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
-                              const T *x, T *y, int64_t n, int64_t vec_stride, int batch,
-                              hipStream_t s);
+hipError_t launch_diag_vjp(const IT *rp, const ColArgs &ca, const T *val, int64_t val_stride,
+                           const T *g, const T *x, T *gx, T *gv, int64_t n, int64_t nnz,
+                           int batch, bool neg, hipStream_t s);
 // the gradient on the pattern; columns from ca as the products read them
 template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
-                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s);
+                       int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s,
+                       const RowPlan *plan = nullptr);
 template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
 // Diagonal-major copy of the CSR values of nsys systems (val_stride apart):

@@ -28,9 +28,6 @@
 
 namespace sla {
 
-constexpr int kEpt = 8;              // staged entries per thread
-constexpr int kCap = kBlock * kEpt;  // staged entries per tile
-
 template <typename T>
 using gptr = __attribute__((address_space(1))) T *;
 
@@ -305,12 +302,14 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
 // (the stored entry whose column is i; every validated pattern has one).
 // pre(): start-up loads issued with the first row pointers (no barrier
 // inside); post(): runs after the first barrier, every thread, and returns
-// false to end the kernel (the same in every thread).
+// false to end the kernel (the same in every thread).  plan_tiles: when not
+// null, the tiles it flags are left alone (a row plan covers them).
 template <typename T, typename IT, int SLOTS, int ROUND, int CM, typename VF, typename GF,
           typename CF, typename OF, typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
                                           ColSrc<CM> col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf,
-                                          OF of, RF rf, PRE pre, POST post) {
+                                          OF of, RF rf, PRE pre, POST post,
+                                          const uint8_t *plan_tiles = nullptr) {
     if constexpr (CM == kColDiaMajor) {
         return dia_rows<T, SLOTS>(tr, n, col, vf, gf, cf, of, rf, pre, post);
     } else {
@@ -349,7 +348,8 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         const uint32_t mk = kDiag ? (uint32_t)col.msk[row0 + me] : 0u;
         const IT base = cr[0];
         const int64_t cnt = (int64_t)(cr[rows] - base);
-        const bool staged = cnt > 0 && cnt <= kCap;
+        const bool planned = plan_tiles && plan_tiles[t];
+        const bool staged = !planned && cnt > 0 && cnt <= kCap;
         if (staged) {
             const int last = (int)cnt - 1;
             T v[kEpt];
@@ -416,7 +416,7 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
                 }
                 rf(row0 + tid, s, own, sm.val[lo + (below < lastk ? below : lastk)]);
             }
-        } else {
+        } else if (!planned) {
             const int lane = tid & 63, wave = tid >> 6;
             T *ps = sm.val;              // row sums
             T *pd = sm.val + kTileRows;  // diagonal entries

@@ -180,6 +180,26 @@ def test_matvec_adjoint_arguments(hip):
         pat.matvec_adjoint(d["val"], x, x, need_grad_x=False, need_grad_values=False)
 
 
+@pytest.mark.parametrize("case", ["cfg2_30", "cfg4_40", "cfg3_batch3_fp32"])
+def test_matvec_adjoint_outputs_alone_equal_both(hip, case):
+    """With diagonal masks one kernel makes grad_x and grad_values together;
+    asking for either alone gives bitwise the same arrays."""
+    banner(f"matvec adjoint alone vs both {case}")
+    p = {"cfg2_30": lambda: W.config(2, size=30), "cfg4_40": lambda: W.config(4, size=40),
+         "cfg3_batch3_fp32": lambda: W.config(3, size=24, batch=3, dtype=np.float32)}[case]()
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p), build_transpose=True)
+    assert pat.column_mode() == "diagonal"
+    rng = np.random.default_rng(31)
+    x = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).cuda()
+    g = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).cuda()
+    gv, gx = pat.matvec_adjoint(d["val"], x, g)
+    gv1, _ = pat.matvec_adjoint(d["val"], x, g, need_grad_x=False)
+    _, gx1 = pat.matvec_adjoint(d["val"], x, g, need_grad_values=False)
+    yt = pat.matvec(d["val"], g, transpose=True)
+    assert torch.equal(gv, gv1) and torch.equal(gx, gx1) and torch.equal(gx, yt)
+
+
 def test_sparse_matvec_autograd(hip):
     banner("autograd matvec")
     rp, col, val = W.random_csr(50, 0.2, 9, symmetric=False)

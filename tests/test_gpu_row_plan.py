@@ -1,0 +1,135 @@
+"""Patterns with long rows: the row plan of the stand-alone products and the
+gradient.
+
+Tiles whose entries exceed the tile walker's LDS stage, or that hold a row
+longer than its gather slots, are covered by a plan built at set-up: short
+blocks (rows of at most 64 entries, at most 4096 entries per block) and long
+rows split into chunks of 4096 entries, one workgroup each, with a last pass
+over the chunks of a split row.  Checked against the oracle: y = A x and
+y = A^T x (fp64 and fp32, batches, int64 row pointers), the product's
+backward pass, and a CG solve + adjoint whose gradient runs on the plan;
+row lengths straddle the plan's limits (64 / 65 entries, 4096 / 4097, a row
+of many chunks).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import FP_TOL, banner, oracle_forward_adjoint, relerr, tdtype, to_dev
+from test_gpu_parity import _spmv_case, _vjp_case
+
+pytestmark = pytest.mark.gpu
+
+
+def lengths_pattern(n, base, special, seed, batch=1, dtype=np.float64, index=np.int32):
+    """Rows of `base` entries each (a list, cycled over the rows) except the
+    rows in `special` (row: length); every row holds its diagonal and
+    distinct random columns, ascending."""
+    rng = np.random.default_rng(seed)
+    cols = []
+    for i in range(n):
+        L = min(special.get(i, base[i % len(base)]), n)
+        other = rng.choice(n - 1, size=L - 1, replace=False)
+        other = other + (other >= i)
+        cols.append(np.sort(np.concatenate([other, [i]])))
+    counts = np.array([c.size for c in cols])
+    rp = np.zeros(n + 1, dtype=index)
+    rp[1:] = np.cumsum(counts)
+    col = np.concatenate(cols).astype(np.int32)
+    val = rng.uniform(-1.0, 1.0, (batch, col.size)).astype(dtype)
+    z = np.zeros((batch, n), dtype=dtype)
+    return W.Problem(f"lengths_{n}_{seed}", n, rp, col, val, z, z)
+
+
+def star_pattern(n, seed):
+    """Row 0 holds every column (a row of n entries, several chunks); every
+    other row holds its diagonal and column 0, so A^T's row 0 is full too."""
+    rng = np.random.default_rng(seed)
+    rows = [np.arange(n)] + [np.array([0, i]) for i in range(1, n)]
+    counts = np.array([r.size for r in rows])
+    rp = np.zeros(n + 1, dtype=np.int32)
+    rp[1:] = np.cumsum(counts)
+    col = np.concatenate(rows).astype(np.int32)
+    val = rng.uniform(-1.0, 1.0, (1, col.size))
+    z = np.zeros((1, n))
+    return W.Problem(f"star_{n}", n, rp, col, val, z, z)
+
+
+def powerlaw(n, seed, batch=1, dtype=np.float64, index=np.int32):
+    rp, col, val = W.powerlaw_graph_laplacian(n, seed)
+    rng = np.random.default_rng(seed + 1)
+    vals = np.repeat(val, batch, axis=0) * rng.uniform(0.5, 1.5, (batch, 1))
+    z = np.zeros((batch, n), dtype=dtype)
+    return W.Problem(f"powerlaw_{n}", n, rp.astype(index), col, vals.astype(dtype), z, z)
+
+
+CASES = {
+    "powerlaw_2^18": lambda: powerlaw(1 << 18, 5),
+    "powerlaw_2^16_batch3_fp32": lambda: powerlaw(1 << 16, 6, batch=3, dtype=np.float32),
+    "powerlaw_2^16_int64": lambda: powerlaw(1 << 16, 7, index=np.int64),
+    # rows of 8 / 9 entries (the walker's slots), 64 / 65 (a short block's rows)
+    "lengths_at_limits": lambda: lengths_pattern(9000, [3, 8, 9, 64, 65, 3, 3, 2, 1], {}, 3),
+    # one chunk exactly, one entry more, two chunks exactly, one more, three
+    "chunk_edges": lambda: lengths_pattern(
+        9000, [3, 5, 2], {5: 4096, 300: 4097, 301: 8192, 8000: 8193, 8999: 12289}, 4),
+    "star_20000": lambda: star_pattern(20000, 8),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_spmv_both_directions(hip, case):
+    banner(f"row plan spmv {case}")
+    p = CASES[case]()
+    _spmv_case(hip, p, transpose=False)
+    _spmv_case(hip, p, transpose=True)
+
+
+@pytest.mark.parametrize("case", ["powerlaw_2^16_batch3_fp32", "chunk_edges", "star_20000"])
+def test_matvec_adjoint(hip, case):
+    banner(f"row plan matvec adjoint {case}")
+    _vjp_case(hip, CASES[case]())
+
+
+def test_repeat_is_bitwise(hip):
+    """The plan's sums run in a fixed order: repeated products agree bit for bit."""
+    banner("row plan determinism")
+    p = powerlaw(1 << 18, 5)
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+    x = torch.from_numpy(np.random.default_rng(2).standard_normal((1, p.n))).cuda()
+    y0, t0 = pat.matvec(d["val"], x), pat.matvec(d["val"], x, transpose=True)
+    for _ in range(3):
+        assert torch.equal(pat.matvec(d["val"], x), y0)
+        assert torch.equal(pat.matvec(d["val"], x, transpose=True), t0)
+
+
+def test_cg_solve_and_adjoint_on_graph(hip):
+    """CG + Jacobi on the power-law graph Laplacian (+ I): the forward's A x0
+    product and the adjoint's gradient on the pattern run on the plan."""
+    banner("row plan solve + adjoint")
+    rp, col, val = W.powerlaw_graph_laplacian(30000, 11)
+    rng = np.random.default_rng(12)
+    p = W.Problem("powerlaw_30000_solve", 30000, rp, col, val, rng.standard_normal((1, 30000)),
+                  rng.uniform(-1.0, 1.0, (1, 30000)), method="cg", precond="jacobi", tol=1e-10,
+                  maxit=2000)
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p))
+    kw = dict(method="cg", precond="jacobi", tol=p.tol, maxit=p.maxit)
+    x, info = pat.solve(d["val"], d["b"], **kw)
+    gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
+    r, a = oracle_forward_adjoint(p)
+    tol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert info["status"][0] == 0 and ainfo["status"][0] == 0
+    assert relerr(x.cpu().numpy()[0], r.x[0]) <= tol
+    assert relerr(gb.cpu().numpy()[0], a.grad_b[0]) <= tol
+    assert relerr(gv.cpu().numpy()[0], a.grad_values[0]) <= tol
+    # the gradient is -lambda_i x_j entry by entry from the GPU's own lambda and x
+    lam, xs = gb.cpu().numpy()[0], x.cpu().numpy()[0]
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    assert np.array_equal(gv.cpu().numpy()[0], -(lam[rows] * xs[p.col]))
+    # an initial guess: A x0 on the plan
+    x0 = torch.from_numpy(rng.standard_normal((1, p.n))).cuda()
+    x2, info2 = pat.solve(d["val"], d["b"], x0=x0, **kw)
+    assert info2["status"][0] == 0
+    assert relerr(x2.cpu().numpy()[0], r.x[0]) <= tol
