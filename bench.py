@@ -88,7 +88,7 @@ def parse():
                     choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"),
                     help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
                          "the differentiable product and its backward pass on the same "
-                         "system, timed per call; inverse: kappa recovery through the "
+                         "system, 100 x steps calls timed; inverse: kappa recovery through the "
                          "differentiable solve (64 x 64 grid, 8 forcings, 40 x steps Adam "
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
                          "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
@@ -284,13 +284,14 @@ def summarize_trace(args):
     trace = _rows(args.summarize_trace, "*kernel_trace.csv")
     stats.sort(key=lambda r: -float(r["TotalDurationNs"]))
     op = "" if args.op == "solve" else f" --op {args.op}"
+    which = " --graph" if args.graph else f" --workload {args.workload}"
     out = [
         f"# Kernel time, bench.py{op} on workload {p.name}",
         "",
         "Commands (repository root; OUT is any output folder):",
         "  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- "
-        f"python3 bench.py{op} --steps 3 --warmup 1 --no-cpu-baseline --workload {args.workload}",
-        f"  python3 bench.py --summarize-trace OUT/trace{op} --workload {args.workload}",
+        f"python3 bench.py{op} --steps 3 --warmup 1 --no-cpu-baseline{which}",
+        f"  python3 bench.py --summarize-trace OUT/trace{op}{which}",
         "",
         "rocprofv3 --stats (all dispatches):",
         f"{'calls':>8} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel",
@@ -466,8 +467,11 @@ def bench_product(args, p):
         kernel = ("diag_vjp_kernel" if pat.column_mode() == "diagonal"
                   else "spmv_perm_kernel+grad_kernel" + plan + ("+plan_grad_kernel" if plan else ""))
     model *= p.batch
-    steps = max(args.steps, 1) * 10
-    for _ in range(max(args.warmup, 1)):
+    # a call takes tens of microseconds: enough calls that the timed region
+    # spans milliseconds, after warm-up calls that bring the clocks up
+    steps = max(args.steps, 1) * 100
+    warm = max(args.warmup, 1) * 50
+    for _ in range(warm):
         call()
     stream = torch.cuda.current_stream()
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -484,7 +488,7 @@ def bench_product(args, p):
     achieved = model / per / 1e9
     print(json.dumps({
         "metric": f"differentiable {args.op} calls/sec", "value": steps / wall,
-        "unit": "calls/s", "n_gpus": 1, "steps": steps, "warmup": max(args.warmup, 1),
+        "unit": "calls/s", "n_gpus": 1, "steps": steps, "warmup": warm,
         "ms_per_step": wall * 1e3 / steps, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f64" if p.values.dtype == np.float64 else "f32",
         "data": "synthetic", "config": {"workload": p.name, "n": p.n, "nnz": p.nnz,

@@ -528,15 +528,16 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
     return st;
 }
 
-// Compact columns for the pattern (rp, col) when every entry fits.
+// Compact columns for the pattern (rp, col), longest row max_len, when
+// every entry fits.
 template <typename IT>
-hipError_t build_col16(sla_ctx *h, const IT *rp, const int32_t *col, int16_t **out,
-                       hipStream_t s) {
+hipError_t build_col16(sla_ctx *h, const IT *rp, const int32_t *col, int32_t max_len,
+                       int16_t **out, hipStream_t s) {
     int32_t fits = 0;
-    hipError_t e = setup_col16<IT>(rp, col, h->n, nullptr, h->flag, &fits, s);
+    hipError_t e = setup_col16<IT>(rp, col, h->n, h->nnz, max_len, nullptr, h->flag, &fits, s);
     if (e != hipSuccess || !fits) return e;
     if ((e = dmalloc(h, out, sizeof(int16_t) * h->nnz)) != hipSuccess) return e;
-    return setup_col16<IT>(rp, col, h->n, *out, h->flag, &fits, s);
+    return setup_col16<IT>(rp, col, h->n, h->nnz, max_len, *out, h->flag, &fits, s);
 }
 
 // Diagonal masks for the pattern (rp, col) when its entries lie on at most
@@ -584,12 +585,14 @@ hipError_t build_plan(sla_ctx *h, int which, const IT *rp_dev, const int32_t *co
     std::vector<PlanFin> fin;
     std::vector<uint8_t> tiles((size_t)tiles_of(n), 0);
     int32_t nslots = 0;
+    int64_t ntiles_planned = 0;
     for (int64_t t = 0; t < tiles_of(n); ++t) {
         const int64_t a = t * kTileRows, b = std::min<int64_t>(a + kTileRows, n);
         int64_t longest = 0;
         for (int64_t r = a; r < b; ++r) longest = std::max<int64_t>(longest, rp[r + 1] - rp[r]);
         if ((int64_t)(rp[b] - rp[a]) <= kCap && longest <= slots) continue;  // the walker's
         tiles[(size_t)t] = 1;
+        ++ntiles_planned;
         for (int64_t r = a; r < b;) {
             const int64_t len = (int64_t)(rp[r + 1] - rp[r]);
             if (len > kShortRow) {  // a long row: chunks of kPlanCap entries
@@ -637,6 +640,7 @@ hipError_t build_plan(sla_ctx *h, int which, const IT *rp_dev, const int32_t *co
     }
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;  // items and fin are host buffers
     pl.tiles = reinterpret_cast<const uint8_t *>(mem[3]);
+    pl.all_tiles = ntiles_planned == (int64_t)tiles.size();
     pl.items = reinterpret_cast<const PlanItem *>(mem[0]);
     pl.nitems = (int32_t)items.size();
     pl.fin = reinterpret_cast<const PlanFin *>(mem[1]);
@@ -682,7 +686,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
                                    h->slots_t, h->plan_t, s)));
         if (compact) {
             const IT *rpt = reinterpret_cast<const IT *>(h->rp_t);
-            HIP_TRY(build_col16<IT>(h, rpt, h->col_t, &h->col16_t, s));
+            HIP_TRY(build_col16<IT>(h, rpt, h->col_t, maxlen, &h->col16_t, s));
             h->ca_t.col16 = h->col16_t;
             if (h->col16_t) h->ca_t.mode = kColTile16;
             HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));
@@ -692,7 +696,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     }
     h->ca.col = h->col;
     if (compact) {
-        HIP_TRY(build_col16<IT>(h, rp, h->col, &h->col16, s));
+        HIP_TRY(build_col16<IT>(h, rp, h->col, h->max_len, &h->col16, s));
         h->ca.col16 = h->col16;
         if (h->col16) h->ca.mode = kColTile16;
         if (!h->dlt) HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));

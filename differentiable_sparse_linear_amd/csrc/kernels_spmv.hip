@@ -286,7 +286,9 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     }
 }
 
-// A split row's value: its chunks' partials added in chunk order.
+// A split row's value from its chunks' partials, one wavefront per split
+// row: lane l adds partials l, l + 64, ... in order, then a fixed-order
+// wavefront sum.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__restrict__ fin,
                                                              int32_t nfin,
@@ -294,13 +296,15 @@ __global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__re
                                                              int32_t nslots, T *__restrict__ y,
                                                              int64_t vec_stride) {
     const int sys = blockIdx.y;
-    const int f = blockIdx.x * kBlock + threadIdx.x;
+    const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);  // the same in the whole wavefront
     if (f >= nfin) return;
+    const int lane = threadIdx.x & 63;
     const PlanFin r = fin[f];
     const T *p = part + (int64_t)sys * nslots + r.slot0;
     T s = T(0);
-    for (int c = 0; c < r.nch; ++c) s += p[c];
-    y[(int64_t)sys * vec_stride + r.row] = s;
+    for (int c = lane; c < r.nch; c += 64) s += p[c];
+    s = wave_sum_t(s);
+    if (lane == 0) y[(int64_t)sys * vec_stride + r.row] = s;
 }
 
 // The gradient on the pattern for one item: g[row(k)] x[col[k]] (NEG:
@@ -430,7 +434,7 @@ void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, cons
     plan_spmv_kernel<T, IT, PERM><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
         pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots);
     if (pl.nfin > 0)
-        plan_finish_kernel<T><<<dim3((pl.nfin + kBlock - 1) / kBlock, batch), kBlock, 0, s>>>(
+        plan_finish_kernel<T><<<dim3((pl.nfin + kWaves - 1) / kWaves, batch), kBlock, 0, s>>>(
             pl.fin, pl.nfin, part, pl.nslots, y, vec_stride);
 }
 
@@ -441,10 +445,12 @@ hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const bool ps = planned(plan);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
-    SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC>
-                                                <<<grid, kBlock, 0, s>>>(rp, ca, val, val_stride,
-                                                                         x, y, n, vec_stride,
-                                                                         pt)));
+    if (!ps || !plan->all_tiles) {
+        SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC>
+                                                    <<<grid, kBlock, 0, s>>>(rp, ca, val,
+                                                                             val_stride, x, y, n,
+                                                                             vec_stride, pt)));
+    }
     if (ps)
         launch_plan_spmv<T, IT, false>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
                                        batch, s);
@@ -458,10 +464,12 @@ hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const in
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const bool ps = planned(plan);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
-    SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
-                                                <<<grid, kBlock, 0, s>>>(rp, ca, perm, val,
-                                                                         val_stride, x, y, n,
-                                                                         vec_stride, pt)));
+    if (!ps || !plan->all_tiles) {
+        SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
+                                                    <<<grid, kBlock, 0, s>>>(rp, ca, perm, val,
+                                                                             val_stride, x, y, n,
+                                                                             vec_stride, pt)));
+    }
     if (ps)
         launch_plan_spmv<T, IT, true>(*plan, rp, perm, val, val_stride, x, y, vec_stride, batch,
                                       s);
@@ -520,7 +528,9 @@ hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x
         grad_kernel<T, IT, true, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt); \
     else                                                                                      \
         grad_kernel<T, IT, false, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt)
-    if (ca.mode == kColTile16) {
+    if (ps && plan->all_tiles) {
+        // every tile is the plan's
+    } else if (ca.mode == kColTile16) {
         SLA_GRAD(kColTile16);
     } else {
         SLA_GRAD(kColWide);

@@ -10,11 +10,25 @@
 // perm[kt] = k in column-major order with rows ascending inside each column,
 // so row kt of A^T is sorted; col_t[kt] = row(perm[kt]); row_ptr_t[c] is the
 // first kt whose key is >= c, found from the sorted keys without atomics.
+//
+// Per-row loops over a row's entries serialise on long rows (a graph hub
+// of half a million entries), so patterns whose longest row exceeds
+// kShortRow are checked entry by entry from the row of every entry.
 #include <hipcub/hipcub.hpp>
 
 #include "sla_internal.h"
 
 namespace sla {
+
+// Sets *flag when any lane of the wavefront saw `bad`: one atomic per
+// wavefront at most, none once the flag reads set (a check that fails
+// everywhere would otherwise queue an atomic from every wavefront on one
+// word).
+__device__ __forceinline__ void raise_flag(int bad, int32_t *flag) {
+    if (__any(bad) && (threadIdx.x & 63) == 0 &&
+        __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        atomicOr(flag, 1);
+}
 
 template <typename IT>
 __global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restrict__ rp, int64_t n,
@@ -27,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restri
         if (i == 0 && a != 0) bad = 1;
         if (i == n - 1 && (int64_t)b != nnz) bad = 1;
     }
-    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+    raise_flag(bad, flag);
 }
 
 template <typename IT>
@@ -50,15 +64,48 @@ __global__ __launch_bounds__(kBlock) void check_cols_kernel(const IT *__restrict
         if (dpos < 0) bad = 1;
         diagpos[i] = dpos;
     }
-    if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1);
+    raise_flag(bad, flag);
 }
 
+// The row of every entry, first step: each row that holds entries writes
+// its index at its first entry (rowidx zeroed before); an inclusive
+// max-scan then carries every mark over the row's other entries (an empty
+// row writes nothing and its index is below the next row's).
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void row_index_kernel(const IT *__restrict__ rp, int64_t n,
+__global__ __launch_bounds__(kBlock) void row_start_kernel(const IT *__restrict__ rp, int64_t n,
                                                            int32_t *__restrict__ rowidx) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
-        for (IT k = rp[i]; k < rp[i + 1]; ++k) rowidx[k] = (int32_t)i;
+        if (rp[i + 1] > rp[i]) rowidx[rp[i]] = (int32_t)i;
+}
+
+// Entry k of row r = rowidx[k]: its column in range and above the previous
+// entry's when that entry is in the same row; the diagonal's position
+// (diagpos preset to -1; check_diag_kernel flags the rows without one).
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void check_cols_entries_kernel(
+    const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ rowidx,
+    int64_t n, int64_t nnz, IT *__restrict__ diagpos, int32_t *flag) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int bad = 0;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride) {
+        const int32_t r = rowidx[k];
+        const int64_t c = col[k];
+        if (c < 0 || c >= n) bad = 1;
+        if (k > (int64_t)rp[r] && c <= (int64_t)col[k - 1]) bad = 1;
+        if (c == r) diagpos[r] = (IT)k;
+    }
+    raise_flag(bad, flag);
+}
+
+template <typename IT>
+__global__ __launch_bounds__(kBlock) void check_diag_kernel(const IT *__restrict__ diagpos,
+                                                            int64_t n, int32_t *flag) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int bad = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+        if (diagpos[i] < 0) bad = 1;
+    raise_flag(bad, flag);
 }
 
 __global__ __launch_bounds__(kBlock) void iota_kernel(int32_t *a, int64_t m) {
@@ -128,7 +175,25 @@ __global__ __launch_bounds__(kBlock) void col16_kernel(const IT *__restrict__ rp
             if (out && ok) out[k] = (int16_t)d;
         }
     }
-    if (__any(b) && (threadIdx.x & 63) == 0) atomicOr(bad, 1);
+    raise_flag(b, bad);
+}
+
+// The same entry by entry, from the row of every entry.
+__global__ __launch_bounds__(kBlock) void col16_entries_kernel(const int32_t *__restrict__ col,
+                                                               const int32_t *__restrict__ rowidx,
+                                                               int64_t nnz,
+                                                               int16_t *__restrict__ out,
+                                                               int32_t *bad) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int b = 0;
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride) {
+        const int64_t row0 = (int64_t)rowidx[k] / kTileRows * kTileRows;
+        const int64_t d = (int64_t)col[k] - row0;
+        const bool ok = d >= -32768 && d <= 32767;
+        b |= !ok;
+        if (out && ok) out[k] = (int16_t)d;
+    }
+    raise_flag(b, bad);
 }
 
 // Distinct diagonals: each block gathers the offsets (col - row) of its
@@ -193,6 +258,33 @@ static unsigned blocks_for(int64_t m) {
     return (unsigned)b;
 }
 
+// rowidx[k] = the row of entry k, for a valid row_ptr (synchronizes the
+// stream; temporary scan storage).
+template <typename IT>
+hipError_t setup_row_index(const IT *rp, int64_t n, int64_t nnz, int32_t *rowidx, hipStream_t s) {
+    hipError_t e = hipMemsetAsync(rowidx, 0, sizeof(int32_t) * nnz, s);
+    if (e != hipSuccess) return e;
+    row_start_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    size_t tb = 0;
+    if ((e = hipcub::DeviceScan::InclusiveScan(nullptr, tb, rowidx, hipcub::Max(), nnz, s)) !=
+        hipSuccess)
+        return e;
+    void *temp = nullptr;
+    if ((e = hipMalloc(&temp, tb > 0 ? tb : 1)) != hipSuccess) return e;
+    e = hipcub::DeviceScan::InclusiveScan(temp, tb, rowidx, hipcub::Max(), nnz, s);
+    const hipError_t es = hipStreamSynchronize(s);
+    (void)hipFree(temp);
+    return e != hipSuccess ? e : es;
+}
+
+// Whether a pattern is checked entry by entry: a row past kShortRow and
+// fewer than 2^31 entries (the row of every entry, 4 bytes each, held
+// while checking).
+inline bool entrywise(int32_t max_len, int64_t nnz) {
+    return max_len > kShortRow && nnz < ((int64_t)1 << 31);
+}
+
 template <typename IT>
 hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
                           int32_t *flag, hipStream_t s) {
@@ -205,8 +297,26 @@ hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t n
         return e;
     if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
     if (h) return hipSuccess;  // flag stays set: row_ptr invalid, columns not read
-    check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
-    return hipGetLastError();
+    int32_t max_len = 0;
+    if ((e = setup_max_row<IT>(rp, n, flag, &max_len, s)) != hipSuccess) return e;
+    if ((e = hipMemsetAsync(flag, 0, sizeof(int32_t), s)) != hipSuccess) return e;
+    if (!entrywise(max_len, nnz)) {
+        check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
+        return hipGetLastError();
+    }
+    int32_t *rowidx = nullptr;
+    if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) return e;
+    do {
+        if ((e = setup_row_index<IT>(rp, n, nnz, rowidx, s)) != hipSuccess) break;
+        if ((e = hipMemsetAsync(diagpos, 0xff, sizeof(IT) * n, s)) != hipSuccess) break;
+        check_cols_entries_kernel<IT>
+            <<<blocks_for(nnz), kBlock, 0, s>>>(rp, col, rowidx, n, nnz, diagpos, flag);
+        check_diag_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(diagpos, n, flag);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        e = hipStreamSynchronize(s);  // rowidx is freed next
+    } while (0);
+    (void)hipFree(rowidx);
+    return e;
 }
 
 // Longest row of a valid pattern (synchronizes the stream).
@@ -266,12 +376,27 @@ hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const i
 }
 
 template <typename IT>
-hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int16_t *out,
-                       int32_t *scratch, int32_t *fits, hipStream_t s) {
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, int32_t max_len,
+                       int16_t *out, int32_t *scratch, int32_t *fits, hipStream_t s) {
     hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
-    col16_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, out, scratch);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!entrywise(max_len, nnz)) {
+        col16_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, out, scratch);
+        e = hipGetLastError();
+    } else {
+        int32_t *rowidx = nullptr;
+        if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) return e;
+        e = setup_row_index<IT>(rp, n, nnz, rowidx, s);
+        if (e == hipSuccess) {
+            col16_entries_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(col, rowidx, nnz, out,
+                                                                    scratch);
+            e = hipGetLastError();
+            const hipError_t es = hipStreamSynchronize(s);  // rowidx is freed next
+            if (e == hipSuccess) e = es;
+        }
+        (void)hipFree(rowidx);
+    }
+    if (e != hipSuccess) return e;
     int32_t bad = 1;
     if ((e = hipMemcpyAsync(&bad, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
@@ -295,8 +420,8 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
         if ((e = hipMalloc(&vals_in, sizeof(int32_t) * nnz)) != hipSuccess) break;
         if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) break;
         iota_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(vals_in, nnz);
-        row_index_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
         if ((e = hipGetLastError()) != hipSuccess) break;
+        if ((e = setup_row_index<IT>(rp, n, nnz, rowidx, s)) != hipSuccess) break;
         e = hipcub::DeviceRadixSort::SortPairs(nullptr, temp_bytes, col, keys_out, vals_in, perm,
                                                m, 0, end_bit, s);
         if (e != hipSuccess) break;
@@ -328,10 +453,10 @@ template hipError_t setup_diag_masks<int32_t>(const int32_t *, const int32_t *, 
                                               const int32_t *, int32_t, uint16_t *, hipStream_t);
 template hipError_t setup_diag_masks<int64_t>(const int64_t *, const int32_t *, int64_t,
                                               const int32_t *, int32_t, uint16_t *, hipStream_t);
-template hipError_t setup_col16<int32_t>(const int32_t *, const int32_t *, int64_t, int16_t *,
-                                         int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_col16<int64_t>(const int64_t *, const int32_t *, int64_t, int16_t *,
-                                         int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_col16<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
+                                         int32_t, int16_t *, int32_t *, int32_t *, hipStream_t);
+template hipError_t setup_col16<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
+                                         int32_t, int16_t *, int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_max_row<int32_t>(const int32_t *, int64_t, int32_t *, int32_t *,
                                            hipStream_t);
 template hipError_t setup_max_row<int64_t>(const int64_t *, int64_t, int32_t *, int32_t *,

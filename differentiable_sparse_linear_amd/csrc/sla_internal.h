@@ -337,7 +337,10 @@ inline void launch_maybe_timed(void (*k)(KArgs...), dim3 grid, dim3 block, uint3
 constexpr int kEpt = 8;              // staged entries per thread (tile walker)
 constexpr int kCap = kBlock * kEpt;  // staged entries per tile
 constexpr int kShortRow = 64;
-constexpr int kPlanEpt = 16;
+#ifndef SLA_PLAN_EPT
+#define SLA_PLAN_EPT 8
+#endif
+constexpr int kPlanEpt = SLA_PLAN_EPT;
 constexpr int kPlanCap = kBlock * kPlanEpt;  // entries per short block or chunk
 struct PlanItem {
     int32_t r0, r1;  // rows [r0, r1) (a long row's chunk: r1 = r0 + 1)
@@ -350,6 +353,7 @@ struct PlanFin {
 };
 struct RowPlan {
     const uint8_t *tiles = nullptr;  // [tiles] 1 where the plan covers the tile
+    bool all_tiles = false;          // it covers every tile: no tile kernel at all
     const PlanItem *items = nullptr;
     int32_t nitems = 0;
     const PlanFin *fin = nullptr;
@@ -481,8 +485,8 @@ hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const i
 // With out == nullptr only checks; *fits = 1 when every entry fits
 // (synchronizes `s`).
 template <typename IT>
-hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int16_t *out,
-                       int32_t *scratch, int32_t *fits, hipStream_t s);
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, int32_t max_len,
+                       int16_t *out, int32_t *scratch, int32_t *fits, hipStream_t s);
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
                            int32_t *col_t, int32_t *perm, hipStream_t s);

@@ -348,7 +348,8 @@ __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<c
         const uint32_t mk = kDiag ? (uint32_t)col.msk[row0 + me] : 0u;
         const IT base = cr[0];
         const int64_t cnt = (int64_t)(cr[rows] - base);
-        const bool planned = plan_tiles && plan_tiles[t];
+        // (a diagonal-mask pattern has rows of at most 8 entries: never a plan)
+        const bool planned = !kDiag && plan_tiles && plan_tiles[t];
         const bool staged = !planned && cnt > 0 && cnt <= kCap;
         if (staged) {
             const int last = (int)cnt - 1;

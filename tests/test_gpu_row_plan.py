@@ -3,18 +3,19 @@ gradient.
 
 Tiles whose entries exceed the tile walker's LDS stage, or that hold a row
 longer than its gather slots, are covered by a plan built at set-up: short
-blocks (rows of at most 64 entries, at most 4096 entries per block) and long
-rows split into chunks of 4096 entries, one workgroup each, with a last pass
+blocks (rows of at most 64 entries, at most 2048 entries per block) and long
+rows split into chunks of 2048 entries, one workgroup each, with a last pass
 over the chunks of a split row.  Checked against the oracle: y = A x and
 y = A^T x (fp64 and fp32, batches, int64 row pointers), the product's
 backward pass, and a CG solve + adjoint whose gradient runs on the plan;
-row lengths straddle the plan's limits (64 / 65 entries, 4096 / 4097, a row
+row lengths straddle the plan's limits (64 / 65 entries, 2048 / 2049, a row
 of many chunks).
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import workloads as W
 from gpu_helpers import FP_TOL, banner, oracle_forward_adjoint, relerr, tdtype, to_dev
 from test_gpu_parity import _spmv_case, _vjp_case
@@ -70,9 +71,11 @@ CASES = {
     "powerlaw_2^16_int64": lambda: powerlaw(1 << 16, 7, index=np.int64),
     # rows of 8 / 9 entries (the walker's slots), 64 / 65 (a short block's rows)
     "lengths_at_limits": lambda: lengths_pattern(9000, [3, 8, 9, 64, 65, 3, 3, 2, 1], {}, 3),
-    # one chunk exactly, one entry more, two chunks exactly, one more, three
+    # one chunk of 2048 exactly, one entry more, two chunks exactly, one
+    # more, four exactly, four and one, six and one
     "chunk_edges": lambda: lengths_pattern(
-        9000, [3, 5, 2], {5: 4096, 300: 4097, 301: 8192, 8000: 8193, 8999: 12289}, 4),
+        9000, [3, 5, 2],
+        {1: 2048, 2: 2049, 5: 4096, 300: 4097, 301: 8192, 8000: 8193, 8999: 12289}, 4),
     "star_20000": lambda: star_pattern(20000, 8),
 }
 
@@ -133,3 +136,45 @@ def test_cg_solve_and_adjoint_on_graph(hip):
     x2, info2 = pat.solve(d["val"], d["b"], x0=x0, **kw)
     assert info2["status"][0] == 0
     assert relerr(x2.cpu().numpy()[0], r.x[0]) <= tol
+
+
+@pytest.mark.parametrize("case", ["powerlaw_2^18", "star_20000", "chunk_edges"])
+def test_setup_with_long_rows_bit_exact(hip, case):
+    """Set-up of patterns with rows past 64 entries (checked entry by entry):
+    the diagonal index and the transpose map equal the oracle's."""
+    banner(f"row plan setup {case}")
+    p = CASES[case]()
+    rp, col, n = p.row_ptr, p.col, p.n
+    st, dp = O.check_pattern(n, rp, col)
+    assert st == O.OK
+    rpt, ct, perm = O.transpose(n, rp, col)
+    pat = hip.Pattern(torch.from_numpy(rp).cuda(), torch.from_numpy(col).cuda(),
+                      build_transpose=True)
+    g_dp, g_rpt, g_ct, g_perm = pat.export_pattern()
+    assert np.array_equal(g_dp.cpu().numpy().astype(np.int64), dp)
+    assert np.array_equal(g_rpt.cpu().numpy().astype(np.int64), rpt)
+    assert np.array_equal(g_ct.cpu().numpy(), ct)
+    assert np.array_equal(g_perm.cpu().numpy().astype(np.int64), perm)
+
+
+def test_invalid_long_row_patterns_rejected(hip):
+    """The entry-by-entry checks reject what the oracle rejects: columns out
+    of order, repeated, out of range, and a row without its diagonal, in a
+    pattern whose longest row is past 64 entries."""
+    banner("row plan invalid patterns")
+    p = CASES["lengths_at_limits"]()
+    rp, col, n = p.row_ptr, p.col, p.n
+    long_row = int(np.argmax(np.diff(rp)))
+    k = int(rp[long_row]) + 10  # inside the long row
+    one = next(i for i in range(n - 1) if rp[i + 1] - rp[i] == 1)  # a row of its diagonal only
+    cases = []
+    bad = col.copy(); bad[k], bad[k + 1] = bad[k + 1], bad[k]; cases.append(bad)
+    bad = col.copy(); bad[k + 1] = bad[k]; cases.append(bad)
+    bad = col.copy(); bad[int(rp[long_row + 1]) - 1] = n; cases.append(bad)
+    bad = col.copy(); bad[int(rp[long_row])] = -1; cases.append(bad)
+    bad = col.copy(); bad[int(rp[one])] = one + 1; cases.append(bad)
+    for c in cases:
+        assert O.check_pattern(n, rp, c)[0] == O.ERR_PATTERN
+        with pytest.raises(hip.SlaError) as ei:
+            hip.Pattern(torch.from_numpy(rp).cuda(), torch.from_numpy(c).cuda())
+        assert ei.value.status == hip.SLA_ERR_PATTERN
