@@ -276,14 +276,31 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                                    nsys, s, op.plan));
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n * nsys, s));
-    if (cg)
+    // CG on an operator with a row plan (long rows) runs split iterations:
+    // the fused kernel's tile walker would take those rows a wavefront each
+    const bool split = cg && !dmaj && op.plan && op.plan->nitems > 0;
+    const IT *dpos = reinterpret_cast<const IT *>(h->diagpos);
+    if (split) {
+        HIP_TRY(launch_cg_split_init<T, IT>(jac, ad, n, nsys, s));
+        HIP_TRY(launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, a.r, a.v[0], n, n, nsys, s,
+                                   op.plan));
+        HIP_TRY(launch_cg_split_w<T, IT>(jac, true, ad, dpos, n, nsys, 0, s));
+    } else if (cg) {
         HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, nsys, s));
-    else
+    } else {
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
+    }
 
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
+        if (split) {
+            if ((e = launch_cg_split_u<T, IT>(jac, ad, n, nsys, k & 1, ss)) != hipSuccess) return e;
+            if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, a.r, a.v[0], n, n, nsys,
+                                        ss, op.plan, st)) != hipSuccess)
+                return e;
+            return launch_cg_split_w<T, IT>(jac, false, ad, dpos, n, nsys, k & 1, ss);
+        }
         if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, nsys, k & 1, ss);
         if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
@@ -304,7 +321,12 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         }
         size_t ev = 0;
         for (int k = 0; k < launches; ++k) {
-            if (cg) {
+            if (split) {  // the three launches between a pair of stream events
+                HIP_TRY(hipEventRecord(h->prof_ev[ev], s));
+                HIP_TRY(one_iter(s, k));
+                HIP_TRY(hipEventRecord(h->prof_ev[ev + 1], s));
+                ev += 2;
+            } else if (cg) {
                 HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, 1, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;

@@ -289,6 +289,162 @@ __global__ __launch_bounds__(kBlock) void cg_lag_kernel(const SolveState *st, co
         x[i] = fmaT(a, p[i], x[i]);
 }
 
+// ------------------------------------------------------------ split iteration
+//
+// Patterns with a row plan (rows past the tile walker's stage or slots) run
+// the same recurrence as three launches per iteration instead of one: the row
+// updates (cg_split_u_kernel), the product w = A u through the products' tile
+// kernel and row plan, and the scaled product with the partial sums
+// (cg_split_w_kernel).  Scalars, stop tests and partial-sum slots are those of
+// cg_iter_kernel; x is brought up to date every iteration (no lag).  Vectors:
+// u in r, w^ in q, s^ in s, p in p[0], the raw product in v[0]; t holds A x0.
+
+// r_0 = b - A x_0, u_0 = M^-1 r_0 (A x_0 in t, zeroed without a guess); x = 0
+// without an initial guess.
+template <typename T, typename IT, bool JAC>
+__global__ __launch_bounds__(kBlock) void cg_split_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;
+    const int64_t n = A->n;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T ri = A->b[i] - A->t[i];
+        A->r[i] = JAC ? A->dinv[i] * ri : ri;
+        if (!A->use_x0) A->x[i] = T(0);
+    }
+}
+
+// Iteration i (i = st->iter_p[PH]): the stop tests and scalars of
+// cg_iter_kernel, then p_i = u_i + beta p_{i-1}, s^_i = w^_i + beta s^_{i-1},
+// u_{i+1} = u_i - alpha s^_i, x_{i+1} = x_i + alpha p_i.
+template <typename T, typename IT, bool JAC, int PH>
+__global__ __launch_bounds__(kBlock) void cg_split_u_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;
+    SolveState *st = A->st;
+    __shared__ int seen[kWaves];
+    __shared__ double red[4][kWaves];
+    const bool stopped = saw_stop(st, seen);
+    const int it = st->iter_p[PH];
+    const bool first = PH == 0 && it == 0;
+    if (!stopped) {
+        if (first) {
+            const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
+            partial_loads<4>(A->part, slot, red);
+        } else {
+            const int slot[3] = {PH ? kCgGA1 : kCgGA, PH ? kCgDE1 : kCgDE, PH ? kCgRR1 : kCgRR};
+            partial_loads<3>(A->part, slot, red);
+        }
+    }
+    __syncthreads();
+    if (any_saw_stop(seen)) return;
+    double tot[4];
+    if (first) {
+        totals<4>(red, tot);
+    } else {
+        double t3[3];
+        totals<3>(red, t3);
+        tot[0] = t3[0];
+        tot[1] = t3[1];
+        tot[2] = t3[2];
+        tot[3] = st->bb;
+    }
+    const double gamma = tot[0], delta = tot[1], rr = tot[2], bb = tot[3];
+    if (first && st->zero_diag) {
+        finish(st, A->ndone, SLA_ERR_ZERO_DIAG, 0, rr);
+        return;
+    }
+    if (first && bb == 0.0) {
+        if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+        finish(st, A->ndone, SLA_OK, 0, 0.0);
+        return;
+    }
+    if (sqrt(rr) <= A->tol * sqrt(bb)) {
+        finish(st, A->ndone, SLA_OK, it, rr);
+        return;
+    }
+    if (it >= A->maxit) {
+        finish(st, A->ndone, SLA_NOT_CONVERGED, it, rr);
+        return;
+    }
+    const double beta_d = first ? 0.0 : gamma / st->rho[PH ^ 1];
+    const double den = first ? delta : delta - beta_d * gamma / st->alpha[PH ^ 1];
+    if (!(den > 0.0)) {
+        finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
+        return;
+    }
+    const double alpha_d = gamma / den;
+    if (block0()) {
+        st->rho[PH] = gamma;
+        st->alpha[PH] = alpha_d;
+        st->iter_p[PH ^ 1] = it + 1;
+        st->nfused += 1;
+        st->spmv += first ? (A->use_x0 ? 3 : 2) : 1;  // init (and A x0) products
+        if (first) st->bb = bb;
+    }
+    const T beta = (T)beta_d, alpha = (T)alpha_d;
+    const int64_t n = A->n;
+    const gptr<T> u = glb(A->r), w = glb(A->q), sv = glb(A->s), p = glb(A->p[0]), x = glb(A->x);
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T ui = u[i], wi = w[i];
+        const T pi = first ? ui : fmaT(beta, p[i], ui);
+        const T si = first ? wi : fmaT(beta, sv[i], wi);
+        p[i] = pi;
+        sv[i] = si;
+        u[i] = fmaT(-alpha, si, ui);
+        x[i] = fmaT(alpha, pi, x[i]);
+    }
+}
+
+// After the product w = A u (in v[0]): w^ = w / a_ii (INIT: w * dinv, as
+// cg_init_kernel), and the partial sums gamma = r.u, delta = w.u, ||r||^2
+// (INIT: r_0 = b - A x0 and also ||b||^2) in the slots cg_iter_kernel uses.
+template <typename T, typename IT, bool JAC, int PH, bool INIT>
+__global__ __launch_bounds__(kBlock) void cg_split_w_kernel(const IterArgs<T, IT> *__restrict__ A,
+                                                            const IT *__restrict__ diagpos) {
+    A += blockIdx.y;
+    if (!INIT && load_done(A->st)) return;  // set by an earlier launch: uniform
+    const int64_t n = A->n;
+    const gptr<const T> wraw = glb((const T *)A->v[0]);
+    const gptr<const T> u = glb((const T *)A->r);
+    const gptr<T> w = glb(A->q);
+    double g = 0.0, d = 0.0, q = 0.0, bb = 0.0;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T acc = wraw[i], ui = u[i];
+        if (INIT) {
+            const T bi = A->b[i];
+            const T ri = bi - A->t[i];
+            w[i] = JAC ? acc * A->dinv[i] : acc;
+            g = fma((double)ri, (double)ui, g);
+            d = fma((double)acc, (double)ui, d);
+            q = fma((double)ri, (double)ri, q);
+            bb = fma((double)bi, (double)bi, bb);
+        } else {
+            const T aii = JAC ? A->val[diagpos[i]] : T(1);
+            w[i] = JAC ? acc / aii : acc;
+            const T ri = JAC ? aii * ui : ui;
+            g = fma((double)ri, (double)ui, g);
+            d = fma((double)acc, (double)ui, d);
+            q = fma((double)ri, (double)ri, q);
+        }
+    }
+    if (INIT) {
+        double v[4] = {g, d, q, bb};
+        const int slot[4] = {kCgGA, kCgDE, kCgRR, kCgBB};
+        store_partials<4>(v, A->part, slot);
+    } else {
+        double v[3] = {g, d, q};
+        const int slot[3] = {PH ? kCgGA : kCgGA1, PH ? kCgDE : kCgDE1, PH ? kCgRR : kCgRR1};
+        store_partials<3>(v, A->part, slot);
+    }
+}
+
 // ------------------------------------------------------------ block path
 
 constexpr int kBW = kBlockSolveThreads / 64;  // waves per workgroup
@@ -643,6 +799,55 @@ hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipSt
     return hipGetLastError();
 }
 
+template <typename T, typename IT>
+hipError_t launch_cg_split_init(bool jac, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                                hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    if (jac)
+        cg_split_init_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(a);
+    else
+        cg_split_init_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_cg_split_u(bool jac, const IterArgs<T, IT> *a, int64_t n, int nsys, int ph,
+                             hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    if (jac) {
+        if (ph)
+            cg_split_u_kernel<T, IT, true, 1><<<grid, kBlock, 0, s>>>(a);
+        else
+            cg_split_u_kernel<T, IT, true, 0><<<grid, kBlock, 0, s>>>(a);
+    } else {
+        if (ph)
+            cg_split_u_kernel<T, IT, false, 1><<<grid, kBlock, 0, s>>>(a);
+        else
+            cg_split_u_kernel<T, IT, false, 0><<<grid, kBlock, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_cg_split_w(bool jac, bool init, const IterArgs<T, IT> *a, const IT *diagpos,
+                             int64_t n, int nsys, int ph, hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+#define SLA_SPLIT_W(J)                                                                   \
+    if (init)                                                                            \
+        cg_split_w_kernel<T, IT, J, 0, true><<<grid, kBlock, 0, s>>>(a, diagpos);        \
+    else if (ph)                                                                         \
+        cg_split_w_kernel<T, IT, J, 1, false><<<grid, kBlock, 0, s>>>(a, diagpos);       \
+    else                                                                                 \
+        cg_split_w_kernel<T, IT, J, 0, false><<<grid, kBlock, 0, s>>>(a, diagpos)
+    if (jac) {
+        SLA_SPLIT_W(true);
+    } else {
+        SLA_SPLIT_W(false);
+    }
+#undef SLA_SPLIT_W
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_cg_lag(const SolveState *st, const T *p, T *x, int64_t n, int nsys,
                          hipStream_t s) {
@@ -663,7 +868,13 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
     template hipError_t launch_cg_iter<T, IT>(int, int, bool, bool, const IterArgs<T, IT> *, \
                                               int64_t, int, int, hipStream_t,                   \
                                               const hipEvent_t *);                              \
-    template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);
+    template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);  \
+    template hipError_t launch_cg_split_init<T, IT>(bool, const IterArgs<T, IT> *, int64_t, int, \
+                                                    hipStream_t);                              \
+    template hipError_t launch_cg_split_u<T, IT>(bool, const IterArgs<T, IT> *, int64_t, int,    \
+                                                 int, hipStream_t);                            \
+    template hipError_t launch_cg_split_w<T, IT>(bool, bool, const IterArgs<T, IT> *, const IT *, \
+                                                 int64_t, int, int, hipStream_t);
 
 SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)

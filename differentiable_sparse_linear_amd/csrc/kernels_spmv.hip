@@ -17,7 +17,11 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride,
-                                                      const uint8_t *plan_tiles) {
+                                                      const uint8_t *plan_tiles,
+                                                      const SolveState *stop) {
+    // a solver's product: nothing to do once the system has stopped (set by
+    // an earlier launch, so every wavefront reads the same)
+    if (stop && load_done(stop + blockIdx.y)) return;
     __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
@@ -228,7 +232,8 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
     const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
     const T *__restrict__ x, T *__restrict__ y, int64_t vec_stride, T *__restrict__ part,
-    int32_t nslots) {
+    int32_t nslots, const SolveState *stop) {
+    if (stop && load_done(stop + blockIdx.y)) return;
     __shared__ T prod[kPlanCap];
     __shared__ T wsum[kWaves];
     const int sys = blockIdx.y;
@@ -294,7 +299,9 @@ __global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__re
                                                              int32_t nfin,
                                                              const T *__restrict__ part,
                                                              int32_t nslots, T *__restrict__ y,
-                                                             int64_t vec_stride) {
+                                                             int64_t vec_stride,
+                                                             const SolveState *stop) {
+    if (stop && load_done(stop + blockIdx.y)) return;
     const int sys = blockIdx.y;
     const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);  // the same in the whole wavefront
     if (f >= nfin) return;
@@ -429,19 +436,19 @@ inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
 template <typename T, typename IT, bool PERM>
 void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, const T *val,
                       int64_t val_stride, const T *x, T *y, int64_t vec_stride, int batch,
-                      hipStream_t s) {
+                      hipStream_t s, const SolveState *stop = nullptr) {
     T *part = reinterpret_cast<T *>(pl.part);
     plan_spmv_kernel<T, IT, PERM><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
-        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots);
+        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, stop);
     if (pl.nfin > 0)
         plan_finish_kernel<T><<<dim3((pl.nfin + kWaves - 1) / kWaves, batch), kBlock, 0, s>>>(
-            pl.fin, pl.nfin, part, pl.nslots, y, vec_stride);
+            pl.fin, pl.nfin, part, pl.nslots, y, vec_stride, stop);
 }
 
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
-                       int batch, hipStream_t s, const RowPlan *plan) {
+                       int batch, hipStream_t s, const RowPlan *plan, const SolveState *stop) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const bool ps = planned(plan);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
@@ -449,11 +456,12 @@ hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
         SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_kernel<T, IT, kS, kC>
                                                     <<<grid, kBlock, 0, s>>>(rp, ca, val,
                                                                              val_stride, x, y, n,
-                                                                             vec_stride, pt)));
+                                                                             vec_stride, pt,
+                                                                             stop)));
     }
     if (ps)
         launch_plan_spmv<T, IT, false>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
-                                       batch, s);
+                                       batch, s, stop);
     return hipGetLastError();
 }
 
@@ -588,7 +596,7 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipSt
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_spmv<T, IT>(int, const IT *, const ColArgs &, const T *, int64_t, \
                                            const T *, T *, int64_t, int64_t, int, hipStream_t,   \
-                                           const RowPlan *);                                     \
+                                           const RowPlan *, const SolveState *);                 \
     template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
                                                 const int32_t *, const T *, int64_t, const T *,  \
                                                 T *, int64_t, int64_t, int, hipStream_t,         \

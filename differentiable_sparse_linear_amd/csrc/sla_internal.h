@@ -363,11 +363,13 @@ struct RowPlan {
     void *part = nullptr;   // [systems of a launch][nslots] partial sums
 };
 
-// y = A x (plan: the tiles past the stage, or null)
+// y = A x (plan: the tiles past the stage, or null; stop: a solver's
+// per-system states, the product of a stopped system is skipped, or null)
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
-                       int batch, hipStream_t s, const RowPlan *plan = nullptr);
+                       int batch, hipStream_t s, const RowPlan *plan = nullptr,
+                       const SolveState *stop = nullptr);
 template <typename T, typename IT>
 hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
@@ -412,6 +414,19 @@ hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T
                           const hipEvent_t *ev = nullptr);
 // whether the z-walk applies to an operator form on n rows
 bool cg_zwalk(const ColArgs &it, int64_t n);
+// CG in three launches per iteration for operators with a row plan: init's
+// first half (u_0, x), then per iteration the row updates (split_u), the
+// product u -> v[0] through the plan (launch_spmv), and split_w (w^ and the
+// partial sums; init = true after init's product)
+template <typename T, typename IT>
+hipError_t launch_cg_split_init(bool jac, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                                hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_cg_split_u(bool jac, const IterArgs<T, IT> *a, int64_t n, int nsys, int ph,
+                             hipStream_t s);
+template <typename T, typename IT>
+hipError_t launch_cg_split_w(bool jac, bool init, const IterArgs<T, IT> *a, const IT *diagpos,
+                             int64_t n, int nsys, int ph, hipStream_t s);
 
 // BiCGStab (grid path, one system)
 template <typename T, typename IT>

@@ -178,3 +178,91 @@ def test_invalid_long_row_patterns_rejected(hip):
         with pytest.raises(hip.SlaError) as ei:
             hip.Pattern(torch.from_numpy(rp).cuda(), torch.from_numpy(c).cuda())
         assert ei.value.status == hip.SLA_ERR_PATTERN
+
+
+def graph_problem(n, seed, batch=1, precond="jacobi"):
+    rp, col, val = W.powerlaw_graph_laplacian(n, seed)
+    rng = np.random.default_rng(seed + 100)
+    vals = np.repeat(val, batch, axis=0) * rng.uniform(0.7, 1.3, (batch, 1))
+    return W.Problem(f"graph_{n}_{seed}_b{batch}", n, rp, col, vals,
+                     rng.standard_normal((batch, n)), rng.uniform(-1.0, 1.0, (batch, n)),
+                     method="cg", precond=precond, tol=1e-10, maxit=2000)
+
+
+@pytest.mark.parametrize("precond", ["jacobi", "none"])
+def test_split_cg_matches_oracle_iterates(hip, precond):
+    """CG on a pattern with a row plan runs three launches per iteration; at
+    fixed iteration counts (even and odd stops) its iterates are the
+    oracle's, forward and adjoint."""
+    banner(f"split cg iterates {precond}")
+    p = graph_problem(30000, 13, precond=precond)
+    # The library's one-reduction arrangement and the oracle's textbook
+    # recurrence give the same iterates in exact arithmetic; their rounding
+    # differences grow like k * kappa * eps.  With Jacobi the operator is well
+    # conditioned; without it this graph's kappa is about 2.4e4 (largest
+    # eigenvalue 1.8e4 from the hubs' degrees, smallest 0.74), so 8
+    # iterations allow ~2e-11.
+    # grad_values (products of the two unconverged iterates, weighted by the
+    # hubs' long rows) is held to that bound with Jacobi; without it, it is
+    # checked as -lambda_i x_j of the GPU's own iterates and, converged,
+    # against the oracle at the usual solution bound.
+    tol = 1e-12 if precond == "jacobi" else 1e-10
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    for k in (1, 2, 5, 8):
+        g = _solve(hip, p, maxit=k)
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert int(g["info"]["iters"][0]) == k == int(r.iters[0])
+        assert relerr(g["x"][0], r.x[0]) <= tol, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= tol, k
+        if precond == "jacobi":
+            assert relerr(g["gv"][0], a.grad_values[0]) <= tol, k
+        assert np.array_equal(g["gv"][0], -(g["gb"][0][rows] * g["x"][0][p.col])), k
+    g = _solve(hip, p)
+    r, a = oracle_forward_adjoint(p)
+    sol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert g["info"]["status"][0] == 0 and g["ainfo"]["status"][0] == 0
+    assert relerr(g["x"][0], r.x[0]) <= sol and relerr(g["gv"][0], a.grad_values[0]) <= sol
+
+
+def _solve(hip, p, profile=False, **kw):
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p))
+    opts = dict(method="cg", precond=p.precond, tol=p.tol, maxit=p.maxit, check=False,
+                profile=profile)
+    opts.update(kw)
+    x, info = pat.solve(d["val"], d["b"], **opts)
+    gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **opts)
+    torch.cuda.synchronize()
+    out = dict(x=x.cpu().numpy(), gv=gv.cpu().numpy(), gb=gb.cpu().numpy(), info=info,
+               ainfo=ainfo)
+    pat.close()
+    return out
+
+
+def test_split_cg_batch_profile_and_edges(hip):
+    """A batch of three graph systems (one launch group) equals the single
+    solves bit for bit; profile mode (one system at a time, every iteration
+    launched directly) gives the same results; a zero right-hand side and
+    maxit = 0 stop at iteration 0."""
+    banner("split cg batch / profile / edges")
+    p = graph_problem(20000, 17, batch=3)
+    g = _solve(hip, p)
+    gp = _solve(hip, p, profile=True)
+    for s in range(3):
+        q = W.Problem("one", p.n, p.row_ptr, p.col, p.values[s:s + 1], p.b[s:s + 1],
+                      p.x_t[s:s + 1], method="cg", precond="jacobi", tol=p.tol, maxit=p.maxit)
+        gs = _solve(hip, q)
+        for key in ("x", "gv", "gb"):
+            assert np.array_equal(gs[key][0], g[key][s]), (s, key)
+            assert np.array_equal(gp[key][s], g[key][s]), (s, key)
+        assert gs["info"]["iters"][0] == g["info"]["iters"][s] == gp["info"]["iters"][s]
+        assert g["info"]["status"][s] == 0 and g["ainfo"]["status"][s] == 0
+    r, a = oracle_forward_adjoint(p, systems=[1])
+    tol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert relerr(g["x"][1], r.x[0]) <= tol and relerr(g["gv"][1], a.grad_values[0]) <= tol
+    z = W.Problem("zero", p.n, p.row_ptr, p.col, p.values[:1], np.zeros((1, p.n)),
+                  p.x_t[:1], method="cg", precond="jacobi", tol=p.tol, maxit=p.maxit)
+    gz = _solve(hip, z)
+    assert gz["info"]["iters"][0] == 0 and not np.any(gz["x"])
+    g0 = _solve(hip, graph_problem(20000, 17), maxit=0)
+    assert g0["info"]["iters"][0] == 0 and g0["info"]["status"][0] == hip.SLA_NOT_CONVERGED
