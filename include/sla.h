@@ -130,6 +130,12 @@ typedef struct {
  * min(batch, 65535, 2^21 / n) systems (at least 1) per grid launch, so the
  * solver vectors (11 per system) and the diagonal-major buffer are sized for
  * that group; BiCGStab and single systems use the first system's share.
+ * Long rows: when some 256-row tile of A (or of A^T) holds more than 2048
+ * entries or a row longer than 8, the handle keeps a row plan for it (short
+ * row blocks and chunks of long rows, 32 bytes each, a flag per tile and one
+ * partial sum per chunk of a split row and system, for up to 65535 systems);
+ * the products, the gradient and CG (then three launches per iteration)
+ * use it.  Building it reads the row pointers to the host once.
  * Checks the pattern on the device (synchronizes `stream`).  Returns
  * SLA_ERR_PATTERN for an invalid pattern and writes *out = NULL on failure.
  */
