@@ -276,9 +276,11 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                                    nsys, s, op.plan));
     else if (cg)
         HIP_TRY(hipMemsetAsync(a.t, 0, sizeof(T) * n * nsys, s));
-    // CG on an operator with a row plan (long rows) runs split iterations:
-    // the fused kernel's tile walker would take those rows a wavefront each
-    const bool split = cg && !dmaj && op.plan && op.plan->nitems > 0;
+    // on an operator with a row plan (long rows) the iterations run split:
+    // the fused kernels' tile walker would take those rows a wavefront each
+    const bool planned_op = !dmaj && op.plan && op.plan->nitems > 0;
+    const bool split = cg && planned_op;
+    const bool bsplit = !cg && planned_op;
     const IT *dpos = reinterpret_cast<const IT *>(h->diagpos);
     if (split) {
         HIP_TRY(launch_cg_split_init<T, IT>(jac, ad, n, nsys, s));
@@ -291,6 +293,20 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
     }
 
+    // split BiCGStab: half h of iteration k (0: updates, p_k -> v_k,
+    // partials; 1: updates, s -> t, partials); split chunks start at even
+    // iterations, so k's parity is the iteration's
+    auto bicg_half = [&](hipStream_t ss, int k, int h) -> hipError_t {
+        hipError_t e;
+        const T *in = h ? a.s : a.p[(k + 1) & 1];
+        T *out = h ? a.t : a.v[(k + 1) & 1];
+        if ((e = launch_bicg_split<T, IT>(2 * h, ad, n, ss)) != hipSuccess) return e;
+        if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, in, out, n, n, 1, ss,
+                                    op.plan, st)) != hipSuccess)
+            return e;
+        return launch_bicg_split<T, IT>(2 * h + 1, ad, n, ss);
+    };
+
     // iteration k; CG launches carry the iteration's parity
     auto one_iter = [&](hipStream_t ss, int k) -> hipError_t {
         hipError_t e;
@@ -302,6 +318,10 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
             return launch_cg_split_w<T, IT>(jac, false, ad, dpos, n, nsys, k & 1, ss);
         }
         if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, nsys, k & 1, ss);
+        if (bsplit) {
+            if ((e = bicg_half(ss, k, 0)) != hipSuccess) return e;
+            return bicg_half(ss, k, 1);
+        }
         if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
         return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
     };
@@ -330,6 +350,13 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                 HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, ad, n, 1, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
+            } else if (bsplit) {  // each half's three launches between stream events
+                for (int hh = 0; hh < 2; ++hh) {
+                    HIP_TRY(hipEventRecord(h->prof_ev[ev], s));
+                    HIP_TRY(bicg_half(s, k, hh));
+                    HIP_TRY(hipEventRecord(h->prof_ev[ev + 1], s));
+                    ev += 2;
+                }
             } else {
                 HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
                 ev += 2;
@@ -360,12 +387,13 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         *prof_launches += active;
     } else {
         // the stop is detected by the first kernel of iteration maxit, so
-        // maxit + 1 iterations may be launched; CG chunks have even length so
-        // that every chunk starts at an even iteration
+        // maxit + 1 iterations may be launched; CG (and split BiCGStab)
+        // chunks have even length so that every chunk starts at an even
+        // iteration
         int chunk = o.graph_chunk == 0 ? kDefaultChunk : (o.graph_chunk < 0 ? -o.graph_chunk : o.graph_chunk);
         if (chunk > o.maxit + 1) chunk = o.maxit + 1;
         if (chunk < 1) chunk = 1;
-        if (cg && (chunk & 1)) ++chunk;
+        if ((cg || bsplit) && (chunk & 1)) ++chunk;
         hipGraphExec_t exec = nullptr;
         if (o.graph_chunk >= 0) {
             const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0) + 8 * nsys;

@@ -290,7 +290,229 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     store_partials<5>(red5, A->part, slot);
 }
 
+// ------------------------------------------------------------ split iteration
+//
+// Operators with a row plan (rows past the tile walker's stage or slots):
+// each kernel above becomes three launches, its row updates, the product
+// through the products' tile kernel and row plan, and its partial sums.  The
+// stop tests, scalars and partial-sum slots are those of the fused kernels.
+// The product of iteration j's first half is p_j -> v_j (buffers p and v of
+// parity (j + 1) & 1, which the host picks: split chunks start at even j),
+// of its second half s -> t.
+
+// bicg_xpv's tests and scalars, then x_j, r_j and p_j per row.
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void bicg_split_xpv_u_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    SolveState *st = A->st;
+    __shared__ int seen[kWaves];
+    __shared__ double red[5][kWaves];
+    const bool stopped = saw_stop(st, seen);
+    const int it = st->iter_a;
+    const bool first = (it == 0);
+    const int64_t n = A->n;
+    const gptr<const T> sv = first ? glb((const T *)A->r) : glb((const T *)A->s);
+    const gptr<const T> tv = first ? sv : glb((const T *)A->t);
+    const gptr<const T> pold = first ? sv : glb((const T *)A->p[it & 1]);
+    const gptr<const T> vold = first ? sv : glb((const T *)A->v[it & 1]);
+    const gptr<T> pnew = glb(A->p[(it + 1) & 1]);
+    const gptr<T> x = glb(A->x);
+    const gptr<T> r = glb(A->r);
+    if (!stopped) {
+        if (first) {
+            const int slot[2] = {kBiRR0, kBiBB};
+            partial_loads<2>(A->part, slot, red);
+        } else {
+            const int slot[5] = {kBiTS, kBiTT, kBiSS, kBiRS, kBiRT};
+            partial_loads<5>(A->part, slot, red);
+        }
+    }
+    __syncthreads();
+    if (any_saw_stop(seen)) return;
+    T alpha = T(0), omega = T(0), beta = T(0);
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    if (first) {
+        double tot[2];
+        totals<2>(red, tot);
+        const double rr = tot[0], bb = tot[1];
+        if (bb == 0.0) {
+            if (block0()) st->zero_x = A->use_x0 ? 1 : 0;
+            finish(st, A->ndone, SLA_OK, 0, 0.0);
+            return;
+        }
+        if (block0()) {
+            st->rho[0] = rr;  // rhat = r_0
+            st->bb = bb;
+            st->iter_b = 0;
+            st->spmv += A->use_x0 ? 1 : 0;  // the A x0 product
+            st->nfused += 1;
+        }
+    } else {
+        double tot[5];
+        totals<5>(red, tot);
+        const double ts = tot[0], tt = tot[1], ss = tot[2], rs = tot[3], rt = tot[4];
+        const int pv = (it + 1) & 1;  // parity slot of iteration j - 1
+        alpha = (T)st->alpha[pv];
+        if (sqrt(ss) <= A->tol * sqrt(st->bb)) {
+            // half step: x_j = x + alpha p; the next launches stop
+            for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+                const int64_t i = t * kTileRows + threadIdx.x;
+                if (i < n) x[i] = fmaB(alpha, pold[i], x[i]);
+            }
+            if (block0()) {
+                st->half_ss = ss;
+                st->half_exit = 1;
+                st->iter_b = it;
+            }
+            return;
+        }
+        if (tt == 0.0 || ts == 0.0) {
+            if (block0()) st->spmv += 1;  // the t product of iteration j - 1
+            finish(st, A->ndone, SLA_BREAKDOWN, it - 1, 0.0);
+            return;
+        }
+        const double omega_d = ts / tt;
+        const double rho = rs - omega_d * rt;
+        omega = (T)omega_d;
+        beta = (T)((rho / st->rho[pv]) * (st->alpha[pv] / omega_d));
+        if (block0()) {
+            st->rho[it & 1] = rho;
+            st->iter_b = it;
+            st->spmv += 1;  // the t product of iteration j - 1
+            st->nfused += 1;
+        }
+    }
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T si = sv[i], ti = tv[i], pi = pold[i], vi = vold[i];
+        const T ri = fmaB(-omega, ti, si);
+        if (!first) {
+            x[i] = fmaB(omega, si, fmaB(alpha, pi, x[i]));
+            r[i] = ri;
+        }
+        pnew[i] = fmaB(beta, fmaB(-omega, vi, pi), ri);
+    }
+}
+
+// After v_j = A p_j: partials rhat.v_j and ||r_j||^2.
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void bicg_split_xpv_w_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    SolveState *st = A->st;
+    if (load_done(st) || st->half_exit) return;  // set by an earlier launch: uniform
+    const int it = st->iter_a;
+    const int64_t n = A->n;
+    const gptr<const T> vnew = glb((const T *)A->v[(it + 1) & 1]);
+    const gptr<const T> r = glb((const T *)A->r);
+    const gptr<const T> rh = glb((const T *)A->rh);
+    double rv = 0.0, rr = 0.0;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T ri = r[i];
+        rv = fma((double)rh[i], (double)vnew[i], rv);
+        rr = fma((double)ri, (double)ri, rr);
+    }
+    double v[2] = {rv, rr};
+    const int slot[2] = {kBiRV, kBiRR};
+    store_partials<2>(v, A->part, slot);
+}
+
+// bicg_st's tests and alpha_j, then s = r_j - alpha_j v_j per row.
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void bicg_split_st_u_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    SolveState *st = A->st;
+    __shared__ int seen[kWaves];
+    __shared__ double red[2][kWaves];
+    const bool stopped = saw_stop(st, seen);
+    const int it = st->iter_b;
+    const int64_t n = A->n;
+    if (!stopped) {
+        const int slot[2] = {kBiRV, kBiRR};
+        partial_loads<2>(A->part, slot, red);
+    }
+    __syncthreads();
+    if (any_saw_stop(seen)) return;
+    if (st->half_exit) {
+        finish(st, A->ndone, SLA_OK, it, st->half_ss);
+        return;
+    }
+    double tot[2];
+    totals<2>(red, tot);
+    const double rv = tot[0], rr = tot[1];
+    if (sqrt(rr) <= A->tol * sqrt(st->bb)) {
+        finish(st, A->ndone, SLA_OK, it, rr);
+        return;
+    }
+    if (it >= A->maxit) {
+        finish(st, A->ndone, SLA_NOT_CONVERGED, it, rr);
+        return;
+    }
+    const double rho = st->rho[it & 1];
+    if (rho == 0.0) {
+        finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
+        return;
+    }
+    if (block0()) st->spmv += 1;  // v_j = A p_j
+    if (rv == 0.0) {
+        finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
+        return;
+    }
+    const double alpha_d = rho / rv;
+    const T alpha = (T)alpha_d;
+    if (block0()) {
+        st->alpha[it & 1] = alpha_d;
+        st->iter_a = it + 1;
+        st->nfused += 1;
+    }
+    const gptr<const T> r = glb((const T *)A->r);
+    const gptr<const T> v = glb((const T *)A->v[(it + 1) & 1]);
+    const gptr<T> s = glb(A->s);
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i < n) s[i] = fmaB(-alpha, v[i], r[i]);
+    }
+}
+
+// After t = A s: partials t.s, t.t, s.s, rhat.s, rhat.t.
+template <typename T, typename IT>
+__global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    if (load_done(A->st)) return;  // set by an earlier launch: uniform
+    const int64_t n = A->n;
+    const gptr<const T> s = glb((const T *)A->s);
+    const gptr<const T> tv = glb((const T *)A->t);
+    const gptr<const T> rh = glb((const T *)A->rh);
+    double ts = 0.0, tt = 0.0, ss = 0.0, rs = 0.0, rt = 0.0;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
+        const int64_t i = t * kTileRows + threadIdx.x;
+        if (i >= n) continue;
+        const T acc = tv[i], si = s[i], rhi = rh[i];
+        ts = fma((double)acc, (double)si, ts);
+        tt = fma((double)acc, (double)acc, tt);
+        ss = fma((double)si, (double)si, ss);
+        rs = fma((double)rhi, (double)si, rs);
+        rt = fma((double)rhi, (double)acc, rt);
+    }
+    double red5[5] = {ts, tt, ss, rs, rt};
+    const int slot[5] = {kBiTS, kBiTT, kBiSS, kBiRS, kBiRT};
+    store_partials<5>(red5, A->part, slot);
+}
+
 // ------------------------------------------------------------------ launchers
+
+template <typename T, typename IT>
+hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
+    const int grid = grid_for_tiles(tiles_of(n));
+    switch (part) {
+        case 0: bicg_split_xpv_u_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
+        case 1: bicg_split_xpv_w_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
+        case 2: bicg_split_st_u_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
+        default: bicg_split_st_w_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
 
 template <typename T, typename IT>
 hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
@@ -321,7 +543,9 @@ hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n
     template hipError_t launch_bicg_xpv<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,    \
                                                hipStream_t, const hipEvent_t *);               \
     template hipError_t launch_bicg_st<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,     \
-                                              hipStream_t, const hipEvent_t *);
+                                              hipStream_t, const hipEvent_t *);               \
+    template hipError_t launch_bicg_split<T, IT>(int, const IterArgs<T, IT> *, int64_t,       \
+                                                 hipStream_t);
 
 SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)

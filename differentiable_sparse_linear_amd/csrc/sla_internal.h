@@ -437,6 +437,11 @@ hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t 
 template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
+// BiCGStab in six launches per iteration for operators with a row plan:
+// part 0 (first half's updates), [p -> v product], 1 (its partials),
+// 2 (second half's updates), [s -> t product], 3 (its partials)
+template <typename T, typename IT>
+hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
 // shared by both grid solvers: x = 0 when the state asks for it (nsys systems)
 template <typename T>

@@ -266,3 +266,80 @@ def test_split_cg_batch_profile_and_edges(hip):
     assert gz["info"]["iters"][0] == 0 and not np.any(gz["x"])
     g0 = _solve(hip, graph_problem(20000, 17), maxit=0)
     assert g0["info"]["iters"][0] == 0 and g0["info"]["status"][0] == hip.SLA_NOT_CONVERGED
+
+
+def directed_graph_problem(n, seed):
+    """The power-law graph with its entries above the diagonal scaled by 0.7
+    and below by 1.3, the diagonal reset to the row's off-diagonal magnitude
+    plus 1 (strictly diagonally dominant, nonsymmetric): BiCGStab."""
+    rp, col, val = W.powerlaw_graph_laplacian(n, seed)
+    rows = np.repeat(np.arange(n), np.diff(rp))
+    v = val[0].copy()
+    off = col != rows
+    v[off & (col > rows)] *= 0.7
+    v[off & (col < rows)] *= 1.3
+    dsum = np.zeros(n)
+    np.add.at(dsum, rows[off], np.abs(v[off]))
+    v[~off] = dsum[rows[~off]] + 1.0
+    rng = np.random.default_rng(seed + 200)
+    return W.Problem(f"directed_graph_{n}_{seed}", n, rp, col, v[None, :],
+                     rng.standard_normal((1, n)), rng.uniform(-1.0, 1.0, (1, n)),
+                     method="bicgstab", precond="none", tol=1e-10, maxit=2000)
+
+
+def _bsolve(hip, p, **kw):
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+    opts = dict(method="bicgstab", precond="none", tol=p.tol, maxit=p.maxit, check=False)
+    opts.update(kw)
+    x, info = pat.solve(d["val"], d["b"], **opts)
+    gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **opts)
+    torch.cuda.synchronize()
+    out = dict(x=x.cpu().numpy(), gv=gv.cpu().numpy(), gb=gb.cpu().numpy(), info=info,
+               ainfo=ainfo)
+    pat.close()
+    return out
+
+
+def test_split_bicgstab(hip):
+    """BiCGStab on an operator with a row plan (A and, for the adjoint, A^T)
+    runs six launches per iteration: the oracle's iterates at fixed counts,
+    the converged forward and adjoint against the oracle, and profile mode
+    and other chunk sizes (an odd one, made even) bit for bit the same."""
+    banner("split bicgstab")
+    p = directed_graph_problem(20000, 19)
+    # the library's arrangement (one product and one set of partial sums per
+    # half-iteration, rho from the identity rhat.(s - omega t) = rhat.s -
+    # omega rhat.t) and the oracle's textbook steps agree in exact
+    # arithmetic; rounding differences grow like k * kappa * eps, and this
+    # operator's 2-norm condition number is about 1.9e4 (singular values
+    # 1.9e4 and 0.99), so 5 iterations allow ~1e-11
+    for k in (1, 2, 5):
+        g = _bsolve(hip, p, maxit=k)
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert int(g["info"]["iters"][0]) == k == int(r.iters[0]), k
+        assert relerr(g["x"][0], r.x[0]) <= 1e-10, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= 1e-10, k
+    g = _bsolve(hip, p)
+    r, a = oracle_forward_adjoint(p)
+    sol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert g["info"]["status"][0] == 0 and g["ainfo"]["status"][0] == 0
+    assert relerr(g["x"][0], r.x[0]) <= sol
+    assert relerr(g["gb"][0], a.grad_b[0]) <= sol
+    assert relerr(g["gv"][0], a.grad_values[0]) <= sol
+    # BiCGStab's residual history on this ill-conditioned operator is
+    # erratic: the rounding differences above move the iteration at which it
+    # first falls below the tolerance (both runs meet it; the solutions agree)
+    assert abs(int(g["info"]["iters"][0]) - int(r.iters[0])) <= int(r.iters[0]) // 4
+    for kw in ({"profile": True}, {"graph_chunk": 5}, {"graph_chunk": -6}):
+        h = _bsolve(hip, p, **kw)
+        for key in ("x", "gv", "gb"):
+            assert np.array_equal(h[key], g[key]), (kw, key)
+        assert h["info"]["iters"][0] == g["info"]["iters"][0], kw
+    # an initial guess: A x0 through the plan
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+    x0 = torch.from_numpy(np.random.default_rng(3).standard_normal((1, p.n))).cuda()
+    x, info = pat.solve(d["val"], d["b"], method="bicgstab", precond="none", tol=p.tol,
+                        maxit=p.maxit, x0=x0)
+    assert info["status"][0] == 0 and relerr(x.cpu().numpy()[0], r.x[0]) <= sol
