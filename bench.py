@@ -22,7 +22,9 @@ bytes per PCG iteration (SpMV plus the textbook recurrence's 11 vector passes)
 matrix once in the form the handle iterates on (CSR values with 4 bytes of
 column per entry, 2 with its compact tile-relative copy, or 2 bytes per row
 with its diagonal masks, plus row pointers; or the diagonal-major values,
-nd * n * sv, for 3/5/7-diagonal stencils) plus, on average over the two
+nd * n * sv, for 3/5/7-diagonal stencils, (nd // 2 + 1) * n * sv when CG
+found the values symmetric and read the lower diagonals through their
+mirrors: the form the profiled solve reports) plus, on average over the two
 iteration parities, 9 vectors (even launches read u, w, s, p and write p, s,
 u, w; odd launches also read and write x).  For BiCGStab both kernels of an
 iteration are timed; each launch is priced at half of one textbook BiCGStab
@@ -98,7 +100,8 @@ def parse():
                          "(2^20 rows unless --size, seed 9; row lengths from 1 to 557 357) "
                          "instead of a numbered workload")
     ap.add_argument("--column-form", default="diagonal-major",
-                    choices=("wide", "tile16", "diagonal", "diagonal-major"),
+                    choices=("wide", "tile16", "diagonal", "diagonal-major",
+                             "diagonal-major-symmetric"),
                     help="storage form the summarised run's iterations read")
     return ap.parse_args()
 
@@ -132,19 +135,10 @@ def form_bytes(form, p):
     sv, sr = p.values.itemsize, p.row_ptr.itemsize
     if form == "diagonal-major":
         return num_diagonals(p) * p.n * sv
+    if form == "diagonal-major-symmetric":  # the main and upper diagonals only
+        return (num_diagonals(p) // 2 + 1) * p.n * sv
     idx = {"wide": 4 * p.nnz, "tile16": 2 * p.nnz, "diagonal": 2 * p.n}[form]
     return p.nnz * sv + idx + (p.n + 1) * sr
-
-
-def iteration_form(p):
-    """(form, matrix bytes per product) of the solver iterations on a handle
-    for this pattern, as the library chose it."""
-    import torch
-    import differentiable_sparse_linear_amd as sla
-    pat = sla.Pattern(torch.from_numpy(p.row_ptr).cuda(), torch.from_numpy(p.col).cuda())
-    form = pat.iteration_form()
-    pat.close()
-    return form, form_bytes(form, p)
 
 
 def sources_sha(files):
@@ -225,6 +219,10 @@ def _counter_pass(d, short_names):
     return sum(active) / len(active), len(active), len(vals), max(copies)
 
 
+def _form_flag(args):
+    return "" if args.column_form == "diagonal-major" else f" --column-form {args.column_form}"
+
+
 def summarize_counters(args):
     p = load_problem(args)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
@@ -246,7 +244,7 @@ def summarize_counters(args):
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- "
         f"python3 bench.py --kernel-only 2 --workload {args.workload}",
         f"  python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write --workload "
-        f"{args.workload}",
+        f"{args.workload}{_form_flag(args)}",
         "",
         "Calibration: a torch copy of 1 GiB (reads 1 GiB, writes 1 GiB) in the same run;",
         "factor = 1 GiB / counter reading of that copy.",
@@ -291,7 +289,7 @@ def summarize_trace(args):
         "Commands (repository root; OUT is any output folder):",
         "  rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- "
         f"python3 bench.py{op} --steps 3 --warmup 1 --no-cpu-baseline{which}",
-        f"  python3 bench.py --summarize-trace OUT/trace{op}{which}",
+        f"  python3 bench.py --summarize-trace OUT/trace{op}{which}{_form_flag(args)}",
         "",
         "rocprofv3 --stats (all dispatches):",
         f"{'calls':>8} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel",
@@ -591,7 +589,8 @@ def main():
         k_ms = fi_p["kernel_ms"] + ai_p["kernel_ms"]
         k_n = fi_p["kernel_launches"] + ai_p["kernel_launches"]
         k_avg_s = (k_ms / k_n) * 1e-3 if k_n else float("nan")
-        form, fb = iteration_form(p)
+        form = fi_p["form"]  # what the profiled iterations read
+        fb = form_bytes(form, p)
         kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
                                                     p.values.itemsize, p.row_ptr.itemsize, fb)
         achieved = kbytes / k_avg_s / 1e9

@@ -65,7 +65,15 @@ class _Opts(ctypes.Structure):
 class _Info(ctypes.Structure):
     _fields_ = [("iters", ctypes.c_void_p), ("spmv", ctypes.c_void_p), ("relres", ctypes.c_void_p),
                 ("status", ctypes.c_void_p), ("kernel_ms", ctypes.c_double),
-                ("kernel_launches", ctypes.c_int64)]
+                ("kernel_launches", ctypes.c_int64), ("form", ctypes.c_int32)]
+
+
+_FORMS = ("wide", "tile16", "diagonal", "diagonal-major", "diagonal-major-symmetric")
+
+
+def _form_name(code: int) -> str:
+    """Name of an sla_solve_info.form code ("block": the one-workgroup solver)."""
+    return "block" if code < 0 else _FORMS[code]
 
 
 _lib = None
@@ -369,6 +377,7 @@ class Pattern:
         arrs["return"] = st
         arrs["kernel_ms"] = info.kernel_ms
         arrs["kernel_launches"] = info.kernel_launches
+        arrs["form"] = _form_name(info.form)
         if check and st < 0:
             raise SlaError(st, "sla_solve")
         return x, arrs
@@ -388,6 +397,7 @@ class Pattern:
         arrs["return"] = st
         arrs["kernel_ms"] = info.kernel_ms
         arrs["kernel_launches"] = info.kernel_launches
+        arrs["form"] = _form_name(info.form)
         if check and st < 0:
             raise SlaError(st, "sla_solve_adjoint")
         return gv, gb, arrs

@@ -189,6 +189,13 @@ struct Operator {
     const RowPlan *plan;  // the products' plan for tiles past the stage
 };
 
+// Diagonal offsets that pair up around the main one: off[q] = -off[nd-1-q].
+static bool mirrored(const ColArgs &c) {
+    bool m = c.nd > 0;
+    for (int q = 0; q < c.nd; ++q) m = m && c.off[q] == -c.off[c.nd - 1 - q];
+    return m;
+}
+
 // nsys consecutive systems on the grid path (nsys <= gbatch; 1 for
 // BiCGStab and in profile mode): fill the argument block, run init, then
 // replay/launch iteration chunks until the device reports every system done.
@@ -211,6 +218,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     a.val = dmaj ? reinterpret_cast<const T *>(h->dia) : val;
     a.rp = reinterpret_cast<const IT *>(op.rp);
     a.cols = op.it;
+    // CG reads the lower diagonals through their mirrors when the pack finds
+    // the values symmetric; the offsets must mirror for that
+    a.cols.sym = cg && dmaj && mirrored(op.it) ? 1 : 0;
     a.x = x;
     a.b = b;
     a.r = vp(0);
@@ -265,8 +275,8 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     HIP_TRY(hipMemsetAsync(st, 0, sizeof(SolveState) * nsys, s));
     HIP_TRY(hipMemsetAsync(h->ndone, 0, sizeof(int32_t), s));
     if (dmaj)
-        HIP_TRY(launch_dia_pack<T, IT>(a.rp, op.cols.msk, op.it.nd, val, nnz,
-                                       reinterpret_cast<T *>(h->dia), n, nsys, s));
+        HIP_TRY(launch_dia_pack<T, IT>(a.rp, a.cols, val, nnz, reinterpret_cast<T *>(h->dia), n,
+                                       nsys, st, s));
     if (jac) HIP_TRY(launch_dinv<T, IT>(reinterpret_cast<const IT *>(h->diagpos), val, nnz, vp(10),
                                         n, st, nsys, s));
     // A x0 goes to t (CG) or q (BiCGStab), which the init kernels read; CG
@@ -458,6 +468,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
     double prof_ms = 0.0;
     int64_t prof_launches = 0;
     const bool block_path = cg && n <= kBlockSolveMaxN && !o.profile;
+    if (info) info->form = block_path ? -1 : op.it.mode;
     if (block_path) {
         BlockCgParams p;
         p.val = val;
@@ -495,9 +506,11 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
     HIP_TRY(hipMemcpyAsync(h->st_host, h->st, sizeof(SolveState) * B, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
     int worst_err = 0, worst_pos = 0;
+    bool sym = !block_path && cg && op.it.mode == kColDiaMajor && mirrored(op.it);
     for (int64_t sys = 0; sys < B; ++sys) {
         const SolveState &ss = h->st_host[sys];
         const int stc = ss.status;
+        sym = sym && !ss.asym;
         if (stc < 0 && stc < worst_err) worst_err = stc;
         if (stc > worst_pos) worst_pos = stc;
         if (info) {
@@ -510,6 +523,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
     if (info) {
         info->kernel_ms = prof_ms;
         info->kernel_launches = prof_launches;
+        if (sym) info->form = 4;
     }
     return (sla_status)(worst_err < 0 ? worst_err : worst_pos);
 }
@@ -543,7 +557,7 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
                 g_last_error = e;
                 return SLA_ERR_DEVICE;
             }
-            sla_solve_info one;
+            sla_solve_info one{};
             one.iters = &it[sys];
             one.spmv = &mv[sys];
             one.relres = &rr[sys];
@@ -552,6 +566,7 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
                                             gb + sys * n, oo, &one, s);
             kms += one.kernel_ms;
             kl += one.kernel_launches;
+            if (info) info->form = one.form;
             if (r < 0 && (st >= 0 || r < st)) st = r;
             if (r > 0 && st >= 0 && r > st) st = r;
             if (r == SLA_ERR_DEVICE) break;

@@ -74,6 +74,16 @@ struct CgOwn {
     T u, w, s, p, x;
 };
 
+// The column source of the iterations: a diagonal-major operator whose
+// offsets mirror reads its lower diagonals through their mirrors unless the
+// pack found the system's values unsymmetric.
+template <int CM>
+__device__ __forceinline__ ColSrc<CM> cg_cols(const ColArgs &a, const SolveState *st) {
+    ColSrc<CM> c = col_src<CM>(a);
+    if constexpr (CM == kColDiaMajor) c.sym = c.sym && !st->asym;
+    return c;
+}
+
 // r_0 = b - A x_0 (A x_0 is in t; the host zeroes t when there is no initial
 // guess), u_0 = M^-1 r_0, w_0 = A u_0; stores u_0 and w^_0 = M^-1 w_0 in the
 // parity-0 buffers and zeroes x without an initial guess; partials gamma_0,
@@ -94,9 +104,9 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
     double ga = 0.0, de = 0.0, rr = 0.0, bb = 0.0;
     auto load = [&](int64_t c) { return G3<T>{b[c], ax0[c], JAC ? dinv[c] : T(1)}; };
     auto u_of = [&](const G3<T> &g) -> T { return JAC ? g.c * (g.a - g.b) : g.a - g.b; };
-    spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
-        load, u_of, load,
+    spmv_rows<T, IT, SLOTS, SLOTS, CM, true>(
+        xcd_tiles(tiles_of(n)), n, glb(A->rp), cg_cols<CM>(A->cols, A->st), sm,
+        [&](auto k) { return val[k]; }, load, u_of, load,
         [&](int64_t i, T acc, const G3<T> &o, T) {
             const T ri = o.a - o.b;
             const T ui = u_of(o);
@@ -254,7 +264,7 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     if constexpr (ZW) {
         __shared__ G3<T> zring[3][kTileRows];
         go = dia_rows_zw<T>(
-            walk_tiles(tiles_of(n), stopped), n, col_src<CM>(A->cols),
+            walk_tiles(tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
             [&](auto k) { return __builtin_nontemporal_load(&val[k]); }, gath, u_of,
             [&](int64_t i, const G3<T> &o) {
                 return CgOwn<T>{o.a, o.b, o.c, __builtin_nontemporal_load(&pprev[i]),
@@ -262,8 +272,8 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
             },
             row, pre, post, zring);
     } else {
-        go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND>(
-            walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
+        go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND, CM, true>(
+            walk_tiles(tiles_of(n), stopped), n, glb(A->rp), cg_cols<CM>(A->cols, st), sm,
             [&](auto k) { return val[k]; }, gath, u_of,
             [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
             row, pre, post);

@@ -371,28 +371,59 @@ __global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restric
         out[k] = val[perm[k]];
 }
 
+// Bit-for-bit equality (a signed zero differs from an unsigned one, a NaN
+// from everything).
+template <typename T>
+__device__ __forceinline__ bool same_bits(T a, T b) {
+    if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(uint64_t, a) == __builtin_bit_cast(uint64_t, b);
+    else
+        return __builtin_bit_cast(uint32_t, a) == __builtin_bit_cast(uint32_t, b);
+}
+
 // out[q * n + i] = row i's entry on diagonal q, 0 where bit q of msk[i] is
 // clear.  The row's entries are stored in ascending column order, which is
 // ascending q, so the k-th set bit takes the k-th entry.  System blockIdx.y
-// reads val + y * val_stride and writes out + y * nd * n.
+// reads val + y * val_stride and writes out + y * nd * n.  With st (mirrored
+// offsets), row i's entry on a diagonal q below the main one is compared
+// with the entry of row j = i + off[q] on the mirrored diagonal nd-1-q
+// (column i): both present and equal in every bit, or both absent; any other
+// outcome sets st[y].asym.  Every pair of mirrored positions is the lower
+// position of exactly one row, so the check covers the whole matrix.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void dia_pack_kernel(const IT *__restrict__ rp,
-                                                          const uint16_t *__restrict__ msk, int nd,
+                                                          const ColArgs cols,
                                                           const T *__restrict__ val,
                                                           int64_t val_stride,
-                                                          T *__restrict__ out, int64_t n) {
+                                                          T *__restrict__ out, int64_t n,
+                                                          SolveState *st) {
+    const uint16_t *__restrict__ msk = cols.msk;
+    const int nd = cols.nd;
     val += (int64_t)blockIdx.y * val_stride;
     out += (int64_t)blockIdx.y * nd * n;
     const int64_t stride = (int64_t)gridDim.x * kBlock;
+    int bad = 0;
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
-        uint32_t m = msk[i];
+        const uint32_t mi = msk[i];
+        uint32_t m = mi;
         IT k = rp[i];
         for (int q = 0; q < nd; ++q, m >>= 1) {
             T v = T(0);
             if (m & 1u) v = val[k++];
             out[(int64_t)q * n + i] = v;
+            if (st && 2 * q + 1 < nd) {
+                const int64_t j = i + cols.off[q];
+                const uint32_t mj = j >= 0 ? msk[j] : 0u;
+                const int qm = nd - 1 - q;
+                const bool hi = (mi >> q) & 1u, hj = (mj >> qm) & 1u;
+                if (hi != hj)
+                    bad = 1;
+                else if (hi)
+                    bad |= !same_bits(v, val[rp[j] + __builtin_popcount(mj & ((1u << qm) - 1u))]);
+            }
         }
     }
+    if (st) raise_flag(bad, &st[blockIdx.y].asym);
 }
 
 // System blockIdx.y: values val + y * val_stride, dinv + y * n, state st + y.
@@ -566,13 +597,13 @@ hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz,
 }
 
 template <typename T, typename IT>
-hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val,
-                           int64_t val_stride, T *out, int64_t n, int nsys, hipStream_t s) {
+hipError_t launch_dia_pack(const IT *rp, const ColArgs &cols, const T *val, int64_t val_stride,
+                           T *out, int64_t n, int nsys, SolveState *st, hipStream_t s) {
     int64_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    dia_pack_kernel<T, IT><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(rp, msk, nd, val,
-                                                                           val_stride, out, n);
+    dia_pack_kernel<T, IT><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(
+        rp, cols, val, val_stride, out, n, cols.sym ? st : nullptr);
     return hipGetLastError();
 }
 
@@ -609,8 +640,8 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipSt
                                            const RowPlan *);                                    \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, int64_t, T *, int64_t,        \
                                            SolveState *, int, hipStream_t);                      \
-    template hipError_t launch_dia_pack<T, IT>(const IT *, const uint16_t *, int, const T *,    \
-                                               int64_t, T *, int64_t, int, hipStream_t);
+    template hipError_t launch_dia_pack<T, IT>(const IT *, const ColArgs &, const T *, int64_t, \
+                                               T *, int64_t, int, SolveState *, hipStream_t);
 
 SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)

@@ -20,16 +20,6 @@
 
 namespace sla {
 
-// Sets *flag when any lane of the wavefront saw `bad`: one atomic per
-// wavefront at most, none once the flag reads set (a check that fails
-// everywhere would otherwise queue an atomic from every wavefront on one
-// word).
-__device__ __forceinline__ void raise_flag(int bad, int32_t *flag) {
-    if (__any(bad) && (threadIdx.x & 63) == 0 &&
-        __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
-        atomicOr(flag, 1);
-}
-
 template <typename IT>
 __global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restrict__ rp, int64_t n,
                                                               int64_t nnz, int32_t *flag) {

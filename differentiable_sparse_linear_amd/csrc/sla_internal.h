@@ -58,7 +58,18 @@ struct SolveState {
     int32_t half_exit;  // BiCGStab: x took its half step, stop next kernel
     int32_t lag;      // CG: stopped at an odd iteration i with x = x_{i-1};
                       // the finishing launch adds alpha[0] p
+    int32_t asym;     // diagonal-major pack: the values are not symmetric
 };
+
+// Sets *flag when any lane of the wavefront saw `bad`: one atomic per
+// wavefront at most, none once the flag reads set (a check that fails
+// everywhere would otherwise queue an atomic from every wavefront on one
+// word).
+__device__ __forceinline__ void raise_flag(int bad, int32_t *flag) {
+    if (__any(bad) && (threadIdx.x & 63) == 0 &&
+        __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        atomicOr(flag, 1);
+}
 
 // Slots of the per-block partial sums ([kMaxRed][kMaxGrid] doubles).  A
 // kernel reads only slots that the previous kernel wrote and writes only
@@ -92,6 +103,12 @@ struct ColArgs {
     int32_t mode = kColWide;
     int32_t nd = 0;                  // number of diagonals (kColDiag, kColDiaMajor)
     int32_t off[kMaxDiaMajor] = {};  // their offsets when nd <= kMaxDiaMajor
+    // kColDiaMajor, CG only: the offsets mirror (off[q] = -off[nd-1-q]), so
+    // when the system's values are symmetric (the pack found no pair
+    // A[i][j], A[j][i] that differs in any bit) the iterations may read a
+    // row's entries below the main diagonal from the upper diagonals of the
+    // rows they mirror: A[i][i-d] = A[i-d][i]
+    int32_t sym = 0;
 };
 
 // Arguments of the grid iteration kernels for one system.  A launch that
@@ -392,10 +409,13 @@ template <typename T>
 hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
 // Diagonal-major copy of the CSR values of nsys systems (val_stride apart):
 // out[s][q * n + i] = the entry of row i on diagonal q (bit q of msk[i]), 0
-// where the row lacks it.
+// where the row lacks it.  With st (cols.sym set: mirrored offsets), the
+// same pass compares every entry below the main diagonal with its mirror
+// bit for bit and sets st[s].asym when a pair differs or one of the two is
+// missing.
 template <typename T, typename IT>
-hipError_t launch_dia_pack(const IT *rp, const uint16_t *msk, int nd, const T *val,
-                           int64_t val_stride, T *out, int64_t n, int nsys, hipStream_t s);
+hipError_t launch_dia_pack(const IT *rp, const ColArgs &cols, const T *val, int64_t val_stride,
+                           T *out, int64_t n, int nsys, SolveState *st, hipStream_t s);
 // per system of nsys: dinv[s][i] = 1 / val[s][diagpos[i]] (values val_stride apart)
 template <typename T, typename IT>
 hipError_t launch_dinv(const IT *diagpos, const T *val, int64_t val_stride, T *dinv, int64_t n,

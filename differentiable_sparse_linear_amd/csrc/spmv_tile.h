@@ -137,6 +137,10 @@ struct ColSrc {
     gptr<const int32_t> dlt;
     int32_t nneg;  // diagonals below the main one (dlt[q] < 0 for q < nneg)
     int32_t off[kMaxDiaMajor];  // kColDiaMajor: the diagonals' offsets, ascending
+    // kColDiaMajor: the values are symmetric and the offsets mirror, so row
+    // i's entry on a diagonal q below the main one is read as the entry of
+    // row i + off[q] on the mirrored diagonal (uniform across the grid)
+    int32_t sym;
     // column of stored entry k in the tile starting at row0 (per-entry modes)
     __device__ __forceinline__ int32_t operator()(int64_t k, int64_t row0) const {
         if constexpr (CM == kColTile16)
@@ -147,10 +151,11 @@ struct ColSrc {
 };
 template <int CM>
 __device__ __forceinline__ ColSrc<CM> col_src(const ColArgs &a) {
-    ColSrc<CM> c{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg, {}};
+    ColSrc<CM> c{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg, {}, 0};
     if constexpr (CM == kColDiaMajor) {
 #pragma unroll
         for (int q = 0; q < kMaxDiaMajor; ++q) c.off[q] = a.off[q];
+        c.sym = a.sym;
     }
     return c;
 }
@@ -169,6 +174,22 @@ struct RowLds {
     int32_t dtab[kMaxDiags];  // diagonal offsets (kColDiag)
 };
 
+// Row i's entry on diagonal q of a diagonal-major operator.  Below the main
+// diagonal with col.sym: the entry of row j = i + off[q] on the mirrored
+// diagonal ND - 1 - q, whose column is i (no such row above the first: 0).
+// One load either way, its address chosen by selects, so that the loads of
+// a tile still issue back to back.
+template <typename T, int ND, typename VF>
+__device__ __forceinline__ T dia_entry(VF vf, const ColSrc<kColDiaMajor> &col, int q, int64_t i,
+                                       int64_t n) {
+    const int64_t own = (int64_t)q * n + i;
+    if (2 * q + 1 >= ND) return vf(own);
+    const int64_t j = i + col.off[q];
+    const bool mir = col.sym != 0;
+    const T v = vf(mir && j >= 0 ? (int64_t)(ND - 1 - q) * n + j : own);
+    return mir && j < 0 ? T(0) : v;
+}
+
 // Rows of a diagonal-major operator with ND diagonals, the main one in the
 // middle (slot ND / 2; the spmv_rows contract below, without the LDS): thread
 // t of a tile takes row row0 + t and reads its ND values as ND coalesced
@@ -177,11 +198,15 @@ struct RowLds {
 // nothing, so the sum over q -- ascending columns, the order of the CSR
 // forms -- equals the sum over the stored entries).  The main diagonal's
 // gathers use the row index itself, so they coincide with the row's own
-// loads.  All loads of a tile are issued before its first use, and the first
-// tile's before the start-up barrier, so that their latency overlaps the
-// kernel's start-up loads.
-template <typename T, int ND, typename VF, typename GF, typename CF, typename OF, typename RF,
-          typename PRE, typename POST>
+// loads.  With SYM and col.sym the slots below the main diagonal are read
+// from the mirrored diagonal at row i + off[q] (0 above the first row): the
+// same bits as the row's own copy, so the sums do not change, and the lower
+// copies' bytes are not read (their lines are the upper diagonals' lines of
+// rows just before, mostly still in the caches).  All loads of a tile are issued
+// before its first use, and the first tile's before the start-up barrier,
+// so that their latency overlaps the kernel's start-up loads.
+template <typename T, int ND, bool SYM, typename VF, typename GF, typename CF, typename OF,
+          typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
                                          const ColSrc<kColDiaMajor> &col, VF vf, GF gf, CF cf,
                                          OF of, RF rf, PRE pre, POST post) {
@@ -200,7 +225,10 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
         own = of(i);
 #pragma unroll
         for (int q = 0; q < ND; ++q) {
-            v[q] = vf((int64_t)q * n + i);
+            if constexpr (SYM)
+                v[q] = dia_entry<T, ND>(vf, col, q, i, n);
+            else
+                v[q] = vf((int64_t)q * n + i);
             int64_t c = i + col.off[q];
             c = c < 0 ? 0 : (c >= n ? n - 1 : c);
             g[q] = gf(q == d0 ? (int32_t)i : (int32_t)c);
@@ -236,7 +264,10 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
 // launch; the -D, own and (inside the tile) +-1 gathers come from the ring,
 // the other gathers from memory.  ofz(i, g) builds a row's own inputs from
 // its gathered entries g.  The terms and their order are those of dia_rows,
-// so the sums are bitwise the same.
+// so the sums are bitwise the same.  With col.sym the -D entry of a row is
+// the +D entry of the row one plane below, which this lane loaded for its
+// previous tile: it is carried in a register, and the -1 and -N entries are
+// read from their mirrors as in dia_rows.
 template <typename T, typename VF, typename GF, typename CF, typename OF, typename RF,
           typename PRE, typename POST, typename G>
 __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
@@ -255,6 +286,8 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
     };
     int prev = 2, cur = 0, next = 1;
     int64_t t = tr.first;
+    T vd = T(0);  // col.sym: the previous tile's +D entry
+    bool carried = false;
     if (t < tr.end) {
         ring[prev][tid] = G{};  // the first plane's -D neighbours are padding
         ring[cur][tid] = gf((int32_t)row_of(t));
@@ -267,7 +300,10 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
         T v[ND];
         G g[ND];
 #pragma unroll
-        for (int q = 0; q < ND; ++q) v[q] = vf((int64_t)q * n + i);
+        for (int q = 0; q < ND; ++q)
+            v[q] = q == 0 && col.sym && carried ? vd : dia_entry<T, ND>(vf, col, q, i, n);
+        vd = v[6];
+        carried = true;
         g[6] = gf(clampc(i + col.off[6]));
         g[1] = gf(clampc(i + col.off[1]));
         g[5] = gf(clampc(i + col.off[5]));
@@ -303,15 +339,16 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
 // pre(): start-up loads issued with the first row pointers (no barrier
 // inside); post(): runs after the first barrier, every thread, and returns
 // false to end the kernel (the same in every thread).  plan_tiles: when not
-// null, the tiles it flags are left alone (a row plan covers them).
-template <typename T, typename IT, int SLOTS, int ROUND, int CM, typename VF, typename GF,
-          typename CF, typename OF, typename RF, typename PRE, typename POST>
+// null, the tiles it flags are left alone (a row plan covers them).  SYM:
+// a diagonal-major operator honours col.sym (CG instantiations only).
+template <typename T, typename IT, int SLOTS, int ROUND, int CM, bool SYM = false, typename VF,
+          typename GF, typename CF, typename OF, typename RF, typename PRE, typename POST>
 __device__ __forceinline__ bool spmv_rows(const TileRange &tr, int64_t n, gptr<const IT> rp,
                                           ColSrc<CM> col, RowLds<T, IT> &sm, VF vf, GF gf, CF cf,
                                           OF of, RF rf, PRE pre, POST post,
                                           const uint8_t *plan_tiles = nullptr) {
     if constexpr (CM == kColDiaMajor) {
-        return dia_rows<T, SLOTS>(tr, n, col, vf, gf, cf, of, rf, pre, post);
+        return dia_rows<T, SLOTS, SYM>(tr, n, col, vf, gf, cf, of, rf, pre, post);
     } else {
     constexpr int R = round_for(SLOTS, ROUND);
     constexpr bool kDiag = CM == kColDiag;

@@ -92,6 +92,12 @@ typedef struct {
     double kernel_ms;        /* profile mode: summed duration of the fused
                                 SpMV kernel launches (ms), else 0              */
     int64_t kernel_launches; /* profile mode: number of those launches         */
+    int32_t form;     /* what the iterations read: the sla_iteration_form
+                         codes 0-3, or 4 = diagonal-major with the entries
+                         below the main diagonal read from their mirrors
+                         above it (CG, mirrored offsets, values found
+                         symmetric bit for bit in every system); -1 when
+                         every system ran on the one-workgroup solver      */
 } sla_solve_info;
 
 /*
@@ -123,8 +129,12 @@ typedef struct {
  *               copies the systems' values into it
  *               diagonal-major, zero where a row lacks a diagonal; the
  *               iterations then read no row pointers or columns
- *               (sla_iteration_form).  Results are identical as long as the
- *               iterates stay finite.
+ *               (sla_iteration_form).  CG on a system whose values are
+ *               symmetric bit for bit (checked by the copy; the diagonals'
+ *               offsets must pair up around the main one) reads only the
+ *               main and upper diagonals, the lower entries through their
+ *               mirrors (sla_solve_info.form = 4).  Results are identical as
+ *               long as the iterates stay finite.
  *               Other bits: SLA_ERR_ARG.
  * Workspace: CG on a batch of systems with n > 4096 advances a group of
  * min(batch, 65535, 2^21 / n) systems (at least 1) per grid launch, so the

@@ -107,10 +107,62 @@ def test_diagonal_major_matches_csr_values_bitwise(hip, case):
         kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit)
         x, info = pat.solve(val, b, **kw)
         gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
+        # CG on symmetric values reads the lower diagonals through their mirrors
+        want = ("diagonal-major-symmetric" if symmetric else "diagonal-major") if dmaj else "diagonal"
+        assert info["form"] == want and ainfo["form"] == want, (name, info["form"], ainfo["form"])
         outs.append([t.cpu().numpy() for t in (x, gv, gb)] + [info["iters"], ainfo["iters"]])
         pat.close()
     for u, v in zip(outs[0], outs[1]):
         assert np.array_equal(np.asarray(u), np.asarray(v)), name
+
+
+def test_unsymmetric_values_read_every_diagonal(hip):
+    """CG on a mirrored pattern reads the lower diagonals through their
+    mirrors only in systems whose values the pack finds symmetric bit for
+    bit.  One launch group of three 5000-row five-band systems: symmetric;
+    one pair one ulp apart; one pair of zeros with opposite signs.  Every
+    system equals, bit for bit, the same solve on the caller's CSR values and
+    the same system solved alone on the diagonal-major handle."""
+    import torch
+    banner("forms: unsymmetric values in a launch group")
+    q = banded("five_band", 5000, (-70, -1, 0, 1, 70), True, seed=9)
+    rows = np.repeat(np.arange(q.n), np.diff(q.row_ptr))
+    pos = {(int(r), int(c)): k for k, (r, c) in enumerate(zip(rows, q.col))}
+    vals = np.repeat(q.values, 3, axis=0)
+    k_up, k_lo = pos[(1000, 1070)], pos[(1070, 1000)]
+    vals[1, k_lo] = np.nextafter(vals[1, k_lo], 0.0)
+    k_up, k_lo = pos[(2000, 2001)], pos[(2001, 2000)]
+    vals[2, k_up], vals[2, k_lo] = 0.0, -0.0
+    rng = np.random.default_rng(10)
+    b = rng.standard_normal((3, q.n))
+    xt = rng.uniform(-1.0, 1.0, (3, q.n))
+    kw = dict(method="cg", precond="jacobi", tol=1e-10, maxit=5000)
+
+    def run(dmaj, sys):
+        rp = torch.from_numpy(q.row_ptr).cuda()
+        col = torch.from_numpy(q.col).cuda()
+        v = torch.from_numpy(np.ascontiguousarray(vals[sys])).cuda()
+        bb = torch.from_numpy(np.ascontiguousarray(b[sys])).cuda()
+        t = torch.from_numpy(np.ascontiguousarray(xt[sys])).cuda()
+        pat = hip.Pattern(rp, col, batch=len(sys), diagonal_major=dmaj)
+        x, info = pat.solve(v, bb, **kw)
+        gv, gb, ainfo = pat.solve_adjoint(v, x, x - t, **kw)
+        assert all(s == 0 for s in info["status"]) and all(s == 0 for s in ainfo["status"])
+        out = [u.cpu().numpy() for u in (x, gv, gb)] + [info["iters"], ainfo["iters"]]
+        pat.close()
+        return out, info["form"], ainfo["form"]
+
+    group, f, af = run(True, [0, 1, 2])
+    assert f == af == "diagonal-major"  # not every system of the call is symmetric
+    csr, f, af = run(False, [0, 1, 2])
+    assert f == af == "diagonal"
+    for u, v in zip(group, csr):
+        assert np.array_equal(np.asarray(u), np.asarray(v))
+    for s, want in ((0, "diagonal-major-symmetric"), (1, "diagonal-major"), (2, "diagonal-major")):
+        alone, f, af = run(True, [s])
+        assert f == af == want, (s, f, af)
+        for u, v in zip(alone, group):
+            assert np.array_equal(np.asarray(u)[0], np.asarray(v)[s]), s
 
 
 def zwalk_problem(Z=16, seed=21):
@@ -182,6 +234,8 @@ def test_zwalk_equals_csr_value_iterations_bitwise(hip, dtype):
         x, info = pat.solve(val, b, **kw)
         gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
         assert info["status"][0] == 0 and ainfo["status"][0] == 0
+        if dmaj:  # the -D entries carried along the walk, the others mirrored
+            assert info["form"] == ainfo["form"] == "diagonal-major-symmetric"
         outs.append([t.cpu().numpy() for t in (x, gv, gb)] + [info["iters"], ainfo["iters"]])
         pat.close()
         del rp, col, val, b, xt, x, gv, gb
