@@ -5,11 +5,12 @@
 // pay kernel-launch overhead on small problems):
 //  * small systems (n <= 4096, short rows) solve with CG in one workgroup per
 //    system, a single launch for the whole batch;
-//  * larger systems run the grid kernels; K iterations are captured once in a
-//    HIP graph that reads its arguments from a device block, every kernel
-//    ends at its first barrier once the device-side `done` flag is set, and
-//    the host keeps one replay in flight while it polls the flag of the
-//    previous one;
+//  * larger systems run the grid kernels; K iterations are captured
+//    once in a HIP graph that reads its arguments from a device block, every
+//    kernel ends at its first barrier once the device-side `done` flag is
+//    set, each replay ends by storing the count of stopped systems into
+//    pinned host memory, and the host keeps one replay in flight while it
+//    reads the count that the previous one left;
 //  * CG on a batch of larger systems advances a group of them per launch
 //    (the y dimension of the grid), as many as fit kGroupRows rows of
 //    workspace, and polls the count of the group's stopped systems.
@@ -37,6 +38,8 @@ constexpr int kDefaultChunk = 16;
 // 2M rows keep a launch's traffic (~190 bytes per row and iteration) two
 // orders of magnitude above the launch overhead; the workspace grows with it.
 constexpr int64_t kGroupRows = (int64_t)1 << 21;
+
+constexpr int kGraphSlots = 8;
 
 struct GraphEntry {
     int key = -1;
@@ -80,12 +83,14 @@ struct sla_ctx {
     void *args_dev = nullptr;    // [gbatch] IterArgs, one per system of a launch group
     void *args_host = nullptr;   // pinned staging copy of args_dev
     int32_t *flag = nullptr;
-    int32_t *poll = nullptr;     // pinned [2]
+    int32_t *poll = nullptr;     // pinned, coherent [2]: stopped systems
+    int32_t *poll_dev = nullptr; // its device address
     SolveState *st_host = nullptr;  // pinned [batch]
     hipStream_t cap = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
     std::vector<hipEvent_t> prof_ev;
-    GraphEntry graphs[8];
+    GraphEntry graphs[kGraphSlots];
+    int graph_next = 0;          // next slot to replace when all are taken
     int64_t ws_bytes = 0;
 };
 
@@ -374,10 +379,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                 ev += 2;
             }
             if ((k & 63) == 63 || k + 1 == launches) {
-                HIP_TRY(hipMemcpyAsync(&h->poll[0], h->ndone, sizeof(int32_t),
-                                       hipMemcpyDeviceToHost, s));
+                HIP_TRY(launch_publish(h->ndone, h->poll_dev, s));
                 HIP_TRY(hipStreamSynchronize(s));
-                if (h->poll[0] >= nsys) break;
+                if (__atomic_load_n(&h->poll[0], __ATOMIC_ACQUIRE) >= nsys) break;
             }
         }
         SolveState hs;
@@ -404,55 +408,72 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         if (chunk > o.maxit + 1) chunk = o.maxit + 1;
         if (chunk < 1) chunk = 1;
         if ((cg || bsplit) && (chunk & 1)) ++chunk;
-        hipGraphExec_t exec = nullptr;
-        if (o.graph_chunk >= 0) {
-            const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0) + 8 * nsys;
+        // (Chunks four times longer after the first two cut the boundaries of
+        // long solves, +0.8 % at 1e6 DOF, but the launches past the stop, up
+        // to two chunks in flight, cost the short solves of a Newton loop 9 %.)
+        const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0) + 8 * nsys;
+        // the replayable graph of `len` iterations plus the publish of the
+        // stopped count: cached per (key, len), captured on first use
+        auto graph_of = [&](int len, hipGraphExec_t *out) -> hipError_t {
+            for (auto &g : h->graphs)
+                if (g.key == key && g.chunk == len) {
+                    *out = g.exec;
+                    return hipSuccess;
+                }
             GraphEntry *slot = nullptr;
             for (auto &g : h->graphs)
-                if (g.key == key && g.chunk == chunk) slot = &g;
-            if (!slot) {
-                for (auto &g : h->graphs)
-                    if (g.key == -1 || g.key == key) {
-                        slot = &g;
-                        break;
-                    }
-                if (!slot) slot = &h->graphs[0];
-                if (slot->exec) {
-                    HIP_TRY(hipGraphExecDestroy(slot->exec));
-                    slot->exec = nullptr;
-                    slot->key = -1;
+                if (g.key == -1) {
+                    slot = &g;
+                    break;
                 }
-                hipGraph_t graph = nullptr;
-                HIP_TRY(hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal));
-                hipError_t ce = hipSuccess;
-                for (int k = 0; k < chunk && ce == hipSuccess; ++k) ce = one_iter(h->cap, k);
-                hipError_t ee = hipStreamEndCapture(h->cap, &graph);
-                HIP_TRY(ce);
-                HIP_TRY(ee);
-                hipError_t ie = hipGraphInstantiate(&slot->exec, graph, nullptr, nullptr, 0);
-                (void)hipGraphDestroy(graph);
-                HIP_TRY(ie);
-                slot->key = key;
-                slot->chunk = chunk;
+            if (!slot) slot = &h->graphs[h->graph_next++ % kGraphSlots];
+            if (slot->exec) {
+                hipError_t de = hipGraphExecDestroy(slot->exec);
+                slot->exec = nullptr;
+                slot->key = -1;
+                if (de != hipSuccess) return de;
             }
-            exec = slot->exec;
-        }
-        const int64_t max_chunks = (o.maxit + 1 + chunk - 1) / chunk + 1;
-        for (int64_t c = 0; c <= max_chunks; ++c) {
-            if (c < max_chunks) {
-                if (exec) {
+            hipGraph_t graph = nullptr;
+            hipError_t ce = hipStreamBeginCapture(h->cap, hipStreamCaptureModeThreadLocal);
+            if (ce != hipSuccess) return ce;
+            for (int k = 0; k < len && ce == hipSuccess; ++k) ce = one_iter(h->cap, k);
+            if (ce == hipSuccess) ce = launch_publish(h->ndone, h->poll_dev, h->cap);
+            hipError_t ee = hipStreamEndCapture(h->cap, &graph);
+            if (ce != hipSuccess) return ce;
+            if (ee != hipSuccess) return ee;
+            hipError_t ie = hipGraphInstantiate(&slot->exec, graph, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(graph);
+            if (ie != hipSuccess) return ie;
+            slot->key = key;
+            slot->chunk = len;
+            *out = slot->exec;
+            return hipSuccess;
+        };
+        // enough chunks to pass maxit + 1 iterations, and one more
+        const int64_t need = (int64_t)o.maxit + 1;
+        int64_t launched = 0;
+        for (int64_t c = 0;; ++c) {
+            const bool more = launched < need + chunk;
+            if (more) {
+                // the chunk ends with the copy of the stopped count to poll
+                if (o.graph_chunk >= 0) {
+                    hipGraphExec_t exec = nullptr;
+                    HIP_TRY(graph_of(chunk, &exec));
                     HIP_TRY(hipGraphLaunch(exec, s));
                 } else {
                     for (int k = 0; k < chunk; ++k) HIP_TRY(one_iter(s, k));
+                    HIP_TRY(launch_publish(h->ndone, h->poll_dev, s));
                 }
-                HIP_TRY(hipMemcpyAsync(&h->poll[c & 1], h->ndone, sizeof(int32_t),
-                                       hipMemcpyDeviceToHost, s));
                 HIP_TRY(hipEventRecord(h->ev[c & 1], s));
+                launched += chunk;
             }
+            // chunk c - 1 has published; chunk c may have published since
+            // (the count only grows), either is a state the device reached
             if (c >= 1) {
                 HIP_TRY(hipEventSynchronize(h->ev[(c - 1) & 1]));
-                if (h->poll[(c - 1) & 1] >= nsys) break;
+                if (__atomic_load_n(&h->poll[0], __ATOMIC_ACQUIRE) >= nsys) break;
             }
+            if (!more) break;
         }
     }
     if (cg) HIP_TRY(launch_cg_lag<T>(st, a.p[0], x, n, nsys, s));
@@ -809,7 +830,9 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     HIP_TRY(dmalloc(h, &h->args_dev, sizeof(IterArgs<T, IT>) * h->gbatch));
     HIP_TRY(hipHostMalloc(&h->args_host, sizeof(IterArgs<T, IT>) * h->gbatch,
                           hipHostMallocDefault));
-    HIP_TRY(hipHostMalloc((void **)&h->poll, 2 * sizeof(int32_t), hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void **)&h->poll, 2 * sizeof(int32_t),
+                          hipHostMallocMapped | hipHostMallocCoherent));
+    HIP_TRY(hipHostGetDevicePointer((void **)&h->poll_dev, h->poll, 0));
     HIP_TRY(hipHostMalloc((void **)&h->st_host, sizeof(SolveState) * h->batch, hipHostMallocDefault));
     HIP_TRY(hipMemsetAsync(h->st, 0, sizeof(SolveState) * h->batch, s));
     HIP_TRY(hipMemsetAsync(h->part, 0, sizeof(double) * kPartStride * h->gbatch, s));

@@ -458,6 +458,14 @@ __global__ __launch_bounds__(kBlock) void zero_if_kernel(const SolveState *st, T
     for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) x[i] = T(0);
 }
 
+// *poll = *ndone, stored at system scope into pinned host memory: once the
+// stream has passed this kernel the host reads the count of stopped systems
+// without a copy of its own.
+__global__ __launch_bounds__(64) void publish_kernel(const int32_t *ndone, int32_t *poll) {
+    if (threadIdx.x == 0)
+        __hip_atomic_store(poll, *ndone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ------------------------------------------------------------------ launchers
 
 inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
@@ -621,6 +629,11 @@ hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipSt
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     zero_if_kernel<T><<<dim3((unsigned)blocks, nsys), kBlock, 0, s>>>(st, x, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s) {
+    publish_kernel<<<1, 64, 0, s>>>(ndone, poll);
     return hipGetLastError();
 }
 

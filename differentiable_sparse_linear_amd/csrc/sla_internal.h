@@ -463,6 +463,8 @@ hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n
 template <typename T, typename IT>
 hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
 
+// *poll = *ndone, poll being the device address of pinned host memory
+hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s);
 // shared by both grid solvers: x = 0 when the state asks for it (nsys systems)
 template <typename T>
 hipError_t launch_zero_if(const SolveState *st, T *x, int64_t n, int nsys, hipStream_t s);

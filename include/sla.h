@@ -73,8 +73,9 @@ typedef struct {
     int32_t precond;     /* SLA_PRECOND_JACOBI or _NONE [JACOBI]; BiCGStab
                             supports NONE only                                  */
     int32_t use_x0;      /* 1: d_x holds the initial guess; 0: start at 0 [0]  */
-    int32_t graph_chunk; /* iterations per captured HIP graph replay for large
-                            systems: 0 = default, < 0 = launch kernels directly */
+    int32_t graph_chunk; /* iterations per captured HIP graph replay for
+                            large systems: 0 = default (16), < 0 = launch
+                            kernels directly in chunks of that length       */
     int32_t profile;     /* 1: no graph; time every launch of the fused SpMV
                             kernel with HIP events on `stream` (slower)       */
 } sla_solve_opts;
