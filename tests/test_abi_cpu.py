@@ -74,3 +74,57 @@ def test_bench_modes_parse_and_refuse_more_gpus():
         r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--op", op,
                             "--gpus", "2"], capture_output=True, text=True, timeout=120)
         assert r.returncode == 2 and "one GPU" in r.stderr, (op, r.stderr)
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    """The ctypes mirrors of sla_solve_opts, sla_solve_info and sla_eig_opts
+    have the C structs' sizes and member offsets (a plain C program built
+    with gcc against include/sla.h prints them)."""
+    import shutil
+    import subprocess
+    import differentiable_sparse_linear_amd as sla
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc missing")
+    structs = {"sla_solve_opts": sla._Opts, "sla_solve_info": sla._Info,
+               "sla_eig_opts": sla._EigOpts}
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "sla.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True,
+                             text=True).stdout.splitlines():
+        cname, member, v = ln.split()
+        got[(cname, member)] = int(v)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+def test_bench_bytes_model():
+    """The bench's per-launch byte counts for the 1e6-DOF workload: the
+    textbook PCG iteration (CSR with int32 columns, SpMV plus 11 vector
+    passes) and the fused kernel's own bytes in each storage form."""
+    import numpy as np
+    import bench
+    import workloads as W
+    n, nnz = 1_000_000, 6_940_000
+    k, alg, own, _ = bench.dominant_kernel("cg", "jacobi", n, nnz, 8, 4, 7 * n * 8)
+    assert k == "cg_iter_kernel"
+    assert alg == nnz * 12 + (n + 1) * 4 + 13 * n * 8 == 191_280_004
+    assert own == 7 * n * 8 + 9 * n * 8
+    p = W.config(2, size=12)
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    assert np.unique(p.col - rows).size == 7
+    assert bench.form_bytes("diagonal-major", p) == 7 * p.n * 8
+    assert bench.form_bytes("diagonal-major-symmetric", p) == 4 * p.n * 8
+    assert bench.form_bytes("diagonal", p) == p.nnz * 8 + 2 * p.n + (p.n + 1) * 4
+    assert bench.form_bytes("wide", p) == p.nnz * 12 + (p.n + 1) * 4
