@@ -265,7 +265,8 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
         __shared__ G3<T> zring[3][kTileRows];
         go = dia_rows_zw<T>(
             walk_tiles(tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
-            [&](auto k) { return __builtin_nontemporal_load(&val[k]); }, gath, u_of,
+            [&](auto k) { return __builtin_nontemporal_load(&val[k]); },
+            [&](auto k) { return val[k]; }, gath, u_of,
             [&](int64_t i, const G3<T> &o) {
                 return CgOwn<T>{o.a, o.b, o.c, __builtin_nontemporal_load(&pprev[i]),
                                 PH ? __builtin_nontemporal_load(&x[i]) : T(0)};

@@ -267,12 +267,14 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
 // so the sums are bitwise the same.  With col.sym the -D entry of a row is
 // the +D entry of the row one plane below, which this lane loaded for its
 // previous tile: it is carried in a register, and the -1 and -N entries are
-// read from their mirrors as in dia_rows.
-template <typename T, typename VF, typename GF, typename CF, typename OF, typename RF,
-          typename PRE, typename POST, typename G>
+// read from their mirrors as in dia_rows.  The values of the +-1 and +-N
+// diagonals then go through vk (loads that keep their lines cached, since
+// the mirrored reads come back to them), the others through vf.
+template <typename T, typename VF, typename VK, typename GF, typename CF, typename OF,
+          typename RF, typename PRE, typename POST, typename G>
 __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
-                                            const ColSrc<kColDiaMajor> &col, VF vf, GF gf, CF cf,
-                                            OF ofz, RF rf, PRE pre, POST post,
+                                            const ColSrc<kColDiaMajor> &col, VF vf, VK vk, GF gf,
+                                            CF cf, OF ofz, RF rf, PRE pre, POST post,
                                             G (*ring)[kTileRows]) {
     constexpr int ND = 7, d0 = 3;
     const int tid = threadIdx.x;
@@ -300,8 +302,14 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
         T v[ND];
         G g[ND];
 #pragma unroll
-        for (int q = 0; q < ND; ++q)
-            v[q] = q == 0 && col.sym && carried ? vd : dia_entry<T, ND>(vf, col, q, i, n);
+        for (int q = 0; q < ND; ++q) {
+            if (q == 0 && col.sym && carried)
+                v[q] = vd;
+            else if (col.sym && q != 0 && q != d0 && q != 6)
+                v[q] = dia_entry<T, ND>(vk, col, q, i, n);
+            else
+                v[q] = dia_entry<T, ND>(vf, col, q, i, n);
+        }
         vd = v[6];
         carried = true;
         g[6] = gf(clampc(i + col.off[6]));
