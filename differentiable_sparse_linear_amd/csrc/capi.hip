@@ -91,6 +91,7 @@ struct sla_ctx {
     std::vector<hipEvent_t> prof_ev;
     GraphEntry graphs[kGraphSlots];
     int graph_next = 0;          // next slot to replace when all are taken
+    int32_t last_iters = 0;      // most iterations of a system in the last grid solve
     int64_t ws_bytes = 0;
 };
 
@@ -404,13 +405,19 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         // maxit + 1 iterations may be launched; CG (and split BiCGStab)
         // chunks have even length so that every chunk starts at an even
         // iteration
-        int chunk = o.graph_chunk == 0 ? kDefaultChunk : (o.graph_chunk < 0 ? -o.graph_chunk : o.graph_chunk);
+        // Default length: a stop leaves up to two chunks of no-op launches
+        // in flight (about 2.4 us each) and every chunk boundary costs a few
+        // us, so the best length grows like the square root of the iteration
+        // count; the handle's previous grid solve (a forward before its
+        // adjoint, the last step of a loop) predicts it.
+        int chunk = o.graph_chunk < 0 ? -o.graph_chunk : o.graph_chunk;
+        if (o.graph_chunk == 0)
+            chunk = h->last_iters >= 1800 ? 4 * kDefaultChunk
+                    : h->last_iters >= 460 ? 2 * kDefaultChunk
+                                           : kDefaultChunk;
         if (chunk > o.maxit + 1) chunk = o.maxit + 1;
         if (chunk < 1) chunk = 1;
         if ((cg || bsplit) && (chunk & 1)) ++chunk;
-        // (Chunks four times longer after the first two cut the boundaries of
-        // long solves, +0.8 % at 1e6 DOF, but the launches past the stop, up
-        // to two chunks in flight, cost the short solves of a Newton loop 9 %.)
         const int key = (cg ? 0 : 4) + (jac ? 1 : 0) + (op.rp != h->rp ? 2 : 0) + 8 * nsys;
         // the replayable graph of `len` iterations plus the publish of the
         // stopped count: cached per (key, len), captured on first use
@@ -528,10 +535,12 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
     HIP_TRY(hipStreamSynchronize(s));
     int worst_err = 0, worst_pos = 0;
     bool sym = !block_path && cg && op.it.mode == kColDiaMajor && mirrored(op.it);
+    int32_t most = 0;
     for (int64_t sys = 0; sys < B; ++sys) {
         const SolveState &ss = h->st_host[sys];
         const int stc = ss.status;
         sym = sym && !ss.asym;
+        most = std::max(most, ss.iter);
         if (stc < 0 && stc < worst_err) worst_err = stc;
         if (stc > worst_pos) worst_pos = stc;
         if (info) {
@@ -541,6 +550,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
             if (info->relres) info->relres[sys] = ss.bb > 0.0 ? sqrt(ss.rr) / sqrt(ss.bb) : 0.0;
         }
     }
+    if (!block_path) h->last_iters = most;
     if (info) {
         info->kernel_ms = prof_ms;
         info->kernel_launches = prof_launches;

@@ -74,8 +74,10 @@ typedef struct {
                             supports NONE only                                  */
     int32_t use_x0;      /* 1: d_x holds the initial guess; 0: start at 0 [0]  */
     int32_t graph_chunk; /* iterations per captured HIP graph replay for
-                            large systems: 0 = default (16), < 0 = launch
-                            kernels directly in chunks of that length       */
+                            large systems: 0 = default (16; 32 or 64 when
+                            the handle's previous grid solve took at least
+                            460 or 1800 iterations), < 0 = launch kernels
+                            directly in chunks of that length              */
     int32_t profile;     /* 1: no graph; time every launch of the fused SpMV
                             kernel with HIP events on `stream` (slower)       */
 } sla_solve_opts;
