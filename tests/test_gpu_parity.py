@@ -525,6 +525,31 @@ def test_determinism_and_launch_modes_agree(hip):
             assert o[3] == outs[0][3]
 
 
+def test_replay_length_changes_nothing(hip):
+    """The default graph replay length follows the handle's previous grid
+    solve: 16 iterations on a fresh handle, 32 once a solve of the 1e6-DOF
+    workload has taken its ~480 iterations.  Those, and explicit lengths of
+    64 and 2, give bitwise the same solutions, adjoints and iteration
+    counts."""
+    banner("replay lengths, 1e6 DOF")
+    p = W.config(2)
+    d = to_dev(p)
+    pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p))
+    outs = []
+    for kw in ({}, {}, {"graph_chunk": 64}, {"graph_chunk": 2}):
+        x, info = pat.solve(d["val"], d["b"], method=p.method, precond=p.precond, tol=p.tol,
+                            maxit=p.maxit, **kw)
+        gv, gb, ai = pat.solve_adjoint(d["val"], x, x - d["xt"], method=p.method,
+                                       precond=p.precond, tol=p.tol, maxit=p.maxit, **kw)
+        outs.append((x.cpu().numpy(), gv.cpu().numpy(), gb.cpu().numpy(),
+                     int(info["iters"][0]), int(ai["iters"][0])))
+    assert outs[0][3] >= 460 and outs[0][4] >= 460  # later solves replay 32 at a time
+    for o in outs[1:]:
+        assert all(np.array_equal(a, b) for a, b in zip(o[:3], outs[0][:3]))
+        assert o[3:] == outs[0][3:]
+    pat.close()
+
+
 def test_compact_columns_change_nothing(hip):
     """The compact column forms (2-byte tile-relative columns, per-row
     diagonal masks) and the diagonal-major values of the solver iterations
