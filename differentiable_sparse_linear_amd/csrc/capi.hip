@@ -317,8 +317,8 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         const T *in = h ? a.s : a.p[(k + 1) & 1];
         T *out = h ? a.t : a.v[(k + 1) & 1];
         if ((e = launch_bicg_split<T, IT>(2 * h, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, in, out, n, n, 1, ss,
-                                    op.plan, st)) != hipSuccess)
+        if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, nullptr, 0, in, out, n, n, 1, ss,
+                                    op.plan, ad)) != hipSuccess)
             return e;
         return launch_bicg_split<T, IT>(2 * h + 1, ad, n, ss);
     };
@@ -328,8 +328,8 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         hipError_t e;
         if (split) {
             if ((e = launch_cg_split_u<T, IT>(jac, ad, n, nsys, k & 1, ss)) != hipSuccess) return e;
-            if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, val, nnz, a.r, a.v[0], n, n, nsys,
-                                        ss, op.plan, st)) != hipSuccess)
+            if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, nullptr, 0, a.r, a.v[0], n, n,
+                                        nsys, ss, op.plan, ad)) != hipSuccess)
                 return e;
             return launch_cg_split_w<T, IT>(jac, false, ad, dpos, n, nsys, k & 1, ss);
         }

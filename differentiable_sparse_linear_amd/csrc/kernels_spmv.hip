@@ -12,19 +12,32 @@
 
 namespace sla {
 
+// System blockIdx.y's values: val + y * val_stride, or, for a solver's
+// product (ind not null), those its argument block names.
+template <typename T, typename IT>
+__device__ __forceinline__ const T *sys_values(const T *val, int64_t val_stride,
+                                               const IterArgs<T, IT> *ind) {
+    return ind ? ind[blockIdx.y].val : val + (int64_t)blockIdx.y * val_stride;
+}
+
+// A solver's product has nothing to do once its system has stopped (set by
+// an earlier launch, so every wavefront reads the same).
+template <typename T, typename IT>
+__device__ __forceinline__ bool sys_stopped(const IterArgs<T, IT> *ind) {
+    return ind && load_done(ind[blockIdx.y].st);
+}
+
 template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ val, int64_t val_stride,
                                                       const T *__restrict__ x, T *__restrict__ y,
                                                       int64_t n, int64_t vec_stride,
                                                       const uint8_t *plan_tiles,
-                                                      const SolveState *stop) {
-    // a solver's product: nothing to do once the system has stopped (set by
-    // an earlier launch, so every wavefront reads the same)
-    if (stop && load_done(stop + blockIdx.y)) return;
+                                                      const IterArgs<T, IT> *ind) {
+    if (sys_stopped(ind)) return;
     __shared__ RowLds<T, IT> sm;
     const int sys = blockIdx.y;
-    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> v = glb(sys_values(val, val_stride, ind));
     const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     spmv_rows<T, IT, SLOTS, SLOTS>(
@@ -232,12 +245,12 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
     const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
     const T *__restrict__ x, T *__restrict__ y, int64_t vec_stride, T *__restrict__ part,
-    int32_t nslots, const SolveState *stop) {
-    if (stop && load_done(stop + blockIdx.y)) return;
+    int32_t nslots, const IterArgs<T, IT> *ind) {
+    if (sys_stopped(ind)) return;
     __shared__ T prod[kPlanCap];
     __shared__ T wsum[kWaves];
     const int sys = blockIdx.y;
-    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
+    const gptr<const T> v = glb(sys_values(val, val_stride, ind));
     const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     const gptr<const int32_t> cg = glb(col);
@@ -294,14 +307,14 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
 // A split row's value from its chunks' partials, one wavefront per split
 // row: lane l adds partials l, l + 64, ... in order, then a fixed-order
 // wavefront sum.
-template <typename T>
+template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__restrict__ fin,
                                                              int32_t nfin,
                                                              const T *__restrict__ part,
                                                              int32_t nslots, T *__restrict__ y,
                                                              int64_t vec_stride,
-                                                             const SolveState *stop) {
-    if (stop && load_done(stop + blockIdx.y)) return;
+                                                             const IterArgs<T, IT> *ind) {
+    if (sys_stopped(ind)) return;
     const int sys = blockIdx.y;
     const int f = blockIdx.x * kWaves + (threadIdx.x >> 6);  // the same in the whole wavefront
     if (f >= nfin) return;
@@ -475,19 +488,21 @@ inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
 template <typename T, typename IT, bool PERM>
 void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, const T *val,
                       int64_t val_stride, const T *x, T *y, int64_t vec_stride, int batch,
-                      hipStream_t s, const SolveState *stop = nullptr) {
+                      hipStream_t s, const IterArgs<T, IT> *ind = nullptr) {
     T *part = reinterpret_cast<T *>(pl.part);
     plan_spmv_kernel<T, IT, PERM><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
-        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, stop);
+        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, ind);
     if (pl.nfin > 0)
-        plan_finish_kernel<T><<<dim3((pl.nfin + kWaves - 1) / kWaves, batch), kBlock, 0, s>>>(
-            pl.fin, pl.nfin, part, pl.nslots, y, vec_stride, stop);
+        plan_finish_kernel<T, IT>
+            <<<dim3((pl.nfin + kWaves - 1) / kWaves, batch), kBlock, 0, s>>>(
+                pl.fin, pl.nfin, part, pl.nslots, y, vec_stride, ind);
 }
 
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
-                       int batch, hipStream_t s, const RowPlan *plan, const SolveState *stop) {
+                       int batch, hipStream_t s, const RowPlan *plan,
+                       const IterArgs<T, IT> *ind) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const bool ps = planned(plan);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
@@ -496,11 +511,11 @@ hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                                                     <<<grid, kBlock, 0, s>>>(rp, ca, val,
                                                                              val_stride, x, y, n,
                                                                              vec_stride, pt,
-                                                                             stop)));
+                                                                             ind)));
     }
     if (ps)
         launch_plan_spmv<T, IT, false>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
-                                       batch, s, stop);
+                                       batch, s, ind);
     return hipGetLastError();
 }
 
@@ -640,7 +655,7 @@ hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s) {
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_spmv<T, IT>(int, const IT *, const ColArgs &, const T *, int64_t, \
                                            const T *, T *, int64_t, int64_t, int, hipStream_t,   \
-                                           const RowPlan *, const SolveState *);                 \
+                                           const RowPlan *, const IterArgs<T, IT> *);           \
     template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
                                                 const int32_t *, const T *, int64_t, const T *,  \
                                                 T *, int64_t, int64_t, int, hipStream_t,         \

@@ -380,13 +380,16 @@ struct RowPlan {
     void *part = nullptr;   // [systems of a launch][nslots] partial sums
 };
 
-// y = A x (plan: the tiles past the stage, or null; stop: a solver's
-// per-system states, the product of a stopped system is skipped, or null)
+// y = A x (plan: the tiles past the stage, or null).  ind: null, or a
+// solver's device argument blocks, one per system of the launch; system y
+// then takes its values from ind[y].val (val and val_stride are unused) and
+// its product is skipped once ind[y].st has stopped.  Reading them there
+// keeps a captured graph of these launches valid for every call.
 template <typename T, typename IT>
 hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
                        int batch, hipStream_t s, const RowPlan *plan = nullptr,
-                       const SolveState *stop = nullptr);
+                       const IterArgs<T, IT> *ind = nullptr);
 template <typename T, typename IT>
 hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
                             const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
