@@ -24,10 +24,11 @@ __all__ = [
     "load", "SlaError", "Pattern", "PatternList", "SparseSolve", "sparse_solve",
     "SparseMatvec", "sparse_matvec", "SparseEigsh", "sparse_eigsh",
     "sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
-    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint",
+    "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint", "sla_solve_noalloc", "solve_noalloc",
     "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
     "SLA_OK", "SLA_NOT_CONVERGED", "SLA_BREAKDOWN", "SLA_ERR_ARG", "SLA_ERR_PATTERN",
-    "SLA_ERR_ZERO_DIAG", "SLA_ERR_NO_MEMORY", "SLA_ERR_DEVICE", "EXPORTED_SYMBOLS",
+    "SLA_ERR_ZERO_DIAG", "SLA_ERR_NO_MEMORY", "SLA_ERR_DEVICE", "SLA_ERR_TOO_LARGE",
+    "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,12 +41,12 @@ SLA_PRECOND_NONE, SLA_PRECOND_JACOBI = 0, 1
 SLA_CREATE_TRANSPOSE, SLA_CREATE_WIDE_COLUMNS, SLA_CREATE_CSR_VALUES = 1, 2, 4
 SLA_OK, SLA_NOT_CONVERGED, SLA_BREAKDOWN = 0, 1, 2
 SLA_ERR_ARG, SLA_ERR_PATTERN, SLA_ERR_ZERO_DIAG = -1, -2, -3
-SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE = -4, -5
+SLA_ERR_NO_MEMORY, SLA_ERR_DEVICE, SLA_ERR_TOO_LARGE = -4, -5, -6
 
 EXPORTED_SYMBOLS = ("sla_create", "sla_destroy", "sla_matvec", "sla_matvec_adjoint", "sla_solve",
                     "sla_solve_adjoint", "sla_eigsh", "sla_eigsh_adjoint", "sla_column_mode",
                     "sla_iteration_form", "sla_export_pattern", "sla_workspace_bytes", "sla_status_string",
-                    "sla_last_error")
+                    "sla_last_error", "sla_solve_noalloc")
 
 _METHODS = {"cg": SLA_CG, "bicgstab": SLA_BICGSTAB}
 _PRECONDS = {"none": SLA_PRECOND_NONE, "jacobi": SLA_PRECOND_JACOBI}
@@ -119,6 +120,9 @@ def load(path: Optional[str] = None):
     lib.sla_status_string.restype = ctypes.c_char_p
     lib.sla_last_error.argtypes = []
     lib.sla_last_error.restype = ctypes.c_char_p
+    lib.sla_solve_noalloc.argtypes = [I64, I64, I64, I32, I32, P, P, P, P, P,
+                                      ctypes.POINTER(_Opts), ctypes.POINTER(_Info), P]
+    lib.sla_solve_noalloc.restype = I32
     _lib = lib
     return lib
 
@@ -223,6 +227,38 @@ def sla_solve_adjoint(h, values, x, grad_x, grad_values, grad_b, opts: _Opts, in
     return load().sla_solve_adjoint(ctypes.c_void_p(h), _ptr(values), _ptr(x), _ptr(grad_x),
                                     _ptr(grad_values), _ptr(grad_b), ctypes.byref(opts),
                                     ctypes.byref(info), _stream(stream))
+
+
+def sla_solve_noalloc(n, nnz, batch, dtype, row_ptr, col, values, b, x, opts: _Opts,
+                      info: _Info, stream=None) -> int:
+    itype = SLA_I64 if row_ptr.dtype == torch.int64 else SLA_I32
+    dt = SLA_F64 if dtype == torch.float64 else SLA_F32
+    return load().sla_solve_noalloc(int(n), int(nnz), int(batch), dt, itype, _ptr(row_ptr),
+                                    _ptr(col), _ptr(values), _ptr(b), _ptr(x), ctypes.byref(opts),
+                                    ctypes.byref(info), _stream(stream))
+
+
+def solve_noalloc(row_ptr: torch.Tensor, col: torch.Tensor, values: torch.Tensor,
+                  b: torch.Tensor, x: torch.Tensor, tol=1e-10, maxit=1000, precond="jacobi",
+                  use_x0=False, check=True, stream=None):
+    """CG through sla_solve_noalloc into the caller's x (n <= 4096, batch <=
+    65535; nothing is allocated on the device).  values [batch, nnz] and b, x
+    [batch, n] of one float type.  Returns info as Pattern.solve does."""
+    _check(row_ptr, "row_ptr")
+    _check(col, "col", torch.int32)
+    n, nnz = row_ptr.numel() - 1, col.numel()
+    batch = b.numel() // n if n > 0 else 0
+    _check(values, "values", b.dtype, batch * nnz)
+    _check(b, "b", None, batch * n)
+    _check(x, "x", b.dtype, batch * n)
+    opts = _make_opts(tol, maxit, "cg", precond, use_x0, 0, 0)
+    info, arrs = _make_info(batch)
+    st = sla_solve_noalloc(n, nnz, batch, b.dtype, row_ptr, col, values, b, x, opts, info, stream)
+    arrs["return"] = st
+    arrs["form"] = _form_name(info.form)
+    if check and st < 0:
+        raise SlaError(st, "sla_solve_noalloc")
+    return arrs
 
 
 def sla_export_pattern(h, diagpos=None, row_ptr_t=None, col_t=None, perm=None, stream=None) -> int:

@@ -29,8 +29,12 @@
 using namespace sla;
 
 namespace {
-
 thread_local hipError_t g_last_error = hipSuccess;
+}  // namespace
+
+void sla::set_last_error(hipError_t e) { g_last_error = e; }
+
+namespace {
 
 constexpr int kNumVec = 11;  // r z q rh s t p0 p1 v0 v1 dinv
 constexpr int kDefaultChunk = 16;
@@ -1287,6 +1291,8 @@ const char *sla_status_string(int32_t status) {
         case SLA_ERR_ZERO_DIAG: return "zero diagonal entry with Jacobi preconditioning";
         case SLA_ERR_NO_MEMORY: return "device out of memory";
         case SLA_ERR_DEVICE: return "HIP runtime error";
+        case SLA_ERR_TOO_LARGE:
+            return "beyond the no-alloc solve's fixed scratch (n <= 4096, batch <= 65535)";
         default: return "unknown status";
     }
 }

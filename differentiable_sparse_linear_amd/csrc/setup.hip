@@ -431,6 +431,40 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
     return e;
 }
 
+// Launchers of the single checks, for callers that keep their own flags
+// (each raises *flag or atomically maxes *out, which must start at 0); they
+// allocate nothing and do not synchronize.
+template <typename IT>
+hipError_t launch_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag,
+                               hipStream_t s) {
+    check_rowptr_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, nnz, flag);
+    return hipGetLastError();
+}
+
+template <typename IT>
+hipError_t launch_check_cols_rows(const IT *rp, const int32_t *col, int64_t n, IT *diagpos,
+                                  int32_t *flag, hipStream_t s) {
+    check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
+    return hipGetLastError();
+}
+
+template <typename IT>
+hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s) {
+    const unsigned nb = blocks_for(n) < 512 ? blocks_for(n) : 512;
+    max_row_kernel<IT><<<nb, kBlock, 0, s>>>(rp, n, out);
+    return hipGetLastError();
+}
+
+#define SLA_CHECK_INST(IT)                                                                     \
+    template hipError_t launch_check_rowptr<IT>(const IT *, int64_t, int64_t, int32_t *,       \
+                                                hipStream_t);                                  \
+    template hipError_t launch_check_cols_rows<IT>(const IT *, const int32_t *, int64_t, IT *, \
+                                                   int32_t *, hipStream_t);                    \
+    template hipError_t launch_max_row<IT>(const IT *, int64_t, int32_t *, hipStream_t);
+SLA_CHECK_INST(int32_t)
+SLA_CHECK_INST(int64_t)
+#undef SLA_CHECK_INST
+
 template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
                                             int32_t *, int32_t *, hipStream_t);
 template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,

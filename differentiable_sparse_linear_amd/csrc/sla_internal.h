@@ -134,6 +134,9 @@ struct IterArgs {
     int32_t use_x0;
 };
 
+// Records a HIP error for sla_last_error (per calling thread).
+void set_last_error(hipError_t e);
+
 // ---------------------------------------------------------------- helpers
 
 // v plus the value that the row-local DPP permutation CTRL brings to this
@@ -532,6 +535,20 @@ hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const i
 template <typename IT>
 hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, int32_t max_len,
                        int16_t *out, int32_t *scratch, int32_t *fits, hipStream_t s);
+// The single checks behind setup_validate and setup_max_row, for callers
+// that keep their own flags: *flag is raised (row pointers not monotone or
+// not ending at nnz; a column out of range or out of order, or no diagonal),
+// *out is atomically maxed with the longest row; both must start at 0.  The
+// column check walks each row in one thread (meant for rows of modest
+// length) and writes diagpos.  Nothing is allocated or synchronized.
+template <typename IT>
+hipError_t launch_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag,
+                               hipStream_t s);
+template <typename IT>
+hipError_t launch_check_cols_rows(const IT *rp, const int32_t *col, int64_t n, IT *diagpos,
+                                  int32_t *flag, hipStream_t s);
+template <typename IT>
+hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s);
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
                            int32_t *col_t, int32_t *perm, hipStream_t s);

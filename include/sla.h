@@ -62,7 +62,9 @@ typedef enum {
     SLA_ERR_PATTERN = -2,   /* invalid CSR pattern (see conventions)        */
     SLA_ERR_ZERO_DIAG = -3, /* Jacobi requested and some A_ii == 0          */
     SLA_ERR_NO_MEMORY = -4, /* device allocation failed at sla_create       */
-    SLA_ERR_DEVICE = -5     /* a HIP runtime call failed                    */
+    SLA_ERR_DEVICE = -5,    /* a HIP runtime call failed                    */
+    SLA_ERR_TOO_LARGE = -6  /* sla_solve_noalloc: n or batch beyond the
+                               fixed scratch (n <= 4096, batch <= 65535)    */
 } sla_status;
 
 /* Solver options.  Pass NULL for the defaults in brackets. */
@@ -209,6 +211,31 @@ sla_status sla_solve_adjoint(sla_handle h, const void *d_values,
                              const void *d_x, const void *d_grad_x,
                              void *d_grad_values, void *d_grad_b,
                              const sla_solve_opts *opts, sla_solve_info *info,
+                             void *stream);
+
+/*
+ * sla_solve_noalloc -- sla_solve for callers that cannot allocate device
+ * memory (serving loops and harnesses that forbid allocation after start-up):
+ * no handle, no hipMalloc, hipFree or allocating library call.
+ *   The pattern (d_row_ptr [n+1] of row_ptr_type, d_col [nnz] int32) and
+ *   d_values [batch][nnz], d_b [batch][n], d_x [batch][n] (output; input
+ *   initial guess when opts->use_x0) are as for sla_create and sla_solve;
+ *   the pattern is validated on every call (SLA_ERR_PATTERN).
+ *   Only CG (opts->method = SLA_CG, Jacobi or no preconditioner, profile 0)
+ *   on the one-workgroup solver: n <= 4096 and batch <= 65535, else
+ *   SLA_ERR_TOO_LARGE; results (x and info) are those of sla_solve on a
+ *   handle of the same pattern, bit for bit.
+ *   Its state lives in a device array of 8 683 776 bytes that each
+ *   device holds from the library's load until the process ends; every call
+ *   on a device shares it, so calls that overlap on one device (two streams
+ *   or two threads) race and must be serialized by the caller.  Synchronizes
+ *   `stream` (three times: after the row-pointer check, after the column
+ *   check, at the end).
+ */
+sla_status sla_solve_noalloc(int64_t n, int64_t nnz, int64_t batch, int32_t dtype,
+                             int32_t row_ptr_type, const void *d_row_ptr,
+                             const int32_t *d_col, const void *d_values, const void *d_b,
+                             void *d_x, const sla_solve_opts *opts, sla_solve_info *info,
                              void *stream);
 
 /*

@@ -42,8 +42,9 @@ def test_library_exports_every_declared_symbol(libpath):
 def test_status_strings_and_null_handle(libpath):
     import differentiable_sparse_linear_amd as sla
     lib = sla.load(libpath)
-    for st in (0, 1, 2, -1, -2, -3, -4, -5):
+    for st in (0, 1, 2, -1, -2, -3, -4, -5, -6):
         assert lib.sla_status_string(st)
+    assert b"unknown" not in lib.sla_status_string(-6)
     # pure argument checks return before touching the device
     assert lib.sla_destroy(None) == sla.SLA_ERR_ARG
     assert lib.sla_workspace_bytes(None) == -1
@@ -52,6 +53,16 @@ def test_status_strings_and_null_handle(libpath):
     assert lib.sla_create(ctypes.byref(h), 0, 4, 1, 1, 0, None, None, 0, None) == sla.SLA_ERR_ARG
     assert lib.sla_solve(None, None, None, None, None, None, None) == sla.SLA_ERR_ARG
     assert lib.sla_matvec_adjoint(None, None, None, None, None, None, None) == sla.SLA_ERR_ARG
+    # the no-alloc solve: sizes beyond its fixed scratch, and missing pointers
+    p = ctypes.c_void_p(16)
+    na = lib.sla_solve_noalloc
+    assert na(4097, 4097, 1, 1, 0, p, p, p, p, p, None, None, None) == sla.SLA_ERR_TOO_LARGE
+    assert na(64, 64, 65536, 1, 0, p, p, p, p, p, None, None, None) == sla.SLA_ERR_TOO_LARGE
+    assert na(64, 64, 1, 1, 0, None, p, p, p, p, None, None, None) == sla.SLA_ERR_ARG
+    assert na(64, 63, 1, 1, 0, p, p, p, p, p, None, None, None) == sla.SLA_ERR_ARG
+    assert na(64, 64, 1, 2, 0, p, p, p, p, p, None, None, None) == sla.SLA_ERR_ARG
+    bicg = sla._make_opts(1e-10, 10, "bicgstab", "none", 0, 0, 0)
+    assert na(64, 64, 1, 1, 0, p, p, p, p, p, ctypes.byref(bicg), None, None) == sla.SLA_ERR_ARG
 
 
 def test_product_path_has_no_oracle_or_fallback():
