@@ -26,7 +26,10 @@ arrays.  What it follows, from the torch-sla explainer pages (gist.science,
   systems);
 * ``oracle.eigen``: dense eigenpairs of small symmetric systems and the
   eigenvalue gradient v_i v_j on the pattern (Methodology section 2,
-  eigenvalue problems).
+  eigenvalue problems);
+* ``oracle.inverse``: the loss, gradient and Adam trajectory of the
+  inverse-coefficient experiment (Results: a coefficient recovered by
+  gradient descent through the solver).
 
 Inputs of any float dtype are promoted to fp64 (an fp32 problem is solved in
 fp64 arithmetic on its fp32-rounded values); int32 row_ptr is widened to int64.

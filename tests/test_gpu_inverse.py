@@ -1,5 +1,6 @@
 """The inverse-coefficient experiment (learning kappa through the
-differentiable solve) against the CPU reference in tests/inverse_ref.py:
+differentiable solve) against its oracle, oracle.inverse (pinned by
+tests/test_oracle_inverse_pins.py):
 matrix values, loss and gradient at a fixed theta, the first Adam steps, and
 recovery of kappa on a 32 x 32 grid."""
 import numpy as np
@@ -8,7 +9,7 @@ import torch
 
 import workloads as W
 from gpu_helpers import banner, relerr
-from inverse_ref import Reference, adam
+from oracle.inverse import Reference, adam
 
 pytestmark = pytest.mark.gpu
 
