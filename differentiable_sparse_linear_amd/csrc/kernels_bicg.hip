@@ -14,7 +14,7 @@
 //            rhat.v_j and ||r_j||^2.  At j = 0, r_0 is read as stored and
 //            rho_0 = ||r_0||^2 (rhat = r_0) comes from the init partials.
 //   bicg_st  (iteration j): stop tests on the exact ||r_j|| (converged, maxit,
-//            rho_j = 0); alpha_j = rho_j / rhat.v_j; s = r_j - alpha v_j
+//            rho_j = 0 or NaN); alpha_j = rho_j / rhat.v_j; s = r_j - alpha v_j
 //            evaluated while gathering, t = A s; partials t.s, t.t, s.s,
 //            rhat.s, rhat.t.
 // The textbook's third reduction (rhat.r_j after the r update) comes from
@@ -37,6 +37,11 @@ template <typename T>
 __device__ __forceinline__ T fmaB(T a, T b, T c) {
     return fma(a, b, c);
 }
+
+// A Krylov denominator that vanished: zero, or NaN (a NaN or an infinity in
+// b or in the values turns the dots into NaN within an iteration or two; the
+// iteration can divide by neither).
+__device__ __forceinline__ bool vanished(double d) { return !(fabs(d) > 0.0); }
 
 // r = rhat = b - A x0 (or b with x = 0); partials ||r||^2 (= rhat.r) and b.b.
 template <typename T, typename IT>
@@ -153,7 +158,7 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
             }
             return false;
         }
-        if (tt == 0.0 || ts == 0.0) {
+        if (vanished(tt) || vanished(ts)) {
             if (block0()) st->spmv += 1;  // the t product of iteration j - 1
             finish(st, A->ndone, SLA_BREAKDOWN, it - 1, 0.0);
             return false;
@@ -249,12 +254,12 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
             return false;
         }
         const double rho = st->rho[it & 1];
-        if (rho == 0.0) {
+        if (vanished(rho)) {
             finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
             return false;
         }
         if (block0()) st->spmv += 1;  // v_j = A p_j
-        if (rv == 0.0) {
+        if (vanished(rv)) {
             finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
             return false;
         }
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void bicg_split_xpv_u_kernel(const IterArgs
             }
             return;
         }
-        if (tt == 0.0 || ts == 0.0) {
+        if (vanished(tt) || vanished(ts)) {
             if (block0()) st->spmv += 1;  // the t product of iteration j - 1
             finish(st, A->ndone, SLA_BREAKDOWN, it - 1, 0.0);
             return;
@@ -449,12 +454,12 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_u_kernel(const IterArgs<
         return;
     }
     const double rho = st->rho[it & 1];
-    if (rho == 0.0) {
+    if (vanished(rho)) {
         finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
         return;
     }
     if (block0()) st->spmv += 1;  // v_j = A p_j
-    if (rv == 0.0) {
+    if (vanished(rv)) {
         finish(st, A->ndone, SLA_BREAKDOWN, it, rr);
         return;
     }

@@ -259,12 +259,12 @@ out:
  *
  *   r = b, rhat = b, rho_prev = alpha = omega = 1, v = p = 0
  *   for k = 1..maxit:
- *     rho = rhat.r                      (0: BREAKDOWN)
+ *     rho = rhat.r                      (0 or NaN: BREAKDOWN)
  *     beta = (rho/rho_prev)(alpha/omega); p = r + beta (p - omega v)
- *     v = A p; alpha = rho / (rhat.v)   (rhat.v = 0: BREAKDOWN)
+ *     v = A p; alpha = rho / (rhat.v)   (rhat.v = 0 or NaN: BREAKDOWN)
  *     s = r - alpha v
  *     if ||s|| <= tol ||b||: x += alpha p, stop (half step; spmv = 2k-1)
- *     t = A s; omega = (t.s)/(t.t)      (t.t = 0 or omega = 0: BREAKDOWN)
+ *     t = A s; omega = (t.s)/(t.t)      (t.t or t.s = 0 or NaN: BREAKDOWN)
  *     x += alpha p + omega s; r = s - omega t; rho_prev = rho
  *     if ||r|| <= tol ||b||: stop (spmv = 2k)
  *
@@ -304,7 +304,7 @@ int orc_bicgstab(int64_t n, const int64_t *row_ptr, const int32_t *col,
     for (k = 1; k <= maxit; ++k) {
         int64_t i;
         double rho = orc_dot(n, rh, r);
-        if (rho == 0.0) {
+        if (!(fabs(rho) > 0.0)) {
             status = ORC_BREAKDOWN;
             --k;
             break;
@@ -316,7 +316,7 @@ int orc_bicgstab(int64_t n, const int64_t *row_ptr, const int32_t *col,
         orc_spmv(n, row_ptr, col, val, p, v);
         ++nmv;
         double rv = orc_dot(n, rh, v);
-        if (rv == 0.0) {
+        if (!(fabs(rv) > 0.0)) {
             status = ORC_BREAKDOWN;
             --k;
             break;
@@ -340,7 +340,7 @@ int orc_bicgstab(int64_t n, const int64_t *row_ptr, const int32_t *col,
         ++nmv;
         double tt = orc_dot(n, t, t);
         double ts = orc_dot(n, t, s);
-        if (tt == 0.0 || ts == 0.0) {
+        if (!(fabs(tt) > 0.0) || !(fabs(ts) > 0.0)) {
             status = ORC_BREAKDOWN;
             --k;
             break;

@@ -16,7 +16,10 @@ The oracle cannot redo 500-iteration solves of this size inside a test, so:
     solves compared at the same iterate); the residual the solver reports
     equals the oracle's recomputation of ||b - A x|| / ||b||;
   * the gradient on the pattern at sampled entries equals -lambda_i x_j
-    exactly (one rounding on both sides), and grad_b equals lambda.
+    exactly (one rounding on both sides), and grad_b equals lambda;
+  * the homogeneity identity (oracle pin P14) over the whole gradient: for
+    the capped solve sum_k gv_k v_k + sum_i gb_i b_i = lambda . (b - A x),
+    with b - A x from the oracle's product of the GPU's x.
 """
 import json
 import os
@@ -137,3 +140,13 @@ def test_config5_configured_solve_matches_oracle_at_maxit(big, hip):
     # of the GPU's x; they drift apart by rounding only
     tr = float(O.true_relres(p.row_ptr, p.col, p.values, xh[None, :], p.b)[0])
     assert abs(tr - rel) <= 1e-6 * tr, (tr, rel)
+    banner("config 5: homogeneity over the whole gradient")
+    gvv = gv.reshape(-1) * d["val"].reshape(-1)
+    gbb = gb.reshape(-1) * d["b"].reshape(-1)
+    S = float(gvv.sum() + gbb.sum())
+    mag = float(gvv.abs().sum() + gbb.abs().sum())
+    del gvv, gbb
+    res = p.b[0] - np.ravel(O.spmv(p.row_ptr, p.col, p.values[0], xh))
+    want = float(np.dot(lam, res))
+    eps = np.finfo(np.float64).eps
+    assert abs(S - want) <= 64 * eps * (mag + float(np.abs(lam) @ np.abs(res))), (S, want, mag)

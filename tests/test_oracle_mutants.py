@@ -31,6 +31,8 @@ MUTANTS = {
                                   "grad_x[i] += val[k] * gy[col[k]];"),
     "vjp_grad_val_transposed": ("grad_val[k] = gy[i] * x[col[k]];",
                                 "grad_val[k] = x[i] * gy[col[k]];"),
+    "bicg_nan_denominator_passes": ("if (!(fabs(tt) > 0.0) || !(fabs(ts) > 0.0)) {",
+                                    "if (tt == 0.0 || ts == 0.0) {"),
     "transpose_unstable": ("int64_t dst = next[col[k]]++;", "int64_t dst = next[col[k]]; next[col[k]] += 1; dst = row_ptr_t[col[k] + 1] - 1 - (dst - row_ptr_t[col[k]]);"),
 }
 

@@ -379,6 +379,39 @@ def pin_special_cases():
 
 
 # --------------------------------------------------------------------------
+# Non-finite input (reading: a Krylov denominator that is zero or NaN ends
+# the iteration with BREAKDOWN).  A NaN in b makes the first denominator
+# NaN (CG: p.Ap; BiCGStab: rhat.r), so both stop at iteration 0 with x = 0.
+# An infinite off-diagonal value A_ij turns r_i into NaN within one
+# iteration (alpha = rho / inf = 0 and r_i - 0 * inf), so the next
+# denominator is NaN.
+# --------------------------------------------------------------------------
+def pin_nonfinite_input():
+    p = W.config(1, size=6)
+    b = p.b.copy()
+    b[0, 7] = np.nan
+    for method, pre in (("cg", "jacobi"), ("cg", "none"), ("bicgstab", "none")):
+        r = O.solve(p.row_ptr, p.col, p.values, b, method, pre, 1e-10, 100)
+        assert r.status[0] == O.BREAKDOWN and r.iters[0] == 0, (method, pre)
+        assert not np.any(r.x), (method, pre)
+    rows = np.repeat(np.arange(p.n), np.diff(p.row_ptr))
+    for k in np.nonzero(rows != p.col)[0][[5, 6, 11, 20]]:
+        i, j = int(rows[k]), int(p.col[k])
+        v = p.values.copy()
+        v[0, k] = np.inf
+        # BiCGStab: rhat.v = b_i * inf is infinite, alpha = 0, s_i = NaN, so
+        # t.t is NaN in iteration 1: breakdown with no iteration completed
+        r = O.solve(p.row_ptr, p.col, v, p.b, "bicgstab", "none", 1e-10, 100)
+        assert r.status[0] == O.BREAKDOWN and r.iters[0] == 0, k
+        # CG: p_0 = z_0 = b / diag(A); p.Ap holds p_i * inf * p_j, negative
+        # (a breakdown at once) or positive (alpha = 0, r_i = NaN, then a NaN
+        # p.Ap in iteration 2)
+        r = O.solve(p.row_ptr, p.col, v, p.b, "cg", "jacobi", 1e-10, 100)
+        expect = 1 if p.b[0, i] * p.b[0, j] > 0 else 0
+        assert r.status[0] == O.BREAKDOWN and r.iters[0] == expect, k
+
+
+# --------------------------------------------------------------------------
 # P16 -- BiCGStab half step: b an eigenvector => s = 0 after one product,
 # x = v / lambda (closed form), one iteration, one SpMV
 # --------------------------------------------------------------------------
@@ -590,7 +623,7 @@ ALL_PINS = [pin_p1_spmv_eigvecs, pin_p2_spmv_dense, pin_p2b_sampled_rows_dense, 
             pin_p19_nonlinear_reduces_to_linear, pin_p20_nonlinear_adjoint_finite_differences,
             pin_p21_nonlinear_adjoint_nonsymmetric, pin_p22_eigsh_laplacian_spectrum,
             pin_p23_eig_grad_finite_differences,
-            pin_pattern_checks, pin_special_cases]
+            pin_pattern_checks, pin_special_cases, pin_nonfinite_input]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=[f.__name__ for f in ALL_PINS])
