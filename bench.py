@@ -31,25 +31,38 @@ iteration are timed; each launch is priced at half of one textbook BiCGStab
 iteration, (2*(nnz*(sv + 4) + (n + 1)*sr) + 19*n*sv) / 2, and moves the
 matrix plus 7.5 vectors on average (bicg_xpv reads s, t, p, v, x, rhat and
 writes x, r, p, v; bicg_st reads r, v, rhat and writes s, t).
-``traffic`` is the HBM bytes per launch measured with rocprofv3 counters
-(FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a
-1 GiB copy) and stored under profiles/ with a hash of the kernel's sources;
-it is null when no such record matches the sources being run.
-``cpu_baseline`` times the oracle (plain fp64 C) on the host on one forward +
-adjoint solve of the same arrays.
+``traffic`` is the bytes per launch past L2 (to HBM or the Infinity Cache)
+measured with rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each scaled by
+what the counter reads for the probe library's 1 GiB copy; a third pass of
+the read-request-size counters checks the scaled FETCH_SIZE without any
+factor) and stored under profiles/ with a hash of the kernel's sources; it is
+null when no such record matches the sources being run.  ``dram_GBps`` and
+``dram_frac`` are that traffic over the average launch time; ``model_frac``
+(= ``frac``) and ``kernel_frac`` price the launch at the textbook and the
+fused kernel's own bytes.  ``ceilings`` are the chip's streaming and LDS
+bandwidths measured in the same run by libsla_probe.so over 2 GiB arrays.
+On the one-workgroup solver (at most 4096 rows) the roofline is LDS
+bandwidth: (S + 11) values per row and iteration (S the gather slots).
+``memory`` is the device memory of one forward + adjoint step.
+``cpu_baseline`` times the oracle (plain fp64 C) on the host on bounded
+samples of the same arrays, on all host threads and on one.
 
 Counter and trace summaries (written under profiles/):
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- \
         python3 bench.py --kernel-only 2
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- \
         python3 bench.py --kernel-only 2
-    python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write
+    rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum \
+        TCC_EA0_RDREQ_128B_sum --output-format csv -d OUT/pmc_sizes -o run -- \
+        python3 bench.py --kernel-only 2
+    python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write OUT/pmc_sizes
     rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace -o run -- \
         python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline
     python3 bench.py --summarize-trace OUT/trace
 """
 import argparse
 import csv
+import ctypes
 import glob
 import hashlib
 import json
@@ -64,8 +77,18 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# LDS: 256 compute units x 256 bytes per clock x 2.4 GHz (CDNA4 doubled the
+# 128 bytes per clock of CDNA3; the probe's ds_read_b128 stream sustains 140
+# TB/s, above what 128 bytes per clock could deliver)
+LDS_PEAK_GBPS = 256 * 256 * 2.4
+LDS_PEAK_CU_GBPS = 256 * 2.4  # one compute unit
 CSRC = os.path.join(ROOT, "differentiable_sparse_linear_amd", "csrc")
-CALIB_BYTES = 1 << 30  # the calibration copy reads and writes 1 GiB
+PROBE_LIB = os.path.join(ROOT, "differentiable_sparse_linear_amd", "libsla_probe.so")
+CALIB_BYTES = 1 << 30  # the calibration kernels move 1 GiB each way
+CEIL_BYTES = 2 << 30   # arrays of the ceiling measurement (beyond the 256 MB Infinity Cache)
+# request-size counters of the optional third counter pass (bytes per request)
+SIZE_COUNTERS = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64,
+                 "TCC_EA0_RDREQ_128B_sum": 128}
 
 
 def parse():
@@ -82,10 +105,14 @@ def parse():
     ap.add_argument("--kernel-only", type=int, default=0,
                     help="run this many steps and a 1 GiB calibration copy, nothing timed "
                          "(for counter collection)")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs of --kernel-only")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="summarise the rocprofv3 --pmc runs of --kernel-only: FETCH_SIZE, "
+                         "WRITE_SIZE and optionally the read-request sizes")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-block", metavar="PMC_DIR",
+                    help="summarise a rocprofv3 --pmc run of the one-workgroup solver's LDS "
+                         "counters (workloads of at most 4096 rows)")
     ap.add_argument("--op", default="solve",
                     choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"),
                     help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
@@ -199,24 +226,57 @@ def _rows(d, pattern):
         return list(csv.DictReader(fh))
 
 
-def _counter_pass(d, short_names):
-    """(mean KiB of the active dominant-kernel dispatches, their count, all
-    dispatches, KiB of the calibration copy)."""
+def _dispatches(d):
+    """Counter rows of a --pmc run grouped by dispatch: [(kernel name,
+    {counter: value})] in dispatch order."""
     rows = _rows(d, "*counter_collection.csv")
-    vals, copies = [], []
+    by = {}
     for r in rows:
-        name = r["Kernel_Name"]
-        v = float(r["Counter_Value"])
+        e = by.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], {}])
+        e[1][r["Counter_Name"]] = e[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [tuple(by[k]) for k in sorted(by)]
+
+
+def _is_probe(name, which):
+    return f"::{which}_kernel(" in name and "sla::" not in name
+
+
+def _pass_stats(d, short_names, counter):
+    """(mean of `counter` over the active dominant-kernel dispatches, their
+    count, all its dispatches, {probe: value} of the calibration kernels)."""
+    vals, probes = [], {}
+    for name, c in _dispatches(d):
+        if counter not in c:
+            continue
         if any(f"sla::{s}<" in name for s in short_names):
-            vals.append(v)
-        elif "copy" in name.lower() and "sla::" not in name:
-            copies.append(v)
-    if not vals or not copies:
+            vals.append(c[counter])
+        for which in ("copy", "read", "write"):
+            if _is_probe(name, which):
+                probes[which] = max(probes.get(which, 0.0), c[counter])
+    if not vals or "copy" not in probes:
         raise SystemExit(f"{d}: dominant kernel or calibration copy not found")
     # launches enqueued after the stop end at their first barrier and read a few bytes
     top = max(vals)
     active = [v for v in vals if v >= 0.01 * top]
-    return sum(active) / len(active), len(active), len(vals), max(copies)
+    return sum(active) / len(active), len(active), len(vals), probes
+
+
+def _size_stats(d, short_names):
+    """Read bytes by request size (32, 64, 128 B) per active dominant-kernel
+    dispatch and for the calibration kernels."""
+    ker, probes = [], {}
+    for name, c in _dispatches(d):
+        if not all(k in c for k in SIZE_COUNTERS):
+            continue
+        by = sum(c[k] * sz for k, sz in SIZE_COUNTERS.items())
+        if any(f"sla::{s}<" in name for s in short_names):
+            ker.append(by)
+        for which in ("copy", "read"):
+            if _is_probe(name, which):
+                probes[which] = max(probes.get(which, 0.0), by)
+    top = max(ker)
+    active = [v for v in ker if v >= 0.01 * top]
+    return sum(active) / len(active), probes
 
 
 def _form_flag(args):
@@ -229,25 +289,32 @@ def summarize_counters(args):
                                                 p.values.itemsize, p.row_ptr.itemsize,
                                                 form_bytes(args.column_form, p))
     names = kernel.split("+")
-    f_kib, f_n, f_all, f_copy = _counter_pass(args.summarize_counters[0], names)
-    w_kib, w_n, w_all, w_copy = _counter_pass(args.summarize_counters[1], names)
-    f_fac = CALIB_BYTES / (f_copy * 1024.0)
-    w_fac = CALIB_BYTES / (w_copy * 1024.0)
+    dirs = args.summarize_counters
+    if len(dirs) not in (2, 3):
+        raise SystemExit("--summarize-counters FETCH_DIR WRITE_DIR [SIZES_DIR]")
+    f_kib, f_n, f_all, f_pr = _pass_stats(dirs[0], names, "FETCH_SIZE")
+    w_kib, w_n, w_all, w_pr = _pass_stats(dirs[1], names, "WRITE_SIZE")
+    f_fac = CALIB_BYTES / (f_pr["copy"] * 1024.0)
+    w_fac = CALIB_BYTES / (w_pr["copy"] * 1024.0)
     fetch = f_kib * 1024.0 * f_fac
     write = w_kib * 1024.0 * w_fac
+    wl = f" --workload {args.workload}"
     out = [
         f"# HBM traffic of {kernel}, workload {p.name}",
         "",
         "Commands (repository root; OUT is any output folder):",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- "
-        f"python3 bench.py --kernel-only 2 --workload {args.workload}",
+        f"python3 bench.py --kernel-only 2{wl}",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- "
-        f"python3 bench.py --kernel-only 2 --workload {args.workload}",
-        f"  python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write --workload "
-        f"{args.workload}{_form_flag(args)}",
+        f"python3 bench.py --kernel-only 2{wl}",
+        "  rocprofv3 --pmc " + " ".join(["TCC_EA0_RDREQ_sum"] + list(SIZE_COUNTERS)) +
+        f" --output-format csv -d OUT/pmc_sizes -o run -- python3 bench.py --kernel-only 2{wl}",
+        f"  python3 bench.py --summarize-counters OUT/pmc_fetch OUT/pmc_write OUT/pmc_sizes"
+        f"{wl}{_form_flag(args)}",
         "",
-        "Calibration: a torch copy of 1 GiB (reads 1 GiB, writes 1 GiB) in the same run;",
-        "factor = 1 GiB / counter reading of that copy.",
+        "Calibration: the probe kernels of libsla_probe.so in the same run, over 1 GiB:",
+        "a copy (reads 1 GiB, writes 1 GiB) and a read-only sum (reads 1 GiB);",
+        "factor = 1 GiB / the counter's reading of the copy.",
         "",
         f"kernel: {kernel}",
         f"workload: {p.name}",
@@ -258,8 +325,13 @@ def summarize_counters(args):
         f"dispatches_active_write_pass: {w_n} of {w_all}",
         f"fetch_kib_per_dispatch: {f_kib:.1f}",
         f"write_kib_per_dispatch: {w_kib:.1f}",
-        f"copy_fetch_kib: {f_copy:.1f}",
-        f"copy_write_kib: {w_copy:.1f}",
+        f"copy_fetch_kib: {f_pr['copy']:.1f}",
+        f"copy_write_kib: {w_pr['copy']:.1f}",
+    ]
+    if "read" in f_pr:
+        out.append(f"read_probe_fetch_kib: {f_pr['read']:.1f}")
+        out.append(f"read_probe_fetch_factor: {CALIB_BYTES / (f_pr['read'] * 1024.0):.4f}")
+    out += [
         f"fetch_factor: {f_fac:.4f}",
         f"write_factor: {w_fac:.4f}",
         f"fetch_bytes_per_launch: {fetch:.0f}",
@@ -268,6 +340,74 @@ def summarize_counters(args):
         f"algorithmic_bytes_per_launch: {kbytes}",
         f"kernel_bytes_per_launch: {own}",
         f"traffic_over_kernel_bytes: {(fetch + write) / own:.3f}",
+    ]
+    if len(dirs) == 3:
+        by, pr = _size_stats(dirs[2], names)
+        out += [
+            "",
+            "Cross-check from the read-request sizes (32 B x RDREQ_32B + 64 B x RDREQ_64B +",
+            "128 B x RDREQ_128B), no calibration factor:",
+            f"sized_read_bytes_per_launch: {by:.0f}",
+            f"sized_read_over_scaled_fetch: {by / fetch:.4f}",
+        ]
+        for which in ("copy", "read"):
+            if which in pr:
+                out.append(f"sized_read_bytes_{which}_probe_over_1GiB: {pr[which] / CALIB_BYTES:.4f}")
+    print("\n".join(out))
+
+
+BLOCK_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+                  "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_BUSY_CU_CYCLES",
+                  "SQ_INSTS_VALU", "SQ_WAIT_INST_LDS")
+
+
+def summarize_block(args):
+    """LDS traffic of the one-workgroup CG solver from one counter run: LDS
+    bytes loaded and stored (the BANDWIDTH counters count 64-byte units),
+    LDS instructions, bank-conflict and LDS-active cycles, busy compute-unit
+    cycles, VALU instructions; per dispatch (forward and adjoint solves
+    alternate) and their mean."""
+    p = load_problem(args)
+    wl = f" --workload {args.workload}" + (" --fp32" if args.fp32 else "")
+    rows = [(n, c) for n, c in _dispatches(args.summarize_block) if "sla::block_cg_kernel<" in n]
+    if not rows:
+        raise SystemExit("no block_cg_kernel dispatches")
+    out = [
+        f"# LDS counters of block_cg_kernel, workload {p.name}",
+        "",
+        "Commands (repository root; OUT is any output folder):",
+        "  rocprofv3 --pmc " + " ".join(BLOCK_COUNTERS) +
+        f" --output-format csv -d OUT/pmc_block -o run -- python3 bench.py --kernel-only 2{wl}",
+        f"  python3 bench.py --summarize-block OUT/pmc_block{wl}",
+        "",
+        f"kernel: {rows[0][0].split('(')[0].replace('void ', '')}",
+        f"workload: {p.name}",
+        f"n: {p.n}",
+        f"batch: {p.batch}",
+        f"source_sha256: {sources_sha(['kernels_cg.hip', 'sla_internal.h'])}",
+        f"dispatches: {len(rows)} (forward and adjoint solves alternate)",
+        "",
+        f"{'dispatch':>8} {'lds_MB':>10} {'lds_insts':>12} {'bank_confl_cyc':>15} "
+        f"{'lds_active_cyc':>15} {'busy_cu_qcyc':>13} {'valu_insts':>12}",
+    ]
+    tot = {k: 0.0 for k in BLOCK_COUNTERS}
+    for i, (_, c) in enumerate(rows):
+        lds = (c.get("SQ_INSTS_LDS_LOAD_BANDWIDTH", 0) + c.get("SQ_INSTS_LDS_STORE_BANDWIDTH", 0)) * 64
+        out.append(f"{i:8d} {lds / 1e6:10.1f} {c.get('SQ_INSTS_LDS', 0):12.0f} "
+                   f"{c.get('SQ_LDS_BANK_CONFLICT', 0):15.0f} {c.get('SQ_LDS_IDX_ACTIVE', 0):15.0f} "
+                   f"{c.get('SQ_BUSY_CU_CYCLES', 0):13.0f} {c.get('SQ_INSTS_VALU', 0):12.0f}")
+        for k in BLOCK_COUNTERS:
+            tot[k] += c.get(k, 0.0)
+    m = len(rows)
+    lds = (tot["SQ_INSTS_LDS_LOAD_BANDWIDTH"] + tot["SQ_INSTS_LDS_STORE_BANDWIDTH"]) * 64 / m
+    out += [
+        "",
+        f"lds_bytes_per_dispatch: {lds:.0f}",
+        f"lds_load_fraction: {tot['SQ_INSTS_LDS_LOAD_BANDWIDTH'] / max(1.0, tot['SQ_INSTS_LDS_LOAD_BANDWIDTH'] + tot['SQ_INSTS_LDS_STORE_BANDWIDTH']):.3f}",
+        f"lds_insts_per_dispatch: {tot['SQ_INSTS_LDS'] / m:.0f}",
+        f"bank_conflict_over_lds_active: {tot['SQ_LDS_BANK_CONFLICT'] / max(1.0, tot['SQ_LDS_IDX_ACTIVE']):.4f}",
+        f"valu_insts_per_lds_inst: {tot['SQ_INSTS_VALU'] / max(1.0, tot['SQ_INSTS_LDS']):.2f}",
+        f"lds_wait_quadcycles_per_dispatch: {tot['SQ_WAIT_INST_LDS'] / m:.0f}",
     ]
     print("\n".join(out))
 
@@ -301,12 +441,21 @@ def summarize_trace(args):
                    f"{float(r['TotalDurationNs']) / 1e6:10.2f} {float(r['Percentage']):6.2f}  "
                    f"{short}")
     durs = []
+    block = p.method == "cg" and p.n <= 4096
+    if block:
+        names = ["block_cg_kernel"]  # one launch per solve of the whole batch
+        kernel = "block_cg_kernel"
     if args.op != "solve":
         names = []  # the per-kernel block below describes the solve's iteration kernel
     for r in trace:
         if any(f"sla::{s}<" in r["Kernel_Name"] for s in names):
             durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    if durs:
+    if durs and block:
+        out += ["", f"kernel: {kernel}", f"dispatches: {len(durs)}",
+                f"avg_us: {sum(durs) / len(durs):.2f}",
+                "forward and adjoint solves alternate: " +
+                ", ".join(f"{d:.1f}" for d in durs[:8]) + " us"]
+    elif durs:
         top = max(durs)
         # launches enqueued after the stop end at their first barrier (a few microseconds)
         active = [d for d in durs if d >= 0.25 * top]
@@ -324,6 +473,95 @@ def summarize_trace(args):
             f"kernel_GBps_active: {own / (avg * 1e-6) / 1e9:.1f}",
         ]
     print("\n".join(out))
+
+
+# ------------------------------------------------------------------ ceilings
+
+_probe = None
+
+
+def probe_lib():
+    """libsla_probe.so: the streaming and LDS ceiling kernels."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build it with "
+                               "`python -m differentiable_sparse_linear_amd.build`")
+        lib = ctypes.CDLL(PROBE_LIB)
+        P, I64, D, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int32
+        lib.sla_probe_blocks.restype = I32
+        lib.sla_probe_read.argtypes = [P, I64, P, P]
+        lib.sla_probe_read.restype = I32
+        lib.sla_probe_copy.argtypes = [P, P, I64, P]
+        lib.sla_probe_copy.restype = I32
+        lib.sla_probe_write.argtypes = [P, I64, D, P]
+        lib.sla_probe_write.restype = I32
+        lib.sla_probe_lds.argtypes = [I64, P, P]
+        lib.sla_probe_lds.restype = I64
+        _probe = lib
+    return _probe
+
+
+def _vp(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def probe_kernels(nbytes, dev, reps=1):
+    """Run the probe's read, copy and write kernels over nbytes on the
+    current stream, reps times each; returns {name: seconds per call} timed
+    with events on that stream (the kernels run there)."""
+    import torch
+    lib = probe_lib()
+    n = nbytes // 8
+    a = torch.rand(n, dtype=torch.float64, device=dev)
+    b = torch.empty_like(a)
+    part = torch.empty(lib.sla_probe_blocks(), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    calls = {"read": lambda: lib.sla_probe_read(_vp(a), n, _vp(part), sp),
+             "copy": lambda: lib.sla_probe_copy(_vp(a), _vp(b), n, sp),
+             "write": lambda: lib.sla_probe_write(_vp(b), n, 1.0, sp)}
+    out = {}
+    for name, call in calls.items():
+        if call() != 0:  # a first call brings the clocks up
+            raise RuntimeError(f"probe {name} failed")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            call()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = ev0.elapsed_time(ev1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_ceilings(dev):
+    """The chip's bandwidth ceilings in GB/s, measured now: read-only, copy
+    (read + write) and write-only over 2 GiB arrays, and LDS reads."""
+    import torch
+    t = probe_kernels(CEIL_BYTES, dev, reps=10)
+    lib = probe_lib()
+    part = torch.empty(max(lib.sla_probe_blocks(), 2048), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    lib.sla_probe_lds(100, _vp(part), sp)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    lds_bytes = lib.sla_probe_lds(500, _vp(part), sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    lds_s = ev0.elapsed_time(ev1) * 1e-3
+    return {"read_GBps": CEIL_BYTES / t["read"] / 1e9,
+            "copy_GBps": 2 * CEIL_BYTES / t["copy"] / 1e9,
+            "write_GBps": CEIL_BYTES / t["write"] / 1e9,
+            "lds_GBps": lds_bytes / lds_s / 1e9,
+            "arrays_bytes": CEIL_BYTES, "kernels": "libsla_probe.so (non-temporal, 16 B per access)"}
 
 
 # ------------------------------------------------------------------ benchmark
@@ -503,6 +741,8 @@ def main():
         return summarize_counters(args)
     if args.summarize_trace:
         return summarize_trace(args)
+    if args.summarize_block:
+        return summarize_block(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); multi-GPU "
               "sharding is a design note, not part of this build", file=sys.stderr)
@@ -551,11 +791,10 @@ def main():
         for _ in range(args.kernel_only):
             step()
         torch.cuda.synchronize()
-        src = torch.empty(CALIB_BYTES // 8, dtype=torch.float64, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        # known-traffic kernels for the counters' calibration: copy, read, write of 1 GiB
+        probe_kernels(CALIB_BYTES, dev)
         torch.cuda.synchronize()
-        print(json.dumps({"kernel_only": args.kernel_only, "calibration_copy_bytes": CALIB_BYTES}))
+        print(json.dumps({"kernel_only": args.kernel_only, "calibration_bytes": CALIB_BYTES}))
         return
 
     for _ in range(args.warmup):
@@ -580,8 +819,9 @@ def main():
         assert np.all((info["status"] == 0) | (info["status"] == 1)), info
 
     block_path = p.method == "cg" and p.n <= 4096
+    ceilings = measure_ceilings(dev)
     if block_path:
-        roofline = None  # one workgroup per system: matrix in registers, vectors in LDS
+        roofline = block_roofline(p, pat, val, b, x, opts, stream)
     else:
         # dominant kernel, timed with HIP events around each launch on `stream`
         fi_p, ai_p = step(profile=True)
@@ -594,12 +834,23 @@ def main():
         kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
                                                     p.values.itemsize, p.row_ptr.itemsize, fb)
         achieved = kbytes / k_avg_s / 1e9
+        traffic = read_traffic(kernel, p.name, sources_sha(srcs))
+        dram = traffic / k_avg_s / 1e9 if traffic else None
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": read_traffic(kernel, p.name, sources_sha(srcs)),
+                    "traffic": traffic,
+                    "model_frac": achieved / HBM_PEAK_GBPS,
                     "bytes_per_launch": kbytes, "kernel_bytes_per_launch": own,
                     "iteration_form": form, "kernel_GBps": own / k_avg_s / 1e9,
-                    "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n}
+                    "kernel_frac": own / k_avg_s / 1e9 / HBM_PEAK_GBPS,
+                    "dram_GBps": dram, "dram_frac": dram / HBM_PEAK_GBPS if dram else None,
+                    "dram_frac_of_copy_ceiling": dram / ceilings["copy_GBps"] if dram else None,
+                    "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
+                    "hbm_target": "at least 70 % of peak HBM bandwidth, read as dram_frac "
+                                  "(bytes past L2 by the counters; model_frac prices a launch at "
+                                  "the textbook iteration's bytes, kernel_frac at the fused "
+                                  "kernel's own)"}
+    memory = peak_memory(pat, step)
 
     result = {
         "metric": "CG iters/sec + achieved HBM GB/s (% peak), fwd+adjoint solve, 1e6-DOF 3D Poisson",
@@ -621,20 +872,83 @@ def main():
         "solves_per_s": 2 * args.steps / wall,
         "event_ms_per_step": ev_ms / args.steps,
         "roofline": roofline,
+        "ceilings": ceilings,
+        "memory": memory,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(p, budget_s=15.0):
-    """The oracle on a bounded sample of the same workload: whole forward +
-    adjoint solves of the batch's systems in order until about `budget_s`
-    seconds have passed (at least one); systems whose solve would take many
-    minutes (n * maxit > 1e10, the 512^3 case) are cut to 5 iterations each
-    way.  Rate in iterations (summed over systems) per second."""
+def block_roofline(p, pat, val, b, x, opts, stream):
+    """The one-workgroup CG solver keeps p, x, r and M^-1 in LDS and the
+    matrix in registers, so its bound is LDS bandwidth.  Per row and
+    iteration it gathers S entries of p (S slots: the longest row) and
+    reads p, x, r, M^-1 for the updates and the dot products (S + 8 loads)
+    and stores x, r, p: (S + 11) values.  One forward solve is timed with
+    events on the stream it runs on; the peak is the LDS of the compute
+    units the batch occupies (one workgroup of 1024 threads per unit)."""
+    import torch
+    sv = p.values.itemsize
+    rows = np.diff(p.row_ptr)
+    S = int(rows.max())
+    S = 4 if S <= 4 else (S if S in (5, 6) else 8)
+    per_row = (S + 11) * sv
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    _, fi = pat.solve(val, b, out=x, **opts)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t = ev0.elapsed_time(ev1) * 1e-3
+    lds = int(fi["iters"].astype(np.int64).sum()) * p.n * per_row
+    cus = min(p.batch, 256)
+    peak = LDS_PEAK_CU_GBPS * cus
+    achieved = lds / t / 1e9
+    return {"bound": "lds", "kernel": "block_cg_kernel", "achieved": achieved, "peak": peak,
+            "unit": "GB/s", "frac": achieved / peak, "traffic": None,
+            "lds_bytes_per_row_iteration": per_row, "slots": S,
+            "forward_ms": t * 1e3, "compute_units": cus,
+            "system_iterations_per_s": float(fi["iters"].sum()) / t}
+
+
+def peak_memory(pat, step):
+    """Device memory of one forward + adjoint step: the handle's workspace
+    (allocated once at create) and the peak of the caller's tensors (values,
+    b, x, the gradients) that torch holds, beside the pages' figures for
+    context (naive backpropagation through 1000 CG iterations at 1e6 unknowns
+    estimated at about 80 GB; the adjoint measured at about 328 MB, 195 times
+    less; Problem statement and Results of the torch-sla explainer)."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    step()
+    torch.cuda.synchronize()
+    peak = int(torch.cuda.max_memory_allocated())
+    ws = int(pat.workspace_bytes())
+    return {"handle_workspace_bytes": ws, "torch_peak_bytes": peak,
+            "peak_device_bytes": ws + peak,
+            "pages_context": {"naive_backprop_GB_estimate": 80, "adjoint_MB_measured": 328,
+                              "reduction": 195}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(p, budget_s, maxit):
+    """Forward + adjoint oracle solves of the batch's systems in order, each
+    cut to `maxit` iterations each way, until about budget_s seconds have
+    passed (at least one system): (iterations, systems, seconds)."""
     import oracle as O
-    maxit = 5 if p.n * p.maxit > 1e10 else p.maxit
     t0 = time.perf_counter()
     its = systems = 0
     for s in range(p.batch):
@@ -647,12 +961,41 @@ def cpu_baseline(p, budget_s=15.0):
         systems += 1
         if time.perf_counter() - t0 > budget_s:
             break
-    t = time.perf_counter() - t0
+    return its, systems, time.perf_counter() - t0
+
+
+def cpu_baseline(p, budget_s=15.0, serial_budget_s=8.0):
+    """The oracle (plain fp64 C, OpenMP loops, fixed-order dot products) on
+    bounded samples of the same workload, on this host's cores: whole
+    forward + adjoint solves on all threads for about budget_s seconds
+    (systems whose solve would take many minutes, n * maxit > 1e10, the
+    512^3 case, cut to 5 iterations each way), then the same on one thread
+    (set in-process), cut to as many iterations each way as fit about
+    serial_budget_s seconds.  Rates in iterations (summed over systems) per
+    second."""
+    import oracle as O
+    maxit = 5 if p.n * p.maxit > 1e10 else p.maxit
+    threads = O.num_threads()
+    its, systems, t = _oracle_rate(p, budget_s, maxit)
     cut = f", cut to {maxit} iterations each way" if maxit != p.maxit else ""
-    return {"value": its / t, "unit": "PCG iterations/s", "cores": O.num_threads(),
-            "kind": "oracle",
+    rate = its / t
+    # one thread: iterations per second are at best the all-thread rate over
+    # the threads; size the cut from it
+    O.set_num_threads(1)
+    try:
+        per_it = threads / rate
+        m1 = int(max(2, min(maxit, serial_budget_s / (2 * per_it))))
+        its1, sys1, t1 = _oracle_rate(p, serial_budget_s, m1)
+    finally:
+        O.set_num_threads(threads)
+    return {"value": rate, "unit": "PCG iterations/s", "cores": threads, "kind": "oracle",
             "sample": f"forward + adjoint solves of {systems} of {p.batch} system(s) of {p.name}"
-                      f"{cut} ({its} iterations, {t:.1f} s)"}
+                      f"{cut} ({its} iterations, {t:.1f} s)",
+            "single_core": {"value": its1 / t1, "unit": "PCG iterations/s", "cores": 1,
+                            "sample": f"forward + adjoint solves of {sys1} system(s) cut to "
+                                      f"{m1} iterations each way ({its1} iterations, "
+                                      f"{t1:.1f} s)"},
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -1,4 +1,5 @@
-"""Build libsla.so (every HIP source under csrc/) for gfx950 with hipcc.
+"""Build libsla.so (every HIP source under csrc/) and the benchmark's
+bandwidth-ceiling kernels libsla_probe.so (probe/) for gfx950 with hipcc.
 
     python -m differentiable_sparse_linear_amd.build
 """
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsla.so")
+PROBE_SRC = os.path.join(PKG, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libsla_probe.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops keeps the compiler from forming packed FP32 arithmetic.
@@ -55,5 +58,18 @@ def build(verbose: bool = False, out: str = LIB, defines=(), tmpdir: str = None)
     return out
 
 
+def build_probe(verbose: bool = False, out: str = PROBE_LIB) -> str:
+    """Compile and link the bandwidth-ceiling kernels."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc, *FLAGS, "-I", INCLUDE, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))

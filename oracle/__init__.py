@@ -116,6 +116,8 @@ def _configure(lib):
     D = ctypes.c_double
     I = ctypes.c_int
     lib.orc_num_threads.restype = I
+    lib.orc_set_num_threads.argtypes = [I]
+    lib.orc_set_num_threads.restype = None
     lib.orc_spmv.argtypes = [I64, P, P, P, P, P]
     lib.orc_spmv.restype = None
     lib.orc_dot.argtypes = [I64, P, P]
@@ -140,6 +142,12 @@ def _configure(lib):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS)."""
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on; the results do not
+    depend on it (every dot product is summed in one fixed order)."""
+    _load().orc_set_num_threads(int(n))
 
 
 def _p(a: Optional[np.ndarray]):

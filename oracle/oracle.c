@@ -50,6 +50,17 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Threads of the OpenMP loops from now on (for a timed serial run). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* y_i = sum over stored k of row i: val[k] * x[col[k]] */
 void orc_spmv(int64_t n, const int64_t *row_ptr, const int32_t *col,
               const double *val, const double *x, double *y)

@@ -39,6 +39,24 @@ def test_library_exports_every_declared_symbol(libpath):
     assert set(_declared()) == set(sla.EXPORTED_SYMBOLS)
 
 
+def test_probe_library_exports_its_header():
+    """The benchmark's ceiling kernels (libsla_probe.so) export every
+    function include/sla_probe.h declares."""
+    import differentiable_sparse_linear_amd.build as b
+    if not os.path.exists(b.PROBE_LIB):
+        b.build_probe()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sla_probe.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(sla_probe_[a-z_]+)\s*\(", text)))
+    assert names == ["sla_probe_blocks", "sla_probe_copy", "sla_probe_lds", "sla_probe_read",
+                     "sla_probe_write"]
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    assert all(hasattr(lib, f) for f in names)
+    # argument checks return before any launch
+    assert lib.sla_probe_read(None, 8, None, None) == -1
+    assert lib.sla_probe_copy(None, None, 8, None) == -1
+
+
 def test_status_strings_and_null_handle(libpath):
     import differentiable_sparse_linear_amd as sla
     lib = sla.load(libpath)
