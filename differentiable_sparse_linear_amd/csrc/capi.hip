@@ -629,16 +629,26 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
 }
 
 // Compact columns for the pattern (rp, col), longest row max_len, when
-// every entry fits.
+// every entry fits; rowidx (the row of every entry) serves patterns with
+// long rows, which are checked entry by entry.
 template <typename IT>
 hipError_t build_col16(sla_ctx *h, const IT *rp, const int32_t *col, int32_t max_len,
-                       int16_t **out, hipStream_t s) {
+                       const int32_t *rowidx, int16_t **out, hipStream_t s) {
     int32_t fits = 0;
-    hipError_t e = setup_col16<IT>(rp, col, h->n, h->nnz, max_len, nullptr, h->flag, &fits, s);
+    const int32_t *ri = setup_entrywise(max_len, h->nnz) ? rowidx : nullptr;
+    if (setup_entrywise(max_len, h->nnz) && !ri) return hipSuccess;  // no row index: keep int32
+    hipError_t e = setup_col16<IT>(rp, col, h->n, h->nnz, ri, nullptr, h->flag, &fits, s);
     if (e != hipSuccess || !fits) return e;
     if ((e = dmalloc(h, out, sizeof(int16_t) * h->nnz)) != hipSuccess) return e;
-    return setup_col16<IT>(rp, col, h->n, h->nnz, max_len, *out, h->flag, &fits, s);
+    return setup_col16<IT>(rp, col, h->n, h->nnz, ri, *out, h->flag, &fits, s);
 }
+
+// The set-up's temporaries: one allocation for the lifetime of sla_create.
+struct SetupMem {
+    void *base = nullptr;
+    SetupScratch scr;
+    ~SetupMem() { (void)hipFree(base); }
+};
 
 // Diagonal masks for the pattern (rp, col) when its entries lie on at most
 // kMaxDiags diagonals and no row holds more than 8 of them; fills `ca`.
@@ -760,13 +770,24 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     const IT *rp = reinterpret_cast<const IT *>(h->rp);
     HIP_TRY(dmalloc(h, &h->diagpos, sizeof(IT) * n));
     HIP_TRY(dmalloc(h, &h->flag, sizeof(int32_t)));
-    HIP_TRY(setup_validate<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->diagpos), h->flag, s));
     int32_t bad = 0;
-    HIP_TRY(hipMemcpyAsync(&bad, h->flag, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-    HIP_TRY(hipStreamSynchronize(s));
-    if (bad) return SLA_ERR_PATTERN;
+    HIP_TRY(setup_check_rowptr<IT>(rp, n, nnz, h->flag, &bad, s));
+    if (bad) return SLA_ERR_PATTERN;  // columns not read
     int32_t maxlen = 0;
     HIP_TRY(setup_max_row<IT>(rp, n, h->flag, &maxlen, s));
+    // the row of every entry serves the entry-by-entry checks of patterns
+    // with long rows and the transpose; one allocation holds it and the
+    // transpose's temporaries until the end of the set-up
+    const bool entrywise = setup_entrywise(maxlen, nnz);
+    SetupMem tmp;
+    if (entrywise || build_t) {
+        HIP_TRY(hipMalloc(&tmp.base, (size_t)setup_scratch_bytes(nnz, true, build_t)));
+        setup_scratch_carve(tmp.base, nnz, true, build_t, &tmp.scr);
+        HIP_TRY(setup_row_index<IT>(rp, n, nnz, tmp.scr.rowidx, tmp.scr.tot, s));
+    }
+    HIP_TRY(setup_check_cols<IT>(rp, h->col, n, nnz, entrywise ? tmp.scr.rowidx : nullptr,
+                                 reinterpret_cast<IT *>(h->diagpos), h->flag, &bad, s));
+    if (bad) return SLA_ERR_PATTERN;
     h->slots = slots_for(maxlen);
     h->max_len = maxlen;
     h->slots_t = h->slots;
@@ -777,7 +798,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
         HIP_TRY(dmalloc(h, &h->perm, sizeof(int32_t) * nnz));
         HIP_TRY(dmalloc(h, &h->val_t, sizeof(T) * nnz));
         HIP_TRY(setup_transpose<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->rp_t), h->col_t,
-                                    h->perm, s));
+                                    h->perm, tmp.scr, s));
         h->has_t = true;
         HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
         h->slots_t = slots_for(maxlen);
@@ -786,7 +807,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
                                    h->slots_t, h->plan_t, s)));
         if (compact) {
             const IT *rpt = reinterpret_cast<const IT *>(h->rp_t);
-            HIP_TRY(build_col16<IT>(h, rpt, h->col_t, maxlen, &h->col16_t, s));
+            HIP_TRY(build_col16<IT>(h, rpt, h->col_t, maxlen, tmp.scr.rowidx_t, &h->col16_t, s));
             h->ca_t.col16 = h->col16_t;
             if (h->col16_t) h->ca_t.mode = kColTile16;
             HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));
@@ -796,7 +817,7 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     }
     h->ca.col = h->col;
     if (compact) {
-        HIP_TRY(build_col16<IT>(h, rp, h->col, h->max_len, &h->col16, s));
+        HIP_TRY(build_col16<IT>(h, rp, h->col, h->max_len, tmp.scr.rowidx, &h->col16, s));
         h->ca.col16 = h->col16;
         if (h->col16) h->ca.mode = kColTile16;
         if (!h->dlt) HIP_TRY(dmalloc(h, &h->dlt, sizeof(int32_t) * 2 * kMaxDiags));

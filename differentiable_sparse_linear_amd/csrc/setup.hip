@@ -5,17 +5,34 @@
 // kept in diagpos for the Jacobi preconditioner -- the native backend's only
 // preconditioner per the torch-sla explainer's Significance section).
 //
+// Row of every entry (rowidx): each row that holds entries marks its first
+// entry with its index, and an inclusive max-scan carries every mark over
+// the row's other entries.
+//
 // Transpose map (needed by the adjoint solve with A^T, Methodology section 2,
-// linear systems): a stable LSD radix sort of (col[k], k) by column gives
-// perm[kt] = k in column-major order with rows ascending inside each column,
-// so row kt of A^T is sorted; col_t[kt] = row(perm[kt]); row_ptr_t[c] is the
-// first kt whose key is >= c, found from the sorted keys without atomics.
+// linear systems): a stable least-significant-digit radix sort of the pairs
+// (col[k], k) by column, eight bits per pass.  Each pass counts the digits
+// of every tile of entries (a histogram in LDS), turns the counts, ordered
+// digit by digit and tile by tile, into starting positions by an exclusive
+// scan, and scatters each tile's entries in their original order: within a
+// round of 256 entries each wavefront finds the lanes that share a lane's
+// digit with eight ballots, one per digit bit, and takes the lane's rank
+// among them; counters in LDS carry the ranks over the wavefronts and the
+// rounds.  Entries of equal digit therefore keep their order, so after the
+// last pass perm[kt] = k lists the entries column by column with rows
+// ascending inside each column, and row kt of A^T is sorted; col_t[kt] =
+// row(perm[kt]); row_ptr_t[c] is the first kt whose key is >= c, found from
+// the sorted keys.  The scans are a reduce-then-scan over tiles: per-tile
+// totals, one workgroup scanning the totals, then each tile scanned with
+// its carry.
 //
 // Per-row loops over a row's entries serialise on long rows (a graph hub
 // of half a million entries), so patterns whose longest row exceeds
 // kShortRow are checked entry by entry from the row of every entry.
-#include <hipcub/hipcub.hpp>
-
+//
+// Temporaries (the row of every entry, the sort's keys and values, digit
+// counts, scan totals) live in one allocation that sla_create makes for the
+// set-up and releases at its end (SetupScratch).
 #include "sla_internal.h"
 
 namespace sla {
@@ -98,28 +115,31 @@ __global__ __launch_bounds__(kBlock) void check_diag_kernel(const IT *__restrict
     raise_flag(bad, flag);
 }
 
-__global__ __launch_bounds__(kBlock) void iota_kernel(int32_t *a, int64_t m) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride)
-        a[k] = (int32_t)k;
-}
-
+// col_t[k] = the row of A entry perm[k] (-1 for a position outside [0, m),
+// which only a faulty sort could leave, so that it shows in the map instead
+// of reading out of bounds)
 __global__ __launch_bounds__(kBlock) void col_t_kernel(const int32_t *__restrict__ perm,
                                                        const int32_t *__restrict__ rowidx,
                                                        int32_t *__restrict__ col_t, int64_t m) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride)
-        col_t[k] = rowidx[perm[k]];
+    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride) {
+        const int64_t j = perm[k];
+        col_t[k] = j >= 0 && j < m ? rowidx[j] : -1;
+    }
 }
 
-// rp_t[c] = first position whose sorted key is >= c, for c in [0, n]
+// rp_t[c] = first position whose sorted key is >= c, for c in [0, n] (keys
+// are columns, in [0, n); the loop bounds are clamped to that range all the
+// same)
 template <typename IT>
 __global__ __launch_bounds__(kBlock) void rowptr_t_kernel(const int32_t *__restrict__ keys,
                                                           int64_t m, int64_t n, IT *__restrict__ rp_t) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k <= m; k += stride) {
-        const int64_t lo = (k == 0) ? -1 : (int64_t)keys[k - 1];
-        const int64_t hi = (k == m) ? n : (int64_t)keys[k];
+        int64_t lo = (k == 0) ? -1 : (int64_t)keys[k - 1];
+        int64_t hi = (k == m) ? n : (int64_t)keys[k];
+        lo = lo < -1 ? -1 : lo;
+        hi = hi > n ? n : hi;
         for (int64_t c = lo + 1; c <= hi; ++c) rp_t[c] = (IT)k;
     }
 }
@@ -241,6 +261,7 @@ __global__ __launch_bounds__(kBlock) void diag_mask_kernel(const IT *__restrict_
     }
 }
 
+
 static unsigned blocks_for(int64_t m) {
     int64_t b = (m + kBlock - 1) / kBlock;
     if (b > 65536) b = 65536;
@@ -248,65 +269,324 @@ static unsigned blocks_for(int64_t m) {
     return (unsigned)b;
 }
 
-// rowidx[k] = the row of entry k, for a valid row_ptr (synchronizes the
-// stream; temporary scan storage).
-template <typename IT>
-hipError_t setup_row_index(const IT *rp, int64_t n, int64_t nnz, int32_t *rowidx, hipStream_t s) {
-    hipError_t e = hipMemsetAsync(rowidx, 0, sizeof(int32_t) * nnz, s);
-    if (e != hipSuccess) return e;
-    row_start_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    size_t tb = 0;
-    if ((e = hipcub::DeviceScan::InclusiveScan(nullptr, tb, rowidx, hipcub::Max(), nnz, s)) !=
-        hipSuccess)
-        return e;
-    void *temp = nullptr;
-    if ((e = hipMalloc(&temp, tb > 0 ? tb : 1)) != hipSuccess) return e;
-    e = hipcub::DeviceScan::InclusiveScan(temp, tb, rowidx, hipcub::Max(), nnz, s);
-    const hipError_t es = hipStreamSynchronize(s);
-    (void)hipFree(temp);
-    return e != hipSuccess ? e : es;
+// ------------------------------------------------------------------ scans
+//
+// Reduce-then-scan of int32 values over tiles of kScanTile, with the sum
+// (MAX = false) or the maximum (MAX = true); every value is >= 0, so 0 is
+// the identity of both.  A tile is loaded coalesced (element j * kBlock + t
+// by thread t) into LDS and read back blocked (thread t owns the kScanItems
+// consecutive elements t * kScanItems ...; a padding word after every 16
+// keeps those reads off a single bank), scanned in registers and across the
+// block, and written back the same way.
+constexpr int kScanItems = 16;
+constexpr int kScanTile = kBlock * kScanItems;
+constexpr int kScanLds = kScanTile + kScanTile / 16;
+
+template <bool MAX>
+__device__ __forceinline__ int32_t scan_op(int32_t a, int32_t b) {
+    return MAX ? (a > b ? a : b) : a + b;
 }
+
+__device__ __forceinline__ int lds_pad(int e) { return e + (e >> 4); }
+
+// Exclusive scan over the block of one value per thread (identity 0);
+// *total gets the block's aggregate.  Every thread gets the same total.
+template <bool MAX>
+__device__ __forceinline__ int32_t block_exclusive(int32_t v, int32_t *total) {
+    __shared__ int32_t wsum[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t u = __shfl_up(inc, off, 64);
+        if (lane >= off) inc = scan_op<MAX>(inc, u);
+    }
+    int32_t exc = __shfl_up(inc, 1, 64);
+    if (lane == 0) exc = 0;
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int32_t carry = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) carry = scan_op<MAX>(carry, wsum[w]);
+        all = scan_op<MAX>(all, wsum[w]);
+    }
+    __syncthreads();  // wsum is reused by the next call
+    *total = all;
+    return scan_op<MAX>(carry, exc);
+}
+
+// Tile b of in[0..m), blocked: thread t gets elements t * kScanItems + j
+// (0 past the end).
+__device__ __forceinline__ void tile_load(const int32_t *__restrict__ in, int64_t m,
+                                          int32_t *sh, int32_t (&v)[kScanItems]) {
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        const int e = j * kBlock + threadIdx.x;
+        sh[lds_pad(e)] = base + e < m ? in[base + e] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) v[j] = sh[lds_pad(threadIdx.x * kScanItems + j)];
+    __syncthreads();
+}
+
+// tot[b] = the aggregate of tile b.
+template <bool MAX>
+__global__ __launch_bounds__(kBlock) void tile_total_kernel(const int32_t *__restrict__ in,
+                                                            int64_t m, int32_t *__restrict__ tot) {
+    __shared__ int32_t sh[kScanLds];
+    int32_t v[kScanItems];
+    tile_load(in, m, sh, v);
+    int32_t a = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) a = scan_op<MAX>(a, v[j]);
+    int32_t all;
+    block_exclusive<MAX>(a, &all);
+    if (threadIdx.x == 0) tot[blockIdx.x] = all;
+}
+
+// tot[0..nt) becomes its exclusive scan: one workgroup, kBlock at a time.
+template <bool MAX>
+__global__ __launch_bounds__(kBlock) void totals_scan_kernel(int32_t *__restrict__ tot,
+                                                             int64_t nt) {
+    int32_t carry = 0;
+    for (int64_t c = 0; c < nt; c += kBlock) {
+        const int64_t i = c + threadIdx.x;
+        const int32_t v = i < nt ? tot[i] : 0;
+        int32_t all;
+        const int32_t exc = block_exclusive<MAX>(v, &all);
+        if (i < nt) tot[i] = scan_op<MAX>(carry, exc);
+        carry = scan_op<MAX>(carry, all);
+    }
+}
+
+// out = the inclusive (EXCL = false) or exclusive scan of in, tile b
+// starting from the exclusive scan of the tile totals, carry[b].  in and
+// out may be the same array (each tile is read before it is written).
+template <bool MAX, bool EXCL>
+__global__ __launch_bounds__(kBlock) void tile_scan_kernel(const int32_t *in, int64_t m,
+                                                           const int32_t *__restrict__ carry,
+                                                           int32_t *out) {
+    __shared__ int32_t sh[kScanLds];
+    int32_t v[kScanItems];
+    tile_load(in, m, sh, v);
+    int32_t a = 0;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) a = scan_op<MAX>(a, v[j]);
+    int32_t all;
+    int32_t run = scan_op<MAX>(carry[blockIdx.x], block_exclusive<MAX>(a, &all));
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        const int32_t nx = scan_op<MAX>(run, v[j]);
+        sh[lds_pad(threadIdx.x * kScanItems + j)] = EXCL ? run : nx;
+        run = nx;
+    }
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+        const int e = j * kBlock + threadIdx.x;
+        if (base + e < m) out[base + e] = sh[lds_pad(e)];
+    }
+}
+
+inline int64_t scan_tiles(int64_t m) { return (m + kScanTile - 1) / kScanTile; }
+
+// data[0..m) becomes its scan in place; tot holds scan_tiles(m) values.
+template <bool MAX, bool EXCL>
+hipError_t scan_inplace(int32_t *data, int64_t m, int32_t *tot, hipStream_t s) {
+    const int64_t nt = scan_tiles(m);
+    if (nt < 1) return hipSuccess;
+    tile_total_kernel<MAX><<<(unsigned)nt, kBlock, 0, s>>>(data, m, tot);
+    totals_scan_kernel<MAX><<<1, kBlock, 0, s>>>(tot, nt);
+    tile_scan_kernel<MAX, EXCL><<<(unsigned)nt, kBlock, 0, s>>>(data, m, tot, data);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ radix sort
+//
+// One pass sorts (key, value) pairs stably by the eight bits of the key at
+// `shift`.  Tile b is entries [b * kSortTile, (b + 1) * kSortTile), taken in
+// kSortRounds rounds of kBlock consecutive entries, wavefront w holding
+// entries [r * kBlock + 64 w, r * kBlock + 64 w + 64) of round r.
+constexpr int kSortRounds = 16;
+constexpr int kSortTile = kBlock * kSortRounds;
+constexpr int kRadix = 256;
+static_assert(kBlock == kRadix, "one thread per digit in the sort's bookkeeping");
+
+inline int64_t sort_tiles(int64_t m) { return (m + kSortTile - 1) / kSortTile; }
+
+__device__ __forceinline__ int32_t sort_value(const int32_t *vin, int64_t e) {
+    return vin ? vin[e] : (int32_t)e;  // the first pass's value is the entry's index
+}
+
+// hist[d * ntiles + b] = entries of tile b whose digit is d.
+__global__ __launch_bounds__(kBlock) void digit_count_kernel(const int32_t *__restrict__ key,
+                                                             int64_t m, int shift,
+                                                             int32_t *__restrict__ hist) {
+    __shared__ int32_t h[kRadix];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int64_t e = base + r * kBlock + threadIdx.x;
+        if (e < m) atomicAdd(&h[(key[e] >> shift) & (kRadix - 1)], 1);
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter of tile b: start[d * ntiles + b] is the position of the
+// tile's first entry of digit d (the exclusive scan of hist).
+__global__ __launch_bounds__(kBlock) void digit_scatter_kernel(
+    const int32_t *__restrict__ kin, const int32_t *__restrict__ vin, int64_t m, int shift,
+    const int32_t *__restrict__ start, int32_t *__restrict__ kout, int32_t *__restrict__ vout) {
+    __shared__ int32_t pos0[kRadix];          // next position of digit d in this tile
+    __shared__ int32_t cnt[kWaves][kRadix];   // this round's count of digit d per wavefront
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    pos0[tid] = start[(int64_t)tid * gridDim.x + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) cnt[w][tid] = 0;
+    __syncthreads();
+    const uint64_t below = __lanemask_lt();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int64_t e = base + r * kBlock + tid;
+        const bool act = e < m;
+        const int32_t k = act ? kin[e] : 0;
+        const int32_t v = act ? sort_value(vin, e) : 0;
+        const int d = (k >> shift) & (kRadix - 1);
+        // the lanes holding the same digit: agree on all eight bits
+        uint64_t peers = __ballot(act);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool one = (d >> bit) & 1;
+            const uint64_t b1 = __ballot(act && one);
+            peers &= one ? b1 : ~b1;
+        }
+        const int rank = __popcll(peers & below);
+        if (act && rank == 0) cnt[wave][d] = __popcll(peers);
+        __syncthreads();
+        if (act) {
+            int32_t p = pos0[d] + rank;
+            for (int w = 0; w < wave; ++w) p += cnt[w][d];
+            if (p >= 0 && p < m) {
+                kout[p] = k;
+                vout[p] = v;
+            }
+        }
+        __syncthreads();
+        int32_t add = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            add += cnt[w][tid];
+            cnt[w][tid] = 0;
+        }
+        pos0[tid] += add;
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ scratch
+
+int64_t setup_scratch_bytes(int64_t nnz, bool rowidx, bool transpose) {
+    auto al = [](int64_t b) { return (b + 255) / 256 * 256; };
+    int64_t b = 0;
+    int64_t scan_len = 0;
+    if (rowidx || transpose) {
+        b += al(4 * nnz);  // rowidx
+        scan_len = nnz;
+    }
+    if (transpose) {
+        const int64_t hist = (int64_t)kRadix * sort_tiles(nnz);
+        b += 3 * al(4 * nnz) + al(4 * hist);  // keys x 2, values, digit counts
+        scan_len = scan_len > hist ? scan_len : hist;
+    }
+    if (scan_len) b += al(4 * (scan_tiles(scan_len) + 1));
+    return b;
+}
+
+void setup_scratch_carve(void *base, int64_t nnz, bool rowidx, bool transpose,
+                         SetupScratch *out) {
+    auto al = [](int64_t b) { return (b + 255) / 256 * 256; };
+    *out = SetupScratch();
+    char *p = static_cast<char *>(base);
+    int64_t scan_len = 0;
+    if (rowidx || transpose) {
+        out->rowidx = reinterpret_cast<int32_t *>(p);
+        p += al(4 * nnz);
+        scan_len = nnz;
+    }
+    if (transpose) {
+        const int64_t hist = (int64_t)kRadix * sort_tiles(nnz);
+        out->keys[0] = reinterpret_cast<int32_t *>(p);
+        p += al(4 * nnz);
+        out->keys[1] = reinterpret_cast<int32_t *>(p);
+        p += al(4 * nnz);
+        out->vals = reinterpret_cast<int32_t *>(p);
+        p += al(4 * nnz);
+        out->hist = reinterpret_cast<int32_t *>(p);
+        p += al(4 * hist);
+        scan_len = scan_len > hist ? scan_len : hist;
+    }
+    if (scan_len) out->tot = reinterpret_cast<int32_t *>(p);
+}
+
+// ------------------------------------------------------------------ set-up steps
 
 // Whether a pattern is checked entry by entry: a row past kShortRow and
 // fewer than 2^31 entries (the row of every entry, 4 bytes each, held
 // while checking).
-inline bool entrywise(int32_t max_len, int64_t nnz) {
+bool setup_entrywise(int32_t max_len, int64_t nnz) {
     return max_len > kShortRow && nnz < ((int64_t)1 << 31);
 }
 
 template <typename IT>
-hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
-                          int32_t *flag, hipStream_t s) {
-    int32_t h = 0;
+hipError_t setup_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag, int32_t *bad,
+                              hipStream_t s) {
     hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
     check_rowptr_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, nnz, flag);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = hipMemcpyAsync(&h, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+    if ((e = hipMemcpyAsync(bad, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
-    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
-    if (h) return hipSuccess;  // flag stays set: row_ptr invalid, columns not read
-    int32_t max_len = 0;
-    if ((e = setup_max_row<IT>(rp, n, flag, &max_len, s)) != hipSuccess) return e;
-    if ((e = hipMemsetAsync(flag, 0, sizeof(int32_t), s)) != hipSuccess) return e;
-    if (!entrywise(max_len, nnz)) {
+    return hipStreamSynchronize(s);
+}
+
+// rowidx[k] = the row of entry k, for a valid row_ptr (tot: scan totals).
+template <typename IT>
+hipError_t setup_row_index(const IT *rp, int64_t n, int64_t nnz, int32_t *rowidx, int32_t *tot,
+                           hipStream_t s) {
+    hipError_t e = hipMemsetAsync(rowidx, 0, sizeof(int32_t) * nnz, s);
+    if (e != hipSuccess) return e;
+    row_start_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return scan_inplace<true, false>(rowidx, nnz, tot, s);
+}
+
+// Columns and diagonals of a pattern whose row pointers passed the check
+// (synchronizes the stream): per row, or entry by entry from rowidx (not
+// null) for patterns with long rows.
+template <typename IT>
+hipError_t setup_check_cols(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
+                            const int32_t *rowidx, IT *diagpos, int32_t *flag, int32_t *bad,
+                            hipStream_t s) {
+    hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
+    if (e != hipSuccess) return e;
+    if (!rowidx) {
         check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
-        return hipGetLastError();
-    }
-    int32_t *rowidx = nullptr;
-    if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) return e;
-    do {
-        if ((e = setup_row_index<IT>(rp, n, nnz, rowidx, s)) != hipSuccess) break;
-        if ((e = hipMemsetAsync(diagpos, 0xff, sizeof(IT) * n, s)) != hipSuccess) break;
+    } else {
+        if ((e = hipMemsetAsync(diagpos, 0xff, sizeof(IT) * n, s)) != hipSuccess) return e;
         check_cols_entries_kernel<IT>
             <<<blocks_for(nnz), kBlock, 0, s>>>(rp, col, rowidx, n, nnz, diagpos, flag);
         check_diag_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(diagpos, n, flag);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        e = hipStreamSynchronize(s);  // rowidx is freed next
-    } while (0);
-    (void)hipFree(rowidx);
-    return e;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(bad, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
+        return e;
+    return hipStreamSynchronize(s);
 }
 
 // Longest row of a valid pattern (synchronizes the stream).
@@ -366,27 +646,16 @@ hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const i
 }
 
 template <typename IT>
-hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, int32_t max_len,
-                       int16_t *out, int32_t *scratch, int32_t *fits, hipStream_t s) {
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
+                       const int32_t *rowidx, int16_t *out, int32_t *scratch, int32_t *fits,
+                       hipStream_t s) {
     hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
-    if (!entrywise(max_len, nnz)) {
+    if (!rowidx)
         col16_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, out, scratch);
-        e = hipGetLastError();
-    } else {
-        int32_t *rowidx = nullptr;
-        if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) return e;
-        e = setup_row_index<IT>(rp, n, nnz, rowidx, s);
-        if (e == hipSuccess) {
-            col16_entries_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(col, rowidx, nnz, out,
-                                                                    scratch);
-            e = hipGetLastError();
-            const hipError_t es = hipStreamSynchronize(s);  // rowidx is freed next
-            if (e == hipSuccess) e = es;
-        }
-        (void)hipFree(rowidx);
-    }
-    if (e != hipSuccess) return e;
+    else
+        col16_entries_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(col, rowidx, nnz, out, scratch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t bad = 1;
     if ((e = hipMemcpyAsync(&bad, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
@@ -397,38 +666,36 @@ hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
 
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
-                           int32_t *col_t, int32_t *perm, hipStream_t s) {
-    int32_t *keys_out = nullptr, *vals_in = nullptr, *rowidx = nullptr;
-    void *temp = nullptr;
-    size_t temp_bytes = 0;
-    int end_bit = 1;
-    while (end_bit < 32 && ((int64_t)1 << end_bit) < n) ++end_bit;
-    const int m = (int)nnz;
+                           int32_t *col_t, int32_t *perm, SetupScratch &scr, hipStream_t s) {
+    (void)rp;
+    int bits = 1;
+    while (bits < 31 && ((int64_t)1 << bits) < n) ++bits;
+    const int passes = (bits + 7) / 8;
+    const int64_t nt = sort_tiles(nnz);
+    const int64_t nh = (int64_t)kRadix * nt;
     hipError_t e = hipSuccess;
-    do {
-        if ((e = hipMalloc(&keys_out, sizeof(int32_t) * nnz)) != hipSuccess) break;
-        if ((e = hipMalloc(&vals_in, sizeof(int32_t) * nnz)) != hipSuccess) break;
-        if ((e = hipMalloc(&rowidx, sizeof(int32_t) * nnz)) != hipSuccess) break;
-        iota_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(vals_in, nnz);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        if ((e = setup_row_index<IT>(rp, n, nnz, rowidx, s)) != hipSuccess) break;
-        e = hipcub::DeviceRadixSort::SortPairs(nullptr, temp_bytes, col, keys_out, vals_in, perm,
-                                               m, 0, end_bit, s);
-        if (e != hipSuccess) break;
-        if ((e = hipMalloc(&temp, temp_bytes > 0 ? temp_bytes : 1)) != hipSuccess) break;
-        e = hipcub::DeviceRadixSort::SortPairs(temp, temp_bytes, col, keys_out, vals_in, perm, m,
-                                               0, end_bit, s);
-        if (e != hipSuccess) break;
-        col_t_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(perm, rowidx, col_t, nnz);
-        rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kBlock, 0, s>>>(keys_out, nnz, n, rp_t);
-        if ((e = hipGetLastError()) != hipSuccess) break;
-        e = hipStreamSynchronize(s);
-    } while (0);
-    (void)hipFree(keys_out);
-    (void)hipFree(vals_in);
-    (void)hipFree(rowidx);
-    (void)hipFree(temp);
-    return e;
+    // pass i reads what pass i - 1 wrote; the last pass writes its keys to
+    // keys[1] and its values to perm
+    const int32_t *kin = col, *vin = nullptr;
+    for (int i = 0; i < passes; ++i) {
+        const bool last = ((passes - 1 - i) & 1) == 0;
+        int32_t *kout = last ? scr.keys[1] : scr.keys[0];
+        int32_t *vout = last ? perm : scr.vals;
+        digit_count_kernel<<<(unsigned)nt, kBlock, 0, s>>>(kin, nnz, 8 * i, scr.hist);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = scan_inplace<false, true>(scr.hist, nh, scr.tot, s)) != hipSuccess) return e;
+        digit_scatter_kernel<<<(unsigned)nt, kBlock, 0, s>>>(kin, vin, nnz, 8 * i, scr.hist,
+                                                            kout, vout);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        kin = kout;
+        vin = vout;
+    }
+    // keys[1] holds the sorted columns: the row of every entry of A^T
+    scr.rowidx_t = scr.keys[1];
+    rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kBlock, 0, s>>>(scr.rowidx_t, nnz, n, rp_t);
+    col_t_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(perm, scr.rowidx, col_t, nnz);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipStreamSynchronize(s);
 }
 
 // Launchers of the single checks, for callers that keep their own flags
@@ -455,39 +722,34 @@ hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s) 
     return hipGetLastError();
 }
 
-#define SLA_CHECK_INST(IT)                                                                     \
+#define SLA_SETUP_INST(IT)                                                                     \
     template hipError_t launch_check_rowptr<IT>(const IT *, int64_t, int64_t, int32_t *,       \
                                                 hipStream_t);                                  \
     template hipError_t launch_check_cols_rows<IT>(const IT *, const int32_t *, int64_t, IT *, \
                                                    int32_t *, hipStream_t);                    \
-    template hipError_t launch_max_row<IT>(const IT *, int64_t, int32_t *, hipStream_t);
-SLA_CHECK_INST(int32_t)
-SLA_CHECK_INST(int64_t)
-#undef SLA_CHECK_INST
-
-template hipError_t setup_validate<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
-                                            int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_validate<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
-                                            int64_t *, int32_t *, hipStream_t);
-template hipError_t setup_diag<int32_t>(const int32_t *, const int32_t *, int64_t, int32_t *,
-                                        int32_t *, int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_diag<int64_t>(const int64_t *, const int32_t *, int64_t, int32_t *,
-                                        int32_t *, int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_diag_masks<int32_t>(const int32_t *, const int32_t *, int64_t,
-                                              const int32_t *, int32_t, uint16_t *, hipStream_t);
-template hipError_t setup_diag_masks<int64_t>(const int64_t *, const int32_t *, int64_t,
-                                              const int32_t *, int32_t, uint16_t *, hipStream_t);
-template hipError_t setup_col16<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
-                                         int32_t, int16_t *, int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_col16<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
-                                         int32_t, int16_t *, int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_max_row<int32_t>(const int32_t *, int64_t, int32_t *, int32_t *,
-                                           hipStream_t);
-template hipError_t setup_max_row<int64_t>(const int64_t *, int64_t, int32_t *, int32_t *,
-                                           hipStream_t);
-template hipError_t setup_transpose<int32_t>(const int32_t *, const int32_t *, int64_t, int64_t,
-                                             int32_t *, int32_t *, int32_t *, hipStream_t);
-template hipError_t setup_transpose<int64_t>(const int64_t *, const int32_t *, int64_t, int64_t,
-                                             int64_t *, int32_t *, int32_t *, hipStream_t);
+    template hipError_t launch_max_row<IT>(const IT *, int64_t, int32_t *, hipStream_t);      \
+    template hipError_t setup_check_rowptr<IT>(const IT *, int64_t, int64_t, int32_t *,        \
+                                               int32_t *, hipStream_t);                        \
+    template hipError_t setup_row_index<IT>(const IT *, int64_t, int64_t, int32_t *,           \
+                                            int32_t *, hipStream_t);                           \
+    template hipError_t setup_check_cols<IT>(const IT *, const int32_t *, int64_t, int64_t,    \
+                                             const int32_t *, IT *, int32_t *, int32_t *,      \
+                                             hipStream_t);                                     \
+    template hipError_t setup_max_row<IT>(const IT *, int64_t, int32_t *, int32_t *,           \
+                                          hipStream_t);                                        \
+    template hipError_t setup_diag<IT>(const IT *, const int32_t *, int64_t, int32_t *,        \
+                                       int32_t *, int32_t *, int32_t *, hipStream_t);          \
+    template hipError_t setup_diag_masks<IT>(const IT *, const int32_t *, int64_t,             \
+                                             const int32_t *, int32_t, uint16_t *,             \
+                                             hipStream_t);                                     \
+    template hipError_t setup_col16<IT>(const IT *, const int32_t *, int64_t, int64_t,         \
+                                        const int32_t *, int16_t *, int32_t *, int32_t *,      \
+                                        hipStream_t);                                          \
+    template hipError_t setup_transpose<IT>(const IT *, const int32_t *, int64_t, int64_t,     \
+                                            IT *, int32_t *, int32_t *, SetupScratch &,        \
+                                            hipStream_t);
+SLA_SETUP_INST(int32_t)
+SLA_SETUP_INST(int64_t)
+#undef SLA_SETUP_INST
 
 }  // namespace sla

@@ -514,9 +514,39 @@ hipError_t launch_eig_outer(const IT *rp, const int32_t *col, const T *X, int k,
                             T *grad, int64_t n, hipStream_t s);
 
 // pattern setup
+
+// Temporaries of the set-up, carved from one allocation that sla_create
+// makes and releases (setup_scratch_bytes / setup_scratch_carve): the row
+// of every entry, the transpose sort's keys (two buffers) and values, its
+// digit counts, and the scans' tile totals.
+struct SetupScratch {
+    int32_t *rowidx = nullptr;    // [nnz] row of every entry of A
+    int32_t *keys[2] = {nullptr, nullptr};
+    int32_t *vals = nullptr;
+    int32_t *hist = nullptr;
+    int32_t *tot = nullptr;
+    int32_t *rowidx_t = nullptr;  // after setup_transpose: row of every entry of A^T
+};
+int64_t setup_scratch_bytes(int64_t nnz, bool rowidx, bool transpose);
+void setup_scratch_carve(void *base, int64_t nnz, bool rowidx, bool transpose, SetupScratch *out);
+// whether a pattern is checked entry by entry (a row longer than kShortRow)
+bool setup_entrywise(int32_t max_len, int64_t nnz);
+
+// *bad = 1 when row_ptr is not a valid CSR row pointer (synchronizes `s`)
 template <typename IT>
-hipError_t setup_validate(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *diagpos,
-                          int32_t *flag, hipStream_t s);
+hipError_t setup_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag, int32_t *bad,
+                              hipStream_t s);
+// rowidx[k] = row of entry k (a valid row_ptr; tot: scan totals)
+template <typename IT>
+hipError_t setup_row_index(const IT *rp, int64_t n, int64_t nnz, int32_t *rowidx, int32_t *tot,
+                           hipStream_t s);
+// *bad = 1 for a column out of range or out of order or a missing diagonal;
+// diagpos[i] = position of A_ii.  rowidx: null (per-row checks) or the row
+// of every entry (entry by entry).  Synchronizes `s`.
+template <typename IT>
+hipError_t setup_check_cols(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
+                            const int32_t *rowidx, IT *diagpos, int32_t *flag, int32_t *bad,
+                            hipStream_t s);
 template <typename IT>
 hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out, hipStream_t s);
 // Diagonal masks: the distinct column offsets (col - row) of the pattern
@@ -531,16 +561,17 @@ hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const i
                             int32_t ndiag, uint16_t *msk, hipStream_t s);
 // Compact columns: out[k] = col[k] - (first row of row(k)'s tile) as int16.
 // With out == nullptr only checks; *fits = 1 when every entry fits
-// (synchronizes `s`).
+// (synchronizes `s`).  rowidx: null (per row) or the row of every entry.
 template <typename IT>
-hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, int32_t max_len,
-                       int16_t *out, int32_t *scratch, int32_t *fits, hipStream_t s);
-// The single checks behind setup_validate and setup_max_row, for callers
-// that keep their own flags: *flag is raised (row pointers not monotone or
-// not ending at nnz; a column out of range or out of order, or no diagonal),
-// *out is atomically maxed with the longest row; both must start at 0.  The
-// column check walks each row in one thread (meant for rows of modest
-// length) and writes diagpos.  Nothing is allocated or synchronized.
+hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
+                       const int32_t *rowidx, int16_t *out, int32_t *scratch, int32_t *fits,
+                       hipStream_t s);
+// The single checks behind the set-up steps, for callers that keep their
+// own flags: *flag is raised (row pointers not monotone or not ending at
+// nnz; a column out of range or out of order, or no diagonal), *out is
+// atomically maxed with the longest row; both must start at 0.  The column
+// check walks each row in one thread (meant for rows of modest length) and
+// writes diagpos.  Nothing is allocated or synchronized.
 template <typename IT>
 hipError_t launch_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag,
                                hipStream_t s);
@@ -549,8 +580,12 @@ hipError_t launch_check_cols_rows(const IT *rp, const int32_t *col, int64_t n, I
                                   int32_t *flag, hipStream_t s);
 template <typename IT>
 hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s);
+// The transpose map of a valid pattern whose row index is in scr.rowidx:
+// rp_t [n+1], col_t [nnz] (row of each A^T entry), perm [nnz] (A's position
+// of each A^T entry); scr.rowidx_t is left pointing at the row of every A^T
+// entry.  Synchronizes `s`.
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
-                           int32_t *col_t, int32_t *perm, hipStream_t s);
+                           int32_t *col_t, int32_t *perm, SetupScratch &scr, hipStream_t s);
 
 }  // namespace sla

@@ -20,16 +20,45 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------------ set-up
 
-@pytest.mark.parametrize("case", ["convdiff_64", "random_nonsym_300", "powerlaw_5000", "poisson_i64"])
+# The transpose map comes from a radix sort of (column, entry) pairs, eight
+# bits per pass: n = 36 takes one pass, 300 / 4096 / 5000 / 64 000 two,
+# 2^18 three.  Columns of a tile of 4096 entries spread over many digits
+# (random, power-law) or few (stencils).
+def _random_pattern(n, k, seed):
+    """Each row: its diagonal and k columns drawn uniformly (repeats merged)."""
+    rng = np.random.default_rng(seed)
+    c = np.concatenate([rng.integers(0, n, size=(n, k)), np.arange(n)[:, None]], axis=1)
+    c.sort(axis=1)
+    keep = np.ones(c.shape, dtype=bool)
+    keep[:, 1:] = c[:, 1:] != c[:, :-1]
+    rp = np.zeros(n + 1, dtype=np.int32)
+    rp[1:] = np.cumsum(keep.sum(axis=1))
+    return rp, c[keep].astype(np.int32)
+
+
+SETUP_CASES = ["laplace_6", "convdiff_64", "random_nonsym_300", "powerlaw_5000", "poisson_i64",
+               "diffusion3d_40", "random_nonsym_70000", "powerlaw_2^18"]
+
+
+@pytest.mark.parametrize("case", SETUP_CASES)
 def test_pattern_setup_bit_exact(hip, case):
     banner(f"setup {case}")
-    if case == "convdiff_64":
+    if case == "laplace_6":
+        rp, col, _ = W.laplacian_2d(6)
+    elif case == "convdiff_64":
         p = W.config(4, size=64)
         rp, col = p.row_ptr, p.col
     elif case == "random_nonsym_300":
         rp, col, _ = W.random_csr(300, 0.05, 3)
+    elif case == "random_nonsym_70000":
+        rp, col = _random_pattern(70000, 6, 5)
     elif case == "powerlaw_5000":
         rp, col, _ = W.powerlaw_graph_laplacian(5000, 4)
+    elif case == "powerlaw_2^18":
+        rp, col, _ = W.powerlaw_graph_laplacian(1 << 18, 6)
+    elif case == "diffusion3d_40":
+        p = W.config(2, size=40)
+        rp, col = p.row_ptr, p.col
     else:
         p = W.config(5, size=9)
         rp, col = p.row_ptr, p.col

@@ -17,12 +17,16 @@ The oracle cannot redo 500-iteration solves of this size inside a test, so:
     equals the oracle's recomputation of ||b - A x|| / ||b||;
   * the gradient on the pattern at sampled entries equals -lambda_i x_j
     exactly (one rounding on both sides), and grad_b equals lambda;
+  * the transpose map (built by a radix sort in four passes at this size):
+    A^T = A structurally, so perm is an involution with col[perm[k]] =
+    row(k), checked on every entry;
   * the homogeneity identity (oracle pin P14) over the whole gradient: for
     the capped solve sum_k gv_k v_k + sum_i gb_i b_i = lambda . (b - A x),
     with b - A x from the oracle's product of the GPU's x.
 """
 import json
 import os
+import time
 
 import numpy as np
 import pytest
@@ -104,6 +108,34 @@ def test_config5_cut_forward_and_adjoint_match_oracle_iterates(big, hip):
     got = gv[0, torch.from_numpy(ent).cuda()].cpu().numpy()
     assert np.array_equal(got, want)
     assert relerr(got, a.grad_values[0][ent]) <= 1e-10
+
+
+@pytest.mark.timeout(900)
+def test_config5_transpose_map_properties(big, hip):
+    """The transpose map of the 512^3 pattern (9.38e8 entries; the radix
+    sort takes four passes of eight bits): the pattern is structurally
+    symmetric, so A^T's row pointers and columns are A's, and perm is an
+    involution taking entry (i, j) to entry (j, i): col[perm[k]] = row(k).
+    Checked on every entry on the device; the set-up time is reported."""
+    p, d, _ = big
+    banner("config 5: pattern with the transpose map")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pat = hip.Pattern(d["rp"], d["col"], batch=1, dtype=torch.float64, build_transpose=True)
+    torch.cuda.synchronize()
+    banner(f"config 5: sla_create with the transpose map took {time.perf_counter() - t0:.2f} s")
+    _, rpt, ct, perm = pat.export_pattern()
+    assert torch.equal(rpt, d["rp"])
+    assert torch.equal(ct, d["col"])
+    pl = perm.long()
+    del perm
+    assert torch.equal(pl[pl], torch.arange(p.nnz, device=pl.device))
+    rows = torch.repeat_interleave(torch.arange(p.n, device=pl.device, dtype=torch.int32),
+                                   torch.diff(d["rp"]))
+    assert torch.equal(d["col"][pl], rows)
+    del pl, rows, rpt, ct
+    pat.close()
+    torch.cuda.empty_cache()
 
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
