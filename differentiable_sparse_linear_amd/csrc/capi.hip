@@ -97,6 +97,12 @@ struct sla_ctx {
     int graph_next = 0;          // next slot to replace when all are taken
     int32_t last_iters = 0;      // most iterations of a system in the last grid solve
     int64_t ws_bytes = 0;
+    // sla_eigsh's Lanczos basis and scalars, grown to the largest call so far
+    void *eig_V = nullptr;       // [(eig_m + 1) * n] values
+    double *eig_sc = nullptr;    // alpha, beta, coefficients, Ritz vectors, norm
+    double *eig_part = nullptr;  // partial sums
+    int eig_m = 0, eig_k = 0;    // basis and eigenpair counts the buffers hold
+    int64_t eig_bytes = 0;
 };
 
 namespace {
@@ -154,6 +160,9 @@ void release(sla_ctx *h) {
     (void)hipFree(h->dia);
     for (auto &pm : h->plan_mem)
         for (void *p : pm) (void)hipFree(p);
+    (void)hipFree(h->eig_V);
+    (void)hipFree(h->eig_sc);
+    (void)hipFree(h->eig_part);
     (void)hipFree(h->vec);
     (void)hipFree(h->st);
     (void)hipFree(h->part);
@@ -946,16 +955,51 @@ inline double start_entry(uint64_t i) {
     return (double)(z >> 11) * (2.0 / 9007199254740992.0) - 1.0;
 }
 
+// Views of the handle's eigensolver buffers for one call.
 struct EigWork {
     void *V = nullptr;       // [m + 1][n] basis
     double *sc = nullptr;    // alpha [m], beta [m], coef [m + 1], S [m * k], norm [1]
     double *part = nullptr;  // partial sums
-    ~EigWork() {
-        (void)hipFree(V);
-        (void)hipFree(sc);
-        (void)hipFree(part);
-    }
 };
+
+constexpr int64_t kEigPartBlocks = 256;  // partial sums per basis vector
+
+// The handle's basis for m Lanczos vectors and k eigenpairs: kept from the
+// largest call so far, reallocated (once per larger request) when too small.
+template <typename T>
+hipError_t eig_buffers(sla_ctx *h, int m, int k, EigWork *w) {
+    if (m > h->eig_m || k > h->eig_k) {
+        const int mm = m > h->eig_m ? m : h->eig_m;
+        const int kk = k > h->eig_k ? k : h->eig_k;
+        (void)hipFree(h->eig_V);
+        (void)hipFree(h->eig_sc);
+        (void)hipFree(h->eig_part);
+        h->eig_V = nullptr;
+        h->eig_sc = h->eig_part = nullptr;
+        h->ws_bytes -= h->eig_bytes;
+        h->eig_bytes = 0;
+        h->eig_m = h->eig_k = 0;
+        const int64_t bytes = (int64_t)sizeof(T) * (mm + 1) * h->n +
+                              (int64_t)sizeof(double) * (3 * mm + 2 + mm * kk) +
+                              (int64_t)sizeof(double) * kEigPartBlocks * (mm + 1);
+        hipError_t e;
+        if ((e = hipMalloc(&h->eig_V, sizeof(T) * (size_t)(mm + 1) * h->n)) != hipSuccess) return e;
+        if ((e = hipMalloc((void **)&h->eig_sc, sizeof(double) * (size_t)(3 * mm + 2 + mm * kk))) !=
+            hipSuccess)
+            return e;
+        if ((e = hipMalloc((void **)&h->eig_part,
+                           sizeof(double) * (size_t)kEigPartBlocks * (mm + 1))) != hipSuccess)
+            return e;
+        h->eig_m = mm;
+        h->eig_k = kk;
+        h->eig_bytes = bytes;
+        h->ws_bytes += bytes;
+    }
+    w->V = h->eig_V;
+    w->sc = h->eig_sc;
+    w->part = h->eig_part;
+    return hipSuccess;
+}
 
 // Lanczos with full reorthogonalisation (two Gram-Schmidt passes) and
 // explicit restarts from the sum of the wanted Ritz vectors, for one system.
@@ -1238,10 +1282,7 @@ sla_status sla_eigsh(sla_handle h, const void *d_values, double *h_evals, void *
         using T = std::remove_pointer_t<decltype(t)>;
         using IT = std::remove_pointer_t<decltype(it)>;
         EigWork wk;
-        const int64_t nb = 256;
-        HIP_TRY(hipMalloc(&wk.V, sizeof(T) * (size_t)(m + 1) * h->n));
-        HIP_TRY(hipMalloc(&wk.sc, sizeof(double) * (size_t)(3 * m + 2 + m * o.k)));
-        HIP_TRY(hipMalloc(&wk.part, sizeof(double) * (size_t)nb * (m + 1)));
+        HIP_TRY(eig_buffers<T>(h, m, o.k, &wk));
         sla_status worst = SLA_OK;
         for (int64_t sys = 0; sys < h->batch; ++sys) {
             sla_status st = eigsh_one<T, IT>(

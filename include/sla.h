@@ -262,9 +262,12 @@ typedef struct {
  * h_evals [batch][k] (host, ascending for the smallest, descending for the
  * largest) and d_evecs [batch][k][n] (device, unit 2-norm, sign arbitrary);
  * h_restarts [batch] (host, may be NULL) gets the restarts used.  The
- * symmetry of A is the caller's promise.  Allocates its basis
- * ((ncv + 1) * n values) for the call and synchronizes `stream`.  Returns
- * SLA_NOT_CONVERGED when some system did not meet tol.
+ * symmetry of A is the caller's promise.  The handle keeps the basis
+ * ((ncv + 1) * n values, ncv at most 512) from the first call until
+ * sla_destroy and reallocates it only for a call with a larger basis or k
+ * than any before (the one exception to "nothing is allocated after
+ * sla_create"); synchronizes `stream`.  Returns SLA_NOT_CONVERGED when some
+ * system did not meet tol.
  */
 sla_status sla_eigsh(sla_handle h, const void *d_values, double *h_evals, void *d_evecs,
                      const sla_eig_opts *opts, int32_t *h_restarts, void *stream);
@@ -308,7 +311,8 @@ int32_t sla_iteration_form(sla_handle h, int32_t transpose);
 sla_status sla_export_pattern(sla_handle h, void *d_diagpos, void *d_row_ptr_t,
                               void *d_col_t, void *d_perm, void *stream);
 
-/* Device bytes owned by the handle (constant after sla_create). */
+/* Device bytes owned by the handle (constant after sla_create, but for the
+ * eigensolver basis that sla_eigsh adds). */
 int64_t sla_workspace_bytes(sla_handle h);
 
 /* Static description of a status code. */

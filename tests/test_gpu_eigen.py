@@ -92,3 +92,27 @@ def test_eigsh_arguments(hip):
     w = np.sort(np.linalg.eigvalsh(E.dense(rp, col, val[0])))
     assert info["return"] == hip.SLA_OK and info["restarts"][0] == 0
     assert relerr(ev.cpu().numpy()[0], w[:8]) <= 1e-12
+
+
+def test_eigsh_basis_kept_by_the_handle(hip):
+    """The handle keeps the Lanczos basis: repeated calls reuse it (same
+    workspace, bitwise the same pairs); a call with a larger basis grows it
+    once, a smaller one after it does not shrink or reallocate it."""
+    banner("eigsh basis reuse")
+    N = 24
+    rp, col, val = W.laplacian_2d(N)
+    pat = _pattern(hip, rp, col)
+    v = torch.from_numpy(val[0]).cuda()
+    w0 = pat.workspace_bytes()
+    ev1, X1, _ = pat.eigsh(v, k=2, tol=1e-10, ncv=40)
+    w1 = pat.workspace_bytes()
+    ev2, X2, _ = pat.eigsh(v, k=2, tol=1e-10, ncv=40)
+    assert pat.workspace_bytes() == w1 > w0
+    assert torch.equal(ev1, ev2) and torch.equal(X1, X2)
+    ev3, _, _ = pat.eigsh(v, k=3, tol=1e-10, ncv=60)
+    w3 = pat.workspace_bytes()
+    assert w3 > w1
+    ev4, X4, _ = pat.eigsh(v, k=2, tol=1e-10, ncv=40)
+    assert pat.workspace_bytes() == w3
+    assert torch.equal(ev4, ev1) and torch.equal(X4, X1)
+    assert abs(ev3[0, 0].item() - ev1[0, 0].item()) <= 1e-10 * ev1[0, 0].item()
