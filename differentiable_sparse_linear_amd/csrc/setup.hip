@@ -37,12 +37,16 @@
 
 namespace sla {
 
+// Threads per workgroup of every set-up kernel (independent of the solver
+// kernels' block size).
+constexpr int kSetupThreads = 256;
+
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restrict__ rp, int64_t n,
+__global__ __launch_bounds__(kSetupThreads) void check_rowptr_kernel(const IT *__restrict__ rp, int64_t n,
                                                               int64_t nnz, int32_t *flag) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int bad = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride) {
         const IT a = rp[i], b = rp[i + 1];
         if (b < a) bad = 1;
         if (i == 0 && a != 0) bad = 1;
@@ -52,13 +56,13 @@ __global__ __launch_bounds__(kBlock) void check_rowptr_kernel(const IT *__restri
 }
 
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void check_cols_kernel(const IT *__restrict__ rp,
+__global__ __launch_bounds__(kSetupThreads) void check_cols_kernel(const IT *__restrict__ rp,
                                                             const int32_t *__restrict__ col,
                                                             int64_t n, IT *__restrict__ diagpos,
                                                             int32_t *flag) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int bad = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride) {
         const IT e = rp[i + 1];
         int64_t prev = -1;
         IT dpos = -1;
@@ -79,10 +83,10 @@ __global__ __launch_bounds__(kBlock) void check_cols_kernel(const IT *__restrict
 // max-scan then carries every mark over the row's other entries (an empty
 // row writes nothing and its index is below the next row's).
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void row_start_kernel(const IT *__restrict__ rp, int64_t n,
+__global__ __launch_bounds__(kSetupThreads) void row_start_kernel(const IT *__restrict__ rp, int64_t n,
                                                            int32_t *__restrict__ rowidx) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride)
         if (rp[i + 1] > rp[i]) rowidx[rp[i]] = (int32_t)i;
 }
 
@@ -90,12 +94,12 @@ __global__ __launch_bounds__(kBlock) void row_start_kernel(const IT *__restrict_
 // entry's when that entry is in the same row; the diagonal's position
 // (diagpos preset to -1; check_diag_kernel flags the rows without one).
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void check_cols_entries_kernel(
+__global__ __launch_bounds__(kSetupThreads) void check_cols_entries_kernel(
     const IT *__restrict__ rp, const int32_t *__restrict__ col, const int32_t *__restrict__ rowidx,
     int64_t n, int64_t nnz, IT *__restrict__ diagpos, int32_t *flag) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int bad = 0;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride) {
+    for (int64_t k = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; k < nnz; k += stride) {
         const int32_t r = rowidx[k];
         const int64_t c = col[k];
         if (c < 0 || c >= n) bad = 1;
@@ -106,11 +110,11 @@ __global__ __launch_bounds__(kBlock) void check_cols_entries_kernel(
 }
 
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void check_diag_kernel(const IT *__restrict__ diagpos,
+__global__ __launch_bounds__(kSetupThreads) void check_diag_kernel(const IT *__restrict__ diagpos,
                                                             int64_t n, int32_t *flag) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int bad = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride)
         if (diagpos[i] < 0) bad = 1;
     raise_flag(bad, flag);
 }
@@ -118,11 +122,11 @@ __global__ __launch_bounds__(kBlock) void check_diag_kernel(const IT *__restrict
 // col_t[k] = the row of A entry perm[k] (-1 for a position outside [0, m),
 // which only a faulty sort could leave, so that it shows in the map instead
 // of reading out of bounds)
-__global__ __launch_bounds__(kBlock) void col_t_kernel(const int32_t *__restrict__ perm,
+__global__ __launch_bounds__(kSetupThreads) void col_t_kernel(const int32_t *__restrict__ perm,
                                                        const int32_t *__restrict__ rowidx,
                                                        int32_t *__restrict__ col_t, int64_t m) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < m; k += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
+    for (int64_t k = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; k < m; k += stride) {
         const int64_t j = perm[k];
         col_t[k] = j >= 0 && j < m ? rowidx[j] : -1;
     }
@@ -132,10 +136,10 @@ __global__ __launch_bounds__(kBlock) void col_t_kernel(const int32_t *__restrict
 // are columns, in [0, n); the loop bounds are clamped to that range all the
 // same)
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void rowptr_t_kernel(const int32_t *__restrict__ keys,
+__global__ __launch_bounds__(kSetupThreads) void rowptr_t_kernel(const int32_t *__restrict__ keys,
                                                           int64_t m, int64_t n, IT *__restrict__ rp_t) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k <= m; k += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
+    for (int64_t k = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; k <= m; k += stride) {
         int64_t lo = (k == 0) ? -1 : (int64_t)keys[k - 1];
         int64_t hi = (k == m) ? n : (int64_t)keys[k];
         lo = lo < -1 ? -1 : lo;
@@ -145,11 +149,11 @@ __global__ __launch_bounds__(kBlock) void rowptr_t_kernel(const int32_t *__restr
 }
 
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ rp, int64_t n,
+__global__ __launch_bounds__(kSetupThreads) void max_row_kernel(const IT *__restrict__ rp, int64_t n,
                                                          int32_t *out) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int64_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride) {
         const int64_t len = (int64_t)(rp[i + 1] - rp[i]);
         m = len > m ? len : m;
     }
@@ -159,11 +163,11 @@ __global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ 
         const int32_t o = __shfl_xor(mi, off, 64);
         mi = o > mi ? o : mi;
     }
-    __shared__ int32_t wm[kWaves];
+    __shared__ int32_t wm[kSetupThreads / 64];
     if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mi;
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < kWaves; ++w) mi = wm[w] > mi ? wm[w] : mi;
+        for (int w = 1; w < kSetupThreads / 64; ++w) mi = wm[w] > mi ? wm[w] : mi;
         atomicMax(out, mi > wm[0] ? mi : wm[0]);  // one atomic per block
     }
 }
@@ -171,12 +175,12 @@ __global__ __launch_bounds__(kBlock) void max_row_kernel(const IT *__restrict__ 
 // One thread per row: the offsets of the row's columns from its tile's first
 // row; any offset outside int16 sets *bad.  `out` may be null (check only).
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void col16_kernel(const IT *__restrict__ rp,
+__global__ __launch_bounds__(kSetupThreads) void col16_kernel(const IT *__restrict__ rp,
                                                        const int32_t *__restrict__ col, int64_t n,
                                                        int16_t *__restrict__ out, int32_t *bad) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int b = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride) {
         const int64_t row0 = i / kTileRows * kTileRows;
         for (IT k = rp[i]; k < rp[i + 1]; ++k) {
             const int64_t d = (int64_t)col[k] - row0;
@@ -189,14 +193,14 @@ __global__ __launch_bounds__(kBlock) void col16_kernel(const IT *__restrict__ rp
 }
 
 // The same entry by entry, from the row of every entry.
-__global__ __launch_bounds__(kBlock) void col16_entries_kernel(const int32_t *__restrict__ col,
+__global__ __launch_bounds__(kSetupThreads) void col16_entries_kernel(const int32_t *__restrict__ col,
                                                                const int32_t *__restrict__ rowidx,
                                                                int64_t nnz,
                                                                int16_t *__restrict__ out,
                                                                int32_t *bad) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     int b = 0;
-    for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride) {
+    for (int64_t k = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; k < nnz; k += stride) {
         const int64_t row0 = (int64_t)rowidx[k] / kTileRows * kTileRows;
         const int64_t d = (int64_t)col[k] - row0;
         const bool ok = d >= -32768 && d <= 32767;
@@ -222,7 +226,7 @@ __device__ __forceinline__ bool set_insert(int32_t *tab, int32_t v) {
 }
 
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void diag_collect_kernel(const IT *__restrict__ rp,
+__global__ __launch_bounds__(kSetupThreads) void diag_collect_kernel(const IT *__restrict__ rp,
                                                               const int32_t *__restrict__ col,
                                                               int64_t n, int32_t *table,
                                                               int32_t *over) {
@@ -231,8 +235,8 @@ __global__ __launch_bounds__(kBlock) void diag_collect_kernel(const IT *__restri
     if (threadIdx.x < kMaxDiags) loc[threadIdx.x] = kEmpty;
     if (threadIdx.x == 0) bad = 0;
     __syncthreads();
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride)
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride)
         for (IT k = rp[i]; k < rp[i + 1]; ++k)
             if (!set_insert(loc, (int32_t)((int64_t)col[k] - i))) bad = 1;
     __syncthreads();
@@ -243,14 +247,14 @@ __global__ __launch_bounds__(kBlock) void diag_collect_kernel(const IT *__restri
 
 // msk[i] = bit q set for every stored entry of row i on diagonal dlt[q].
 template <typename IT>
-__global__ __launch_bounds__(kBlock) void diag_mask_kernel(const IT *__restrict__ rp,
+__global__ __launch_bounds__(kSetupThreads) void diag_mask_kernel(const IT *__restrict__ rp,
                                                            const int32_t *__restrict__ col,
                                                            int64_t n,
                                                            const int32_t *__restrict__ dlt,
                                                            int32_t ndiag,
                                                            uint16_t *__restrict__ msk) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; i < n; i += stride) {
         uint32_t m = 0;
         for (IT k = rp[i]; k < rp[i + 1]; ++k) {
             const int64_t d = (int64_t)col[k] - i;
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void diag_mask_kernel(const IT *__restrict_
 
 
 static unsigned blocks_for(int64_t m) {
-    int64_t b = (m + kBlock - 1) / kBlock;
+    int64_t b = (m + kSetupThreads - 1) / kSetupThreads;
     if (b > 65536) b = 65536;
     if (b < 1) b = 1;
     return (unsigned)b;
@@ -273,13 +277,13 @@ static unsigned blocks_for(int64_t m) {
 //
 // Reduce-then-scan of int32 values over tiles of kScanTile, with the sum
 // (MAX = false) or the maximum (MAX = true); every value is >= 0, so 0 is
-// the identity of both.  A tile is loaded coalesced (element j * kBlock + t
+// the identity of both.  A tile is loaded coalesced (element j * kSetupThreads + t
 // by thread t) into LDS and read back blocked (thread t owns the kScanItems
 // consecutive elements t * kScanItems ...; a padding word after every 16
 // keeps those reads off a single bank), scanned in registers and across the
 // block, and written back the same way.
 constexpr int kScanItems = 16;
-constexpr int kScanTile = kBlock * kScanItems;
+constexpr int kScanTile = kSetupThreads * kScanItems;
 constexpr int kScanLds = kScanTile + kScanTile / 16;
 
 template <bool MAX>
@@ -293,7 +297,7 @@ __device__ __forceinline__ int lds_pad(int e) { return e + (e >> 4); }
 // *total gets the block's aggregate.  Every thread gets the same total.
 template <bool MAX>
 __device__ __forceinline__ int32_t block_exclusive(int32_t v, int32_t *total) {
-    __shared__ int32_t wsum[kWaves];
+    __shared__ int32_t wsum[kSetupThreads / 64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int32_t inc = v;
 #pragma unroll
@@ -307,7 +311,7 @@ __device__ __forceinline__ int32_t block_exclusive(int32_t v, int32_t *total) {
     __syncthreads();
     int32_t carry = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kSetupThreads / 64; ++w) {
         if (w < wave) carry = scan_op<MAX>(carry, wsum[w]);
         all = scan_op<MAX>(all, wsum[w]);
     }
@@ -323,7 +327,7 @@ __device__ __forceinline__ void tile_load(const int32_t *__restrict__ in, int64_
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
-        const int e = j * kBlock + threadIdx.x;
+        const int e = j * kSetupThreads + threadIdx.x;
         sh[lds_pad(e)] = base + e < m ? in[base + e] : 0;
     }
     __syncthreads();
@@ -334,7 +338,7 @@ __device__ __forceinline__ void tile_load(const int32_t *__restrict__ in, int64_
 
 // tot[b] = the aggregate of tile b.
 template <bool MAX>
-__global__ __launch_bounds__(kBlock) void tile_total_kernel(const int32_t *__restrict__ in,
+__global__ __launch_bounds__(kSetupThreads) void tile_total_kernel(const int32_t *__restrict__ in,
                                                             int64_t m, int32_t *__restrict__ tot) {
     __shared__ int32_t sh[kScanLds];
     int32_t v[kScanItems];
@@ -347,12 +351,12 @@ __global__ __launch_bounds__(kBlock) void tile_total_kernel(const int32_t *__res
     if (threadIdx.x == 0) tot[blockIdx.x] = all;
 }
 
-// tot[0..nt) becomes its exclusive scan: one workgroup, kBlock at a time.
+// tot[0..nt) becomes its exclusive scan: one workgroup, kSetupThreads at a time.
 template <bool MAX>
-__global__ __launch_bounds__(kBlock) void totals_scan_kernel(int32_t *__restrict__ tot,
+__global__ __launch_bounds__(kSetupThreads) void totals_scan_kernel(int32_t *__restrict__ tot,
                                                              int64_t nt) {
     int32_t carry = 0;
-    for (int64_t c = 0; c < nt; c += kBlock) {
+    for (int64_t c = 0; c < nt; c += kSetupThreads) {
         const int64_t i = c + threadIdx.x;
         const int32_t v = i < nt ? tot[i] : 0;
         int32_t all;
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void totals_scan_kernel(int32_t *__restrict
 // starting from the exclusive scan of the tile totals, carry[b].  in and
 // out may be the same array (each tile is read before it is written).
 template <bool MAX, bool EXCL>
-__global__ __launch_bounds__(kBlock) void tile_scan_kernel(const int32_t *in, int64_t m,
+__global__ __launch_bounds__(kSetupThreads) void tile_scan_kernel(const int32_t *in, int64_t m,
                                                            const int32_t *__restrict__ carry,
                                                            int32_t *out) {
     __shared__ int32_t sh[kScanLds];
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(kBlock) void tile_scan_kernel(const int32_t *in, in
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
 #pragma unroll
     for (int j = 0; j < kScanItems; ++j) {
-        const int e = j * kBlock + threadIdx.x;
+        const int e = j * kSetupThreads + threadIdx.x;
         if (base + e < m) out[base + e] = sh[lds_pad(e)];
     }
 }
@@ -399,9 +403,9 @@ template <bool MAX, bool EXCL>
 hipError_t scan_inplace(int32_t *data, int64_t m, int32_t *tot, hipStream_t s) {
     const int64_t nt = scan_tiles(m);
     if (nt < 1) return hipSuccess;
-    tile_total_kernel<MAX><<<(unsigned)nt, kBlock, 0, s>>>(data, m, tot);
-    totals_scan_kernel<MAX><<<1, kBlock, 0, s>>>(tot, nt);
-    tile_scan_kernel<MAX, EXCL><<<(unsigned)nt, kBlock, 0, s>>>(data, m, tot, data);
+    tile_total_kernel<MAX><<<(unsigned)nt, kSetupThreads, 0, s>>>(data, m, tot);
+    totals_scan_kernel<MAX><<<1, kSetupThreads, 0, s>>>(tot, nt);
+    tile_scan_kernel<MAX, EXCL><<<(unsigned)nt, kSetupThreads, 0, s>>>(data, m, tot, data);
     return hipGetLastError();
 }
 
@@ -409,12 +413,13 @@ hipError_t scan_inplace(int32_t *data, int64_t m, int32_t *tot, hipStream_t s) {
 //
 // One pass sorts (key, value) pairs stably by the eight bits of the key at
 // `shift`.  Tile b is entries [b * kSortTile, (b + 1) * kSortTile), taken in
-// kSortRounds rounds of kBlock consecutive entries, wavefront w holding
-// entries [r * kBlock + 64 w, r * kBlock + 64 w + 64) of round r.
+// kSortRounds rounds of kSetupThreads consecutive entries, wavefront w holding
+// entries [r * kSetupThreads + 64 w, r * kSetupThreads + 64 w + 64) of round r.
 constexpr int kSortRounds = 16;
-constexpr int kSortTile = kBlock * kSortRounds;
+constexpr int kSortTile = kSetupThreads * kSortRounds;
 constexpr int kRadix = 256;
-static_assert(kBlock == kRadix, "one thread per digit in the sort's bookkeeping");
+static_assert(kSetupThreads == kRadix, "one thread per digit in the sort's bookkeeping");
+constexpr int kSetupWaves = kSetupThreads / 64;
 
 inline int64_t sort_tiles(int64_t m) { return (m + kSortTile - 1) / kSortTile; }
 
@@ -423,7 +428,7 @@ __device__ __forceinline__ int32_t sort_value(const int32_t *vin, int64_t e) {
 }
 
 // hist[d * ntiles + b] = entries of tile b whose digit is d.
-__global__ __launch_bounds__(kBlock) void digit_count_kernel(const int32_t *__restrict__ key,
+__global__ __launch_bounds__(kSetupThreads) void digit_count_kernel(const int32_t *__restrict__ key,
                                                              int64_t m, int shift,
                                                              int32_t *__restrict__ hist) {
     __shared__ int32_t h[kRadix];
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(kBlock) void digit_count_kernel(const int32_t *__re
     __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
     for (int r = 0; r < kSortRounds; ++r) {
-        const int64_t e = base + r * kBlock + threadIdx.x;
+        const int64_t e = base + r * kSetupThreads + threadIdx.x;
         if (e < m) atomicAdd(&h[(key[e] >> shift) & (kRadix - 1)], 1);
     }
     __syncthreads();
@@ -440,20 +445,20 @@ __global__ __launch_bounds__(kBlock) void digit_count_kernel(const int32_t *__re
 
 // Stable scatter of tile b: start[d * ntiles + b] is the position of the
 // tile's first entry of digit d (the exclusive scan of hist).
-__global__ __launch_bounds__(kBlock) void digit_scatter_kernel(
+__global__ __launch_bounds__(kSetupThreads) void digit_scatter_kernel(
     const int32_t *__restrict__ kin, const int32_t *__restrict__ vin, int64_t m, int shift,
     const int32_t *__restrict__ start, int32_t *__restrict__ kout, int32_t *__restrict__ vout) {
     __shared__ int32_t pos0[kRadix];          // next position of digit d in this tile
-    __shared__ int32_t cnt[kWaves][kRadix];   // this round's count of digit d per wavefront
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ int32_t cnt[kSetupWaves][kRadix];   // this round's count of digit d per wavefront
+    const int tid = threadIdx.x, wave = tid >> 6;
     pos0[tid] = start[(int64_t)tid * gridDim.x + blockIdx.x];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) cnt[w][tid] = 0;
+    for (int w = 0; w < kSetupWaves; ++w) cnt[w][tid] = 0;
     __syncthreads();
     const uint64_t below = __lanemask_lt();
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
     for (int r = 0; r < kSortRounds; ++r) {
-        const int64_t e = base + r * kBlock + tid;
+        const int64_t e = base + r * kSetupThreads + tid;
         const bool act = e < m;
         const int32_t k = act ? kin[e] : 0;
         const int32_t v = act ? sort_value(vin, e) : 0;
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(kBlock) void digit_scatter_kernel(
         __syncthreads();
         int32_t add = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kSetupWaves; ++w) {
             add += cnt[w][tid];
             cnt[w][tid] = 0;
         }
@@ -548,7 +553,7 @@ hipError_t setup_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *fla
                               hipStream_t s) {
     hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
-    check_rowptr_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, nnz, flag);
+    check_rowptr_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, n, nnz, flag);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(bad, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
@@ -561,7 +566,7 @@ hipError_t setup_row_index(const IT *rp, int64_t n, int64_t nnz, int32_t *rowidx
                            hipStream_t s) {
     hipError_t e = hipMemsetAsync(rowidx, 0, sizeof(int32_t) * nnz, s);
     if (e != hipSuccess) return e;
-    row_start_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, rowidx);
+    row_start_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, n, rowidx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return scan_inplace<true, false>(rowidx, nnz, tot, s);
 }
@@ -576,12 +581,12 @@ hipError_t setup_check_cols(const IT *rp, const int32_t *col, int64_t n, int64_t
     hipError_t e = hipMemsetAsync(flag, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
     if (!rowidx) {
-        check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
+        check_cols_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, col, n, diagpos, flag);
     } else {
         if ((e = hipMemsetAsync(diagpos, 0xff, sizeof(IT) * n, s)) != hipSuccess) return e;
         check_cols_entries_kernel<IT>
-            <<<blocks_for(nnz), kBlock, 0, s>>>(rp, col, rowidx, n, nnz, diagpos, flag);
-        check_diag_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(diagpos, n, flag);
+            <<<blocks_for(nnz), kSetupThreads, 0, s>>>(rp, col, rowidx, n, nnz, diagpos, flag);
+        check_diag_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(diagpos, n, flag);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(bad, flag, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -597,7 +602,7 @@ hipError_t setup_max_row(const IT *rp, int64_t n, int32_t *scratch, int32_t *out
     // a few hundred blocks striding over the rows: the atomics on one word
     // serialise, so their number is kept small
     const unsigned nb = blocks_for(n) < 512 ? blocks_for(n) : 512;
-    max_row_kernel<IT><<<nb, kBlock, 0, s>>>(rp, n, scratch);
+    max_row_kernel<IT><<<nb, kSetupThreads, 0, s>>>(rp, n, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipMemcpyAsync(out, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
         return e;
@@ -614,7 +619,7 @@ hipError_t setup_diag(const IT *rp, const int32_t *col, int64_t n, int32_t *dev_
     if (e != hipSuccess) return e;
     if ((e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s)) != hipSuccess) return e;
     const unsigned nb = blocks_for(n) < 1024 ? blocks_for(n) : 1024;
-    diag_collect_kernel<IT><<<nb, kBlock, 0, s>>>(rp, col, n, dev_table, scratch);
+    diag_collect_kernel<IT><<<nb, kSetupThreads, 0, s>>>(rp, col, n, dev_table, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t tab[kMaxDiags], over = 1;
     if ((e = hipMemcpyAsync(tab, dev_table, sizeof(tab), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -641,7 +646,7 @@ hipError_t setup_diag(const IT *rp, const int32_t *col, int64_t n, int32_t *dev_
 template <typename IT>
 hipError_t setup_diag_masks(const IT *rp, const int32_t *col, int64_t n, const int32_t *dlt_dev,
                             int32_t ndiag, uint16_t *msk, hipStream_t s) {
-    diag_mask_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, dlt_dev, ndiag, msk);
+    diag_mask_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, col, n, dlt_dev, ndiag, msk);
     return hipGetLastError();
 }
 
@@ -652,9 +657,9 @@ hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
     hipError_t e = hipMemsetAsync(scratch, 0, sizeof(int32_t), s);
     if (e != hipSuccess) return e;
     if (!rowidx)
-        col16_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, out, scratch);
+        col16_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, col, n, out, scratch);
     else
-        col16_entries_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(col, rowidx, nnz, out, scratch);
+        col16_entries_kernel<<<blocks_for(nnz), kSetupThreads, 0, s>>>(col, rowidx, nnz, out, scratch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     int32_t bad = 1;
     if ((e = hipMemcpyAsync(&bad, scratch, sizeof(int32_t), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -681,10 +686,10 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
         const bool last = ((passes - 1 - i) & 1) == 0;
         int32_t *kout = last ? scr.keys[1] : scr.keys[0];
         int32_t *vout = last ? perm : scr.vals;
-        digit_count_kernel<<<(unsigned)nt, kBlock, 0, s>>>(kin, nnz, 8 * i, scr.hist);
+        digit_count_kernel<<<(unsigned)nt, kSetupThreads, 0, s>>>(kin, nnz, 8 * i, scr.hist);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = scan_inplace<false, true>(scr.hist, nh, scr.tot, s)) != hipSuccess) return e;
-        digit_scatter_kernel<<<(unsigned)nt, kBlock, 0, s>>>(kin, vin, nnz, 8 * i, scr.hist,
+        digit_scatter_kernel<<<(unsigned)nt, kSetupThreads, 0, s>>>(kin, vin, nnz, 8 * i, scr.hist,
                                                             kout, vout);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         kin = kout;
@@ -692,8 +697,8 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
     }
     // keys[1] holds the sorted columns: the row of every entry of A^T
     scr.rowidx_t = scr.keys[1];
-    rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kBlock, 0, s>>>(scr.rowidx_t, nnz, n, rp_t);
-    col_t_kernel<<<blocks_for(nnz), kBlock, 0, s>>>(perm, scr.rowidx, col_t, nnz);
+    rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kSetupThreads, 0, s>>>(scr.rowidx_t, nnz, n, rp_t);
+    col_t_kernel<<<blocks_for(nnz), kSetupThreads, 0, s>>>(perm, scr.rowidx, col_t, nnz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return hipStreamSynchronize(s);
 }
@@ -704,21 +709,21 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
 template <typename IT>
 hipError_t launch_check_rowptr(const IT *rp, int64_t n, int64_t nnz, int32_t *flag,
                                hipStream_t s) {
-    check_rowptr_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, n, nnz, flag);
+    check_rowptr_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, n, nnz, flag);
     return hipGetLastError();
 }
 
 template <typename IT>
 hipError_t launch_check_cols_rows(const IT *rp, const int32_t *col, int64_t n, IT *diagpos,
                                   int32_t *flag, hipStream_t s) {
-    check_cols_kernel<IT><<<blocks_for(n), kBlock, 0, s>>>(rp, col, n, diagpos, flag);
+    check_cols_kernel<IT><<<blocks_for(n), kSetupThreads, 0, s>>>(rp, col, n, diagpos, flag);
     return hipGetLastError();
 }
 
 template <typename IT>
 hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s) {
     const unsigned nb = blocks_for(n) < 512 ? blocks_for(n) : 512;
-    max_row_kernel<IT><<<nb, kBlock, 0, s>>>(rp, n, out);
+    max_row_kernel<IT><<<nb, kSetupThreads, 0, s>>>(rp, n, out);
     return hipGetLastError();
 }
 

@@ -61,11 +61,12 @@ ERR_ARG, ERR_PATTERN, ERR_ZERO_DIAG, ERR_NO_MEMORY = -1, -2, -3, -4
 _lib = None
 
 
-def compile_source(src: str, out: str) -> str:
-    """gcc build of an oracle source file into a shared library."""
+def compile_source(src: str, out: str, extra=()) -> str:
+    """gcc build of an oracle source file into a shared library (extra:
+    more gcc flags, e.g. sanitizers)."""
     tmp = out + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-ffp-contract=off",
-           "-fno-fast-math", "-fopenmp", src, "-o", tmp, "-lm"]
+           "-fno-fast-math", "-fopenmp", *extra, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
