@@ -228,7 +228,6 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     const int cm = op.it.mode;
     const int slots = op.it_slots;
     const bool dmaj = cm == kColDiaMajor;
-    const bool zw = cg && cg_zwalk(op.it, n);
     // vector v of system j of the group: vec + (v * G + j) * n
     T *vec = reinterpret_cast<T *>(h->vec);
     auto vp = [&](int v) { return vec + (int64_t)v * G * n; };
@@ -240,6 +239,8 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     // CG reads the lower diagonals through their mirrors when the pack finds
     // the values symmetric; the offsets must mirror for that
     a.cols.sym = cg && dmaj && mirrored(op.it) ? 1 : 0;
+    // CG on a 3D seven-point form walks each column of planes (z-walk)
+    const int zw = cg ? cg_zwalk_plan(a.cols, n, (int64_t)sizeof(T)) : 0;
     a.x = x;
     a.b = b;
     a.r = vp(0);

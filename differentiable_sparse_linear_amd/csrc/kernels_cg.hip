@@ -132,12 +132,16 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 #ifndef SLA_CG_WAVES
 #define SLA_CG_WAVES 5
 #endif
-// ZW: the z-walk of dia_rows_zw (diagonal-major, seven diagonals, the host
-// has checked that the outermost offset is one round of tiles).
-template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, bool ZW = false>
+// ZW: 0, or the z-walk of dia_rows_zw (diagonal-major, seven diagonals, a
+// plan from cg_zwalk_plan in the operator's column arguments); ZW == 2
+// streams the values, p, x and the vectors written here with non-temporal
+// hints (grids far beyond the Infinity Cache, where these are touched once
+// per iteration and L2 is better left to the plane's +-N neighbours).
+template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
+    constexpr bool NT = ZW == 2;
     A += blockIdx.y;
     SolveState *st = A->st;
     __shared__ int seen[kWaves];
@@ -236,15 +240,17 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
     auto gath = [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; };
-    // The z-walk runs on grids far beyond the Infinity Cache: there the
-    // values, p, x and the vectors written here are touched once per
-    // iteration, so they stream with non-temporal hints and leave L2 to the
-    // plane's +-N neighbours.
     auto put = [&](gptr<T> v, int64_t i, T a) {
-        if constexpr (ZW)
+        if constexpr (NT)
             __builtin_nontemporal_store(a, &v[i]);
         else
             v[i] = a;
+    };
+    auto stream = [&](gptr<const T> v, int64_t i) -> T {
+        if constexpr (NT)
+            return __builtin_nontemporal_load(&v[i]);
+        else
+            return v[i];
     };
     auto row = [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
         const T pi = fmaT(beta, o.p, o.u);
@@ -264,12 +270,11 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     if constexpr (ZW) {
         __shared__ G3<T> zring[3][kTileRows];
         go = dia_rows_zw<T>(
-            walk_tiles(tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
-            [&](auto k) { return __builtin_nontemporal_load(&val[k]); },
+            !stopped, n, cg_cols<CM>(A->cols, st), [&](auto k) { return stream(val, k); },
             [&](auto k) { return val[k]; }, gath, u_of,
             [&](int64_t i, const G3<T> &o) {
-                return CgOwn<T>{o.a, o.b, o.c, __builtin_nontemporal_load(&pprev[i]),
-                                PH ? __builtin_nontemporal_load(&x[i]) : T(0)};
+                return CgOwn<T>{o.a, o.b, o.c, stream(pprev, i),
+                                PH ? stream((gptr<const T>)x, i) : T(0)};
             },
             row, pre, post, zring);
     } else {
@@ -713,14 +718,36 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 
 // ------------------------------------------------------------------ launchers
 
-bool cg_zwalk(const ColArgs &it, int64_t n) {
-    if (it.mode != kColDiaMajor || it.nd != 7) return false;
-    const int64_t nt = tiles_of(n);
-    const int64_t grid = grid_for_tiles(nt);
-    // tiles in rounds of `grid` (xcd_tiles) and the outermost offset exactly
-    // one round of tiles, so that a block's next tile is the next plane
-    return it.off[2] == -1 && it.off[4] == 1 && it.off[0] == -it.off[6] &&
-           (int64_t)it.off[6] == grid * kTileRows && nt >= kRoundsFrom * grid;
+// Planes per workgroup below which the z-walk is not used.  A segment reads
+// the plane below its first one and the plane above its last one, which its
+// neighbouring segments load at the other end of their walks, by then out
+// of L2: with short segments these reloads cost more than the ring saves
+// (100^3, 4 planes per segment: 94.7 MB read per launch instead of the
+// 80.1 MB of the tiles in slabs, 25.2 instead of 24.5 us).
+constexpr int64_t kZwMinPlanes = 16;
+// Working sets beyond this stay out of the 256 MB Infinity Cache.
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
+
+int cg_zwalk_plan(ColArgs &it, int64_t n, int64_t value_bytes) {
+    it.zw_tw = it.zw_ncol = it.zw_nseg = it.zw_nz = 0;
+    if (it.mode != kColDiaMajor || it.nd != 7) return 0;
+    const int64_t D = it.off[6];
+    if (!(it.off[2] == -1 && it.off[4] == 1 && it.off[0] == -D && it.off[1] == -it.off[5] &&
+          it.off[5] > 1 && D > it.off[5] && n % D == 0))
+        return 0;
+    const int64_t nz = n / D;
+    const int64_t grid = grid_for_tiles(tiles_of(n));
+    const int64_t ncol = (D + kTileRows - 1) / kTileRows;  // columns of at most 256 rows
+    const int64_t tw = (D + ncol - 1) / ncol;                // as even as they go
+    int64_t nseg = grid / ncol;                              // segments per column
+    if (nseg < 1 || nz / nseg < kZwMinPlanes) return 0;
+    it.zw_tw = (int32_t)tw;
+    it.zw_ncol = (int32_t)ncol;
+    it.zw_nseg = (int32_t)nseg;
+    it.zw_nz = (int32_t)nz;
+    // the iteration touches 4 values (symmetric: main and upper diagonals)
+    // and 9 vectors of each row on average
+    return n * 13 * value_bytes > kInfinityCacheBytes ? 2 : 1;
 }
 
 template <typename T, typename IT>
@@ -738,12 +765,15 @@ hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
                           int64_t n, int nsys, int ph, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
 #define SLA_CG_ITER(J, P)                                                                      \
-    if (zw)                                                                                    \
-        launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, true>, grid,           \
+    if (zw == 2)                                                                               \
+        launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, 2>, grid,              \
+                           dim3(kBlock), 0, s, ev, a);                                         \
+    else if (zw == 1)                                                                          \
+        launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, 1>, grid,              \
                            dim3(kBlock), 0, s, ev, a);                                         \
     else                                                                                       \
         SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(cg_iter_kernel<T, IT, J, kS, P, kC>,   \
@@ -876,7 +906,7 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
                                               int64_t, int, hipStream_t);                       \
-    template hipError_t launch_cg_iter<T, IT>(int, int, bool, bool, const IterArgs<T, IT> *, \
+    template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, const IterArgs<T, IT> *, \
                                               int64_t, int, int, hipStream_t,                   \
                                               const hipEvent_t *);                              \
     template hipError_t launch_block_cg<T, IT>(int, const BlockCgParams &, int, hipStream_t);  \

@@ -109,6 +109,11 @@ struct ColArgs {
     // row's entries below the main diagonal from the upper diagonals of the
     // rows they mirror: A[i][i-d] = A[i-d][i]
     int32_t sym = 0;
+    // kColDiaMajor, seven diagonals (0, +-1, +-N, +-D), CG: the plan of the
+    // z-walk (cg_zwalk_plan) -- each plane of D rows cut into zw_ncol
+    // columns of at most zw_tw rows, each column's zw_nz planes into zw_nseg
+    // segments, one workgroup per segment; 0 when there is no z-walk
+    int32_t zw_tw = 0, zw_ncol = 0, zw_nseg = 0, zw_nz = 0;
 };
 
 // Arguments of the grid iteration kernels for one system.  A launch that
@@ -432,14 +437,18 @@ hipError_t launch_dinv(const IT *diagpos, const T *val, int64_t val_stride, T *d
 template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           int nsys, hipStream_t s);
-// zw: the z-walk variant (diagonal-major, seven diagonals with off[2] = -1,
-// off[4] = 1, off[0] = -off[6] = -kTileRows * grid, tiles in rounds)
+// zw: 0, or the z-walk (cg_zwalk_plan) with plain (1) or non-temporal (2)
+// streams of the values and the vectors touched once
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, bool zw, const IterArgs<T, IT> *a,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
                           int64_t n, int nsys, int ph, hipStream_t s,
                           const hipEvent_t *ev = nullptr);
-// whether the z-walk applies to an operator form on n rows
-bool cg_zwalk(const ColArgs &it, int64_t n);
+// The z-walk of a seven-diagonal operator form on n rows (3D stencils: a
+// plane of D = off[6] rows, nz = n / D planes): fills it's zw_* fields and
+// returns 1 (working set within the Infinity Cache: plain accesses) or 2
+// (beyond it: non-temporal streams), or 0 when the walk does not apply
+// (other forms, fewer than kZwMinPlanes planes per workgroup).
+int cg_zwalk_plan(ColArgs &it, int64_t n, int64_t value_bytes);
 // CG in three launches per iteration for operators with a row plan: init's
 // first half (u_0, x), then per iteration the row updates (split_u), the
 // product u -> v[0] through the plan (launch_spmv), and split_w (w^ and the

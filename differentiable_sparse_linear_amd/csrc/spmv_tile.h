@@ -141,6 +141,7 @@ struct ColSrc {
     // i's entry on a diagonal q below the main one is read as the entry of
     // row i + off[q] on the mirrored diagonal (uniform across the grid)
     int32_t sym;
+    int32_t zw_tw, zw_ncol, zw_nseg, zw_nz;  // the z-walk's plan (ColArgs)
     // column of stored entry k in the tile starting at row0 (per-entry modes)
     __device__ __forceinline__ int32_t operator()(int64_t k, int64_t row0) const {
         if constexpr (CM == kColTile16)
@@ -151,11 +152,15 @@ struct ColSrc {
 };
 template <int CM>
 __device__ __forceinline__ ColSrc<CM> col_src(const ColArgs &a) {
-    ColSrc<CM> c{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg, {}, 0};
+    ColSrc<CM> c{glb(a.col), glb(a.col16), glb(a.msk), glb(a.dlt), a.nneg, {}, 0, 0, 0, 0, 0};
     if constexpr (CM == kColDiaMajor) {
 #pragma unroll
         for (int q = 0; q < kMaxDiaMajor; ++q) c.off[q] = a.off[q];
         c.sym = a.sym;
+        c.zw_tw = a.zw_tw;
+        c.zw_ncol = a.zw_ncol;
+        c.zw_nseg = a.zw_nseg;
+        c.zw_nz = a.zw_nz;
     }
     return c;
 }
@@ -255,50 +260,69 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
 }
 
 // Rows of a seven-diagonal operator walked along its outermost offset
-// D = off[6] = -off[0] (a 3D stencil's plane), with off[2] = -1, off[4] = 1.
-// When the tiles go in rounds of gridDim.x and D = gridDim.x * kTileRows, a
-// block's next tile is the plane above its current one, lane for lane.  The
-// block then keeps, per lane, the gathered entries of its column in planes
-// z - 1, z and z + 1 in an LDS ring: the +D gathers of plane z are plane
-// z + 1's own entries, so every plane's entries are read from memory once per
-// launch; the -D, own and (inside the tile) +-1 gathers come from the ring,
-// the other gathers from memory.  ofz(i, g) builds a row's own inputs from
-// its gathered entries g.  The terms and their order are those of dia_rows,
-// so the sums are bitwise the same.  With col.sym the -D entry of a row is
-// the +D entry of the row one plane below, which this lane loaded for its
-// previous tile: it is carried in a register, and the -1 and -N entries are
-// read from their mirrors as in dia_rows.  The values of the +-1 and +-N
-// diagonals then go through vk (loads that keep their lines cached, since
-// the mirrored reads come back to them), the others through vf.
+// D = off[6] = -off[0] (a 3D stencil's plane of D rows; off[2] = -1,
+// off[4] = 1).  The plan (cg_zwalk_plan, in col.zw_*) cuts every plane into
+// zw_ncol columns of zw_tw consecutive rows (the last one possibly narrower)
+// and the zw_nz planes of each column into zw_nseg segments; workgroup b
+// takes one segment and walks it plane by plane, lane t taking in-plane row
+// column * zw_tw + t, so its next rows are the plane above its current ones,
+// lane for lane.  Segments are numbered column by column and each XCD takes
+// a contiguous range of them, so a column's segments and its neighbouring
+// columns (the +-N gathers) share an L2.  The block keeps, per lane, the
+// gathered entries of its column in planes z - 1, z and z + 1 in an LDS
+// ring: the +D gathers of plane z are plane z + 1's own entries, so a
+// segment reads each plane's entries from memory once (plus the plane
+// below its first one); the -D, own and (inside the column) +-1 gathers
+// come from the ring, the +-N gathers and the column-edge +-1 from memory.
+// ofz(i, g) builds a row's own inputs from its gathered entries g.  The
+// terms and their order are those of dia_rows, so every row's sum is
+// bitwise the same.  With col.sym the -D entry of a row is the +D entry of
+// the row one plane below, which this lane loaded for its previous plane: it
+// is carried in a register, and the -1 and -N entries are read from their
+// mirrors as in dia_rows.  The values of the +-1 and +-N diagonals then go
+// through vk (loads that keep their lines cached, since the mirrored reads
+// come back to them), the others through vf.  With one segment per column
+// and 256-row columns this is the assignment of the tiles in rounds
+// (xcd_tiles), so the partial sums are also those of the other forms.
 template <typename T, typename VF, typename VK, typename GF, typename CF, typename OF,
           typename RF, typename PRE, typename POST, typename G>
-__device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
+__device__ __forceinline__ bool dia_rows_zw(bool active, int64_t n,
                                             const ColSrc<kColDiaMajor> &col, VF vf, VK vk, GF gf,
                                             CF cf, OF ofz, RF rf, PRE pre, POST post,
                                             G (*ring)[kTileRows]) {
     constexpr int ND = 7, d0 = 3;
     const int tid = threadIdx.x;
-    auto row_of = [&](int64_t t) -> int64_t {
-        const int64_t row0 = t * kTileRows;
-        const int64_t left = n - row0;
-        return row0 + (tid < left ? tid : left - 1);
-    };
-    auto clampc = [&](int64_t c) -> int32_t {
-        return (int32_t)(c < 0 ? 0 : (c >= n ? n - 1 : c));
+    const int64_t D = col.off[6];
+    // this workgroup's segment
+    const int xcd = blockIdx.x % kNumXcd, local = blockIdx.x / kNumXcd;
+    const int64_t total = (int64_t)col.zw_ncol * col.zw_nseg;
+    const int64_t lo = total * xcd / kNumXcd, hi = total * (xcd + 1) / kNumXcd;
+    const int64_t seg = lo + local;
+    if (seg >= hi) active = false;
+    const int64_t c = active ? seg / col.zw_nseg : 0;
+    const int64_t sg = active ? seg % col.zw_nseg : 0;
+    const int64_t z0 = active ? col.zw_nz * sg / col.zw_nseg : 0;
+    const int64_t z1 = active ? col.zw_nz * (sg + 1) / col.zw_nseg : 0;
+    const int64_t j0 = c * col.zw_tw;
+    const int64_t wl = D - j0 < col.zw_tw ? D - j0 : col.zw_tw;  // lanes of this column
+    const bool lane_on = tid < wl;
+    const int64_t j = j0 + (lane_on ? tid : wl - 1);  // in-plane row (clamped)
+    auto clampc = [&](int64_t x) -> int32_t {
+        return (int32_t)(x < 0 ? 0 : (x >= n ? n - 1 : x));
     };
     int prev = 2, cur = 0, next = 1;
-    int64_t t = tr.first;
-    T vd = T(0);  // col.sym: the previous tile's +D entry
+    T vd = T(0);  // col.sym: the previous plane's +D entry
     bool carried = false;
-    if (t < tr.end) {
-        ring[prev][tid] = G{};  // the first plane's -D neighbours are padding
-        ring[cur][tid] = gf((int32_t)row_of(t));
+    if (z0 < z1) {
+        // the plane below the first one: padding below the grid
+        ring[prev][tid] = z0 > 0 ? gf((int32_t)((z0 - 1) * D + j)) : G{};
+        ring[cur][tid] = gf((int32_t)(z0 * D + j));
     }
     pre();
     __syncthreads();
     if (!post()) return false;
-    for (; t < tr.end; t += tr.stride) {
-        const int64_t i = row_of(t);
+    for (int64_t z = z0; z < z1; ++z) {
+        const int64_t i = z * D + j;
         T v[ND];
         G g[ND];
 #pragma unroll
@@ -316,7 +340,7 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
         g[1] = gf(clampc(i + col.off[1]));
         g[5] = gf(clampc(i + col.off[5]));
         g[2] = tid > 0 ? ring[cur][tid - 1] : gf(clampc(i - 1));
-        g[4] = tid < kTileRows - 1 ? ring[cur][tid + 1] : gf(clampc(i + 1));
+        g[4] = tid < wl - 1 ? ring[cur][tid + 1] : gf(clampc(i + 1));
         g[0] = ring[prev][tid];
         g[3] = ring[cur][tid];
         const auto own = ofz(i, g[3]);
@@ -324,8 +348,7 @@ __device__ __forceinline__ bool dia_rows_zw(const TileRange &tr, int64_t n,
         T s = T(0);
 #pragma unroll
         for (int q = 0; q < ND; ++q) s = fma(v[q], cf(g[q]), s);
-        const int64_t r = t * kTileRows + tid;
-        if (r < n) rf(r, s, own, v[d0]);
+        if (lane_on) rf(i, s, own, v[d0]);
         // the next plane's ring slot is complete, and this plane's reads of
         // the slot about to be overwritten are done
         __syncthreads();

@@ -14,6 +14,7 @@ negated offsets).  n = 5000 keeps every solve on the grid kernels.
 import numpy as np
 import pytest
 
+import oracle as O
 import workloads as W
 from gpu_helpers import FP_TOL, banner, gpu_forward_adjoint, oracle_forward_adjoint, relerr
 
@@ -165,33 +166,86 @@ def test_unsymmetric_values_read_every_diagonal(hip):
             assert np.array_equal(np.asarray(u)[0], np.asarray(v)[s]), s
 
 
-def zwalk_problem(Z=16, seed=21):
-    """Lognormal-kappa diffusion on a 512 x 512 x Z grid: seven diagonals
-    with offsets 0, +-1, +-512, +-262144, and 262144 rows = 1024 tiles of 256
-    rows per plane -- the case where the CG kernel walks each block's column
-    along z with the plane above and below in LDS (tiles go in rounds of 1024
-    once there are 16 rounds, Z >= 16)."""
+def zwalk_problem(Z=16, seed=21, NX=512, NY=512):
+    """Lognormal-kappa diffusion on an NX x NY x Z grid: seven diagonals
+    with offsets 0, +-1, +-NX, +-NX*NY.  At 512 x 512 x 16 a plane is 1024
+    columns of 256 rows, one per workgroup, each walked over all 16 planes
+    (the tiles' order in rounds, so the partial sums are those of the other
+    forms); at 90 x 90 x 520 a plane of 8100 rows is 31 columns of 254 rows
+    and one of 226, each column's 520 planes cut into 32 segments of 16 or
+    17."""
     rng = np.random.default_rng(seed)
-    dims = (512, 512, Z)
-    n = 512 * 512 * Z
+    dims = (NX, NY, Z)
+    n = NX * NY * Z
     kap = np.exp(rng.standard_normal(n))
     rp, col, val = W.varcoef_diffusion(dims, kap)
     b = rng.standard_normal(n)[None, :]
     xt = rng.uniform(-1.0, 1.0, n)[None, :]
-    return W.Problem(f"diffusion_512x512x{Z}", n, rp, col, val, b, xt, method="cg",
+    return W.Problem(f"diffusion_{NX}x{NY}x{Z}", n, rp, col, val, b, xt, method="cg",
                      precond="jacobi", tol=1e-10, maxit=1000)
 
 
+def zwalk_plan(n, D):
+    """The z-walk plan the library derives for a 3D seven-point operator
+    (restated): columns of at most 256 rows, segments per column from the
+    1024-workgroup grid, at least 16 planes per segment."""
+    tiles = (n + 255) // 256
+    grid = 8 * min(128, (tiles + 7) // 8)
+    ncol = (D + 255) // 256
+    tw = (D + ncol - 1) // ncol
+    nseg = grid // ncol
+    nz = n // D
+    ok = nseg >= 1 and nz // nseg >= 16
+    return ok, ncol, tw, nseg, nz
+
+
 def test_zwalk_conditions_hold():
-    """The pattern of zwalk_problem meets the z-walk's conditions (the rule
-    the library applies at launch, restated): 7 diagonals with off[2] = -1,
-    off[4] = 1 and off[6] = -off[0] = 1024 * 256, and at least 16 rounds of
-    1024 tiles."""
+    """The patterns of zwalk_problem meet the z-walk's conditions, and the
+    workloads of 100^3 (4 planes per segment) do not."""
     p = zwalk_problem()
     rows = np.repeat(np.arange(p.n, dtype=np.int64), np.diff(p.row_ptr))
     off = np.unique(p.col.astype(np.int64) - rows)
     assert list(off) == [-262144, -512, -1, 0, 1, 512, 262144]
-    assert (p.n + 255) // 256 >= 16 * 1024
+    assert zwalk_plan(p.n, 262144) == (True, 1024, 256, 1, 16)
+    assert zwalk_plan(90 * 90 * 520, 8100) == (True, 32, 254, 32, 520)
+    assert zwalk_plan(10 ** 6, 10 ** 4)[0] is False
+    assert zwalk_plan(512 ** 3, 512 ** 2) == (True, 1024, 256, 1, 512)
+
+
+def test_zwalk_ragged_columns_and_segments(hip):
+    """90 x 90 x 520 (4.2e6 rows): ragged columns and segments of 16 or 17
+    planes.  Fixed iteration counts against the oracle's iterates; the
+    converged forward + adjoint against the same solve on the caller's CSR
+    values (a different order of the partial sums, so to the solve's
+    precision, not bit for bit) and the oracle's true residuals."""
+    import torch
+    banner("z-walk: ragged columns and segments")
+    p = zwalk_problem(Z=520, seed=23, NX=90, NY=90)
+    for k in (1, 6, 7):
+        g = gpu_forward_adjoint(hip, p, maxit=k)
+        assert g["pattern"].iteration_form() == "diagonal-major"
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert g["info"]["iters"][0] == k == r.iters[0]
+        assert relerr(g["x"][0], r.x[0]) <= 1e-12, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= 1e-12, k
+        g["pattern"].close()
+    outs = []
+    for dmaj in (True, False):
+        d = {k: torch.from_numpy(v).cuda() for k, v in
+             (("rp", p.row_ptr), ("col", p.col), ("val", p.values), ("b", p.b), ("xt", p.x_t))}
+        pat = hip.Pattern(d["rp"], d["col"], diagonal_major=dmaj)
+        kw = dict(method="cg", precond="jacobi", tol=p.tol, maxit=p.maxit)
+        x, info = pat.solve(d["val"], d["b"], **kw)
+        gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
+        assert info["status"][0] == 0 and ainfo["status"][0] == 0
+        outs.append((x.cpu().numpy(), gv.cpu().numpy(), gb.cpu().numpy(), info, ainfo))
+        pat.close()
+    (x1, gv1, gb1, i1, a1), (x2, gv2, gb2, i2, a2) = outs
+    assert i1["form"] == "diagonal-major-symmetric"
+    assert abs(int(i1["iters"][0]) - int(i2["iters"][0])) <= 2
+    assert relerr(x1, x2) <= 1e-8 and relerr(gb1, gb2) <= 1e-8 and relerr(gv1, gv2) <= 1e-8
+    tr = O.true_relres(p.row_ptr, p.col, p.values, x1, p.b)[0]
+    assert tr <= 10 * p.tol, tr
 
 
 def test_zwalk_matches_oracle_iterates(hip):
