@@ -881,19 +881,24 @@ def main():
 
 
 def block_roofline(p, pat, val, b, x, opts, stream):
-    """The one-workgroup CG solver keeps p, x, r and M^-1 in LDS and the
-    matrix in registers, so its bound is LDS bandwidth.  Per row and
-    iteration it gathers S entries of p (S slots: the longest row) and
-    reads p, x, r, M^-1 for the updates and the dot products (S + 8 loads)
-    and stores x, r, p: (S + 11) values.  One forward solve is timed with
-    events on the stream it runs on; the peak is the LDS of the compute
+    """The one-workgroup CG solver keeps p and x in LDS (p is gathered by
+    every row's product) and r, M^-1, the row's own p and the matrix in
+    registers, so its bound is LDS bandwidth.  Per row and iteration it
+    gathers S entries of p (S slots: the longest row), stores the new p and
+    reads and writes x: S + 3 values; with fp64 and four rows per thread
+    M^-1 is read from LDS twice more (S + 5), and without the resident
+    matrix r and the own p as well (S + 11).  One forward solve is timed
+    with events on the stream it runs on; the peak is the LDS of the compute
     units the batch occupies (one workgroup of 1024 threads per unit)."""
     import torch
     sv = p.values.itemsize
     rows = np.diff(p.row_ptr)
-    S = int(rows.max())
-    S = 4 if S <= 4 else (S if S in (5, 6) else 8)
-    per_row = (S + 11) * sv
+    longest = int(rows.max())
+    S = 4 if longest <= 4 else (longest if longest in (5, 6) else 8)
+    rpt = (p.n + 1023) // 1024
+    resident = longest <= 8 and rpt * (S * (sv // 4) + (S + 1) // 2) <= 56
+    dreg = sv == 4 or rpt <= 2
+    per_row = (S + 3 + (0 if dreg else 2) + (0 if dreg or resident else 6)) * sv
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

@@ -515,18 +515,25 @@ __device__ __forceinline__ T block_row_dot(const T (&v)[SLOTS], CF colf, gptr<co
 }
 
 // Row ownership: thread t owns rows t, t + 1024, ... (RPT rows, interleaved
-// so the vector loads of a wavefront are consecutive).  The vectors p, x, r
-// and M^-1 live in LDS (p is gathered by every row's product anyway); only
-// the product q stays in registers.  With RESIDENT (every row fits the
-// slots) the thread's matrix entries are loaded once -- values with the
-// padding slots zeroed, columns packed two per register -- and kept in
-// registers for the whole solve, so the matrix is read from memory once per
-// solve instead of once per iteration.  Otherwise the entries are re-read
-// every iteration (the row offsets go through an empty asm so the compiler
-// cannot hoist the address arithmetic out of the iteration loop).  Products:
-// SLOTS slots per row, p gathered from LDS (neighbouring rows gather
-// neighbouring LDS words), entry-order sums; rows longer than SLOTS finish
-// with a loop.
+// so the vector accesses of a wavefront are consecutive).  The direction p
+// lives in LDS, where every row's product gathers it, and so does x (read
+// and written once per iteration); r, the row's own p and the product q of
+// the owned rows stay in the thread's registers (each is read and written
+// by its owner only), and so does M^-1 unless registers run short (fp64 with
+// four rows per thread: then it is read from LDS twice per iteration, and
+// without the resident matrix r and the row's own p are read from LDS too).
+// An iteration touches LDS S + 3 (S + 5; S + 11) times per row: the S
+// gathers of p, the store of the new p, x read and written (M^-1 read
+// twice; r read twice and written, p read three times).  With RESIDENT
+// (every row fits the slots) the thread's matrix entries are loaded once --
+// values with the padding slots zeroed, columns packed two per register --
+// and kept in registers for the whole solve, so the matrix is read from
+// memory once per solve instead of once per iteration.  Otherwise the
+// entries are re-read every iteration (the row offsets go through an empty
+// asm so the compiler cannot hoist the address arithmetic out of the
+// iteration loop).  Products: SLOTS slots per row, p gathered from LDS
+// (neighbouring rows gather neighbouring LDS words), entry-order sums; rows
+// longer than SLOTS finish with a loop.
 // FULL: n == RPT * kBlockSolveThreads, every owned row exists, so the row
 // loops carry no guard (a guard is a branch, and the compiler does not move
 // the next row's LDS accesses above it).
@@ -536,8 +543,10 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     const int64_t n = P.n, nnz = P.nnz;
     T *ps = reinterpret_cast<T *>(lds_raw);  // direction p (or x0 at the start)
     T *xs = ps + n;                          // iterate x
-    T *rs = xs + n;                          // residual r
-    T *ds = rs + n;                          // M^-1 (1 without preconditioner)
+    T *ds = xs + n;                          // M^-1 (1 without preconditioner), when in LDS
+    T *rs = ds + n;                          // r, when in LDS
+    constexpr bool DREG = sizeof(T) == 4 || RPT <= 2;  // M^-1 in registers
+    constexpr bool RREG = DREG || RESIDENT;            // r and own p in registers
     __shared__ double slots[4][3][kBW];
     const int sys = blockIdx.x;
     const int tid = threadIdx.x;
@@ -555,7 +564,23 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     constexpr int SR = RESIDENT ? 1 : RPT;
 
     int lo[SR], len[SR];  // row offsets (streaming mode only)
-    T qr[RPT];
+    T qr[RPT];            // product of the owned rows
+    T pr_[RREG ? RPT : 1];  // p of the owned rows (RREG)
+    T rr_[RREG ? RPT : 1];  // r of the owned rows (RREG)
+    T dr[DREG ? RPT : 1];  // M^-1 of the owned rows (DREG)
+    auto dinv = [&](int j, int i) -> T { return DREG ? dr[DREG ? j : 0] : ds[i]; };
+    auto rget = [&](int j, int i) -> T { return RREG ? rr_[RREG ? j : 0] : rs[i]; };
+    auto pget = [&](int j, int i) -> T { return RREG ? pr_[RREG ? j : 0] : ps[i]; };
+    auto pset = [&](int j, int i, T v) {
+        if (RREG) pr_[RREG ? j : 0] = v;
+        ps[i] = v;
+    };
+    auto rset = [&](int j, int i, T v) {
+        if (RREG)
+            rr_[RREG ? j : 0] = v;
+        else
+            rs[i] = v;
+    };
     T mv[MR][SLOTS];
     uint32_t mc[MR][PC];  // two 16-bit columns per register
     int bad = 0;
@@ -564,6 +589,8 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
         const int i = row_of(j);
         int l = 0, ln = 0;
         qr[j] = T(0);
+        if (RREG) rr_[RREG ? j : 0] = pr_[RREG ? j : 0] = T(0);
+        if (DREG) dr[DREG ? j : 0] = T(1);
         if (owned(i)) {
             l = (int)rp[i];
             ln = (int)(rp[i + 1] - rp[i]);
@@ -576,7 +603,10 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
                 bad |= (a == T(0));
                 d = T(1) / a;
             }
-            ds[i] = d;
+            if (DREG)
+                dr[DREG ? j : 0] = d;
+            else
+                ds[i] = d;
         }
         if (RESIDENT) {
             T v[SLOTS];
@@ -627,8 +657,8 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
         if (owned(i)) {
             const T bi = b[i];
             const T ri = P.use_x0 ? bi - qr[j] : bi;
-            rs[i] = ri;
-            const T zi = ds[i] * ri;
+            rset(j, i, ri);
+            const T zi = dinv(j, i) * ri;
             r0[0] += (double)ri * (double)zi;
             r0[1] += (double)ri * (double)ri;
             r0[2] += (double)bi * (double)bi;
@@ -638,7 +668,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int i = row_of(j);
-        if (owned(i)) ps[i] = ds[i] * rs[i];  // p_0 = z_0
+        if (owned(i)) pset(j, i, dinv(j, i) * rget(j, i));  // p_0 = z_0
     }
     const int any_bad = __syncthreads_or(bad);
     double rho = r0[0], rnorm2 = r0[1];
@@ -661,7 +691,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
-                if (owned(i)) pq[0] += (double)ps[i] * (double)qr[j];
+                if (owned(i)) pq[0] += (double)pget(j, i) * (double)qr[j];
             }
             block_sum<1>(pq, slots[slot]);  // every gather of p is done
             slot = (slot + 1) & 3;
@@ -675,10 +705,10 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
                 if (owned(i)) {
-                    xs[i] = fmaT(alpha, ps[i], xs[i]);
-                    const T ri = fmaT(-alpha, qr[j], rs[i]);
-                    rs[i] = ri;
-                    const T zi = ds[i] * ri;
+                    xs[i] = fmaT(alpha, pget(j, i), xs[i]);
+                    const T ri = fmaT(-alpha, qr[j], rget(j, i));
+                    rset(j, i, ri);
+                    const T zi = dinv(j, i) * ri;
                     red[0] += (double)ri * (double)zi;
                     red[1] += (double)ri * (double)ri;
                 }
@@ -696,7 +726,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
 #pragma unroll
             for (int j = 0; j < RPT; ++j) {
                 const int i = row_of(j);
-                if (owned(i)) ps[i] = fmaT(beta, ps[i], ds[i] * rs[i]);
+                if (owned(i)) pset(j, i, fmaT(beta, pget(j, i), dinv(j, i) * rget(j, i)));
             }
             __syncthreads();  // the new p is complete before the next product
         }
@@ -806,7 +836,7 @@ constexpr bool block_resident() {
 // or 8 (5 is the five-point stencil's exact width); longer rows stream.
 template <typename T, typename IT>
 hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipStream_t s) {
-    const size_t lds = 4 * (size_t)p.n * sizeof(T);  // p, x, r, M^-1
+    const size_t lds = 4 * (size_t)p.n * sizeof(T);  // p, x, M^-1, r
     const int rpt = (int)((p.n + kBlockSolveThreads - 1) / kBlockSolveThreads);
     const bool fits = max_len <= 8;
 #define SLA_BLOCK_LAUNCH(R, S)                                                                     \
