@@ -283,7 +283,140 @@ def _form_flag(args):
     return "" if args.column_form == "diagonal-major" else f" --column-form {args.column_form}"
 
 
+PRODUCT_KERNELS = ("spmv_kernel", "spmv_perm_kernel", "plan_spmv_kernel", "plan_finish_kernel",
+                   "plan_grad_kernel", "grad_kernel", "rowsum_kernel", "diag_vjp_kernel")
+CACHE_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCP_TCC_READ_REQ_sum",
+                  "TCP_TOTAL_CACHE_ACCESSES_sum")
+
+
+def product_model_bytes(op, p):
+    """Algorithmic bytes of one call of the product (op matvec) or its
+    backward pass (matvec_vjp: grad_x = A^T g and grad_values)."""
+    sv, sr = p.values.itemsize, p.row_ptr.itemsize
+    if op == "matvec":
+        return (p.nnz * (sv + 4) + (p.n + 1) * sr + 2 * p.n * sv) * p.batch
+    return (p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv) * p.batch
+
+
+def _product_table(d, counter, calls):
+    """{kernel (name with template arguments): (dispatches, mean of
+    `counter` per dispatch, total per call)} over the product's kernels,
+    and the calibration probes' readings."""
+    per, probes = {}, {}
+    for name, c in _dispatches(d):
+        for which in ("copy", "read", "write"):
+            if _is_probe(name, which) and counter in c:
+                probes[which] = max(probes.get(which, 0.0), c[counter])
+        short = name.split("(")[0].replace("void ", "")
+        if counter not in c or not any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
+            continue
+        e = per.setdefault(short, [0, 0.0])
+        e[0] += 1
+        e[1] += c[counter]
+    return {k: (n, v / n, v / calls) for k, (n, v) in per.items()}, probes
+
+
+def summarize_product_counters(args):
+    """Bytes past L2 of the product or its backward pass, per kernel and
+    per call, from the --pmc runs of bench.py --op OP --kernel-only K
+    (10 K calls): FETCH_SIZE, WRITE_SIZE, optionally the read-request sizes
+    and the L2 / L1 hit counters."""
+    p = load_problem(args)
+    dirs = args.summarize_counters
+    if len(dirs) not in (2, 3, 4):
+        raise SystemExit("--summarize-counters FETCH_DIR WRITE_DIR [SIZES_DIR [CACHE_DIR]]")
+    calls = 20
+    which = " --graph" if args.graph else f" --workload {args.workload}"
+    run = f"python3 bench.py --op {args.op} --kernel-only 2{which}"
+    fetch, f_pr = _product_table(dirs[0], "FETCH_SIZE", calls)
+    write, w_pr = _product_table(dirs[1], "WRITE_SIZE", calls)
+    f_fac = CALIB_BYTES / (f_pr["copy"] * 1024.0)
+    w_fac = CALIB_BYTES / (w_pr["copy"] * 1024.0)
+    model = product_model_bytes(args.op, p)
+    out = [
+        f"# Bytes past L2 of the {args.op} call, workload {p.name}",
+        "",
+        "Commands (repository root; OUT is any output folder):",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- {run}",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- {run}",
+        "  rocprofv3 --pmc " + " ".join(["TCC_EA0_RDREQ_sum"] + list(SIZE_COUNTERS)) +
+        f" --output-format csv -d OUT/pmc_sizes -o run -- {run}",
+        "  rocprofv3 --pmc " + " ".join(CACHE_COUNTERS) +
+        f" --output-format csv -d OUT/pmc_cache -o run -- {run}",
+        f"  python3 bench.py --op {args.op}{which} --summarize-counters OUT/pmc_fetch "
+        "OUT/pmc_write OUT/pmc_sizes OUT/pmc_cache",
+        "",
+        f"The run makes {calls} calls, then the probe library's 1 GiB copy, read and write;",
+        "FETCH_SIZE and WRITE_SIZE are scaled by 1 GiB over their reading of the copy.",
+        "",
+        f"op: {args.op}",
+        f"workload: {p.name}",
+        f"n: {p.n}",
+        f"nnz: {p.nnz}",
+        f"source_sha256: {sources_sha(['kernels_spmv.hip', 'spmv_tile.h', 'sla_internal.h'])}",
+        f"fetch_factor: {f_fac:.4f}",
+        f"write_factor: {w_fac:.4f}",
+        f"algorithmic_bytes_per_call: {model}",
+        "",
+        f"{'dispatches':>10} {'fetch_MB':>10} {'write_MB':>10}  kernel (per dispatch, scaled)",
+    ]
+    tot_f = tot_w = 0.0
+    for k in sorted(fetch, key=lambda k: -fetch[k][2]):
+        n, fk, fc = fetch[k]
+        wk = write.get(k, (0, 0.0, 0.0))
+        out.append(f"{n:10d} {fk * 1024 * f_fac / 1e6:10.2f} {wk[1] * 1024 * w_fac / 1e6:10.2f}  {k}")
+        tot_f += fc * 1024 * f_fac
+        tot_w += wk[2] * 1024 * w_fac
+    out += [
+        "",
+        f"fetch_bytes_per_call: {tot_f:.0f}",
+        f"write_bytes_per_call: {tot_w:.0f}",
+        f"bytes_past_l2_per_call: {tot_f + tot_w:.0f}",
+        f"traffic_over_algorithmic_bytes: {(tot_f + tot_w) / model:.3f}",
+    ]
+    if len(dirs) >= 3:
+        sized = {}
+        for name, c in _dispatches(dirs[2]):
+            if not all(k in c for k in SIZE_COUNTERS):
+                continue
+            short = name.split("(")[0].replace("void ", "")
+            if any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
+                e = sized.setdefault(short, [0, 0.0, [0.0, 0.0, 0.0]])
+                e[0] += 1
+                for i, (kc, sz) in enumerate(SIZE_COUNTERS.items()):
+                    e[1] += c[kc] * sz
+                    e[2][i] += c[kc]
+        out += ["", "Read requests past L2 by size (no calibration factor), per dispatch:",
+                f"{'read_MB':>10} {'req32':>10} {'req64':>10} {'req128':>10}  kernel"]
+        tot = 0.0
+        for k, (n, by, rq) in sorted(sized.items(), key=lambda kv: -kv[1][1]):
+            out.append(f"{by / n / 1e6:10.2f} {rq[0] / n:10.0f} {rq[1] / n:10.0f} "
+                       f"{rq[2] / n:10.0f}  {k}")
+            tot += by / calls
+        out += [f"sized_read_bytes_per_call: {tot:.0f}",
+                f"sized_read_over_scaled_fetch: {tot / tot_f:.4f}" if tot_f else ""]
+    if len(dirs) == 4:
+        cache = {}
+        for name, c in _dispatches(dirs[3]):
+            if not all(k in c for k in CACHE_COUNTERS):
+                continue
+            short = name.split("(")[0].replace("void ", "")
+            if any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
+                e = cache.setdefault(short, [0.0] * len(CACHE_COUNTERS))
+                for i, kc in enumerate(CACHE_COUNTERS):
+                    e[i] += c[kc]
+        out += ["", "L2 and L1 hit rates (TCC_HIT / (TCC_HIT + TCC_MISS); L1 requests to L2 over",
+                "L1 accesses):", f"{'l2_hit':>8} {'l1_to_l2':>9}  kernel"]
+        for k, e in sorted(cache.items()):
+            l2 = e[0] / max(1.0, e[0] + e[1])
+            l1 = e[2] / max(1.0, e[3])
+            out.append(f"{l2:8.3f} {l1:9.3f}  {k}")
+    print("\n".join(x for x in out if x is not None))
+
+
 def summarize_counters(args):
+    if args.op in ("matvec", "matvec_vjp"):
+        return summarize_product_counters(args)
     p = load_problem(args)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
                                                 p.values.itemsize, p.row_ptr.itemsize,
@@ -684,6 +817,18 @@ def bench_product(args, p):
     g = torch.from_numpy(rng.standard_normal((p.batch, p.n)).astype(p.values.dtype)).to(dev)
     y = torch.empty_like(x)
     sv, sr = p.values.itemsize, p.row_ptr.itemsize
+    if args.kernel_only:
+        for _ in range(args.kernel_only * 10):
+            if args.op == "matvec":
+                pat.matvec(val, x, out=y)
+            else:
+                pat.matvec_adjoint(val, x, g)
+        torch.cuda.synchronize()
+        probe_kernels(CALIB_BYTES, dev)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernel_only": args.kernel_only, "calls": args.kernel_only * 10,
+                          "calibration_bytes": CALIB_BYTES}))
+        return
     # a pattern with rows past the tile walker's slots (the graph) also runs
     # the row plan's kernels
     plan = "+plan_spmv_kernel+plan_finish_kernel" if args.graph else ""
@@ -697,11 +842,11 @@ def bench_product(args, p):
         # values + columns + row pointers once, g, x read, grad_x and
         # grad_values written
         model = p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv
-        # with diagonal masks one kernel makes both from A's own rows, else
-        # A^T x goes through the transpose map and the gradient is a second
-        # kernel
+        # with diagonal masks one kernel makes both from A's own rows; else a
+        # pass over A's rows writes grad_values and scatters the terms of
+        # A^T g to A^T's order, and a second pass sums A^T's rows
         kernel = ("diag_vjp_kernel" if pat.column_mode() == "diagonal"
-                  else "spmv_perm_kernel+grad_kernel" + plan + ("+plan_grad_kernel" if plan else ""))
+                  else "grad_kernel+rowsum_kernel" + ("+plan_grad_kernel" if plan else "") + plan)
     model *= p.batch
     # a call takes tens of microseconds: enough calls that the timed region
     # spans milliseconds, after warm-up calls that bring the clocks up

@@ -71,8 +71,9 @@ struct sla_ctx {
     void *rp_t = nullptr;
     int32_t *col_t = nullptr;
     int16_t *col16_t = nullptr;  // compact columns of A^T, or null
-    int32_t *perm = nullptr;
-    void *val_t = nullptr;
+    int32_t *perm = nullptr;     // A's position of each A^T entry
+    int32_t *pinv = nullptr;     // A^T's position of each A entry
+    void *val_t = nullptr;       // one system's values (or products) in A^T's order
     int slots = 8;   // gather slots per row (A), from its longest row
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
@@ -156,6 +157,7 @@ void release(sla_ctx *h) {
     (void)hipFree(h->col_t);
     (void)hipFree(h->col16_t);
     (void)hipFree(h->perm);
+    (void)hipFree(h->pinv);
     (void)hipFree(h->val_t);
     (void)hipFree(h->dia);
     for (auto &pm : h->plan_mem)
@@ -584,8 +586,8 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
         Operator op{h->rp, h->ca, h->slots, h->ia, h->it_slots, &h->plan};
         st = solve_all<T, IT>(h, op, val, gx, gb, oo, info, s);
     } else {
-        // A^T with values gathered through the transpose map, one system at
-        // a time into the handle's buffer
+        // A^T with its values put in A^T's order, one system at a time into
+        // the handle's buffer
         Operator op{h->rp_t, h->ca_t, h->slots_t, h->ia_t, h->it_slots_t, &h->plan_t};
         const int64_t B0 = h->batch;
         st = SLA_OK;
@@ -595,8 +597,8 @@ sla_status adjoint_all(sla_ctx *h, const T *val, const T *x, const T *gx, T *gva
         int64_t kl = 0;
         h->batch = 1;
         for (int64_t sys = 0; sys < B0; ++sys) {
-            hipError_t e = launch_gather<T>(h->perm, val + sys * nnz, reinterpret_cast<T *>(h->val_t),
-                                            nnz, s);
+            hipError_t e = launch_scatter<T>(h->pinv, val + sys * nnz,
+                                             reinterpret_cast<T *>(h->val_t), nnz, s);
             if (e != hipSuccess) {
                 h->batch = B0;
                 g_last_error = e;
@@ -806,9 +808,10 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
         HIP_TRY(dmalloc(h, &h->rp_t, sizeof(IT) * (n + 1)));
         HIP_TRY(dmalloc(h, &h->col_t, sizeof(int32_t) * nnz));
         HIP_TRY(dmalloc(h, &h->perm, sizeof(int32_t) * nnz));
+        HIP_TRY(dmalloc(h, &h->pinv, sizeof(int32_t) * nnz));
         HIP_TRY(dmalloc(h, &h->val_t, sizeof(T) * nnz));
         HIP_TRY(setup_transpose<IT>(rp, h->col, n, nnz, reinterpret_cast<IT *>(h->rp_t), h->col_t,
-                                    h->perm, tmp.scr, s));
+                                    h->perm, h->pinv, tmp.scr, s));
         h->has_t = true;
         HIP_TRY(setup_max_row<IT>(reinterpret_cast<const IT *>(h->rp_t), n, h->flag, &maxlen, s));
         h->slots_t = slots_for(maxlen);
@@ -1102,15 +1105,44 @@ sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, dou
 
 namespace {
 
-// y = A^T x for `batch` systems: through A's diagonal masks when it has them
-// (no transpose map read), else through the transpose map.
+// The backward pass and A^T products of the per-entry column forms go in two
+// passes (A's rows scatter the terms v_k g_i to A^T's order in the handle's
+// buffer, then A^T's rows are summed) one system at a time, for single
+// systems and for patterns of at least this many entries; smaller batches
+// read A^T's values through the transpose map in one launch for all.
+constexpr int64_t kScatterMinEntries = (int64_t)1 << 20;
+
+bool two_pass(const sla_ctx *h, int batch) {
+    return h->ca.mode != kColDiag && (batch == 1 || h->nnz >= kScatterMinEntries);
+}
+
+// For `batch` systems: grad_x = A^T g (when gx is not null) and grad_values
+// = g_i x_j on the pattern (when gv is not null).
 template <typename T, typename IT>
-hipError_t transposed_product(sla_ctx *h, const T *v, const T *x, T *y, int batch, hipStream_t s) {
-    if (h->ca.mode == kColDiag)
-        return launch_diag_vjp<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v, h->nnz, x,
-                                      nullptr, y, nullptr, h->n, h->nnz, batch, false, s);
-    return launch_spmv_perm<T, IT>(h->slots_t, reinterpret_cast<const IT *>(h->rp_t), h->ca_t,
-                                   h->perm, v, h->nnz, x, y, h->n, h->n, batch, s, &h->plan_t);
+hipError_t product_backward(sla_ctx *h, const T *v, const T *x, const T *g, T *gx, T *gv,
+                            int batch, hipStream_t s) {
+    const IT *rp = reinterpret_cast<const IT *>(h->rp);
+    const IT *rpt = reinterpret_cast<const IT *>(h->rp_t);
+    const int64_t n = h->n, nnz = h->nnz;
+    if (h->ca.mode == kColDiag)  // both outputs from one pass over A's rows
+        return launch_diag_vjp<T, IT>(rp, h->ca, v, nnz, g, x, gx, gv, n, nnz, batch, false, s);
+    if (gx && two_pass(h, batch)) {
+        T *c = reinterpret_cast<T *>(h->val_t);
+        for (int sys = 0; sys < batch; ++sys) {
+            hipError_t e = launch_terms_t<T, IT>(rp, h->ca, g + sys * n, v + sys * nnz, h->pinv, c,
+                                                 n, nnz, 1, s, &h->plan);
+            if (e == hipSuccess)
+                e = launch_rowsum<T, IT>(rpt, c, nnz, nullptr, nullptr, nullptr, gx + sys * n, n,
+                                         1, s, &h->plan_t);
+            if (e != hipSuccess) return e;
+        }
+    } else if (gx) {
+        hipError_t e = launch_rowsum<T, IT>(rpt, v, nnz, h->perm, h->col_t, g, gx, n, batch, s,
+                                            &h->plan_t);
+        if (e != hipSuccess) return e;
+    }
+    if (gv) return launch_grad<T, IT>(rp, h->ca, g, x, gv, n, nnz, batch, false, s, &h->plan);
+    return hipSuccess;
 }
 
 }  // namespace
@@ -1182,7 +1214,7 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x, void 
             const T *x = reinterpret_cast<const T *>(d_x) + s0 * h->n;
             T *y = reinterpret_cast<T *>(d_y) + s0 * h->n;
             if (transpose)
-                HIP_TRY(transposed_product<T, IT>(h, v, x, y, nb, s));
+                HIP_TRY((product_backward<T, IT>(h, v, nullptr, x, y, nullptr, nb, s)));
             else
                 HIP_TRY((launch_spmv<T, IT>(h->slots, reinterpret_cast<const IT *>(h->rp), h->ca,
                                             v, h->nnz, x, y, h->n, h->n, nb, s, &h->plan)));
@@ -1206,24 +1238,10 @@ sla_status sla_matvec_adjoint(sla_handle h, const void *d_values, const void *d_
             const int nb = (int)((h->batch - s0) < 65535 ? (h->batch - s0) : 65535);
             const T *v = reinterpret_cast<const T *>(d_values) + s0 * h->nnz;
             const T *gy = reinterpret_cast<const T *>(d_grad_y) + s0 * h->n;
-            if (h->ca.mode == kColDiag) {  // both outputs from one pass over A's rows
-                T *gx = d_grad_x ? reinterpret_cast<T *>(d_grad_x) + s0 * h->n : nullptr;
-                T *gv = d_grad_values ? reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz
-                                      : nullptr;
-                const T *x = d_x ? reinterpret_cast<const T *>(d_x) + s0 * h->n : nullptr;
-                HIP_TRY((launch_diag_vjp<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, v,
-                                                h->nnz, gy, x, gx, gv, h->n, h->nnz, nb, false,
-                                                s)));
-                continue;
-            }
-            if (d_grad_x)
-                HIP_TRY(transposed_product<T, IT>(
-                    h, v, gy, reinterpret_cast<T *>(d_grad_x) + s0 * h->n, nb, s));
-            if (d_grad_values)
-                HIP_TRY((launch_grad<T, IT>(reinterpret_cast<const IT *>(h->rp), h->ca, gy,
-                                            reinterpret_cast<const T *>(d_x) + s0 * h->n,
-                                            reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz,
-                                            h->n, h->nnz, nb, false, s, &h->plan)));
+            T *gx = d_grad_x ? reinterpret_cast<T *>(d_grad_x) + s0 * h->n : nullptr;
+            T *gv = d_grad_values ? reinterpret_cast<T *>(d_grad_values) + s0 * h->nnz : nullptr;
+            const T *x = d_x ? reinterpret_cast<const T *>(d_x) + s0 * h->n : nullptr;
+            HIP_TRY((product_backward<T, IT>(h, v, x, gy, gx, gv, nb, s)));
         }
         return SLA_OK;
     });

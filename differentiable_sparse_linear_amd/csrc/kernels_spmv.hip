@@ -27,6 +27,15 @@ __device__ __forceinline__ bool sys_stopped(const IterArgs<T, IT> *ind) {
     return ind && load_done(ind[blockIdx.y].st);
 }
 
+// s + a * b with the product rounded before the addition (no fused
+// multiply-add): the terms of A^T g are formed this way on every path, so
+// that the paths agree bit for bit.
+template <typename T>
+__device__ __forceinline__ T add_product(T s, T a, T b) {
+#pragma clang fp contract(off)
+    return s + a * b;
+}
+
 template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp, ColArgs ca,
                                                       const T *__restrict__ val, int64_t val_stride,
@@ -46,31 +55,13 @@ __global__ __launch_bounds__(kBlock) void spmv_kernel(const IT *__restrict__ rp,
         [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost(), plan_tiles);
 }
 
-// y = A^T x through the transpose map: rp/col describe A^T and the value of
-// A^T entry kt is val[perm[kt]].
-template <typename T, typename IT, int SLOTS, int CM>
-__global__ __launch_bounds__(kBlock) void spmv_perm_kernel(
-    const IT *__restrict__ rp, ColArgs ca, const int32_t *__restrict__ perm,
-    const T *__restrict__ val, int64_t val_stride, const T *__restrict__ x, T *__restrict__ y,
-    int64_t n, int64_t vec_stride, const uint8_t *plan_tiles) {
-    __shared__ RowLds<T, IT> sm;
-    const int sys = blockIdx.y;
-    const gptr<const T> v = glb(val + (int64_t)sys * val_stride);
-    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
-    const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
-    const gptr<const int32_t> pm = glb(perm);
-    spmv_rows<T, IT, SLOTS, SLOTS>(
-        xcd_tiles(tiles_of(n)), n, glb(rp), col_src<CM>(ca), sm, [&](IT k) { return v[pm[k]]; },
-        [&](int32_t c) { return xs[c]; }, PlainGather(), NoOwn(),
-        [&](int64_t i, T s, int, T) { ys[i] = s; }, NoPre(), NoPost(), plan_tiles);
-}
-
 // Backward pass of y = A x on a pattern with per-row diagonal masks, one row
 // i per thread, reading A's own rows (no transpose map):
 //  GX: gx[i] = (A^T g)_i.  Row i of A^T holds A[j][i] for j = i - dlt[q],
 //      stored when bit q of msk[j] is set, at position rp[j] + (set bits of
-//      msk[j] below q).  q runs downwards, so the terms are added in
-//      ascending j, the column order of A^T's row.  All NDT slots are
+//      msk[j] below q).  q runs downwards, so the terms A[j][i] g_j (each
+//      rounded, then added, from 0) are added in ascending j, the column
+//      order of A^T's row: the sums of rowsum_kernel.  All NDT slots are
 //      unrolled so every mask and row-pointer load of a row is in flight
 //      before its values are gathered.
 //  GV: gv[k] = g_i x_j for row i's stored entries (NEG: -g_i x_j, the
@@ -149,35 +140,57 @@ __global__ __launch_bounds__(kBlock) void diag_vjp_kernel(const IT *__restrict__
             T s = T(0);
 #pragma unroll
             for (int q = NDT - 1; q >= 0; --q) {
-                if (on[q]) s = fma(v[k[q]], gs[jj[q]], s);
+                if (on[q]) s = add_product(s, v[k[q]], gs[jj[q]]);
             }
             gxs[i] = s;
         }
     }
 }
 
-// grad[k] = -lambda[row(k)] * x[col[k]] (NEG; the solve's gradient on the
-// pattern) or g[row(k)] * x[col[k]] (the product's), for the per-entry column
-// forms (int32 or tile-relative int16; diagonal masks use diag_vjp_kernel).
-// Short tiles: each thread marks the tile-local row of its row's entries in
-// LDS, then the entries are written as one coalesced run.  Tiles that
-// plan_tiles flags are left to the row plan; other tiles past the stage take
-// one wavefront per row.
-template <typename T, typename IT, bool NEG, int CM>
+// One pass over A's entries by row, entry k of row i (g = g[i]), writing
+// one of:
+//  GV: the gradient on the pattern, grad[k] = g x[col[k]] (NEG: -lambda_i
+//      x_j, the solve's gradient with g = lambda; else the product's);
+//  SC: the terms of A^T g, c[pinv[k]] = val[k] g, each written to entry k's
+//      place among A^T's entries (pinv: A's entry -> A^T's), so that a
+//      second pass (rowsum_kernel) sums every row of A^T over consecutive
+//      memory.  The values are read in A's order, coalesced; the writes land
+//      at scattered 8-byte places, where reading val[perm[kt]] row by row of
+//      A^T would fetch a whole line per entry.
+// (Both in one pass measured slower than the two passes: the scattered
+// partial-line writes and the gradient's streaming writes contend.)  The
+// gradient is stored non-temporally: written once and not read here, it
+// would otherwise push the scattered terms and the inputs of the next pass
+// out of the Infinity Cache (measured on a 2^20-row power-law graph, the
+// backward pass with both outputs: 258 us with plain stores, 168 us with
+// these).  plan_grad_kernel stores it the same way.
+// Per-entry column forms (int32 or tile-relative int16; diagonal masks use
+// diag_vjp_kernel).  Short tiles: each thread marks the tile-local row of its
+// row's entries in LDS, then the entries go as one coalesced run.  Tiles
+// that plan_tiles flags are left to the row plan; other tiles past the stage
+// take one wavefront per row.  System blockIdx.y: g, x + y * n; grad, val,
+// c + y * nnz.
+template <typename T, typename IT, bool NEG, int CM, bool GV, bool SC>
 __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp, ColArgs ca,
-                                                      const T *__restrict__ lam,
+                                                      const T *__restrict__ g,
                                                       const T *__restrict__ x, T *__restrict__ grad,
-                                                      int64_t n, int64_t nnz,
+                                                      const T *__restrict__ val,
+                                                      const int32_t *__restrict__ pinv,
+                                                      T *__restrict__ c, int64_t n, int64_t nnz,
                                                       const uint8_t *plan_tiles) {
     static_assert(CM == kColWide || CM == kColTile16, "per-entry column forms");
+    static_assert(GV != SC, "one of the two outputs");
     __shared__ IT srp[kTileRows + 1];
-    __shared__ T slam[kTileRows];
+    __shared__ T sg[kTileRows];
     __shared__ uint16_t rid[kCap];
     const int sys = blockIdx.y;
     const ColSrc<CM> col = col_src<CM>(ca);
-    lam += (int64_t)sys * n;
-    x += (int64_t)sys * n;
-    grad += (int64_t)sys * nnz;
+    const gptr<const T> gs = glb(g + (int64_t)sys * n);
+    const gptr<const T> xs = glb(GV ? x + (int64_t)sys * n : x);
+    const gptr<T> gr = glb(GV ? grad + (int64_t)sys * nnz : grad);
+    const gptr<const T> vs = glb(SC ? val + (int64_t)sys * nnz : val);
+    const gptr<T> cs = glb(SC ? c + (int64_t)sys * nnz : c);
+    const gptr<const int32_t> pv = glb(pinv);
     const int tid = threadIdx.x;
     const TileRange tr = xcd_tiles(tiles_of(n));
     for (int64_t t = tr.first; t < tr.end; t += tr.stride) {
@@ -186,7 +199,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
         const int rows = left < kTileRows ? (int)left : kTileRows;
         if (tid < rows) {
             srp[tid] = rp[row0 + tid];
-            slam[tid] = lam[row0 + tid];
+            sg[tid] = gs[row0 + tid];
         }
         if (tid == 0) srp[rows] = rp[row0 + rows];
         __syncthreads();
@@ -199,29 +212,139 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
                     rid[e] = (uint16_t)tid;
             }
             __syncthreads();
-            int32_t c[kEpt];
+            int32_t cj[kEpt], pj[kEpt];
+            T vj[kEpt];
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
-                if (e < cnt) c[j] = col(base + e, row0);
+                if (e < cnt) {
+                    if constexpr (GV) cj[j] = col(base + e, row0);
+                    if constexpr (SC) {
+                        vj[j] = vs[base + e];
+                        pj[j] = pv[base + e];
+                    }
+                }
             }
 #pragma unroll
             for (int j = 0; j < kEpt; ++j) {
                 const int e = tid + j * kBlock;
                 if (e < cnt) {
-                    const T g = slam[rid[e]] * x[c[j]];
-                    grad[base + e] = NEG ? -g : g;
+                    const T gi = sg[rid[e]];
+                    if constexpr (GV) {
+                        const T p = gi * xs[cj[j]];
+                        __builtin_nontemporal_store(NEG ? -p : p, &gr[base + e]);
+                    }
+                    if constexpr (SC) {
+                        if ((uint32_t)pj[j] < (uint64_t)nnz) cs[pj[j]] = vj[j] * gi;
+                    }
                 }
             }
         } else if (!planned) {
             const int lane = tid & 63, wave = tid >> 6;
             for (int r = wave; r < rows; r += kWaves) {
-                const T li = slam[r];
+                const T gi = sg[r];
                 const IT lo = srp[r], hi = srp[r + 1];
                 for (IT k = lo + lane; k < hi; k += 64) {
-                    const T g = li * x[col(k, row0)];
-                    grad[k] = NEG ? -g : g;
+                    if constexpr (GV) {
+                        const T p = gi * xs[col(k, row0)];
+                        __builtin_nontemporal_store(NEG ? -p : p, &gr[k]);
+                    }
+                    if constexpr (SC) {
+                        const int32_t q = pv[k];
+                        if ((uint32_t)q < (uint64_t)nnz) cs[q] = vs[k] * gi;
+                    }
                 }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// y = A^T g summed row by row of A^T (rp: A^T's row pointers), each row's
+// terms A_ij g_i in entry order (ascending i), each rounded, then added from
+// 0.  The terms come from
+//  - !PERM: the scatter pass (grad_kernel / plan_grad_kernel with SC), which
+//    left them in A^T's order in t (one system per blockIdx.y, nnz apart);
+//  - PERM: A^T's values through the transpose map, t[perm[k]] * g[col[k]]
+//    (col: A^T's columns; values val_stride apart, g and y n apart), the
+//    form for a batch of systems in one launch.
+// A tile's terms are staged in LDS as one run, then thread t adds row t's
+// one after another (the order and the rounding of the row plan's short
+// blocks).  Tiles that plan_tiles flags are left to the row plan; other
+// tiles past the stage take one wavefront per row (lane-strided partial
+// sums, then a fixed-order wavefront sum).
+template <typename T, typename IT, bool PERM>
+__global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ rp,
+                                                        const T *__restrict__ t,
+                                                        int64_t t_stride,
+                                                        const int32_t *__restrict__ perm,
+                                                        const int32_t *__restrict__ col,
+                                                        const T *__restrict__ g,
+                                                        T *__restrict__ y, int64_t n,
+                                                        const uint8_t *plan_tiles) {
+    __shared__ IT srp[kTileRows + 1];
+    __shared__ T sc[kCap];
+    const int sys = blockIdx.y;
+    const gptr<const T> ts = glb(t + (int64_t)sys * t_stride);
+    const gptr<const T> gs = glb(PERM ? g + (int64_t)sys * n : g);
+    const gptr<const int32_t> pm = glb(perm);
+    const gptr<const int32_t> cl = glb(col);
+    const gptr<T> ys = glb(y + (int64_t)sys * n);
+    const int tid = threadIdx.x;
+    const TileRange tr = xcd_tiles(tiles_of(n));
+    for (int64_t tt = tr.first; tt < tr.end; tt += tr.stride) {
+        const int64_t row0 = tt * kTileRows;
+        const int64_t left = n - row0;
+        const int rows = left < kTileRows ? (int)left : kTileRows;
+        if (plan_tiles && plan_tiles[tt]) continue;  // the same in the whole workgroup
+        if (tid < rows) srp[tid] = rp[row0 + tid];
+        if (tid == 0) srp[rows] = rp[row0 + rows];
+        __syncthreads();
+        const IT base = srp[0];
+        const int64_t cnt = (int64_t)(srp[rows] - base);
+        if (cnt <= kCap) {
+            T v[kEpt];
+            if constexpr (PERM) {
+                int32_t pj[kEpt], cj[kEpt];
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j) {
+                    const int e = tid + j * kBlock;
+                    pj[j] = e < cnt ? pm[base + e] : 0;
+                    cj[j] = e < cnt ? cl[base + e] : 0;
+                }
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j) {
+                    const int e = tid + j * kBlock;
+                    v[j] = e < cnt ? ts[pj[j]] * gs[cj[j]] : T(0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j) {
+                    const int e = tid + j * kBlock;
+                    v[j] = e < cnt ? ts[base + e] : T(0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kEpt; ++j) sc[tid + j * kBlock] = v[j];
+            __syncthreads();
+            if (tid < rows) {
+                const int hi = (int)(srp[tid + 1] - base);
+                T s = T(0);
+                for (int e = (int)(srp[tid] - base); e < hi; ++e) s += sc[e];
+                ys[row0 + tid] = s;
+            }
+        } else {
+            const int lane = tid & 63, wave = tid >> 6;
+            for (int r = wave; r < rows; r += kWaves) {
+                T s = T(0);
+                for (IT k = srp[r] + lane; k < srp[r + 1]; k += 64) {
+                    if constexpr (PERM)
+                        s = add_product(s, ts[pm[k]], gs[cl[k]]);
+                    else
+                        s += ts[k];
+                }
+                s = wave_sum_t(s);
+                if (lane == 0) ys[row0 + r] = s;
             }
         }
         __syncthreads();
@@ -232,15 +355,18 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
 //
 // The tiles past the stage (PlanItem): workgroup b takes item b, system
 // blockIdx.y (values val_stride apart, vectors vec_stride apart, partials
-// nslots apart).  PERM: the operator is A^T through the transpose map, entry k's
-// value val[perm[k]].
+// nslots apart).  MODE kPlanA: the operator's own values; kPlanPerm: A^T
+// through the transpose map, entry k's value val[perm[k]]; kPlanSum: the
+// row sums of val alone (rowsum_kernel's rows past the stage; x unused).
+// The A^T modes round every term before adding it, as rowsum_kernel does.
+constexpr int kPlanA = 0, kPlanPerm = 1, kPlanSum = 2;
 
 // Products of one item.  Short block: the run's products v x[col] go to
 // LDS in one coalesced pass, then thread t adds row r0 + t's products in
 // entry order.  Long-row chunk: thread t takes entries t, t + 256, ... of
 // the chunk (all loads first, then an fma chain), a fixed-order workgroup
 // sum, y[row] or the chunk's partial.
-template <typename T, typename IT, bool PERM>
+template <typename T, typename IT, int MODE>
 __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
     const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
@@ -251,11 +377,11 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     __shared__ T wsum[kWaves];
     const int sys = blockIdx.y;
     const gptr<const T> v = glb(sys_values(val, val_stride, ind));
-    const gptr<const T> xs = glb(x + (int64_t)sys * vec_stride);
+    const gptr<const T> xs = glb(MODE == kPlanSum ? x : x + (int64_t)sys * vec_stride);
     const gptr<T> ys = glb(y + (int64_t)sys * vec_stride);
     const gptr<const int32_t> cg = glb(col);
     const gptr<const int32_t> pm = glb(perm);
-    auto vf = [&](int64_t k) { return PERM ? v[pm[k]] : v[k]; };
+    auto vf = [&](int64_t k) { return MODE == kPlanPerm ? v[pm[k]] : v[k]; };
     const PlanItem it = items[blockIdx.x];
     const int tid = threadIdx.x;
     const int64_t e0 = it.e0;
@@ -268,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
         px[j] = T(0);
         if (e < cnt) {
             pv[j] = vf(e0 + e);
-            px[j] = xs[cg[e0 + e]];
+            px[j] = MODE == kPlanSum ? T(1) : xs[cg[e0 + e]];
         }
     }
     if (it.kind == 0) {
@@ -288,7 +414,8 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     } else {
         T s = T(0);
 #pragma unroll
-        for (int j = 0; j < kPlanEpt; ++j) s = fma(pv[j], px[j], s);  // 0 * 0 past the chunk
+        for (int j = 0; j < kPlanEpt; ++j)  // 0 * 0 past the chunk
+            s = MODE == kPlanA ? fma(pv[j], px[j], s) : add_product(s, pv[j], px[j]);
         s = wave_sum_t(s);
         if ((tid & 63) == 0) wsum[tid >> 6] = s;
         __syncthreads();
@@ -327,26 +454,32 @@ __global__ __launch_bounds__(kBlock) void plan_finish_kernel(const PlanFin *__re
     if (lane == 0) y[(int64_t)sys * vec_stride + r.row] = s;
 }
 
-// The gradient on the pattern for one item: g[row(k)] x[col[k]] (NEG:
-// negated).  Short block: thread t marks row r0 + t's entries in LDS, then
-// the run is written coalesced; long-row chunk: one row, written coalesced.
-template <typename T, typename IT, bool NEG>
+// grad_kernel's pass (GV, SC, NEG as there) for one item.  Short block:
+// thread t marks row r0 + t's entries in LDS, then the run goes coalesced;
+// long-row chunk: one row, coalesced.
+template <typename T, typename IT, bool NEG, bool GV, bool SC>
 __global__ __launch_bounds__(kBlock) void plan_grad_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
-    const T *__restrict__ g, const T *__restrict__ x, T *__restrict__ grad, int64_t n,
+    const T *__restrict__ g, const T *__restrict__ x, T *__restrict__ grad,
+    const T *__restrict__ val, const int32_t *__restrict__ pinv, T *__restrict__ c, int64_t n,
     int64_t nnz) {
+    static_assert(GV != SC, "one of the two outputs");
     __shared__ uint16_t rid[kPlanCap];
     __shared__ T sg[kTileRows];
     const int sys = blockIdx.y;
     const gptr<const T> gs = glb(g + (int64_t)sys * n);
-    const gptr<const T> xs = glb(x + (int64_t)sys * n);
-    const gptr<T> gr = glb(grad + (int64_t)sys * nnz);
+    const gptr<const T> xs = glb(GV ? x + (int64_t)sys * n : x);
+    const gptr<T> gr = glb(GV ? grad + (int64_t)sys * nnz : grad);
+    const gptr<const T> vs = glb(SC ? val + (int64_t)sys * nnz : val);
+    const gptr<T> cs = glb(SC ? c + (int64_t)sys * nnz : c);
+    const gptr<const int32_t> pv = glb(pinv);
     const gptr<const int32_t> cg = glb(col);
     const PlanItem it = items[blockIdx.x];
     const int tid = threadIdx.x;
     const int64_t e0 = it.e0;
     const int cnt = (int)(it.e1 - e0);
-    if (it.kind == 0) {
+    const bool block = it.kind == 0;
+    if (block) {
         if (tid < it.r1 - it.r0) {
             const int64_t r = it.r0 + tid;
             sg[tid] = gs[r];
@@ -354,34 +487,47 @@ __global__ __launch_bounds__(kBlock) void plan_grad_kernel(
             for (int e = (int)(rp[r] - e0); e < hi; ++e) rid[e] = (uint16_t)tid;
         }
         __syncthreads();
+    }
+    const T g0 = block ? T(0) : gs[it.r0];
+    int32_t cj[kPlanEpt], pj[kPlanEpt];
+    T vj[kPlanEpt];
 #pragma unroll
-        for (int j = 0; j < kPlanEpt; ++j) {
-            const int e = tid + j * kBlock;
-            if (e < cnt) {
-                const T p = sg[rid[e]] * xs[cg[e0 + e]];
-                gr[e0 + e] = NEG ? -p : p;
+    for (int j = 0; j < kPlanEpt; ++j) {
+        const int e = tid + j * kBlock;
+        if (e < cnt) {
+            if constexpr (GV) cj[j] = cg[e0 + e];
+            if constexpr (SC) {
+                vj[j] = vs[e0 + e];
+                pj[j] = pv[e0 + e];
             }
         }
-    } else {
-        const T gi = gs[it.r0];
+    }
 #pragma unroll
-        for (int j = 0; j < kPlanEpt; ++j) {
-            const int e = tid + j * kBlock;
-            if (e < cnt) {
-                const T p = gi * xs[cg[e0 + e]];
-                gr[e0 + e] = NEG ? -p : p;
+    for (int j = 0; j < kPlanEpt; ++j) {
+        const int e = tid + j * kBlock;
+        if (e < cnt) {
+            const T gi = block ? sg[rid[e]] : g0;
+            if constexpr (GV) {
+                const T p = gi * xs[cj[j]];
+                __builtin_nontemporal_store(NEG ? -p : p, &gr[e0 + e]);
             }
+            if constexpr (SC) {
+                        if ((uint32_t)pj[j] < (uint64_t)nnz) cs[pj[j]] = vj[j] * gi;
+                    }
         }
     }
 }
 
+// out[pinv[k]] = val[k]: the values in A^T's entry order, read coalesced.
+// (Here and in the scatter pass a position outside [0, nnz), which only a
+// faulty map could hold, is skipped rather than written.)
 template <typename T>
-__global__ __launch_bounds__(kBlock) void gather_kernel(const int32_t *__restrict__ perm,
-                                                        const T *__restrict__ val,
-                                                        T *__restrict__ out, int64_t nnz) {
+__global__ __launch_bounds__(kBlock) void scatter_kernel(const int32_t *__restrict__ pinv,
+                                                         const T *__restrict__ val,
+                                                         T *__restrict__ out, int64_t nnz) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
     for (int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x; k < nnz; k += stride)
-        out[k] = val[perm[k]];
+        if ((uint32_t)pinv[k] < (uint64_t)nnz) out[pinv[k]] = val[k];
 }
 
 // Bit-for-bit equality (a signed zero differs from an unsigned one, a NaN
@@ -483,14 +629,14 @@ __global__ __launch_bounds__(64) void publish_kernel(const int32_t *ndone, int32
 
 inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
 
-// The plan's rows of y = A x (PERM: A^T through the transpose map), after
-// the tile kernel has done the others.
-template <typename T, typename IT, bool PERM>
+// The plan's rows of y = A x (MODE as for plan_spmv_kernel), after the tile
+// kernel has done the others.
+template <typename T, typename IT, int MODE>
 void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, const T *val,
                       int64_t val_stride, const T *x, T *y, int64_t vec_stride, int batch,
                       hipStream_t s, const IterArgs<T, IT> *ind = nullptr) {
     T *part = reinterpret_cast<T *>(pl.part);
-    plan_spmv_kernel<T, IT, PERM><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
+    plan_spmv_kernel<T, IT, MODE><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
         pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, ind);
     if (pl.nfin > 0)
         plan_finish_kernel<T, IT>
@@ -514,27 +660,8 @@ hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                                                                              ind)));
     }
     if (ps)
-        launch_plan_spmv<T, IT, false>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
-                                       batch, s, ind);
-    return hipGetLastError();
-}
-
-template <typename T, typename IT>
-hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
-                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                            int64_t vec_stride, int batch, hipStream_t s, const RowPlan *plan) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
-    const bool ps = planned(plan);
-    const uint8_t *pt = ps ? plan->tiles : nullptr;
-    if (!ps || !plan->all_tiles) {
-        SLA_DISPATCH_CM(ca.mode, SLA_DISPATCH_SLOTS(slots, spmv_perm_kernel<T, IT, kS, kC>
-                                                    <<<grid, kBlock, 0, s>>>(rp, ca, perm, val,
-                                                                             val_stride, x, y, n,
-                                                                             vec_stride, pt)));
-    }
-    if (ps)
-        launch_plan_spmv<T, IT, true>(*plan, rp, perm, val, val_stride, x, y, vec_stride, batch,
-                                      s);
+        launch_plan_spmv<T, IT, kPlanA>(*plan, rp, nullptr, val, val_stride, x, y, vec_stride,
+                                        batch, s, ind);
     return hipGetLastError();
 }
 
@@ -575,6 +702,27 @@ hipError_t launch_diag_vjp(const IT *rp, const ColArgs &ca, const T *val, int64_
     return hipGetLastError();
 }
 
+template <typename T, typename IT, bool NEG, bool GV, bool SC>
+void launch_grad_t(const IT *rp, const ColArgs &ca, const T *g, const T *x, T *grad,
+                   const T *val, const int32_t *pinv, T *c, int64_t n, int64_t nnz, int batch,
+                   hipStream_t s, const RowPlan *plan) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    const bool ps = planned(plan);
+    const uint8_t *pt = ps ? plan->tiles : nullptr;
+    if (ps && plan->all_tiles) {
+        // every tile is the plan's
+    } else if (ca.mode == kColTile16) {
+        grad_kernel<T, IT, NEG, kColTile16, GV, SC>
+            <<<grid, kBlock, 0, s>>>(rp, ca, g, x, grad, val, pinv, c, n, nnz, pt);
+    } else {
+        grad_kernel<T, IT, NEG, kColWide, GV, SC>
+            <<<grid, kBlock, 0, s>>>(rp, ca, g, x, grad, val, pinv, c, n, nnz, pt);
+    }
+    if (ps)
+        plan_grad_kernel<T, IT, NEG, GV, SC><<<dim3(plan->nitems, batch), kBlock, 0, s>>>(
+            plan->items, rp, plan->col, g, x, grad, val, pinv, c, n, nnz);
+}
+
 template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
                        int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s,
@@ -582,40 +730,56 @@ hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x
     if (ca.mode == kColDiag)
         return launch_diag_vjp<T, IT>(rp, ca, nullptr, 0, lam, x, nullptr, grad, n, nnz, batch,
                                       neg, s);
-    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
+    if (neg)
+        launch_grad_t<T, IT, true, true, false>(rp, ca, lam, x, grad, nullptr, nullptr, nullptr,
+                                                n, nnz, batch, s, plan);
+    else
+        launch_grad_t<T, IT, false, true, false>(rp, ca, lam, x, grad, nullptr, nullptr, nullptr,
+                                                 n, nnz, batch, s, plan);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_terms_t(const IT *rp, const ColArgs &ca, const T *g, const T *val,
+                          const int32_t *pinv, T *c, int64_t n, int64_t nnz, int batch,
+                          hipStream_t s, const RowPlan *plan) {
+    launch_grad_t<T, IT, false, false, true>(rp, ca, g, nullptr, nullptr, val, pinv, c, n, nnz,
+                                             batch, s, plan);
+    return hipGetLastError();
+}
+
+template <typename T, typename IT>
+hipError_t launch_rowsum(const IT *rp, const T *t, int64_t t_stride, const int32_t *perm,
+                         const int32_t *col, const T *g, T *y, int64_t n, int batch,
+                         hipStream_t s, const RowPlan *plan) {
     const bool ps = planned(plan);
+    const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
-#define SLA_GRAD(C)                                                                           \
-    if (neg)                                                                                  \
-        grad_kernel<T, IT, true, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt); \
-    else                                                                                      \
-        grad_kernel<T, IT, false, C><<<grid, kBlock, 0, s>>>(rp, ca, lam, x, grad, n, nnz, pt)
-    if (ps && plan->all_tiles) {
-        // every tile is the plan's
-    } else if (ca.mode == kColTile16) {
-        SLA_GRAD(kColTile16);
-    } else {
-        SLA_GRAD(kColWide);
-    }
-#undef SLA_GRAD
-    if (ps) {
-        const dim3 pg(plan->nitems, batch);
-        if (neg)
-            plan_grad_kernel<T, IT, true>
-                <<<pg, kBlock, 0, s>>>(plan->items, rp, plan->col, lam, x, grad, n, nnz);
+    if (!ps || !plan->all_tiles) {
+        if (perm)
+            rowsum_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(rp, t, t_stride, perm, col, g, y,
+                                                               n, pt);
         else
-            plan_grad_kernel<T, IT, false>
-                <<<pg, kBlock, 0, s>>>(plan->items, rp, plan->col, lam, x, grad, n, nnz);
+            rowsum_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(rp, t, t_stride, nullptr,
+                                                                nullptr, nullptr, y, n, pt);
+    }
+    if (ps) {
+        if (perm)
+            launch_plan_spmv<T, IT, kPlanPerm>(*plan, rp, perm, t, t_stride, g, y, n, batch, s);
+        else
+            launch_plan_spmv<T, IT, kPlanSum>(*plan, rp, nullptr, t, t_stride, nullptr, y, n,
+                                              batch, s);
     }
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s) {
+hipError_t launch_scatter(const int32_t *pinv, const T *val, T *out, int64_t nnz,
+                          hipStream_t s) {
     int64_t blocks = (nnz + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    gather_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(perm, val, out, nnz);
+    scatter_kernel<T><<<(unsigned)blocks, kBlock, 0, s>>>(pinv, val, out, nnz);
     return hipGetLastError();
 }
 
@@ -656,16 +820,18 @@ hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s) {
     template hipError_t launch_spmv<T, IT>(int, const IT *, const ColArgs &, const T *, int64_t, \
                                            const T *, T *, int64_t, int64_t, int, hipStream_t,   \
                                            const RowPlan *, const IterArgs<T, IT> *);           \
-    template hipError_t launch_spmv_perm<T, IT>(int, const IT *, const ColArgs &,               \
-                                                const int32_t *, const T *, int64_t, const T *,  \
-                                                T *, int64_t, int64_t, int, hipStream_t,         \
-                                                const RowPlan *);                                \
     template hipError_t launch_diag_vjp<T, IT>(const IT *, const ColArgs &, const T *, int64_t,  \
                                                const T *, const T *, T *, T *, int64_t, int64_t, \
                                                int, bool, hipStream_t);                          \
     template hipError_t launch_grad<T, IT>(const IT *, const ColArgs &, const T *, const T *,   \
                                            T *, int64_t, int64_t, int, bool, hipStream_t,       \
                                            const RowPlan *);                                    \
+    template hipError_t launch_terms_t<T, IT>(const IT *, const ColArgs &, const T *,           \
+                                              const T *, const int32_t *, T *, int64_t, int64_t, \
+                                              int, hipStream_t, const RowPlan *);                \
+    template hipError_t launch_rowsum<T, IT>(const IT *, const T *, int64_t, const int32_t *,  \
+                                             const int32_t *, const T *, T *, int64_t, int,      \
+                                             hipStream_t, const RowPlan *);                      \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, int64_t, T *, int64_t,        \
                                            SolveState *, int, hipStream_t);                      \
     template hipError_t launch_dia_pack<T, IT>(const IT *, const ColArgs &, const T *, int64_t, \
@@ -675,9 +841,9 @@ SLA_INST(float, int32_t)
 SLA_INST(float, int64_t)
 SLA_INST(double, int32_t)
 SLA_INST(double, int64_t)
-template hipError_t launch_gather<float>(const int32_t *, const float *, float *, int64_t,
+template hipError_t launch_scatter<float>(const int32_t *, const float *, float *, int64_t,
                                          hipStream_t);
-template hipError_t launch_gather<double>(const int32_t *, const double *, double *, int64_t,
+template hipError_t launch_scatter<double>(const int32_t *, const double *, double *, int64_t,
                                           hipStream_t);
 template hipError_t launch_zero_if<float>(const SolveState *, float *, int64_t, int, hipStream_t);
 template hipError_t launch_zero_if<double>(const SolveState *, double *, int64_t, int,

@@ -119,16 +119,20 @@ __global__ __launch_bounds__(kSetupThreads) void check_diag_kernel(const IT *__r
     raise_flag(bad, flag);
 }
 
-// col_t[k] = the row of A entry perm[k] (-1 for a position outside [0, m),
-// which only a faulty sort could leave, so that it shows in the map instead
-// of reading out of bounds)
+// col_t[k] = the row of A entry perm[k] and pinv[perm[k]] = k, the inverse
+// map (-1 in col_t for a position outside [0, m), which only a faulty sort
+// could leave, so that it shows in the map instead of reading or writing out
+// of bounds)
 __global__ __launch_bounds__(kSetupThreads) void col_t_kernel(const int32_t *__restrict__ perm,
                                                        const int32_t *__restrict__ rowidx,
-                                                       int32_t *__restrict__ col_t, int64_t m) {
+                                                       int32_t *__restrict__ col_t,
+                                                       int32_t *__restrict__ pinv, int64_t m) {
     const int64_t stride = (int64_t)gridDim.x * kSetupThreads;
     for (int64_t k = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x; k < m; k += stride) {
         const int64_t j = perm[k];
-        col_t[k] = j >= 0 && j < m ? rowidx[j] : -1;
+        const bool ok = j >= 0 && j < m;
+        col_t[k] = ok ? rowidx[j] : -1;
+        if (ok) pinv[j] = (int32_t)k;
     }
 }
 
@@ -671,7 +675,8 @@ hipError_t setup_col16(const IT *rp, const int32_t *col, int64_t n, int64_t nnz,
 
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
-                           int32_t *col_t, int32_t *perm, SetupScratch &scr, hipStream_t s) {
+                           int32_t *col_t, int32_t *perm, int32_t *pinv, SetupScratch &scr,
+                           hipStream_t s) {
     (void)rp;
     int bits = 1;
     while (bits < 31 && ((int64_t)1 << bits) < n) ++bits;
@@ -698,7 +703,7 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
     // keys[1] holds the sorted columns: the row of every entry of A^T
     scr.rowidx_t = scr.keys[1];
     rowptr_t_kernel<IT><<<blocks_for(nnz + 1), kSetupThreads, 0, s>>>(scr.rowidx_t, nnz, n, rp_t);
-    col_t_kernel<<<blocks_for(nnz), kSetupThreads, 0, s>>>(perm, scr.rowidx, col_t, nnz);
+    col_t_kernel<<<blocks_for(nnz), kSetupThreads, 0, s>>>(perm, scr.rowidx, col_t, pinv, nnz);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return hipStreamSynchronize(s);
 }
@@ -751,8 +756,8 @@ hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s) 
                                         const int32_t *, int16_t *, int32_t *, int32_t *,      \
                                         hipStream_t);                                          \
     template hipError_t setup_transpose<IT>(const IT *, const int32_t *, int64_t, int64_t,     \
-                                            IT *, int32_t *, int32_t *, SetupScratch &,        \
-                                            hipStream_t);
+                                            IT *, int32_t *, int32_t *, int32_t *,             \
+                                            SetupScratch &, hipStream_t);
 SLA_SETUP_INST(int32_t)
 SLA_SETUP_INST(int64_t)
 #undef SLA_SETUP_INST

@@ -398,11 +398,6 @@ hipError_t launch_spmv(int slots, const IT *rp, const ColArgs &ca, const T *val,
                        int64_t val_stride, const T *x, T *y, int64_t n, int64_t vec_stride,
                        int batch, hipStream_t s, const RowPlan *plan = nullptr,
                        const IterArgs<T, IT> *ind = nullptr);
-template <typename T, typename IT>
-hipError_t launch_spmv_perm(int slots, const IT *rp, const ColArgs &ca, const int32_t *perm,
-                            const T *val, int64_t val_stride, const T *x, T *y, int64_t n,
-                            int64_t vec_stride, int batch, hipStream_t s,
-                            const RowPlan *plan = nullptr);
 // Backward of y = A x through A's diagonal masks (ca.mode == kColDiag), from
 // A's own rows: gx = A^T g (when gx is not null, values val_stride apart) and
 // gv[k] = g_i x_j on the pattern (when gv is not null; -g_i x_j with neg),
@@ -416,8 +411,26 @@ template <typename T, typename IT>
 hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x, T *grad,
                        int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s,
                        const RowPlan *plan = nullptr);
+// A^T g for the per-entry column forms, first pass over A's rows: c[pinv[k]]
+// = val[k] g_i, the terms in A^T's entry order (pinv: A's entry -> A^T's); g
+// n apart, val and c nnz apart.
+template <typename T, typename IT>
+hipError_t launch_terms_t(const IT *rp, const ColArgs &ca, const T *g, const T *val,
+                          const int32_t *pinv, T *c, int64_t n, int64_t nnz, int batch,
+                          hipStream_t s, const RowPlan *plan = nullptr);
+// y = A^T g row by row of A^T (rp, plan: A^T's row pointers and row plan),
+// every row's terms rounded and added in entry order: the terms the scatter
+// pass left in t (perm null; t_stride apart), or A's values t through the
+// transpose map perm with A^T's columns col and g (values t_stride apart,
+// g and y n apart).
+template <typename T, typename IT>
+hipError_t launch_rowsum(const IT *rp, const T *t, int64_t t_stride, const int32_t *perm,
+                         const int32_t *col, const T *g, T *y, int64_t n, int batch,
+                         hipStream_t s, const RowPlan *plan = nullptr);
+// out[pinv[k]] = val[k]: one system's values in A^T's entry order.
 template <typename T>
-hipError_t launch_gather(const int32_t *perm, const T *val, T *out, int64_t nnz, hipStream_t s);
+hipError_t launch_scatter(const int32_t *pinv, const T *val, T *out, int64_t nnz,
+                          hipStream_t s);
 // Diagonal-major copy of the CSR values of nsys systems (val_stride apart):
 // out[s][q * n + i] = the entry of row i on diagonal q (bit q of msk[i]), 0
 // where the row lacks it.  With st (cols.sym set: mirrored offsets), the
@@ -591,10 +604,12 @@ template <typename IT>
 hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s);
 // The transpose map of a valid pattern whose row index is in scr.rowidx:
 // rp_t [n+1], col_t [nnz] (row of each A^T entry), perm [nnz] (A's position
-// of each A^T entry); scr.rowidx_t is left pointing at the row of every A^T
-// entry.  Synchronizes `s`.
+// of each A^T entry) and pinv [nnz] (A^T's position of each A entry);
+// scr.rowidx_t is left pointing at the row of every A^T entry.  Synchronizes
+// `s`.
 template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
-                           int32_t *col_t, int32_t *perm, SetupScratch &scr, hipStream_t s);
+                           int32_t *col_t, int32_t *perm, int32_t *pinv, SetupScratch &scr,
+                           hipStream_t s);
 
 }  // namespace sla

@@ -114,8 +114,11 @@ typedef struct {
  *   d_row_ptr   [n+1] device array of row_ptr_type (borrowed)
  *   d_col       [nnz] device int32 column indices (borrowed)
  *   flags       SLA_CREATE_TRANSPOSE: build the map of A^T (needed by
- *               sla_matvec with transpose = 1 and by the BiCGStab adjoint);
- *               requires nnz < 2^31.
+ *               sla_matvec with transpose = 1, by grad_x of
+ *               sla_matvec_adjoint and by the BiCGStab adjoint): A^T's row
+ *               pointers and rows, A's position of each A^T entry and A^T's
+ *               position of each A entry (12 bytes per entry), and one
+ *               system's buffer of nnz values; requires nnz < 2^31.
  *               SLA_CREATE_WIDE_COLUMNS: read the caller's int32 columns in
  *               every product.  Without it the handle also keeps a compact
  *               copy (each column as an int16 offset from the first row of
@@ -165,6 +168,12 @@ sla_status sla_destroy(sla_handle h);
  * sla_matvec -- y[s] = A_s x[s] (transpose = 0) or A_s^T x[s] (transpose = 1)
  * for every system s of the batch.  d_values [batch][nnz], d_x and d_y
  * [batch][n]; d_y must not alias d_x.  Asynchronous on `stream`.
+ * A^T x sums each row of A^T in ascending row order of A, every term
+ * A_ij x_i rounded before it is added (bitwise the same through every
+ * storage form and launch shape).  Without diagonal masks, a single system
+ * (or any batch on a pattern of at least 2^20 entries) goes in two passes,
+ * one system at a time: the terms are written to A^T's order in the
+ * handle's buffer, then A^T's rows are summed.
  */
 sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x,
                       void *d_y, int32_t transpose, void *stream);
@@ -175,7 +184,8 @@ sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x,
  * explainer, Methodology section 1) for an upstream gradient
  * d_grad_y[s] = dL/dy:
  *   d_grad_x [batch][n]        = A_s^T grad_y[s]  (needs SLA_CREATE_TRANSPOSE;
- *                                 must not alias d_grad_y)
+ *                                 must not alias d_grad_y; bitwise the
+ *                                 sla_matvec transpose = 1 result)
  *   d_grad_values [batch][nnz] = grad_y[s][row(k)] * x[s][col(k)] for every
  *                                 stored entry k (needs d_x)
  * Either output may be NULL (not both).  d_values, d_x, d_grad_y are inputs

@@ -1,6 +1,12 @@
 """Patterns with long rows: the row plan of the stand-alone products and the
 gradient.
 
+The backward pass and the A^T products of a single system (or of any batch
+on a pattern of at least 2^20 entries) go in two passes: A's rows scatter
+the terms v_k g_i to A^T's entry order, then A^T's rows are summed; smaller
+batches read A^T's values through the transpose map (the 2^16-row batch of
+three).
+
 Tiles whose entries exceed the tile walker's LDS stage, or that hold a row
 longer than its gather slots, are covered by a plan built at set-up: short
 blocks (rows of at most 64 entries, at most 2048 entries per block) and long
@@ -69,6 +75,9 @@ CASES = {
     "powerlaw_2^18": lambda: powerlaw(1 << 18, 5),
     "powerlaw_2^16_batch3_fp32": lambda: powerlaw(1 << 16, 6, batch=3, dtype=np.float32),
     "powerlaw_2^16_int64": lambda: powerlaw(1 << 16, 7, index=np.int64),
+    # A^T products in two passes one system after another (2.2e6 entries)
+    "powerlaw_2^18_batch2": lambda: powerlaw(1 << 18, 8, batch=2),
+    "powerlaw_2^16_fp32": lambda: powerlaw(1 << 16, 9, dtype=np.float32),
     # rows of 8 / 9 entries (the walker's slots), 64 / 65 (a short block's rows)
     "lengths_at_limits": lambda: lengths_pattern(9000, [3, 8, 9, 64, 65, 3, 3, 2, 1], {}, 3),
     # one chunk of 2048 exactly, one entry more, two chunks exactly, one
@@ -88,23 +97,34 @@ def test_spmv_both_directions(hip, case):
     _spmv_case(hip, p, transpose=True)
 
 
-@pytest.mark.parametrize("case", ["powerlaw_2^16_batch3_fp32", "chunk_edges", "star_20000"])
+@pytest.mark.parametrize("case", ["powerlaw_2^16_batch3_fp32", "powerlaw_2^18_batch2",
+                                  "powerlaw_2^16_fp32", "chunk_edges", "star_20000"])
 def test_matvec_adjoint(hip, case):
     banner(f"row plan matvec adjoint {case}")
     _vjp_case(hip, CASES[case]())
 
 
 def test_repeat_is_bitwise(hip):
-    """The plan's sums run in a fixed order: repeated products agree bit for bit."""
+    """The plan's sums run in a fixed order: repeated products agree bit for
+    bit, and the backward pass's grad_x is the A^T product's bits whether or
+    not grad_values is made in the same pass."""
     banner("row plan determinism")
     p = powerlaw(1 << 18, 5)
     d = to_dev(p)
     pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
-    x = torch.from_numpy(np.random.default_rng(2).standard_normal((1, p.n))).cuda()
-    y0, t0 = pat.matvec(d["val"], x), pat.matvec(d["val"], x, transpose=True)
+    rng = np.random.default_rng(2)
+    x = torch.from_numpy(rng.standard_normal((1, p.n))).cuda()
+    g = torch.from_numpy(rng.standard_normal((1, p.n))).cuda()
+    y0, t0 = pat.matvec(d["val"], x), pat.matvec(d["val"], g, transpose=True)
+    gv0, gx0 = pat.matvec_adjoint(d["val"], x, g)
     for _ in range(3):
         assert torch.equal(pat.matvec(d["val"], x), y0)
-        assert torch.equal(pat.matvec(d["val"], x, transpose=True), t0)
+        assert torch.equal(pat.matvec(d["val"], g, transpose=True), t0)
+        gv, gx = pat.matvec_adjoint(d["val"], x, g)
+        assert torch.equal(gv, gv0) and torch.equal(gx, gx0)
+    _, gx1 = pat.matvec_adjoint(d["val"], x, g, need_grad_values=False)
+    gv1, _ = pat.matvec_adjoint(d["val"], x, g, need_grad_x=False)
+    assert torch.equal(gx0, t0) and torch.equal(gx1, t0) and torch.equal(gv1, gv0)
 
 
 def test_cg_solve_and_adjoint_on_graph(hip):
