@@ -80,7 +80,7 @@ struct sla_ctx {
     int it_slots = 8, it_slots_t = 8;  // slots (or diagonals) of the iteration form
     RowPlan plan, plan_t;        // tiles past the LDS stage, of A and of A^T (or empty)
     void *plan_mem[2][4] = {};   // their items, split rows, partial sums and tile flags
-    int64_t gbatch = 1;          // systems per grid CG launch
+    int64_t gbatch = 1;          // systems per grid launch
     void *vec = nullptr;         // [kNumVec][gbatch][n]
     SolveState *st = nullptr;
     double *part = nullptr;      // [gbatch][kPartStride]
@@ -217,8 +217,8 @@ static bool mirrored(const ColArgs &c) {
     return m;
 }
 
-// nsys consecutive systems on the grid path (nsys <= gbatch; 1 for
-// BiCGStab and in profile mode): fill the argument block, run init, then
+// nsys consecutive systems on the grid path (nsys <= gbatch; 1 in profile
+// mode and for the BiCGStab adjoint): fill the argument blocks, run init, then
 // replay/launch iteration chunks until the device reports every system done.
 template <typename T, typename IT>
 sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const T *b, T *x,
@@ -322,7 +322,7 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     } else if (cg) {
         HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, nsys, s));
     } else {
-        HIP_TRY(launch_bicg_init<T, IT>(ad, n, s));
+        HIP_TRY(launch_bicg_init<T, IT>(ad, n, nsys, s));
     }
 
     // split BiCGStab: half h of iteration k (0: updates, p_k -> v_k,
@@ -332,11 +332,11 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
         hipError_t e;
         const T *in = h ? a.s : a.p[(k + 1) & 1];
         T *out = h ? a.t : a.v[(k + 1) & 1];
-        if ((e = launch_bicg_split<T, IT>(2 * h, ad, n, ss)) != hipSuccess) return e;
-        if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, nullptr, 0, in, out, n, n, 1, ss,
+        if ((e = launch_bicg_split<T, IT>(2 * h, ad, n, nsys, ss)) != hipSuccess) return e;
+        if ((e = launch_spmv<T, IT>(op.slots, a.rp, op.cols, nullptr, 0, in, out, n, n, nsys, ss,
                                     op.plan, ad)) != hipSuccess)
             return e;
-        return launch_bicg_split<T, IT>(2 * h + 1, ad, n, ss);
+        return launch_bicg_split<T, IT>(2 * h + 1, ad, n, nsys, ss);
     };
 
     // iteration k; CG launches carry the iteration's parity
@@ -354,8 +354,8 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
             if ((e = bicg_half(ss, k, 0)) != hipSuccess) return e;
             return bicg_half(ss, k, 1);
         }
-        if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, ss)) != hipSuccess) return e;
-        return launch_bicg_st<T, IT>(slots, cm, ad, n, ss);
+        if ((e = launch_bicg_xpv<T, IT>(slots, cm, ad, n, nsys, ss)) != hipSuccess) return e;
+        return launch_bicg_st<T, IT>(slots, cm, ad, n, nsys, ss);
     };
 
     if (o.profile) {
@@ -390,9 +390,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                     ev += 2;
                 }
             } else {
-                HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, ad, n, 1, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_st<T, IT>(slots, cm, ad, n, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_st<T, IT>(slots, cm, ad, n, 1, s, &h->prof_ev[ev]));
                 ev += 2;
             }
             if ((k & 63) == 63 || k + 1 == launches) {
@@ -538,7 +538,7 @@ sla_status solve_all(sla_ctx *h, const Operator &op, const T *val, const T *b, T
             HIP_TRY(launch_block_cg<T, IT>(h->max_len, q, nb, s));
         }
     } else {
-        const int64_t G = cg && !o.profile ? std::min(h->gbatch, B) : 1;
+        const int64_t G = !o.profile ? std::min(h->gbatch, B) : 1;
         for (int64_t s0 = 0; s0 < B; s0 += G) {
             const int nsys = (int)std::min(G, B - s0);
             sla_status r = grid_solve_group<T, IT>(h, op, val + s0 * nnz, b + s0 * n, x + s0 * n,
@@ -866,8 +866,8 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
             nd = std::max(nd, (int)h->ca_t.nd);
         }
     }
-    // CG on a batch of systems too large for the one-workgroup solver
-    // advances up to gbatch of them per grid launch
+    // CG and BiCGStab on a batch of systems too large for the one-workgroup
+    // solver advance up to gbatch of them per grid launch
     if (h->batch > 1 && n > kBlockSolveMaxN)
         h->gbatch = std::max<int64_t>(1, std::min<int64_t>({h->batch, 65535, kGroupRows / n}));
     if (nd) HIP_TRY(dmalloc(h, &h->dia, sizeof(T) * (size_t)nd * n * h->gbatch));

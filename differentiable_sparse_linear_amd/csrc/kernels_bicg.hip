@@ -27,8 +27,11 @@
 // scalars are identical everywhere and no kernel needs a grid-wide fence.
 // p and v are double-buffered by iteration parity (the product kernels read
 // the old vectors at neighbouring rows while they write the new ones); r is
-// written only by bicg_xpv at j >= 1, whose gathers read s and t.  These
-// launches advance one system (a batch is solved one system after another).
+// written only by bicg_xpv at j >= 1, whose gathers read s and t.  A launch
+// advances a group of systems, one per row of the grid's y dimension, each
+// through its own argument block (vectors, state and partial sums of its
+// own); a system that has stopped ends each later launch at its first
+// barrier.
 #include "spmv_tile.h"
 
 namespace sla {
@@ -46,6 +49,7 @@ __device__ __forceinline__ bool vanished(double d) { return !(fabs(d) > 0.0); }
 // r = rhat = b - A x0 (or b with x = 0); partials ||r||^2 (= rhat.r) and b.b.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_init_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     const int64_t n = A->n;
     const gptr<const T> b = glb(A->b);
     const gptr<const T> ax0 = glb((const T *)A->q);
@@ -87,6 +91,7 @@ struct XpvOwn {
 template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
     __shared__ int seen[kWaves];
     const bool stopped = saw_stop(st, seen);
@@ -217,6 +222,7 @@ struct StOwn {
 template <typename T, typename IT, int SLOTS, int CM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
     __shared__ int seen[kWaves];
     const bool stopped = saw_stop(st, seen);
@@ -308,6 +314,7 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
 // bicg_xpv's tests and scalars, then x_j, r_j and p_j per row.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_split_xpv_u_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
     __shared__ int seen[kWaves];
     __shared__ double red[5][kWaves];
@@ -402,6 +409,7 @@ __global__ __launch_bounds__(kBlock) void bicg_split_xpv_u_kernel(const IterArgs
 // After v_j = A p_j: partials rhat.v_j and ||r_j||^2.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_split_xpv_w_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
     if (load_done(st) || st->half_exit) return;  // set by an earlier launch: uniform
     const int it = st->iter_a;
@@ -426,6 +434,7 @@ __global__ __launch_bounds__(kBlock) void bicg_split_xpv_w_kernel(const IterArgs
 // bicg_st's tests and alpha_j, then s = r_j - alpha_j v_j per row.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_split_st_u_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
     __shared__ int seen[kWaves];
     __shared__ double red[2][kWaves];
@@ -483,6 +492,7 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_u_kernel(const IterArgs<
 // After t = A s: partials t.s, t.t, s.s, rhat.s, rhat.t.
 template <typename T, typename IT>
 __global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<T, IT> *__restrict__ A) {
+    A += blockIdx.y;  // system blockIdx.y of the launch
     if (load_done(A->st)) return;  // set by an earlier launch: uniform
     const int64_t n = A->n;
     const gptr<const T> s = glb((const T *)A->s);
@@ -508,8 +518,9 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<
 // ------------------------------------------------------------------ launchers
 
 template <typename T, typename IT>
-hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    const int grid = grid_for_tiles(tiles_of(n));
+hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                             hipStream_t s) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
     switch (part) {
         case 0: bicg_split_xpv_u_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
         case 1: bicg_split_xpv_w_kernel<T, IT><<<grid, kBlock, 0, s>>>(a); break;
@@ -520,36 +531,37 @@ hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipS
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s) {
-    bicg_init_kernel<T, IT><<<grid_for_tiles(tiles_of(n)), kBlock, 0, s>>>(a);
+hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, int nsys, hipStream_t s) {
+    bicg_init_kernel<T, IT><<<dim3(grid_for_tiles(tiles_of(n)), nsys), kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)));
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
     SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kC>, grid,
                                                     dim3(kBlock), 0, s, ev, a));
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
-                          hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)));
+hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                           hipStream_t s, const hipEvent_t *ev) {
+    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
     SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kC>, grid,
                                                     dim3(kBlock), 0, s, ev, a));
     return hipGetLastError();
 }
 
 #define SLA_INST(T, IT)                                                                        \
-    template hipError_t launch_bicg_init<T, IT>(const IterArgs<T, IT> *, int64_t, hipStream_t); \
+    template hipError_t launch_bicg_init<T, IT>(const IterArgs<T, IT> *, int64_t, int,         \
+                                                hipStream_t);                                  \
     template hipError_t launch_bicg_xpv<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,    \
-                                               hipStream_t, const hipEvent_t *);               \
-    template hipError_t launch_bicg_st<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,     \
+                                               int, hipStream_t, const hipEvent_t *);          \
+    template hipError_t launch_bicg_st<T, IT>(int, int, const IterArgs<T, IT> *, int64_t, int, \
                                               hipStream_t, const hipEvent_t *);               \
-    template hipError_t launch_bicg_split<T, IT>(int, const IterArgs<T, IT> *, int64_t,       \
+    template hipError_t launch_bicg_split<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,  \
                                                  hipStream_t);
 
 SLA_INST(float, int32_t)

@@ -476,20 +476,21 @@ template <typename T, typename IT>
 hipError_t launch_cg_split_w(bool jac, bool init, const IterArgs<T, IT> *a, const IT *diagpos,
                              int64_t n, int nsys, int ph, hipStream_t s);
 
-// BiCGStab (grid path, one system)
+// BiCGStab (grid path; nsys systems, argument blocks a[0 .. nsys))
 template <typename T, typename IT>
-hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, int nsys, hipStream_t s);
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                           hipStream_t s, const hipEvent_t *ev = nullptr);
 // BiCGStab in six launches per iteration for operators with a row plan:
 // part 0 (first half's updates), [p -> v product], 1 (its partials),
 // 2 (second half's updates), [s -> t product], 3 (its partials)
 template <typename T, typename IT>
-hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, hipStream_t s);
+hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                             hipStream_t s);
 
 // *poll = *ndone, poll being the device address of pinned host memory
 hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s);

@@ -144,10 +144,12 @@ typedef struct {
  *               mirrors (sla_solve_info.form = 4).  Results are identical as
  *               long as the iterates stay finite.
  *               Other bits: SLA_ERR_ARG.
- * Workspace: CG on a batch of systems with n > 4096 advances a group of
- * min(batch, 65535, 2^21 / n) systems (at least 1) per grid launch, so the
- * solver vectors (11 per system) and the diagonal-major buffer are sized for
- * that group; BiCGStab and single systems use the first system's share.
+ * Workspace: CG and BiCGStab on a batch of systems with n > 4096 advance a
+ * group of min(batch, 65535, 2^21 / n) systems (at least 1) per grid
+ * launch, so the solver vectors (11 per system) and the diagonal-major
+ * buffer are sized for that group; single systems, profile-mode solves and
+ * the BiCGStab adjoint (which puts one system's values in A^T's order at a
+ * time) use the first system's share.
  * Long rows: when some 256-row tile of A (or of A^T) holds more than 2048
  * entries or a row longer than 8, the handle keeps a row plan for it (short
  * row blocks and chunks of long rows, 32 bytes each, a flag per tile and one

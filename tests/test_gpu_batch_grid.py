@@ -1,6 +1,7 @@
 """Batches of systems too large for the one-workgroup solver (n > 4096).
 
-CG advances a group of min(batch, 65535, 2^21 // n) systems per grid launch
+CG and BiCGStab advance a group of min(batch, 65535, 2^21 // n) systems per
+grid launch
 (one system per row of the launch grid's y dimension), each with its own
 vectors, state and partial sums; a system that stops ends each later launch
 at its first barrier while the rest of its group goes on.  Every system of
@@ -24,8 +25,9 @@ pytestmark = pytest.mark.gpu
 
 def _run(hip, p, x0=None):
     d = to_dev(p)
-    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p))
-    kw = dict(method="cg", precond=p.precond, tol=p.tol, maxit=p.maxit, check=False)
+    pat = hip.Pattern(d["rp"], d["col"], batch=p.batch, dtype=tdtype(p),
+                      build_transpose=p.method == "bicgstab")
+    kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit, check=False)
     xin = None if x0 is None else torch.from_numpy(np.ascontiguousarray(x0)).cuda()
     x, info = pat.solve(d["val"], d["b"], x0=xin, **kw)
     gv, gb, ainfo = pat.solve_adjoint(d["val"], x, x - d["xt"], **kw)
@@ -135,6 +137,70 @@ def test_several_groups_equal_singles(hip):
         assert np.array_equal(gb.cpu().numpy(), g["gb"]), rep
         assert np.array_equal(gv.cpu().numpy(), g["gv"]), rep
     pat.close()
+
+
+def _scaled_batch(q, B, seed):
+    """B systems on q's pattern, system s with its off-diagonal entries
+    scaled by 1 - 0.08 s (each its own iteration count), seeded right-hand
+    sides and targets."""
+    rows = np.repeat(np.arange(q.n), np.diff(q.row_ptr))
+    off = q.col != rows
+    vals = np.repeat(q.values, B, axis=0)
+    vals[:, off] *= (1.0 - 0.08 * np.arange(B))[:, None]
+    rng = np.random.default_rng(seed)
+    return W.Problem(f"{q.name}_batch{B}", q.n, q.row_ptr, q.col, vals,
+                     rng.standard_normal((B, q.n)), rng.uniform(-1.0, 1.0, (B, q.n)),
+                     method=q.method, precond=q.precond, tol=q.tol, maxit=q.maxit)
+
+
+def test_bicgstab_group_equals_singles(hip):
+    """Four 72 x 72 upwind convection-diffusion systems (n = 5184, one
+    BiCGStab launch group), one zero right-hand side; with and without an
+    initial guess; two systems against the oracle."""
+    banner("grid batch: BiCGStab group")
+    p = _scaled_batch(W.config(4, size=72), 4, 21)
+    p.b[1] = 0.0
+    g = _equal_to_singles(hip, p)
+    its = [int(v) for v in g["info"]["iters"]]
+    print("iterations per system:", its, flush=True)
+    assert its[1] == 0 and not np.any(g["x"][1])
+    assert len(set(its) - {0}) > 1
+    assert all(s == 0 for s in g["info"]["status"])
+    rng = np.random.default_rng(5)
+    _equal_to_singles(hip, p, x0=rng.standard_normal((p.batch, p.n)))
+    systems = [0, 3]
+    r, a = oracle_forward_adjoint(p, systems=systems)
+    tol = FP_TOL[np.dtype(np.float64)]["sol"]
+    for j, s in enumerate(systems):
+        assert relerr(g["x"][s], r.x[j]) <= tol
+        assert relerr(g["gb"][s], a.grad_b[j]) <= tol
+        assert relerr(g["gv"][s], a.grad_values[j]) <= tol
+
+
+def test_bicgstab_split_group_equals_singles(hip):
+    """Three systems on a directed power-law graph (rows past the tile
+    walker: split BiCGStab iterations, the product on the row plan) in one
+    group."""
+    banner("grid batch: split BiCGStab group")
+    from test_gpu_row_plan import directed_graph_problem
+    p = _scaled_batch(directed_graph_problem(20000, 19), 3, 22)
+    g = _equal_to_singles(hip, p)
+    its = [int(v) for v in g["info"]["iters"]]
+    print("iterations per system:", its, flush=True)
+    assert all(s == 0 for s in g["info"]["status"])
+    assert len(set(its)) > 1
+
+
+def test_bicgstab_several_groups_equal_singles(hip):
+    """Three 800 x 800 convection-diffusion systems (n = 640000): a group
+    holds 2^21 // n = 3 of them; a batch of four runs as groups of 3 and 1."""
+    banner("grid batch: BiCGStab groups of 3 + 1 at 800^2")
+    p = _scaled_batch(W.config(4, size=800), 4, 23)
+    g = _equal_to_singles(hip, p)
+    its = [int(v) for v in g["info"]["iters"]]
+    print("iterations per system:", its, flush=True)
+    assert all(s == 0 for s in g["info"]["status"])
+    assert len(set(its)) > 1
 
 
 def test_group_workspace(hip):
