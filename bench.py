@@ -199,6 +199,25 @@ def read_traffic(kernel, workload, sha):
         return None
 
 
+def read_product_traffic(op, workload, sha):
+    """Bytes past L2 per call of the product (op matvec) or its backward pass
+    (matvec_vjp) from a counter summary under profiles/ made from these
+    sources, else None."""
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*.{workload}.counters.txt"))):
+        rec = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+        if rec.get("op") == op and rec.get("source_sha256") == sha:
+            try:
+                return float(rec["bytes_past_l2_per_call"])
+            except (KeyError, ValueError):
+                return None
+    return None
+
+
 def load_problem(args):
     import workloads as W
     if getattr(args, "graph", False):
@@ -867,6 +886,9 @@ def bench_product(args, p):
     wall = time.perf_counter() - t0
     per = ev0.elapsed_time(ev1) / steps * 1e-3
     achieved = model / per / 1e9
+    traffic = read_product_traffic(
+        args.op, p.name, sources_sha(["kernels_spmv.hip", "spmv_tile.h", "sla_internal.h"]))
+    dram = traffic / per / 1e9 if traffic else None
     print(json.dumps({
         "metric": f"differentiable {args.op} calls/sec", "value": steps / wall,
         "unit": "calls/s", "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -876,7 +898,9 @@ def bench_product(args, p):
                                         "batch": p.batch},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "bytes_per_launch": model, "avg_launch_us": per * 1e6},
+                     "traffic": traffic, "dram_GBps": dram,
+                     "dram_frac": dram / HBM_PEAK_GBPS if dram else None,
+                     "bytes_per_launch": model, "avg_launch_us": per * 1e6},
     }), flush=True)
 
 
@@ -905,6 +929,7 @@ def main():
     if args.op == "inverse":
         return bench_inverse(args)
     p = load_problem(args)
+    print(f"workload {p.name} ready", file=sys.stderr, flush=True)
     if args.op == "nonlinear":
         return bench_nonlinear(args, p)
     if args.op == "eigsh":
@@ -933,9 +958,11 @@ def main():
         return fi, ai
 
     if args.kernel_only:
-        for _ in range(args.kernel_only):
+        for i in range(args.kernel_only):
             step()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            print(f"kernel-only: step {i + 1} of {args.kernel_only} done", file=sys.stderr,
+                  flush=True)
         # known-traffic kernels for the counters' calibration: copy, read, write of 1 GiB
         probe_kernels(CALIB_BYTES, dev)
         torch.cuda.synchronize()
