@@ -237,6 +237,12 @@ def load_problem(args):
 
 # ------------------------------------------------------------------ summaries
 
+def _short(name):
+    """A kernel's name without its parameter list (and without the return
+    type and anonymous-namespace prefixes)."""
+    return name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
 def _rows(d, pattern):
     files = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
     if not files:
@@ -326,7 +332,7 @@ def _product_table(d, counter, calls):
         for which in ("copy", "read", "write"):
             if _is_probe(name, which) and counter in c:
                 probes[which] = max(probes.get(which, 0.0), c[counter])
-        short = name.split("(")[0].replace("void ", "")
+        short = _short(name)
         if counter not in c or not any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
             continue
         e = per.setdefault(short, [0, 0.0])
@@ -398,7 +404,7 @@ def summarize_product_counters(args):
         for name, c in _dispatches(dirs[2]):
             if not all(k in c for k in SIZE_COUNTERS):
                 continue
-            short = name.split("(")[0].replace("void ", "")
+            short = _short(name)
             if any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
                 e = sized.setdefault(short, [0, 0.0, [0.0, 0.0, 0.0]])
                 e[0] += 1
@@ -419,7 +425,7 @@ def summarize_product_counters(args):
         for name, c in _dispatches(dirs[3]):
             if not all(k in c for k in CACHE_COUNTERS):
                 continue
-            short = name.split("(")[0].replace("void ", "")
+            short = _short(name)
             if any(f"sla::{k}<" in name for k in PRODUCT_KERNELS):
                 e = cache.setdefault(short, [0.0] * len(CACHE_COUNTERS))
                 for i, kc in enumerate(CACHE_COUNTERS):
@@ -532,7 +538,7 @@ def summarize_block(args):
         f" --output-format csv -d OUT/pmc_block -o run -- python3 bench.py --kernel-only 2{wl}",
         f"  python3 bench.py --summarize-block OUT/pmc_block{wl}",
         "",
-        f"kernel: {rows[0][0].split('(')[0].replace('void ', '')}",
+        f"kernel: {_short(rows[0][0])}",
         f"workload: {p.name}",
         f"n: {p.n}",
         f"batch: {p.batch}",
@@ -588,7 +594,7 @@ def summarize_trace(args):
     ]
     for r in stats[:12]:
         name = r["Name"]
-        short = name.split("(")[0].replace("void ", "")
+        short = _short(name)
         out.append(f"{int(r['Calls']):8d} {float(r['AverageNs']) / 1e3:10.2f} "
                    f"{float(r['TotalDurationNs']) / 1e6:10.2f} {float(r['Percentage']):6.2f}  "
                    f"{short}")
