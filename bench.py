@@ -308,7 +308,7 @@ def _form_flag(args):
     return "" if args.column_form == "diagonal-major" else f" --column-form {args.column_form}"
 
 
-PRODUCT_KERNELS = ("spmv_kernel", "spmv_perm_kernel", "plan_spmv_kernel", "plan_finish_kernel",
+PRODUCT_KERNELS = ("spmv_kernel", "plan_spmv_kernel", "plan_finish_kernel",
                    "plan_grad_kernel", "grad_kernel", "rowsum_kernel", "diag_vjp_kernel")
 CACHE_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCP_TCC_READ_REQ_sum",
                   "TCP_TOTAL_CACHE_ACCESSES_sum")
