@@ -145,12 +145,15 @@ void set_last_error(hipError_t e);
 // ---------------------------------------------------------------- helpers
 
 // v plus the value that the row-local DPP permutation CTRL brings to this
-// lane (both 32-bit halves moved in the VALU, no LDS traffic).
+// lane (both 32-bit halves moved in the VALU, no LDS traffic).  Every
+// permutation used here reads a lane of the same row, so with all rows and
+// banks enabled every lane is written: the move needs no old value (giving
+// it one, as update_dpp does, costs a zeroing move per half and step).
 template <int CTRL>
 __device__ __forceinline__ double dpp_add(double v) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, 0xf, 0xf, false);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xf, 0xf, false);
     return v + __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
                                                 (unsigned)lo));
 }
