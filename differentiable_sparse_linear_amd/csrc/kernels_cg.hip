@@ -463,16 +463,15 @@ __global__ __launch_bounds__(kBlock) void cg_split_w_kernel(const IterArgs<T, IT
 
 // ------------------------------------------------------------ block path
 
-constexpr int kBW = kBlockSolveThreads / 64;  // waves per workgroup
-
-// Sum over the workgroup; every thread receives the same, order-fixed total.
-// Wavefront sums go to LDS; after the barrier lane l of every wavefront reads
-// wavefront (l mod 16)'s sum and a 16-lane DPP row sum adds them (the same
-// steps in every row of every wavefront, so every thread gets bitwise the
-// same total).
-static_assert(kBW == 16, "the workgroup sum takes one wavefront sum per lane of a row");
-template <int NR>
-__device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW]) {
+// Sum over a workgroup of NW wavefronts (16 or 4); every thread receives the
+// same, order-fixed total.  Wavefront sums go to LDS; after the barrier,
+// with 16 wavefronts lane l of every wavefront reads wavefront (l mod 16)'s
+// sum and a 16-lane DPP row sum adds them (the same steps in every row of
+// every wavefront); with 4, every lane reads the four sums and adds them in
+// pairs.  Either way every thread gets bitwise the same total.
+template <int NW, int NR>
+__device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[NW]) {
+    static_assert(NW == 16 || NW == 4, "workgroups of 1024 or 256 threads");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -481,7 +480,12 @@ __device__ __forceinline__ void block_sum(double (&v)[NR], double (*slots)[kBW])
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = row16_sum(slots[r][lane & (kBW - 1)]);
+    for (int r = 0; r < NR; ++r) {
+        if constexpr (NW == 16)
+            v[r] = row16_sum(slots[r][lane & (NW - 1)]);
+        else
+            v[r] = (slots[r][0] + slots[r][1]) + (slots[r][2] + slots[r][3]);
+    }
 }
 
 // One row's matrix entries, SLOTS slots (slots past the row repeat its last
@@ -514,8 +518,9 @@ __device__ __forceinline__ T block_row_dot(const T (&v)[SLOTS], CF colf, gptr<co
     return acc;
 }
 
-// Row ownership: thread t owns rows t, t + 1024, ... (RPT rows, interleaved
-// so the vector accesses of a wavefront are consecutive).  The direction p
+// NT threads per workgroup (1024, or 256 for systems of at most 1024 rows).
+// Row ownership: thread t owns rows t, t + NT, ... (RPT rows, interleaved so
+// the vector accesses of a wavefront are consecutive).  The direction p
 // lives in LDS, where every row's product gathers it, and so does x (read
 // and written once per iteration); r, the row's own p and the product q of
 // the owned rows stay in the thread's registers (each is read and written
@@ -534,11 +539,11 @@ __device__ __forceinline__ T block_row_dot(const T (&v)[SLOTS], CF colf, gptr<co
 // iteration loop).  Products: SLOTS slots per row, p gathered from LDS
 // (neighbouring rows gather neighbouring LDS words), entry-order sums; rows
 // longer than SLOTS finish with a loop.
-// FULL: n == RPT * kBlockSolveThreads, every owned row exists, so the row
+// FULL: n == RPT * NT, every owned row exists, so the row
 // loops carry no guard (a guard is a branch, and the compiler does not move
 // the next row's LDS accesses above it).
-template <typename T, typename IT, int RPT, int SLOTS, bool RESIDENT, bool FULL>
-__global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgParams P) {
+template <typename T, typename IT, int NT, int RPT, int SLOTS, bool RESIDENT, bool FULL>
+__global__ __launch_bounds__(NT) void block_cg_kernel(BlockCgParams P) {
     extern __shared__ unsigned char lds_raw[];
     const int64_t n = P.n, nnz = P.nnz;
     T *ps = reinterpret_cast<T *>(lds_raw);  // direction p (or x0 at the start)
@@ -547,7 +552,8 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     T *rs = ds + n;                          // r, when in LDS
     constexpr bool DREG = sizeof(T) == 4 || RPT <= 2;  // M^-1 in registers
     constexpr bool RREG = DREG || RESIDENT;            // r and own p in registers
-    __shared__ double slots[4][3][kBW];
+    constexpr int NW = NT / 64;  // wavefronts per workgroup
+    __shared__ double slots[4][3][NW];
     const int sys = blockIdx.x;
     const int tid = threadIdx.x;
     const gptr<const T> val = glb(reinterpret_cast<const T *>(P.val) + (int64_t)sys * nnz);
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
     const gptr<const IT> dpos = glb(reinterpret_cast<const IT *>(P.diagpos));
     const gptr<const int32_t> col = glb(P.col);
     SolveState *st = P.st + sys;
-    auto row_of = [&](int j) -> int { return tid + j * kBlockSolveThreads; };
+    auto row_of = [&](int j) -> int { return tid + j * NT; };
     auto owned = [&](int i) -> bool { return FULL || i < n; };
     constexpr int MR = RESIDENT ? RPT : 1;
     constexpr int PC = (SLOTS + 1) / 2;
@@ -664,7 +670,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
             r0[2] += (double)bi * (double)bi;
         }
     }
-    block_sum<3>(r0, slots[0]);  // its barrier also ends every read of x0 in ps
+    block_sum<NW>(r0, slots[0]);  // its barrier also ends every read of x0 in ps
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
         const int i = row_of(j);
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
                 const int i = row_of(j);
                 if (owned(i)) pq[0] += (double)pget(j, i) * (double)qr[j];
             }
-            block_sum<1>(pq, slots[slot]);  // every gather of p is done
+            block_sum<NW>(pq, slots[slot]);  // every gather of p is done
             slot = (slot + 1) & 3;
             if (!(pq[0] > 0.0)) {
                 status = SLA_BREAKDOWN;
@@ -713,7 +719,7 @@ __global__ __launch_bounds__(kBlockSolveThreads) void block_cg_kernel(BlockCgPar
                     red[1] += (double)ri * (double)ri;
                 }
             }
-            block_sum<2>(red, slots[slot]);
+            block_sum<NW>(red, slots[slot]);
             slot = (slot + 1) & 3;
             ++it;
             rnorm2 = red[1];
@@ -834,36 +840,52 @@ constexpr bool block_resident() {
 
 // Slots per row for the block solver: the longest row rounded up to 4, 5, 6
 // or 8 (5 is the five-point stencil's exact width); longer rows stream.
+// Systems of at most kBlockSmallN rows take 256-thread workgroups (up to four
+// rows per thread), larger ones 1024 threads.  Every thread runs the
+// iteration's reductions and scalar steps whatever its row count, so for a
+// small system four wavefronts issue a quarter of the instructions that
+// sixteen would; batches of small systems also fit several workgroups per
+// compute unit.
+constexpr int64_t kBlockSmallN = 1024;
+
 template <typename T, typename IT>
 hipError_t launch_block_cg(int max_len, const BlockCgParams &p, int batch, hipStream_t s) {
     const size_t lds = 4 * (size_t)p.n * sizeof(T);  // p, x, M^-1, r
-    const int rpt = (int)((p.n + kBlockSolveThreads - 1) / kBlockSolveThreads);
+    const bool small = p.n <= kBlockSmallN;
+    const int nt = small ? 256 : kBlockSolveThreads;
+    const int rpt = (int)((p.n + nt - 1) / nt);
     const bool fits = max_len <= 8;
-#define SLA_BLOCK_LAUNCH(R, S)                                                                     \
-    if (fits && block_resident<T, R, S>() && p.n == R * kBlockSolveThreads)                       \
-        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>(), true>                              \
-            <<<batch, kBlockSolveThreads, lds, s>>>(p);                                            \
+#define SLA_BLOCK_LAUNCH(N, R, S)                                                                  \
+    if (fits && block_resident<T, R, S>() && p.n == R * N)                                        \
+        block_cg_kernel<T, IT, N, R, S, block_resident<T, R, S>(), true>                           \
+            <<<batch, N, lds, s>>>(p);                                                             \
     else if (fits && block_resident<T, R, S>())                                                    \
-        block_cg_kernel<T, IT, R, S, block_resident<T, R, S>(), false>                             \
-            <<<batch, kBlockSolveThreads, lds, s>>>(p);                                            \
+        block_cg_kernel<T, IT, N, R, S, block_resident<T, R, S>(), false>                          \
+            <<<batch, N, lds, s>>>(p);                                                             \
     else                                                                                           \
-        block_cg_kernel<T, IT, R, S, false, false><<<batch, kBlockSolveThreads, lds, s>>>(p)
-#define SLA_BLOCK_ROWS(R)                     \
+        block_cg_kernel<T, IT, N, R, S, false, false><<<batch, N, lds, s>>>(p)
+#define SLA_BLOCK_ROWS(N, R)                  \
     if (max_len <= 4) {                       \
-        SLA_BLOCK_LAUNCH(R, 4);               \
+        SLA_BLOCK_LAUNCH(N, R, 4);            \
     } else if (max_len == 5) {                \
-        SLA_BLOCK_LAUNCH(R, 5);               \
+        SLA_BLOCK_LAUNCH(N, R, 5);            \
     } else if (max_len == 6) {                \
-        SLA_BLOCK_LAUNCH(R, 6);               \
+        SLA_BLOCK_LAUNCH(N, R, 6);            \
     } else {                                  \
-        SLA_BLOCK_LAUNCH(R, 8);               \
+        SLA_BLOCK_LAUNCH(N, R, 8);            \
     }
-    if (rpt <= 1) {
-        SLA_BLOCK_ROWS(1)
-    } else if (rpt <= 2) {
-        SLA_BLOCK_ROWS(2)
+    if (small) {
+        if (rpt <= 1) {
+            SLA_BLOCK_ROWS(256, 1)
+        } else if (rpt <= 2) {
+            SLA_BLOCK_ROWS(256, 2)
+        } else {
+            SLA_BLOCK_ROWS(256, 4)
+        }
+    } else if (rpt <= 2) {  // n > 1024: at least two rows per thread
+        SLA_BLOCK_ROWS(kBlockSolveThreads, 2)
     } else {
-        SLA_BLOCK_ROWS(4)
+        SLA_BLOCK_ROWS(kBlockSolveThreads, 4)
     }
 #undef SLA_BLOCK_ROWS
 #undef SLA_BLOCK_LAUNCH
