@@ -542,7 +542,7 @@ def summarize_block(args):
         f"workload: {p.name}",
         f"n: {p.n}",
         f"batch: {p.batch}",
-        f"source_sha256: {sources_sha(['kernels_cg.hip', 'sla_internal.h'])}",
+        f"source_sha256: {sources_sha(['kernels_block.hip', 'sla_internal.h'])}",
         f"dispatches: {len(rows)} (forward and adjoint solves alternate)",
         "",
         f"{'dispatch':>8} {'lds_MB':>10} {'lds_insts':>12} {'bank_confl_cyc':>15} "
