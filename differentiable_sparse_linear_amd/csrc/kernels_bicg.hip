@@ -88,7 +88,9 @@ struct XpvOwn {
 #ifndef SLA_BICG_WAVES
 #define SLA_BICG_WAVES 5
 #endif
-template <typename T, typename IT, int SLOTS, int CM>
+// O32 (both kernels): the diagonal-major form with 32-bit byte offsets when
+// nd * n * sizeof(T) fits 32 bits (elem).
+template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
@@ -186,20 +188,23 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
         return fmaB(beta, fmaB(-omega, g.d, g.c), rj(g.a, g.b));
     };
     double rv_acc = 0.0, rr_acc = 0.0;
+    auto ld = [&](gptr<const T> v, int64_t i) -> T { return *elem<O32>(v, i); };
     const bool go = spmv_rows<T, IT, SLOTS, 4>(
-        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
-        [&](int32_t c) { return G4<T>{sv[c], tv[c], pold[c], vold[c]}; }, pj,
+        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
+        [&](auto k) { return ld(val, k); },
+        [&](int32_t c) { return G4<T>{ld(sv, c), ld(tv, c), ld(pold, c), ld(vold, c)}; }, pj,
         [&](int64_t i) {
-            return XpvOwn<T>{sv[i], tv[i], pold[i], vold[i], first ? T(0) : x[i], rh[i]};
+            return XpvOwn<T>{ld(sv, i), ld(tv, i), ld(pold, i), ld(vold, i),
+                             first ? T(0) : ld((gptr<const T>)x, i), ld(rh, i)};
         },
         [&](int64_t i, T acc, const XpvOwn<T> &o, T) {
             const T ri = rj(o.s, o.t);
             if (!first) {
-                x[i] = fmaB(omega, o.s, fmaB(alpha, o.p, o.x));
-                r[i] = ri;
+                *elem<O32>(x, i) = fmaB(omega, o.s, fmaB(alpha, o.p, o.x));
+                *elem<O32>(r, i) = ri;
             }
-            pnew[i] = pj(G4<T>{o.s, o.t, o.p, o.v});
-            vnew[i] = acc;
+            *elem<O32>(pnew, i) = pj(G4<T>{o.s, o.t, o.p, o.v});
+            *elem<O32>(vnew, i) = acc;
             rv_acc = fma((double)o.rh, (double)acc, rv_acc);
             rr_acc = fma((double)ri, (double)ri, rr_acc);
         },
@@ -219,7 +224,7 @@ struct StOwn {
 // on ||r_j|| (converged, then maxit) and rho_j = 0 (breakdown);
 // alpha_j = rho_j / rhat.v_j (rhat.v_j = 0: breakdown); s = r - alpha v
 // evaluated while gathering, t = A s; partials t.s, t.t, s.s, rhat.s, rhat.t.
-template <typename T, typename IT, int SLOTS, int CM>
+template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
@@ -280,14 +285,16 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     };
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0, rs = 0.0, rt = 0.0;
+    auto ld = [&](gptr<const T> w, int64_t i) -> T { return *elem<O32>(w, i); };
     const bool go = spmv_rows<T, IT, SLOTS, SLOTS>(
-        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm, [&](auto k) { return val[k]; },
-        [&](int32_t c) { return G2<T>{r[c], v[c]}; }, sk,
-        [&](int64_t i) { return StOwn<T>{r[i], v[i], rh[i]}; },
+        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
+        [&](auto k) { return ld(val, k); },
+        [&](int32_t c) { return G2<T>{ld(r, c), ld(v, c)}; }, sk,
+        [&](int64_t i) { return StOwn<T>{ld(r, i), ld(v, i), ld(rh, i)}; },
         [&](int64_t i, T acc, const StOwn<T> &o, T) {
             const T si = sk(G2<T>{o.r, o.v});
-            s[i] = si;
-            tv[i] = acc;
+            *elem<O32>(s, i) = si;
+            *elem<O32>(tv, i) = acc;
             ts = fma((double)acc, (double)si, ts);
             tt = fma((double)acc, (double)acc, tt);
             ss = fma((double)si, (double)si, ss);
@@ -517,6 +524,19 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<
 
 // ------------------------------------------------------------------ launchers
 
+// The diagonal-major form with every byte offset (at most nd * n values) in
+// 32 bits takes the O32 kernels.
+template <typename T>
+bool bicg_o32(int cm, int slots, int64_t n) {
+    return cm == kColDiaMajor && (int64_t)slots * n * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
+}
+#define SLA_BICG_O32(slots, ...)                                   \
+    switch (slots) {                                               \
+        case 3: { constexpr int kS = 3; __VA_ARGS__; } break;      \
+        case 5: { constexpr int kS = 5; __VA_ARGS__; } break;      \
+        default: { constexpr int kS = 7; __VA_ARGS__; } break;     \
+    }
+
 template <typename T, typename IT>
 hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, int nsys,
                              hipStream_t s) {
@@ -540,8 +560,13 @@ template <typename T, typename IT>
 hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
-    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kC>, grid,
-                                                    dim3(kBlock), 0, s, ev, a));
+    if (bicg_o32<T>(cm, slots, n)) {
+        SLA_BICG_O32(slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kColDiaMajor, true>,
+                                               grid, dim3(kBlock), 0, s, ev, a));
+    } else {
+        SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kC>, grid,
+                                                        dim3(kBlock), 0, s, ev, a));
+    }
     return hipGetLastError();
 }
 
@@ -549,8 +574,13 @@ template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
-    SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kC>, grid,
-                                                    dim3(kBlock), 0, s, ev, a));
+    if (bicg_o32<T>(cm, slots, n)) {
+        SLA_BICG_O32(slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kColDiaMajor, true>,
+                                               grid, dim3(kBlock), 0, s, ev, a));
+    } else {
+        SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kC>, grid,
+                                                        dim3(kBlock), 0, s, ev, a));
+    }
     return hipGetLastError();
 }
 

@@ -132,10 +132,14 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 // streams the values, p, x and the vectors written here with non-temporal
 // hints (grids far beyond the Infinity Cache, where these are touched once
 // per iteration and L2 is better left to the plane's +-N neighbours).
-template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0>
+// O32: the diagonal-major tiles (ZW == 0) with 32-bit byte offsets, when
+// nd * n * sizeof(T) fits 32 bits (elem).
+template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0,
+          bool O32 = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
+    static_assert(!O32 || (CM == kColDiaMajor && !ZW), "32-bit offsets: diagonal-major tiles");
     constexpr bool NT = ZW == 2;
     A += blockIdx.y;
     SolveState *st = A->st;
@@ -234,18 +238,19 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto s_of = [&](T w, T sv) -> T { return fmaT(beta, sv, w); };
     auto u_of = [&](const G3<T> &g) -> T { return fmaT(-alpha, s_of(g.b, g.c), g.a); };
     double g = 0.0, d = 0.0, q = 0.0;
-    auto gath = [&](int32_t c) { return G3<T>{uc[c], wc[c], sprev[c]}; };
+    auto ld = [&](gptr<const T> v, int64_t i) -> T { return *elem<O32>(v, i); };
+    auto gath = [&](int32_t c) { return G3<T>{ld(uc, c), ld(wc, c), ld(sprev, c)}; };
     auto put = [&](gptr<T> v, int64_t i, T a) {
         if constexpr (NT)
-            __builtin_nontemporal_store(a, &v[i]);
+            __builtin_nontemporal_store(a, elem<O32>(v, i));
         else
-            v[i] = a;
+            *elem<O32>(v, i) = a;
     };
     auto stream = [&](gptr<const T> v, int64_t i) -> T {
         if constexpr (NT)
-            return __builtin_nontemporal_load(&v[i]);
+            return __builtin_nontemporal_load(elem<O32>(v, i));
         else
-            return v[i];
+            return ld(v, i);
     };
     auto row = [&](int64_t i, T acc, const CgOwn<T> &o, T aii) {
         const T pi = fmaT(beta, o.p, o.u);
@@ -275,8 +280,11 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     } else {
         go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND, CM, true>(
             walk_tiles(tiles_of(n), stopped), n, glb(A->rp), cg_cols<CM>(A->cols, st), sm,
-            [&](auto k) { return val[k]; }, gath, u_of,
-            [&](int64_t i) { return CgOwn<T>{uc[i], wc[i], sprev[i], pprev[i], PH ? x[i] : T(0)}; },
+            [&](auto k) { return ld(val, k); }, gath, u_of,
+            [&](int64_t i) {
+                return CgOwn<T>{ld(uc, i), ld(wc, i), ld(sprev, i), ld(pprev, i),
+                                PH ? ld((gptr<const T>)x, i) : T(0)};
+            },
             row, pre, post);
     }
     if (!go) return;
@@ -508,6 +516,12 @@ template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
                           int64_t n, int nsys, int ph, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    // diagonal-major tiles with every byte offset (at most nd * n values) in 32 bits
+    const bool o32 = cm == kColDiaMajor && zw == 0 &&
+                     (int64_t)slots * n * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
+#define SLA_CG_O32(J, P, S) \
+    launch_maybe_timed(cg_iter_kernel<T, IT, J, S, P, kColDiaMajor, 0, true>, grid, dim3(kBlock), \
+                       0, s, ev, a)
 #define SLA_CG_ITER(J, P)                                                                      \
     if (zw == 2)                                                                               \
         launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, 2>, grid,              \
@@ -515,6 +529,12 @@ hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T,
     else if (zw == 1)                                                                          \
         launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, 1>, grid,              \
                            dim3(kBlock), 0, s, ev, a);                                         \
+    else if (o32 && slots == 3)                                                                \
+        SLA_CG_O32(J, P, 3);                                                                   \
+    else if (o32 && slots == 5)                                                                \
+        SLA_CG_O32(J, P, 5);                                                                   \
+    else if (o32)                                                                              \
+        SLA_CG_O32(J, P, 7);                                                                   \
     else                                                                                       \
         SLA_DISPATCH_FORM(cm, slots, launch_maybe_timed(cg_iter_kernel<T, IT, J, kS, P, kC>,   \
                                                         grid, dim3(kBlock), 0, s, ev, a))
@@ -532,6 +552,7 @@ hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T,
         }
     }
 #undef SLA_CG_ITER
+#undef SLA_CG_O32
     return hipGetLastError();
 }
 
