@@ -144,11 +144,12 @@ void set_last_error(hipError_t e);
 
 // ---------------------------------------------------------------- helpers
 
-// v plus the value that the row-local DPP permutation CTRL brings to this
-// lane (both 32-bit halves moved in the VALU, no LDS traffic).  Every
-// permutation used here reads a lane of the same row, so with all rows and
-// banks enabled every lane is written: the move needs no old value (giving
-// it one, as update_dpp does, costs a zeroing move per half and step).
+// v plus the value that the DPP move CTRL brings to this lane (both 32-bit
+// halves moved in the VALU, no LDS traffic).  The row-local permutations
+// write every lane; the row broadcasts leave the lanes of the first row(s)
+// unwritten, whose results wave_sum does not read.  So the move needs no old
+// value (giving it one, as update_dpp does, costs a zeroing move per half and
+// step).
 template <int CTRL>
 __device__ __forceinline__ double dpp_add(double v) {
     const unsigned long long u = (unsigned long long)__double_as_longlong(v);
@@ -178,11 +179,17 @@ __device__ __forceinline__ double lane_value(double v, int lane) {
                                             (unsigned)lo));
 }
 
-// Sum over the wavefront, the same bits in every lane: row sums by DPP, then
-// the four row sums (read as uniform values) in a fixed order.
+// Sum over the wavefront as a uniform value: row sums r0..r3 by DPP, then
+// row 3 adds row 2 and row 1 adds row 0 (row_bcast:15), row 3 adds row 1's
+// total (row_bcast:31), and lane 63, (r3 + r2) + (r1 + r0), is read.  IEEE
+// addition is commutative, so this is bitwise the sum (r0 + r1) + (r2 + r3)
+// of the four row sums read one by one, in two DPP steps and two lane reads
+// instead of eight lane reads, two moves and three adds.
 __device__ __forceinline__ double wave_sum(double v) {
     v = row16_sum(v);
-    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+    v = dpp_add<0x142>(v);  // row_bcast:15
+    v = dpp_add<0x143>(v);  // row_bcast:31
+    return lane_value(v, 63);
 }
 
 // Contiguous tile range of this block's XCD, strided over the XCD's blocks.
