@@ -175,7 +175,9 @@ sla_status sla_destroy(sla_handle h);
  * storage form and launch shape).  Without diagonal masks, a single system
  * (or any batch on a pattern of at least 2^20 entries) goes in two passes,
  * one system at a time: the terms are written to A^T's order in the
- * handle's buffer, then A^T's rows are summed.
+ * handle's buffer, then A^T's rows are summed; the product alone does so
+ * while nnz * (2 * value size + 4) <= 192 MB, and beyond that reads A^T's
+ * values through the transpose map (same bits).
  */
 sla_status sla_matvec(sla_handle h, const void *d_values, const void *d_x,
                       void *d_y, int32_t transpose, void *stream);
