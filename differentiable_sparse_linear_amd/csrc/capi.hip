@@ -320,9 +320,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                                    op.plan));
         HIP_TRY(launch_cg_split_w<T, IT>(jac, true, ad, dpos, n, nsys, 0, s));
     } else if (cg) {
-        HIP_TRY(launch_cg_init<T, IT>(slots, cm, jac, ad, n, nsys, s));
+        HIP_TRY(launch_cg_init<T, IT>(slots, cm, zw, jac, ad, n, nsys, s));
     } else {
-        HIP_TRY(launch_bicg_init<T, IT>(ad, n, nsys, s));
+        HIP_TRY(launch_bicg_init<T, IT>(cm, ad, n, nsys, s));
     }
 
     // split BiCGStab: half h of iteration k (0: updates, p_k -> v_k,

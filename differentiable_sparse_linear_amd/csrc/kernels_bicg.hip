@@ -91,7 +91,7 @@ struct XpvOwn {
 // O32 (both kernels): the diagonal-major form with 32-bit byte offsets when
 // nd * n * sizeof(T) fits 32 bits (elem).
 template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 3 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
@@ -225,7 +225,7 @@ struct StOwn {
 // alpha_j = rho_j / rhat.v_j (rhat.v_j = 0: breakdown); s = r - alpha v
 // evaluated while gathering, t = A s; partials t.s, t.t, s.s, rhat.s, rhat.t.
 template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_BICG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 3 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
     SolveState *st = A->st;
@@ -551,15 +551,17 @@ hipError_t launch_bicg_split(int part, const IterArgs<T, IT> *a, int64_t n, int 
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_init(const IterArgs<T, IT> *a, int64_t n, int nsys, hipStream_t s) {
-    bicg_init_kernel<T, IT><<<dim3(grid_for_tiles(tiles_of(n)), nsys), kBlock, 0, s>>>(a);
+hipError_t launch_bicg_init(int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
+                            hipStream_t s) {
+    // the iterations' grid: they read these partial sums
+    bicg_init_kernel<T, IT><<<dim3(iter_grid(cm, 0, n), nsys), kBlock, 0, s>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, typename IT>
 hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    const dim3 grid(iter_grid(cm, 0, n), nsys);
     if (bicg_o32<T>(cm, slots, n)) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
@@ -573,7 +575,7 @@ hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t 
 template <typename T, typename IT>
 hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
                            hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    const dim3 grid(iter_grid(cm, 0, n), nsys);
     if (bicg_o32<T>(cm, slots, n)) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
@@ -585,7 +587,7 @@ hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n
 }
 
 #define SLA_INST(T, IT)                                                                        \
-    template hipError_t launch_bicg_init<T, IT>(const IterArgs<T, IT> *, int64_t, int,         \
+    template hipError_t launch_bicg_init<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,    \
                                                 hipStream_t);                                  \
     template hipError_t launch_bicg_xpv<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,    \
                                                int, hipStream_t, const hipEvent_t *);          \

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 // nd * n * sizeof(T) fits 32 bits (elem).
 template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0,
           bool O32 = false>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 4 : SLA_CG_WAVES)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? (ZW ? 4 : 3) : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
     static_assert(!O32 || (CM == kColDiaMajor && !ZW), "32-bit offsets: diagonal-major tiles");
@@ -499,9 +499,9 @@ int cg_zwalk_plan(ColArgs &it, int64_t n, int64_t value_bytes) {
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a, int64_t n,
-                          int nsys, hipStream_t s) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+hipError_t launch_cg_init(int slots, int cm, int zw, bool jac, const IterArgs<T, IT> *a,
+                          int64_t n, int nsys, hipStream_t s) {
+    const dim3 grid(iter_grid(cm, zw, n), nsys);  // the iterations' grid (partial sums)
     if (jac) {
         SLA_DISPATCH_FORM(cm, slots, cg_init_kernel<T, IT, true, kS, kC>
                                                  <<<grid, kBlock, 0, s>>>(a));
@@ -515,7 +515,7 @@ hipError_t launch_cg_init(int slots, int cm, bool jac, const IterArgs<T, IT> *a,
 template <typename T, typename IT>
 hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
                           int64_t n, int nsys, int ph, hipStream_t s, const hipEvent_t *ev) {
-    const dim3 grid(grid_for_tiles(tiles_of(n)), nsys);
+    const dim3 grid(iter_grid(cm, zw, n), nsys);
     // diagonal-major tiles with every byte offset (at most nd * n values) in 32 bits
     const bool o32 = cm == kColDiaMajor && zw == 0 &&
                      (int64_t)slots * n * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
@@ -620,7 +620,7 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
                                           int, hipStream_t);
 
 #define SLA_INST(T, IT)                                                                         \
-    template hipError_t launch_cg_init<T, IT>(int, int, bool, const IterArgs<T, IT> *,       \
+    template hipError_t launch_cg_init<T, IT>(int, int, int, bool, const IterArgs<T, IT> *,  \
                                               int64_t, int, hipStream_t);                       \
     template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, const IterArgs<T, IT> *, \
                                               int64_t, int, int, hipStream_t,                   \
