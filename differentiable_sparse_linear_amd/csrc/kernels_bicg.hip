@@ -88,8 +88,8 @@ struct XpvOwn {
 #ifndef SLA_BICG_WAVES
 #define SLA_BICG_WAVES 5
 #endif
-// O32 (both kernels): the diagonal-major form with 32-bit byte offsets when
-// nd * n * sizeof(T) fits 32 bits (elem).
+// O32 (both kernels): the fast diagonal-major tiles (dia_fast): 32-bit byte
+// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ).
 template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 3 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
@@ -189,10 +189,21 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     };
     double rv_acc = 0.0, rr_acc = 0.0;
     auto ld = [&](gptr<const T> v, int64_t i) -> T { return *elem<O32>(v, i); };
-    const bool go = spmv_rows<T, IT, SLOTS, 4>(
-        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
+    auto rows = [&](auto vf, auto gf, auto of, auto rf) {
+        if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
+            return dia_rows<T, SLOTS, false, true>(
+                walk_tiles(tiles_of(n), stopped), n, col_src<CM>(A->cols), vf, gf, pj, of, rf,
+                pre, post, nullptr, [&](int64_t c) {
+                    return G4<T>{sld(sv, c), sld(tv, c), sld(pold, c), sld(vold, c)};
+                });
+        else
+            return spmv_rows<T, IT, SLOTS, 4>(walk_tiles(tiles_of(n), stopped), n, glb(A->rp),
+                                              col_src<CM>(A->cols), sm, vf, gf, pj, of, rf, pre,
+                                              post);
+    };
+    const bool go = rows(
         [&](auto k) { return ld(val, k); },
-        [&](int32_t c) { return G4<T>{ld(sv, c), ld(tv, c), ld(pold, c), ld(vold, c)}; }, pj,
+        [&](int32_t c) { return G4<T>{ld(sv, c), ld(tv, c), ld(pold, c), ld(vold, c)}; },
         [&](int64_t i) {
             return XpvOwn<T>{ld(sv, i), ld(tv, i), ld(pold, i), ld(vold, i),
                              first ? T(0) : ld((gptr<const T>)x, i), ld(rh, i)};
@@ -207,8 +218,7 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
             *elem<O32>(vnew, i) = acc;
             rv_acc = fma((double)o.rh, (double)acc, rv_acc);
             rr_acc = fma((double)ri, (double)ri, rr_acc);
-        },
-        pre, post);
+        });
     if (!go) return;
     double v[2] = {rv_acc, rr_acc};
     const int slot[2] = {kBiRV, kBiRR};
@@ -286,10 +296,19 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0, rs = 0.0, rt = 0.0;
     auto ld = [&](gptr<const T> w, int64_t i) -> T { return *elem<O32>(w, i); };
-    const bool go = spmv_rows<T, IT, SLOTS, SLOTS>(
-        walk_tiles(tiles_of(n), stopped), n, glb(A->rp), col_src<CM>(A->cols), sm,
+    auto rows = [&](auto vf, auto gf, auto of, auto rf) {
+        if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
+            return dia_rows<T, SLOTS, false, true>(
+                walk_tiles(tiles_of(n), stopped), n, col_src<CM>(A->cols), vf, gf, sk, of, rf,
+                pre, post, nullptr, [&](int64_t c) { return G2<T>{sld(r, c), sld(v, c)}; });
+        else
+            return spmv_rows<T, IT, SLOTS, SLOTS>(walk_tiles(tiles_of(n), stopped), n,
+                                                  glb(A->rp), col_src<CM>(A->cols), sm, vf, gf,
+                                                  sk, of, rf, pre, post);
+    };
+    const bool go = rows(
         [&](auto k) { return ld(val, k); },
-        [&](int32_t c) { return G2<T>{ld(r, c), ld(v, c)}; }, sk,
+        [&](int32_t c) { return G2<T>{ld(r, c), ld(v, c)}; },
         [&](int64_t i) { return StOwn<T>{ld(r, i), ld(v, i), ld(rh, i)}; },
         [&](int64_t i, T acc, const StOwn<T> &o, T) {
             const T si = sk(G2<T>{o.r, o.v});
@@ -300,8 +319,7 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
             ss = fma((double)si, (double)si, ss);
             rs = fma((double)o.rh, (double)si, rs);
             rt = fma((double)o.rh, (double)acc, rt);
-        },
-        pre, post);
+        });
     if (!go) return;
     double red5[5] = {ts, tt, ss, rs, rt};
     const int slot[5] = {kBiTS, kBiTT, kBiSS, kBiRS, kBiRT};
@@ -524,12 +542,6 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<
 
 // ------------------------------------------------------------------ launchers
 
-// The diagonal-major form with every byte offset (at most nd * n values) in
-// 32 bits takes the O32 kernels.
-template <typename T>
-bool bicg_o32(int cm, int slots, int64_t n) {
-    return cm == kColDiaMajor && (int64_t)slots * n * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
-}
 #define SLA_BICG_O32(slots, ...)                                   \
     switch (slots) {                                               \
         case 3: { constexpr int kS = 3; __VA_ARGS__; } break;      \
@@ -559,10 +571,10 @@ hipError_t launch_bicg_init(int cm, const IterArgs<T, IT> *a, int64_t n, int nsy
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
-                           hipStream_t s, const hipEvent_t *ev) {
+hipError_t launch_bicg_xpv(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+                           int nsys, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, 0, n), nsys);
-    if (bicg_o32<T>(cm, slots, n)) {
+    if (fast && cm == kColDiaMajor) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
     } else {
@@ -573,10 +585,10 @@ hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t 
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
-                           hipStream_t s, const hipEvent_t *ev) {
+hipError_t launch_bicg_st(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+                          int nsys, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, 0, n), nsys);
-    if (bicg_o32<T>(cm, slots, n)) {
+    if (fast && cm == kColDiaMajor) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
     } else {
@@ -589,9 +601,9 @@ hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n
 #define SLA_INST(T, IT)                                                                        \
     template hipError_t launch_bicg_init<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,    \
                                                 hipStream_t);                                  \
-    template hipError_t launch_bicg_xpv<T, IT>(int, int, const IterArgs<T, IT> *, int64_t,    \
+    template hipError_t launch_bicg_xpv<T, IT>(int, int, bool, const IterArgs<T, IT> *, int64_t, \
                                                int, hipStream_t, const hipEvent_t *);          \
-    template hipError_t launch_bicg_st<T, IT>(int, int, const IterArgs<T, IT> *, int64_t, int, \
+    template hipError_t launch_bicg_st<T, IT>(int, int, bool, const IterArgs<T, IT> *, int64_t, int, \
                                               hipStream_t, const hipEvent_t *);               \
     template hipError_t launch_bicg_split<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,  \
                                                  hipStream_t);

@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 // streams the values, p, x and the vectors written here with non-temporal
 // hints (grids far beyond the Infinity Cache, where these are touched once
 // per iteration and L2 is better left to the plane's +-N neighbours).
-// O32: the diagonal-major tiles (ZW == 0) with 32-bit byte offsets, when
-// nd * n * sizeof(T) fits 32 bits (elem).
+// O32: the fast diagonal-major tiles (ZW == 0, dia_fast): 32-bit byte
+// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ).
 template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0,
           bool O32 = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? (ZW ? 4 : 3) : SLA_CG_WAVES)))
@@ -278,14 +278,20 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
             },
             row, pre, post, zring);
     } else {
-        go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND, CM, true>(
-            walk_tiles(tiles_of(n), stopped), n, glb(A->rp), cg_cols<CM>(A->cols, st), sm,
-            [&](auto k) { return ld(val, k); }, gath, u_of,
-            [&](int64_t i) {
-                return CgOwn<T>{ld(uc, i), ld(wc, i), ld(sprev, i), ld(pprev, i),
-                                PH ? ld((gptr<const T>)x, i) : T(0)};
-            },
-            row, pre, post);
+        auto own_of = [&](int64_t i) {
+            return CgOwn<T>{ld(uc, i), ld(wc, i), ld(sprev, i), ld(pprev, i),
+                            PH ? ld((gptr<const T>)x, i) : T(0)};
+        };
+        if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
+            go = dia_rows<T, SLOTS, true, true>(
+                walk_tiles(tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
+                [&](auto k) { return ld(val, k); }, gath, u_of, own_of, row, pre, post,
+                [&](int64_t k) { return sld(val, k); },
+                [&](int64_t c) { return G3<T>{sld(uc, c), sld(wc, c), sld(sprev, c)}; });
+        else
+            go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND, CM, true>(
+                walk_tiles(tiles_of(n), stopped), n, glb(A->rp), cg_cols<CM>(A->cols, st), sm,
+                [&](auto k) { return ld(val, k); }, gath, u_of, own_of, row, pre, post);
     }
     if (!go) return;
     double v[3] = {g, d, q};
@@ -513,12 +519,11 @@ hipError_t launch_cg_init(int slots, int cm, int zw, bool jac, const IterArgs<T,
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
-                          int64_t n, int nsys, int ph, hipStream_t s, const hipEvent_t *ev) {
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, bool fast,
+                          const IterArgs<T, IT> *a, int64_t n, int nsys, int ph, hipStream_t s,
+                          const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, zw, n), nsys);
-    // diagonal-major tiles with every byte offset (at most nd * n values) in 32 bits
-    const bool o32 = cm == kColDiaMajor && zw == 0 &&
-                     (int64_t)slots * n * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
+    const bool o32 = fast && cm == kColDiaMajor && zw == 0;
 #define SLA_CG_O32(J, P, S) \
     launch_maybe_timed(cg_iter_kernel<T, IT, J, S, P, kColDiaMajor, 0, true>, grid, dim3(kBlock), \
                        0, s, ev, a)
@@ -622,9 +627,9 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, int, int, bool, const IterArgs<T, IT> *,  \
                                               int64_t, int, hipStream_t);                       \
-    template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, const IterArgs<T, IT> *, \
-                                              int64_t, int, int, hipStream_t,                   \
-                                              const hipEvent_t *);                              \
+    template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, bool,                    \
+                                              const IterArgs<T, IT> *, int64_t, int, int,       \
+                                              hipStream_t, const hipEvent_t *);                 \
     template hipError_t launch_cg_split_init<T, IT>(bool, const IterArgs<T, IT> *, int64_t, int, \
                                                     hipStream_t);                              \
     template hipError_t launch_cg_split_u<T, IT>(bool, const IterArgs<T, IT> *, int64_t, int,    \

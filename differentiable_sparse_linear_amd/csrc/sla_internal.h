@@ -7,6 +7,7 @@
 #pragma once
 
 #include <algorithm>
+#include <cstddef>
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -23,7 +24,8 @@ namespace sla {
 #define SLA_BLOCKS_PER_XCD 128
 #endif
 constexpr int kBlock = SLA_BLOCK;  // threads per block of the grid kernels
-constexpr int kWaves = kBlock / 64;
+constexpr int kWaveSize = 64;  // lanes of a wavefront
+constexpr int kWaves = kBlock / kWaveSize;
 constexpr int kTileRows = kBlock;  // rows per tile (one row per thread in
                                    // element-wise kernels)
 constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, 32 CUs each
@@ -340,6 +342,18 @@ __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileRows -
 // -> 22.69 us per launch, BiCGStab on the 1024^2 upwind system 21.0 -> 20.5
 // us.  The z-walk's plan and the other forms use grid_for_tiles.
 constexpr int kDiaBlocksPerXcd = 96;
+
+// The fast form of the diagonal-major tile kernels (their O32
+// instantiations): every byte offset formed (at most nd * n values of
+// value_bytes) fits 32 bits, and the diagonals next to the main one are at
+// -1 and +1, so that their gathers come from the adjacent lanes (dia_rows
+// ADJ).  Other diagonal-major forms take the general tile kernels.
+inline bool dia_fast(const ColArgs &c, int64_t n, int64_t value_bytes) {
+    if (c.mode != kColDiaMajor || c.nd < 3 || c.nd > kMaxDiaMajor) return false;
+    const int d0 = c.nd / 2;
+    return (int64_t)c.nd * n * value_bytes <= (int64_t)0xffffffff && c.off[d0 - 1] == -1 &&
+           c.off[d0 + 1] == 1;
+}
 inline int iter_grid(int cm, int zw, int64_t n) {
     const int g = grid_for_tiles(tiles_of(n));
     return cm == kColDiaMajor && zw == 0 ? std::min(g, kNumXcd * kDiaBlocksPerXcd) : g;
@@ -476,10 +490,11 @@ template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, int zw, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           int nsys, hipStream_t s);
 // zw: 0, or the z-walk (cg_zwalk_plan) with plain (1) or non-temporal (2)
-// streams of the values and the vectors touched once
+// streams of the values and the vectors touched once; fast: dia_fast of the
+// operator form (without the z-walk)
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, const IterArgs<T, IT> *a,
-                          int64_t n, int nsys, int ph, hipStream_t s,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, bool fast,
+                          const IterArgs<T, IT> *a, int64_t n, int nsys, int ph, hipStream_t s,
                           const hipEvent_t *ev = nullptr);
 // The z-walk of a seven-diagonal operator form on n rows (3D stencils: a
 // plane of D = off[6] rows, nz = n / D planes): fills it's zw_* fields and
@@ -504,12 +519,13 @@ hipError_t launch_cg_split_w(bool jac, bool init, const IterArgs<T, IT> *a, cons
 // BiCGStab (grid path; nsys systems, argument blocks a[0 .. nsys))
 template <typename T, typename IT>
 hipError_t launch_bicg_init(int cm, const IterArgs<T, IT> *a, int64_t n, int nsys, hipStream_t s);
+// fast: dia_fast of the operator form
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
-                           hipStream_t s, const hipEvent_t *ev = nullptr);
+hipError_t launch_bicg_xpv(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+                           int nsys, hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, const IterArgs<T, IT> *a, int64_t n, int nsys,
-                          hipStream_t s, const hipEvent_t *ev = nullptr);
+hipError_t launch_bicg_st(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+                          int nsys, hipStream_t s, const hipEvent_t *ev = nullptr);
 // BiCGStab in six launches per iteration for operators with a row plan:
 // part 0 (first half's updates), [p -> v product], 1 (its partials),
 // 2 (second half's updates), [s -> t product], 3 (its partials)

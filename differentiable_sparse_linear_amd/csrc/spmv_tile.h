@@ -119,6 +119,48 @@ struct G4 {
     T a, b, c, d;
 };
 
+// v[k] through the scalar data cache: k must be the same in every lane of
+// the wavefront, and nothing may write v while the kernel runs (the cache is
+// invalidated when a kernel starts, not when another one writes).
+template <typename T>
+__device__ __forceinline__ T sld(gptr<const T> v, int64_t k) {
+    return ((const __attribute__((address_space(4))) T *)v)[k];
+}
+
+// Lane shifts of the wavefront by DPP: CTRL 0x138 (wave_shr:1) gives lane t
+// the value of lane t - 1 and lane 0 `edge`; 0x130 (wave_shl:1) gives lane t
+// the value of lane t + 1 and lane 63 `edge`.  A move, so the bits are kept.
+template <int CTRL, typename T>
+__device__ __forceinline__ T lane_shift(T v, T edge) {
+    static_assert(CTRL == 0x138 || CTRL == 0x130, "wave_shr:1 or wave_shl:1");
+    if constexpr (sizeof(T) == 8) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, v), e = __builtin_bit_cast(uint64_t, edge);
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)e, (int)(uint32_t)b,
+                                                                  CTRL, 0xf, 0xf, false);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+            (int)(uint32_t)(e >> 32), (int)(uint32_t)(b >> 32), CTRL, 0xf, 0xf, false);
+        return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+    } else {
+        static_assert(sizeof(T) == 4, "4- or 8-byte values");
+        return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, edge),
+                                                                 __builtin_bit_cast(int, v), CTRL,
+                                                                 0xf, 0xf, false));
+    }
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ G2<T> lane_shift(const G2<T> &v, const G2<T> &e) {
+    return G2<T>{lane_shift<CTRL>(v.a, e.a), lane_shift<CTRL>(v.b, e.b)};
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ G3<T> lane_shift(const G3<T> &v, const G3<T> &e) {
+    return G3<T>{lane_shift<CTRL>(v.a, e.a), lane_shift<CTRL>(v.b, e.b), lane_shift<CTRL>(v.c, e.c)};
+}
+template <int CTRL, typename T>
+__device__ __forceinline__ G4<T> lane_shift(const G4<T> &v, const G4<T> &e) {
+    return G4<T>{lane_shift<CTRL>(v.a, e.a), lane_shift<CTRL>(v.b, e.b), lane_shift<CTRL>(v.c, e.c),
+                 lane_shift<CTRL>(v.d, e.d)};
+}
+
 // Gathering one vector entry: the load and the use are the same.
 struct PlainGather {
     template <typename V>
@@ -227,12 +269,28 @@ __device__ __forceinline__ T dia_entry(VF vf, const ColSrc<kColDiaMajor> &col, i
 // rows just before, mostly still in the caches).  All loads of a tile are issued
 // before its first use, and the first tile's before the start-up barrier,
 // so that their latency overlaps the kernel's start-up loads.
-template <typename T, int ND, bool SYM, typename VF, typename GF, typename CF, typename OF,
-          typename RF, typename PRE, typename POST>
+//
+// ADJ (the diagonals next to the main one are at -1 and +1): the gathers of
+// those two diagonals are the main diagonal's gathers of the rows before and
+// after, which the neighbouring lanes hold, so they move across by lane
+// shifts instead of being loaded again; lane 0 and lane 63 take theirs from
+// uniform loads through the scalar cache, gs(c) (and vs(k) for values).
+// With SYM the -1 diagonal's mirrored value (row i - 1's entry on the +1
+// diagonal) comes from lane t - 1 the same way.  The texture addresser's
+// work per row falls by seven of thirty wavefront loads in the CG iteration;
+// it bounded the kernel (busy for 60-66 % of its cycles on the 1e6-row 3D
+// diffusion system).  The values moved are the bits the loads would return,
+// so the sums are unchanged.  gf, gs and vs must read arrays that the
+// kernel does not write.
+template <typename T, int ND, bool SYM, bool ADJ = false, typename VF, typename GF, typename CF,
+          typename OF, typename RF, typename PRE, typename POST, typename VS = std::nullptr_t,
+          typename GS = std::nullptr_t>
 __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
                                          const ColSrc<kColDiaMajor> &col, VF vf, GF gf, CF cf,
-                                         OF of, RF rf, PRE pre, POST post) {
+                                         OF of, RF rf, PRE pre, POST post, VS vs = nullptr,
+                                         GS gs = nullptr) {
     static_assert(ND >= 1 && ND <= kMaxDiaMajor && (ND & 1), "diagonal count");
+    static_assert(!ADJ || ND >= 3, "ADJ: diagonals on both sides of the main one");
     using G = decltype(gf(0));
     using O = decltype(of(0));
     constexpr int d0 = ND / 2;  // the main diagonal's slot
@@ -240,6 +298,10 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
     T v[ND];
     G g[ND];
     O own;
+    G elo{}, ehi{};  // ADJ: the gathers of rows wb - 1 and wb + 64
+    T ev = T(0);     // ADJ with SYM: row wb - 1's entry on the +1 diagonal
+    // ADJ with SYM: the -1 diagonal's value comes from lane t - 1
+    auto shifted_val = [&](int q) { return ADJ && SYM && q == d0 - 1 && col.sym != 0; };
     auto load = [&](int64_t t) {
         const int64_t row0 = t * kTileRows;
         const int64_t left = n - row0;
@@ -247,17 +309,37 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
         own = of(i);
 #pragma unroll
         for (int q = 0; q < ND; ++q) {
-            if constexpr (SYM)
-                v[q] = dia_entry<T, ND>(vf, col, q, i, n);
-            else
-                v[q] = vf((int64_t)q * n + i);
+            if (!shifted_val(q)) {
+                if constexpr (SYM)
+                    v[q] = dia_entry<T, ND>(vf, col, q, i, n);
+                else
+                    v[q] = vf((int64_t)q * n + i);
+            }
+            if (ADJ && (q == d0 - 1 || q == d0 + 1)) continue;
             int64_t c = i + col.off[q];
             c = c < 0 ? 0 : (c >= n ? n - 1 : c);
             g[q] = gf(q == d0 ? (int32_t)i : (int32_t)c);
         }
+        if constexpr (ADJ) {
+            // lane 0's row wb (rows past n take row n - 1, as above); its
+            // neighbours clamped into [0, n) like the gathered columns
+            const int64_t wb = row0 + kWaveSize * (int64_t)__builtin_amdgcn_readfirstlane(tid >> 6);
+            const int64_t lo = wb < 1 ? 0 : (wb - 1 < n ? wb - 1 : n - 1);
+            const int64_t hi = wb + kWaveSize < n ? wb + kWaveSize : n - 1;
+            elo = gs(lo);
+            ehi = gs(hi);
+            if constexpr (SYM) {
+                if (col.sym) ev = wb >= 1 ? vs((int64_t)(d0 + 1) * n + lo) : T(0);
+            }
+        }
     };
     auto use = [&](int64_t t) {
         const int64_t i = t * kTileRows + tid;
+        if constexpr (ADJ) {
+            g[d0 - 1] = lane_shift<0x138>(g[d0], elo);
+            g[d0 + 1] = lane_shift<0x130>(g[d0], ehi);
+            if (shifted_val(d0 - 1)) v[d0 - 1] = lane_shift<0x138>(v[d0 + 1], ev);
+        }
         T s = T(0);
 #pragma unroll
         for (int q = 0; q < ND; ++q) s = fma(v[q], cf(g[q]), s);

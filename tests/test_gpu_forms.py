@@ -117,6 +117,79 @@ def test_diagonal_major_matches_csr_values_bitwise(hip, case):
         assert np.array_equal(np.asarray(u), np.asarray(v)), name
 
 
+# A seven-band operator shaped like a 3D stencil on a 61 x 67 x 63 grid
+# (offsets +-1, +-61, +-4087): too few planes per workgroup for the z-walk, so
+# the iterations take the fast diagonal-major tiles, whose +-1 gathers come
+# from the adjacent lanes and, for the lanes at a wavefront's edges, from
+# scalar loads.  n = 257481 spans 1006 tiles (more than one per workgroup)
+# and ends 201 rows into the last one, inside its fourth wavefront.  Past
+# 768 tiles these solves launch 96 workgroups per XCD while the CSR-value
+# iterations launch up to 128, so their partial sums are added in another
+# order: the check is the oracle's iterates at fixed counts (every lane's
+# neighbours enter from the first iteration on), and converged solves
+# within rounding of each other.  The 5000-row cases above compare the same
+# tiles with the CSR-value iterations bit for bit (one grid there).
+FAST_OFFSETS = (-4087, -61, -1, 0, 1, 61, 4087)
+
+
+def fast_problem(symmetric):
+    return banded("seven_band", 61 * 67 * 63, FAST_OFFSETS, symmetric, seed=3)
+
+
+@pytest.mark.parametrize("symmetric", [True, False], ids=["cg", "bicgstab"])
+def test_fast_tiles_fixed_counts_match_oracle(hip, symmetric):
+    """Forward and adjoint iterates after 1, 6 and 7 iterations (both
+    parities of the CG kernel) on the fast tiles equal the oracle's to
+    1e-12."""
+    banner(f"forms: fast tiles at fixed counts {'cg' if symmetric else 'bicgstab'}")
+    p = fast_problem(symmetric)
+    form = "diagonal-major-symmetric" if symmetric else "diagonal-major"
+    for k in (1, 6, 7):
+        g = gpu_forward_adjoint(hip, p, maxit=k)
+        assert g["info"]["form"] == g["ainfo"]["form"] == form, (g["info"]["form"], k)
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert g["info"]["iters"][0] == r.iters[0], (k, g["info"]["iters"], r.iters)
+        assert g["ainfo"]["iters"][0] == a.iters[0], (k, g["ainfo"]["iters"], a.iters)
+        assert relerr(g["x"][0], r.x[0]) <= 1e-12, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= 1e-12, k
+        assert relerr(g["gv"][0], a.grad_values[0]) <= 1e-12, k
+        g["pattern"].close()
+
+
+@pytest.mark.parametrize("symmetric", [True, False], ids=["cg", "bicgstab"])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_fast_tiles_converge_with_csr_values(hip, dtype, symmetric):
+    """Converged forward + adjoint on the fast tiles and on the caller's CSR
+    values (diagonal masks, every gather loaded) agree within rounding: 1e-8
+    in fp64 (tol 1e-10), 1e-4 in fp32 (tol 1e-5)."""
+    import torch
+    banner(f"forms: fast tiles converged {np.dtype(dtype).name} {'cg' if symmetric else 'bicgstab'}")
+    p = fast_problem(symmetric)
+    tol, agree = 1e-10, 1e-8
+    if dtype == np.float32:
+        p = p.astype(np.float32)
+        tol, agree = 1e-5, 1e-4
+    outs = []
+    for dmaj in (True, False):
+        rp = torch.from_numpy(p.row_ptr).cuda()
+        col = torch.from_numpy(p.col).cuda()
+        val = torch.from_numpy(p.values).cuda()
+        b = torch.from_numpy(p.b).cuda()
+        xt = torch.from_numpy(p.x_t).cuda()
+        pat = hip.Pattern(rp, col, dtype=val.dtype, build_transpose=not symmetric,
+                          diagonal_major=dmaj)
+        kw = dict(method=p.method, precond=p.precond, tol=tol, maxit=p.maxit)
+        x, info = pat.solve(val, b, **kw)
+        gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
+        assert info["status"][0] == 0 and ainfo["status"][0] == 0, (info, ainfo)
+        want = ("diagonal-major-symmetric" if symmetric else "diagonal-major") if dmaj else "diagonal"
+        assert info["form"] == ainfo["form"] == want, (info["form"], ainfo["form"])
+        outs.append([t.cpu().numpy().astype(np.float64) for t in (x, gv, gb)])
+        pat.close()
+    for u, v in zip(outs[0], outs[1]):
+        assert relerr(u, v) <= agree
+
+
 def test_unsymmetric_values_read_every_diagonal(hip):
     """CG on a mirrored pattern reads the lower diagonals through their
     mirrors only in systems whose values the pack finds symmetric bit for
