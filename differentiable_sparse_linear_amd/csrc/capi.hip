@@ -243,8 +243,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
     a.cols.sym = cg && dmaj && mirrored(op.it) ? 1 : 0;
     // CG on a 3D seven-point form walks each column of planes (z-walk)
     const int zw = cg ? cg_zwalk_plan(a.cols, n, (int64_t)sizeof(T)) : 0;
-    // the fast diagonal-major tiles: 32-bit offsets, +-1 gathers across lanes
-    const bool fast = dia_fast(a.cols, n, (int64_t)sizeof(T));
+    // the diagonal-major tiles: general, fast (32-bit offsets, +-1 gathers
+    // across lanes) or fast with row pairs
+    const int tile = dia_tile(a.cols, n, (int64_t)sizeof(T));
     a.x = x;
     a.b = b;
     a.r = vp(0);
@@ -351,13 +352,13 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                 return e;
             return launch_cg_split_w<T, IT>(jac, false, ad, dpos, n, nsys, k & 1, ss);
         }
-        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, fast, ad, n, nsys, k & 1, ss);
+        if (cg) return launch_cg_iter<T, IT>(slots, cm, jac, zw, tile, ad, n, nsys, k & 1, ss);
         if (bsplit) {
             if ((e = bicg_half(ss, k, 0)) != hipSuccess) return e;
             return bicg_half(ss, k, 1);
         }
-        if ((e = launch_bicg_xpv<T, IT>(slots, cm, fast, ad, n, nsys, ss)) != hipSuccess) return e;
-        return launch_bicg_st<T, IT>(slots, cm, fast, ad, n, nsys, ss);
+        if ((e = launch_bicg_xpv<T, IT>(slots, cm, tile, ad, n, nsys, ss)) != hipSuccess) return e;
+        return launch_bicg_st<T, IT>(slots, cm, tile, ad, n, nsys, ss);
     };
 
     if (o.profile) {
@@ -381,7 +382,7 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                 HIP_TRY(hipEventRecord(h->prof_ev[ev + 1], s));
                 ev += 2;
             } else if (cg) {
-                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, fast, ad, n, 1, k & 1, s,
+                HIP_TRY(launch_cg_iter<T, IT>(slots, cm, jac, zw, tile, ad, n, 1, k & 1, s,
                                               &h->prof_ev[ev]));
                 ev += 2;
             } else if (bsplit) {  // each half's three launches between stream events
@@ -392,9 +393,9 @@ sla_status grid_solve_group(sla_ctx *h, const Operator &op, const T *val, const 
                     ev += 2;
                 }
             } else {
-                HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, fast, ad, n, 1, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_xpv<T, IT>(slots, cm, tile, ad, n, 1, s, &h->prof_ev[ev]));
                 ev += 2;
-                HIP_TRY(launch_bicg_st<T, IT>(slots, cm, fast, ad, n, 1, s, &h->prof_ev[ev]));
+                HIP_TRY(launch_bicg_st<T, IT>(slots, cm, tile, ad, n, 1, s, &h->prof_ev[ev]));
                 ev += 2;
             }
             if ((k & 63) == 63 || k + 1 == launches) {

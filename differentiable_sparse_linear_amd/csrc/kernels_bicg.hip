@@ -88,9 +88,10 @@ struct XpvOwn {
 #ifndef SLA_BICG_WAVES
 #define SLA_BICG_WAVES 5
 #endif
-// O32 (both kernels): the fast diagonal-major tiles (dia_fast): 32-bit byte
-// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ).
-template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
+// O32 (both kernels): the fast diagonal-major tiles (dia_tile): 32-bit byte
+// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ);
+// PAIR: the same with two rows per lane (fp64, dia_rows_pair).
+template <typename T, typename IT, int SLOTS, int CM, bool O32 = false, bool PAIR = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 3 : SLA_BICG_WAVES)))
 void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
@@ -189,6 +190,49 @@ void bicg_xpv_kernel(const IterArgs<T, IT> *__restrict__ A) {
     };
     double rv_acc = 0.0, rr_acc = 0.0;
     auto ld = [&](gptr<const T> v, int64_t i) -> T { return *elem<O32>(v, i); };
+    if constexpr (PAIR) {
+        static_assert(O32 && sizeof(T) == 8, "row pairs: fast fp64 tiles");
+        auto ld2 = [&](gptr<const T> v, int64_t i) -> pair_t {
+            return *(const __attribute__((address_space(1))) pair_t *)elem<O32>(v, i);
+        };
+        auto put2 = [&](gptr<T> v, int64_t i, pair_t a) {
+            *(__attribute__((address_space(1))) pair_t *)elem<O32>(v, i) = a;
+        };
+        const bool go = dia_rows_pair<SLOTS, false>(
+            walk_tiles(pair_tiles_of(n), stopped), n, col_src<CM>(A->cols),
+            [&](int64_t k) { return ld2(val, k); }, nullptr,
+            [&](int64_t c) {
+                return G4<pair_t>{ld2(sv, c), ld2(tv, c), ld2(pold, c), ld2(vold, c)};
+            },
+            [&](int64_t c) { return G4<T>{sld(sv, c), sld(tv, c), sld(pold, c), sld(vold, c)}; },
+            pj,
+            [&](int64_t i) {
+                return XpvOwn<pair_t>{ld2(sv, i), ld2(tv, i), ld2(pold, i), ld2(vold, i),
+                                      first ? pair_t{0.0, 0.0} : ld2((gptr<const T>)x, i),
+                                      ld2(rh, i)};
+            },
+            [&](int64_t i, T acc0, T acc1, const XpvOwn<pair_t> &o, T, T) {
+                const pair_t ri = {rj(o.s.x, o.t.x), rj(o.s.y, o.t.y)};
+                if (!first) {
+                    put2(x, i, pair_t{fmaB(omega, o.s.x, fmaB(alpha, o.p.x, o.x.x)),
+                                      fmaB(omega, o.s.y, fmaB(alpha, o.p.y, o.x.y))});
+                    put2(r, i, ri);
+                }
+                put2(pnew, i, pair_t{pj(G4<T>{o.s.x, o.t.x, o.p.x, o.v.x}),
+                                     pj(G4<T>{o.s.y, o.t.y, o.p.y, o.v.y})});
+                put2(vnew, i, pair_t{acc0, acc1});
+                rv_acc = fma(o.rh.x, acc0, rv_acc);
+                rr_acc = fma(ri.x, ri.x, rr_acc);
+                rv_acc = fma(o.rh.y, acc1, rv_acc);
+                rr_acc = fma(ri.y, ri.y, rr_acc);
+            },
+            pre, post);
+        if (!go) return;
+        double v[2] = {rv_acc, rr_acc};
+        const int slot[2] = {kBiRV, kBiRR};
+        store_partials<2>(v, A->part, slot);
+        return;
+    }
     auto rows = [&](auto vf, auto gf, auto of, auto rf) {
         if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
             return dia_rows<T, SLOTS, false, true>(
@@ -234,7 +278,7 @@ struct StOwn {
 // on ||r_j|| (converged, then maxit) and rho_j = 0 (breakdown);
 // alpha_j = rho_j / rhat.v_j (rhat.v_j = 0: breakdown); s = r - alpha v
 // evaluated while gathering, t = A s; partials t.s, t.t, s.s, rhat.s, rhat.t.
-template <typename T, typename IT, int SLOTS, int CM, bool O32 = false>
+template <typename T, typename IT, int SLOTS, int CM, bool O32 = false, bool PAIR = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? 3 : SLA_BICG_WAVES)))
 void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     A += blockIdx.y;  // system blockIdx.y of the launch
@@ -296,6 +340,41 @@ void bicg_st_kernel(const IterArgs<T, IT> *__restrict__ A) {
     auto sk = [&](const G2<T> &g) -> T { return fmaB(-alpha, g.b, g.a); };
     double ts = 0.0, tt = 0.0, ss = 0.0, rs = 0.0, rt = 0.0;
     auto ld = [&](gptr<const T> w, int64_t i) -> T { return *elem<O32>(w, i); };
+    if constexpr (PAIR) {
+        static_assert(O32 && sizeof(T) == 8, "row pairs: fast fp64 tiles");
+        auto ld2 = [&](gptr<const T> w, int64_t i) -> pair_t {
+            return *(const __attribute__((address_space(1))) pair_t *)elem<O32>(w, i);
+        };
+        auto put2 = [&](gptr<T> w, int64_t i, pair_t a) {
+            *(__attribute__((address_space(1))) pair_t *)elem<O32>(w, i) = a;
+        };
+        const bool go = dia_rows_pair<SLOTS, false>(
+            walk_tiles(pair_tiles_of(n), stopped), n, col_src<CM>(A->cols),
+            [&](int64_t k) { return ld2(val, k); }, nullptr,
+            [&](int64_t c) { return G2<pair_t>{ld2(r, c), ld2(v, c)}; },
+            [&](int64_t c) { return G2<T>{sld(r, c), sld(v, c)}; }, sk,
+            [&](int64_t i) { return StOwn<pair_t>{ld2(r, i), ld2(v, i), ld2(rh, i)}; },
+            [&](int64_t i, T acc0, T acc1, const StOwn<pair_t> &o, T, T) {
+                const pair_t si = {sk(G2<T>{o.r.x, o.v.x}), sk(G2<T>{o.r.y, o.v.y})};
+                put2(s, i, si);
+                put2(tv, i, pair_t{acc0, acc1});
+                const T sh[2] = {si.x, si.y}, ah[2] = {acc0, acc1}, rhh[2] = {o.rh.x, o.rh.y};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    ts = fma(ah[h], sh[h], ts);
+                    tt = fma(ah[h], ah[h], tt);
+                    ss = fma(sh[h], sh[h], ss);
+                    rs = fma(rhh[h], sh[h], rs);
+                    rt = fma(rhh[h], ah[h], rt);
+                }
+            },
+            pre, post);
+        if (!go) return;
+        double red5[5] = {ts, tt, ss, rs, rt};
+        const int slot[5] = {kBiTS, kBiTT, kBiSS, kBiRS, kBiRT};
+        store_partials<5>(red5, A->part, slot);
+        return;
+    }
     auto rows = [&](auto vf, auto gf, auto of, auto rf) {
         if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
             return dia_rows<T, SLOTS, false, true>(
@@ -542,11 +621,24 @@ __global__ __launch_bounds__(kBlock) void bicg_split_st_w_kernel(const IterArgs<
 
 // ------------------------------------------------------------------ launchers
 
+// Row pairs: fp64 only (dia_tile never asks them for other types), and not
+// on seven diagonals, where bicg_xpv's pairs (four vectors gathered at four
+// offsets) need more than the 168 registers of three waves per SIMD and
+// spill: those take the one-row fast tiles.
+template <typename T>
+bool bicg_pair(int cm, int tile, int slots) {
+    return sizeof(T) == 8 && cm == kColDiaMajor && tile == kDiaTilePair && slots < 7;
+}
 #define SLA_BICG_O32(slots, ...)                                   \
     switch (slots) {                                               \
         case 3: { constexpr int kS = 3; __VA_ARGS__; } break;      \
         case 5: { constexpr int kS = 5; __VA_ARGS__; } break;      \
         default: { constexpr int kS = 7; __VA_ARGS__; } break;     \
+    }
+#define SLA_BICG_PAIR(slots, ...)                                  \
+    switch (slots) {                                               \
+        case 3: { constexpr int kS = 3; __VA_ARGS__; } break;      \
+        default: { constexpr int kS = 5; __VA_ARGS__; } break;     \
     }
 
 template <typename T, typename IT>
@@ -571,10 +663,15 @@ hipError_t launch_bicg_init(int cm, const IterArgs<T, IT> *a, int64_t n, int nsy
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_xpv(int slots, int cm, int tile, const IterArgs<T, IT> *a, int64_t n,
                            int nsys, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, 0, n), nsys);
-    if (fast && cm == kColDiaMajor) {
+    if (bicg_pair<T>(cm, tile, slots)) {
+        if constexpr (sizeof(T) == 8)
+            SLA_BICG_PAIR(slots, launch_maybe_timed(
+                                     bicg_xpv_kernel<T, IT, kS, kColDiaMajor, true, true>, grid,
+                                     dim3(kBlock), 0, s, ev, a));
+    } else if (tile != kDiaTileGeneral && cm == kColDiaMajor) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_xpv_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
     } else {
@@ -585,10 +682,15 @@ hipError_t launch_bicg_xpv(int slots, int cm, bool fast, const IterArgs<T, IT> *
 }
 
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_st(int slots, int cm, int tile, const IterArgs<T, IT> *a, int64_t n,
                           int nsys, hipStream_t s, const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, 0, n), nsys);
-    if (fast && cm == kColDiaMajor) {
+    if (bicg_pair<T>(cm, tile, slots)) {
+        if constexpr (sizeof(T) == 8)
+            SLA_BICG_PAIR(slots, launch_maybe_timed(
+                                     bicg_st_kernel<T, IT, kS, kColDiaMajor, true, true>, grid,
+                                     dim3(kBlock), 0, s, ev, a));
+    } else if (tile != kDiaTileGeneral && cm == kColDiaMajor) {
         SLA_BICG_O32(slots, launch_maybe_timed(bicg_st_kernel<T, IT, kS, kColDiaMajor, true>,
                                                grid, dim3(kBlock), 0, s, ev, a));
     } else {
@@ -601,9 +703,9 @@ hipError_t launch_bicg_st(int slots, int cm, bool fast, const IterArgs<T, IT> *a
 #define SLA_INST(T, IT)                                                                        \
     template hipError_t launch_bicg_init<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,    \
                                                 hipStream_t);                                  \
-    template hipError_t launch_bicg_xpv<T, IT>(int, int, bool, const IterArgs<T, IT> *, int64_t, \
+    template hipError_t launch_bicg_xpv<T, IT>(int, int, int, const IterArgs<T, IT> *, int64_t, \
                                                int, hipStream_t, const hipEvent_t *);          \
-    template hipError_t launch_bicg_st<T, IT>(int, int, bool, const IterArgs<T, IT> *, int64_t, int, \
+    template hipError_t launch_bicg_st<T, IT>(int, int, int, const IterArgs<T, IT> *, int64_t, int, \
                                               hipStream_t, const hipEvent_t *);               \
     template hipError_t launch_bicg_split<T, IT>(int, const IterArgs<T, IT> *, int64_t, int,  \
                                                  hipStream_t);

@@ -132,14 +132,16 @@ __global__ __launch_bounds__(kBlock) void cg_init_kernel(const IterArgs<T, IT> *
 // streams the values, p, x and the vectors written here with non-temporal
 // hints (grids far beyond the Infinity Cache, where these are touched once
 // per iteration and L2 is better left to the plane's +-N neighbours).
-// O32: the fast diagonal-major tiles (ZW == 0, dia_fast): 32-bit byte
-// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ).
+// O32: the fast diagonal-major tiles (ZW == 0, dia_tile): 32-bit byte
+// offsets (elem) and the +-1 gathers from the adjacent lanes (dia_rows ADJ);
+// PAIR: the same with two rows per lane (fp64, dia_rows_pair).
 template <typename T, typename IT, bool JAC, int SLOTS, int PH, int CM, int ZW = 0,
-          bool O32 = false>
+          bool O32 = false, bool PAIR = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(CM == kColDiaMajor ? (ZW ? 4 : 3) : SLA_CG_WAVES)))
 void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
     static_assert(!ZW || (CM == kColDiaMajor && SLOTS == 7), "the z-walk is for seven diagonals");
     static_assert(!O32 || (CM == kColDiaMajor && !ZW), "32-bit offsets: diagonal-major tiles");
+    static_assert(!PAIR || (O32 && sizeof(T) == 8), "row pairs: fast fp64 tiles");
     constexpr bool NT = ZW == 2;
     A += blockIdx.y;
     SolveState *st = A->st;
@@ -282,16 +284,54 @@ void cg_iter_kernel(const IterArgs<T, IT> *__restrict__ A) {
             return CgOwn<T>{ld(uc, i), ld(wc, i), ld(sprev, i), ld(pprev, i),
                             PH ? ld((gptr<const T>)x, i) : T(0)};
         };
-        if constexpr (O32)  // and the +-1 gathers from the adjacent lanes
+        if constexpr (PAIR) {
+            auto ld2 = [&](gptr<const T> v, int64_t i) -> pair_t {
+                return *(const __attribute__((address_space(1))) pair_t *)elem<O32>(v, i);
+            };
+            auto put2 = [&](gptr<T> v, int64_t i, pair_t a) {
+                *(__attribute__((address_space(1))) pair_t *)elem<O32>(v, i) = a;
+            };
+            // row's updates and partial-sum terms for rows i and i + 1
+            auto row2 = [&](int64_t i, T acc0, T acc1, const CgOwn<pair_t> &o, T a0, T a1) {
+                const pair_t pi = {fmaT(beta, o.p.x, o.u.x), fmaT(beta, o.p.y, o.u.y)};
+                const pair_t si = {s_of(o.w.x, o.s.x), s_of(o.w.y, o.s.y)};
+                const pair_t ui = {fmaT(-alpha, si.x, o.u.x), fmaT(-alpha, si.y, o.u.y)};
+                if (PH)
+                    put2(x, i, pair_t{fmaT(alpha, pi.x, fmaT(alpha_prev, o.p.x, o.x.x)),
+                                      fmaT(alpha, pi.y, fmaT(alpha_prev, o.p.y, o.x.y))});
+                put2(p, i, pi);
+                put2(sc, i, si);
+                put2(un, i, ui);
+                put2(wn, i, pair_t{JAC ? acc0 / a0 : acc0, JAC ? acc1 / a1 : acc1});
+                const T r0 = JAC ? a0 * ui.x : ui.x, r1 = JAC ? a1 * ui.y : ui.y;
+                g = fma(r0, ui.x, g);
+                d = fma(acc0, ui.x, d);
+                q = fma(r0, r0, q);
+                g = fma(r1, ui.y, g);
+                d = fma(acc1, ui.y, d);
+                q = fma(r1, r1, q);
+            };
+            go = dia_rows_pair<SLOTS, true>(
+                walk_tiles(pair_tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
+                [&](int64_t k) { return ld2(val, k); }, [&](int64_t k) { return sld(val, k); },
+                [&](int64_t c) { return G3<pair_t>{ld2(uc, c), ld2(wc, c), ld2(sprev, c)}; },
+                [&](int64_t c) { return G3<T>{sld(uc, c), sld(wc, c), sld(sprev, c)}; }, u_of,
+                [&](int64_t i) {
+                    return CgOwn<pair_t>{ld2(uc, i), ld2(wc, i), ld2(sprev, i), ld2(pprev, i),
+                                         PH ? ld2((gptr<const T>)x, i) : pair_t{0.0, 0.0}};
+                },
+                row2, pre, post);
+        } else if constexpr (O32) {  // and the +-1 gathers from the adjacent lanes
             go = dia_rows<T, SLOTS, true, true>(
                 walk_tiles(tiles_of(n), stopped), n, cg_cols<CM>(A->cols, st),
                 [&](auto k) { return ld(val, k); }, gath, u_of, own_of, row, pre, post,
                 [&](int64_t k) { return sld(val, k); },
                 [&](int64_t c) { return G3<T>{sld(uc, c), sld(wc, c), sld(sprev, c)}; });
-        else
+        } else {
             go = spmv_rows<T, IT, SLOTS, SLA_CG_ROUND, CM, true>(
                 walk_tiles(tiles_of(n), stopped), n, glb(A->rp), cg_cols<CM>(A->cols, st), sm,
                 [&](auto k) { return ld(val, k); }, gath, u_of, own_of, row, pre, post);
+        }
     }
     if (!go) return;
     double v[3] = {g, d, q};
@@ -519,14 +559,25 @@ hipError_t launch_cg_init(int slots, int cm, int zw, bool jac, const IterArgs<T,
 }
 
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, bool fast,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, int tile,
                           const IterArgs<T, IT> *a, int64_t n, int nsys, int ph, hipStream_t s,
                           const hipEvent_t *ev) {
     const dim3 grid(iter_grid(cm, zw, n), nsys);
-    const bool o32 = fast && cm == kColDiaMajor && zw == 0;
-#define SLA_CG_O32(J, P, S) \
-    launch_maybe_timed(cg_iter_kernel<T, IT, J, S, P, kColDiaMajor, 0, true>, grid, dim3(kBlock), \
-                       0, s, ev, a)
+    const bool o32 = tile != kDiaTileGeneral && cm == kColDiaMajor && zw == 0;
+    // row pairs: fp64 only (dia_tile never asks them for other types)
+    const bool pair = sizeof(T) == 8 && o32 && tile == kDiaTilePair;
+#define SLA_CG_O32(J, P, S)                                                                     \
+    do {                                                                                        \
+        if constexpr (sizeof(T) == 8) {                                                         \
+            if (pair) {                                                                         \
+                launch_maybe_timed(cg_iter_kernel<T, IT, J, S, P, kColDiaMajor, 0, true, true>, \
+                                   grid, dim3(kBlock), 0, s, ev, a);                            \
+                break;                                                                          \
+            }                                                                                   \
+        }                                                                                       \
+        launch_maybe_timed(cg_iter_kernel<T, IT, J, S, P, kColDiaMajor, 0, true>, grid,        \
+                           dim3(kBlock), 0, s, ev, a);                                          \
+    } while (0)
 #define SLA_CG_ITER(J, P)                                                                      \
     if (zw == 2)                                                                               \
         launch_maybe_timed(cg_iter_kernel<T, IT, J, 7, P, kColDiaMajor, 2>, grid,              \
@@ -627,7 +678,7 @@ template hipError_t launch_cg_lag<double>(const SolveState *, const double *, do
 #define SLA_INST(T, IT)                                                                         \
     template hipError_t launch_cg_init<T, IT>(int, int, int, bool, const IterArgs<T, IT> *,  \
                                               int64_t, int, hipStream_t);                       \
-    template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, bool,                    \
+    template hipError_t launch_cg_iter<T, IT>(int, int, bool, int, int,                     \
                                               const IterArgs<T, IT> *, int64_t, int, int,       \
                                               hipStream_t, const hipEvent_t *);                 \
     template hipError_t launch_cg_split_init<T, IT>(bool, const IterArgs<T, IT> *, int64_t, int, \

@@ -342,21 +342,35 @@ __host__ __device__ inline int64_t tiles_of(int64_t n) { return (n + kTileRows -
 // -> 22.69 us per launch, BiCGStab on the 1024^2 upwind system 21.0 -> 20.5
 // us.  The z-walk's plan and the other forms use grid_for_tiles.
 constexpr int kDiaBlocksPerXcd = 96;
-
-// The fast form of the diagonal-major tile kernels (their O32
-// instantiations): every byte offset formed (at most nd * n values of
-// value_bytes) fits 32 bits, and the diagonals next to the main one are at
-// -1 and +1, so that their gathers come from the adjacent lanes (dia_rows
-// ADJ).  Other diagonal-major forms take the general tile kernels.
-inline bool dia_fast(const ColArgs &c, int64_t n, int64_t value_bytes) {
-    if (c.mode != kColDiaMajor || c.nd < 3 || c.nd > kMaxDiaMajor) return false;
-    const int d0 = c.nd / 2;
-    return (int64_t)c.nd * n * value_bytes <= (int64_t)0xffffffff && c.off[d0 - 1] == -1 &&
-           c.off[d0 + 1] == 1;
-}
 inline int iter_grid(int cm, int zw, int64_t n) {
     const int g = grid_for_tiles(tiles_of(n));
     return cm == kColDiaMajor && zw == 0 ? std::min(g, kNumXcd * kDiaBlocksPerXcd) : g;
+}
+
+// Tiles of the diagonal-major iteration kernels (not the z-walk), by
+// dia_tile: kDiaTileGeneral, the general ones; kDiaTileFast, 32-bit byte
+// offsets and the gathers of the -1 and +1 diagonals from the adjacent lanes
+// (dia_rows ADJ), when every byte offset formed (at most nd * n values)
+// fits 32 bits and the diagonals next to the main one are at -1 and +1;
+// kDiaTilePair, the same with two rows per lane (dia_rows_pair), for fp64
+// with n and every other offset even, on systems of more tiles than the
+// grid's workgroups (below that, pairs would halve the grid rather than a
+// workgroup's loads per row).
+constexpr int kDiaTileGeneral = 0, kDiaTileFast = 1, kDiaTilePair = 2;
+inline int dia_tile(const ColArgs &c, int64_t n, int64_t value_bytes) {
+    if (c.mode != kColDiaMajor || c.nd < 3 || c.nd > kMaxDiaMajor) return kDiaTileGeneral;
+    const int d0 = c.nd / 2;
+    if ((int64_t)c.nd * n * value_bytes > (int64_t)0xffffffff || c.off[d0 - 1] != -1 ||
+        c.off[d0 + 1] != 1)
+        return kDiaTileGeneral;
+    bool even = value_bytes == 8 && n % 2 == 0 && tiles_of(n) > kNumXcd * kDiaBlocksPerXcd;
+    for (int q = 0; q < c.nd; ++q)
+        if (q != d0 - 1 && q != d0 + 1) even = even && c.off[q] % 2 == 0;
+    return even ? kDiaTilePair : kDiaTileFast;
+}
+// tiles of 2 * kTileRows rows (dia_rows_pair)
+__host__ __device__ inline int64_t pair_tiles_of(int64_t n) {
+    return (n + 2 * kTileRows - 1) / (2 * kTileRows);
 }
 
 // Gather slots per row for the row-per-lane SpMV from the longest row:
@@ -490,10 +504,10 @@ template <typename T, typename IT>
 hipError_t launch_cg_init(int slots, int cm, int zw, bool jac, const IterArgs<T, IT> *a, int64_t n,
                           int nsys, hipStream_t s);
 // zw: 0, or the z-walk (cg_zwalk_plan) with plain (1) or non-temporal (2)
-// streams of the values and the vectors touched once; fast: dia_fast of the
-// operator form (without the z-walk)
+// streams of the values and the vectors touched once; tile: dia_tile of the
+// operator form (used without the z-walk)
 template <typename T, typename IT>
-hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, bool fast,
+hipError_t launch_cg_iter(int slots, int cm, bool jac, int zw, int tile,
                           const IterArgs<T, IT> *a, int64_t n, int nsys, int ph, hipStream_t s,
                           const hipEvent_t *ev = nullptr);
 // The z-walk of a seven-diagonal operator form on n rows (3D stencils: a
@@ -519,12 +533,12 @@ hipError_t launch_cg_split_w(bool jac, bool init, const IterArgs<T, IT> *a, cons
 // BiCGStab (grid path; nsys systems, argument blocks a[0 .. nsys))
 template <typename T, typename IT>
 hipError_t launch_bicg_init(int cm, const IterArgs<T, IT> *a, int64_t n, int nsys, hipStream_t s);
-// fast: dia_fast of the operator form
+// tile: dia_tile of the operator form
 template <typename T, typename IT>
-hipError_t launch_bicg_xpv(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_xpv(int slots, int cm, int tile, const IterArgs<T, IT> *a, int64_t n,
                            int nsys, hipStream_t s, const hipEvent_t *ev = nullptr);
 template <typename T, typename IT>
-hipError_t launch_bicg_st(int slots, int cm, bool fast, const IterArgs<T, IT> *a, int64_t n,
+hipError_t launch_bicg_st(int slots, int cm, int tile, const IterArgs<T, IT> *a, int64_t n,
                           int nsys, hipStream_t s, const hipEvent_t *ev = nullptr);
 // BiCGStab in six launches per iteration for operators with a row plan:
 // part 0 (first half's updates), [p -> v product], 1 (its partials),

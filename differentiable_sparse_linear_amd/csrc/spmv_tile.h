@@ -358,6 +358,144 @@ __device__ __forceinline__ bool dia_rows(const TileRange &tr, int64_t n,
     return true;
 }
 
+// Two consecutive fp64 values, 8-byte aligned: one 16-byte wavefront load
+// or store (global memory needs 4-byte alignment for it).
+typedef double pair_t __attribute__((ext_vector_type(2), aligned(8)));
+
+// Row H (0: the first, 1: the second) of a pair, for a gather of several
+// vectors at one column.
+template <int H>
+__device__ __forceinline__ double half(pair_t v) {
+    return H ? v.y : v.x;
+}
+template <int H>
+__device__ __forceinline__ G2<double> half(const G2<pair_t> &v) {
+    return G2<double>{half<H>(v.a), half<H>(v.b)};
+}
+template <int H>
+__device__ __forceinline__ G3<double> half(const G3<pair_t> &v) {
+    return G3<double>{half<H>(v.a), half<H>(v.b), half<H>(v.c)};
+}
+template <int H>
+__device__ __forceinline__ G4<double> half(const G4<pair_t> &v) {
+    return G4<double>{half<H>(v.a), half<H>(v.b), half<H>(v.c), half<H>(v.d)};
+}
+
+// dia_rows (with ADJ) for fp64 values taking two consecutive rows per lane:
+// lane t of a tile of 2 * kTileRows rows takes rows i = row0 + 2t and i + 1,
+// and every load and store moves the pair's two values as one 16-byte
+// access.  On MI355X a wavefront load of 16 bytes per lane keeps the texture
+// addresser busy about 20 cycles and one of 8 bytes about 18 (a probe of L2
+// resident loads), so the pairs need little more than half of its time per
+// row; CG on the 1e6-row 3D diffusion system: 21.6 -> 20.2 us per launch.
+// Requires n even and every offset but the -1 and +1 ones even, so that no
+// pair straddles the ends of a vector: the pair at an even column c holds
+// columns c and c + 1, both inside [0, n) or both outside (those clamped to
+// the pair at 0 or n - 2; their padding values are 0).  The -1 and +1
+// gathers come from the lane's own pair and, for the rows at its ends, from
+// lanes t - 1 and t + 1 by lane shifts (gs at a wavefront's edges); with SYM
+// the -1 diagonal's values are row i - 1's (lane t - 1, or vs) and row i's
+// entries on the +1 diagonal.  vf2, gf2 and of2 load pairs; rf2(i, s0, s1,
+// own, d0, d1) consumes both rows' products and diagonal entries.  A row's
+// terms and their order are those of dia_rows; each thread adds its two
+// rows' contributions to the partial sums in row order, so the partial sums
+// are added in another order than with one row per lane.
+template <int ND, bool SYM, typename VF2, typename VS, typename GF2, typename GS, typename CF,
+          typename OF2, typename RF2, typename PRE, typename POST>
+__device__ __forceinline__ bool dia_rows_pair(const TileRange &tr, int64_t n,
+                                              const ColSrc<kColDiaMajor> &col, VF2 vf2, VS vs,
+                                              GF2 gf2, GS gs, CF cf, OF2 of2, RF2 rf2, PRE pre,
+                                              POST post) {
+    static_assert(ND >= 3 && ND <= kMaxDiaMajor && (ND & 1), "diagonal count");
+    using GP = decltype(gf2(0));  // the gathered vectors' pairs at a column
+    using G = decltype(gs(0));    // the same for one row
+    using O = decltype(of2(0));
+    constexpr int d0 = ND / 2;
+    constexpr int64_t kRows = 2 * kTileRows;
+    const int tid = threadIdx.x;
+    const int64_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool msym = SYM && col.sym != 0;
+    pair_t v[ND];
+    GP g[ND];
+    O own;
+    G elo{}, ehi{};  // the gathers of rows wb - 1 and wb + 128
+    double ev = 0.0;  // with msym: row wb - 1's entry on the +1 diagonal
+    auto load = [&](int64_t t) {
+        const int64_t row0 = t * kRows;
+        int64_t i = row0 + 2 * tid;
+        i = i < n - 2 ? i : n - 2;  // pairs past the end read the last one
+        own = of2(i);
+#pragma unroll
+        for (int q = 0; q < ND; ++q) {
+            if (q == d0 - 1 && msym) {
+                // from lane t - 1 and this pair's +1 diagonal
+            } else if (SYM && q < d0 && msym) {
+                // rows i + off[q] and i + 1 + off[q] on the mirrored diagonal
+                const int64_t j = i + col.off[q];
+                const pair_t m = vf2(j >= 0 ? (int64_t)(ND - 1 - q) * n + j : (int64_t)q * n + i);
+                v[q] = j >= 0 ? m : pair_t{0.0, 0.0};
+            } else {
+                v[q] = vf2((int64_t)q * n + i);
+            }
+            if (q == d0 - 1 || q == d0 + 1) continue;
+            int64_t c = i + col.off[q];
+            c = c < 0 ? 0 : (c > n - 2 ? n - 2 : c);
+            g[q] = gf2(q == d0 ? i : c);
+        }
+        const int64_t wb = row0 + 2 * kWaveSize * wave;  // lane 0's first row
+        const int64_t lo = wb < 1 ? 0 : (wb - 1 < n ? wb - 1 : n - 1);
+        const int64_t hi = wb + 2 * kWaveSize < n ? wb + 2 * kWaveSize : n - 1;
+        elo = gs(lo);
+        ehi = gs(hi);
+        if constexpr (SYM) {
+            if (msym) ev = wb >= 1 ? vs((int64_t)(d0 + 1) * n + lo) : 0.0;
+        }
+    };
+    auto use = [&](int64_t t) {
+        const int64_t i = t * kRows + 2 * tid;
+        const G g0 = half<0>(g[d0]), g1 = half<1>(g[d0]);
+        const G gm = lane_shift<0x138>(g1, elo);  // row i - 1
+        const G gp = lane_shift<0x130>(g0, ehi);  // row i + 2
+        double m0, m1;  // the -1 diagonal's values of rows i and i + 1
+        if (msym) {
+            m0 = lane_shift<0x138>(v[d0 + 1].y, ev);
+            m1 = v[d0 + 1].x;
+        } else {
+            m0 = v[d0 - 1].x;
+            m1 = v[d0 - 1].y;
+        }
+        double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+        for (int q = 0; q < ND; ++q) {
+            if (q == d0 - 1) {
+                s0 = fma(m0, cf(gm), s0);
+                s1 = fma(m1, cf(g0), s1);
+            } else if (q == d0) {
+                s0 = fma(v[q].x, cf(g0), s0);
+                s1 = fma(v[q].y, cf(g1), s1);
+            } else if (q == d0 + 1) {
+                s0 = fma(v[q].x, cf(g1), s0);
+                s1 = fma(v[q].y, cf(gp), s1);
+            } else {
+                s0 = fma(v[q].x, cf(half<0>(g[q])), s0);
+                s1 = fma(v[q].y, cf(half<1>(g[q])), s1);
+            }
+        }
+        if (i < n) rf2(i, s0, s1, own, v[d0].x, v[d0].y);
+    };
+    int64_t t = tr.first;
+    if (t < tr.end) load(t);
+    pre();
+    __syncthreads();
+    if (!post()) return false;
+    if (t < tr.end) use(t);
+    for (t += tr.stride; t < tr.end; t += tr.stride) {
+        load(t);
+        use(t);
+    }
+    return true;
+}
+
 // Rows of a seven-diagonal operator walked along its outermost offset
 // D = off[6] = -off[0] (a 3D stencil's plane of D rows; off[2] = -1,
 // off[4] = 1).  The plan (cg_zwalk_plan, in col.zw_*) cuts every plane into

@@ -190,6 +190,75 @@ def test_fast_tiles_converge_with_csr_values(hip, dtype, symmetric):
         assert relerr(u, v) <= agree
 
 
+# Row pairs (fp64, n and the offsets other than +-1 even, more tiles than the
+# grid's 768 workgroups): two consecutive rows per lane, 16-byte accesses.
+# Five bands at +-1 and +-510 on n = 510 x 403 = 205530 rows (402 tiles of
+# 512 rows, the last one 218 rows long, ending inside its second wavefront),
+# CG on symmetric values and BiCGStab; seven bands shaped like a 62 x 64 x 67
+# grid (+-1, +-62, +-3968; n = 265856, the last tile one wavefront long), CG.
+# BiCGStab on seven diagonals keeps one row per lane (its pair kernel would
+# spill), as does fp32.
+PAIR_CASES = [
+    ("five_band_cg", (-510, -1, 0, 1, 510), 510 * 403, True),
+    ("five_band_bicgstab", (-510, -1, 0, 1, 510), 510 * 403, False),
+    ("seven_band_cg", (-3968, -62, -1, 0, 1, 62, 3968), 62 * 64 * 67, True),
+]
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_pair_tiles_fixed_counts_match_oracle(hip, case):
+    """Forward and adjoint iterates after 1, 6 and 7 iterations on the row
+    pair tiles equal the oracle's to 1e-12."""
+    name, offsets, n, symmetric = case
+    banner(f"forms: pair tiles at fixed counts {name}")
+    p = banded(name, n, offsets, symmetric, seed=4)
+    form = "diagonal-major-symmetric" if symmetric else "diagonal-major"
+    for k in (1, 6, 7):
+        g = gpu_forward_adjoint(hip, p, maxit=k)
+        assert g["info"]["form"] == g["ainfo"]["form"] == form, (g["info"]["form"], k)
+        r, a = oracle_forward_adjoint(p, maxit=k)
+        assert g["info"]["iters"][0] == r.iters[0], (k, g["info"]["iters"], r.iters)
+        assert g["ainfo"]["iters"][0] == a.iters[0], (k, g["ainfo"]["iters"], a.iters)
+        assert relerr(g["x"][0], r.x[0]) <= 1e-12, k
+        assert relerr(g["gb"][0], a.grad_b[0]) <= 1e-12, k
+        assert relerr(g["gv"][0], a.grad_values[0]) <= 1e-12, k
+        g["pattern"].close()
+
+
+@pytest.mark.parametrize("case", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_pair_tiles_converge_with_csr_values(hip, case):
+    """Converged forward + adjoint on the row pair tiles and on the caller's
+    CSR values (diagonal masks, one row per lane) agree to 1e-8 (tol 1e-10),
+    and with the oracle's to the parity tolerance."""
+    import torch
+    name, offsets, n, symmetric = case
+    banner(f"forms: pair tiles converged {name}")
+    p = banded(name, n, offsets, symmetric, seed=4)
+    outs = []
+    for dmaj in (True, False):
+        rp = torch.from_numpy(p.row_ptr).cuda()
+        col = torch.from_numpy(p.col).cuda()
+        val = torch.from_numpy(p.values).cuda()
+        b = torch.from_numpy(p.b).cuda()
+        xt = torch.from_numpy(p.x_t).cuda()
+        pat = hip.Pattern(rp, col, build_transpose=not symmetric, diagonal_major=dmaj)
+        kw = dict(method=p.method, precond=p.precond, tol=p.tol, maxit=p.maxit)
+        x, info = pat.solve(val, b, **kw)
+        gv, gb, ainfo = pat.solve_adjoint(val, x, x - xt, **kw)
+        assert info["status"][0] == 0 and ainfo["status"][0] == 0, (info, ainfo)
+        want = ("diagonal-major-symmetric" if symmetric else "diagonal-major") if dmaj else "diagonal"
+        assert info["form"] == ainfo["form"] == want, (info["form"], ainfo["form"])
+        outs.append([t.cpu().numpy() for t in (x, gv, gb)])
+        pat.close()
+    for u, v in zip(outs[0], outs[1]):
+        assert relerr(u, v) <= 1e-8
+    r, a = oracle_forward_adjoint(p)
+    tol = FP_TOL[np.dtype(np.float64)]["sol"]
+    assert relerr(outs[0][0], r.x[0]) <= tol
+    assert relerr(outs[0][1], a.grad_values[0]) <= tol
+    assert relerr(outs[0][2], a.grad_b[0]) <= tol
+
+
 def test_unsymmetric_values_read_every_diagonal(hip):
     """CG on a mirrored pattern reads the lower diagonals through their
     mirrors only in systems whose values the pack finds symmetric bit for
