@@ -142,7 +142,11 @@ typedef struct {
  *               offsets must pair up around the main one) reads only the
  *               main and upper diagonals, the lower entries through their
  *               mirrors (sla_solve_info.form = 4).  Results are identical as
- *               long as the iterates stay finite.
+ *               long as the iterates stay finite on systems of at most
+ *               196 608 rows (768 tiles of 256); on larger ones the
+ *               diagonal-major iterations run fewer workgroups (and, in
+ *               fp64, two rows per lane), so their dot products add the
+ *               same terms in another order and results agree to rounding.
  *               Other bits: SLA_ERR_ARG.
  * Workspace: CG and BiCGStab on a batch of systems with n > 4096 advance a
  * group of min(batch, 65535, 2^21 / n) systems (at least 1) per grid
