@@ -40,7 +40,11 @@ null when no such record matches the sources being run.  ``dram_GBps`` and
 ``dram_frac`` are that traffic over the average launch time; ``model_frac``
 (= ``frac``) and ``kernel_frac`` price the launch at the textbook and the
 fused kernel's own bytes.  ``ceilings`` are the chip's streaming and LDS
-bandwidths measured in the same run by libsla_probe.so over 2 GiB arrays.
+bandwidths measured in the same run by libsla_probe.so over 2 GiB arrays
+(beyond the 256 MB Infinity Cache) and, as ``*_in_cache``, over 64 MiB
+arrays that stay in it; ``dram_frac_of_copy_ceiling`` and
+``dram_frac_of_in_cache_copy_ceiling`` set the traffic against the two
+copies.
 On the one-workgroup solver (at most 4096 rows) the roofline is LDS
 bandwidth: (S + 11) values per row and iteration (S the gather slots).
 ``memory`` is the device memory of one forward + adjoint step.
@@ -86,6 +90,7 @@ CSRC = os.path.join(ROOT, "differentiable_sparse_linear_amd", "csrc")
 PROBE_LIB = os.path.join(ROOT, "differentiable_sparse_linear_amd", "libsla_probe.so")
 CALIB_BYTES = 1 << 30  # the calibration kernels move 1 GiB each way
 CEIL_BYTES = 2 << 30   # arrays of the ceiling measurement (beyond the 256 MB Infinity Cache)
+CACHE_CEIL_BYTES = 64 << 20  # arrays of the in-cache ceilings (a copy touches 128 MiB)
 # request-size counters of the optional third counter pass (bytes per request)
 SIZE_COUNTERS = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64,
                  "TCC_EA0_RDREQ_128B_sum": 128}
@@ -654,6 +659,8 @@ def probe_lib():
         lib.sla_probe_copy.restype = I32
         lib.sla_probe_write.argtypes = [P, I64, D, P]
         lib.sla_probe_write.restype = I32
+        lib.sla_probe_copy_passes.argtypes = [P, P, I64, I32, P]
+        lib.sla_probe_copy_passes.restype = I32
         lib.sla_probe_lds.argtypes = [I64, P, P]
         lib.sla_probe_lds.restype = I64
         _probe = lib
@@ -715,11 +722,42 @@ def measure_ceilings(dev):
     ev1.record(stream)
     torch.cuda.synchronize()
     lds_s = ev0.elapsed_time(ev1) * 1e-3
+    in_cache = in_cache_copy(dev)
     return {"read_GBps": CEIL_BYTES / t["read"] / 1e9,
             "copy_GBps": 2 * CEIL_BYTES / t["copy"] / 1e9,
             "write_GBps": CEIL_BYTES / t["write"] / 1e9,
             "lds_GBps": lds_bytes / lds_s / 1e9,
-            "arrays_bytes": CEIL_BYTES, "kernels": "libsla_probe.so (non-temporal, 16 B per access)"}
+            "arrays_bytes": CEIL_BYTES,
+            "copy_GBps_in_cache": in_cache, "in_cache_arrays_bytes": CACHE_CEIL_BYTES,
+            "kernels": "libsla_probe.so (16 B per access; non-temporal over 2 GiB, plain "
+                       "in the cache)"}
+
+
+def in_cache_copy(dev, passes=32, reps=10):
+    """Copy bandwidth in GB/s with both arrays (CACHE_CEIL_BYTES each) in the
+    Infinity Cache: sla_probe_copy_passes, `passes` ping-pong copies per
+    launch, timed with events over `reps` launches after one untimed."""
+    import torch
+    lib = probe_lib()
+    n = CACHE_CEIL_BYTES // 8
+    a = torch.rand(n, dtype=torch.float64, device=dev)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    if lib.sla_probe_copy_passes(_vp(a), _vp(b), n, passes, sp) != 0:
+        raise RuntimeError("probe copy_passes failed")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(reps):
+        lib.sla_probe_copy_passes(_vp(a), _vp(b), n, passes, sp)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    s = ev0.elapsed_time(ev1) * 1e-3 / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return passes * 2 * CACHE_CEIL_BYTES / s / 1e9
 
 
 # ------------------------------------------------------------------ benchmark
@@ -1023,6 +1061,11 @@ def main():
                     "kernel_frac": own / k_avg_s / 1e9 / HBM_PEAK_GBPS,
                     "dram_GBps": dram, "dram_frac": dram / HBM_PEAK_GBPS if dram else None,
                     "dram_frac_of_copy_ceiling": dram / ceilings["copy_GBps"] if dram else None,
+                    # a working set within the Infinity Cache (the 1e6-row
+                    # 3D diffusion system's) is read past L2 from the cache
+                    # and written into it: this is its ceiling
+                    "dram_frac_of_in_cache_copy_ceiling":
+                        dram / ceilings["copy_GBps_in_cache"] if dram else None,
                     "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
                     "hbm_target": "at least 70 % of peak HBM bandwidth, read as dram_frac "
                                   "(bytes past L2 by the counters; model_frac prices a launch at "

@@ -4,6 +4,8 @@
 //   read   sum of a[0..n) (each element read once; one partial per block)
 //   copy   b = a
 //   write  b = v
+//   copy_passes  b = a + 1, a = b + 1, ... over arrays that stay in the
+//          256 MB Infinity Cache, one launch (the in-cache copy ceiling)
 //   lds    workgroups (two resident per compute unit) each read their own
 //          64 KB of LDS over and over
 //
@@ -78,6 +80,33 @@ __global__ __launch_bounds__(kThreads) void write_kernel(v2d *__restrict__ b, in
         st(x, &b[i]);
 }
 
+// In-cache copy: `passes` passes over two arrays of n2 16-byte elements,
+// small enough to stay in the Infinity Cache, with plain accesses so that
+// their lines stay there; pass p reads one array and writes the other.  A
+// thread touches the same elements in every pass, so the passes need no
+// barrier between them, and each pass's values depend on the last one's.
+constexpr int kPassBlocks = 256 * 8;  // eight workgroups per compute unit
+
+__global__ __launch_bounds__(kThreads) void copy_passes_kernel(v2d *__restrict__ a,
+                                                               v2d *__restrict__ b, int64_t n2,
+                                                               int32_t passes) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    const int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    for (int32_t p = 0; p < passes; ++p) {
+        const v2d *src = (p & 1) ? b : a;
+        v2d *dst = (p & 1) ? a : b;
+        int64_t i = i0;
+        for (; i + (kUnroll - 1) * stride < n2; i += kUnroll * stride) {
+            v2d x[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) x[u] = src[i + u * stride];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) dst[i + u * stride] = x[u] + 1.0;
+        }
+        for (; i < n2; i += stride) dst[i] = src[i] + 1.0;
+    }
+}
+
 // LDS reads: thread t reads 16 bytes at a rotating offset of a 64 KB block
 // of LDS (consecutive lanes take consecutive 16-byte words, no bank
 // conflicts); the sum keeps the reads alive.
@@ -128,6 +157,13 @@ int32_t sla_probe_write(void *d_b, int64_t n, double v, void *stream) {
     if (!d_b || n < 2 || (n & 1)) return -1;
     write_kernel<<<kBlocks, kThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         reinterpret_cast<v2d *>(d_b), n / 2, v);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int32_t sla_probe_copy_passes(void *d_a, void *d_b, int64_t n, int32_t passes, void *stream) {
+    if (!d_a || !d_b || n < 2 || (n & 1) || passes < 1) return -1;
+    copy_passes_kernel<<<kPassBlocks, kThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        reinterpret_cast<v2d *>(d_a), reinterpret_cast<v2d *>(d_b), n / 2, passes);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -31,6 +31,13 @@ int32_t sla_probe_copy(const void *d_a, void *d_b, int64_t n, void *stream);
 /* d_b[0..n) = v (n even).  Moves n * 8 bytes. */
 int32_t sla_probe_write(void *d_b, int64_t n, double v, void *stream);
 
+/* In-cache copy ceiling: `passes` passes over d_a and d_b (n doubles each,
+ * n even, no overlap; 64 MiB each stays in the 256 MB Infinity Cache), pass
+ * p reading one and writing the other with plain loads and stores
+ * (d_b = d_a + 1, d_a = d_b + 1, ...); one launch of 2048 workgroups.
+ * Moves passes * 2 * n * 8 bytes. */
+int32_t sla_probe_copy_passes(void *d_a, void *d_b, int64_t n, int32_t passes, void *stream);
+
 /* 2048 workgroups (two resident per compute unit, 1024 threads each) read
  * 16 bytes per thread from their LDS 4 * reps times; returns the bytes read
  * from LDS over the launch (< 0 on error).  d_part holds at least 2048

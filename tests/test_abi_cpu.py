@@ -48,8 +48,8 @@ def test_probe_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "sla_probe.h")).read(),
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(sla_probe_[a-z_]+)\s*\(", text)))
-    assert names == ["sla_probe_blocks", "sla_probe_copy", "sla_probe_lds", "sla_probe_read",
-                     "sla_probe_write"]
+    assert names == ["sla_probe_blocks", "sla_probe_copy", "sla_probe_copy_passes",
+                     "sla_probe_lds", "sla_probe_read", "sla_probe_write"]
     lib = ctypes.CDLL(b.PROBE_LIB)
     assert all(hasattr(lib, f) for f in names)
     # argument checks return before any launch
