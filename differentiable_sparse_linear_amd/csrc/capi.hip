@@ -74,6 +74,8 @@ struct sla_ctx {
     int32_t *perm = nullptr;     // A's position of each A^T entry
     int32_t *pinv = nullptr;     // A^T's position of each A entry
     void *val_t = nullptr;       // one system's values (or products) in A^T's order
+    int32_t *bpos = nullptr;     // where the terms pass stores each A entry's term (or null)
+    uint16_t *lidx = nullptr;    // for the row sums: each such term's offset in its tile
     int slots = 8;   // gather slots per row (A), from its longest row
     int max_len = 0; // longest row of A
     int slots_t = 8; // the same for A^T
@@ -159,6 +161,8 @@ void release(sla_ctx *h) {
     (void)hipFree(h->perm);
     (void)hipFree(h->pinv);
     (void)hipFree(h->val_t);
+    (void)hipFree(h->bpos);
+    (void)hipFree(h->lidx);
     (void)hipFree(h->dia);
     for (auto &pm : h->plan_mem)
         for (void *p : pm) (void)hipFree(p);
@@ -844,6 +848,14 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
             h->ws_bytes -= (int64_t)sizeof(int32_t) * 2 * kMaxDiags;
         }
     }
+    // the two-pass A^T products of the per-entry column forms write their
+    // terms tile by tile of A^T in A's entry order (setup_buckets)
+    if (h->has_t && h->ca.mode != kColDiag) {
+        HIP_TRY(dmalloc(h, &h->bpos, sizeof(int32_t) * nnz));
+        HIP_TRY(dmalloc(h, &h->lidx, sizeof(uint16_t) * nnz));
+        HIP_TRY(setup_buckets<IT>(reinterpret_cast<const IT *>(h->rp_t), h->perm, h->plan_t, n,
+                                  nnz, h->bpos, h->lidx, s));
+    }
     // The iterations read diagonal-major values for patterns on 3, 5 or 7
     // diagonals with the main one in the middle (nearest-neighbour stencils
     // in 1, 2 and 3 dimensions) whose padding -- the slots of boundary rows
@@ -1109,25 +1121,19 @@ sla_status eigsh_one(sla_ctx *h, const T *val, const sla_eig_opts &o, int m, dou
 namespace {
 
 // The backward pass and A^T products of the per-entry column forms go in two
-// passes (A's rows scatter the terms v_k g_i to A^T's order in the handle's
-// buffer, then A^T's rows are summed) one system at a time, for single
-// systems and for patterns of at least this many entries; smaller batches
-// read A^T's values through the transpose map in one launch for all.
+// passes (A's rows write the terms v_k g_i to the handle's buffer at bpos,
+// then A^T's rows are summed, the terms of a run put back in A^T's order in
+// LDS) one system at a time, for single systems and for patterns of at least
+// this many entries; smaller batches read A^T's values through the transpose
+// map in one launch for all.  Both ways give the same bits.  On power-law
+// graphs the A^T product alone took 74.9 / 224.7 / 440.4 us in two passes at
+// 2^20 / 2^21 / 2^22 rows, against 332.0 / 669.3 us through the map at
+// 2^21 / 2^22 and 112.4 us at 2^20 when the first pass wrote every term
+// straight to its place in A^T's order.
 constexpr int64_t kScatterMinEntries = (int64_t)1 << 20;
 
-// The A^T product alone (no gradient pass in between) keeps the two passes
-// only while the terms, the values and the inverse map (nnz * (2 s_v + 4)
-// bytes) stay well within the 256 MB Infinity Cache: beyond it the scattered
-// partial-line writes reach HBM, and on a 2^21-row power-law graph the
-// product took 350 us in two passes against 330 us through the map (at 2^20
-// rows 112 against 162 us).  The backward pass with both outputs took less
-// in two passes at every size measured.  Both ways give the same bits.
-constexpr int64_t kScatterCacheBytes = (int64_t)192 << 20;
-
-template <typename T>
-bool two_pass(const sla_ctx *h, int batch, bool with_gradient) {
-    if (h->ca.mode == kColDiag || !(batch == 1 || h->nnz >= kScatterMinEntries)) return false;
-    return with_gradient || h->nnz * (int64_t)(2 * sizeof(T) + 4) <= kScatterCacheBytes;
+bool two_pass(const sla_ctx *h, int batch) {
+    return h->ca.mode != kColDiag && h->bpos && (batch == 1 || h->nnz >= kScatterMinEntries);
 }
 
 // For `batch` systems: grad_x = A^T g (when gx is not null) and grad_values
@@ -1140,14 +1146,14 @@ hipError_t product_backward(sla_ctx *h, const T *v, const T *x, const T *g, T *g
     const int64_t n = h->n, nnz = h->nnz;
     if (h->ca.mode == kColDiag)  // both outputs from one pass over A's rows
         return launch_diag_vjp<T, IT>(rp, h->ca, v, nnz, g, x, gx, gv, n, nnz, batch, false, s);
-    if (gx && two_pass<T>(h, batch, gv != nullptr)) {
+    if (gx && two_pass(h, batch)) {
         T *c = reinterpret_cast<T *>(h->val_t);
         for (int sys = 0; sys < batch; ++sys) {
-            hipError_t e = launch_terms_t<T, IT>(rp, h->ca, g + sys * n, v + sys * nnz, h->pinv, c,
+            hipError_t e = launch_terms_t<T, IT>(rp, h->ca, g + sys * n, v + sys * nnz, h->bpos, c,
                                                  n, nnz, 1, s, &h->plan);
             if (e == hipSuccess)
                 e = launch_rowsum<T, IT>(rpt, c, nnz, nullptr, nullptr, nullptr, gx + sys * n, n,
-                                         1, s, &h->plan_t);
+                                         1, s, &h->plan_t, h->lidx);
             if (e != hipSuccess) return e;
         }
     } else if (gx) {

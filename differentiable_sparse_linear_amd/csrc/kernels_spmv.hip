@@ -274,9 +274,12 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(const IT *__restrict__ rp,
 //    form for a batch of systems in one launch.
 // A tile's terms are staged in LDS as one run, then thread t adds row t's
 // one after another (the order and the rounding of the row plan's short
-// blocks).  Tiles that plan_tiles flags are left to the row plan; other
-// tiles past the stage take one wavefront per row (lane-strided partial
-// sums, then a fixed-order wavefront sum).
+// blocks).  With lidx (!PERM) the staged tiles' terms are in A's entry
+// order in t and go to their places in A^T's order in LDS (lidx[k]: the
+// offset in the tile of the term at k; setup_buckets).  Tiles that
+// plan_tiles flags are left to the row plan (whose short blocks honour lidx
+// the same way); other tiles past the stage take one wavefront per row
+// (lane-strided partial sums, then a fixed-order wavefront sum).
 template <typename T, typename IT, bool PERM>
 __global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ rp,
                                                         const T *__restrict__ t,
@@ -285,7 +288,8 @@ __global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ r
                                                         const int32_t *__restrict__ col,
                                                         const T *__restrict__ g,
                                                         T *__restrict__ y, int64_t n,
-                                                        const uint8_t *plan_tiles) {
+                                                        const uint8_t *plan_tiles,
+                                                        const uint16_t *__restrict__ lidx) {
     __shared__ IT srp[kTileRows + 1];
     __shared__ T sc[kCap];
     const int sys = blockIdx.y;
@@ -321,6 +325,17 @@ __global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ r
                     const int e = tid + j * kBlock;
                     v[j] = e < cnt ? ts[pj[j]] * gs[cj[j]] : T(0);
                 }
+            } else if (lidx) {
+                int dst[kEpt];
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j) {
+                    const int e = tid + j * kBlock;
+                    v[j] = e < cnt ? ts[base + e] : T(0);
+                    dst[j] = e < cnt ? (int)lidx[base + e] & (kCap - 1) : -1;
+                }
+#pragma unroll
+                for (int j = 0; j < kEpt; ++j)
+                    if (dst[j] >= 0) sc[dst[j]] = v[j];
             } else {
 #pragma unroll
                 for (int j = 0; j < kEpt; ++j) {
@@ -328,8 +343,10 @@ __global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ r
                     v[j] = e < cnt ? ts[base + e] : T(0);
                 }
             }
+            if (PERM || !lidx) {
 #pragma unroll
-            for (int j = 0; j < kEpt; ++j) sc[tid + j * kBlock] = v[j];
+                for (int j = 0; j < kEpt; ++j) sc[tid + j * kBlock] = v[j];
+            }
             __syncthreads();
             if (tid < rows) {
                 const int hi = (int)(srp[tid + 1] - base);
@@ -366,8 +383,9 @@ __global__ __launch_bounds__(kBlock) void rowsum_kernel(const IT *__restrict__ r
 constexpr int kPlanA = 0, kPlanPerm = 1, kPlanSum = 2;
 
 // Products of one item.  Short block: the run's products v x[col] go to
-// LDS in one coalesced pass, then thread t adds row r0 + t's products in
-// entry order.  Long-row chunk: thread t takes entries t, t + 256, ... of
+// LDS in one coalesced pass (kPlanSum with lidx: the terms the scatter pass
+// wrote in A's entry order, each to its offset lidx[k] in A^T's order),
+// then thread t adds row r0 + t's products in entry order.  Long-row chunk: thread t takes entries t, t + 256, ... of
 // the chunk (all loads first, then an fma chain), a fixed-order workgroup
 // sum, y[row] or the chunk's partial.
 template <typename T, typename IT, int MODE>
@@ -375,7 +393,8 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
     const int32_t *__restrict__ perm, const T *__restrict__ val, int64_t val_stride,
     const T *__restrict__ x, T *__restrict__ y, int64_t vec_stride, T *__restrict__ part,
-    int32_t nslots, const IterArgs<T, IT> *ind) {
+    int32_t nslots, const IterArgs<T, IT> *ind, const uint16_t *__restrict__ lidx) {
+    static_assert((kPlanCap & (kPlanCap - 1)) == 0, "lidx offsets are masked to the block");
     if (sys_stopped(ind)) return;
     __shared__ T prod[kPlanCap];
     __shared__ T wsum[kWaves];
@@ -402,10 +421,22 @@ __global__ __launch_bounds__(kBlock) void plan_spmv_kernel(
         }
     }
     if (it.kind == 0) {
+        if (MODE == kPlanSum && lidx) {  // terms in A's order: back to A^T's
+            int dst[kPlanEpt];
 #pragma unroll
-        for (int j = 0; j < kPlanEpt; ++j) {
-            const int e = tid + j * kBlock;
-            if (e < cnt) prod[e] = pv[j] * px[j];
+            for (int j = 0; j < kPlanEpt; ++j) {
+                const int e = tid + j * kBlock;
+                dst[j] = e < cnt ? (int)lidx[e0 + e] & (kPlanCap - 1) : -1;
+            }
+#pragma unroll
+            for (int j = 0; j < kPlanEpt; ++j)
+                if (dst[j] >= 0) prod[dst[j]] = pv[j] * px[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPlanEpt; ++j) {
+                const int e = tid + j * kBlock;
+                if (e < cnt) prod[e] = pv[j] * px[j];
+            }
         }
         __syncthreads();
         if (tid < it.r1 - it.r0) {
@@ -466,10 +497,16 @@ __global__ __launch_bounds__(kBlock) void plan_grad_kernel(
     const PlanItem *__restrict__ items, const IT *__restrict__ rp, const int32_t *__restrict__ col,
     const T *__restrict__ g, const T *__restrict__ x, T *__restrict__ grad,
     const T *__restrict__ val, const int32_t *__restrict__ pinv, T *__restrict__ c, int64_t n,
-    int64_t nnz) {
+    int64_t nnz, int32_t nitems) {
     static_assert(GV != SC, "one of the two outputs");
     __shared__ uint16_t rid[kPlanCap];
     __shared__ T sg[kTileRows];
+    // each XCD takes a contiguous range of items (workgroups go to the XCDs
+    // in turn), so the scatter pass's writes to one tile of A^T (pinv: the
+    // handle's bpos) come from one XCD in runs of consecutive addresses
+    const int per = (int)gridDim.x / kNumXcd;
+    const int64_t item = (int64_t)(blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
+    if (item >= nitems) return;
     const int sys = blockIdx.y;
     const gptr<const T> gs = glb(g + (int64_t)sys * n);
     const gptr<const T> xs = glb(GV ? x + (int64_t)sys * n : x);
@@ -478,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void plan_grad_kernel(
     const gptr<T> cs = glb(SC ? c + (int64_t)sys * nnz : c);
     const gptr<const int32_t> pv = glb(pinv);
     const gptr<const int32_t> cg = glb(col);
-    const PlanItem it = items[blockIdx.x];
+    const PlanItem it = items[item];
     const int tid = threadIdx.x;
     const int64_t e0 = it.e0;
     const int cnt = (int)(it.e1 - e0);
@@ -516,8 +553,8 @@ __global__ __launch_bounds__(kBlock) void plan_grad_kernel(
                 __builtin_nontemporal_store(NEG ? -p : p, &gr[e0 + e]);
             }
             if constexpr (SC) {
-                        if ((uint32_t)pj[j] < (uint64_t)nnz) cs[pj[j]] = vj[j] * gi;
-                    }
+                if ((uint32_t)pj[j] < (uint64_t)nnz) cs[pj[j]] = vj[j] * gi;
+            }
         }
     }
 }
@@ -638,10 +675,12 @@ inline bool planned(const RowPlan *plan) { return plan && plan->nitems > 0; }
 template <typename T, typename IT, int MODE>
 void launch_plan_spmv(const RowPlan &pl, const IT *rp, const int32_t *perm, const T *val,
                       int64_t val_stride, const T *x, T *y, int64_t vec_stride, int batch,
-                      hipStream_t s, const IterArgs<T, IT> *ind = nullptr) {
+                      hipStream_t s, const IterArgs<T, IT> *ind = nullptr,
+                      const uint16_t *lidx = nullptr) {
     T *part = reinterpret_cast<T *>(pl.part);
     plan_spmv_kernel<T, IT, MODE><<<dim3(pl.nitems, batch), kBlock, 0, s>>>(
-        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, ind);
+        pl.items, rp, pl.col, perm, val, val_stride, x, y, vec_stride, part, pl.nslots, ind,
+        lidx);
     if (pl.nfin > 0)
         plan_finish_kernel<T, IT>
             <<<dim3((pl.nfin + kWaves - 1) / kWaves, batch), kBlock, 0, s>>>(
@@ -723,8 +762,9 @@ void launch_grad_t(const IT *rp, const ColArgs &ca, const T *g, const T *x, T *g
             <<<grid, kBlock, 0, s>>>(rp, ca, g, x, grad, val, pinv, c, n, nnz, pt);
     }
     if (ps)
-        plan_grad_kernel<T, IT, NEG, GV, SC><<<dim3(plan->nitems, batch), kBlock, 0, s>>>(
-            plan->items, rp, plan->col, g, x, grad, val, pinv, c, n, nnz);
+        plan_grad_kernel<T, IT, NEG, GV, SC>
+            <<<dim3((plan->nitems + kNumXcd - 1) / kNumXcd * kNumXcd, batch), kBlock, 0, s>>>(
+                plan->items, rp, plan->col, g, x, grad, val, pinv, c, n, nnz, plan->nitems);
 }
 
 template <typename T, typename IT>
@@ -755,24 +795,24 @@ hipError_t launch_terms_t(const IT *rp, const ColArgs &ca, const T *g, const T *
 template <typename T, typename IT>
 hipError_t launch_rowsum(const IT *rp, const T *t, int64_t t_stride, const int32_t *perm,
                          const int32_t *col, const T *g, T *y, int64_t n, int batch,
-                         hipStream_t s, const RowPlan *plan) {
+                         hipStream_t s, const RowPlan *plan, const uint16_t *lidx) {
     const bool ps = planned(plan);
     const dim3 grid(grid_for_tiles(tiles_of(n)), batch);
     const uint8_t *pt = ps ? plan->tiles : nullptr;
     if (!ps || !plan->all_tiles) {
         if (perm)
             rowsum_kernel<T, IT, true><<<grid, kBlock, 0, s>>>(rp, t, t_stride, perm, col, g, y,
-                                                               n, pt);
+                                                               n, pt, nullptr);
         else
             rowsum_kernel<T, IT, false><<<grid, kBlock, 0, s>>>(rp, t, t_stride, nullptr,
-                                                                nullptr, nullptr, y, n, pt);
+                                                                nullptr, nullptr, y, n, pt, lidx);
     }
     if (ps) {
         if (perm)
             launch_plan_spmv<T, IT, kPlanPerm>(*plan, rp, perm, t, t_stride, g, y, n, batch, s);
         else
             launch_plan_spmv<T, IT, kPlanSum>(*plan, rp, nullptr, t, t_stride, nullptr, y, n,
-                                              batch, s);
+                                              batch, s, nullptr, lidx);
     }
     return hipGetLastError();
 }
@@ -835,7 +875,7 @@ hipError_t launch_publish(const int32_t *ndone, int32_t *poll, hipStream_t s) {
                                               int, hipStream_t, const RowPlan *);                \
     template hipError_t launch_rowsum<T, IT>(const IT *, const T *, int64_t, const int32_t *,  \
                                              const int32_t *, const T *, T *, int64_t, int,      \
-                                             hipStream_t, const RowPlan *);                      \
+                                             hipStream_t, const RowPlan *, const uint16_t *);    \
     template hipError_t launch_dinv<T, IT>(const IT *, const T *, int64_t, T *, int64_t,        \
                                            SolveState *, int, hipStream_t);                      \
     template hipError_t launch_dia_pack<T, IT>(const IT *, const ColArgs &, const T *, int64_t, \

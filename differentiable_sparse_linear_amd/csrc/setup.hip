@@ -708,6 +708,110 @@ hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t 
     return hipStreamSynchronize(s);
 }
 
+// Write positions of the two-pass A^T products (sla_ctx::bpos, lidx).  The
+// terms pass walks A's entries in order and stores entry k's term at
+// bpos[k]; the row sums then add A^T's rows tile by tile (kTileRows rows of
+// A^T).  With bpos = pinv every term is an 8-byte write to a scattered place
+// and a cache line of A^T's order is completed by many writes far apart in
+// time.  Instead, for each run of A^T's entries that the row sums stage in
+// LDS -- a tile of at most kCap entries outside A^T's row plan, or a short
+// block of the plan -- the run's entries are kept in A's entry order:
+// bpos[k] = the run's first A^T position + the rank of k among the run's
+// entries, and lidx at that position = the entry's offset in A^T's order
+// inside the run, so that the row sums put every term back in A^T's order in
+// LDS before adding.  Since each XCD walks a contiguous range of A's entries
+// (the tiles by xcd_tiles, the plan's items likewise), its writes to a run
+// land in one stretch of consecutive addresses.  The other entries keep
+// A^T's order (bpos = pinv; their lidx is not read).  One workgroup per
+// tile (bucket_kernel) or plan item (bucket_items_kernel).
+// One run of cnt <= kCap entries of A^T at base: sorts the pairs (perm[base
+// + e], e) by A's entry index in key[] (a bitonic network over the next
+// power of two, padded with the largest key), then entry k of rank r gets
+// bpos[k] = base + r and lidx[base + r] = its offset e.  Every thread of the
+// workgroup takes part.
+__device__ void bucket_run(int64_t *key, const int32_t *__restrict__ perm, int64_t base, int cnt,
+                           int64_t nnz, int32_t *__restrict__ bpos, uint16_t *__restrict__ lidx) {
+    const int tid = threadIdx.x;
+    int m = 1;
+    while (m < cnt) m <<= 1;
+    for (int e = tid; e < m; e += kSetupThreads)
+        key[e] = e < cnt ? ((int64_t)perm[base + e] << 16) | e : INT64_MAX;
+    __syncthreads();
+    for (int size = 2; size <= m; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < m / 2; i += kSetupThreads) {
+                const int a = 2 * i - (i & (stride - 1)), b = a + stride;
+                const int64_t ka = key[a], kb = key[b];
+                if ((ka > kb) == ((a & size) == 0)) {
+                    key[a] = kb;
+                    key[b] = ka;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int r = tid; r < cnt; r += kSetupThreads) {
+        const int64_t kv = key[r];
+        if ((kv >> 16) < nnz) bpos[kv >> 16] = (int32_t)(base + r);
+        lidx[base + r] = (uint16_t)(kv & 0xFFFF);
+    }
+}
+
+template <typename IT>
+__global__ __launch_bounds__(kSetupThreads) void bucket_kernel(const IT *__restrict__ rp_t,
+                                                               const int32_t *__restrict__ perm,
+                                                               const uint8_t *__restrict__ planned,
+                                                               int64_t n, int64_t nnz,
+                                                               int32_t *__restrict__ bpos,
+                                                               uint16_t *__restrict__ lidx) {
+    static_assert(kCap <= 65536, "offsets inside a tile fit 16 bits");
+    __shared__ int64_t key[kCap];
+    const int tid = threadIdx.x;
+    const int64_t tt = blockIdx.x;
+    const int64_t row0 = tt * kTileRows;
+    const int64_t rows = n - row0 < kTileRows ? n - row0 : kTileRows;
+    const int64_t base = (int64_t)rp_t[row0];
+    const int64_t cnt = (int64_t)rp_t[row0 + rows] - base;
+    if (planned && planned[tt]) return;  // bucket_items_kernel
+    if (cnt > kCap) {
+        for (int64_t e = tid; e < cnt; e += kSetupThreads) bpos[perm[base + e]] = (int32_t)(base + e);
+        return;
+    }
+    bucket_run(key, perm, base, (int)cnt, nnz, bpos, lidx);
+}
+
+// The same for the tiles A^T's row plan covers, item by item: a short block
+// (whole rows, at most kPlanCap entries) is listed in A's entry order; a
+// long row's chunk is in A's order already (a row of A^T lists its entries
+// by ascending row of A), so there bpos = pinv.
+__global__ __launch_bounds__(kSetupThreads) void bucket_items_kernel(
+    const PlanItem *__restrict__ items, const int32_t *__restrict__ perm, int64_t nnz,
+    int32_t *__restrict__ bpos, uint16_t *__restrict__ lidx) {
+    static_assert(kPlanCap <= kCap, "a short block fits the sort");
+    __shared__ int64_t key[kCap];
+    const PlanItem it = items[blockIdx.x];
+    const int64_t cnt = it.e1 - it.e0;
+    if (it.kind != 0) {
+        for (int64_t e = threadIdx.x; e < cnt; e += kSetupThreads)
+            bpos[perm[it.e0 + e]] = (int32_t)(it.e0 + e);
+        return;
+    }
+    bucket_run(key, perm, it.e0, (int)cnt, nnz, bpos, lidx);
+}
+
+template <typename IT>
+hipError_t setup_buckets(const IT *rp_t, const int32_t *perm, const RowPlan &plan_t, int64_t n,
+                         int64_t nnz, int32_t *bpos, uint16_t *lidx, hipStream_t s) {
+    const int64_t nt = (n + kTileRows - 1) / kTileRows;
+    const bool ps = plan_t.nitems > 0;
+    bucket_kernel<IT><<<(unsigned)nt, kSetupThreads, 0, s>>>(rp_t, perm, ps ? plan_t.tiles : nullptr,
+                                                             n, nnz, bpos, lidx);
+    if (ps)
+        bucket_items_kernel<<<(unsigned)plan_t.nitems, kSetupThreads, 0, s>>>(plan_t.items, perm,
+                                                                              nnz, bpos, lidx);
+    return hipGetLastError();
+}
+
 // Launchers of the single checks, for callers that keep their own flags
 // (each raises *flag or atomically maxes *out, which must start at 0); they
 // allocate nothing and do not synchronize.
@@ -757,7 +861,9 @@ hipError_t launch_max_row(const IT *rp, int64_t n, int32_t *out, hipStream_t s) 
                                         hipStream_t);                                          \
     template hipError_t setup_transpose<IT>(const IT *, const int32_t *, int64_t, int64_t,     \
                                             IT *, int32_t *, int32_t *, int32_t *,             \
-                                            SetupScratch &, hipStream_t);
+                                            SetupScratch &, hipStream_t);                         \
+    template hipError_t setup_buckets<IT>(const IT *, const int32_t *, const RowPlan &, int64_t, \
+                                          int64_t, int32_t *, uint16_t *, hipStream_t);
 SLA_SETUP_INST(int32_t)
 SLA_SETUP_INST(int64_t)
 #undef SLA_SETUP_INST

@@ -465,21 +465,24 @@ hipError_t launch_grad(const IT *rp, const ColArgs &ca, const T *lam, const T *x
                        int64_t n, int64_t nnz, int batch, bool neg, hipStream_t s,
                        const RowPlan *plan = nullptr);
 // A^T g for the per-entry column forms, first pass over A's rows: c[pinv[k]]
-// = val[k] g_i, the terms in A^T's entry order (pinv: A's entry -> A^T's); g
-// n apart, val and c nnz apart.
+// = val[k] g_i, the terms in A^T's entry order (pinv: A's entry -> A^T's, or
+// the handle's bpos, which lists the terms of the tiles launch_rowsum
+// stages in LDS in A's order); g n apart, val and c nnz apart.
 template <typename T, typename IT>
 hipError_t launch_terms_t(const IT *rp, const ColArgs &ca, const T *g, const T *val,
                           const int32_t *pinv, T *c, int64_t n, int64_t nnz, int batch,
                           hipStream_t s, const RowPlan *plan = nullptr);
 // y = A^T g row by row of A^T (rp, plan: A^T's row pointers and row plan),
 // every row's terms rounded and added in entry order: the terms the scatter
-// pass left in t (perm null; t_stride apart), or A's values t through the
-// transpose map perm with A^T's columns col and g (values t_stride apart,
-// g and y n apart).
+// pass left in t (perm null; t_stride apart; with lidx, the handle's map
+// of the tiles whose terms the pass wrote at bpos, in A's order), or A's
+// values t through the transpose map perm with A^T's columns col and g
+// (values t_stride apart, g and y n apart).
 template <typename T, typename IT>
 hipError_t launch_rowsum(const IT *rp, const T *t, int64_t t_stride, const int32_t *perm,
                          const int32_t *col, const T *g, T *y, int64_t n, int batch,
-                         hipStream_t s, const RowPlan *plan = nullptr);
+                         hipStream_t s, const RowPlan *plan = nullptr,
+                         const uint16_t *lidx = nullptr);
 // out[pinv[k]] = val[k]: one system's values in A^T's entry order.
 template <typename T>
 hipError_t launch_scatter(const int32_t *pinv, const T *val, T *out, int64_t nnz,
@@ -667,5 +670,13 @@ template <typename IT>
 hipError_t setup_transpose(const IT *rp, const int32_t *col, int64_t n, int64_t nnz, IT *rp_t,
                            int32_t *col_t, int32_t *perm, int32_t *pinv, SetupScratch &scr,
                            hipStream_t s);
+// Write positions of the two-pass A^T products from the transpose map:
+// bpos [nnz] (where the terms pass stores entry k's term) and lidx [nnz]
+// (for each of those places in a tile the row sums stage in LDS, the
+// entry's offset in A^T's order inside its tile or row-plan block), given
+// A^T's row plan (empty or not).  Does not synchronize.
+template <typename IT>
+hipError_t setup_buckets(const IT *rp_t, const int32_t *perm, const RowPlan &plan_t, int64_t n,
+                         int64_t nnz, int32_t *bpos, uint16_t *lidx, hipStream_t s);
 
 }  // namespace sla

@@ -118,7 +118,10 @@ typedef struct {
  *               sla_matvec_adjoint and by the BiCGStab adjoint): A^T's row
  *               pointers and rows, A's position of each A^T entry and A^T's
  *               position of each A entry (12 bytes per entry), and one
- *               system's buffer of nnz values; requires nnz < 2^31.
+ *               system's buffer of nnz values; for patterns whose products
+ *               read per-entry columns (no diagonal masks), 6 more bytes per
+ *               entry: where the two-pass A^T products store each entry's
+ *               term; requires nnz < 2^31.
  *               SLA_CREATE_WIDE_COLUMNS: read the caller's int32 columns in
  *               every product.  Without it the handle also keeps a compact
  *               copy (each column as an int16 offset from the first row of

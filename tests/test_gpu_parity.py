@@ -628,7 +628,11 @@ def test_compact_columns_change_nothing(hip):
         for o in outs[1:]:
             for a, b in zip(outs[0], o):
                 assert np.array_equal(a, b), p.name
-        assert ws[1] > ws[2], (p.name, ws)
+        # with per-entry columns (the wide form, and tile16) the handle also
+        # keeps the two-pass A^T products' write positions, 6 bytes per entry,
+        # which the diagonal-mask form does not need
+        extra = 6 * p.nnz if mode == "diagonal" else 0
+        assert ws[1] > ws[2] - extra, (p.name, ws)
         assert (ws[0] > ws[1]) == (form == "diagonal-major"), (p.name, ws)
     # offsets beyond int16 and more than 16 diagonals: no compact form
     rp, col, val = W.powerlaw_graph_laplacian(60000, 9)

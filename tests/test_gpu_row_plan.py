@@ -2,10 +2,10 @@
 gradient.
 
 The backward pass and the A^T products of a single system (or of any batch
-on a pattern of at least 2^20 entries) go in two passes: A's rows scatter
-the terms v_k g_i to A^T's entry order, then A^T's rows are summed; smaller
-batches read A^T's values through the transpose map (the 2^16-row batch of
-three).
+on a pattern of at least 2^20 entries) go in two passes: A's rows write the
+terms v_k g_i in runs of A^T's rows, then A^T's rows are summed (each run
+put back in A^T's order in LDS); smaller batches read A^T's values through
+the transpose map (the 2^16-row batch of three).
 
 Tiles whose entries exceed the tile walker's LDS stage, or that hold a row
 longer than its gather slots, are covered by a plan built at set-up: short
@@ -128,12 +128,30 @@ def test_repeat_is_bitwise(hip):
 
 
 def test_transposed_paths_agree_bitwise(hip):
-    """On a 2^21-row graph (1.75e7 entries) the A^T product alone reads A^T's
-    values through the transpose map, and the backward pass with both
-    outputs goes in two passes (scattered terms, then row sums): both round
-    each term and add them in the same order, so grad_x is the product's
-    bits.  The product is also checked against the oracle."""
-    banner("A^T through the map and in two passes, 2^21 rows")
+    """A^T products go in two passes for a single system (the terms written
+    in runs, then put back in A^T's order in LDS and summed) and through the
+    transpose map for a batch on a small pattern: both round each term and
+    add a row's terms in the same order, so they agree bit for bit.  On a
+    2^21-row graph (1.75e7 entries) the product alone and the backward pass
+    with both outputs give the same bits, and the product matches the
+    oracle."""
+    banner("A^T through the map and in two passes")
+    p = powerlaw(1 << 16, 11, batch=2)
+    d = to_dev(p)
+    one = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+    two = hip.Pattern(d["rp"], d["col"], batch=2, dtype=tdtype(p), build_transpose=True)
+    rng = np.random.default_rng(4)
+    g = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
+    x = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
+    yb = two.matvec(d["val"], g, transpose=True)
+    _, gxb = two.matvec_adjoint(d["val"], x, g)
+    for s in range(2):
+        ys = one.matvec(d["val"][s:s + 1].contiguous(), g[s:s + 1].contiguous(), transpose=True)
+        assert torch.equal(ys[0], yb[s]) and torch.equal(ys[0], gxb[s]), s
+    one.close()
+    two.close()
+
+    banner("A^T in two passes, 2^21 rows")
     p = powerlaw(1 << 21, 13)
     d = to_dev(p)
     pat = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
