@@ -555,11 +555,11 @@ def test_determinism_and_launch_modes_agree(hip):
 
 
 def test_replay_length_changes_nothing(hip):
-    """The default graph replay length follows the handle's previous grid
-    solve: 16 iterations on a fresh handle, 32 once a solve of the 1e6-DOF
-    workload has taken its ~480 iterations.  Those, and explicit lengths of
-    64 and 2, give bitwise the same solutions, adjoints and iteration
-    counts."""
+    """The default chunk length follows the handle's previous grid solve:
+    16 iterations on a fresh handle, 32 once a solve of the 1e6-DOF workload
+    has taken its ~480 iterations (at this size the chunks are launched
+    directly).  Those, and graph replays of 64 and 2 iterations, give
+    bitwise the same solutions, adjoints and iteration counts."""
     banner("replay lengths, 1e6 DOF")
     p = W.config(2)
     d = to_dev(p)
