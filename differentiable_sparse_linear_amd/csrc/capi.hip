@@ -105,6 +105,8 @@ struct sla_ctx {
     SolveState *st_host = nullptr;  // pinned [batch]
     hipStream_t cap = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
+    hipStream_t side = nullptr;  // the product backward's gradient pass, beside the A^T passes
+    hipEvent_t fork = nullptr, join = nullptr;
     std::vector<hipEvent_t> prof_ev;
     GraphEntry graphs[kGraphSlots];
     int graph_next = 0;          // next slot to replace when all are taken
@@ -160,6 +162,9 @@ void release(sla_ctx *h) {
     for (auto e : h->ev)
         if (e) (void)hipEventDestroy(e);
     if (h->cap) (void)hipStreamDestroy(h->cap);
+    if (h->side) (void)hipStreamDestroy(h->side);
+    if (h->fork) (void)hipEventDestroy(h->fork);
+    if (h->join) (void)hipEventDestroy(h->join);
     (void)hipFree(h->diagpos);
     (void)hipFree(h->col16);
     (void)hipFree(h->dlt);
@@ -916,6 +921,9 @@ sla_status create_typed(sla_ctx *h, int32_t flags, hipStream_t s) {
     HIP_TRY(hipMemsetAsync(h->st, 0, sizeof(SolveState) * h->batch, s));
     HIP_TRY(hipMemsetAsync(h->part, 0, sizeof(double) * kPartStride * h->gbatch, s));
     HIP_TRY(hipStreamCreateWithFlags(&h->cap, hipStreamNonBlocking));
+    HIP_TRY(hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&h->fork, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&h->join, hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&h->ev[0], hipEventDisableTiming));
     HIP_TRY(hipEventCreateWithFlags(&h->ev[1], hipEventDisableTiming));
     HIP_TRY(hipStreamSynchronize(s));
@@ -1164,6 +1172,16 @@ hipError_t product_backward(sla_ctx *h, const T *v, const T *x, const T *g, T *g
         return launch_diag_vjp<T, IT>(rp, h->ca, v, nnz, g, x, gx, gv, n, nnz, batch, false, s);
     if (gx && two_pass(h, batch)) {
         T *c = reinterpret_cast<T *>(h->val_t);
+        // the gradient pass (random x gathers) runs on a side stream beside
+        // the A^T passes (streaming reads, runs of writes)
+        if (gv) {
+            hipError_t e = hipEventRecord(h->fork, s);
+            if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+            if (e == hipSuccess)
+                e = launch_grad<T, IT>(rp, h->ca, g, x, gv, n, nnz, batch, false, h->side, &h->plan);
+            if (e == hipSuccess) e = hipEventRecord(h->join, h->side);
+            if (e != hipSuccess) return e;
+        }
         for (int sys = 0; sys < batch; ++sys) {
             hipError_t e = launch_terms_t<T, IT>(rp, h->ca, g + sys * n, v + sys * nnz, h->bpos, c,
                                                  n, nnz, 1, s, &h->plan);
@@ -1172,6 +1190,8 @@ hipError_t product_backward(sla_ctx *h, const T *v, const T *x, const T *g, T *g
                                          1, s, &h->plan_t, h->lidx);
             if (e != hipSuccess) return e;
         }
+        if (gv) return hipStreamWaitEvent(s, h->join, 0);
+        return hipSuccess;
     } else if (gx) {
         hipError_t e = launch_rowsum<T, IT>(rpt, v, nnz, h->perm, h->col_t, g, gx, n, batch, s,
                                             &h->plan_t);
