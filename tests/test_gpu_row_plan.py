@@ -136,20 +136,31 @@ def test_transposed_paths_agree_bitwise(hip):
     with both outputs give the same bits, and the product matches the
     oracle."""
     banner("A^T through the map and in two passes")
-    p = powerlaw(1 << 16, 11, batch=2)
-    d = to_dev(p)
-    one = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
-    two = hip.Pattern(d["rp"], d["col"], batch=2, dtype=tdtype(p), build_transpose=True)
-    rng = np.random.default_rng(4)
-    g = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
-    x = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
-    yb = two.matvec(d["val"], g, transpose=True)
-    _, gxb = two.matvec_adjoint(d["val"], x, g)
-    for s in range(2):
-        ys = one.matvec(d["val"][s:s + 1].contiguous(), g[s:s + 1].contiguous(), transpose=True)
-        assert torch.equal(ys[0], yb[s]) and torch.equal(ys[0], gxb[s]), s
-    one.close()
-    two.close()
+    # runs of A^T's rows of every kind: tiles the row sums stage whole, short
+    # blocks and long-row chunks of A^T's row plan, tiles past the stage
+    for name, p in (("powerlaw_2^16", powerlaw(1 << 16, 11, batch=2)),
+                    ("chunk_edges", CASES["chunk_edges"]()),
+                    ("star_20000", CASES["star_20000"]()),
+                    ("lengths_at_limits", CASES["lengths_at_limits"]())):
+        if p.batch == 1:  # a second system with its own values
+            p = W.Problem(p.name, p.n, p.row_ptr, p.col,
+                          np.concatenate([p.values, -0.5 * p.values]), np.zeros((2, p.n)),
+                          np.zeros((2, p.n)))
+        d = to_dev(p)
+        one = hip.Pattern(d["rp"], d["col"], dtype=tdtype(p), build_transpose=True)
+        two = hip.Pattern(d["rp"], d["col"], batch=2, dtype=tdtype(p), build_transpose=True)
+        rng = np.random.default_rng(4)
+        g = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
+        x = torch.from_numpy(rng.standard_normal((2, p.n))).cuda()
+        yb = two.matvec(d["val"], g, transpose=True)
+        _, gxb = two.matvec_adjoint(d["val"], x, g)
+        for s in range(2):
+            vs, gs = d["val"][s:s + 1].contiguous(), g[s:s + 1].contiguous()
+            ys = one.matvec(vs, gs, transpose=True)
+            _, gxs = one.matvec_adjoint(vs, x[s:s + 1].contiguous(), gs)
+            assert torch.equal(ys[0], yb[s]) and torch.equal(gxs[0], gxb[s]), (name, s)
+        one.close()
+        two.close()
 
     banner("A^T in two passes, 2^21 rows")
     p = powerlaw(1 << 21, 13)
