@@ -119,16 +119,19 @@ def parse():
                     help="summarise a rocprofv3 --pmc run of the one-workgroup solver's LDS "
                          "counters (workloads of at most 4096 rows)")
     ap.add_argument("--op", default="solve",
-                    choices=("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"),
-                    help="solve: the forward + adjoint step (default); matvec / matvec_vjp: "
-                         "the differentiable product and its backward pass on the same "
-                         "system, 100 x steps calls timed; inverse: kappa recovery through the "
+                    choices=("solve", "matvec", "matvec_t", "matvec_vjp", "inverse", "nonlinear",
+                             "eigsh"),
+                    help="solve: the forward + adjoint step (default); matvec / matvec_t / "
+                         "matvec_vjp: the differentiable product, the A^T product alone and "
+                         "the product's backward pass on the same system, 100 x steps calls "
+                         "timed; inverse: kappa recovery through the "
                          "differentiable solve (64 x 64 grid, 8 forcings, 40 x steps Adam "
                          "steps); nonlinear: differentiable Newton solve of A u + c u^3 = f "
                          "on the workload's matrix; eigsh: its largest eigenpair by Lanczos "
                          "and the eigenvalue gradient")
     ap.add_argument("--graph", action="store_true",
-                    help="with --op matvec / matvec_vjp: the seeded power-law graph Laplacian "
+                    help="with --op matvec / matvec_t / matvec_vjp: the seeded power-law graph "
+                         "Laplacian "
                          "(2^20 rows unless --size, seed 9; row lengths from 1 to 557 357) "
                          "instead of a numbered workload")
     ap.add_argument("--column-form", default="diagonal-major",
@@ -320,10 +323,12 @@ CACHE_COUNTERS = ("TCC_HIT_sum", "TCC_MISS_sum", "TCP_TCC_READ_REQ_sum",
 
 
 def product_model_bytes(op, p):
-    """Algorithmic bytes of one call of the product (op matvec) or its
-    backward pass (matvec_vjp: grad_x = A^T g and grad_values)."""
+    """Algorithmic bytes of one call of the product (op matvec), of the A^T
+    product (matvec_t, the same bytes: values and columns once, one vector
+    read, one written) or of the product's backward pass (matvec_vjp:
+    grad_x = A^T g and grad_values)."""
     sv, sr = p.values.itemsize, p.row_ptr.itemsize
-    if op == "matvec":
+    if op in ("matvec", "matvec_t"):
         return (p.nnz * (sv + 4) + (p.n + 1) * sr + 2 * p.n * sv) * p.batch
     return (p.nnz * (2 * sv + 4) + (p.n + 1) * sr + 3 * p.n * sv) * p.batch
 
@@ -356,7 +361,8 @@ def summarize_product_counters(args):
     if len(dirs) not in (2, 3, 4):
         raise SystemExit("--summarize-counters FETCH_DIR WRITE_DIR [SIZES_DIR [CACHE_DIR]]")
     calls = 20
-    which = " --graph" if args.graph else f" --workload {args.workload}"
+    which = (" --graph" + (f" --size {args.size}" if args.size else "") if args.graph
+             else f" --workload {args.workload}")
     run = f"python3 bench.py --op {args.op} --kernel-only 2{which}"
     fetch, f_pr = _product_table(dirs[0], "FETCH_SIZE", calls)
     write, w_pr = _product_table(dirs[1], "WRITE_SIZE", calls)
@@ -445,7 +451,7 @@ def summarize_product_counters(args):
 
 
 def summarize_counters(args):
-    if args.op in ("matvec", "matvec_vjp"):
+    if args.op in ("matvec", "matvec_t", "matvec_vjp"):
         return summarize_product_counters(args)
     p = load_problem(args)
     kernel, kbytes, own, srcs = dominant_kernel(p.method, p.precond, p.n, p.nnz,
@@ -884,6 +890,8 @@ def bench_product(args, p):
         for _ in range(args.kernel_only * 10):
             if args.op == "matvec":
                 pat.matvec(val, x, out=y)
+            elif args.op == "matvec_t":
+                pat.matvec(val, g, transpose=True, out=y)
             else:
                 pat.matvec_adjoint(val, x, g)
         torch.cuda.synchronize()
@@ -900,6 +908,13 @@ def bench_product(args, p):
         # values + columns + row pointers, x once, y written
         model = p.nnz * (sv + 4) + (p.n + 1) * sr + 2 * p.n * sv
         kernel = "spmv_kernel" + plan
+    elif args.op == "matvec_t":
+        call = lambda: pat.matvec(val, g, transpose=True, out=y)
+        model = product_model_bytes(args.op, p) // p.batch
+        # with diagonal masks one kernel reads A's own rows; else the terms
+        # pass over A's rows and the row sums of A^T
+        kernel = ("diag_vjp_kernel" if pat.column_mode() == "diagonal"
+                  else "grad_kernel+rowsum_kernel" + ("+plan_grad_kernel" if plan else "") + plan)
     else:
         call = lambda: pat.matvec_adjoint(val, x, g)
         # values + columns + row pointers once, g, x read, grad_x and
@@ -967,8 +982,8 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     sla.load()
-    if args.graph and args.op not in ("matvec", "matvec_vjp"):
-        print("--graph is for --op matvec / matvec_vjp", file=sys.stderr)
+    if args.graph and args.op not in ("matvec", "matvec_t", "matvec_vjp"):
+        print("--graph is for --op matvec / matvec_t / matvec_vjp", file=sys.stderr)
         sys.exit(2)
     if args.op == "inverse":
         return bench_inverse(args)

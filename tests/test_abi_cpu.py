@@ -99,7 +99,7 @@ def test_bench_modes_parse_and_refuse_more_gpus():
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    for op in ("solve", "matvec", "matvec_vjp", "inverse", "nonlinear", "eigsh"):
+    for op in ("solve", "matvec", "matvec_t", "matvec_vjp", "inverse", "nonlinear", "eigsh"):
         r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--op", op,
                             "--gpus", "2"], capture_output=True, text=True, timeout=120)
         assert r.returncode == 2 and "one GPU" in r.stderr, (op, r.stderr)
