@@ -63,6 +63,26 @@ def star_pattern(n, seed):
     return W.Problem(f"star_{n}", n, rp, col, val, z, z)
 
 
+def circulant_pattern(n, stride, seed):
+    """A circulant with columns (i + k * stride) mod n, k = 0..7, in row i,
+    relabelled by one random permutation of rows and columns alike (the
+    diagonal stays, the offsets scatter past any diagonal masks): every row
+    and every column holds 8 entries, so A^T's tiles of 256 rows hold exactly
+    2048 entries, the most the row sums stage whole (the last tile is
+    ragged)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n)
+    cols = [None] * n
+    for i in range(n):
+        cols[perm[i]] = np.sort(perm[(i + stride * np.arange(8)) % n])
+    rp = np.zeros(n + 1, dtype=np.int32)
+    rp[1:] = np.cumsum([c.size for c in cols])
+    col = np.concatenate(cols).astype(np.int32)
+    val = rng.uniform(-1.0, 1.0, (1, col.size))
+    z = np.zeros((1, n))
+    return W.Problem(f"circulant_{n}", n, rp, col, val, z, z)
+
+
 def powerlaw(n, seed, batch=1, dtype=np.float64, index=np.int32):
     rp, col, val = W.powerlaw_graph_laplacian(n, seed)
     rng = np.random.default_rng(seed + 1)
@@ -86,6 +106,7 @@ CASES = {
         9000, [3, 5, 2],
         {1: 2048, 2: 2049, 5: 4096, 300: 4097, 301: 8192, 8000: 8193, 8999: 12289}, 4),
     "star_20000": lambda: star_pattern(20000, 8),
+    "circulant_9000": lambda: circulant_pattern(9000, 1001, 12),
 }
 
 
@@ -98,7 +119,8 @@ def test_spmv_both_directions(hip, case):
 
 
 @pytest.mark.parametrize("case", ["powerlaw_2^16_batch3_fp32", "powerlaw_2^18_batch2",
-                                  "powerlaw_2^16_fp32", "chunk_edges", "star_20000"])
+                                  "powerlaw_2^16_fp32", "chunk_edges", "star_20000",
+                                  "circulant_9000"])
 def test_matvec_adjoint(hip, case):
     banner(f"row plan matvec adjoint {case}")
     _vjp_case(hip, CASES[case]())
@@ -141,7 +163,8 @@ def test_transposed_paths_agree_bitwise(hip):
     for name, p in (("powerlaw_2^16", powerlaw(1 << 16, 11, batch=2)),
                     ("chunk_edges", CASES["chunk_edges"]()),
                     ("star_20000", CASES["star_20000"]()),
-                    ("lengths_at_limits", CASES["lengths_at_limits"]())):
+                    ("lengths_at_limits", CASES["lengths_at_limits"]()),
+                    ("circulant_9000", CASES["circulant_9000"]())):
         if p.batch == 1:  # a second system with its own values
             p = W.Problem(p.name, p.n, p.row_ptr, p.col,
                           np.concatenate([p.values, -0.5 * p.values]), np.zeros((2, p.n)),
