@@ -44,7 +44,9 @@ bandwidths measured in the same run by libsla_probe.so over 2 GiB arrays
 (beyond the 256 MB Infinity Cache) and, as ``*_in_cache``, over 64 MiB
 arrays that stay in it; ``dram_frac_of_copy_ceiling`` and
 ``dram_frac_of_in_cache_copy_ceiling`` set the traffic against the two
-copies.
+copies, and ``dram_frac_of_in_cache_stream_ceiling`` against launches of
+pure in-cache streams shaped like the CG iteration (8 MB arrays, 8 read and
+4 written, 9 and 5; ``streams_GBps_in_cache`` lists every shape measured).
 On the one-workgroup solver (at most 4096 rows) the roofline is LDS
 bandwidth: (S + 11) values per row and iteration (S the gather slots).
 ``memory`` is the device memory of one forward + adjoint step.
@@ -667,6 +669,8 @@ def probe_lib():
         lib.sla_probe_write.restype = I32
         lib.sla_probe_copy_passes.argtypes = [P, P, I64, I32, P]
         lib.sla_probe_copy_passes.restype = I32
+        lib.sla_probe_streams.argtypes = [P, I64, I32, I32, P]
+        lib.sla_probe_streams.restype = I32
         lib.sla_probe_lds.argtypes = [I64, P, P]
         lib.sla_probe_lds.restype = I64
         _probe = lib
@@ -729,14 +733,50 @@ def measure_ceilings(dev):
     torch.cuda.synchronize()
     lds_s = ev0.elapsed_time(ev1) * 1e-3
     in_cache = in_cache_copy(dev)
+    streams = in_cache_streams(dev)
     return {"read_GBps": CEIL_BYTES / t["read"] / 1e9,
             "copy_GBps": 2 * CEIL_BYTES / t["copy"] / 1e9,
             "write_GBps": CEIL_BYTES / t["write"] / 1e9,
             "lds_GBps": lds_bytes / lds_s / 1e9,
             "arrays_bytes": CEIL_BYTES,
             "copy_GBps_in_cache": in_cache, "in_cache_arrays_bytes": CACHE_CEIL_BYTES,
+            "streams_GBps_in_cache": streams, "streams_array_bytes": STREAM_ARRAY_BYTES,
             "kernels": "libsla_probe.so (16 B per access; non-temporal over 2 GiB, plain "
                        "in the cache)"}
+
+
+STREAM_ARRAY_BYTES = 8_000_000  # one vector of the 1e6-row system
+STREAM_SHAPES = ((2, 2), (8, 4), (9, 5), (12, 4))
+
+
+def in_cache_streams(dev, reps=50):
+    """GB/s of sla_probe_streams, R arrays read and W written per launch, for
+    each (R, W) of STREAM_SHAPES, arrays of STREAM_ARRAY_BYTES that stay in
+    the Infinity Cache, one launch per pass as an iteration kernel runs:
+    {"RrWw": GB/s}, timed with events over `reps` launches after two."""
+    import torch
+    lib = probe_lib()
+    n = STREAM_ARRAY_BYTES // 8
+    out = {}
+    for r, w in STREAM_SHAPES:
+        buf = torch.rand((r + w) * n, dtype=torch.float64, device=dev)
+        stream = torch.cuda.current_stream()
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        for _ in range(2):
+            if lib.sla_probe_streams(_vp(buf), n, r, w, sp) != 0:
+                raise RuntimeError(f"probe streams {r}r{w}w failed")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(reps):
+            lib.sla_probe_streams(_vp(buf), n, r, w, sp)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) * 1e-3 / reps
+        out[f"{r}r{w}w"] = (r + w) * STREAM_ARRAY_BYTES / sec / 1e9
+        del buf
+    return out
 
 
 def in_cache_copy(dev, passes=32, reps=10):
@@ -1081,6 +1121,13 @@ def main():
                     # and written into it: this is its ceiling
                     "dram_frac_of_in_cache_copy_ceiling":
                         dram / ceilings["copy_GBps_in_cache"] if dram else None,
+                    # the same against pure streams of the CG iteration's
+                    # shape in the cache (8 vectors read and 4 written on
+                    # even launches, 9 and 5 on odd ones), one launch each
+                    "dram_frac_of_in_cache_stream_ceiling":
+                        dram / (0.5 * (ceilings["streams_GBps_in_cache"]["8r4w"] +
+                                       ceilings["streams_GBps_in_cache"]["9r5w"]))
+                        if dram else None,
                     "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
                     "hbm_target": "at least 70 % of peak HBM bandwidth, read as dram_frac "
                                   "(bytes past L2 by the counters; model_frac prices a launch at "

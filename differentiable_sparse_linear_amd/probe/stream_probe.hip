@@ -6,6 +6,8 @@
 //   write  b = v
 //   copy_passes  b = a + 1, a = b + 1, ... over arrays that stay in the
 //          256 MB Infinity Cache, one launch (the in-cache copy ceiling)
+//   streams  R arrays read and W written at once, in the cache, one launch
+//          per pass (the shape of a grid iteration kernel)
 //   lds    workgroups (two resident per compute unit) each read their own
 //          64 KB of LDS over and over
 //
@@ -107,6 +109,29 @@ __global__ __launch_bounds__(kThreads) void copy_passes_kernel(v2d *__restrict__
     }
 }
 
+// Many streams at once, in the cache: R arrays read and W arrays written per
+// launch, n2 16-byte elements each, consecutive in one buffer; element i of
+// every written array gets the sum of element i of the read ones (plus its
+// index).  768 workgroups of 256 threads, plain accesses, one launch per
+// pass: the shape of a grid iteration kernel that reads and writes many
+// vectors of a system that stays in the Infinity Cache.
+constexpr int kStreamBlocks = 768;
+
+template <int R, int W>
+__global__ __launch_bounds__(kThreads) void streams_kernel(v2d *__restrict__ buf, int64_t n2) {
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n2; i += stride) {
+        v2d x[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = buf[r * n2 + i];
+        v2d t = x[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r) t += x[r];
+#pragma unroll
+        for (int w = 0; w < W; ++w) buf[(R + w) * n2 + i] = t + (double)w;
+    }
+}
+
 // LDS reads: thread t reads 16 bytes at a rotating offset of a 64 KB block
 // of LDS (consecutive lanes take consecutive 16-byte words, no bank
 // conflicts); the sum keeps the reads alive.
@@ -164,6 +189,25 @@ int32_t sla_probe_copy_passes(void *d_a, void *d_b, int64_t n, int32_t passes, v
     if (!d_a || !d_b || n < 2 || (n & 1) || passes < 1) return -1;
     copy_passes_kernel<<<kPassBlocks, kThreads, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         reinterpret_cast<v2d *>(d_a), reinterpret_cast<v2d *>(d_b), n / 2, passes);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int32_t sla_probe_streams(void *d_buf, int64_t n, int32_t reads, int32_t writes,
+                          void *stream) {
+    if (!d_buf || n < 2 || (n & 1)) return -1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    v2d *b = reinterpret_cast<v2d *>(d_buf);
+    const int64_t n2 = n / 2;
+    if (reads == 2 && writes == 2)
+        streams_kernel<2, 2><<<kStreamBlocks, kThreads, 0, s>>>(b, n2);
+    else if (reads == 8 && writes == 4)
+        streams_kernel<8, 4><<<kStreamBlocks, kThreads, 0, s>>>(b, n2);
+    else if (reads == 9 && writes == 5)
+        streams_kernel<9, 5><<<kStreamBlocks, kThreads, 0, s>>>(b, n2);
+    else if (reads == 12 && writes == 4)
+        streams_kernel<12, 4><<<kStreamBlocks, kThreads, 0, s>>>(b, n2);
+    else
+        return -1;
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

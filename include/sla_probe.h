@@ -38,6 +38,13 @@ int32_t sla_probe_write(void *d_b, int64_t n, double v, void *stream);
  * Moves passes * 2 * n * 8 bytes. */
 int32_t sla_probe_copy_passes(void *d_a, void *d_b, int64_t n, int32_t passes, void *stream);
 
+/* Many streams in one launch: d_buf holds reads + writes arrays of n doubles
+ * each (n even), consecutive; arrays reads .. reads + writes - 1 get, element
+ * by element, the sum of arrays 0 .. reads - 1 (16-byte plain accesses, 768
+ * workgroups).  (reads, writes) is one of (2, 2), (8, 4), (9, 5), (12, 4),
+ * else -1.  Moves (reads + writes) * n * 8 bytes. */
+int32_t sla_probe_streams(void *d_buf, int64_t n, int32_t reads, int32_t writes, void *stream);
+
 /* 2048 workgroups (two resident per compute unit, 1024 threads each) read
  * 16 bytes per thread from their LDS 4 * reps times; returns the bytes read
  * from LDS over the launch (< 0 on error).  d_part holds at least 2048

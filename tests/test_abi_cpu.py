@@ -49,12 +49,13 @@ def test_probe_library_exports_its_header():
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(sla_probe_[a-z_]+)\s*\(", text)))
     assert names == ["sla_probe_blocks", "sla_probe_copy", "sla_probe_copy_passes",
-                     "sla_probe_lds", "sla_probe_read", "sla_probe_write"]
+                     "sla_probe_lds", "sla_probe_read", "sla_probe_streams", "sla_probe_write"]
     lib = ctypes.CDLL(b.PROBE_LIB)
     assert all(hasattr(lib, f) for f in names)
     # argument checks return before any launch
     assert lib.sla_probe_read(None, 8, None, None) == -1
     assert lib.sla_probe_copy(None, None, 8, None) == -1
+    assert lib.sla_probe_streams(None, ctypes.c_int64(8), 2, 2, None) == -1
 
 
 def test_status_strings_and_null_handle(libpath):
