@@ -46,7 +46,10 @@ arrays that stay in it; ``dram_frac_of_copy_ceiling`` and
 ``dram_frac_of_in_cache_copy_ceiling`` set the traffic against the two
 copies, and ``dram_frac_of_in_cache_stream_ceiling`` against launches of
 pure in-cache streams shaped like the CG iteration (8 MB arrays, 8 read and
-4 written, 9 and 5; ``streams_GBps_in_cache`` lists every shape measured).
+4 written, 9 and 5; ``streams_GBps_in_cache`` lists every shape measured);
+for a working set beyond the cache (512^3) ``streams_GBps_hbm`` gives the
+8 + 4 and 9 + 5 launches over 1 GiB arrays and
+``dram_frac_of_hbm_stream_ceiling`` the traffic against them.
 On the one-workgroup solver (at most 4096 rows) the roofline is LDS
 bandwidth: (S + 11) values per row and iteration (S the gather slots).
 ``memory`` is the device memory of one forward + adjoint step.
@@ -747,18 +750,19 @@ def measure_ceilings(dev):
 
 STREAM_ARRAY_BYTES = 8_000_000  # one vector of the 1e6-row system
 STREAM_SHAPES = ((2, 2), (8, 4), (9, 5), (12, 4))
+HBM_STREAM_ARRAY_BYTES = 1 << 30
 
 
-def in_cache_streams(dev, reps=50):
+def in_cache_streams(dev, reps=50, array_bytes=STREAM_ARRAY_BYTES, shapes=STREAM_SHAPES):
     """GB/s of sla_probe_streams, R arrays read and W written per launch, for
-    each (R, W) of STREAM_SHAPES, arrays of STREAM_ARRAY_BYTES that stay in
-    the Infinity Cache, one launch per pass as an iteration kernel runs:
-    {"RrWw": GB/s}, timed with events over `reps` launches after two."""
+    each (R, W) of `shapes`, arrays of `array_bytes` (by default ones that
+    stay in the Infinity Cache), one launch per pass as an iteration kernel
+    runs: {"RrWw": GB/s}, timed with events over `reps` launches after two."""
     import torch
     lib = probe_lib()
-    n = STREAM_ARRAY_BYTES // 8
+    n = array_bytes // 8
     out = {}
-    for r, w in STREAM_SHAPES:
+    for r, w in shapes:
         buf = torch.rand((r + w) * n, dtype=torch.float64, device=dev)
         stream = torch.cuda.current_stream()
         sp = ctypes.c_void_p(stream.cuda_stream)
@@ -774,8 +778,9 @@ def in_cache_streams(dev, reps=50):
         ev1.record(stream)
         torch.cuda.synchronize()
         sec = ev0.elapsed_time(ev1) * 1e-3 / reps
-        out[f"{r}r{w}w"] = (r + w) * STREAM_ARRAY_BYTES / sec / 1e9
+        out[f"{r}r{w}w"] = (r + w) * array_bytes / sec / 1e9
         del buf
+    torch.cuda.empty_cache()
     return out
 
 
@@ -1091,6 +1096,13 @@ def main():
 
     block_path = p.method == "cg" and p.n <= 4096
     ceilings = measure_ceilings(dev)
+    # a working set beyond the Infinity Cache (the 512^3 system's): the same
+    # stream launches over arrays of 1 GiB, read from and written to HBM
+    big = p.n * 13 * p.values.itemsize > (256 << 20)
+    if big:
+        ceilings["streams_GBps_hbm"] = in_cache_streams(
+            dev, reps=5, array_bytes=HBM_STREAM_ARRAY_BYTES, shapes=((8, 4), (9, 5)))
+        ceilings["streams_hbm_array_bytes"] = HBM_STREAM_ARRAY_BYTES
     if block_path:
         roofline = block_roofline(p, pat, val, b, x, opts, stream)
     else:
@@ -1128,6 +1140,11 @@ def main():
                         dram / (0.5 * (ceilings["streams_GBps_in_cache"]["8r4w"] +
                                        ceilings["streams_GBps_in_cache"]["9r5w"]))
                         if dram else None,
+                    # beyond the cache: against the same launches over 1 GiB arrays
+                    "dram_frac_of_hbm_stream_ceiling":
+                        dram / (0.5 * (ceilings["streams_GBps_hbm"]["8r4w"] +
+                                       ceilings["streams_GBps_hbm"]["9r5w"]))
+                        if dram and "streams_GBps_hbm" in ceilings else None,
                     "avg_launch_us": k_avg_s * 1e6, "launches_timed": k_n,
                     "hbm_target": "at least 70 % of peak HBM bandwidth, read as dram_frac "
                                   "(bytes past L2 by the counters; model_frac prices a launch at "
